@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the verify-and-sample step and the MTP shift.
+
+This module only draws random inputs.  It holds none of the verification
+arithmetic (no softmax, no acceptance test, no inverse CDF, no shift).  The GPU
+parity tests, the CPU oracle tests and the benchmark all take their inputs from
+here, so both sides of every comparison see the same tensors.
+
+Workload shapes follow the five configurations the benchmark and tests use:
+
+  1  tiny sampling:        B=1,    n=4, V=32000,  fp32, T=1.0, L=4
+  2  Llama-vocab sampling: B=64,   n=4, V=128256, bf16, T=0.7, L ~ U{1..4}
+  3  greedy + MTP shift:   B=256,  n=4, V=128256, bf16, greedy, L=4, H=8192
+  4  single-token MTP:     B=512,  n=1, V=129280, bf16, T=0.6, L=1, H=7168
+  5  long ragged drafts:   B=1024, n=8, V=152064, bf16, T in {0,0.7,1}, L ~ U{0..8}
+
+Draft tokens for sampling sequences are drawn from the draft distribution
+softmax(z_d / T) with the Gumbel-max construction (argmax of z_d / T plus
+Gumbel noise): this is the draft model's own sampling, which precedes the step.
+Greedy sequences (T = 0) draft the argmax of the draft logits.  For the greedy
+configuration the target's top token is planted at a random index of every row,
+so the draft can "match the target argmax" without this module computing it.
+
+Every tensor is produced by a torch.Generator seeded with the given seed on the
+given device; no step depends on the code under test.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    cid: int
+    name: str
+    B: int
+    n: int
+    V: int
+    dtype: torch.dtype
+    H: int = 0            # hidden size of the MTP carry (0: no hidden buffer)
+    mode: str = "sample"  # "sample" or "greedy"
+
+
+CONFIGS = {
+    1: Config(1, "tiny_sampling_fp32", 1, 4, 32000, torch.float32),
+    2: Config(2, "llama_vocab_sampling", 64, 4, 128256, torch.bfloat16),
+    3: Config(3, "greedy_verify_mtp_shift", 256, 4, 128256, torch.bfloat16, H=8192, mode="greedy"),
+    4: Config(4, "single_token_mtp", 512, 1, 129280, torch.bfloat16, H=7168),
+    5: Config(5, "long_ragged_drafts", 1024, 8, 152064, torch.bfloat16),
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _gumbel_draft(zd: torch.Tensor, T: torch.Tensor, g: torch.Generator) -> torch.Tensor:
+    """Draft tokens drawn from softmax(zd / T) by Gumbel-max; zd [b, n, V]."""
+    u = torch.rand(zd.shape, generator=g, device=zd.device, dtype=torch.float32)
+    u.clamp_(min=1e-12, max=1.0 - 1e-7)
+    gumbel = -torch.log(-torch.log(u))
+    scaled = zd.float() / T.view(-1, 1, 1)
+    return torch.argmax(scaled + gumbel, dim=-1).to(torch.int32)
+
+
+def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None = None,
+         H: int | None = None, n: int | None = None, block: int = 64) -> dict:
+    """Inputs of configuration ``cid`` (shape overrides allowed for small cases).
+
+    Returns a dict of tensors on ``device``:
+      target [B, n+1, V], draft [B, n, V] (None in greedy mode), draft_tokens [B, n],
+      draft_lens [B], temperature [B], uniforms [B, n+1], tokens [B, n+1] (MTP
+      token buffer: slot 0 the last committed token, slots 1..n the drafts),
+      hidden [B, n+1, H] (when H > 0).
+    """
+    cfg = CONFIGS[cid]
+    B = cfg.B if B is None else B
+    V = cfg.V if V is None else V
+    n = cfg.n if n is None else n
+    H = cfg.H if H is None else H
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    dt = cfg.dtype
+
+    target = torch.empty((B, n + 1, V), dtype=dt, device=dev)
+    draft = None if cfg.mode == "greedy" else torch.empty((B, n, V), dtype=dt, device=dev)
+    draft_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+
+    # per-sequence scalars first (small), drawn in a fixed order
+    if cid == 1:
+        lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+        temp = torch.full((B,), 1.0, dtype=torch.float32, device=dev)
+        sigma = torch.full((B,), 0.5, device=dev)
+        scale = 2.0
+    elif cid == 2:
+        lens = torch.randint(1, n + 1, (B,), generator=g, device=dev, dtype=torch.int32) if n > 0 \
+            else torch.zeros(B, dtype=torch.int32, device=dev)
+        temp = torch.full((B,), 0.7, dtype=torch.float32, device=dev)
+        sigma = torch.full((B,), 1.0, device=dev)
+        scale = 3.0
+    elif cid == 3:
+        lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+        temp = torch.zeros((B,), dtype=torch.float32, device=dev)
+        sigma = None
+        scale = 3.0
+    elif cid == 4:
+        lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+        temp = torch.full((B,), 0.6, dtype=torch.float32, device=dev)
+        sigma = torch.full((B,), 0.7, device=dev)
+        scale = 3.0
+    elif cid == 5:
+        lens = torch.randint(0, n + 1, (B,), generator=g, device=dev, dtype=torch.int32)
+        choices = torch.tensor([0.0, 0.7, 1.0], device=dev)
+        temp = choices[torch.randint(0, 3, (B,), generator=g, device=dev)].to(torch.float32)
+        sigma = 0.3 + 1.7 * torch.rand((B,), generator=g, device=dev)
+        scale = 3.0
+    else:
+        raise ValueError(cid)
+
+    for b0 in range(0, B, block):
+        b1 = min(B, b0 + block)
+        nb = b1 - b0
+        zt = scale * torch.randn((nb, n + 1, V), generator=g, device=dev, dtype=torch.float32)
+        if cid == 2 and V > 20:
+            # top-20 boost: the 20 largest logits of each target row gain +6
+            top = torch.topk(zt, 20, dim=-1).indices
+            zt.scatter_add_(-1, top, torch.full(top.shape, 6.0, device=dev))
+        if cid == 3:
+            # plant the row's top token (in 1/8 of rows also a tied twin)
+            rows = nb * (n + 1)
+            ztf = zt.view(rows, V)
+            a_top = torch.randint(0, V, (rows,), generator=g, device=dev)
+            a_tie = (a_top + 1 + torch.randint(0, max(V - 1, 1), (rows,), generator=g, device=dev)) % V
+            tie = torch.rand((rows,), generator=g, device=dev) < 0.125
+            level = 20.0 + 4.0 * torch.rand((rows,), generator=g, device=dev)
+            r = torch.arange(rows, device=dev)
+            ztf[r, a_top] = level
+            ztf[r[tie], a_tie[tie]] = level[tie]
+            target[b0:b1] = zt.to(dt)
+            # drafts: the planted top (or its twin, evenly) with probability 0.7,
+            # otherwise a uniform index other than the planted top
+            a_top = a_top.view(nb, n + 1)[:, :n]
+            a_tie = a_tie.view(nb, n + 1)[:, :n]
+            tie = tie.view(nb, n + 1)[:, :n]
+            hit = torch.rand((nb, n), generator=g, device=dev) < 0.7
+            pick_twin = tie & (torch.rand((nb, n), generator=g, device=dev) < 0.5)
+            match = torch.where(pick_twin, a_tie, a_top)
+            other = torch.randint(0, max(V - 1, 1), (nb, n), generator=g, device=dev)
+            other = torch.where(other >= a_top, other + 1, other) % V
+            draft_tokens[b0:b1] = torch.where(hit, match, other).to(torch.int32)
+            continue
+        target[b0:b1] = zt.to(dt)
+        zt_r = target[b0:b1, :n].float()                       # the values both sides read
+        noise = torch.randn((nb, n, V), generator=g, device=dev, dtype=torch.float32)
+        zd = (zt_r + sigma[b0:b1].view(-1, 1, 1) * noise).to(dt)
+        draft[b0:b1] = zd
+        tb = temp[b0:b1]
+        greedy_rows = tb == 0
+        tsafe = torch.where(greedy_rows, torch.ones_like(tb), tb)
+        x = _gumbel_draft(zd, tsafe, g) if n > 0 else torch.empty((nb, 0), dtype=torch.int32, device=dev)
+        if greedy_rows.any() and n > 0:
+            xg = torch.argmax(zd.float(), dim=-1).to(torch.int32)
+            x = torch.where(greedy_rows.view(-1, 1), xg, x)
+        draft_tokens[b0:b1] = x
+        del zt, zt_r, noise, zd
+
+    uniforms = torch.rand((B, n + 1), generator=g, device=dev, dtype=torch.float32)
+    first = torch.randint(0, V, (B, 1), generator=g, device=dev, dtype=torch.int32)
+    tokens = torch.cat([first, draft_tokens], dim=1).contiguous()
+    out = dict(cfg=cfg, B=B, n=n, V=V, target=target, draft=draft, draft_tokens=draft_tokens,
+               draft_lens=lens, temperature=temp, uniforms=uniforms, tokens=tokens)
+    if H:
+        out["hidden"] = torch.randn((B, n + 1, H), generator=g, device=dev,
+                                    dtype=torch.float32).to(torch.bfloat16)
+    out["H"] = H
+    return out
+
+
+def make_law_case(seed: int, trials: int, V: int = 8, n: int = 4, T: float = 1.0,
+                  draft_sigma: float = 1.0, device="cpu") -> dict:
+    """Many trials of one fixed set of rows (for distribution-law tests).
+
+    Target rows [n+1, V] and draft rows [n, V] are drawn once from the seed and
+    repeated for every trial; each trial gets fresh draft tokens drawn from the
+    draft distribution and fresh uniforms.  fp32 logits.
+    """
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    zt = 1.5 * torch.randn((n + 1, V), generator=g, device=dev)
+    zd = zt[:n] + draft_sigma * torch.randn((n, V), generator=g, device=dev)
+    target = zt.expand(trials, n + 1, V).contiguous()
+    draft = zd.expand(trials, n, V).contiguous()
+    temp = torch.full((trials,), float(T), device=dev)
+    x = _gumbel_draft(draft, temp, g)
+    uniforms = torch.rand((trials, n + 1), generator=g, device=dev)
+    lens = torch.full((trials,), n, dtype=torch.int32, device=dev)
+    return dict(target=target, draft=draft, draft_tokens=x, draft_lens=lens, temperature=temp,
+                uniforms=uniforms, rows_t=zt, rows_d=zd, T=T, B=trials, n=n, V=V)
+
+
+def bf16_bits(t: torch.Tensor):
+    """numpy uint16 view of a bfloat16 tensor (for the oracle)."""
+    import numpy as np
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_logits(t: torch.Tensor):
+    """numpy array the oracle accepts: fp32 as float32, bf16 as uint16 bits."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.detach().cpu().contiguous().numpy()
+
+
+def expected_rows(cfg: Config) -> float:
+    """Mean number of logit rows a step reads for the config's recipe."""
+    n = cfg.n
+    if cfg.cid == 1:
+        return 2 * n + 1
+    if cfg.cid == 2:
+        return sum((L + 1) + L for L in range(1, n + 1)) / n * cfg.B
+    if cfg.cid == 3:
+        return (n + 1) * cfg.B
+    if cfg.cid == 4:
+        return (2 * n + 1) * cfg.B
+    if cfg.cid == 5:
+        per = sum((L + 1) + (2.0 / 3.0) * L for L in range(0, n + 1)) / (n + 1)
+        return per * cfg.B
+    return math.nan

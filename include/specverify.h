@@ -1,0 +1,181 @@
+/*
+ * specverify.h -- C ABI of libspecverify: the batched verify-and-sample step of
+ * speculative decoding and the MTP token shift/insert, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operations are those of "Accelerating Sonar through speculation"
+ * (Perplexity Research, 2025): a target model scores n drafted tokens plus one
+ * bonus position in one pass; the longest acceptable prefix is kept and the
+ * target supplies one more token (Speculative decoding section, second paragraph
+ * and the four inference stages).  The acceptance test and the residual
+ * distribution are those of "Fast Inference from Transformers via Speculative
+ * Decoding", the first reference that page lists.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is DEVICE memory owned by the caller, row-major and
+ *     contiguous.  The library never allocates, frees or synchronises: each call
+ *     validates its host-side arguments, enqueues kernels on `stream` (a
+ *     hipStream_t; NULL means the null stream) and returns.  Outputs are ready
+ *     when the stream reaches them.
+ *   - Logits are IEEE binary32 (SV_F32) or bfloat16 (SV_BF16).  bfloat16 is
+ *     widened to binary32 exactly; all arithmetic is binary32 except the
+ *     per-sequence decision, which is binary64.
+ *   - Status codes report host-checkable errors synchronously: SV_EINVAL for a
+ *     NULL required pointer, B < 0, n outside [0, SV_MAX_DRAFT], V < 1, H < 0,
+ *     an unknown dtype or sizes whose element count overflows; SV_EALIGN for a
+ *     pointer not aligned to its element type; SV_EWORKSPACE when the workspace
+ *     is NULL or smaller than sv_workspace_bytes(); SV_EHIP when a launch fails
+ *     (the HIP error string is then available from sv_last_hip_error()).  On
+ *     any non-OK status nothing has been enqueued by the failing call.  Kernel
+ *     faults surface at the caller's next synchronisation.
+ *   - Values that live on the device cannot be checked synchronously.  They
+ *     follow fixed fallback rules and set bits in *err_flags (OR-ed in; the
+ *     caller clears the word):
+ *       draft_lens[b] outside [0, n]   -> clamped                SV_FLAG_LEN_CLAMPED
+ *       draft token outside [0, V)     -> rejected at its slot   SV_FLAG_TOKEN_OOR
+ *       temperature < 0 or NaN         -> treated as 0 (greedy)  SV_FLAG_BAD_TEMP
+ *       uniform NaN or < 0 / >= 1      -> 0 / largest float < 1  SV_FLAG_BAD_UNIFORM
+ *       residual mass not positive     -> draw from p_k          SV_FLAG_ZERO_RESIDUAL
+ *   - Rows the step does not need are never read: target rows r > L_b, draft
+ *     rows r >= L_b, and draft rows of sequences with T_b = 0.
+ *   - Calls that share one workspace must not overlap in time (same stream, or
+ *     ordered by events).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_MAX_DRAFT 64
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
+
+typedef enum {
+    SV_OK = 0,
+    SV_EINVAL = 1,
+    SV_EALIGN = 2,
+    SV_EWORKSPACE = 3,
+    SV_EHIP = 4
+} sv_status_t;
+
+enum {
+    SV_FLAG_LEN_CLAMPED = 1,
+    SV_FLAG_TOKEN_OOR = 2,
+    SV_FLAG_BAD_TEMP = 4,
+    SV_FLAG_BAD_UNIFORM = 8,
+    SV_FLAG_ZERO_RESIDUAL = 16
+};
+
+/* Bytes of device workspace spec_verify_sample() and spec_verify_greedy() need
+ * for these sizes (0 on invalid sizes).  The workspace holds per-chunk partial
+ * results and per-sequence arrival counters.  It must be filled with zero bytes
+ * before its first use (hipMemset, or sv_workspace_clear()); every call that
+ * completes leaves it zero-filled again, so one clear at allocation suffices. */
+size_t sv_workspace_bytes(int B, int n, int V, sv_dtype_t dt);
+
+/* Enqueue a fill of `workspace` with zero bytes on `stream` (a kernel, not a
+ * memset node, so it may be captured in a HIP graph). */
+sv_status_t sv_workspace_clear(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *sv_status_string(sv_status_t s);
+
+/* Text of the last HIP error seen by this library in the calling thread
+ * ("" if none). */
+const char *sv_last_hip_error(void);
+
+/* Verify-and-sample for a batch of B sequences with n draft slots each.
+ *
+ * Follows the Speculative decoding section (acceptance and target-generation
+ * stages) and the Target-draft section's decode paragraph of "Accelerating Sonar
+ * through speculation"; draft length 0 is the standard sampling of one token
+ * that the Target-draft section prescribes for batches without speculation.
+ *
+ * For sequence b with L = draft_lens[b], T = temperature[b], drafts x_j =
+ * draft_tokens[b][j] and p_r = softmax(target[b][r] / T), q_r = softmax(draft[b][r] / T):
+ *   - T > 0: draft j (j < L) is accepted iff u[b][j] < p_j(x_j) / q_j(x_j); the
+ *     first rejection k ends the scan.  The token after the accepted prefix is
+ *     drawn by inverse CDF with u[b][n] from max(0, p_k - q_k) (normalised) after
+ *     a rejection, or from p_L when all L drafts are accepted (k = L).
+ *   - T = 0: draft j is accepted iff it equals the argmax of target row j (raw
+ *     logits, lowest index on ties); the emitted token is the argmax of row k.
+ * Outputs: accepted_len[b] = k (0 <= k <= L <= n); emitted[b][0..k-1] = x_0..x_{k-1},
+ * emitted[b][k] = the drawn token, emitted[b][k+1..n] = -1.
+ *
+ *   target_logits [B][n+1][V] dt    draft_logits [B][n][V] dt (may be NULL when every
+ *                                   T_b = 0; never read for T_b = 0 sequences)
+ *   draft_tokens  [B][n] int32      draft_lens [B] int32     temperature [B] float
+ *   uniforms      [B][n+1] float in [0,1): [b][j] drives test j, [b][n] the draw
+ *   accepted_len  [B] int32 out     emitted [B][n+1] int32 out
+ *   row_lse       [B][2n+1] float out, nullable: ln sum exp(z/T) of target rows
+ *                 0..n then draft rows 0..n-1; NaN for rows not read (and for
+ *                 every row of a T_b = 0 sequence)
+ *   err_flags     [1] uint32, nullable: SV_FLAG_* bits OR-ed in
+ *   workspace     device scratch of at least sv_workspace_bytes(B, n, V, dt) bytes,
+ *                 zero-filled before first use
+ */
+sv_status_t spec_verify_sample(const void *target_logits, const void *draft_logits,
+                               sv_dtype_t dt, const int32_t *draft_tokens,
+                               const int32_t *draft_lens, const float *temperature,
+                               const float *uniforms, int B, int n, int V,
+                               int32_t *accepted_len, int32_t *emitted, float *row_lse,
+                               uint32_t *err_flags, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Greedy verify: the T = 0 rule of spec_verify_sample() for every sequence,
+ * without draft logits, temperatures or uniforms.  Accepts the longest prefix of
+ * drafts equal to the argmax of their target rows (lowest index on ties) and
+ * emits the argmax of the first mismatching row, or of row L when all match.
+ * Target-draft section, decode paragraph ("the draft samples its top token") of
+ * "Accelerating Sonar through speculation"; the argmax is sampling at T -> 0.
+ * Arguments as in spec_verify_sample(). */
+sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
+                               const int32_t *draft_tokens, const int32_t *draft_lens, int B,
+                               int n, int V, int32_t *accepted_len, int32_t *emitted,
+                               uint32_t *err_flags, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* MTP bookkeeping on the device, with no host synchronisation.
+ *
+ * MTP section, first paragraph, and Single-token MTP scheduling section, third
+ * paragraph, of "Accelerating Sonar through speculation": the draft predicts
+ * from a hidden state and the token that follows it (token t_{i+1} comes from
+ * logits L_i, which come from hidden state H_i), so its input token buffer is
+ * the target's shifted left one step relative to the target's hidden states, and
+ * a kernel writes the target's next token into its slot.
+ *
+ * For each sequence b with a = clamp(accepted_len[b], 0, n):
+ *   tokens[b][i] <- tokens[b][i+1]  for i < n;  tokens[b][n] keeps its value;
+ *   tokens[b][a] <- emitted[b][a]   (the token the verify step produced).
+ * Before the call, slot 0 holds the last committed token and slots 1..n the
+ * drafts; afterwards slot i <= a holds the committed token that follows
+ * position i, and slots past a hold unaccepted drafts (redundant work the draft
+ * re-run may do).
+ * Hidden states are carried unshifted: hidden_dst[b][i][:] = hidden_src[b][i][:]
+ * (a bit copy of B*(n+1)*H bfloat16 values).  hidden_dst == hidden_src, or both
+ * NULL, copies nothing.  The buffers must not partially overlap.
+ *
+ *   tokens       [B][n+1] int32, in/out     accepted_len [B] int32
+ *   emitted      [B][n+1] int32             hidden_src / hidden_dst [B][n+1][H] bf16
+ */
+sv_status_t mtp_shift_insert(int32_t *tokens, const void *hidden_src, void *hidden_dst, int H,
+                             const int32_t *accepted_len, const int32_t *emitted, int B, int n,
+                             void *stream);
+
+/* Parity/debug only (not on the hot path): full binary32 probabilities
+ * softmax(logits[r] / temperature[r]) of `rows` rows of length V, computed with
+ * the same row statistics the verify kernels use.  temperature[r] must be > 0
+ * (rows with T <= 0 or NaN are written as NaN).  probs_out [rows][V] float. */
+sv_status_t sv_softmax_rows_debug(const void *logits, sv_dtype_t dt, const float *temperature,
+                                  int rows, int V, float *probs_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

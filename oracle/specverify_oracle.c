@@ -1,0 +1,450 @@
+/*
+ * specverify_oracle.c -- CPU oracle for the batched verify-and-sample step of
+ * speculative decoding and the MTP token shift/insert.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU library never links,
+ * includes or calls it, and it shares no source with the GPU library: this file
+ * includes only the C standard library and pthreads.
+ *
+ * Source of the rules: "Accelerating Sonar through speculation" (Perplexity
+ * Research, N. Licker and E. McKnight, 2025-06-10), and the paper that page lists
+ * first among its references, "Fast Inference from Transformers via Speculative
+ * Decoding", for the acceptance test u < p/q and the residual max(0, p - q).
+ *
+ *   - Speculative decoding section, second paragraph: every candidate prefix is
+ *     scored by probability, the longest acceptable prefix is kept, and the target
+ *     supplies one extra token, so n drafts give at most n + 1 tokens per step.
+ *   - Speculative decoding section, four inference stages ("acceptance" and
+ *     "target generation"): at the mismatch, or after the last draft, the target
+ *     logits of that position yield one more token, which ends the sequence.
+ *   - Target-draft section, prefill paragraph: batches without speculation use
+ *     standard sampling (here: draft length 0).
+ *   - Target-draft section, decode paragraph: acceptance compares the full draft
+ *     and target distributions.
+ *   - MTP section, first paragraph (figure lost): token t_{i+1} is sampled from
+ *     logits L_i derived from hidden state H_i, so the input token buffer is
+ *     shifted left one step relative to the target's hidden states.
+ *   - Single-token MTP scheduling section, third paragraph: after the target's
+ *     input tokens are shifted, a kernel writes the next target token into its
+ *     slot, so no CPU sync is needed after acceptance.
+ *
+ * Everything is computed in double precision, scalar, with sums taken in
+ * ascending index order.  Nothing is blocked, fused or reordered.
+ *
+ * Readings of points the pages leave open (each is also listed in the design doc):
+ *   - acceptance of draft x_j:  u[b][j] < p_j(x_j) / q_j(x_j); q(x) = 0 gives
+ *     ratio +inf when p(x) > 0 and 0 when p(x) = 0;
+ *   - p and q are softmax(z / T_b) at the same per-sequence temperature T_b;
+ *   - after the first rejection at k: draw from max(0, p_k - q_k) normalised; if
+ *     its total is not positive (impossible in exact arithmetic) draw from p_k and
+ *     flag ZERO_RESIDUAL; after all drafts are accepted: draw from p_L;
+ *   - the final draw always uses u[b][n]; inverse CDF with unnormalised weights
+ *     in ascending index: y = min{i : C_i > u * Z}, else the last i with w_i > 0;
+ *   - T_b = 0 selects the greedy rule (argmax prefix match, lowest index on ties,
+ *     raw logits); T_b < 0 or NaN is treated as 0 and flagged;
+ *   - draft lengths outside [0, n] are clamped and flagged; a draft token outside
+ *     [0, V) is rejected at its position and flagged;
+ *   - a uniform outside [0, 1) or NaN is replaced (NaN or < 0 -> 0, >= 1 -> the
+ *     largest float below 1) and flagged;
+ *   - emitted slots after the correction/bonus token hold -1;
+ *   - MTP shift: out[i] = in[i+1] for i < n, out[n] = in[n], then
+ *     out[a_b] = emitted[b][a_b]; hidden states are carried unshifted.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+#define OR_FLAG_LEN_CLAMPED 1u
+#define OR_FLAG_TOKEN_OOR 2u
+#define OR_FLAG_BAD_TEMP 4u
+#define OR_FLAG_BAD_UNIFORM 8u
+#define OR_FLAG_ZERO_RESIDUAL 16u
+
+#define OR_MODE_SAMPLE 0
+#define OR_MODE_GREEDY 1
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Widen one logit to double.  bf16 is the top half of an IEEE binary32, so the
+ * widening is exact: place the 16 bits in the high half of a 32-bit word. */
+static double logit_at(const void *rows, int dt, size_t idx)
+{
+    if (dt == OR_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t *)rows)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)rows)[idx];
+}
+
+/* Greedy choice of one row: the maximum raw logit, lowest index on ties
+ * (strict '>' scan in ascending index). */
+static int row_argmax(const void *rows, int dt, size_t base, int V)
+{
+    int best = 0;
+    double bv = logit_at(rows, dt, base);
+    for (int i = 1; i < V; ++i) {
+        double v = logit_at(rows, dt, base + (size_t)i);
+        if (v > bv) {
+            bv = v;
+            best = i;
+        }
+    }
+    return best;
+}
+
+/* Softmax of z / T over one row, by its definition:
+ *   m = max_i z_i,  S = sum_i exp((z_i - m) / T),  lse = m / T + ln S,
+ *   p_i = exp((z_i - m) / T - ln S).
+ * Returns lse; writes m and ln S for later probability evaluation. */
+static double row_softmax_stats(const void *rows, int dt, size_t base, int V, double T,
+                                double *m_out, double *logS_out)
+{
+    double m = logit_at(rows, dt, base);
+    for (int i = 1; i < V; ++i) {
+        double v = logit_at(rows, dt, base + (size_t)i);
+        if (v > m) m = v;
+    }
+    double S = 0.0;
+    for (int i = 0; i < V; ++i)
+        S += exp((logit_at(rows, dt, base + (size_t)i) - m) / T);
+    double logS = log(S);
+    *m_out = m;
+    *logS_out = logS;
+    return m / T + logS;
+}
+
+static double prob_at(const void *rows, int dt, size_t base, int i, double T, double m, double logS)
+{
+    return exp((logit_at(rows, dt, base + (size_t)i) - m) / T - logS);
+}
+
+/* Inverse CDF over unnormalised weights in ascending index order.
+ *   Z = sum w_i,  t = u * Z,  C_i = w_0 + ... + w_i,  y = min{i : C_i > t};
+ *   if no index qualifies (t >= C_{V-1} through rounding), y = the last i with
+ *   w_i > 0 (or 0 if all weights are zero).
+ * *margin receives min(t - C_{y-1}, C_y - t) / Z with C_{-1} = 0: the distance of
+ * the threshold to the nearest CDF boundary of the chosen bucket. */
+static int draw_inverse_cdf(const double *w, int V, double u, double *margin)
+{
+    double Z = 0.0;
+    for (int i = 0; i < V; ++i) Z += w[i];
+    double t = u * Z;
+    double C = 0.0;
+    for (int i = 0; i < V; ++i) {
+        double prev = C;
+        C += w[i];
+        if (C > t) {
+            if (margin) {
+                double a = t - prev, b = C - t;
+                *margin = (Z > 0.0) ? ((a < b ? a : b) / Z) : 0.0;
+            }
+            return i;
+        }
+    }
+    int last = 0;
+    for (int i = 0; i < V; ++i)
+        if (w[i] > 0.0) last = i;
+    if (margin) *margin = 0.0;
+    return last;
+}
+
+static double sanitize_uniform(float uf, uint32_t *flags)
+{
+    double u = (double)uf;
+    if (!(u >= 0.0)) { /* NaN or negative */
+        *flags |= OR_FLAG_BAD_UNIFORM;
+        return 0.0;
+    }
+    if (u >= 1.0) {
+        *flags |= OR_FLAG_BAD_UNIFORM;
+        return 1.0 - ldexp(1.0, -24); /* largest float below 1 */
+    }
+    return u;
+}
+
+/* ------------------------------------------------------- one sequence step */
+
+typedef struct {
+    const void *target;  /* [B][n+1][V] */
+    const void *draft;   /* [B][n][V], may be NULL if every T_b = 0 */
+    int dt;
+    const int32_t *draft_tokens; /* [B][n] */
+    const int32_t *draft_lens;   /* [B] */
+    const float *temperature;    /* [B], NULL in greedy mode */
+    const float *uniforms;       /* [B][n+1], NULL in greedy mode */
+    int B, n, V, mode;
+    int32_t *accepted_len;  /* [B] */
+    int32_t *emitted;       /* [B][n+1] */
+    double *row_lse;        /* [B][2n+1] nullable */
+    double *accept_margin;  /* [B][n] nullable */
+    double *draw_margin;    /* [B] nullable */
+    uint32_t *seq_flags;    /* [B] nullable */
+} job_t;
+
+static void verify_one(const job_t *J, int b, double *w /* scratch [V] */)
+{
+    const int n = J->n, V = J->V;
+    uint32_t flags = 0;
+    int L = J->draft_lens[b];
+    if (L < 0) { L = 0; flags |= OR_FLAG_LEN_CLAMPED; }
+    if (L > n) { L = n; flags |= OR_FLAG_LEN_CLAMPED; }
+
+    double T = 0.0;
+    if (J->mode == OR_MODE_SAMPLE) {
+        T = (double)J->temperature[b];
+        if (!(T >= 0.0)) { T = 0.0; flags |= OR_FLAG_BAD_TEMP; }
+    }
+    const int32_t *x = J->draft_tokens + (size_t)b * n;
+    const size_t trow0 = (size_t)b * (size_t)(n + 1) * (size_t)V; /* target row 0 of b */
+    const size_t drow0 = (size_t)b * (size_t)n * (size_t)V;       /* draft row 0 of b  */
+
+    if (J->row_lse)
+        for (int r = 0; r < 2 * n + 1; ++r) J->row_lse[(size_t)b * (2 * n + 1) + r] = NAN;
+    if (J->accept_margin)
+        for (int j = 0; j < n; ++j) J->accept_margin[(size_t)b * n + j] = INFINITY;
+    if (J->draw_margin) J->draw_margin[b] = INFINITY;
+
+    int k = L, y = -1;
+    if (J->mode == OR_MODE_GREEDY || T == 0.0) {
+        /* greedy rule: accept x_j iff it is the target argmax of row j */
+        k = L;
+        for (int j = 0; j < L; ++j) {
+            int g = row_argmax(J->target, J->dt, trow0 + (size_t)j * V, V);
+            if (x[j] < 0 || x[j] >= V) flags |= OR_FLAG_TOKEN_OOR;
+            if (x[j] != g) { k = j; y = g; break; }
+        }
+        if (k == L) y = row_argmax(J->target, J->dt, trow0 + (size_t)L * V, V);
+    } else {
+        /* softmax statistics of every row the step may read */
+        double mt[129], lst[129], md[129], lsd[129]; /* n <= 128 */
+        for (int r = 0; r <= L; ++r) {
+            double lse = row_softmax_stats(J->target, J->dt, trow0 + (size_t)r * V, V, T, &mt[r], &lst[r]);
+            if (J->row_lse) J->row_lse[(size_t)b * (2 * n + 1) + r] = lse;
+        }
+        for (int r = 0; r < L; ++r) {
+            double lse = row_softmax_stats(J->draft, J->dt, drow0 + (size_t)r * V, V, T, &md[r], &lsd[r]);
+            if (J->row_lse) J->row_lse[(size_t)b * (2 * n + 1) + (n + 1) + r] = lse;
+        }
+        /* acceptance tests in order; the first rejection ends the scan */
+        int rejected = 0;
+        for (int j = 0; j < L; ++j) {
+            if (x[j] < 0 || x[j] >= V) {
+                flags |= OR_FLAG_TOKEN_OOR;
+                k = j;
+                rejected = 1;
+                break;
+            }
+            double u = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + j], &flags);
+            double p = prob_at(J->target, J->dt, trow0 + (size_t)j * V, x[j], T, mt[j], lst[j]);
+            double q = prob_at(J->draft, J->dt, drow0 + (size_t)j * V, x[j], T, md[j], lsd[j]);
+            double ratio = (q > 0.0) ? p / q : (p > 0.0 ? INFINITY : 0.0);
+            if (J->accept_margin) J->accept_margin[(size_t)b * n + j] = fabs(u - ratio);
+#if SV_ORACLE_PLANT == 3
+            /* planted mistake for negative-control tests: the ratio inverted */
+            ratio = (p > 0.0) ? q / p : (q > 0.0 ? INFINITY : 0.0);
+#endif
+            if (!(u < ratio)) {
+                k = j;
+                rejected = 1;
+                break;
+            }
+        }
+        double ufinal = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + n], &flags);
+#if SV_ORACLE_PLANT == 2
+        /* planted mistake: the rejected position's own uniform drives the draw */
+        if (rejected) ufinal = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + k], &flags);
+#endif
+        if (rejected) {
+            /* residual distribution max(0, p_k - q_k) */
+            double Z = 0.0;
+            for (int i = 0; i < V; ++i) {
+                double p = prob_at(J->target, J->dt, trow0 + (size_t)k * V, i, T, mt[k], lst[k]);
+                double q = prob_at(J->draft, J->dt, drow0 + (size_t)k * V, i, T, md[k], lsd[k]);
+                double d = p - q;
+                w[i] = d > 0.0 ? d : 0.0;
+#if SV_ORACLE_PLANT == 1
+                /* planted mistake: plain target sampling at the rejection */
+                w[i] = p;
+#endif
+                Z += w[i];
+            }
+            if (!(Z > 0.0)) {
+                flags |= OR_FLAG_ZERO_RESIDUAL;
+                for (int i = 0; i < V; ++i)
+                    w[i] = prob_at(J->target, J->dt, trow0 + (size_t)k * V, i, T, mt[k], lst[k]);
+            }
+        } else {
+            /* every draft accepted: the bonus token comes from p_L */
+            for (int i = 0; i < V; ++i)
+                w[i] = prob_at(J->target, J->dt, trow0 + (size_t)L * V, i, T, mt[L], lst[L]);
+        }
+        double margin = 0.0;
+        y = draw_inverse_cdf(w, V, ufinal, &margin);
+        if (J->draw_margin) J->draw_margin[b] = margin;
+    }
+
+    /* emit: accepted prefix, then the correction or bonus token, then -1 */
+    J->accepted_len[b] = k;
+    int32_t *e = J->emitted + (size_t)b * (n + 1);
+    for (int j = 0; j < k; ++j) e[j] = x[j];
+    e[k] = y;
+    for (int j = k + 1; j <= n; ++j) e[j] = -1;
+    if (J->seq_flags) J->seq_flags[b] = flags;
+}
+
+typedef struct {
+    const job_t *job;
+    int b0, b1;
+    int status;
+} slice_t;
+
+static void *run_slice(void *arg)
+{
+    slice_t *s = (slice_t *)arg;
+    double *w = (double *)malloc(sizeof(double) * (size_t)s->job->V);
+    if (!w) { s->status = -2; return NULL; }
+    for (int b = s->b0; b < s->b1; ++b) verify_one(s->job, b, w);
+    free(w);
+    s->status = 0;
+    return NULL;
+}
+
+static int run_job(const job_t *J, int threads)
+{
+    if (J->B <= 0) return 0;
+    if (threads < 1) threads = 1;
+    if (threads > J->B) threads = J->B;
+    slice_t *sl = (slice_t *)calloc((size_t)threads, sizeof(slice_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!sl || !th) { free(sl); free(th); return -2; }
+    for (int t = 0; t < threads; ++t) {
+        sl[t].job = J;
+        sl[t].b0 = (int)((long long)J->B * t / threads);
+        sl[t].b1 = (int)((long long)J->B * (t + 1) / threads);
+    }
+    int rc = 0;
+    if (threads == 1) {
+        run_slice(&sl[0]);
+        rc = sl[0].status;
+    } else {
+        for (int t = 0; t < threads; ++t) pthread_create(&th[t], NULL, run_slice, &sl[t]);
+        for (int t = 0; t < threads; ++t) {
+            pthread_join(th[t], NULL);
+            if (sl[t].status) rc = sl[t].status;
+        }
+    }
+    free(sl);
+    free(th);
+    return rc;
+}
+
+static int check_dims(int B, int n, int V)
+{
+    if (B < 0 || n < 0 || n > 128 || V < 1) return -1;
+    return 0;
+}
+
+/* ---------------------------------------------------------------- exports */
+
+/* Verify-and-sample for every sequence.  Returns 0 on success, -1 on bad sizes,
+ * -2 if scratch memory cannot be had.  seq_flags receives per-sequence OR_FLAG_*
+ * bits (the GPU library reports their OR). */
+int sv_oracle_verify_sample(const void *target_logits, const void *draft_logits, int dt,
+                            const int32_t *draft_tokens, const int32_t *draft_lens,
+                            const float *temperature, const float *uniforms, int B, int n, int V,
+                            int32_t *accepted_len, int32_t *emitted, double *row_lse,
+                            double *accept_margin, double *draw_margin, uint32_t *seq_flags,
+                            int threads)
+{
+    if (check_dims(B, n, V)) return -1;
+    job_t J = {target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms,
+               B, n, V, OR_MODE_SAMPLE, accepted_len, emitted, row_lse, accept_margin,
+               draw_margin, seq_flags};
+    return run_job(&J, threads);
+}
+
+/* Greedy verify: accept the longest prefix whose drafts equal the target argmax;
+ * the emitted token after it is the argmax of the first mismatching (or bonus)
+ * row. */
+int sv_oracle_verify_greedy(const void *target_logits, int dt, const int32_t *draft_tokens,
+                            const int32_t *draft_lens, int B, int n, int V, int32_t *accepted_len,
+                            int32_t *emitted, uint32_t *seq_flags, int threads)
+{
+    if (check_dims(B, n, V)) return -1;
+    job_t J = {target_logits, NULL, dt, draft_tokens, draft_lens, NULL, NULL, B, n, V,
+               OR_MODE_GREEDY, accepted_len, emitted, NULL, NULL, NULL, seq_flags};
+    return run_job(&J, threads);
+}
+
+/* MTP bookkeeping.  The draft's input slot i pairs the target hidden state H_i
+ * with the token that follows position i, so the token buffer moves left by one
+ * relative to the hidden states, and the token the target just produced (emitted
+ * at slot a_b) goes into slot a_b.  Slot n keeps its old value unless a_b = n.
+ * Hidden states are copied unchanged (elem_bytes per element, B*(n+1)*H
+ * elements); hidden_src == hidden_dst, or both NULL, copies nothing.  accepted
+ * lengths outside [0, n] are clamped. */
+int sv_oracle_mtp_shift_insert(int32_t *tokens, const void *hidden_src, void *hidden_dst, int H,
+                               int elem_bytes, const int32_t *accepted_len,
+                               const int32_t *emitted, int B, int n)
+{
+    if (B < 0 || n < 0 || H < 0 || elem_bytes < 0) return -1;
+    int32_t *old = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n + 1));
+    if (!old) return -2;
+    for (int b = 0; b < B; ++b) {
+        int32_t *t = tokens + (size_t)b * (n + 1);
+        for (int i = 0; i <= n; ++i) old[i] = t[i];
+        for (int i = 0; i < n; ++i) t[i] = old[i + 1];
+        t[n] = old[n];
+        int a = accepted_len[b];
+        if (a < 0) a = 0;
+        if (a > n) a = n;
+        t[a] = emitted[(size_t)b * (n + 1) + a];
+    }
+    free(old);
+    if (hidden_src && hidden_dst && hidden_src != hidden_dst)
+        memcpy(hidden_dst, hidden_src, (size_t)B * (size_t)(n + 1) * (size_t)H * (size_t)elem_bytes);
+    return 0;
+}
+
+/* Softmax of one row at temperature T (> 0): returns lse = log sum exp(z / T) and,
+ * if p_out is not NULL, writes p_i = exp(z_i / T - lse). */
+double sv_oracle_softmax_row(const void *z, int dt, int V, double T, double *p_out)
+{
+    double m, logS;
+    double lse = row_softmax_stats(z, dt, 0, V, T, &m, &logS);
+    if (p_out)
+        for (int i = 0; i < V; ++i) p_out[i] = prob_at(z, dt, 0, i, T, m, logS);
+    return lse;
+}
+
+/* Greedy choice of one row (lowest index of the maximum). */
+int sv_oracle_argmax_row(const void *z, int dt, int V)
+{
+    return row_argmax(z, dt, 0, V);
+}
+
+/* The inverse-CDF step on explicit weights (exposed for pinning). */
+int sv_oracle_draw_weights(const double *w, int V, double u, double *margin)
+{
+    return draw_inverse_cdf(w, V, u, margin);
+}
+
+/* Which planted mistake this build carries (0 = none).  Test-only builds set
+ * SV_ORACLE_PLANT to show that the statistical tests reject a wrong rule. */
+int sv_oracle_plant(void)
+{
+#ifdef SV_ORACLE_PLANT
+    return SV_ORACLE_PLANT;
+#else
+    return 0;
+#endif
+}
