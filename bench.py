@@ -1,0 +1,265 @@
+"""Benchmark of the verify-and-sample hot path on one MI355X.
+
+Default workload (the headline): greedy verify + MTP shift/insert at B=256
+sequences, n=4 drafts, V=128256 bf16 logits, hidden size 8192.  One step =
+spec_verify_greedy() over the [256, 5, 128256] target logits followed by
+mtp_shift_insert() of the [256, 5] token buffer and the [256, 5, 8192] hidden
+states.  Inputs are synthetic (seeded), resident in HBM, and rotate over
+several independent copies so that no step finds its inputs in the 256 MB
+last-level cache.
+
+Prints one JSON line: verified vocab rows/s (value), HBM GB/s and % of the
+8 TB/s peak, a roofline entry for the dominant kernel (the verify kernel,
+timed with HIP events on its stream), and the CPU oracle timed on host cores.
+
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "draft_token_verification_08_amd", "csrc", "sv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--seed", type=int, default=303)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    only if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel}|{workload}")
+    if not e or e.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sequences shard "
+              "across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_token_verification_08_amd as sv
+    from draft_token_verification_08_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    greedy = cfg.mode == "greedy"
+    es = 2 if cfg.dtype == torch.bfloat16 else 4
+
+    # ---------------------------------------------------------------- inputs
+    one = cfg.B * (cfg.n + 1) * cfg.V * es * (1 if greedy else 2) + 2 * cfg.B * (cfg.n + 1) * cfg.H * 2
+    sets = args.sets or max(2, min(8, int(np.ceil(1.2e9 / one))))
+    data = []
+    for i in range(sets):
+        d = synth.make(args.config, args.seed + i, device=dev)
+        d["hidden_dst"] = torch.empty_like(d["hidden"]) if cfg.H else None
+        d["tokens0"] = d["tokens"].clone()
+        d["acc"] = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+        d["emi"] = torch.empty((cfg.B, cfg.n + 1), dtype=torch.int32, device=dev)
+        data.append(d)
+    torch.cuda.synchronize()
+    ws = sv.Workspace(dev)
+    wsbuf = ws.get(sv.sv_workspace_bytes(cfg.B, cfg.n, cfg.V, sv.SV_BF16 if es == 2 else sv.SV_F32))
+    stream = torch.cuda.current_stream(dev)
+
+    def verify(d):
+        if greedy:
+            sv.spec_verify_greedy(d["target"], d["draft_tokens"], d["draft_lens"], accepted_len=d["acc"],
+                                  emitted=d["emi"], workspace=wsbuf)
+        else:
+            sv.spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                  d["temperature"], d["uniforms"], accepted_len=d["acc"], emitted=d["emi"],
+                                  workspace=wsbuf)
+
+    def mtp(d):
+        if cfg.H:
+            sv.mtp_shift_insert(d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+
+    # algorithmic bytes per step (each required row counted once)
+    lens = [d["draft_lens"].clamp(0, cfg.n).to(torch.int64) for d in data]
+    temps = [d["temperature"] for d in data]
+    rows_t = [int((L + 1).sum()) for L in lens]
+    rows_d = [0 if greedy else int((L * (t > 0).to(torch.int64)).sum()) for L, t in zip(lens, temps)]
+    side = cfg.B * cfg.n * 4 + cfg.B * 4 + cfg.B * 4 + cfg.B * (cfg.n + 1) * 4
+    if not greedy:
+        side += cfg.B * 4 + cfg.B * (cfg.n + 1) * 4
+    verify_bytes = [(rt + rd) * cfg.V * es + side for rt, rd in zip(rows_t, rows_d)]
+    mtp_bytes = (2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4 + cfg.B * 4
+                 + cfg.B * (cfg.n + 1) * 4) if cfg.H else 0
+    rows_per_step = [rt + rd for rt, rd in zip(rows_t, rows_d)]
+
+    # ---------------------------------------------------------------- warmup
+    for i in range(args.warmup):
+        d = data[i % sets]
+        verify(d)
+        mtp(d)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        d = data[i % sets]
+        ev[i][0].record(stream)
+        verify(d)
+        ev[i][1].record(stream)
+        mtp(d)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    verify_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    mtp_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = elapsed * 1e3 / K
+    rows_total = sum(rows_per_step[i % sets] for i in range(K))
+    bytes_total = sum(verify_bytes[i % sets] + mtp_bytes for i in range(K))
+    value = rows_total / elapsed
+    gbps = bytes_total / elapsed / 1e9
+    v_avg_ms = statistics.fmean(verify_ms)
+    v_bytes = statistics.fmean(verify_bytes[i % sets] for i in range(K))
+    v_gbps = v_bytes / (v_avg_ms * 1e-3) / 1e9
+    m_avg_ms = statistics.fmean(mtp_ms) if cfg.H else 0.0
+    mean_acc = float(torch.stack([d["acc"].float().mean() for d in data]).mean())
+
+    kernel = "k_stats_greedy" if greedy else "k_stats_sample+k_draw"
+    workload = cfg.name
+    traffic = measured_traffic(kernel, workload)
+
+    out = {
+        "metric": "verified vocab rows/s + HBM GB/s (% of peak), V=128256 bf16, B=256, n=4",
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if es == 2 else "f32",
+        "data": "synthetic (seeded; inputs resident in HBM, rotated over %d copies)" % sets,
+        "config": {"workload": ("greedy verify + MTP shift/insert" if greedy else "sampling verify")
+                   + f" ({cfg.name})", "B": cfg.B, "n": cfg.n, "V": cfg.V, "H": cfg.H,
+                   "logits": "bf16" if es == 2 else "f32", "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(gbps, 1),
+        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "verify_us": round(v_avg_ms * 1e3, 2),
+        "mtp_us": round(m_avg_ms * 1e3, 2),
+        "mean_accepted": round(mean_acc, 4),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(v_gbps, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(v_gbps / PEAK_GBPS, 4),
+                     "bytes_per_launch": int(v_bytes), "avg_launch_us": round(v_avg_ms * 1e3, 2),
+                     "traffic": traffic},
+    }
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(data[0], cfg, greedy)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(d, cfg, greedy):
+    """The oracle (plain C, double precision, untuned) on one full step of the same
+    workload, on the host cores: single-threaded and with one thread per core of
+    this process's CPU share (sequences split evenly)."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    host = dict(target=synth.host_logits(d["target"]),
+                draft=None if greedy else synth.host_logits(d["draft"]),
+                x=d["draft_tokens"].cpu().numpy(), L=d["draft_lens"].cpu().numpy(),
+                T=d["temperature"].cpu().numpy(), u=d["uniforms"].cpu().numpy(),
+                tok=d["tokens0"].cpu().numpy(),
+                hid=d["hidden"].cpu().view(__import__("torch").int16).numpy() if cfg.H else None)
+    rows = int((np.clip(host["L"], 0, cfg.n) + 1).sum())
+    if not greedy:
+        rows += int((np.clip(host["L"], 0, cfg.n) * (host["T"] > 0)).sum())
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+
+    def step(th):
+        if greedy:
+            o = orc.verify_greedy(host["target"], host["x"], host["L"], threads=th)
+        else:
+            o = orc.verify_sample(host["target"], host["draft"], host["x"], host["L"], host["T"], host["u"],
+                                  threads=th)
+        if cfg.H:
+            orc.mtp_shift_insert(host["tok"], host["hid"], o["accepted_len"], o["emitted"])
+
+    def timed(th, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            step(th)
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    t1 = timed(1, 3)
+    tn = timed(threads, 3)
+    return {"value": round(rows / tn, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step ({cfg.B} sequences, {rows} rows of V={cfg.V}"
+                      + (", + MTP shift/hidden copy" if cfg.H else "") + "), median of 3",
+            "single_thread_rows_per_s": round(rows / t1, 1), "seconds_per_step": round(tn, 4),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+// sv_api.cpp -- the C ABI of libspecverify: argument checks, workspace layout and
+// launch configuration.  Every check here uses host-visible values only; nothing
+// reads device memory and nothing synchronises.
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+sv_status_t hip_fail(hipError_t e) {
+    std::snprintf(g_hip_error, sizeof g_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return SV_EHIP;
+}
+
+size_t elem_bytes(sv_dtype_t dt) { return dt == SV_BF16 ? 2 : 4; }
+int vec_elems(sv_dtype_t dt) { return dt == SV_BF16 ? 8 : 4; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_sizes(int B, int n, int V) {
+    return B >= 0 && n >= 0 && n <= sv::kMaxDraft && V >= 1;
+}
+
+// Chunking of rows over workgroups.  Depends on (B, n, V, dt) only, so the
+// sample and greedy entry points agree with sv_workspace_bytes().
+//   stats pass: enough chunks that ~kTargetWorkgroups workgroups cover the
+//     B*(n+1) target rows; chunk length a multiple of one vector per thread.
+//   draw pass: fixed chunks of kThreads * kDrawPerThread elements.
+bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
+    const long long tile = (long long)sv::kThreads * vec_elems(dt);
+    const long long rows_t = (long long)B * (n + 1);
+    long long nc = rows_t > 0 ? ceil_div(sv::kTargetWorkgroups, rows_t) : 1;
+    const long long nc_max = ceil_div(V, tile);
+    if (nc > nc_max) nc = nc_max;
+    if (nc < 1) nc = 1;
+    long long ch = ceil_div(ceil_div(V, nc), tile) * tile;
+    nc = ceil_div(V, ch);
+    const long long chd = (long long)sv::kThreads * sv::kDrawPerThread;
+    const long long ncd = ceil_div(V, chd);
+    if (ncd > sv::kMaxDrawChunks) return false;
+    L->NC = (int)nc;
+    L->CH = (int)ch;
+    L->NCd = (int)ncd;
+    L->CHd = (int)chd;
+    const size_t slots = (size_t)(2 * n + 1);
+    size_t off = 0;
+    L->off_part = off;
+    off = align_up(off + (size_t)B * slots * nc * sizeof(sv::Partial), 256);
+    L->off_cnt = off;
+    off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+    L->off_cnt_draw = off;
+    off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+    L->off_desc = off;
+    off = align_up(off + (size_t)B * sizeof(sv::DrawDesc), 256);
+    L->off_dpart = off;
+    off = align_up(off + (size_t)B * ncd * sizeof(float), 256);
+    L->bytes = off < 256 ? 256 : off;
+    return true;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// grid sizes stay within one 32-bit dimension of 256-thread workgroups
+bool grid_ok(long long blocks) { return blocks >= 0 && blocks * sv::kThreads <= 0xFFFFFFFFll; }
+
+bool rows_aligned(const void* base, int V, sv_dtype_t dt) {
+    return aligned_to(base, 16) && ((size_t)V * elem_bytes(dt)) % 16 == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(int B, int n, int V, sv_dtype_t dt) {
+    if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return 0;
+    sv::Layout L;
+    if (!make_layout(B, n, V, dt, &L)) return 0;
+    return L.bytes;
+}
+
+sv_status_t sv_workspace_clear(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace_bytes == 0) return SV_OK;
+    if (!workspace) return SV_EINVAL;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    hipError_t e = sv::launch_clear(workspace, workspace_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+const char* sv_status_string(sv_status_t s) {
+    switch (s) {
+        case SV_OK: return "SV_OK: success";
+        case SV_EINVAL: return "SV_EINVAL: invalid argument (NULL pointer or size out of range)";
+        case SV_EALIGN: return "SV_EALIGN: pointer not aligned to its element type";
+        case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing or smaller than sv_workspace_bytes()";
+        case SV_EHIP: return "SV_EHIP: HIP launch failed (see sv_last_hip_error())";
+    }
+    return "unknown status";
+}
+
+const char* sv_last_hip_error(void) { return g_hip_error; }
+
+sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                               const int32_t* draft_tokens, const int32_t* draft_lens,
+                               const float* temperature, const float* uniforms, int B, int n, int V,
+                               int32_t* accepted_len, int32_t* emitted, float* row_lse,
+                               uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_lens || !temperature || !uniforms || !accepted_len || !emitted ||
+        (n > 0 && !draft_tokens))
+        return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(target_logits, es) || (draft_logits && !aligned_to(draft_logits, es)) ||
+        !aligned_to(draft_tokens, 4) || !aligned_to(draft_lens, 4) || !aligned_to(temperature, 4) ||
+        !aligned_to(uniforms, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) ||
+        !aligned_to(row_lse, 4) || !aligned_to(err_flags, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, n, V, dt, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    const int S = 2 * n + 1;
+    if (!grid_ok((long long)B * S * L.NC) || !grid_ok((long long)B * L.NCd)) return SV_EINVAL;
+
+    const bool aligned = rows_aligned(target_logits, V, dt) && (!draft_logits || aligned_to(draft_logits, 16));
+    hipStream_t s = (hipStream_t)stream;
+
+    sv::StatsParams sp{};
+    sp.target = target_logits;
+    sp.draft = draft_logits;
+    sp.tokens = draft_tokens;
+    sp.lens = draft_lens;
+    sp.temp = temperature;
+    sp.unif = uniforms;
+    sp.B = B; sp.n = n; sp.V = V; sp.NC = L.NC; sp.CH = L.CH; sp.S = S;
+    sp.acc = accepted_len;
+    sp.emitted = emitted;
+    sp.row_lse = row_lse;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
+    if (e != hipSuccess) return hip_fail(e);
+
+    sv::DrawParams dp{};
+    dp.target = target_logits;
+    dp.draft = draft_logits;
+    dp.B = B; dp.n = n; dp.V = V; dp.NCd = L.NCd; dp.CHd = L.CHd;
+    dp.emitted = emitted;
+    dp.flags = err_flags;
+    dp.desc = sp.desc;
+    dp.dpart = at<float>(workspace, L.off_dpart);
+    dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+    e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                               const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
+                               int32_t* emitted, uint32_t* err_flags, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_lens || !accepted_len || !emitted || (n > 0 && !draft_tokens))
+        return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(target_logits, es) || !aligned_to(draft_tokens, 4) || !aligned_to(draft_lens, 4) ||
+        !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) || !aligned_to(err_flags, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, n, V, dt, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    const int S = n + 1;
+    if (!grid_ok((long long)B * S * L.NC)) return SV_EINVAL;
+
+    sv::StatsParams sp{};
+    sp.target = target_logits;
+    sp.draft = nullptr;
+    sp.tokens = draft_tokens;
+    sp.lens = draft_lens;
+    sp.B = B; sp.n = n; sp.V = V; sp.NC = L.NC; sp.CH = L.CH; sp.S = S;
+    sp.acc = accepted_len;
+    sp.emitted = emitted;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kGreedy,
+                                    rows_aligned(target_logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+sv_status_t mtp_shift_insert(int32_t* tokens, const void* hidden_src, void* hidden_dst, int H,
+                             const int32_t* accepted_len, const int32_t* emitted, int B, int n,
+                             void* stream) {
+    if (B < 0 || n < 0 || n > sv::kMaxDraft || H < 0) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!tokens || !accepted_len || !emitted) return SV_EINVAL;
+    if ((hidden_src == nullptr) != (hidden_dst == nullptr)) return SV_EINVAL;
+    if (hidden_src && H < 1) return SV_EINVAL;
+    if (!aligned_to(tokens, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) ||
+        !aligned_to(hidden_src, 2) || !aligned_to(hidden_dst, 2))
+        return SV_EALIGN;
+    sv::MtpParams mp{};
+    mp.tokens = tokens;
+    mp.hsrc = hidden_src;
+    mp.hdst = hidden_dst;
+    mp.hidden_elems = hidden_src ? (long long)B * (n + 1) * H : 0;
+    mp.acc = accepted_len;
+    mp.emitted = emitted;
+    mp.B = B;
+    mp.n = n;
+    const bool aligned = aligned_to(hidden_src, 16) && aligned_to(hidden_dst, 16);
+    hipError_t e = sv::launch_mtp(mp, aligned, (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+sv_status_t sv_softmax_rows_debug(const void* logits, sv_dtype_t dt, const float* temperature, int rows,
+                                  int V, float* probs_out, void* stream) {
+    if (rows < 0 || V < 1 || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (rows == 0) return SV_OK;
+    if (!logits || !temperature || !probs_out) return SV_EINVAL;
+    if (!aligned_to(logits, elem_bytes(dt)) || !aligned_to(temperature, 4) || !aligned_to(probs_out, 4))
+        return SV_EALIGN;
+    hipError_t e = sv::launch_softmax_debug(logits, dt == SV_BF16 ? sv::kBF16 : sv::kF32, temperature, rows,
+                                            V, probs_out, rows_aligned(logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// sv_internal.h -- layouts and launch parameters shared by the kernels
+// (sv_kernels.hip) and the host ABI layer (sv_api.cpp) of libspecverify.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;        // workgroup size of every kernel (4 wave64s)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxDraft = 64;        // n <= kMaxDraft
+constexpr int kMaxSlots = 2 * kMaxDraft + 1;
+constexpr int kDrawPerThread = 16;   // draw pass: contiguous elements per thread
+constexpr int kMaxDrawChunks = 1024; // LDS bound of the draw selection
+constexpr int kTargetWorkgroups = 2048;  // stats pass: aim for ~8 workgroups per CU
+
+enum Dt : int { kF32 = 0, kBF16 = 1 };
+enum Mode : int { kSample = 0, kGreedy = 1 };
+
+// kinds of the final draw of a sequence
+enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
+
+// One per (sequence, row slot, vocab chunk): the chunk's reduction.
+//   sampling rows: a = chunk max m_c, b = sum over the chunk of 2^((z - m_c) c)
+//   greedy rows:   a = chunk max value, b = bit pattern of the lowest index of it
+struct Partial {
+    float a;
+    float b;
+};
+
+// Per sequence, written by the decision and read by the draw pass.
+struct DrawDesc {
+    int kind;       // DrawKind
+    int k;          // row index of the draw (target row k, and draft row k if residual)
+    float c;        // log2(e) / T as used for every exponent of this sequence
+    float m_t;      // max of target row k
+    float inv_s_t;  // 1 / sum 2^((z - m_t) c) of target row k
+    float m_d;      // same for draft row k (residual only)
+    float inv_s_d;
+    float u;        // the (sanitised) final uniform u[b][n]
+};
+
+// Workspace layout (byte offsets from the workspace base; every region 256-aligned).
+struct Layout {
+    int NC;          // vocab chunks per row in the stats pass
+    int CH;          // elements per stats chunk (multiple of the vector tile)
+    int NCd;         // chunks per row in the draw pass
+    int CHd;         // elements per draw chunk
+    size_t off_part;     // Partial [B][2n+1][NC]
+    size_t off_cnt;      // uint32 [B]   stats-pass arrival counters
+    size_t off_cnt_draw; // uint32 [B]   draw-pass arrival counters
+    size_t off_desc;     // DrawDesc [B]
+    size_t off_dpart;    // float [B][NCd] draw-pass chunk sums
+    size_t bytes;
+};
+
+struct StatsParams {
+    const void* target;       // [B][n+1][V]
+    const void* draft;        // [B][n][V] or nullptr
+    const int32_t* tokens;    // [B][n]
+    const int32_t* lens;      // [B]
+    const float* temp;        // [B] (sample mode)
+    const float* unif;        // [B][n+1] (sample mode)
+    int B, n, V, NC, CH, S;   // S = row slots per sequence (2n+1 sample, n+1 greedy)
+    int32_t* acc;             // [B]
+    int32_t* emitted;         // [B][n+1]
+    float* row_lse;           // [B][2n+1] or nullptr
+    uint32_t* flags;          // [1] or nullptr
+    Partial* part;
+    uint32_t* cnt;
+    DrawDesc* desc;
+};
+
+struct DrawParams {
+    const void* target;
+    const void* draft;
+    int B, n, V, NCd, CHd;
+    int32_t* emitted;
+    uint32_t* flags;
+    DrawDesc* desc;
+    float* dpart;
+    uint32_t* cnt;
+};
+
+struct MtpParams {
+    int32_t* tokens;          // [B][n+1]
+    const void* hsrc;         // [B][n+1][H] bf16 or nullptr
+    void* hdst;
+    long long hidden_elems;   // B*(n+1)*H
+    const int32_t* acc;
+    const int32_t* emitted;
+    int B, n;
+};
+
+// launches (sv_kernels.hip); return the hipGetLastError() after the launch
+hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s);
+hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s);
+hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s);
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
+hipError_t launch_softmax_debug(const void* logits, Dt dt, const float* temp, int rows, int V,
+                                float* out, bool aligned, hipStream_t s);
+
+}  // namespace sv

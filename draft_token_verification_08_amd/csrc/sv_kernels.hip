@@ -1,0 +1,910 @@
+// sv_kernels.hip -- gfx950 kernels of libspecverify.
+//
+// The verify-and-sample step of "Accelerating Sonar through speculation"
+// (Speculative decoding section: acceptance and target-generation stages;
+// Target-draft section: acceptance compares the full draft and target
+// distributions) with the acceptance test u < p/q and the residual max(0, p - q)
+// of "Fast Inference from Transformers via Speculative Decoding", plus the MTP
+// token shift/insert of the MTP and Single-token MTP scheduling sections.
+//
+// Passes (all on the caller's stream, no host synchronisation):
+//   k_stats  one workgroup per (sequence, row slot, vocab chunk).  Streams its
+//            chunk once with 16-byte loads and reduces it: greedy rows to
+//            (max, lowest index), sampling rows to an online softmax partial
+//            (chunk max m_c, sum of 2^((z - m_c) log2(e)/T)).  The last
+//            workgroup of a sequence to finish (arrival counter) merges the
+//            partials, runs the acceptance tests in order, finds the first
+//            rejection and writes the accepted length and emitted tokens.
+//   k_draw   sampling sequences only: one workgroup per (sequence, draw chunk)
+//            sums the draw weights of its chunk (residual max(0, p_k - q_k) or
+//            p_L); the last workgroup of the sequence picks the chunk holding
+//            u*Z, re-reads that chunk only, and finds the token with an LDS
+//            block prefix sum.
+//   k_mtp    token shift + insert and the hidden-state carry (16-byte copies).
+//
+// Determinism: every reduction has a fixed order (DPP/shuffle trees, then
+// waves in order, then chunks in order); no floating-point atomics.
+#include <cfloat>
+#include <climits>
+#include <cmath>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+// --------------------------------------------------------------- element access
+
+template <int DT> struct Elem;
+template <> struct Elem<kBF16> { using T = uint16_t; static constexpr int kVec = 8; };
+template <> struct Elem<kF32> { using T = float; static constexpr int kVec = 4; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* row, long long i) {
+    if constexpr (DT == kBF16) {
+        return __uint_as_float(((uint32_t)((const uint16_t*)row)[i]) << 16);
+    } else {
+        return ((const float*)row)[i];
+    }
+}
+
+// Widen one 16-byte vector to floats (bf16 -> binary32 is exact: the 16 bits are
+// the high half of the binary32 pattern).
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4& w, float* f) {
+    if constexpr (DT == kBF16) {
+        f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+        f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+        f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+        f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+    } else {
+        f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ const void* row_ptr(const void* base, long long row, int V) {
+    return (const char*)base + (size_t)row * (size_t)V * sizeof(typename Elem<DT>::T);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// --------------------------------------------------------------- wave / block reductions
+// Lanes within a row of 16 combine with DPP (quad_perm, half-row and row
+// mirrors); rows combine with cross-lane shuffles (xor 16, xor 32).
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+struct ArgMax {
+    float v;
+    int i;
+};
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+    // larger value wins; equal values keep the lower index
+    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ ArgMax dpp_am(ArgMax a) {
+    return ArgMax{dpp_f<CTRL>(a.v), dpp_i<CTRL>(a.i)};
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+    a = better(a, dpp_am<kDppXor1>(a));
+    a = better(a, dpp_am<kDppXor2>(a));
+    a = better(a, dpp_am<kDppHalfMirror>(a));
+    a = better(a, dpp_am<kDppMirror>(a));
+    a = better(a, ArgMax{__shfl_xor(a.v, 16, 64), __shfl_xor(a.i, 16, 64)});
+    a = better(a, ArgMax{__shfl_xor(a.v, 32, 64), __shfl_xor(a.i, 32, 64)});
+    return a;
+}
+
+// online-softmax partial: (max, sum of 2^((z - max) * c))
+struct MS {
+    float m;
+    float s;
+};
+__device__ __forceinline__ MS ms_combine(MS a, MS b, float c) {
+    float m = fmaxf(a.m, b.m);
+    float s = a.s * exp2_fast((a.m - m) * c) + b.s * exp2_fast((b.m - m) * c);
+    return MS{m, s};
+}
+template <int CTRL>
+__device__ __forceinline__ MS dpp_ms(MS a) {
+    return MS{dpp_f<CTRL>(a.m), dpp_f<CTRL>(a.s)};
+}
+__device__ __forceinline__ MS wave_ms(MS a, float c) {
+    a = ms_combine(a, dpp_ms<kDppXor1>(a), c);
+    a = ms_combine(a, dpp_ms<kDppXor2>(a), c);
+    a = ms_combine(a, dpp_ms<kDppHalfMirror>(a), c);
+    a = ms_combine(a, dpp_ms<kDppMirror>(a), c);
+    a = ms_combine(a, MS{__shfl_xor(a.m, 16, 64), __shfl_xor(a.s, 16, 64)}, c);
+    a = ms_combine(a, MS{__shfl_xor(a.m, 32, 64), __shfl_xor(a.s, 32, 64)}, c);
+    return a;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+    v = max(v, dpp_i<kDppXor1>(v));
+    v = max(v, dpp_i<kDppXor2>(v));
+    v = max(v, dpp_i<kDppHalfMirror>(v));
+    v = max(v, dpp_i<kDppMirror>(v));
+    v = max(v, __shfl_xor(v, 16, 64));
+    v = max(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// Block reductions: waves in order 0..3 combined by thread 0; the result is
+// valid in thread 0 only unless broadcast.
+__device__ ArgMax block_argmax(ArgMax a) {
+    __shared__ ArgMax sh[kWaves];
+    a = wave_argmax(a);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = a;
+    __syncthreads();
+    ArgMax r = sh[0];
+    if (threadIdx.x == 0)
+        for (int i = 1; i < kWaves; ++i) r = better(r, sh[i]);
+    return r;
+}
+__device__ MS block_ms(MS a, float c) {
+    __shared__ MS sh[kWaves];
+    a = wave_ms(a, c);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = a;
+    __syncthreads();
+    MS r = sh[0];
+    if (threadIdx.x == 0)
+        for (int i = 1; i < kWaves; ++i) r = ms_combine(r, sh[i], c);
+    return r;
+}
+// Sum broadcast to every thread.
+__device__ float block_sum_all(float v) {
+    __shared__ float sh[kWaves];
+    __shared__ float total;
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = sh[0];
+        for (int i = 1; i < kWaves; ++i) t += sh[i];
+        total = t;
+    }
+    __syncthreads();
+    return total;
+}
+__device__ int block_max_all(int v) {
+    __shared__ int sh[kWaves];
+    __shared__ int total;
+    v = wave_max_i(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = sh[0];
+        for (int i = 1; i < kWaves; ++i) t = max(t, sh[i]);
+        total = t;
+    }
+    __syncthreads();
+    return total;
+}
+
+// --------------------------------------------------------------- per-thread row work
+
+// Greedy: (max, lowest index) over elements [lo, hi) of one row.  Aligned path:
+// thread t reads vectors t, t+256, ... in ascending order and remembers the
+// first vector whose maximum beats its running maximum; the lane inside that
+// vector is resolved once at the end.
+template <int DT, bool ALIGNED>
+__device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
+    constexpr int kVec = Elem<DT>::kVec;
+    const int tid = threadIdx.x;
+    if constexpr (ALIGNED) {
+        const uint4* vrow = (const uint4*)row;
+        const int v0 = lo / kVec, v1 = hi / kVec;
+        constexpr int U = 8;
+        float best = -INFINITY;
+        int bestv = -1;
+        int v = v0 + tid;
+        for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = vrow[v + u * kThreads];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[kVec];
+                unpack<DT>(w[u], f);
+                float m = f[0];
+#pragma unroll
+                for (int e = 1; e < kVec; ++e) m = fmaxf(m, f[e]);
+                if (m > best) {
+                    best = m;
+                    bestv = v + u * kThreads;
+                }
+            }
+        }
+        for (; v < v1; v += kThreads) {
+            float f[kVec];
+            unpack<DT>(vrow[v], f);
+            float m = f[0];
+#pragma unroll
+            for (int e = 1; e < kVec; ++e) m = fmaxf(m, f[e]);
+            if (m > best) {
+                best = m;
+                bestv = v;
+            }
+        }
+        ArgMax r{best, INT_MAX};
+        if (bestv >= 0) {
+            float f[kVec];
+            unpack<DT>(vrow[bestv], f);
+            int j = kVec - 1;
+#pragma unroll
+            for (int e = kVec - 1; e >= 0; --e)
+                if (f[e] == best) j = e;
+            r.i = bestv * kVec + j;
+        } else if (v0 + tid < v1) {
+            r.i = (v0 + tid) * kVec;  // every element -inf: the lowest own index
+        }
+        return r;
+    } else {
+        ArgMax r{-INFINITY, INT_MAX};
+        for (int i = lo + tid; i < hi; i += kThreads) {
+            const float x = load_elem<DT>(row, i);
+            if (x > r.v || r.i == INT_MAX) r = ArgMax{x, i};  // first element, then strict '>'
+        }
+        return r;
+    }
+}
+
+// Sampling: online softmax partial over [lo, hi) at c = log2(e)/T.  Per group of
+// U vectors: take the group maximum, rescale the accumulators if it grew, then
+// add 2^((z - m) c) with (z - m) formed first (exact for bf16 inputs).
+template <int DT, bool ALIGNED>
+__device__ MS thread_ms(const void* row, int lo, int hi, float c) {
+    constexpr int kVec = Elem<DT>::kVec;
+    const int tid = threadIdx.x;
+    float m = -FLT_MAX;
+    float acc[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
+    if constexpr (ALIGNED) {
+        const uint4* vrow = (const uint4*)row;
+        const int v0 = lo / kVec, v1 = hi / kVec;
+        constexpr int U = 4;
+        int v = v0 + tid;
+        for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = vrow[v + u * kThreads];
+            float f[U][kVec];
+#pragma unroll
+            for (int u = 0; u < U; ++u) unpack<DT>(w[u], f[u]);
+            float gm = m;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) gm = fmaxf(gm, f[u][e]);
+            if (gm > m) {
+                const float sc = exp2_fast((m - gm) * c);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] *= sc;
+                m = gm;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] += exp2_fast((f[u][e] - m) * c);
+        }
+        for (; v < v1; v += kThreads) {
+            float f[kVec];
+            unpack<DT>(vrow[v], f);
+            float gm = m;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) gm = fmaxf(gm, f[e]);
+            if (gm > m) {
+                const float sc = exp2_fast((m - gm) * c);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] *= sc;
+                m = gm;
+            }
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] += exp2_fast((f[e] - m) * c);
+        }
+    } else {
+        for (int i = lo + tid; i < hi; i += kThreads) {
+            float x = load_elem<DT>(row, i);
+            if (x > m) {
+                acc[0] *= exp2_fast((m - x) * c);
+                m = x;
+            }
+            acc[0] += exp2_fast((x - m) * c);
+        }
+    }
+    float s = acc[0];
+#pragma unroll
+    for (int e = 1; e < kVec; ++e) s += acc[e];
+    return MS{m, s};
+}
+
+// --------------------------------------------------------------- decision helpers
+
+__device__ __forceinline__ int clamp_len(int L, int n, uint32_t& flags) {
+    if (L < 0) { flags |= SV_FLAG_LEN_CLAMPED; L = 0; }
+    if (L > n) { flags |= SV_FLAG_LEN_CLAMPED; L = n; }
+    return L;
+}
+
+__device__ __forceinline__ double sanitize_u(float uf, uint32_t& flags) {
+    double u = (double)uf;
+    if (!(u >= 0.0)) { flags |= SV_FLAG_BAD_UNIFORM; return 0.0; }
+    if (u >= 1.0) { flags |= SV_FLAG_BAD_UNIFORM; return 1.0 - 5.9604644775390625e-08; }
+    return u;
+}
+
+// log2(e) / T, kept finite so that (z - m) * c stays well defined for tiny T.
+__device__ __forceinline__ float exp2_scale(float T) {
+    float c = 1.4426950408889634f / T;
+    return fminf(c, FLT_MAX);
+}
+
+// Per-sequence settings every workgroup of a sequence derives identically.
+struct SeqInfo {
+    int L;          // effective draft length
+    float T;        // temperature (sanitised)
+    bool greedy;    // greedy rule for this sequence
+    uint32_t flags; // flags raised while deriving the above
+};
+
+template <int MODE>
+__device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
+    SeqInfo s;
+    s.flags = 0;
+    s.L = clamp_len(p.lens[b], p.n, s.flags);
+    s.T = 0.f;
+    s.greedy = true;
+    if constexpr (MODE == kSample) {
+        float T = p.temp[b];
+        if (!(T >= 0.f)) { s.flags |= SV_FLAG_BAD_TEMP; T = 0.f; }
+        s.T = T;
+        s.greedy = !(T > 0.f);
+        if (!s.greedy && p.draft == nullptr && s.L > 0) {
+            // no draft logits: nothing can be verified, plain sampling of one token
+            s.flags |= SV_FLAG_LEN_CLAMPED;
+            s.L = 0;
+        }
+    }
+    return s;
+}
+
+// The decision of sequence b, run by the last workgroup of b to finish.
+template <int DT, int MODE>
+__device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
+    __shared__ float s_m[kMaxSlots];
+    __shared__ double s_S[kMaxSlots];
+    __shared__ int s_idx[kMaxSlots];
+    __shared__ unsigned char s_acc[kMaxDraft];
+    __shared__ unsigned char s_oor[kMaxDraft];
+    __shared__ unsigned char s_badu[kMaxDraft];
+
+    const int tid = threadIdx.x;
+    const int n = p.n, V = p.V, NC = p.NC, S = p.S, L = si.L;
+    const float cf = si.greedy ? 0.f : exp2_scale(si.T);
+    const double cd = (double)cf;
+    const Partial* part = p.part + (size_t)b * S * NC;
+
+    // 1. merge the chunk partials of every row read (chunks in ascending order)
+    if (si.greedy) {
+        if (tid <= L) {
+            ArgMax r{part[(size_t)tid * NC].a, __float_as_int(part[(size_t)tid * NC].b)};
+            for (int c = 1; c < NC; ++c) {
+                const Partial q = part[(size_t)tid * NC + c];
+                r = better(r, ArgMax{q.a, __float_as_int(q.b)});
+            }
+            s_m[tid] = r.v;
+            s_idx[tid] = r.i;
+        }
+    } else {
+        const bool row_read = (tid <= L) || (tid > n && tid < S && tid - n - 1 < L);
+        if (row_read) {
+            float m = part[(size_t)tid * NC].a;
+            for (int c = 1; c < NC; ++c) m = fmaxf(m, part[(size_t)tid * NC + c].a);
+            double Ssum = 0.0;
+            for (int c = 0; c < NC; ++c) {
+                const Partial q = part[(size_t)tid * NC + c];
+                Ssum += (double)q.b * exp2((double)(q.a - m) * cd);
+            }
+            s_m[tid] = m;
+            s_S[tid] = Ssum;
+        }
+    }
+    __syncthreads();
+    // the partials of this sequence have been consumed: leave them zero
+    for (int i = tid; i < S * NC; i += kThreads) p.part[(size_t)b * S * NC + i] = Partial{0.f, 0.f};
+    if constexpr (MODE == kSample) {
+        if (p.row_lse && tid < 2 * n + 1) {
+            const bool row_read = !si.greedy && ((tid <= L) || (tid > n && tid - n - 1 < L));
+            float v = __builtin_nanf("");
+            if (row_read) v = (float)((double)s_m[tid] / (double)si.T + log(s_S[tid]));
+            p.row_lse[(size_t)b * (2 * n + 1) + tid] = v;
+        }
+    }
+    __syncthreads();
+
+    // 2. the acceptance test of every draft slot (evaluated in parallel; the
+    //    scan below uses them in order and stops at the first rejection)
+    if (tid < L) {
+        const int j = tid;
+        const int x = p.tokens[(size_t)b * n + j];
+        s_oor[j] = 0;
+        s_badu[j] = 0;
+        if (x < 0 || x >= V) {
+            s_oor[j] = 1;
+            s_acc[j] = 0;
+        } else if (si.greedy) {
+            s_acc[j] = (x == s_idx[j]);
+        } else {
+            const float zt = load_elem<DT>(row_ptr<DT>(p.target, (long long)b * (n + 1) + j, V), x);
+            const float zd = load_elem<DT>(row_ptr<DT>(p.draft, (long long)b * n + j, V), x);
+            uint32_t fl = 0;
+            const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + j], fl);
+            s_badu[j] = fl ? 1 : 0;
+            const int jd = n + 1 + j;
+            double ratio;
+            const bool pz = (zt == -INFINITY), qz = (zd == -INFINITY);
+            if (qz) ratio = pz ? 0.0 : INFINITY;
+            else if (pz) ratio = 0.0;
+            else {
+                // p/q = 2^((zt - m_t) c) / S_t  /  (2^((zd - m_d) c) / S_d)
+                const double lr = ((double)zt - (double)s_m[j]) * cd - ((double)zd - (double)s_m[jd]) * cd;
+                ratio = exp2(lr) * (s_S[jd] / s_S[j]);
+            }
+            s_acc[j] = (u < ratio) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+
+    // 3. first rejection, emitted tokens, draw descriptor
+    if (tid == 0) {
+        uint32_t flags = si.flags;
+        int k = L;
+        for (int j = 0; j < L; ++j) {
+            if (s_oor[j]) flags |= SV_FLAG_TOKEN_OOR;
+            if (s_badu[j]) flags |= SV_FLAG_BAD_UNIFORM;
+            if (!s_acc[j]) { k = j; break; }
+        }
+        int32_t* e = p.emitted + (size_t)b * (n + 1);
+        const int32_t* x = p.tokens + (size_t)b * n;
+        for (int j = 0; j < k; ++j) e[j] = x[j];
+        for (int j = k + 1; j <= n; ++j) e[j] = -1;
+        p.acc[b] = k;
+        if (si.greedy) {
+            e[k] = s_idx[k];  // the descriptor stays zero (kDrawNone)
+        } else {
+            e[k] = -1;  // written by the draw pass
+            const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + n], flags);
+            DrawDesc d;
+            d.kind = (k < L) ? kDrawResidual : kDrawBonus;
+            d.k = k;
+            d.c = cf;
+            d.m_t = s_m[k];
+            d.inv_s_t = (float)(1.0 / s_S[k]);
+            d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
+            d.inv_s_d = (k < L) ? (float)(1.0 / s_S[n + 1 + k]) : 0.f;
+            d.u = (float)u;
+            p.desc[b] = d;
+        }
+        if (flags && p.flags) atomicOr(p.flags, flags);
+        p.cnt[b] = 0u;  // leave the counter zero for the next call
+    }
+}
+
+// --------------------------------------------------------------- stats pass
+
+template <int DT, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
+    const int bid = blockIdx.x;
+    const int c = bid % p.NC;
+    const int rest = bid / p.NC;
+    const int slot = rest % p.S;
+    const int b = rest / p.S;
+    const int n = p.n;
+
+    const SeqInfo si = seq_info<MODE>(p, b);
+    const bool target_row = slot <= n;
+    const bool needed = target_row ? (slot <= si.L) : (!si.greedy && slot - n - 1 < si.L);
+    if (!needed) return;
+    const unsigned expected = (unsigned)p.NC * (unsigned)(si.L + 1 + (si.greedy ? 0 : si.L));
+
+    const void* row = target_row ? row_ptr<DT>(p.target, (long long)b * (n + 1) + slot, p.V)
+                                 : row_ptr<DT>(p.draft, (long long)b * n + (slot - n - 1), p.V);
+    const int lo = c * p.CH;
+    const int hi = min(p.V, lo + p.CH);
+
+    Partial res;
+    if (si.greedy) {
+        const ArgMax r = block_argmax(thread_argmax<DT, ALIGNED>(row, lo, hi));
+        res = Partial{r.v, __int_as_float(r.i)};
+    } else {
+        const float cf = exp2_scale(si.T);
+        const MS r = block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
+        res = Partial{r.m, r.s};
+    }
+
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+        p.part[((size_t)b * p.S + slot) * p.NC + c] = res;
+        __threadfence();
+        const unsigned prev = atomicAdd(&p.cnt[b], 1u);
+        s_last = (prev == expected - 1u);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    decide<DT, MODE>(p, b, si);
+}
+
+// --------------------------------------------------------------- draw pass
+
+// Weight of element i for the draw: p_L (bonus) or max(0, p_k - q_k) (residual).
+template <int DT>
+__device__ __forceinline__ float draw_weight(const DrawDesc& d, bool residual, float zt, float zd) {
+    const float pt = exp2_fast((zt - d.m_t) * d.c) * d.inv_s_t;
+    if (!residual) return pt;
+    const float qd = exp2_fast((zd - d.m_d) * d.c) * d.inv_s_d;
+    return fmaxf(pt - qd, 0.f);
+}
+
+// Thread t owns the kDrawPerThread contiguous elements starting at
+// lo + t * kDrawPerThread (clipped to hi).  Weights are produced in ascending
+// index order; f is called as f(index, weight).
+template <int DT, bool ALIGNED, class F>
+__device__ __forceinline__ void for_thread_weights(const DrawDesc& d, bool residual, const void* trow,
+                                                   const void* drow, int lo, int hi, F&& f) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kNV = kDrawPerThread / kVec;
+    const int i0 = lo + threadIdx.x * kDrawPerThread;
+    if constexpr (ALIGNED) {
+        const uint4* vt = (const uint4*)trow;
+        const uint4* vd = (const uint4*)drow;
+#pragma unroll
+        for (int q = 0; q < kNV; ++q) {
+            const int base = i0 + q * kVec;
+            if (base < hi) {
+                float ft[kVec], fd[kVec];
+                unpack<DT>(vt[base / kVec], ft);
+                if (residual) unpack<DT>(vd[base / kVec], fd);
+                else {
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) fd[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) f(base + e, draw_weight<DT>(d, residual, ft[e], fd[e]));
+            }
+        }
+    } else {
+        for (int e = 0; e < kDrawPerThread; ++e) {
+            const int i = i0 + e;
+            if (i < hi) {
+                const float zt = load_elem<DT>(trow, i);
+                const float zd = residual ? load_elem<DT>(drow, i) : 0.f;
+                f(i, draw_weight<DT>(d, residual, zt, zd));
+            }
+        }
+    }
+}
+
+template <int DT, bool ALIGNED>
+__device__ float thread_weight_sum(const DrawDesc& d, bool residual, const void* trow, const void* drow,
+                                   int lo, int hi) {
+    float s = 0.f;
+    for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int, float w) { s += w; });
+    return s;
+}
+
+// Inverse CDF inside one chunk: the first index whose running weight sum
+// (starting from P, the mass of the chunks before) exceeds t.  Thread sums are
+// scanned in double across the workgroup (shuffles inside a wave, then waves in
+// order); only the thread whose range crosses t walks its elements again.
+// Returns -1 if nothing in the chunk crosses t; *last_pos receives the last
+// index with positive weight.
+template <int DT, bool ALIGNED>
+__device__ int scan_chunk(const DrawDesc& d, bool residual, const void* trow, const void* drow, int lo,
+                          int hi, double P, double t, int* last_pos) {
+    __shared__ double s_wave[kWaves];
+    __shared__ int s_found;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float ts = 0.f;
+    int my_last = -1;
+    for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int i, float wgt) {
+        ts += wgt;
+        if (wgt > 0.f) my_last = i;
+    });
+    double incl = (double)ts;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wave[w] = incl;
+    if (tid == 0) s_found = INT_MAX;
+    __syncthreads();
+    double before = P;
+    for (int i = 0; i < w; ++i) before += s_wave[i];
+    const double excl = before + incl - (double)ts;
+    if (excl <= t && excl + (double)ts > t) {
+        double run = excl;
+        int hit = INT_MAX;
+        for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int i, float wgt) {
+            run += (double)wgt;
+            if (hit == INT_MAX && run > t) hit = i;
+        });
+        if (hit != INT_MAX) atomicMin(&s_found, hit);
+    }
+    *last_pos = block_max_all(my_last);
+    __syncthreads();
+    const int r = s_found;
+    return (r == INT_MAX) ? -1 : r;
+}
+
+// Chunk selection and final scan (last workgroup of a sequence).
+template <int DT, bool ALIGNED>
+__device__ void draw_select(const DrawParams& p, int b, DrawDesc d) {
+    __shared__ float s_sum[kMaxDrawChunks];
+    __shared__ int s_c;
+    __shared__ double s_P, s_t;
+    __shared__ int s_zero;
+    const int tid = threadIdx.x;
+    const int NCd = p.NCd, CHd = p.CHd, V = p.V, n = p.n;
+    const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + d.k, V);
+    const void* drow = (d.kind == kDrawResidual) ? row_ptr<DT>(p.draft, (long long)b * n + d.k, V) : nullptr;
+    bool residual = (d.kind == kDrawResidual);
+
+    for (int c = tid; c < NCd; c += kThreads) {
+        s_sum[c] = p.dpart[(size_t)b * NCd + c];
+        p.dpart[(size_t)b * NCd + c] = 0.f;  // consumed: leave it zero
+    }
+    __syncthreads();
+
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (tid == 0) {
+            double Z = 0.0;
+            for (int c = 0; c < NCd; ++c) Z += (double)s_sum[c];
+            s_zero = !(Z > 0.0);
+            const double t = (double)d.u * Z;
+            double P = 0.0;
+            int cs = -1;
+            for (int c = 0; c < NCd; ++c) {
+                if (P + (double)s_sum[c] > t) { cs = c; break; }
+                P += (double)s_sum[c];
+            }
+            if (cs < 0) {  // t at or past the total (rounding): last chunk with mass
+                P = 0.0;
+                for (int c = 0; c < NCd; ++c)
+                    if (s_sum[c] > 0.f) cs = c;
+                for (int c = 0; c < cs; ++c) P += (double)s_sum[c];
+                if (cs < 0) cs = 0;
+            }
+            s_c = cs;
+            s_P = P;
+            s_t = t;
+        }
+        __syncthreads();
+        if (s_zero && residual) {
+            // no residual mass left after rounding: draw from p_k instead
+            if (tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
+            residual = false;
+            for (int c = 0; c < NCd; ++c) {
+                const int lo = c * CHd, hi = min(V, lo + CHd);
+                const float cs = block_sum_all(thread_weight_sum<DT, ALIGNED>(d, false, trow, nullptr, lo, hi));
+                if (tid == 0) s_sum[c] = cs;
+            }
+            __syncthreads();
+            continue;
+        }
+        break;
+    }
+    const int cs = s_c;
+    const int lo = cs * CHd, hi = min(V, lo + CHd);
+    int last_pos = -1;
+    int y = scan_chunk<DT, ALIGNED>(d, residual, trow, drow, lo, hi, s_P, s_t, &last_pos);
+    if (tid == 0) {
+        if (y < 0) y = (last_pos >= 0) ? last_pos : lo;
+        p.emitted[(size_t)b * (n + 1) + d.k] = y;
+        p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        p.cnt[b] = 0u;
+    }
+}
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+    const int c = blockIdx.x % p.NCd;
+    const int b = blockIdx.x / p.NCd;
+    const DrawDesc d = p.desc[b];
+    if (d.kind == kDrawNone) return;
+    const bool residual = (d.kind == kDrawResidual);
+    const void* trow = row_ptr<DT>(p.target, (long long)b * (p.n + 1) + d.k, p.V);
+    const void* drow = residual ? row_ptr<DT>(p.draft, (long long)b * p.n + d.k, p.V) : nullptr;
+    const int lo = c * p.CHd, hi = min(p.V, lo + p.CHd);
+    const float cs = block_sum_all(thread_weight_sum<DT, ALIGNED>(d, residual, trow, drow, lo, hi));
+
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+        p.dpart[(size_t)b * p.NCd + c] = cs;
+        __threadfence();
+        const unsigned prev = atomicAdd(&p.cnt[b], 1u);
+        s_last = (prev == (unsigned)p.NCd - 1u);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    draw_select<DT, ALIGNED>(p, b, d);
+}
+
+// --------------------------------------------------------------- MTP shift / insert
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long nthreads = (long long)gridDim.x * kThreads;
+    if (gid < p.B) {
+        // tokens: left shift by one in place (ascending, so each slot is read
+        // before it is overwritten), then the target's next token at slot a
+        const int n = p.n;
+        int32_t* t = p.tokens + gid * (n + 1);
+        for (int i = 0; i < n; ++i) t[i] = t[i + 1];
+        int a = p.acc[gid];
+        a = a < 0 ? 0 : (a > n ? n : a);
+        t[a] = p.emitted[gid * (n + 1) + a];
+    }
+    if (p.hsrc == nullptr || p.hdst == nullptr || p.hsrc == p.hdst) return;
+    if constexpr (ALIGNED) {
+        // hidden carry: 16-byte vectors, 4 in flight per thread
+        const long long nvec = p.hidden_elems / 8;
+        const uint4* src = (const uint4*)p.hsrc;
+        uint4* dst = (uint4*)p.hdst;
+        long long v = gid;
+        for (; v + 3 * nthreads < nvec; v += 4 * nthreads) {
+            const uint4 w0 = src[v], w1 = src[v + nthreads];
+            const uint4 w2 = src[v + 2 * nthreads], w3 = src[v + 3 * nthreads];
+            dst[v] = w0;
+            dst[v + nthreads] = w1;
+            dst[v + 2 * nthreads] = w2;
+            dst[v + 3 * nthreads] = w3;
+        }
+        for (; v < nvec; v += nthreads) dst[v] = src[v];
+        // tail elements past the last full vector
+        const long long tail0 = nvec * 8;
+        const uint16_t* s16 = (const uint16_t*)p.hsrc;
+        uint16_t* d16 = (uint16_t*)p.hdst;
+        for (long long i = tail0 + gid; i < p.hidden_elems; i += nthreads) d16[i] = s16[i];
+    } else {
+        const uint16_t* s16 = (const uint16_t*)p.hsrc;
+        uint16_t* d16 = (uint16_t*)p.hdst;
+        for (long long i = gid; i < p.hidden_elems; i += nthreads) d16[i] = s16[i];
+    }
+}
+
+// --------------------------------------------------------------- workspace clear
+
+__global__ __launch_bounds__(kThreads) void k_clear(uint4* ws, long long nvec, uint8_t* tail, int ntail) {
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long nthreads = (long long)gridDim.x * kThreads;
+    for (long long v = gid; v < nvec; v += nthreads) ws[v] = make_uint4(0, 0, 0, 0);
+    if (gid < ntail) tail[gid] = 0;
+}
+
+// --------------------------------------------------------------- debug softmax
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, const float* temp, int V,
+                                                            float* out) {
+    const int r = blockIdx.x;
+    const float T = temp[r];
+    const void* row = row_ptr<DT>(logits, r, V);
+    float* o = out + (size_t)r * V;
+    if (!(T > 0.f)) {
+        for (int i = threadIdx.x; i < V; i += kThreads) o[i] = __builtin_nanf("");
+        return;
+    }
+    const float c = exp2_scale(T);
+    __shared__ MS s_ms;
+    const MS ms = block_ms(thread_ms<DT, ALIGNED>(row, 0, V, c), c);
+    if (threadIdx.x == 0) s_ms = ms;
+    __syncthreads();
+    const float m = s_ms.m;
+    const float inv_s = (float)(1.0 / (double)s_ms.s);
+    for (int i = threadIdx.x; i < V; i += kThreads) o[i] = exp2_fast((load_elem<DT>(row, i) - m) * c) * inv_s;
+}
+
+// --------------------------------------------------------------- launches
+
+hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.S * p.NC);
+    const dim3 grid(blocks), block(kThreads);
+#define SV_STATS(DT_, MODE_, AL_) hipLaunchKernelGGL((k_stats<DT_, MODE_, AL_>), grid, block, 0, s, p)
+    if (dt == kBF16) {
+        if (mode == kSample) { if (aligned) SV_STATS(kBF16, kSample, true); else SV_STATS(kBF16, kSample, false); }
+        else { if (aligned) SV_STATS(kBF16, kGreedy, true); else SV_STATS(kBF16, kGreedy, false); }
+    } else {
+        if (mode == kSample) { if (aligned) SV_STATS(kF32, kSample, true); else SV_STATS(kF32, kSample, false); }
+        else { if (aligned) SV_STATS(kF32, kGreedy, true); else SV_STATS(kF32, kGreedy, false); }
+    }
+#undef SV_STATS
+    return hipGetLastError();
+}
+
+hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.NCd);
+    const dim3 grid(blocks), block(kThreads);
+    if (dt == kBF16) {
+        if (aligned) hipLaunchKernelGGL((k_draw<kBF16, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_draw<kBF16, false>), grid, block, 0, s, p);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_draw<kF32, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_draw<kF32, false>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s) {
+    const long long work_tok = p.B;
+    const long long work_hid = (p.hsrc && p.hdst && p.hsrc != p.hdst) ? (p.hidden_elems / 8 + 3) / 4 : 0;
+    long long threads = work_tok > work_hid ? work_tok : work_hid;
+    long long blocks = (threads + kThreads - 1) / kThreads;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65536) blocks = 65536;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (aligned) hipLaunchKernelGGL((k_mtp<true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_mtp<false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s) {
+    const long long nvec = (long long)(bytes / 16);
+    const int ntail = (int)(bytes % 16);
+    long long blocks = (nvec + kThreads - 1) / kThreads;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(kThreads), 0, s, (uint4*)ws, nvec,
+                       (uint8_t*)ws + nvec * 16, ntail);
+    return hipGetLastError();
+}
+
+hipError_t launch_softmax_debug(const void* logits, Dt dt, const float* temp, int rows, int V, float* out,
+                                bool aligned, hipStream_t s) {
+    const dim3 grid((unsigned)rows), block(kThreads);
+    if (dt == kBF16) {
+        if (aligned) hipLaunchKernelGGL((k_softmax_debug<kBF16, true>), grid, block, 0, s, logits, temp, V, out);
+        else hipLaunchKernelGGL((k_softmax_debug<kBF16, false>), grid, block, 0, s, logits, temp, V, out);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_softmax_debug<kF32, true>), grid, block, 0, s, logits, temp, V, out);
+        else hipLaunchKernelGGL((k_softmax_debug<kF32, false>), grid, block, 0, s, logits, temp, V, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+public header declares, and rejects host-checkable bad arguments synchronously
+(these paths return before any HIP call)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import draft_token_verification_08_amd as sv
+from draft_token_verification_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ["spec_verify_sample", "spec_verify_greedy", "mtp_shift_insert", "sv_workspace_bytes",
+              "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug"]:
+        assert f in names, names
+
+
+def test_library_exports_every_declared_function():
+    L = sv.lib()
+    missing = [f for f in declared_functions() if not hasattr(L, f)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    L = sv.lib()
+    for code in range(5):
+        s = L.sv_status_string(code).decode()
+        assert s.startswith("SV_")
+    assert L.sv_last_hip_error().decode() == ""
+
+
+def test_workspace_bytes():
+    assert sv.sv_workspace_bytes(0, 4, 100, sv.SV_BF16) >= 256
+    assert sv.sv_workspace_bytes(-1, 4, 100, sv.SV_BF16) == 0
+    assert sv.sv_workspace_bytes(4, sv.SV_MAX_DRAFT + 1, 100, sv.SV_BF16) == 0
+    assert sv.sv_workspace_bytes(4, 4, 0, sv.SV_BF16) == 0
+    assert sv.sv_workspace_bytes(4, 4, 100, 7) == 0
+    a = sv.sv_workspace_bytes(256, 4, 128256, sv.SV_BF16)
+    b = sv.sv_workspace_bytes(1024, 8, 152064, sv.SV_BF16)
+    assert 0 < a < b < 64 << 20
+    assert a % 256 == 0 and b % 256 == 0
+
+
+NULL = None
+
+
+def _sample(**kw):
+    args = dict(t=C.c_void_p(16), d=C.c_void_p(16), dt=sv.SV_BF16, x=C.c_void_p(16), L=C.c_void_p(16),
+                T=C.c_void_p(16), u=C.c_void_p(16), B=4, n=4, V=1024, acc=C.c_void_p(16),
+                emi=C.c_void_p(16), lse=NULL, fl=NULL, ws=C.c_void_p(256), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_sample(*args.values())
+
+
+def test_sample_host_checks():
+    assert _sample(B=0) == sv.SV_OK                       # no-op, nothing touched
+    assert _sample(B=-1) == sv.SV_EINVAL
+    assert _sample(n=-1) == sv.SV_EINVAL
+    assert _sample(n=sv.SV_MAX_DRAFT + 1) == sv.SV_EINVAL
+    assert _sample(V=0) == sv.SV_EINVAL
+    assert _sample(dt=5) == sv.SV_EINVAL
+    assert _sample(t=NULL) == sv.SV_EINVAL
+    assert _sample(x=NULL) == sv.SV_EINVAL
+    assert _sample(L=NULL) == sv.SV_EINVAL
+    assert _sample(T=NULL) == sv.SV_EINVAL
+    assert _sample(u=NULL) == sv.SV_EINVAL
+    assert _sample(acc=NULL) == sv.SV_EINVAL
+    assert _sample(emi=NULL) == sv.SV_EINVAL
+    assert _sample(t=C.c_void_p(17)) == sv.SV_EALIGN
+    assert _sample(acc=C.c_void_p(18)) == sv.SV_EALIGN
+    assert _sample(ws=NULL) == sv.SV_EWORKSPACE
+    assert _sample(wsb=16) == sv.SV_EWORKSPACE
+    assert _sample(ws=C.c_void_p(264)) == sv.SV_EALIGN
+
+
+def _greedy(**kw):
+    args = dict(t=C.c_void_p(16), dt=sv.SV_F32, x=C.c_void_p(16), L=C.c_void_p(16), B=4, n=4, V=1024,
+                acc=C.c_void_p(16), emi=C.c_void_p(16), fl=NULL, ws=C.c_void_p(256), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_greedy(*args.values())
+
+
+def test_greedy_host_checks():
+    assert _greedy(B=0) == sv.SV_OK
+    assert _greedy(B=-3) == sv.SV_EINVAL
+    assert _greedy(t=NULL) == sv.SV_EINVAL
+    assert _greedy(x=NULL) == sv.SV_EINVAL
+    assert _greedy(t=C.c_void_p(18)) == sv.SV_EALIGN
+    assert _greedy(wsb=0) == sv.SV_EWORKSPACE
+
+
+def test_mtp_host_checks():
+    f = sv.lib().mtp_shift_insert
+    p = C.c_void_p(16)
+    assert f(p, NULL, NULL, 0, p, p, 0, 4, NULL) == sv.SV_OK
+    assert f(p, NULL, NULL, 0, p, p, -1, 4, NULL) == sv.SV_EINVAL
+    assert f(NULL, NULL, NULL, 0, p, p, 4, 4, NULL) == sv.SV_EINVAL
+    assert f(p, p, NULL, 8, p, p, 4, 4, NULL) == sv.SV_EINVAL         # one hidden pointer only
+    assert f(p, p, p, 0, p, p, 4, 4, NULL) == sv.SV_EINVAL            # hidden without H
+    assert f(C.c_void_p(18), NULL, NULL, 0, p, p, 4, 4, NULL) == sv.SV_EALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libspecverify.so not found"):
+        _lib.lib()
