@@ -101,18 +101,22 @@ def main():
     wsbuf = ws.get(sv.sv_workspace_bytes(cfg.B, cfg.n, cfg.V, sv.SV_BF16 if es == 2 else sv.SV_F32))
     stream = torch.cuda.current_stream(dev)
 
-    def verify(d):
+    # calls marshalled once per input copy (the C entry points are re-issued as is)
+    for d in data:
         if greedy:
-            sv.spec_verify_greedy(d["target"], d["draft_tokens"], d["draft_lens"], accepted_len=d["acc"],
-                                  emitted=d["emi"], workspace=wsbuf)
+            d["verify"] = sv.prepare_spec_verify_greedy(d["target"], d["draft_tokens"], d["draft_lens"], d["acc"],
+                                                        d["emi"], wsbuf)
         else:
-            sv.spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
-                                  d["temperature"], d["uniforms"], accepted_len=d["acc"], emitted=d["emi"],
-                                  workspace=wsbuf)
+            d["verify"] = sv.prepare_spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                                        d["temperature"], d["uniforms"], d["acc"], d["emi"], wsbuf)
+        d["mtp"] = (sv.prepare_mtp_shift_insert(d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+                    if cfg.H else (lambda: None))
+
+    def verify(d):
+        d["verify"]()
 
     def mtp(d):
-        if cfg.H:
-            sv.mtp_shift_insert(d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+        d["mtp"]()
 
     # algorithmic bytes per step (each required row counted once)
     lens = [d["draft_lens"].clamp(0, cfg.n).to(torch.int64) for d in data]

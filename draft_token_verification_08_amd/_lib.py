@@ -238,3 +238,80 @@ def sv_softmax_rows_debug(logits, temperature, *, probs_out=None, stream=None):
     _call("sv_softmax_rows_debug", _ptr(logits), _dt(logits), _ptr(temperature), rows, V, _ptr(probs_out),
           _stream(stream, dev))
     return probs_out
+
+
+# ------------------------------------------------------------------ prepared calls
+
+class Prepared:
+    """A C entry point with its arguments marshalled once (same tensors every
+    call, e.g. in a serving loop or a benchmark); calling it re-issues the C call
+    on the stream that was current when it was prepared."""
+
+    def __init__(self, fn: str, args: tuple, keep: tuple):
+        self._f = getattr(lib(), fn)
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # tensors whose storage the pointers refer to
+
+    def __call__(self):
+        st = self._f(*self._args)
+        if st != SV_OK:
+            raise SpecVerifyError(self._fn, st)
+
+
+def prepare_spec_verify_greedy(target_logits, draft_tokens, draft_lens, accepted_len, emitted, workspace,
+                               err_flags=None, stream=None) -> Prepared:
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    args = (_ptr(target_logits), _dt(target_logits), _ptr(draft_tokens), _ptr(draft_lens), B, n, V,
+            _ptr(accepted_len), _ptr(emitted), _ptr(err_flags), _ptr(workspace), workspace.numel(),
+            _stream(stream, dev))
+    return Prepared("spec_verify_greedy", args, (target_logits, draft_tokens, draft_lens, accepted_len,
+                                                  emitted, workspace, err_flags))
+
+
+def prepare_spec_verify_sample(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms,
+                               accepted_len, emitted, workspace, row_lse=None, err_flags=None,
+                               stream=None) -> Prepared:
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    args = (_ptr(target_logits), _ptr(draft_logits), _dt(target_logits), _ptr(draft_tokens), _ptr(draft_lens),
+            _ptr(temperature), _ptr(uniforms), B, n, V, _ptr(accepted_len), _ptr(emitted), _ptr(row_lse),
+            _ptr(err_flags), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return Prepared("spec_verify_sample", args, (target_logits, draft_logits, draft_tokens, draft_lens,
+                                                  temperature, uniforms, accepted_len, emitted, workspace,
+                                                  row_lse, err_flags))
+
+
+def prepare_mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitted, stream=None) -> Prepared:
+    B, n1 = tokens.shape
+    dev = tokens.device
+    _check(tokens, "tokens", torch.int32, None, dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    H = 0
+    if hidden_src is not None:
+        H = hidden_src.shape[-1]
+        _check(hidden_src, "hidden_src", torch.bfloat16, (B, n1, H), dev)
+        _check(hidden_dst, "hidden_dst", torch.bfloat16, (B, n1, H), dev)
+    args = (_ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(accepted_len), _ptr(emitted), B, n1 - 1,
+            _stream(stream, dev))
+    return Prepared("mtp_shift_insert", args, (tokens, hidden_src, hidden_dst, accepted_len, emitted))

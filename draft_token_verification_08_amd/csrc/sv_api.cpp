@@ -39,6 +39,8 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     long long nc = rows_t > 0 ? ceil_div(sv::kTargetWorkgroups, rows_t) : 1;
     const long long nc_max = ceil_div(V, tile);
     if (nc > nc_max) nc = nc_max;
+    const long long nc_lds = sv::kMaxPartials / (2 * n + 1);  // partials staged in LDS by the decision
+    if (nc > nc_lds) nc = nc_lds;
     if (nc < 1) nc = 1;
     long long ch = ceil_div(ceil_div(V, nc), tile) * tile;
     nc = ceil_div(V, ch);

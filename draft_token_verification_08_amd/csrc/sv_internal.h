@@ -18,6 +18,7 @@ constexpr int kMaxSlots = 2 * kMaxDraft + 1;
 constexpr int kDrawPerThread = 16;   // draw pass: contiguous elements per thread
 constexpr int kMaxDrawChunks = 1024; // LDS bound of the draw selection
 constexpr int kTargetWorkgroups = 2048;  // stats pass: aim for ~8 workgroups per CU
+constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
@@ -25,9 +26,9 @@ enum Mode : int { kSample = 0, kGreedy = 1 };
 // kinds of the final draw of a sequence
 enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
 
-// One per (sequence, row slot, vocab chunk): the chunk's reduction.
-//   sampling rows: a = chunk max m_c, b = sum over the chunk of 2^((z - m_c) c)
-//   greedy rows:   a = chunk max value, b = bit pattern of the lowest index of it
+// One 64-bit slot per (sequence, row slot, vocab chunk), exchanged atomically:
+//   sampling rows: low word chunk max m_c, high word sum over the chunk of 2^((z - m_c) c)
+//   greedy rows:   chunk slot 0 holds the row's argmax key (atomic max over chunks)
 struct Partial {
     float a;
     float b;

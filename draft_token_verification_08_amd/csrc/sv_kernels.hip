@@ -72,6 +72,35 @@ __device__ __forceinline__ const void* row_ptr(const void* base, long long row, 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// --------------------------------------------------------------- cross-workgroup exchange
+// Workgroups of one sequence hand their partial results to the last one to
+// finish through device-scope atomic read-modify-writes only: the writer's data
+// atomic returns before its arrival on the counter is performed, and the last
+// workgroup reads (and resets to zero) the data with atomic exchanges.  No
+// L2 writeback/invalidate fences are needed on the streaming workgroups.
+
+__device__ __forceinline__ unsigned long long xchg64(unsigned long long* p, unsigned long long v) {
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned xchg32(unsigned* p, unsigned v) {
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long max64(unsigned long long* p, unsigned long long v) {
+    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Arrive on a counter after the data atomic whose returned value is `dep` has
+// completed; returns the counter value before this arrival.
+__device__ __forceinline__ unsigned arrive(unsigned* cnt, unsigned long long dep) {
+    asm volatile("" ::"v"((unsigned)dep), "v"((unsigned)(dep >> 32)));
+    __builtin_amdgcn_s_waitcnt(0);
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long pack2(float a, float b) {
+    return ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
+}
+__device__ __forceinline__ float lo_f(unsigned long long v) { return __uint_as_float((unsigned)v); }
+__device__ __forceinline__ float hi_f(unsigned long long v) { return __uint_as_float((unsigned)(v >> 32)); }
+
 // --------------------------------------------------------------- wave / block reductions
 // Lanes within a row of 16 combine with DPP (quad_perm, half-row and row
 // mirrors); rows combine with cross-lane shuffles (xor 16, xor 32).
@@ -96,6 +125,20 @@ struct ArgMax {
 __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
     // larger value wins; equal values keep the lower index
     return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+// 64-bit key whose unsigned order is the argmax order: order-preserving map of
+// the float in the high word, the inverted index in the low word (equal values:
+// the lower index has the larger key).  Zero is below every key of a number.
+__device__ __forceinline__ unsigned long long argmax_key(ArgMax a) {
+    unsigned u = __float_as_uint(a.v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (unsigned)a.i);
+}
+__device__ __forceinline__ ArgMax argmax_unkey(unsigned long long k) {
+    unsigned u = (unsigned)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return ArgMax{__uint_as_float(u), (int)(0xFFFFFFFFu - (unsigned)k)};
 }
 
 template <int CTRL>
@@ -414,36 +457,40 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     const int n = p.n, V = p.V, NC = p.NC, S = p.S, L = si.L;
     const float cf = si.greedy ? 0.f : exp2_scale(si.T);
     const double cd = (double)cf;
-    const Partial* part = p.part + (size_t)b * S * NC;
+    unsigned long long* part = reinterpret_cast<unsigned long long*>(p.part) + (size_t)b * S * NC;
+    __shared__ unsigned long long s_part[kMaxPartials];
 
-    // 1. merge the chunk partials of every row read (chunks in ascending order)
-    if (si.greedy) {
+    // 1. collect (and reset to zero) the partials of every row read, then merge
+    //    them per row in ascending chunk order
+    if (MODE == kGreedy || si.greedy) {
+        // one argmax key per row (chunk slot 0), already merged by atomic max
         if (tid <= L) {
-            ArgMax r{part[(size_t)tid * NC].a, __float_as_int(part[(size_t)tid * NC].b)};
-            for (int c = 1; c < NC; ++c) {
-                const Partial q = part[(size_t)tid * NC + c];
-                r = better(r, ArgMax{q.a, __float_as_int(q.b)});
-            }
+            const ArgMax r = argmax_unkey(xchg64(part + (size_t)tid * NC, 0ull));
             s_m[tid] = r.v;
             s_idx[tid] = r.i;
         }
     } else {
+        for (int i = tid; i < S * NC; i += kThreads) s_part[i] = xchg64(part + i, 0ull);
+        __syncthreads();
         const bool row_read = (tid <= L) || (tid > n && tid < S && tid - n - 1 < L);
         if (row_read) {
-            float m = part[(size_t)tid * NC].a;
-            for (int c = 1; c < NC; ++c) m = fmaxf(m, part[(size_t)tid * NC + c].a);
+            // online merge in double: running max, rescaled sum
+            float m = -FLT_MAX;
             double Ssum = 0.0;
             for (int c = 0; c < NC; ++c) {
-                const Partial q = part[(size_t)tid * NC + c];
-                Ssum += (double)q.b * exp2((double)(q.a - m) * cd);
+                const unsigned long long q = s_part[tid * NC + c];
+                const float mc = lo_f(q), sc = hi_f(q);
+                if (mc > m) {
+                    Ssum *= exp2((double)(m - mc) * cd);
+                    m = mc;
+                }
+                Ssum += (double)sc * exp2((double)(mc - m) * cd);
             }
             s_m[tid] = m;
             s_S[tid] = Ssum;
         }
     }
     __syncthreads();
-    // the partials of this sequence have been consumed: leave them zero
-    for (int i = tid; i < S * NC; i += kThreads) p.part[(size_t)b * S * NC + i] = Partial{0.f, 0.f};
     if constexpr (MODE == kSample) {
         if (p.row_lse && tid < 2 * n + 1) {
             const bool row_read = !si.greedy && ((tid <= L) || (tid > n && tid - n - 1 < L));
@@ -518,7 +565,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             p.desc[b] = d;
         }
         if (flags && p.flags) atomicOr(p.flags, flags);
-        p.cnt[b] = 0u;  // leave the counter zero for the next call
+        xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
     }
 }
 
@@ -544,26 +591,25 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     const int lo = c * p.CH;
     const int hi = min(p.V, lo + p.CH);
 
-    Partial res;
+    unsigned long long* slot_part =
+        reinterpret_cast<unsigned long long*>(p.part) + ((size_t)b * p.S + slot) * p.NC;
+    __shared__ int s_last;
     if (si.greedy) {
         const ArgMax r = block_argmax(thread_argmax<DT, ALIGNED>(row, lo, hi));
-        res = Partial{r.v, __int_as_float(r.i)};
+        if (threadIdx.x == 0) {
+            const unsigned long long dep = max64(slot_part, argmax_key(r));  // merged across chunks
+            s_last = (arrive(&p.cnt[b], dep) == expected - 1u);
+        }
     } else {
         const float cf = exp2_scale(si.T);
         const MS r = block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
-        res = Partial{r.m, r.s};
-    }
-
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-        p.part[((size_t)b * p.S + slot) * p.NC + c] = res;
-        __threadfence();
-        const unsigned prev = atomicAdd(&p.cnt[b], 1u);
-        s_last = (prev == expected - 1u);
+        if (threadIdx.x == 0) {
+            const unsigned long long dep = xchg64(slot_part + c, pack2(r.m, r.s));
+            s_last = (arrive(&p.cnt[b], dep) == expected - 1u);
+        }
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     decide<DT, MODE>(p, b, si);
 }
 
@@ -683,10 +729,8 @@ __device__ void draw_select(const DrawParams& p, int b, DrawDesc d) {
     const void* drow = (d.kind == kDrawResidual) ? row_ptr<DT>(p.draft, (long long)b * n + d.k, V) : nullptr;
     bool residual = (d.kind == kDrawResidual);
 
-    for (int c = tid; c < NCd; c += kThreads) {
-        s_sum[c] = p.dpart[(size_t)b * NCd + c];
-        p.dpart[(size_t)b * NCd + c] = 0.f;  // consumed: leave it zero
-    }
+    unsigned* dpart = reinterpret_cast<unsigned*>(p.dpart) + (size_t)b * NCd;
+    for (int c = tid; c < NCd; c += kThreads) s_sum[c] = __uint_as_float(xchg32(dpart + c, 0u));
     __syncthreads();
 
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -735,7 +779,7 @@ __device__ void draw_select(const DrawParams& p, int b, DrawDesc d) {
         if (y < 0) y = (last_pos >= 0) ? last_pos : lo;
         p.emitted[(size_t)b * (n + 1) + d.k] = y;
         p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        p.cnt[b] = 0u;
+        xchg32(&p.cnt[b], 0u);
     }
 }
 
@@ -753,14 +797,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 
     __shared__ int s_last;
     if (threadIdx.x == 0) {
-        p.dpart[(size_t)b * p.NCd + c] = cs;
-        __threadfence();
-        const unsigned prev = atomicAdd(&p.cnt[b], 1u);
-        s_last = (prev == (unsigned)p.NCd - 1u);
+        const unsigned dep = xchg32(reinterpret_cast<unsigned*>(p.dpart) + (size_t)b * p.NCd + c,
+                                    __float_as_uint(cs));
+        s_last = (arrive(&p.cnt[b], dep) == (unsigned)p.NCd - 1u);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     draw_select<DT, ALIGNED>(p, b, d);
 }
 
