@@ -35,15 +35,17 @@ def _run(cmd):
     return out
 
 
-def build(out: str = LIB, verbose: bool = False) -> str:
-    objdir = os.path.join(HERE, "_build")
+def build(out: str = LIB, verbose: bool = False, defines=(), objdir: str | None = None) -> str:
+    """Compile and link; `defines` are extra -D tuning flags (e.g. SV_ARGMAX_UNROLL=16)."""
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     k_obj = os.path.join(objdir, "sv_kernels.o")
     a_obj = os.path.join(objdir, "sv_api.o")
     logs = []
-    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, "-x", "hip", "-c",
+    dflags = [f"-D{d}" for d in defines]
+    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
                       os.path.join(CSRC, "sv_kernels.hip"), "-o", k_obj]))
-    logs.append(_run([HIPCC, *COMMON, "-c", os.path.join(CSRC, "sv_api.cpp"), "-o", a_obj]))
+    logs.append(_run([HIPCC, *COMMON, *dflags, "-c", os.path.join(CSRC, "sv_api.cpp"), "-o", a_obj]))
     tmp = out + ".tmp"
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp]))
     os.replace(tmp, out)

@@ -11,13 +11,21 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;        // workgroup size of every kernel (4 wave64s)
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef SV_THREADS
+#define SV_THREADS 256
+#endif
+#ifndef SV_TARGET_WORKGROUPS
+#define SV_TARGET_WORKGROUPS 1024
+#endif
+
+constexpr int kThreads = SV_THREADS; // workgroup size of every kernel (wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDraft = 64;        // n <= kMaxDraft
 constexpr int kMaxSlots = 2 * kMaxDraft + 1;
 constexpr int kDrawPerThread = 16;   // draw pass: contiguous elements per thread
 constexpr int kMaxDrawChunks = 1024; // LDS bound of the draw selection
-constexpr int kTargetWorkgroups = 2048;  // stats pass: aim for ~8 workgroups per CU
+constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };

@@ -30,9 +30,36 @@
 
 #include "sv_internal.h"
 
+#ifndef SV_ARGMAX_UNROLL
+#define SV_ARGMAX_UNROLL 4
+#endif
+#ifndef SV_MS_UNROLL
+#define SV_MS_UNROLL 4
+#endif
+#ifndef SV_NT_LOAD
+#define SV_NT_LOAD 1
+#endif
+#ifndef SV_NT_COPY
+#define SV_NT_COPY 0
+#endif
+#ifndef SV_COPY_VECS
+#define SV_COPY_VECS 8  // 16-byte vectors per thread in the hidden-state copy
+#endif
+
 namespace sv {
 
 // --------------------------------------------------------------- element access
+
+// one 16-byte load of streamed logits (read once: optionally non-temporal)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const uint4* p) {
+#if SV_NT_LOAD
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
+}
 
 template <int DT> struct Elem;
 template <> struct Elem<kBF16> { using T = uint16_t; static constexpr int kVec = 8; };
@@ -258,9 +285,10 @@ __device__ int block_max_all(int v) {
 // --------------------------------------------------------------- per-thread row work
 
 // Greedy: (max, lowest index) over elements [lo, hi) of one row.  Aligned path:
-// thread t reads vectors t, t+256, ... in ascending order and remembers the
-// first vector whose maximum beats its running maximum; the lane inside that
-// vector is resolved once at the end.
+// thread t reads vectors t, t+256, ... in ascending order and keeps the first
+// vector whose maximum beats its running maximum (index and contents, in
+// registers: the streamed lines are not cached, so nothing is re-read); the lane
+// inside that vector is resolved once at the end.
 template <int DT, bool ALIGNED>
 __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
     constexpr int kVec = Elem<DT>::kVec;
@@ -268,14 +296,15 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
     if constexpr (ALIGNED) {
         const uint4* vrow = (const uint4*)row;
         const int v0 = lo / kVec, v1 = hi / kVec;
-        constexpr int U = 8;
+        constexpr int U = SV_ARGMAX_UNROLL;
         float best = -INFINITY;
         int bestv = -1;
+        uint4 bestw = make_uint4(0, 0, 0, 0);
         int v = v0 + tid;
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = vrow[v + u * kThreads];
+            for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float f[kVec];
@@ -286,24 +315,27 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
                 if (m > best) {
                     best = m;
                     bestv = v + u * kThreads;
+                    bestw = w[u];
                 }
             }
         }
         for (; v < v1; v += kThreads) {
+            const uint4 w = ld16(vrow + v);
             float f[kVec];
-            unpack<DT>(vrow[v], f);
+            unpack<DT>(w, f);
             float m = f[0];
 #pragma unroll
             for (int e = 1; e < kVec; ++e) m = fmaxf(m, f[e]);
             if (m > best) {
                 best = m;
                 bestv = v;
+                bestw = w;
             }
         }
         ArgMax r{best, INT_MAX};
         if (bestv >= 0) {
             float f[kVec];
-            unpack<DT>(vrow[bestv], f);
+            unpack<DT>(bestw, f);
             int j = kVec - 1;
 #pragma unroll
             for (int e = kVec - 1; e >= 0; --e)
@@ -337,12 +369,12 @@ __device__ MS thread_ms(const void* row, int lo, int hi, float c) {
     if constexpr (ALIGNED) {
         const uint4* vrow = (const uint4*)row;
         const int v0 = lo / kVec, v1 = hi / kVec;
-        constexpr int U = 4;
+        constexpr int U = SV_MS_UNROLL;
         int v = v0 + tid;
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = vrow[v + u * kThreads];
+            for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
             float f[U][kVec];
 #pragma unroll
             for (int u = 0; u < U; ++u) unpack<DT>(w[u], f[u]);
@@ -364,7 +396,7 @@ __device__ MS thread_ms(const void* row, int lo, int hi, float c) {
         }
         for (; v < v1; v += kThreads) {
             float f[kVec];
-            unpack<DT>(vrow[v], f);
+            unpack<DT>(ld16(vrow + v), f);
             float gm = m;
 #pragma unroll
             for (int e = 0; e < kVec; ++e) gm = fmaxf(gm, f[e]);
@@ -808,6 +840,21 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 
 // --------------------------------------------------------------- MTP shift / insert
 
+__device__ __forceinline__ u32x4 ld_copy(const u32x4* p) {
+#if SV_NT_COPY
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ void st_copy(u32x4* p, u32x4 v) {
+#if SV_NT_COPY
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 template <bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -824,20 +871,26 @@ __global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
     }
     if (p.hsrc == nullptr || p.hdst == nullptr || p.hsrc == p.hdst) return;
     if constexpr (ALIGNED) {
-        // hidden carry: 16-byte vectors, 4 in flight per thread
+        // hidden carry: each workgroup copies one contiguous region of
+        // kThreads * SV_COPY_VECS 16-byte vectors, 4 loads in flight per thread
         const long long nvec = p.hidden_elems / 8;
-        const uint4* src = (const uint4*)p.hsrc;
-        uint4* dst = (uint4*)p.hdst;
-        long long v = gid;
-        for (; v + 3 * nthreads < nvec; v += 4 * nthreads) {
-            const uint4 w0 = src[v], w1 = src[v + nthreads];
-            const uint4 w2 = src[v + 2 * nthreads], w3 = src[v + 3 * nthreads];
-            dst[v] = w0;
-            dst[v + nthreads] = w1;
-            dst[v + 2 * nthreads] = w2;
-            dst[v + 3 * nthreads] = w3;
+        const u32x4* src = (const u32x4*)p.hsrc;
+        u32x4* dst = (u32x4*)p.hdst;
+        constexpr int kPer = kThreads * SV_COPY_VECS;
+        for (long long base = (long long)blockIdx.x * kPer; base < nvec; base += (long long)gridDim.x * kPer) {
+            long long v = base + threadIdx.x;
+            const long long end = (base + kPer < nvec) ? base + kPer : nvec;
+#pragma unroll 1
+            for (; v + 3 * kThreads < end; v += 4 * kThreads) {
+                const u32x4 w0 = ld_copy(src + v), w1 = ld_copy(src + v + kThreads);
+                const u32x4 w2 = ld_copy(src + v + 2 * kThreads), w3 = ld_copy(src + v + 3 * kThreads);
+                st_copy(dst + v, w0);
+                st_copy(dst + v + kThreads, w1);
+                st_copy(dst + v + 2 * kThreads, w2);
+                st_copy(dst + v + 3 * kThreads, w3);
+            }
+            for (; v < end; v += kThreads) st_copy(dst + v, ld_copy(src + v));
         }
-        for (; v < nvec; v += nthreads) dst[v] = src[v];
         // tail elements past the last full vector
         const long long tail0 = nvec * 8;
         const uint16_t* s16 = (const uint16_t*)p.hsrc;
@@ -914,9 +967,12 @@ hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s) 
 
 hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s) {
     const long long work_tok = p.B;
-    const long long work_hid = (p.hsrc && p.hdst && p.hsrc != p.hdst) ? (p.hidden_elems / 8 + 3) / 4 : 0;
-    long long threads = work_tok > work_hid ? work_tok : work_hid;
-    long long blocks = (threads + kThreads - 1) / kThreads;
+    const long long copy_blocks = (p.hsrc && p.hdst && p.hsrc != p.hdst)
+                                      ? (p.hidden_elems / 8 + (long long)kThreads * SV_COPY_VECS - 1) /
+                                            ((long long)kThreads * SV_COPY_VECS)
+                                      : 0;
+    const long long tok_blocks = (work_tok + kThreads - 1) / kThreads;
+    long long blocks = copy_blocks > tok_blocks ? copy_blocks : tok_blocks;
     if (blocks < 1) blocks = 1;
     if (blocks > 65536) blocks = 65536;
     const dim3 grid((unsigned)blocks), block(kThreads);
