@@ -32,7 +32,7 @@ bool valid_sizes(int B, int n, int V) {
 // sample and greedy entry points agree with sv_workspace_bytes().
 //   stats pass: enough chunks that ~kTargetWorkgroups workgroups cover the
 //     B*(n+1) target rows; chunk length a multiple of one vector per thread.
-//   draw pass: fixed chunks of kThreads * kDrawPerThread elements.
+//   draw pass: tiles of kThreads * (elements per 16-byte vector), kDrawTiles per chunk.
 bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     const long long tile = (long long)sv::kThreads * vec_elems(dt);
     const long long rows_t = (long long)B * (n + 1);
@@ -44,13 +44,13 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     if (nc < 1) nc = 1;
     long long ch = ceil_div(ceil_div(V, nc), tile) * tile;
     nc = ceil_div(V, ch);
-    const long long chd = (long long)sv::kThreads * sv::kDrawPerThread;
-    const long long ncd = ceil_div(V, chd);
-    if (ncd > sv::kMaxDrawChunks) return false;
+    const long long nt = ceil_div(V, tile);
+    const long long ncd = ceil_div(nt, sv::kDrawTiles);
+    if (nt > sv::kMaxTiles) return false;
     L->NC = (int)nc;
     L->CH = (int)ch;
+    L->NT = (int)nt;
     L->NCd = (int)ncd;
-    L->CHd = (int)chd;
     const size_t slots = (size_t)(2 * n + 1);
     size_t off = 0;
     L->off_part = off;
@@ -61,8 +61,12 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
     L->off_desc = off;
     off = align_up(off + (size_t)B * sizeof(sv::DrawDesc), 256);
-    L->off_dpart = off;
-    off = align_up(off + (size_t)B * ncd * sizeof(float), 256);
+    L->off_tiles = off;
+    off = align_up(off + (size_t)B * nt * sizeof(unsigned long long), 256);
+    L->off_dres = off;
+    off = align_up(off + (size_t)B * nt * sizeof(float), 256);
+    L->off_dp = off;
+    off = align_up(off + (size_t)B * nt * sizeof(float), 256);
     L->bytes = off < 256 ? 256 : off;
     return true;
 }
@@ -153,17 +157,21 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     sp.part = at<sv::Partial>(workspace, L.off_part);
     sp.cnt = at<uint32_t>(workspace, L.off_cnt);
     sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.NT = L.NT;
+    sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
 
     sv::DrawParams dp{};
     dp.target = target_logits;
     dp.draft = draft_logits;
-    dp.B = B; dp.n = n; dp.V = V; dp.NCd = L.NCd; dp.CHd = L.CHd;
+    dp.B = B; dp.n = n; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
+    dp.tiles = sp.tiles;
     dp.emitted = emitted;
     dp.flags = err_flags;
     dp.desc = sp.desc;
-    dp.dpart = at<float>(workspace, L.off_dpart);
+    dp.dres = at<float>(workspace, L.off_dres);
+    dp.dp = at<float>(workspace, L.off_dp);
     dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
     e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
     if (e != hipSuccess) return hip_fail(e);

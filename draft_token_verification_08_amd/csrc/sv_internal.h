@@ -23,8 +23,8 @@ constexpr int kThreads = SV_THREADS; // workgroup size of every kernel (wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDraft = 64;        // n <= kMaxDraft
 constexpr int kMaxSlots = 2 * kMaxDraft + 1;
-constexpr int kDrawPerThread = 16;   // draw pass: contiguous elements per thread
-constexpr int kMaxDrawChunks = 1024; // LDS bound of the draw selection
+constexpr int kDrawTiles = 8;        // draw pass: tiles (kThreads * elements per 16-byte vector) per chunk
+constexpr int kMaxTiles = 1024;      // tiles per row (4 per thread in the draw selections)
 constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
 
@@ -58,13 +58,15 @@ struct DrawDesc {
 struct Layout {
     int NC;          // vocab chunks per row in the stats pass
     int CH;          // elements per stats chunk (multiple of the vector tile)
-    int NCd;         // chunks per row in the draw pass
-    int CHd;         // elements per draw chunk
+    int NT;          // tiles per row (kThreads * elements per 16-byte vector each)
+    int NCd;         // chunks of kDrawTiles tiles per row in the draw pass
     size_t off_part;     // Partial [B][2n+1][NC]
     size_t off_cnt;      // uint32 [B]   stats-pass arrival counters
     size_t off_cnt_draw; // uint32 [B]   draw-pass arrival counters
     size_t off_desc;     // DrawDesc [B]
-    size_t off_dpart;    // float [B][NCd] draw-pass chunk sums
+    size_t off_tiles;    // uint64 [B][NT] tile partials (m_t, s_t) of target row L (sampling)
+    size_t off_dres;     // float [B][NT] residual mass per tile (draw pass)
+    size_t off_dp;       // float [B][NT] 2^((z - m_t) c) mass per tile of target row k (draw pass)
     size_t bytes;
 };
 
@@ -76,6 +78,8 @@ struct StatsParams {
     const float* temp;        // [B] (sample mode)
     const float* unif;        // [B][n+1] (sample mode)
     int B, n, V, NC, CH, S;   // S = row slots per sequence (2n+1 sample, n+1 greedy)
+    int NT;                   // tiles per row
+    unsigned long long* tiles;  // [B][NT] tile partials (m_t, s_t) of target row L
     int32_t* acc;             // [B]
     int32_t* emitted;         // [B][n+1]
     float* row_lse;           // [B][2n+1] or nullptr
@@ -88,11 +92,13 @@ struct StatsParams {
 struct DrawParams {
     const void* target;
     const void* draft;
-    int B, n, V, NCd, CHd;
+    int B, n, V, NT, NCd;
+    unsigned long long* tiles;
     int32_t* emitted;
     uint32_t* flags;
     DrawDesc* desc;
-    float* dpart;
+    float* dres;
+    float* dp;
     uint32_t* cnt;
 };
 

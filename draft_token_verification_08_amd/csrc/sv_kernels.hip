@@ -92,6 +92,13 @@ __device__ __forceinline__ void unpack(const uint4& w, float* f) {
     }
 }
 
+// a 16-byte vector of -inf (absent elements)
+template <int DT>
+__device__ __forceinline__ uint4 neg_inf_vec() {
+    if constexpr (DT == kBF16) return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+    else return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+}
+
 template <int DT>
 __device__ __forceinline__ const void* row_ptr(const void* base, long long row, int V) {
     return (const char*)base + (size_t)row * (size_t)V * sizeof(typename Elem<DT>::T);
@@ -214,6 +221,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<kDppMirror>(v);
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
     return v;
 }
 __device__ __forceinline__ int wave_max_i(int v) {
@@ -425,6 +441,219 @@ __device__ MS thread_ms(const void* row, int lo, int hi, float c) {
     return MS{m, s};
 }
 
+// Elements [e0, e0 + kVec) of a row as floats; indices at or past `hi` read as
+// -inf (never loaded).  e0 is a multiple of kVec.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void load_vec(const void* row, int e0, int hi, float* f) {
+    constexpr int kVec = Elem<DT>::kVec;
+    if constexpr (ALIGNED) {
+        if (e0 < hi) {
+            unpack<DT>(ld16((const uint4*)row + e0 / kVec), f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) f[e] = -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) f[e] = (e0 + e < hi) ? load_elem<DT>(row, e0 + e) : -INFINITY;
+    }
+}
+
+// Sampling rows: softmax statistics over [lo, hi) (lo a multiple of the tile)
+// in tiles of kThreads * kVec contiguous elements.  Wave w takes tiles w,
+// w + kWaves, ...; inside a tile lane l reads vectors l, l + 64, l + 128, ...
+// (coalesced).  Per tile: the wave maximum m_t, then s_t = sum 2^((z - m_t) c),
+// each term formed as 2^fma(z, c, -fl(m_t c)) and the rounding of fl(m_t c)
+// corrected once per tile (its exact residual is fma(m_t, c, -fl(m_t c))).
+// Tile partials (m_t, s_t) are handed over through atomic exchanges into `tiles`
+// (when not null) for the bonus draw; the workgroup's merged (m, s) is returned
+// in thread 0.
+template <int DT, bool ALIGNED>
+__device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigned long long* tiles) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kTile = kThreads * kVec;
+    constexpr int U = kThreads / 64;  // vectors per lane per tile
+    __shared__ MS s_wave[kWaves];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t0 = lo / kTile, t1 = (hi + kTile - 1) / kTile;
+    float M = -FLT_MAX, S = 0.f;
+    unsigned long long dep = 0ull;
+    // aligned rows: the next tile's 16-byte loads are issued before the current
+    // tile is reduced (double buffer in registers); vectors past `hi` read -inf
+    uint4 nxt[U];
+    auto issue = [&](int tt) {
+        if constexpr (ALIGNED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = tt * kTile + (lane + 64 * u) * kVec;
+                nxt[u] = (e0 < hi) ? ld16((const uint4*)row + e0 / kVec) : neg_inf_vec<DT>();
+            }
+        }
+    };
+    if (t0 + w < t1) issue(t0 + w);
+    for (int t = t0 + w; t < t1; t += kWaves) {
+        float f[U][kVec];
+        if constexpr (ALIGNED) {
+            uint4 cur[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            if (t + kWaves < t1) issue(t + kWaves);
+#pragma unroll
+            for (int u = 0; u < U; ++u) unpack<DT>(cur[u], f[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_vec<DT, ALIGNED>(row, t * kTile + (lane + 64 * u) * kVec, hi, f[u]);
+        }
+        float lm = f[0][0];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) lm = fmaxf(lm, f[u][e]);
+        const float tmax = wave_max_f(lm);
+        float ts = 0.f;
+        if (tmax != -INFINITY) {
+            const float mc = tmax * c;
+            const float delta = fmaf(tmax, c, -mc);
+            float acc[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] += exp2_fast(fmaf(f[u][e], c, -mc));
+            float ls = acc[0];
+#pragma unroll
+            for (int e = 1; e < kVec; ++e) ls += acc[e];
+            ts = wave_sum(ls) * exp2_fast(-delta);
+        }
+        if (tiles != nullptr && lane == 0) dep ^= xchg64(tiles + t, pack2(tmax, ts));
+        const MS r = ms_combine(MS{M, S}, MS{tmax, ts}, c);
+        M = r.m;
+        S = r.s;
+    }
+    if (lane == 0) {
+        // this wave's tile exchanges have been performed before the workgroup arrives
+        asm volatile("" ::"v"((unsigned)dep), "v"((unsigned)(dep >> 32)));
+        __builtin_amdgcn_s_waitcnt(0);
+        s_wave[w] = MS{M, S};
+    }
+    __syncthreads();
+    MS r = s_wave[0];
+    if (threadIdx.x == 0)
+        for (int i = 1; i < kWaves; ++i) r = ms_combine(r, s_wave[i], c);
+    return r;
+}
+
+// --------------------------------------------------------------- inverse CDF
+// Inverse CDF with unnormalised weights: y = the first index whose running sum
+// exceeds t = u * Z.  Work is organised in tiles of kThreads * kVec contiguous
+// elements (thread i of a tile owns elements [i*kVec, (i+1)*kVec) of it), tiles
+// in chunks of kDrawTiles.  Every "which item holds t" question (chunk, tile,
+// thread) is one block-wide prefix scan in binary64 (shuffle scan inside each
+// wave, wave totals through LDS), run in passes of kThreads items.
+
+struct Pick {
+    int i;          // first item whose prefix range [before, before + w) holds t; -1 if none
+    double before;  // prefix mass before item i
+};
+
+// Items 0..N-1, weight(i) >= 0 evaluated by thread i % kThreads in pass i / kThreads.
+template <class W>
+__device__ __forceinline__ Pick block_first_crossing(int N, double t, W&& weight) {
+    __shared__ double s_wave[kWaves];
+    __shared__ double s_pass_total;
+    __shared__ int s_hit;
+    __shared__ double s_before;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    double carry = 0.0;
+    if (tid == 0) s_hit = INT_MAX;
+    for (int base = 0; base < N; base += kThreads) {
+        const int i = base + tid;
+        const double wi = (i < N) ? weight(i) : 0.0;
+        double incl = wi;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) s_wave[w] = incl;
+        __syncthreads();
+        double prev = carry;
+        for (int k = 0; k < w; ++k) prev += s_wave[k];
+        incl += prev;
+        const double excl = incl - wi;
+        if (wi > 0.0 && excl <= t && t < incl) atomicMin(&s_hit, i);
+        if (tid == kThreads - 1) s_pass_total = incl;
+        __syncthreads();
+        const int hit = s_hit;
+        if (hit != INT_MAX) {
+            if (i == hit) s_before = excl;
+            __syncthreads();
+            return Pick{hit, s_before};
+        }
+        carry = s_pass_total;
+        __syncthreads();
+    }
+    return Pick{-1, carry};
+}
+
+// Weight of one element for the draw.  Bonus / fallback rows: 2^((z - m_t) c),
+// on the same scale as the stored tile partials.  Residual rows:
+// max(0, p_k - q_k) with p and q normalised.
+__device__ __forceinline__ float w_target(const DrawDesc& d, float zt) {
+    return exp2_fast((zt - d.m_t) * d.c);
+}
+__device__ __forceinline__ float w_residual(const DrawDesc& d, float zt, float zd) {
+    const float pt = exp2_fast((zt - d.m_t) * d.c) * d.inv_s_t;
+    const float qd = exp2_fast((zd - d.m_d) * d.c) * d.inv_s_d;
+    return fmaxf(pt - qd, 0.f);
+}
+
+// Scan one tile: returns the element whose running weight (starting at P)
+// first exceeds t, or, if none does (rounding), the tile's last element with
+// positive weight, or the tile's first element.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ int scan_tile(const DrawDesc& d, bool residual, const void* trow, const void* drow, int V, int tile,
+                         double P, double t, bool take_last) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kTile = kThreads * kVec;
+    const int e0 = tile * kTile + threadIdx.x * kVec;
+    float zt[kVec], zd[kVec], wv[kVec];
+    load_vec<DT, ALIGNED>(trow, e0, V, zt);
+    if (residual) load_vec<DT, ALIGNED>(drow, e0, V, zd);
+    float ts = 0.f;
+    int my_last = -1;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        wv[e] = (e0 + e < V) ? (residual ? w_residual(d, zt[e], zd[e]) : w_target(d, zt[e])) : 0.f;
+        ts += wv[e];
+        if (wv[e] > 0.f) my_last = e0 + e;
+    }
+    __shared__ float s_ts[kThreads];
+    __shared__ int s_y;
+    s_ts[threadIdx.x] = ts;
+    if (threadIdx.x == 0) s_y = -1;
+    __syncthreads();
+    Pick pk{-1, 0.0};
+    if (!take_last) pk = block_first_crossing(kThreads, t - P, [&](int i) { return (double)s_ts[i]; });
+    if (pk.i == (int)threadIdx.x) {
+        double run = P + pk.before;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            run += (double)wv[e];
+            if (run > t && wv[e] > 0.f) {
+                s_y = e0 + e;
+                break;
+            }
+        }
+    }
+    const int last = block_max_all(my_last);
+    __syncthreads();
+    int y = s_y;
+    if (y < 0) y = (last >= 0) ? last : tile * kTile;
+    return y;
+}
+
 // --------------------------------------------------------------- decision helpers
 
 __device__ __forceinline__ int clamp_len(int L, int n, uint32_t& flags) {
@@ -476,7 +705,7 @@ __device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
 }
 
 // The decision of sequence b, run by the last workgroup of b to finish.
-template <int DT, int MODE>
+template <int DT, int MODE, bool ALIGNED>
 __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __shared__ float s_m[kMaxSlots];
     __shared__ double s_S[kMaxSlots];
@@ -566,7 +795,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     }
     __syncthreads();
 
-    // 3. first rejection, emitted tokens, draw descriptor
+    // 3. first rejection, emitted tokens; sampling sequences: the draw descriptor
     if (tid == 0) {
         uint32_t flags = si.flags;
         int k = L;
@@ -581,10 +810,12 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
         for (int j = k + 1; j <= n; ++j) e[j] = -1;
         p.acc[b] = k;
         if (si.greedy) {
-            e[k] = s_idx[k];  // the descriptor stays zero (kDrawNone)
+            e[k] = s_idx[k];
         } else {
-            e[k] = -1;  // written by the draw pass
             const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + n], flags);
+            // the draw (residual after a rejection, bonus after full acceptance)
+            // is done by the draw pass
+            e[k] = -1;
             DrawDesc d;
             d.kind = (k < L) ? kDrawResidual : kDrawBonus;
             d.k = k;
@@ -634,7 +865,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
         }
     } else {
         const float cf = exp2_scale(si.T);
-        const MS r = block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
+        // target row L is the only row a bonus token can be drawn from: it alone
+        // streams in tiles and keeps per-tile partials
+        const MS r = (target_row && slot == si.L)
+                         ? wg_softmax_tiles<DT, ALIGNED>(row, lo, hi, cf, p.tiles + (size_t)b * p.NT)
+                         : block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
         if (threadIdx.x == 0) {
             const unsigned long long dep = xchg64(slot_part + c, pack2(r.m, r.s));
             s_last = (arrive(&p.cnt[b], dep) == expected - 1u);
@@ -642,200 +877,191 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     }
     __syncthreads();
     if (!s_last) return;
-    decide<DT, MODE>(p, b, si);
+    decide<DT, MODE, ALIGNED>(p, b, si);
 }
 
-// --------------------------------------------------------------- draw pass
-
-// Weight of element i for the draw: p_L (bonus) or max(0, p_k - q_k) (residual).
-template <int DT>
-__device__ __forceinline__ float draw_weight(const DrawDesc& d, bool residual, float zt, float zd) {
-    const float pt = exp2_fast((zt - d.m_t) * d.c) * d.inv_s_t;
-    if (!residual) return pt;
-    const float qd = exp2_fast((zd - d.m_d) * d.c) * d.inv_s_d;
-    return fmaxf(pt - qd, 0.f);
-}
-
-// Thread t owns the kDrawPerThread contiguous elements starting at
-// lo + t * kDrawPerThread (clipped to hi).  Weights are produced in ascending
-// index order; f is called as f(index, weight).
-template <int DT, bool ALIGNED, class F>
-__device__ __forceinline__ void for_thread_weights(const DrawDesc& d, bool residual, const void* trow,
-                                                   const void* drow, int lo, int hi, F&& f) {
-    constexpr int kVec = Elem<DT>::kVec;
-    constexpr int kNV = kDrawPerThread / kVec;
-    const int i0 = lo + threadIdx.x * kDrawPerThread;
-    if constexpr (ALIGNED) {
-        const uint4* vt = (const uint4*)trow;
-        const uint4* vd = (const uint4*)drow;
-#pragma unroll
-        for (int q = 0; q < kNV; ++q) {
-            const int base = i0 + q * kVec;
-            if (base < hi) {
-                float ft[kVec], fd[kVec];
-                unpack<DT>(vt[base / kVec], ft);
-                if (residual) unpack<DT>(vd[base / kVec], fd);
-                else {
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) fd[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) f(base + e, draw_weight<DT>(d, residual, ft[e], fd[e]));
-            }
-        }
-    } else {
-        for (int e = 0; e < kDrawPerThread; ++e) {
-            const int i = i0 + e;
-            if (i < hi) {
-                const float zt = load_elem<DT>(trow, i);
-                const float zd = residual ? load_elem<DT>(drow, i) : 0.f;
-                f(i, draw_weight<DT>(d, residual, zt, zd));
-            }
-        }
-    }
-}
-
+// Draw from the target row's own distribution (the bonus token from p_L after
+// full acceptance): pick the tile holding u * Z from the tile partials (m_t, s_t)
+// the stats pass stored for this row, weighted on the scale 2^((z - m) c) of the
+// row maximum m, with one block prefix scan; then scan only that tile.
 template <int DT, bool ALIGNED>
-__device__ float thread_weight_sum(const DrawDesc& d, bool residual, const void* trow, const void* drow,
-                                   int lo, int hi) {
-    float s = 0.f;
-    for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int, float w) { s += w; });
-    return s;
-}
-
-// Inverse CDF inside one chunk: the first index whose running weight sum
-// (starting from P, the mass of the chunks before) exceeds t.  Thread sums are
-// scanned in double across the workgroup (shuffles inside a wave, then waves in
-// order); only the thread whose range crosses t walks its elements again.
-// Returns -1 if nothing in the chunk crosses t; *last_pos receives the last
-// index with positive weight.
-template <int DT, bool ALIGNED>
-__device__ int scan_chunk(const DrawDesc& d, bool residual, const void* trow, const void* drow, int lo,
-                          int hi, double P, double t, int* last_pos) {
-    __shared__ double s_wave[kWaves];
-    __shared__ int s_found;
+__device__ __forceinline__ int tile_draw(const DrawParams& p, int b, const DrawDesc& d, const void* trow,
+                                         double* s_w /* LDS, >= kMaxTiles */) {
+    const unsigned long long* tiles = p.tiles + (size_t)b * p.NT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    float ts = 0.f;
+    double mine = 0.0;
     int my_last = -1;
-    for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int i, float wgt) {
-        ts += wgt;
-        if (wgt > 0.f) my_last = i;
-    });
-    double incl = (double)ts;
+    for (int i = tid; i < p.NT; i += kThreads) {
+        const unsigned long long q = tiles[i];
+        const float ts = hi_f(q);
+        const double wi = ts > 0.f ? (double)ts * exp2(((double)lo_f(q) - (double)d.m_t) * (double)d.c) : 0.0;
+        s_w[i] = wi;
+        mine += wi;
+        if (wi > 0.0) my_last = i;
+    }
+    __shared__ double s_part[kWaves];
+    __shared__ double s_t;
+    __shared__ int s_last_tile;
+    double incl = mine;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const double o = __shfl_up(incl, off, 64);
         if (lane >= off) incl += o;
     }
-    if (lane == 63) s_wave[w] = incl;
-    if (tid == 0) s_found = INT_MAX;
-    __syncthreads();
-    double before = P;
-    for (int i = 0; i < w; ++i) before += s_wave[i];
-    const double excl = before + incl - (double)ts;
-    if (excl <= t && excl + (double)ts > t) {
-        double run = excl;
-        int hit = INT_MAX;
-        for_thread_weights<DT, ALIGNED>(d, residual, trow, drow, lo, hi, [&](int i, float wgt) {
-            run += (double)wgt;
-            if (hit == INT_MAX && run > t) hit = i;
-        });
-        if (hit != INT_MAX) atomicMin(&s_found, hit);
-    }
-    *last_pos = block_max_all(my_last);
-    __syncthreads();
-    const int r = s_found;
-    return (r == INT_MAX) ? -1 : r;
-}
-
-// Chunk selection and final scan (last workgroup of a sequence).
-template <int DT, bool ALIGNED>
-__device__ void draw_select(const DrawParams& p, int b, DrawDesc d) {
-    __shared__ float s_sum[kMaxDrawChunks];
-    __shared__ int s_c;
-    __shared__ double s_P, s_t;
-    __shared__ int s_zero;
-    const int tid = threadIdx.x;
-    const int NCd = p.NCd, CHd = p.CHd, V = p.V, n = p.n;
-    const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + d.k, V);
-    const void* drow = (d.kind == kDrawResidual) ? row_ptr<DT>(p.draft, (long long)b * n + d.k, V) : nullptr;
-    bool residual = (d.kind == kDrawResidual);
-
-    unsigned* dpart = reinterpret_cast<unsigned*>(p.dpart) + (size_t)b * NCd;
-    for (int c = tid; c < NCd; c += kThreads) s_sum[c] = __uint_as_float(xchg32(dpart + c, 0u));
-    __syncthreads();
-
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        if (tid == 0) {
-            double Z = 0.0;
-            for (int c = 0; c < NCd; ++c) Z += (double)s_sum[c];
-            s_zero = !(Z > 0.0);
-            const double t = (double)d.u * Z;
-            double P = 0.0;
-            int cs = -1;
-            for (int c = 0; c < NCd; ++c) {
-                if (P + (double)s_sum[c] > t) { cs = c; break; }
-                P += (double)s_sum[c];
-            }
-            if (cs < 0) {  // t at or past the total (rounding): last chunk with mass
-                P = 0.0;
-                for (int c = 0; c < NCd; ++c)
-                    if (s_sum[c] > 0.f) cs = c;
-                for (int c = 0; c < cs; ++c) P += (double)s_sum[c];
-                if (cs < 0) cs = 0;
-            }
-            s_c = cs;
-            s_P = P;
-            s_t = t;
-        }
-        __syncthreads();
-        if (s_zero && residual) {
-            // no residual mass left after rounding: draw from p_k instead
-            if (tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
-            residual = false;
-            for (int c = 0; c < NCd; ++c) {
-                const int lo = c * CHd, hi = min(V, lo + CHd);
-                const float cs = block_sum_all(thread_weight_sum<DT, ALIGNED>(d, false, trow, nullptr, lo, hi));
-                if (tid == 0) s_sum[c] = cs;
-            }
-            __syncthreads();
-            continue;
-        }
-        break;
-    }
-    const int cs = s_c;
-    const int lo = cs * CHd, hi = min(V, lo + CHd);
-    int last_pos = -1;
-    int y = scan_chunk<DT, ALIGNED>(d, residual, trow, drow, lo, hi, s_P, s_t, &last_pos);
+    if (lane == 63) s_part[w] = incl;
+    const int last_tile = block_max_all(my_last);
     if (tid == 0) {
-        if (y < 0) y = (last_pos >= 0) ? last_pos : lo;
-        p.emitted[(size_t)b * (n + 1) + d.k] = y;
-        p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        xchg32(&p.cnt[b], 0u);
+        double Z = 0.0;
+        for (int k = 0; k < kWaves; ++k) Z += s_part[k];
+        s_t = (double)d.u * Z;
+        s_last_tile = last_tile < 0 ? 0 : last_tile;
     }
+    __syncthreads();
+    const double t = s_t;
+    const Pick pk = block_first_crossing(p.NT, t, [&](int i) { return s_w[i]; });
+    if (pk.i >= 0) return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, p.V, pk.i, pk.before, t, false);
+    return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, p.V, s_last_tile, 0.0, t, true);
 }
 
+// --------------------------------------------------------------- draw pass
+// Bonus draws (all drafts accepted): workgroup (b, 0) alone, with tile_draw().
+// Residual draws (draft k rejected) from max(0, p_k - q_k): workgroup (b, c)
+// reads its chunk of kDrawTiles tiles of target row k and draft row k once
+// (thread i: vector i of every tile), and hands over per-tile sums of the
+// residual and of 2^((z - m_t) c) (the p_k fallback) by atomic exchange.  The
+// last workgroup of the sequence picks the tile holding u * Z with one block
+// prefix scan and scans only that tile.
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kTile = kThreads * kVec;
     const int c = blockIdx.x % p.NCd;
     const int b = blockIdx.x / p.NCd;
     const DrawDesc d = p.desc[b];
     if (d.kind == kDrawNone) return;
-    const bool residual = (d.kind == kDrawResidual);
-    const void* trow = row_ptr<DT>(p.target, (long long)b * (p.n + 1) + d.k, p.V);
-    const void* drow = residual ? row_ptr<DT>(p.draft, (long long)b * p.n + d.k, p.V) : nullptr;
-    const int lo = c * p.CHd, hi = min(p.V, lo + p.CHd);
-    const float cs = block_sum_all(thread_weight_sum<DT, ALIGNED>(d, residual, trow, drow, lo, hi));
+    const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
+    const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + d.k, V);
+    __shared__ double s_buf[kMaxTiles];
+    if (d.kind == kDrawBonus) {
+        if (c != 0) return;
+        const int y = tile_draw<DT, ALIGNED>(p, b, d, trow, s_buf);
+        for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;  // used: leave zero
+        if (tid == 0) {
+            p.emitted[(size_t)b * (n + 1) + d.k] = y;
+            p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+    const void* drow = row_ptr<DT>(p.draft, (long long)b * n + d.k, V);
+    unsigned* dres = reinterpret_cast<unsigned*>(p.dres) + (size_t)b * NT;
+    unsigned* dp = reinterpret_cast<unsigned*>(p.dp) + (size_t)b * NT;
 
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-        const unsigned dep = xchg32(reinterpret_cast<unsigned*>(p.dpart) + (size_t)b * p.NCd + c,
-                                    __float_as_uint(cs));
-        s_last = (arrive(&p.cnt[b], dep) == (unsigned)p.NCd - 1u);
+    const int tile0 = c * kDrawTiles;
+    const int cnt = min(kDrawTiles, NT - tile0);
+    __shared__ float s_r[kWaves][kDrawTiles], s_p[kWaves][kDrawTiles];
+#pragma unroll
+    for (int k = 0; k < kDrawTiles; ++k) {
+        float zt[kVec], zd[kVec];
+        const int e0 = (tile0 + k) * kTile + tid * kVec;
+        const int lim = (k < cnt) ? V : 0;
+        load_vec<DT, ALIGNED>(trow, e0, lim, zt);
+        load_vec<DT, ALIGNED>(drow, e0, lim, zd);
+        float ar = 0.f, ap = 0.f;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            ar += w_residual(d, zt[e], zd[e]);  // absent elements read -inf: weight 0
+            ap += w_target(d, zt[e]);
+        }
+        ar = wave_sum(ar);
+        ap = wave_sum(ap);
+        if ((tid & 63) == 0) {
+            s_r[tid >> 6][k] = ar;
+            s_p[tid >> 6][k] = ap;
+        }
     }
     __syncthreads();
+    if (tid < cnt) {
+        float r = s_r[0][tid], q = s_p[0][tid];
+        for (int w = 1; w < kWaves; ++w) {
+            r += s_r[w][tid];
+            q += s_p[w][tid];
+        }
+        const unsigned d1 = xchg32(dres + tile0 + tid, __float_as_uint(r));
+        const unsigned d2 = xchg32(dp + tile0 + tid, __float_as_uint(q));
+        asm volatile("" ::"v"(d1), "v"(d2));
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) s_last = (arrive(&p.cnt[b], 0ull) == (unsigned)p.NCd - 1u);
+    __syncthreads();
     if (!s_last) return;
-    draw_select<DT, ALIGNED>(p, b, d);
+
+    // last workgroup: collect (and reset) the per-tile sums of the whole row pair
+    float* s_wr = reinterpret_cast<float*>(s_buf);
+    float* s_wp = s_wr + kMaxTiles;
+    double mr = 0.0, mp = 0.0;
+    for (int i = tid; i < NT; i += kThreads) {
+        const float r = __uint_as_float(xchg32(dres + i, 0u));
+        const float q = __uint_as_float(xchg32(dp + i, 0u));
+        s_wr[i] = r;
+        s_wp[i] = q;
+        mr += (double)r;
+        mp += (double)q;
+    }
+    __shared__ double s_zr[kWaves], s_zp[kWaves];
+    __shared__ double s_t;
+    __shared__ int s_use_p;
+    {
+        const int lane = tid & 63, w = tid >> 6;
+        double ir = mr, ip = mp;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double o1 = __shfl_up(ir, off, 64), o2 = __shfl_up(ip, off, 64);
+            if (lane >= off) {
+                ir += o1;
+                ip += o2;
+            }
+        }
+        if (lane == 63) {
+            s_zr[w] = ir;
+            s_zp[w] = ip;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double Zr = 0.0, Zp = 0.0;
+            for (int k = 0; k < kWaves; ++k) {
+                Zr += s_zr[k];
+                Zp += s_zp[k];
+            }
+            s_use_p = !(Zr > 0.0);
+            s_t = (double)d.u * (s_use_p ? Zp : Zr);
+            if (s_use_p && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
+        }
+        __syncthreads();
+    }
+    const bool use_p = s_use_p;  // no residual mass left after rounding: draw from p_k
+    const float* sw = use_p ? s_wp : s_wr;
+    const double t = s_t;
+    const Pick pk = block_first_crossing(NT, t, [&](int i) { return (double)sw[i]; });
+    int tile = pk.i;
+    bool take_last = false;
+    if (tile < 0) {  // t at or past the total through rounding: the last tile with mass
+        int my_last = -1;
+        for (int i = tid; i < NT; i += kThreads)
+            if (sw[i] > 0.f) my_last = i;
+        const int lt = block_max_all(my_last);
+        tile = lt < 0 ? 0 : lt;
+        take_last = true;
+    }
+    const int y = scan_tile<DT, ALIGNED>(d, !use_p, trow, drow, V, tile, pk.before, t, take_last);
+    // row L's tile partials (written by the stats pass, unused here): leave them zero
+    for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;
+    if (tid == 0) {
+        p.emitted[(size_t)b * (n + 1) + d.k] = y;
+        p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        xchg32(&p.cnt[b], 0u);
+    }
 }
 
 // --------------------------------------------------------------- MTP shift / insert
@@ -927,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, 
     }
     const float c = exp2_scale(T);
     __shared__ MS s_ms;
-    const MS ms = block_ms(thread_ms<DT, ALIGNED>(row, 0, V, c), c);
+    const MS ms = wg_softmax_tiles<DT, ALIGNED>(row, 0, V, c, nullptr);
     if (threadIdx.x == 0) s_ms = ms;
     __syncthreads();
     const float m = s_ms.m;
