@@ -6,8 +6,9 @@ binding (torch tensors in, device pointers and the current stream out).
 """
 from ._lib import (  # noqa: F401
     SV_BF16, SV_EALIGN, SV_EHIP, SV_EINVAL, SV_EWORKSPACE, SV_F32, SV_FLAG_BAD_TEMP,
-    SV_FLAG_BAD_UNIFORM, SV_FLAG_LEN_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_ZERO_RESIDUAL, SV_MAX_DRAFT,
+    SV_FLAG_BAD_UNIFORM, SV_FLAG_LEN_CLAMPED, SV_FLAG_ROW_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_ZERO_RESIDUAL,
+    SV_MAX_DRAFT,
     SV_OK, Prepared, SpecVerifyError, Workspace, lib, mtp_shift_insert, prepare_mtp_shift_insert,
     prepare_spec_verify_greedy, prepare_spec_verify_sample, spec_verify_greedy, spec_verify_sample,
-    sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
+    sv_sample_rows, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
 )

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_F32, SV_BF16 = 0, 1
 SV_OK, SV_EINVAL, SV_EALIGN, SV_EWORKSPACE, SV_EHIP = 0, 1, 2, 3, 4
 SV_FLAG_LEN_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_BAD_TEMP, SV_FLAG_BAD_UNIFORM, SV_FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
+SV_FLAG_ROW_CLAMPED = 32
 SV_MAX_DRAFT = 64
 
 _lib = None
@@ -57,6 +58,8 @@ def lib():
     L.spec_verify_greedy.restype = i
     L.mtp_shift_insert.argtypes = [vp, vp, vp, i, vp, vp, i, i, vp]
     L.mtp_shift_insert.restype = i
+    L.sv_sample_rows.argtypes = [vp, i, i, vp, vp, vp, i, i, vp, vp, vp, sz, vp]
+    L.sv_sample_rows.restype = i
     L.sv_softmax_rows_debug.argtypes = [vp, i, vp, i, i, vp, vp]
     L.sv_softmax_rows_debug.restype = i
     _lib = L
@@ -315,3 +318,34 @@ def prepare_mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitt
     args = (_ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(accepted_len), _ptr(emitted), B, n1 - 1,
             _stream(stream, dev))
     return Prepared("mtp_shift_insert", args, (tokens, hidden_src, hidden_dst, accepted_len, emitted))
+
+
+# ------------------------------------------------------------------ standard sampling of chosen rows
+
+def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None, err_flags=None,
+                   workspace=None, stream=None):
+    """One token per sequence from logits[b][row_index[b]] (row 0 when row_index
+    is None): logits [B][R][V] (or [B][V]), temperature [B], uniforms [B].
+    Returns tokens [B] int32 (see include/specverify.h)."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(1)
+    B, R, V = logits.shape
+    dev = logits.device
+    dt = _dt(logits)
+    _check(logits, "logits")
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B,), dev)
+    if row_index is not None:
+        _check(row_index, "row_index", torch.int32, (B,), dev)
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(tokens, "tokens", torch.int32, (B,), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, 0, V, dt)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("sv_sample_rows", _ptr(logits), dt, R, _ptr(row_index), _ptr(temperature), _ptr(uniforms), B, V,
+          _ptr(tokens), _ptr(err_flags), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return tokens

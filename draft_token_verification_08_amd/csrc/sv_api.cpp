@@ -67,6 +67,8 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     off = align_up(off + (size_t)B * nt * sizeof(float), 256);
     L->off_dp = off;
     off = align_up(off + (size_t)B * nt * sizeof(float), 256);
+    L->off_acc = off;
+    off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L->bytes = off < 256 ? 256 : off;
     return true;
 }
@@ -159,6 +161,8 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
     sp.NT = L.NT;
     sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
+    sp.R = n + 1;
+    sp.row_index = nullptr;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
 
@@ -166,6 +170,8 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     dp.target = target_logits;
     dp.draft = draft_logits;
     dp.B = B; dp.n = n; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
+    dp.R = sp.R;
+    dp.row_index = sp.row_index;
     dp.tiles = sp.tiles;
     dp.emitted = emitted;
     dp.flags = err_flags;
@@ -209,8 +215,67 @@ sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const i
     sp.part = at<sv::Partial>(workspace, L.off_part);
     sp.cnt = at<uint32_t>(workspace, L.off_cnt);
     sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.R = n + 1;
+    sp.row_index = nullptr;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kGreedy,
                                     rows_aligned(target_logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32_t* row_index,
+                           const float* temperature, const float* uniforms, int B, int V, int32_t* tokens,
+                           uint32_t* err_flags, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || R < 1 || V < 1 || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!logits || !temperature || !uniforms || !tokens) return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(logits, es) || !aligned_to(row_index, 4) || !aligned_to(temperature, 4) ||
+        !aligned_to(uniforms, 4) || !aligned_to(tokens, 4) || !aligned_to(err_flags, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, 0, V, dt, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    if (!grid_ok((long long)B * L.NC) || !grid_ok((long long)B * L.NCd)) return SV_EINVAL;
+    const bool aligned = rows_aligned(logits, V, dt);
+    hipStream_t s = (hipStream_t)stream;
+
+    // the verify step with no drafts: one target slot per sequence, row chosen on the device
+    sv::StatsParams sp{};
+    sp.target = logits;
+    sp.draft = nullptr;
+    sp.tokens = nullptr;
+    sp.lens = nullptr;
+    sp.temp = temperature;
+    sp.unif = uniforms;
+    sp.B = B; sp.n = 0; sp.V = V; sp.NC = L.NC; sp.CH = L.CH; sp.S = 1;
+    sp.acc = at<int32_t>(workspace, L.off_acc);
+    sp.emitted = tokens;
+    sp.row_lse = nullptr;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.NT = L.NT;
+    sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
+    sp.R = R;
+    sp.row_index = row_index;
+    hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
+    if (e != hipSuccess) return hip_fail(e);
+    sv::DrawParams dp{};
+    dp.target = logits;
+    dp.draft = nullptr;
+    dp.B = B; dp.n = 0; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
+    dp.R = R;
+    dp.row_index = row_index;
+    dp.tiles = sp.tiles;
+    dp.emitted = tokens;
+    dp.flags = err_flags;
+    dp.desc = sp.desc;
+    dp.dres = at<float>(workspace, L.off_dres);
+    dp.dp = at<float>(workspace, L.off_dp);
+    dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+    e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 

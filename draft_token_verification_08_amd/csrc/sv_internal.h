@@ -67,6 +67,7 @@ struct Layout {
     size_t off_tiles;    // uint64 [B][NT] tile partials (m_t, s_t) of target row L (sampling)
     size_t off_dres;     // float [B][NT] residual mass per tile (draw pass)
     size_t off_dp;       // float [B][NT] 2^((z - m_t) c) mass per tile of target row k (draw pass)
+    size_t off_acc;      // int32 [B] accepted lengths of sv_sample_rows (always 0)
     size_t bytes;
 };
 
@@ -80,6 +81,8 @@ struct StatsParams {
     int B, n, V, NC, CH, S;   // S = row slots per sequence (2n+1 sample, n+1 greedy)
     int NT;                   // tiles per row
     unsigned long long* tiles;  // [B][NT] tile partials (m_t, s_t) of target row L
+    int R;                    // target rows per sequence in memory (n + 1, or R of sv_sample_rows)
+    const int32_t* row_index; // [B] or nullptr: target row 0 of sequence b is row_index[b] (clamped)
     int32_t* acc;             // [B]
     int32_t* emitted;         // [B][n+1]
     float* row_lse;           // [B][2n+1] or nullptr
@@ -93,6 +96,8 @@ struct DrawParams {
     const void* target;
     const void* draft;
     int B, n, V, NT, NCd;
+    int R;
+    const int32_t* row_index;
     unsigned long long* tiles;
     int32_t* emitted;
     uint32_t* flags;

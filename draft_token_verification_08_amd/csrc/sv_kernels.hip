@@ -106,6 +106,16 @@ __device__ __forceinline__ const void* row_ptr(const void* base, long long row, 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Row (in the target buffer) of target slot `slot` of sequence b: the slots of a
+// sequence are R consecutive rows; with a row index, slot 0 is row row_index[b]
+// clamped to [0, R) (only used with n = 0).
+__device__ __forceinline__ long long target_row_of(int R, const int32_t* row_index, int b, int slot) {
+    if (row_index == nullptr) return (long long)b * R + slot;
+    int r = row_index[b];
+    r = r < 0 ? 0 : (r >= R ? R - 1 : r);
+    return (long long)b * R + r;
+}
+
 // --------------------------------------------------------------- cross-workgroup exchange
 // Workgroups of one sequence hand their partial results to the last one to
 // finish through device-scope atomic read-modify-writes only: the writer's data
@@ -687,7 +697,8 @@ template <int MODE>
 __device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
     SeqInfo s;
     s.flags = 0;
-    s.L = clamp_len(p.lens[b], p.n, s.flags);
+    s.L = (p.lens != nullptr) ? clamp_len(p.lens[b], p.n, s.flags) : 0;
+    if (p.row_index != nullptr && (p.row_index[b] < 0 || p.row_index[b] >= p.R)) s.flags |= SV_FLAG_ROW_CLAMPED;
     s.T = 0.f;
     s.greedy = true;
     if constexpr (MODE == kSample) {
@@ -775,7 +786,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
         } else if (si.greedy) {
             s_acc[j] = (x == s_idx[j]);
         } else {
-            const float zt = load_elem<DT>(row_ptr<DT>(p.target, (long long)b * (n + 1) + j, V), x);
+            const float zt = load_elem<DT>(row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, j), V), x);
             const float zd = load_elem<DT>(row_ptr<DT>(p.draft, (long long)b * n + j, V), x);
             uint32_t fl = 0;
             const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + j], fl);
@@ -849,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     if (!needed) return;
     const unsigned expected = (unsigned)p.NC * (unsigned)(si.L + 1 + (si.greedy ? 0 : si.L));
 
-    const void* row = target_row ? row_ptr<DT>(p.target, (long long)b * (n + 1) + slot, p.V)
+    const void* row = target_row ? row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, slot), p.V)
                                  : row_ptr<DT>(p.draft, (long long)b * n + (slot - n - 1), p.V);
     const int lo = c * p.CH;
     const int hi = min(p.V, lo + p.CH);
@@ -940,7 +951,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     const DrawDesc d = p.desc[b];
     if (d.kind == kDrawNone) return;
     const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
-    const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + d.k, V);
+    const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
     __shared__ double s_buf[kMaxTiles];
     if (d.kind == kDrawBonus) {
         if (c != 0) return;

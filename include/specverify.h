@@ -36,6 +36,7 @@
  *       temperature < 0 or NaN         -> treated as 0 (greedy)  SV_FLAG_BAD_TEMP
  *       uniform NaN or < 0 / >= 1      -> 0 / largest float < 1  SV_FLAG_BAD_UNIFORM
  *       residual mass not positive     -> draw from p_k          SV_FLAG_ZERO_RESIDUAL
+ *       row_index[b] outside [0, R)    -> clamped                SV_FLAG_ROW_CLAMPED
  *   - Rows the step does not need are never read: target rows r > L_b, draft
  *     rows r >= L_b, and draft rows of sequences with T_b = 0.
  *   - Calls that share one workspace must not overlap in time (same stream, or
@@ -68,7 +69,8 @@ enum {
     SV_FLAG_TOKEN_OOR = 2,
     SV_FLAG_BAD_TEMP = 4,
     SV_FLAG_BAD_UNIFORM = 8,
-    SV_FLAG_ZERO_RESIDUAL = 16
+    SV_FLAG_ZERO_RESIDUAL = 16,
+    SV_FLAG_ROW_CLAMPED = 32
 };
 
 /* Bytes of device workspace spec_verify_sample() and spec_verify_greedy() need
@@ -131,8 +133,9 @@ sv_status_t spec_verify_sample(const void *target_logits, const void *draft_logi
  * without draft logits, temperatures or uniforms.  Accepts the longest prefix of
  * drafts equal to the argmax of their target rows (lowest index on ties) and
  * emits the argmax of the first mismatching row, or of row L when all match.
- * Target-draft section, decode paragraph ("the draft samples its top token") of
- * "Accelerating Sonar through speculation"; the argmax is sampling at T -> 0.
+ * Target-draft section, decode paragraph, of "Accelerating Sonar through
+ * speculation": the draft takes its highest-scoring token at each stage; the
+ * argmax is sampling at T -> 0.
  * Arguments as in spec_verify_sample(). */
 sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
                                const int32_t *draft_tokens, const int32_t *draft_lens, int B,
@@ -166,6 +169,28 @@ sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
 sv_status_t mtp_shift_insert(int32_t *tokens, const void *hidden_src, void *hidden_dst, int H,
                              const int32_t *accepted_len, const int32_t *emitted, int B, int n,
                              void *stream);
+
+/* Standard sampling of one token per sequence from a row chosen on the device.
+ *
+ * Sequence b draws from logits[b][r_b][:] with r_b = row_index[b] (clamped to
+ * [0, R); row 0 when row_index is NULL): inverse CDF of softmax(z / T_b) with
+ * uniforms[b], or the argmax (lowest index) when T_b = 0 -- the rule of
+ * spec_verify_sample() with no drafts.  Two uses from "Accelerating Sonar
+ * through speculation": the first draft token of the next step comes from the
+ * carried draft logits at the accepted slot a_b (Target-draft section, decode
+ * paragraph; Single-token MTP scheduling section, second paragraph: pass the
+ * [B][n+1][V] draft/MTP logits, R = n + 1 and row_index = accepted_len), and the
+ * draft's own per-step sampling (R = 1, row_index = NULL).  No host sync.
+ *
+ *   logits     [B][R][V] dt      row_index [B] int32, nullable
+ *   temperature [B] float        uniforms [B] float in [0,1)
+ *   tokens     [B] int32 out     err_flags [1] uint32, nullable
+ *   workspace  >= sv_workspace_bytes(B, 0, V, dt) bytes, zero-filled before first use
+ */
+sv_status_t sv_sample_rows(const void *logits, sv_dtype_t dt, int R, const int32_t *row_index,
+                           const float *temperature, const float *uniforms, int B, int V,
+                           int32_t *tokens, uint32_t *err_flags, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Parity/debug only (not on the hot path): full binary32 probabilities
  * softmax(logits[r] / temperature[r]) of `rows` rows of length V, computed with

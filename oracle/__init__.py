@@ -19,6 +19,7 @@ LIB = os.path.join(HERE, "libspecverify_oracle.so")
 
 F32, BF16 = 0, 1
 FLAG_LEN_CLAMPED, FLAG_TOKEN_OOR, FLAG_BAD_TEMP, FLAG_BAD_UNIFORM, FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
+FLAG_ROW_CLAMPED = 32
 
 
 def build(out_path: str = LIB, plant: int = 0) -> str:
@@ -55,6 +56,9 @@ class Oracle:
         L.sv_oracle_argmax_row.restype = C.c_int
         L.sv_oracle_draw_weights.argtypes = [f64p, C.c_int, C.c_double, f64p]
         L.sv_oracle_draw_weights.restype = C.c_int
+        L.sv_oracle_sample_rows.argtypes = [vp, C.c_int, C.c_int, i32p, f32p, f32p, C.c_int, C.c_int, i32p,
+                                            u32p, C.c_int]
+        L.sv_oracle_sample_rows.restype = C.c_int
         L.sv_oracle_plant.argtypes = []
         L.sv_oracle_plant.restype = C.c_int
 
@@ -140,6 +144,21 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"sv_oracle_mtp_shift_insert failed: {rc}")
         return tok, hd
+
+    def sample_rows(self, logits, temperature, uniforms, row_index=None, threads=1):
+        """One token per sequence from logits[b][row_index[b]] (row 0 if None)."""
+        logits, dt = self._logits(logits)
+        B, R, V = logits.shape
+        ri = None if row_index is None else np.ascontiguousarray(row_index, dtype=np.int32).reshape(B)
+        temperature = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+        uniforms = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B)
+        tok = np.empty(B, np.int32)
+        fl = np.empty(B, np.uint32)
+        rc = self.lib.sv_oracle_sample_rows(self._p(logits), dt, R, self._p(ri), self._p(temperature),
+                                            self._p(uniforms), B, V, self._p(tok), self._p(fl), int(threads))
+        if rc != 0:
+            raise RuntimeError(f"sv_oracle_sample_rows failed: {rc}")
+        return dict(tokens=tok, seq_flags=fl)
 
     def softmax_row(self, z, T):
         z, dt = self._logits(np.asarray(z).reshape(-1))

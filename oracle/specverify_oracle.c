@@ -15,8 +15,8 @@
  *   - Speculative decoding section, second paragraph: every candidate prefix is
  *     scored by probability, the longest acceptable prefix is kept, and the target
  *     supplies one extra token, so n drafts give at most n + 1 tokens per step.
- *   - Speculative decoding section, four inference stages ("acceptance" and
- *     "target generation"): at the mismatch, or after the last draft, the target
+ *   - Speculative decoding section, the acceptance and target-generation stages
+ *     of its four inference stages: at the mismatch, or after the last draft, the target
  *     logits of that position yield one more token, which ends the sequence.
  *   - Target-draft section, prefill paragraph: batches without speculation use
  *     standard sampling (here: draft length 0).
@@ -413,6 +413,47 @@ int sv_oracle_mtp_shift_insert(int32_t *tokens, const void *hidden_src, void *hi
     if (hidden_src && hidden_dst && hidden_src != hidden_dst)
         memcpy(hidden_dst, hidden_src, (size_t)B * (size_t)(n + 1) * (size_t)H * (size_t)elem_bytes);
     return 0;
+}
+
+/* Standard sampling of one token per sequence from a row chosen per sequence:
+ * sequence b draws from logits[b][r_b][:] with r_b = row_index[b] clamped to
+ * [0, R) (row 0 when row_index is NULL), by the same rule as a verify step with
+ * no drafts (draft length 0): inverse CDF of softmax(z / T_b) with uniforms[b],
+ * or the argmax when T_b = 0.  This is how the first draft token of the next
+ * step comes from the carried draft logits at the accepted slot (Target-draft
+ * section, decode paragraph; Single-token MTP scheduling section, second
+ * paragraph).  seq_flags bit 32 marks a clamped row index. */
+int sv_oracle_sample_rows(const void *logits, int dt, int R, const int32_t *row_index,
+                          const float *temperature, const float *uniforms, int B, int V,
+                          int32_t *tokens, uint32_t *seq_flags, int threads)
+{
+    if (B < 0 || R < 1 || V < 1) return -1;
+    if (B == 0) return 0;
+    const size_t es = (dt == OR_BF16) ? 2 : 4;
+    unsigned char *rows = (unsigned char *)malloc((size_t)B * (size_t)V * es);
+    int32_t *zeros = (int32_t *)calloc((size_t)B, sizeof(int32_t));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)B);
+    if (!rows || !zeros || !acc) { free(rows); free(zeros); free(acc); return -2; }
+    for (int b = 0; b < B; ++b) {
+        int r = row_index ? row_index[b] : 0;
+        uint32_t f = 0;
+        if (r < 0) { r = 0; f = 32u; }
+        if (r >= R) { r = R - 1; f = 32u; }
+        if (seq_flags) seq_flags[b] = f;
+        memcpy(rows + (size_t)b * V * es, (const unsigned char *)logits + ((size_t)b * R + r) * V * es,
+               (size_t)V * es);
+    }
+    uint32_t *fl = (uint32_t *)calloc((size_t)B, sizeof(uint32_t));
+    job_t J = {rows, NULL, dt, NULL, zeros, temperature, uniforms, B, 0, V, OR_MODE_SAMPLE,
+               acc, tokens, NULL, NULL, NULL, fl};
+    int rc = fl ? run_job(&J, threads) : -2;
+    if (seq_flags && fl)
+        for (int b = 0; b < B; ++b) seq_flags[b] |= fl[b];
+    free(fl);
+    free(rows);
+    free(zeros);
+    free(acc);
+    return rc;
 }
 
 /* Softmax of one row at temperature T (> 0): returns lse = log sum exp(z / T) and,

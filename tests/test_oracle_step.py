@@ -286,3 +286,41 @@ def test_mtp_clamps_accepted_length_and_in_place(oracle):
     new_tok, hid = oracle.mtp_shift_insert(tokens, None, np.array([9, -4], np.int32), emitted)
     assert new_tok.tolist() == [[6, 7, 9], [8, 3, 3]]
     assert hid is None
+
+
+# ------------------------------------------------------------------ standard sampling of a chosen row
+
+def test_sample_rows_greedy_is_numpy_argmax_of_chosen_row(oracle):
+    rng = np.random.default_rng(12)
+    B, R, V = 40, 5, 999
+    z = rng.integers(-6, 6, (B, R, V)).astype(np.float32)       # many ties
+    ri = rng.integers(0, R, B).astype(np.int32)
+    out = oracle.sample_rows(z, np.zeros(B, np.float32), rng.random(B).astype(np.float32), ri)
+    assert np.array_equal(out["tokens"], [int(np.argmax(z[b, ri[b]])) for b in range(B)])
+    assert (out["seq_flags"] == 0).all()
+
+
+def test_sample_rows_is_inverse_cdf_of_chosen_row(oracle):
+    rng = np.random.default_rng(13)
+    B, R, V = 60, 3, 500
+    z = (2 * rng.standard_normal((B, R, V))).astype(np.float32)
+    ri = rng.integers(0, R, B).astype(np.int32)
+    T = np.full(B, 0.8, np.float32)
+    u = rng.random(B).astype(np.float32)
+    out = oracle.sample_rows(z, T, u, ri)
+    Td = float(np.float32(0.8))
+    for b in range(B):
+        c = np.cumsum(sps.softmax(z[b, ri[b]].astype(np.float64) / Td))
+        assert out["tokens"][b] == int(np.searchsorted(c, float(u[b]) * c[-1], side="right"))
+
+
+def test_sample_rows_clamps_row_index(oracle):
+    rng = np.random.default_rng(14)
+    z = rng.standard_normal((4, 3, 50)).astype(np.float32)
+    ri = np.array([-1, 0, 3, 2], np.int32)
+    out = oracle.sample_rows(z, np.zeros(4, np.float32), np.zeros(4, np.float32), ri)
+    assert out["tokens"].tolist() == [int(np.argmax(z[0, 0])), int(np.argmax(z[1, 0])),
+                                      int(np.argmax(z[2, 2])), int(np.argmax(z[3, 2]))]
+    assert (out["seq_flags"] & orc.FLAG_ROW_CLAMPED).tolist() == [32, 0, 32, 0]
+    none = oracle.sample_rows(z, np.zeros(4, np.float32), np.zeros(4, np.float32), None)
+    assert none["tokens"].tolist() == [int(np.argmax(z[b, 0])) for b in range(4)]
