@@ -180,6 +180,17 @@ def main():
     m_avg_ms = statistics.fmean(mtp_ms) if cfg.H else 0.0
     mean_acc = float(torch.stack([d["acc"].float().mean() for d in data]).mean())
 
+    # a bare event pair on the same stream: the queue time an event pair adds to
+    # each bracketed launch (reported, not subtracted)
+    bare = []
+    for _ in range(20):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b2.record(stream)
+        bare.append((a, b2))
+    torch.cuda.synchronize()
+    event_pair_us = statistics.median(a.elapsed_time(b2) for a, b2 in bare) * 1e3
+
     kernel = "k_stats_greedy" if greedy else "k_stats_sample+k_draw"
     workload = cfg.name
     traffic = measured_traffic(kernel, workload)
@@ -208,7 +219,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(v_gbps, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(v_gbps / PEAK_GBPS, 4),
                      "bytes_per_launch": int(v_bytes), "avg_launch_us": round(v_avg_ms * 1e3, 2),
-                     "timed_launches": len(verify_ms), "traffic": traffic},
+                     "timed_launches": len(verify_ms), "bare_event_pair_us": round(event_pair_us, 2),
+                     "traffic": traffic},
     }
 
     # ---------------------------------------------------------------- CPU oracle
@@ -251,19 +263,20 @@ def cpu_baseline(d, cfg, greedy):
         if cfg.H:
             orc.mtp_shift_insert(host["tok"], host["hid"], o["accepted_len"], o["emitted"])
 
-    def timed(th, reps):
-        ts = []
-        for _ in range(reps):
-            t0 = time.perf_counter()
+    def timed(th, budget_s):
+        # whole steps repeated until the wall-clock budget is used (at least 3)
+        done, t0 = 0, time.perf_counter()
+        while done < 3 or time.perf_counter() - t0 < budget_s:
             step(th)
-            ts.append(time.perf_counter() - t0)
-        return statistics.median(ts)
+            done += 1
+        return (time.perf_counter() - t0) / done, done
 
-    t1 = timed(1, 3)
-    tn = timed(threads, 3)
+    t1, n1 = timed(1, 2.0)
+    tn, nn = timed(threads, 1.0)
     return {"value": round(rows / tn, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step ({cfg.B} sequences, {rows} rows of V={cfg.V}"
-                      + (", + MTP shift/hidden copy" if cfg.H else "") + "), median of 3",
+            "sample": f"{nn} full steps ({cfg.B} sequences, {rows} rows of V={cfg.V} each"
+                      + (", + MTP shift/hidden copy" if cfg.H else "") + f") on {threads} threads, "
+                      f"about {nn * tn * threads:.0f} s of CPU work; single thread: {n1} steps",
             "single_thread_rows_per_s": round(rows / t1, 1), "seconds_per_step": round(tn, 4),
             "cpu_model": cpu_model()}
 

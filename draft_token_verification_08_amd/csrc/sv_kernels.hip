@@ -721,9 +721,6 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __shared__ float s_m[kMaxSlots];
     __shared__ double s_S[kMaxSlots];
     __shared__ int s_idx[kMaxSlots];
-    __shared__ unsigned char s_acc[kMaxDraft];
-    __shared__ unsigned char s_oor[kMaxDraft];
-    __shared__ unsigned char s_badu[kMaxDraft];
 
     const int tid = threadIdx.x;
     const int n = p.n, V = p.V, NC = p.NC, S = p.S, L = si.L;
@@ -773,48 +770,59 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     }
     __syncthreads();
 
-    // 2. the acceptance test of every draft slot (evaluated in parallel; the
-    //    scan below uses them in order and stops at the first rejection)
-    if (tid < L) {
+    // 2. the acceptance tests: lane j of wave 0 tests draft slot j (n <= 64); a
+    //    wave ballot of the rejections and find-first-set give the first
+    //    rejection k (slots past k are evaluated but unused)
+    __shared__ int s_k;
+    __shared__ uint32_t s_flags;
+    if (tid < 64) {
         const int j = tid;
-        const int x = p.tokens[(size_t)b * n + j];
-        s_oor[j] = 0;
-        s_badu[j] = 0;
-        if (x < 0 || x >= V) {
-            s_oor[j] = 1;
-            s_acc[j] = 0;
-        } else if (si.greedy) {
-            s_acc[j] = (x == s_idx[j]);
-        } else {
-            const float zt = load_elem<DT>(row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, j), V), x);
-            const float zd = load_elem<DT>(row_ptr<DT>(p.draft, (long long)b * n + j, V), x);
-            uint32_t fl = 0;
-            const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + j], fl);
-            s_badu[j] = fl ? 1 : 0;
-            const int jd = n + 1 + j;
-            double ratio;
-            const bool pz = (zt == -INFINITY), qz = (zd == -INFINITY);
-            if (qz) ratio = pz ? 0.0 : INFINITY;
-            else if (pz) ratio = 0.0;
-            else {
-                // p/q = 2^((zt - m_t) c) / S_t  /  (2^((zd - m_d) c) / S_d)
-                const double lr = ((double)zt - (double)s_m[j]) * cd - ((double)zd - (double)s_m[jd]) * cd;
-                ratio = exp2(lr) * (s_S[jd] / s_S[j]);
+        bool rej = false, oor = false, badu = false;
+        if (j < L) {
+            const int x = p.tokens[(size_t)b * n + j];
+            if (x < 0 || x >= V) {
+                oor = true;
+                rej = true;
+            } else if (si.greedy) {
+                rej = (x != s_idx[j]);
+            } else {
+                const float zt = load_elem<DT>(row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, j), V), x);
+                const float zd = load_elem<DT>(row_ptr<DT>(p.draft, (long long)b * n + j, V), x);
+                uint32_t fl = 0;
+                const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + j], fl);
+                badu = (fl != 0);
+                const int jd = n + 1 + j;
+                double ratio;
+                const bool pz = (zt == -INFINITY), qz = (zd == -INFINITY);
+                if (qz) ratio = pz ? 0.0 : INFINITY;
+                else if (pz) ratio = 0.0;
+                else {
+                    // p/q = 2^((zt - m_t) c) / S_t  /  (2^((zd - m_d) c) / S_d)
+                    const double lr = ((double)zt - (double)s_m[j]) * cd - ((double)zd - (double)s_m[jd]) * cd;
+                    ratio = exp2(lr) * (s_S[jd] / s_S[j]);
+                }
+                rej = !(u < ratio);
             }
-            s_acc[j] = (u < ratio) ? 1 : 0;
+        }
+        const unsigned long long rmask = __ballot(rej);
+        const unsigned long long omask = __ballot(oor);
+        const unsigned long long bmask = __ballot(badu);
+        const int k = rmask ? __ffsll((long long)rmask) - 1 : L;
+        const unsigned long long upto = (k >= 63) ? ~0ull : ((2ull << k) - 1ull);  // slots 0..k
+        if (tid == 0) {
+            uint32_t f = si.flags;
+            if (omask & upto) f |= SV_FLAG_TOKEN_OOR;
+            if (bmask & upto) f |= SV_FLAG_BAD_UNIFORM;
+            s_k = k;
+            s_flags = f;
         }
     }
     __syncthreads();
 
-    // 3. first rejection, emitted tokens; sampling sequences: the draw descriptor
+    // 3. emitted tokens; sampling sequences: the draw descriptor
     if (tid == 0) {
-        uint32_t flags = si.flags;
-        int k = L;
-        for (int j = 0; j < L; ++j) {
-            if (s_oor[j]) flags |= SV_FLAG_TOKEN_OOR;
-            if (s_badu[j]) flags |= SV_FLAG_BAD_UNIFORM;
-            if (!s_acc[j]) { k = j; break; }
-        }
+        uint32_t flags = s_flags;
+        const int k = s_k;
         int32_t* e = p.emitted + (size_t)b * (n + 1);
         const int32_t* x = p.tokens + (size_t)b * n;
         for (int j = 0; j < k; ++j) e[j] = x[j];

@@ -117,3 +117,25 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="libspecverify.so not found"):
         _lib.lib()
+
+
+def test_vocabulary_limit():
+    assert sv.sv_workspace_bytes(4, 4, 1024 * 2048, sv.SV_BF16) > 0
+    assert sv.sv_workspace_bytes(4, 4, 1024 * 2048 + 1, sv.SV_BF16) == 0
+    assert sv.sv_workspace_bytes(4, 4, 1024 * 1024 + 1, sv.SV_F32) == 0
+    assert _sample(V=1024 * 2048 + 1) == sv.SV_EINVAL
+    assert _greedy(V=1024 * 1024 + 1) == sv.SV_EINVAL
+
+
+def test_sample_rows_host_checks():
+    f = sv.lib().sv_sample_rows
+    p = C.c_void_p(16)
+    ws = C.c_void_p(256)
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(z=p, dt=sv.SV_BF16, R=2, ri=NULL, T=p, u=p, B=4, V=100,
+                                                       tok=p, fl=NULL, ws=ws, wsb=1 << 20, s=NULL).items()]
+    assert f(*args(B=0)) == sv.SV_OK
+    assert f(*args(R=0)) == sv.SV_EINVAL
+    assert f(*args(z=NULL)) == sv.SV_EINVAL
+    assert f(*args(tok=NULL)) == sv.SV_EINVAL
+    assert f(*args(ri=C.c_void_p(18))) == sv.SV_EALIGN
+    assert f(*args(wsb=8)) == sv.SV_EWORKSPACE

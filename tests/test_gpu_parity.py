@@ -365,3 +365,40 @@ def test_mtp_parity(oracle, cid, B, H):
     sv.mtp_shift_insert(tok3, None, None, torch.as_tensor(acc, device=DEV), torch.as_tensor(emi, device=DEV))
     _sync()
     assert np.array_equal(tok3.cpu().numpy(), ref_tok)
+
+
+# ------------------------------------------------------------------ limits
+
+def test_max_draft_length(oracle):
+    """n = 64 (the largest draft length): ragged lengths up to 64, half the
+    sequences with identical draft/target rows so long prefixes are accepted."""
+    B, n, V = 10, sv.SV_MAX_DRAFT, 3001
+    d = synth.make(5, 64, device=DEV, B=B, V=V, n=n)
+    d["draft_lens"].copy_(torch.tensor([64, 64, 63, 0, 1, 32, 64, 17, 64, 5], dtype=torch.int32))
+    d["temperature"].copy_(torch.tensor([0.7, 1.0, 0.0, 0.7, 1.0, 0.7, 0.0, 1.0, 0.9, 0.7]))
+    for b in (0, 1, 6, 8):
+        d["draft"][b] = d["target"][b, :n]
+    acc, emi, lse, fl = run_sample(d)
+    ora = oracle_sample(oracle, d)
+    rep = compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), d["temperature"].cpu().numpy(), n)
+    assert rep.hard == 0, rep
+    check_lse(lse, ora)
+    assert acc[0] > 40 and acc[1] > 40     # identical rows accept (almost) everything
+    g_acc, g_emi, _ = run_greedy(d)
+    gor = oracle_greedy(oracle, d)
+    assert np.array_equal(g_acc, gor["accepted_len"]) and np.array_equal(g_emi, gor["emitted"])
+
+
+def test_max_vocab(oracle):
+    """V = 1024 tiles of 2048 bf16 elements, the largest vocabulary."""
+    B, n, V = 2, 1, 1024 * 2048
+    d = synth.make(4, 77, device=DEV, B=B, V=V, n=n, H=0)
+    acc, emi, lse, fl = run_sample(d)
+    ora = oracle_sample(oracle, d)
+    rep = compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), d["temperature"].cpu().numpy(), n)
+    assert rep.hard == 0, rep
+    check_lse(lse, ora)
+    g = synth.make(3, 78, device=DEV, B=B, V=V, n=n, H=0)
+    g_acc, g_emi, _ = run_greedy(g)
+    gor = oracle_greedy(oracle, g)
+    assert np.array_equal(g_acc, gor["accepted_len"]) and np.array_equal(g_emi, gor["emitted"])
