@@ -978,18 +978,38 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     const int tile0 = c * kDrawTiles;
     const int cnt = min(kDrawTiles, NT - tile0);
     __shared__ float s_r[kWaves][kDrawTiles], s_p[kWaves][kDrawTiles];
+    // every load of the chunk is issued before any is used (one memory round trip)
+    float zt[kDrawTiles][kVec], zd[kDrawTiles][kVec];
+    if constexpr (ALIGNED) {
+        uint4 rt[kDrawTiles], rd[kDrawTiles];
+#pragma unroll
+        for (int k = 0; k < kDrawTiles; ++k) {
+            const int e0 = (tile0 + k) * kTile + tid * kVec;
+            const bool ok = k < cnt && e0 < V;
+            rt[k] = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+            rd[k] = ok ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+        }
+#pragma unroll
+        for (int k = 0; k < kDrawTiles; ++k) {
+            unpack<DT>(rt[k], zt[k]);
+            unpack<DT>(rd[k], zd[k]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kDrawTiles; ++k) {
+            const int e0 = (tile0 + k) * kTile + tid * kVec;
+            const int lim = (k < cnt) ? V : 0;
+            load_vec<DT, ALIGNED>(trow, e0, lim, zt[k]);
+            load_vec<DT, ALIGNED>(drow, e0, lim, zd[k]);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kDrawTiles; ++k) {
-        float zt[kVec], zd[kVec];
-        const int e0 = (tile0 + k) * kTile + tid * kVec;
-        const int lim = (k < cnt) ? V : 0;
-        load_vec<DT, ALIGNED>(trow, e0, lim, zt);
-        load_vec<DT, ALIGNED>(drow, e0, lim, zd);
         float ar = 0.f, ap = 0.f;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            ar += w_residual(d, zt[e], zd[e]);  // absent elements read -inf: weight 0
-            ap += w_target(d, zt[e]);
+            ar += w_residual(d, zt[k][e], zd[k][e]);  // absent elements read -inf: weight 0
+            ap += w_target(d, zt[k][e]);
         }
         ar = wave_sum(ar);
         ap = wave_sum(ap);
