@@ -2,9 +2,10 @@
 
 Default workload (the headline): greedy verify + MTP shift/insert at B=256
 sequences, n=4 drafts, V=128256 bf16 logits, hidden size 8192.  One step =
-spec_verify_greedy() over the [256, 5, 128256] target logits followed by
-mtp_shift_insert() of the [256, 5] token buffer and the [256, 5, 8192] hidden
-states.  Inputs are synthetic (seeded), resident in HBM, and rotate over
+spec_verify_greedy_mtp(): the verification of the [256, 5, 128256] target
+logits with the shift/insert of the [256, 5] token buffer and the carry of the
+[256, 5, 8192] hidden states fused in (--unfused: spec_verify_greedy() then
+mtp_shift_insert(), two launches).  Inputs are synthetic (seeded), resident in HBM, and rotate over
 several independent copies so that no step finds its inputs in the 256 MB
 last-level cache.
 
@@ -12,7 +13,7 @@ Prints one JSON line: verified vocab rows/s (value), HBM GB/s and % of the
 8 TB/s peak, a roofline entry for the dominant kernel (the verify kernel,
 timed with HIP events on its stream), and the CPU oracle timed on host cores.
 
-    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--no-cpu] [--unfused]
 """
 from __future__ import annotations
 
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=303)
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate verify and mtp_shift_insert calls instead of the fused call")
     return ap.parse_args()
 
 
@@ -102,7 +105,20 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     # calls marshalled once per input copy (the C entry points are re-issued as is)
+    fused = bool(cfg.H) and not args.unfused
     for d in data:
+        if fused:
+            if greedy:
+                d["verify"] = sv.prepare_spec_verify_greedy_mtp(d["target"], d["draft_tokens"], d["draft_lens"],
+                                                                d["acc"], d["emi"], d["tokens"], d["hidden"],
+                                                                d["hidden_dst"], wsbuf)
+            else:
+                d["verify"] = sv.prepare_spec_verify_sample_mtp(d["target"], d["draft"], d["draft_tokens"],
+                                                                d["draft_lens"], d["temperature"], d["uniforms"],
+                                                                d["acc"], d["emi"], d["tokens"], d["hidden"],
+                                                                d["hidden_dst"], wsbuf)
+            d["mtp"] = lambda: None
+            continue
         if greedy:
             d["verify"] = sv.prepare_spec_verify_greedy(d["target"], d["draft_tokens"], d["draft_lens"], d["acc"],
                                                         d["emi"], wsbuf)
@@ -147,7 +163,7 @@ def main():
     ev_v = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for i in range(0, K, EVERY)}
     ev_m = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for i in range(EVERY // 2, K, EVERY)}
+            for i in range(EVERY // 2, K, EVERY)} if cfg.H and not fused else {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -171,13 +187,17 @@ def main():
     mtp_ms = [a.elapsed_time(b) for a, b in ev_m.values()] or [0.0]
     ms_per_step = elapsed * 1e3 / K
     rows_total = sum(rows_per_step[i % sets] for i in range(K))
-    bytes_total = sum(verify_bytes[i % sets] + mtp_bytes for i in range(K))
+    step_mtp_bytes = (2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4) if fused else mtp_bytes
+    bytes_total = sum(verify_bytes[i % sets] + step_mtp_bytes for i in range(K))
     value = rows_total / elapsed
     gbps = bytes_total / elapsed / 1e9
     v_avg_ms = statistics.fmean(verify_ms)
-    v_bytes = statistics.fmean(verify_bytes[i % sets] for i in ev_v)
+    # fused: the hidden states and the token buffer cross HBM once each way (the
+    # verify outputs are not read back)
+    fused_mtp_bytes = 2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4
+    v_bytes = statistics.fmean(verify_bytes[i % sets] + (fused_mtp_bytes if fused else 0) for i in ev_v)
     v_gbps = v_bytes / (v_avg_ms * 1e-3) / 1e9
-    m_avg_ms = statistics.fmean(mtp_ms) if cfg.H else 0.0
+    m_avg_ms = statistics.fmean(mtp_ms) if cfg.H and not fused else 0.0
     mean_acc = float(torch.stack([d["acc"].float().mean() for d in data]).mean())
 
     # a bare event pair on the same stream: the queue time an event pair adds to
@@ -191,7 +211,7 @@ def main():
     torch.cuda.synchronize()
     event_pair_us = statistics.median(a.elapsed_time(b2) for a, b2 in bare) * 1e3
 
-    kernel = "k_stats_greedy" if greedy else "k_stats_sample+k_draw"
+    kernel = ("k_stats_greedy" if greedy else "k_stats_sample+k_draw") + ("+mtp_fused" if fused else "")
     workload = cfg.name
     traffic = measured_traffic(kernel, workload)
 
@@ -208,7 +228,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic (seeded; inputs resident in HBM, rotated over %d copies)" % sets,
-        "config": {"workload": ("greedy verify + MTP shift/insert" if greedy else "sampling verify")
+        "config": {"workload": ("greedy verify" if greedy else "sampling verify")
+                   + (" + MTP shift/insert" + (" (fused call)" if fused else " (two calls)") if cfg.H else "")
                    + f" ({cfg.name})", "B": cfg.B, "n": cfg.n, "V": cfg.V, "H": cfg.H,
                    "logits": "bf16" if es == 2 else "f32", "parallelism": "none (1 GPU)"},
         "hbm_gbps": round(gbps, 1),

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     SV_FLAG_BAD_UNIFORM, SV_FLAG_LEN_CLAMPED, SV_FLAG_ROW_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_ZERO_RESIDUAL,
     SV_MAX_DRAFT,
     SV_OK, Prepared, SpecVerifyError, Workspace, lib, mtp_shift_insert, prepare_mtp_shift_insert,
-    prepare_spec_verify_greedy, prepare_spec_verify_sample, spec_verify_greedy, spec_verify_sample,
-    sv_sample_rows, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
+    prepare_spec_verify_greedy, prepare_spec_verify_greedy_mtp, prepare_spec_verify_sample,
+    prepare_spec_verify_sample_mtp, spec_verify_greedy, spec_verify_greedy_mtp, spec_verify_sample,
+    spec_verify_sample_mtp, sv_sample_rows, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
 )

@@ -56,6 +56,11 @@ def lib():
     L.spec_verify_sample.restype = i
     L.spec_verify_greedy.argtypes = [vp, i, vp, vp, i, i, i, vp, vp, vp, vp, sz, vp]
     L.spec_verify_greedy.restype = i
+    L.spec_verify_sample_mtp.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, vp,
+                                         sz, vp]
+    L.spec_verify_sample_mtp.restype = i
+    L.spec_verify_greedy_mtp.argtypes = [vp, i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, i, vp, sz, vp]
+    L.spec_verify_greedy_mtp.restype = i
     L.mtp_shift_insert.argtypes = [vp, vp, vp, i, vp, vp, i, i, vp]
     L.mtp_shift_insert.restype = i
     L.sv_sample_rows.argtypes = [vp, i, i, vp, vp, vp, i, i, vp, vp, vp, sz, vp]
@@ -207,6 +212,88 @@ def spec_verify_greedy(target_logits, draft_tokens, draft_lens, *, accepted_len=
     return accepted_len, emitted
 
 
+def _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev) -> int:
+    """Checks the MTP tensors of a call; returns H (0 without hidden states)."""
+    _check(tokens, "tokens", torch.int32, (B, n1), dev)
+    if hidden_src is None and hidden_dst is None:
+        return 0
+    if hidden_src is None or hidden_dst is None:
+        raise ValueError("hidden_src and hidden_dst must both be given or both be None")
+    H = hidden_src.shape[-1]
+    _check(hidden_src, "hidden_src", torch.bfloat16, (B, n1, H), dev)
+    _check(hidden_dst, "hidden_dst", torch.bfloat16, (B, n1, H), dev)
+    return H
+
+
+def spec_verify_greedy_mtp(target_logits, draft_tokens, draft_lens, tokens, hidden_src, hidden_dst, *,
+                           accepted_len=None, emitted=None, err_flags=None, workspace=None, stream=None):
+    """Greedy verify and the MTP shift/insert of the same step in one call (see
+    include/specverify.h).  Returns (accepted_len, emitted); tokens is updated in
+    place and hidden_dst receives the carried hidden states."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n1), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, n, V, dt)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("spec_verify_greedy_mtp", _ptr(target_logits), dt, _ptr(draft_tokens), _ptr(draft_lens), B, n, V,
+          _ptr(accepted_len), _ptr(emitted), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst),
+          H, _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted
+
+
+def spec_verify_sample_mtp(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms, tokens,
+                           hidden_src, hidden_dst, *, accepted_len=None, emitted=None, row_lse=None,
+                           err_flags=None, workspace=None, stream=None):
+    """Verify-and-sample and the MTP shift/insert of the same step in one call
+    (see include/specverify.h).  Returns (accepted_len, emitted)."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n1), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    if row_lse is not None:
+        _check(row_lse, "row_lse", torch.float32, (B, 2 * n + 1), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, n, V, dt)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("spec_verify_sample_mtp", _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+          _ptr(draft_lens), _ptr(temperature), _ptr(uniforms), B, n, V, _ptr(accepted_len), _ptr(emitted),
+          _ptr(row_lse), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(workspace),
+          workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted
+
+
 def mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitted, *, stream=None):
     """MTP shift/insert (see include/specverify.h); tokens is updated in place,
     hidden_dst receives the carried hidden states."""
@@ -318,6 +405,51 @@ def prepare_mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitt
     args = (_ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(accepted_len), _ptr(emitted), B, n1 - 1,
             _stream(stream, dev))
     return Prepared("mtp_shift_insert", args, (tokens, hidden_src, hidden_dst, accepted_len, emitted))
+
+
+def prepare_spec_verify_greedy_mtp(target_logits, draft_tokens, draft_lens, accepted_len, emitted, tokens,
+                                   hidden_src, hidden_dst, workspace, err_flags=None, stream=None) -> Prepared:
+    B, n1, V = target_logits.shape
+    dev = target_logits.device
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n1 - 1), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    args = (_ptr(target_logits), _dt(target_logits), _ptr(draft_tokens), _ptr(draft_lens), B, n1 - 1, V,
+            _ptr(accepted_len), _ptr(emitted), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst),
+            H, _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return Prepared("spec_verify_greedy_mtp", args, (target_logits, draft_tokens, draft_lens, accepted_len,
+                                                      emitted, tokens, hidden_src, hidden_dst, workspace,
+                                                      err_flags))
+
+
+def prepare_spec_verify_sample_mtp(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms,
+                                   accepted_len, emitted, tokens, hidden_src, hidden_dst, workspace, row_lse=None,
+                                   err_flags=None, stream=None) -> Prepared:
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    args = (_ptr(target_logits), _ptr(draft_logits), _dt(target_logits), _ptr(draft_tokens), _ptr(draft_lens),
+            _ptr(temperature), _ptr(uniforms), B, n, V, _ptr(accepted_len), _ptr(emitted), _ptr(row_lse),
+            _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(workspace),
+            workspace.numel(), _stream(stream, dev))
+    return Prepared("spec_verify_sample_mtp", args, (target_logits, draft_logits, draft_tokens, draft_lens,
+                                                      temperature, uniforms, accepted_len, emitted, tokens,
+                                                      hidden_src, hidden_dst, workspace, row_lse, err_flags))
 
 
 # ------------------------------------------------------------------ standard sampling of chosen rows

@@ -85,6 +85,91 @@ bool rows_aligned(const void* base, int V, sv_dtype_t dt) {
     return aligned_to(base, 16) && ((size_t)V * elem_bytes(dt)) % 16 == 0;
 }
 
+// Byte range of a caller buffer, for the aliasing checks of the fused calls.
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool overlaps_any(Span a, const Span* others, int k) {
+    for (int i = 0; i < k; ++i)
+        if (overlap(a, others[i])) return true;
+    return false;
+}
+
+// Hidden-state element count B * (n+1) * H, or -1 when it does not fit the
+// byte range of the address space.
+long long hidden_elems(int B, int n, int H) {
+    const long long rows = (long long)B * (n + 1);
+    if (H <= 0 || rows == 0) return 0;
+    if (rows > (1ll << 62) / 2 / H) return -1;
+    return rows * H;
+}
+
+// The MTP arguments of a fused verify + MTP call.
+struct MtpArgs {
+    int32_t* tokens;
+    const void* hsrc;
+    void* hdst;
+    int H;
+};
+
+// Checks shared by mtp_shift_insert() and the fused calls; *elems receives the
+// hidden element count (0 when there is nothing to copy).
+sv_status_t check_mtp(const MtpArgs& m, int B, int n, long long* elems) {
+    if (m.H < 0) return SV_EINVAL;
+    if (!m.tokens) return SV_EINVAL;
+    if ((m.hsrc == nullptr) != (m.hdst == nullptr)) return SV_EINVAL;
+    if (m.hsrc && m.H < 1) return SV_EINVAL;
+    if (!aligned_to(m.tokens, 4) || !aligned_to(m.hsrc, 2) || !aligned_to(m.hdst, 2)) return SV_EALIGN;
+    const long long e = m.hsrc ? hidden_elems(B, n, m.H) : 0;
+    if (e < 0) return SV_EINVAL;
+    if (m.hsrc && m.hsrc != m.hdst && overlap(Span{m.hsrc, (size_t)e * 2}, Span{m.hdst, (size_t)e * 2}))
+        return SV_EINVAL;  // partial overlap of the hidden buffers
+    *elems = (m.hsrc == m.hdst) ? 0 : e;
+    return SV_OK;
+}
+
+// Launch plan of the MTP part of a fused call: copy and token shift inside the
+// verify kernels when the hidden buffers allow 16-byte vectors, else the
+// separate MTP kernel after them.
+struct MtpPlan {
+    bool fused;
+    sv::MtpFuse f;
+    sv::MtpParams sep;
+    bool sep_aligned;
+};
+
+MtpPlan plan_mtp(const MtpArgs& m, long long elems, const int32_t* accepted_len, const int32_t* emitted,
+                 int B, int n) {
+    MtpPlan pl{};
+    const bool vec_ok = elems == 0 || (aligned_to(m.hsrc, 16) && aligned_to(m.hdst, 16) && elems % 8 == 0);
+    pl.fused = vec_ok;
+    if (pl.fused) {
+        pl.f.tokens = m.tokens;
+        pl.f.hsrc = elems > 0 ? m.hsrc : nullptr;
+        pl.f.hdst = elems > 0 ? m.hdst : nullptr;
+        pl.f.nvec = elems / 8;
+    } else {
+        pl.sep.tokens = m.tokens;
+        pl.sep.hsrc = m.hsrc;
+        pl.sep.hdst = m.hdst;
+        pl.sep.hidden_elems = elems;
+        pl.sep.acc = accepted_len;
+        pl.sep.emitted = emitted;
+        pl.sep.B = B;
+        pl.sep.n = n;
+        pl.sep_aligned = aligned_to(m.hsrc, 16) && aligned_to(m.hdst, 16);
+    }
+    return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,12 +202,15 @@ const char* sv_status_string(sv_status_t s) {
 
 const char* sv_last_hip_error(void) { return g_hip_error; }
 
-sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
-                               const int32_t* draft_tokens, const int32_t* draft_lens,
-                               const float* temperature, const float* uniforms, int B, int n, int V,
-                               int32_t* accepted_len, int32_t* emitted, float* row_lse,
-                               uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+sv_status_t verify_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                          const int32_t* draft_tokens, const int32_t* draft_lens, const float* temperature,
+                          const float* uniforms, int B, int n, int V, int32_t* accepted_len, int32_t* emitted,
+                          float* row_lse, uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                          void* stream, const MtpArgs* mtp) {
     if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_lens || !temperature || !uniforms || !accepted_len || !emitted ||
@@ -141,6 +229,30 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     const int S = 2 * n + 1;
     if (!grid_ok((long long)B * S * L.NC) || !grid_ok((long long)B * L.NCd)) return SV_EINVAL;
 
+    MtpPlan pl{};
+    if (mtp) {
+        long long elems = 0;
+        const sv_status_t ms = check_mtp(*mtp, B, n, &elems);
+        if (ms != SV_OK) return ms;
+        const size_t es_ = elem_bytes(dt);
+        const Span tok{mtp->tokens, (size_t)B * (n + 1) * 4};
+        const Span others[] = {{target_logits, (size_t)B * (n + 1) * V * es_},
+                               {draft_logits, (size_t)B * n * V * es_},
+                               {draft_tokens, (size_t)B * n * 4},
+                               {draft_lens, (size_t)B * 4},
+                               {temperature, (size_t)B * 4},
+                               {uniforms, (size_t)B * (n + 1) * 4},
+                               {accepted_len, (size_t)B * 4},
+                               {emitted, (size_t)B * (n + 1) * 4},
+                               {row_lse, row_lse ? (size_t)B * (2 * n + 1) * 4 : 0},
+                               {err_flags, err_flags ? 4u : 0u},
+                               {workspace, workspace_bytes},
+                               tok};
+        constexpr int kOthers = sizeof(others) / sizeof(others[0]);
+        if (overlaps_any(tok, others, kOthers - 1)) return SV_EINVAL;
+        if (elems > 0 && overlaps_any(Span{mtp->hdst, (size_t)elems * 2}, others, kOthers)) return SV_EINVAL;
+        pl = plan_mtp(*mtp, elems, accepted_len, emitted, B, n);
+    }
     const bool aligned = rows_aligned(target_logits, V, dt) && (!draft_logits || aligned_to(draft_logits, 16));
     hipStream_t s = (hipStream_t)stream;
 
@@ -163,6 +275,7 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
     sp.R = n + 1;
     sp.row_index = nullptr;
+    if (mtp && pl.fused) sp.mtp = pl.f;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
 
@@ -179,15 +292,20 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
     dp.dres = at<float>(workspace, L.off_dres);
     dp.dp = at<float>(workspace, L.off_dp);
     dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+    if (mtp && pl.fused) dp.mtp_tokens = pl.f.tokens;
     e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
+    if (mtp && !pl.fused) {
+        e = sv::launch_mtp(pl.sep, pl.sep_aligned, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     return SV_OK;
 }
 
-sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
-                               const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
-                               int32_t* emitted, uint32_t* err_flags, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+sv_status_t verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                          const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len, int32_t* emitted,
+                          uint32_t* err_flags, void* workspace, size_t workspace_bytes, void* stream,
+                          const MtpArgs* mtp) {
     if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_lens || !accepted_len || !emitted || (n > 0 && !draft_tokens))
@@ -202,6 +320,26 @@ sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const i
     if (!aligned_to(workspace, 16)) return SV_EALIGN;
     const int S = n + 1;
     if (!grid_ok((long long)B * S * L.NC)) return SV_EINVAL;
+    MtpPlan pl{};
+    if (mtp) {
+        long long elems = 0;
+        const sv_status_t ms = check_mtp(*mtp, B, n, &elems);
+        if (ms != SV_OK) return ms;
+        const Span tok{mtp->tokens, (size_t)B * (n + 1) * 4};
+        const Span others[] = {{target_logits, (size_t)B * (n + 1) * V * es},
+                               {draft_tokens, (size_t)B * n * 4},
+                               {draft_lens, (size_t)B * 4},
+                               {accepted_len, (size_t)B * 4},
+                               {emitted, (size_t)B * (n + 1) * 4},
+                               {err_flags, err_flags ? 4u : 0u},
+                               {workspace, workspace_bytes},
+                               tok};
+        constexpr int kOthers = sizeof(others) / sizeof(others[0]);
+        if (overlaps_any(tok, others, kOthers - 1)) return SV_EINVAL;
+        if (elems > 0 && overlaps_any(Span{mtp->hdst, (size_t)elems * 2}, others, kOthers)) return SV_EINVAL;
+        pl = plan_mtp(*mtp, elems, accepted_len, emitted, B, n);
+    }
+    hipStream_t s = (hipStream_t)stream;
 
     sv::StatsParams sp{};
     sp.target = target_logits;
@@ -217,9 +355,60 @@ sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const i
     sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
     sp.R = n + 1;
     sp.row_index = nullptr;
+    if (mtp && pl.fused) sp.mtp = pl.f;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kGreedy,
-                                    rows_aligned(target_logits, V, dt), (hipStream_t)stream);
-    return e == hipSuccess ? SV_OK : hip_fail(e);
+                                    rows_aligned(target_logits, V, dt), s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (mtp && !pl.fused) {
+        e = sv::launch_mtp(pl.sep, pl.sep_aligned, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                               const int32_t* draft_tokens, const int32_t* draft_lens,
+                               const float* temperature, const float* uniforms, int B, int n, int V,
+                               int32_t* accepted_len, int32_t* emitted, float* row_lse,
+                               uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
+                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream,
+                         nullptr);
+}
+
+sv_status_t spec_verify_sample_mtp(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                                   const int32_t* draft_tokens, const int32_t* draft_lens,
+                                   const float* temperature, const float* uniforms, int B, int n, int V,
+                                   int32_t* accepted_len, int32_t* emitted, float* row_lse,
+                                   uint32_t* err_flags, int32_t* tokens, const void* hidden_src,
+                                   void* hidden_dst, int H, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    const MtpArgs m{tokens, hidden_src, hidden_dst, H};
+    return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
+                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream, &m);
+}
+
+sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                               const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
+                               int32_t* emitted, uint32_t* err_flags, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return verify_greedy(target_logits, dt, draft_tokens, draft_lens, B, n, V, accepted_len, emitted, err_flags,
+                         workspace, workspace_bytes, stream, nullptr);
+}
+
+sv_status_t spec_verify_greedy_mtp(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                                   const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
+                                   int32_t* emitted, uint32_t* err_flags, int32_t* tokens,
+                                   const void* hidden_src, void* hidden_dst, int H, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    const MtpArgs m{tokens, hidden_src, hidden_dst, H};
+    return verify_greedy(target_logits, dt, draft_tokens, draft_lens, B, n, V, accepted_len, emitted, err_flags,
+                         workspace, workspace_bytes, stream, &m);
 }
 
 sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32_t* row_index,
@@ -284,17 +473,16 @@ sv_status_t mtp_shift_insert(int32_t* tokens, const void* hidden_src, void* hidd
                              void* stream) {
     if (B < 0 || n < 0 || n > sv::kMaxDraft || H < 0) return SV_EINVAL;
     if (B == 0) return SV_OK;
-    if (!tokens || !accepted_len || !emitted) return SV_EINVAL;
-    if ((hidden_src == nullptr) != (hidden_dst == nullptr)) return SV_EINVAL;
-    if (hidden_src && H < 1) return SV_EINVAL;
-    if (!aligned_to(tokens, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) ||
-        !aligned_to(hidden_src, 2) || !aligned_to(hidden_dst, 2))
-        return SV_EALIGN;
+    if (!accepted_len || !emitted) return SV_EINVAL;
+    long long elems = 0;
+    const sv_status_t ms = check_mtp(MtpArgs{tokens, hidden_src, hidden_dst, H}, B, n, &elems);
+    if (ms != SV_OK) return ms;
+    if (!aligned_to(accepted_len, 4) || !aligned_to(emitted, 4)) return SV_EALIGN;
     sv::MtpParams mp{};
     mp.tokens = tokens;
     mp.hsrc = hidden_src;
     mp.hdst = hidden_dst;
-    mp.hidden_elems = hidden_src ? (long long)B * (n + 1) * H : 0;
+    mp.hidden_elems = hidden_src ? hidden_elems(B, n, H) : 0;
     mp.acc = accepted_len;
     mp.emitted = emitted;
     mp.B = B;

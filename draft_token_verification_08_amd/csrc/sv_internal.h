@@ -71,6 +71,16 @@ struct Layout {
     size_t bytes;
 };
 
+// MTP bookkeeping fused into the verify kernels: the token shift/insert and the
+// hidden-state carry of one decode step.  tokens == nullptr disables it; hsrc ==
+// nullptr (or nvec == 0) skips the copy.
+struct MtpFuse {
+    int32_t* tokens;          // [B][n+1] or nullptr
+    const void* hsrc;         // nvec 16-byte vectors (bf16 hidden states), or nullptr
+    void* hdst;
+    long long nvec;
+};
+
 struct StatsParams {
     const void* target;       // [B][n+1][V]
     const void* draft;        // [B][n][V] or nullptr
@@ -90,6 +100,7 @@ struct StatsParams {
     Partial* part;
     uint32_t* cnt;
     DrawDesc* desc;
+    MtpFuse mtp;              // zero: not fused
 };
 
 struct DrawParams {
@@ -105,6 +116,7 @@ struct DrawParams {
     float* dres;
     float* dp;
     uint32_t* cnt;
+    int32_t* mtp_tokens;      // [B][n+1] or nullptr: the drawn token is also written to slot k
 };
 
 struct MtpParams {

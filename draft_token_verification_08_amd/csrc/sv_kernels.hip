@@ -15,12 +15,18 @@
 //            workgroup of a sequence to finish (arrival counter) merges the
 //            partials, runs the acceptance tests in order, finds the first
 //            rejection and writes the accepted length and emitted tokens.
-//   k_draw   sampling sequences only: one workgroup per (sequence, draw chunk)
-//            sums the draw weights of its chunk (residual max(0, p_k - q_k) or
-//            p_L); the last workgroup of the sequence picks the chunk holding
-//            u*Z, re-reads that chunk only, and finds the token with an LDS
-//            block prefix sum.
+//            Target row L of a sampling sequence keeps per-tile partials for a
+//            bonus draw.
+//   k_draw   sampling sequences only.  Bonus draws (all drafts accepted): one
+//            workgroup picks the tile of row L holding u*Z from the tile
+//            partials and scans that tile.  Residual draws: one workgroup per
+//            (sequence, draw chunk) sums max(0, p_k - q_k) per tile of its
+//            chunk; the last workgroup of the sequence picks the tile holding
+//            u*Z and scans only that tile.
 //   k_mtp    token shift + insert and the hidden-state carry (16-byte copies).
+//   The fused verify + MTP calls run no k_mtp: the decision shifts the token
+//   buffer, the drawn token is written to both outputs, and every k_stats
+//   workgroup copies an equal share of the hidden states after its rows.
 //
 // Determinism: every reduction has a fixed order (DPP/shuffle trees, then
 // waves in order, then chunks in order); no floating-point atomics.
@@ -32,6 +38,12 @@
 
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
+#endif
+#ifndef SV_LOAD_FENCE
+#define SV_LOAD_FENCE 0
+#endif
+#ifndef SV_PIPELINE
+#define SV_PIPELINE 0
 #endif
 #ifndef SV_MS_UNROLL
 #define SV_MS_UNROLL 4
@@ -52,6 +64,14 @@ namespace sv {
 
 // one 16-byte load of streamed logits (read once: optionally non-temporal)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Keeps the scheduler from moving the consumers of a group of loads above the
+// group: every load of the group is in flight before the first wait.
+#if SV_LOAD_FENCE
+#define SV_AFTER_LOADS() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SV_AFTER_LOADS() ((void)0)
+#endif
+
 __device__ __forceinline__ uint4 ld16(const uint4* p) {
 #if SV_NT_LOAD
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -327,10 +347,30 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
         int bestv = -1;
         uint4 bestw = make_uint4(0, 0, 0, 0);
         int v = v0 + tid;
+#if SV_PIPELINE
+        uint4 nxt[U];
+        bool more = v + (U - 1) * kThreads < v1;
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + u * kThreads);
+        }
+        while (more) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = nxt[u];
+            more = v + U * kThreads + (U - 1) * kThreads < v1;
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + U * kThreads + u * kThreads);
+            }
+            SV_AFTER_LOADS();
+#else
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
+            SV_AFTER_LOADS();
+#endif
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float f[kVec];
@@ -344,6 +384,9 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
                     bestw = w[u];
                 }
             }
+#if SV_PIPELINE
+            v += U * kThreads;
+#endif
         }
         for (; v < v1; v += kThreads) {
             const uint4 w = ld16(vrow + v);
@@ -397,10 +440,31 @@ __device__ MS thread_ms(const void* row, int lo, int hi, float c) {
         const int v0 = lo / kVec, v1 = hi / kVec;
         constexpr int U = SV_MS_UNROLL;
         int v = v0 + tid;
+#if SV_PIPELINE
+        uint4 nxt[U];
+        bool more = v + (U - 1) * kThreads < v1;
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + u * kThreads);
+        }
+        while (more) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = nxt[u];
+            more = v + U * kThreads + (U - 1) * kThreads < v1;
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + U * kThreads + u * kThreads);
+            }
+            v += U * kThreads;
+            SV_AFTER_LOADS();
+#else
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
+            SV_AFTER_LOADS();
+#endif
             float f[U][kVec];
 #pragma unroll
             for (int u = 0; u < U; ++u) unpack<DT>(w[u], f[u]);
@@ -664,6 +728,58 @@ __device__ __forceinline__ int scan_tile(const DrawDesc& d, bool residual, const
     return y;
 }
 
+// --------------------------------------------------------------- MTP helpers
+
+__device__ __forceinline__ u32x4 ld_copy(const u32x4* p) {
+#if SV_NT_COPY
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ void st_copy(u32x4* p, u32x4 v) {
+#if SV_NT_COPY
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// Copy vectors [v0, v1) of src to dst with the workgroup: coalesced, four
+// 16-byte loads in flight per thread.
+__device__ __forceinline__ void copy_range(const u32x4* src, u32x4* dst, long long v0, long long v1) {
+    long long v = v0 + threadIdx.x;
+#pragma unroll 1
+    for (; v + 3 * kThreads < v1; v += 4 * kThreads) {
+        const u32x4 w0 = ld_copy(src + v), w1 = ld_copy(src + v + kThreads);
+        const u32x4 w2 = ld_copy(src + v + 2 * kThreads), w3 = ld_copy(src + v + 3 * kThreads);
+        st_copy(dst + v, w0);
+        st_copy(dst + v + kThreads, w1);
+        st_copy(dst + v + 2 * kThreads, w2);
+        st_copy(dst + v + 3 * kThreads, w3);
+    }
+    for (; v < v1; v += kThreads) st_copy(dst + v, ld_copy(src + v));
+}
+
+// Workgroup `part` of `nparts` copies its share of the hidden states: whole
+// units of kThreads vectors, split as evenly as the unit count allows.
+__device__ __forceinline__ void copy_share(const MtpFuse& m, long long part, long long nparts) {
+    if (m.hsrc == nullptr || m.nvec <= 0) return;
+    const long long units = (m.nvec + kThreads - 1) / kThreads;
+    const long long q = units / nparts, r = units % nparts;
+    const long long u0 = q * part + (part < r ? part : r);
+    const long long u1 = u0 + q + (part < r ? 1 : 0);
+    const long long v0 = u0 * kThreads;
+    const long long v1 = u1 * kThreads < m.nvec ? u1 * kThreads : m.nvec;
+    if (v0 < v1) copy_range((const u32x4*)m.hsrc, (u32x4*)m.hdst, v0, v1);
+}
+
+// Token shift of sequence b (slot i <- slot i + 1 for i < n; slot n kept).
+__device__ __forceinline__ void shift_tokens(int32_t* tokens, int b, int n) {
+    int32_t* t = tokens + (size_t)b * (n + 1);
+    for (int i = 0; i < n; ++i) t[i] = t[i + 1];
+}
+
 // --------------------------------------------------------------- decision helpers
 
 __device__ __forceinline__ int clamp_len(int L, int n, uint32_t& flags) {
@@ -828,8 +944,10 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
         for (int j = 0; j < k; ++j) e[j] = x[j];
         for (int j = k + 1; j <= n; ++j) e[j] = -1;
         p.acc[b] = k;
+        if (p.mtp.tokens) shift_tokens(p.mtp.tokens, b, n);  // fused MTP step
         if (si.greedy) {
             e[k] = s_idx[k];
+            if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + k] = s_idx[k];
         } else {
             const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + n], flags);
             // the draw (residual after a rejection, bonus after full acceptance)
@@ -865,7 +983,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     const SeqInfo si = seq_info<MODE>(p, b);
     const bool target_row = slot <= n;
     const bool needed = target_row ? (slot <= si.L) : (!si.greedy && slot - n - 1 < si.L);
-    if (!needed) return;
+    if (!needed) {
+        copy_share(p.mtp, bid, gridDim.x);
+        return;
+    }
     const unsigned expected = (unsigned)p.NC * (unsigned)(si.L + 1 + (si.greedy ? 0 : si.L));
 
     const void* row = target_row ? row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, slot), p.V)
@@ -895,8 +1016,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
         }
     }
     __syncthreads();
-    if (!s_last) return;
-    decide<DT, MODE, ALIGNED>(p, b, si);
+    if (s_last) decide<DT, MODE, ALIGNED>(p, b, si);
+    // fused MTP step: every workgroup of the grid carries an equal share of the
+    // hidden states once its row chunk is done (the copy's writes then come as
+    // one burst at the end of the read stream instead of interleaved with it)
+    copy_share(p.mtp, bid, gridDim.x);
 }
 
 // Draw from the target row's own distribution (the bonus token from p_L after
@@ -967,6 +1091,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
         for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;  // used: leave zero
         if (tid == 0) {
             p.emitted[(size_t)b * (n + 1) + d.k] = y;
+            if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.k] = y;
             p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         }
         return;
@@ -1098,27 +1223,13 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;
     if (tid == 0) {
         p.emitted[(size_t)b * (n + 1) + d.k] = y;
+        if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.k] = y;
         p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         xchg32(&p.cnt[b], 0u);
     }
 }
 
 // --------------------------------------------------------------- MTP shift / insert
-
-__device__ __forceinline__ u32x4 ld_copy(const u32x4* p) {
-#if SV_NT_COPY
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
-}
-__device__ __forceinline__ void st_copy(u32x4* p, u32x4 v) {
-#if SV_NT_COPY
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
-}
 
 template <bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
@@ -1129,7 +1240,7 @@ __global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
         // before it is overwritten), then the target's next token at slot a
         const int n = p.n;
         int32_t* t = p.tokens + gid * (n + 1);
-        for (int i = 0; i < n; ++i) t[i] = t[i + 1];
+        shift_tokens(p.tokens, (int)gid, n);
         int a = p.acc[gid];
         a = a < 0 ? 0 : (a > n ? n : a);
         t[a] = p.emitted[gid * (n + 1) + a];
@@ -1142,20 +1253,8 @@ __global__ __launch_bounds__(kThreads) void k_mtp(MtpParams p) {
         const u32x4* src = (const u32x4*)p.hsrc;
         u32x4* dst = (u32x4*)p.hdst;
         constexpr int kPer = kThreads * SV_COPY_VECS;
-        for (long long base = (long long)blockIdx.x * kPer; base < nvec; base += (long long)gridDim.x * kPer) {
-            long long v = base + threadIdx.x;
-            const long long end = (base + kPer < nvec) ? base + kPer : nvec;
-#pragma unroll 1
-            for (; v + 3 * kThreads < end; v += 4 * kThreads) {
-                const u32x4 w0 = ld_copy(src + v), w1 = ld_copy(src + v + kThreads);
-                const u32x4 w2 = ld_copy(src + v + 2 * kThreads), w3 = ld_copy(src + v + 3 * kThreads);
-                st_copy(dst + v, w0);
-                st_copy(dst + v + kThreads, w1);
-                st_copy(dst + v + 2 * kThreads, w2);
-                st_copy(dst + v + 3 * kThreads, w3);
-            }
-            for (; v < end; v += kThreads) st_copy(dst + v, ld_copy(src + v));
-        }
+        for (long long base = (long long)blockIdx.x * kPer; base < nvec; base += (long long)gridDim.x * kPer)
+            copy_range(src, dst, base, (base + kPer < nvec) ? base + kPer : nvec);
         // tail elements past the last full vector
         const long long tail0 = nvec * 8;
         const uint16_t* s16 = (const uint16_t*)p.hsrc;

@@ -161,7 +161,7 @@ sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
  * re-run may do).
  * Hidden states are carried unshifted: hidden_dst[b][i][:] = hidden_src[b][i][:]
  * (a bit copy of B*(n+1)*H bfloat16 values).  hidden_dst == hidden_src, or both
- * NULL, copies nothing.  The buffers must not partially overlap.
+ * NULL, copies nothing.  Partially overlapping hidden buffers are SV_EINVAL.
  *
  *   tokens       [B][n+1] int32, in/out     accepted_len [B] int32
  *   emitted      [B][n+1] int32             hidden_src / hidden_dst [B][n+1][H] bf16
@@ -169,6 +169,43 @@ sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
 sv_status_t mtp_shift_insert(int32_t *tokens, const void *hidden_src, void *hidden_dst, int H,
                              const int32_t *accepted_len, const int32_t *emitted, int B, int n,
                              void *stream);
+
+/* One decode step's verification and MTP bookkeeping in one call.
+ *
+ * spec_verify_greedy_mtp() has the effect of spec_verify_greedy() followed by
+ * mtp_shift_insert(tokens, hidden_src, hidden_dst, H, accepted_len, emitted, B, n)
+ * on the same stream; spec_verify_sample_mtp() likewise with spec_verify_sample().
+ * The step the pages describe (Speculative decoding section, four inference
+ * stages; Single-token MTP scheduling section, third paragraph: the insert kernel
+ * runs right after verification) has no host work between the two, so the
+ * library fuses them: the hidden-state carry runs inside the verify kernels
+ * (every workgroup of the statistics pass copies an equal share after its rows),
+ * the token shift is done by the per-sequence decision and the drawn token is
+ * written to both outputs.  No
+ * extra launch is made when hidden_src and hidden_dst are 16-byte aligned and
+ * B*(n+1)*H is a multiple of 8 (or nothing is copied); otherwise the MTP kernel
+ * runs after the verify kernels.
+ *
+ * Because the copy overlaps the verification, tokens and hidden_dst must not
+ * overlap any other argument (SV_EINVAL otherwise), and hidden_src must not be
+ * written by the call (it is only read).  Other arguments and status codes are
+ * those of the two calls it replaces.
+ */
+sv_status_t spec_verify_greedy_mtp(const void *target_logits, sv_dtype_t dt,
+                                   const int32_t *draft_tokens, const int32_t *draft_lens, int B,
+                                   int n, int V, int32_t *accepted_len, int32_t *emitted,
+                                   uint32_t *err_flags, int32_t *tokens, const void *hidden_src,
+                                   void *hidden_dst, int H, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+sv_status_t spec_verify_sample_mtp(const void *target_logits, const void *draft_logits,
+                                   sv_dtype_t dt, const int32_t *draft_tokens,
+                                   const int32_t *draft_lens, const float *temperature,
+                                   const float *uniforms, int B, int n, int V,
+                                   int32_t *accepted_len, int32_t *emitted, float *row_lse,
+                                   uint32_t *err_flags, int32_t *tokens, const void *hidden_src,
+                                   void *hidden_dst, int H, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* Standard sampling of one token per sequence from a row chosen on the device.
  *

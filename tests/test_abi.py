@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ["spec_verify_sample", "spec_verify_greedy", "mtp_shift_insert", "sv_workspace_bytes",
-              "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug"]:
+              "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug",
+              "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "sv_sample_rows"]:
         assert f in names, names
 
 
@@ -139,3 +140,49 @@ def test_sample_rows_host_checks():
     assert f(*args(tok=NULL)) == sv.SV_EINVAL
     assert f(*args(ri=C.c_void_p(18))) == sv.SV_EALIGN
     assert f(*args(wsb=8)) == sv.SV_EWORKSPACE
+
+
+def _addr(k):
+    """Distinct fake device addresses (never dereferenced: host checks only)."""
+    return C.c_void_p((1 << 40) + (k << 32))
+
+
+def _greedy_mtp(**kw):
+    args = dict(t=_addr(0), dt=sv.SV_BF16, x=_addr(1), L=_addr(2), B=4, n=4, V=1024, acc=_addr(3), emi=_addr(4),
+                fl=NULL, tok=_addr(5), hs=_addr(6), hd=_addr(7), H=64, ws=_addr(8), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_greedy_mtp(*args.values())
+
+
+def _sample_mtp(**kw):
+    args = dict(t=_addr(0), d=_addr(9), dt=sv.SV_BF16, x=_addr(1), L=_addr(2), T=_addr(10), u=_addr(11), B=4, n=4,
+                V=1024, acc=_addr(3), emi=_addr(4), lse=NULL, fl=NULL, tok=_addr(5), hs=_addr(6), hd=_addr(7),
+                H=64, ws=_addr(8), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_sample_mtp(*args.values())
+
+
+def test_fused_mtp_host_checks():
+    for f in (_greedy_mtp, _sample_mtp):
+        assert f(B=0) == sv.SV_OK
+        assert f(tok=NULL) == sv.SV_EINVAL                     # tokens required
+        assert f(hs=NULL) == sv.SV_EINVAL                      # one hidden pointer only
+        assert f(hd=NULL) == sv.SV_EINVAL
+        assert f(H=0) == sv.SV_EINVAL                          # hidden without H
+        assert f(H=-1) == sv.SV_EINVAL
+        assert f(tok=C.c_void_p((1 << 40) + (5 << 32) + 2)) == sv.SV_EALIGN
+        assert f(hs=C.c_void_p((1 << 40) + (6 << 32) + 1)) == sv.SV_EALIGN
+        # aliasing: the copy and the token shift run inside the verify kernels
+        assert f(tok=_addr(4)) == sv.SV_EINVAL                 # tokens == emitted
+        assert f(tok=C.c_void_p((1 << 40) + (1 << 32) + 8)) == sv.SV_EINVAL  # inside draft_tokens
+        assert f(hd=_addr(0)) == sv.SV_EINVAL                  # hidden_dst over the target logits
+        assert f(hd=_addr(8)) == sv.SV_EINVAL                  # hidden_dst over the workspace
+        assert f(hd=C.c_void_p((1 << 40) + (6 << 32) + 256)) == sv.SV_EINVAL  # partial overlap with hidden_src
+        assert f(hs=NULL, hd=NULL, H=0, wsb=8) == sv.SV_EWORKSPACE
+
+
+def test_mtp_partial_overlap_rejected():
+    f = sv.lib().mtp_shift_insert
+    p = C.c_void_p(16)
+    src = C.c_void_p(1 << 20)
+    assert f(p, src, C.c_void_p((1 << 20) + 64), 64, p, p, 4, 4, NULL) == sv.SV_EINVAL
