@@ -23,7 +23,10 @@ constexpr int kThreads = SV_THREADS; // workgroup size of every kernel (wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDraft = 64;        // n <= kMaxDraft
 constexpr int kMaxSlots = 2 * kMaxDraft + 1;
-constexpr int kDrawTiles = 8;        // draw pass: tiles (kThreads * elements per 16-byte vector) per chunk
+#ifndef SV_DRAW_TILES
+#define SV_DRAW_TILES 8
+#endif
+constexpr int kDrawTiles = SV_DRAW_TILES;  // draw pass: tiles (kThreads * elements per 16-byte vector) per chunk
 constexpr int kMaxTiles = 1024;      // tiles per row (4 per thread in the draw selections)
 constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision

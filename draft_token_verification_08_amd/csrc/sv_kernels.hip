@@ -539,9 +539,9 @@ __device__ __forceinline__ void load_vec(const void* row, int e0, int hi, float*
 // (coalesced).  Per tile: the wave maximum m_t, then s_t = sum 2^((z - m_t) c),
 // each term formed as 2^fma(z, c, -fl(m_t c)) and the rounding of fl(m_t c)
 // corrected once per tile (its exact residual is fma(m_t, c, -fl(m_t c))).
-// Tile partials (m_t, s_t) are handed over through atomic exchanges into `tiles`
-// (when not null) for the bonus draw; the workgroup's merged (m, s) is returned
-// in thread 0.
+// Tile partials (m_t, s_t) are stored into `tiles` (when not null) for the
+// bonus draw of the draw pass; the workgroup's merged (m, s) is returned in
+// thread 0.
 template <int DT, bool ALIGNED>
 __device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigned long long* tiles) {
     constexpr int kVec = Elem<DT>::kVec;
@@ -551,7 +551,6 @@ __device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigne
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t0 = lo / kTile, t1 = (hi + kTile - 1) / kTile;
     float M = -FLT_MAX, S = 0.f;
-    unsigned long long dep = 0ull;
     // aligned rows: the next tile's 16-byte loads are issued before the current
     // tile is reduced (double buffer in registers); vectors past `hi` read -inf
     uint4 nxt[U];
@@ -600,17 +599,13 @@ __device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigne
             for (int e = 1; e < kVec; ++e) ls += acc[e];
             ts = wave_sum(ls) * exp2_fast(-delta);
         }
-        if (tiles != nullptr && lane == 0) dep ^= xchg64(tiles + t, pack2(tmax, ts));
+        // read only by the draw pass (the kernel boundary orders it): a plain store
+        if (tiles != nullptr && lane == 0) tiles[t] = pack2(tmax, ts);
         const MS r = ms_combine(MS{M, S}, MS{tmax, ts}, c);
         M = r.m;
         S = r.s;
     }
-    if (lane == 0) {
-        // this wave's tile exchanges have been performed before the workgroup arrives
-        asm volatile("" ::"v"((unsigned)dep), "v"((unsigned)(dep >> 32)));
-        __builtin_amdgcn_s_waitcnt(0);
-        s_wave[w] = MS{M, S};
-    }
+    if (lane == 0) s_wave[w] = MS{M, S};
     __syncthreads();
     MS r = s_wave[0];
     if (threadIdx.x == 0)
