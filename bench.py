@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=303)
+    ap.add_argument("--draft-stats", action="store_true",
+                    help="sampling configs: feed the draft rows' statistics from the draft's sampling step "
+                         "(spec_verify_sample_ex) instead of streaming the draft rows")
     ap.add_argument("--unfused", action="store_true",
                     help="separate verify and mtp_shift_insert calls instead of the fused call")
     return ap.parse_args()
@@ -106,7 +109,18 @@ def main():
 
     # calls marshalled once per input copy (the C entry points are re-issued as is)
     fused = bool(cfg.H) and not args.unfused
+    dstats = args.draft_stats and not greedy
     for d in data:
+        if dstats:
+            # the draft's sampling step computes these; it is not part of the timed step
+            d["dstats"] = sv.draft_row_stats(d["draft"], d["temperature"])
+            d["verify"] = sv.prepare_spec_verify_sample_ex(
+                d["target"], d["draft"], d["draft_tokens"], d["draft_lens"], d["temperature"], d["uniforms"],
+                d["acc"], d["emi"], wsbuf, draft_stats=d["dstats"], tokens=d["tokens"] if fused else None,
+                hidden_src=d["hidden"] if fused else None, hidden_dst=d["hidden_dst"] if fused else None)
+            d["mtp"] = (lambda: None) if fused or not cfg.H else sv.prepare_mtp_shift_insert(
+                d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+            continue
         if fused:
             if greedy:
                 d["verify"] = sv.prepare_spec_verify_greedy_mtp(d["target"], d["draft_tokens"], d["draft_lens"],
@@ -142,10 +156,20 @@ def main():
     side = cfg.B * cfg.n * 4 + cfg.B * 4 + cfg.B * 4 + cfg.B * (cfg.n + 1) * 4
     if not greedy:
         side += cfg.B * 4 + cfg.B * (cfg.n + 1) * 4
-    verify_bytes = [(rt + rd) * cfg.V * es + side for rt, rd in zip(rows_t, rows_d)]
+    rows_verified = [rt + rd for rt, rd in zip(rows_t, rows_d)]
+    if dstats:
+        # draft rows are not streamed: their statistics (8 B per row) and one
+        # gathered logit per test are read instead
+        side += cfg.B * cfg.n * 8
+        verify_bytes_extra = [rd * es for rd in rows_d]
+        rows_d = [0 for _ in rows_d]
+    else:
+        verify_bytes_extra = [0 for _ in rows_d]
+    verify_bytes = [(rt + rd) * cfg.V * es + side + x for rt, rd, x in zip(rows_t, rows_d, verify_bytes_extra)]
     mtp_bytes = (2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4 + cfg.B * 4
                  + cfg.B * (cfg.n + 1) * 4) if cfg.H else 0
-    rows_per_step = [rt + rd for rt, rd in zip(rows_t, rows_d)]
+    # rows streamed by the step (with the draft's statistics the draft rows are not)
+    rows_per_step = rows_t if dstats else rows_verified
 
     # ---------------------------------------------------------------- warmup
     for i in range(args.warmup):
@@ -211,7 +235,8 @@ def main():
     torch.cuda.synchronize()
     event_pair_us = statistics.median(a.elapsed_time(b2) for a, b2 in bare) * 1e3
 
-    kernel = ("k_stats_greedy" if greedy else "k_stats_sample+k_draw") + ("+mtp_fused" if fused else "")
+    kernel = (("k_stats_greedy" if greedy else "k_stats_sample+k_draw") + ("+draft_stats" if dstats else "")
+              + ("+mtp_fused" if fused else ""))
     workload = cfg.name
     traffic = measured_traffic(kernel, workload)
 
@@ -229,6 +254,7 @@ def main():
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic (seeded; inputs resident in HBM, rotated over %d copies)" % sets,
         "config": {"workload": ("greedy verify" if greedy else "sampling verify")
+                   + (" with the draft's row statistics" if dstats else "")
                    + (" + MTP shift/insert" + (" (fused call)" if fused else " (two calls)") if cfg.H else "")
                    + f" ({cfg.name})", "B": cfg.B, "n": cfg.n, "V": cfg.V, "H": cfg.H,
                    "logits": "bf16" if es == 2 else "f32", "parallelism": "none (1 GPU)"},

@@ -63,7 +63,10 @@ def lib():
     L.spec_verify_greedy_mtp.restype = i
     L.mtp_shift_insert.argtypes = [vp, vp, vp, i, vp, vp, i, i, vp]
     L.mtp_shift_insert.restype = i
-    L.sv_sample_rows.argtypes = [vp, i, i, vp, vp, vp, i, i, vp, vp, vp, sz, vp]
+    L.sv_sample_rows.argtypes = [vp, i, i, vp, vp, vp, i, i, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_sample_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i,
+                                        vp, sz, vp]
+    L.spec_verify_sample_ex.restype = i
     L.sv_sample_rows.restype = i
     L.sv_softmax_rows_debug.argtypes = [vp, i, vp, i, i, vp, vp]
     L.sv_softmax_rows_debug.restype = i
@@ -294,6 +297,65 @@ def spec_verify_sample_mtp(target_logits, draft_logits, draft_tokens, draft_lens
     return accepted_len, emitted
 
 
+def spec_verify_sample_ex(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms, *,
+                          draft_stats=None, tokens=None, hidden_src=None, hidden_dst=None, accepted_len=None,
+                          emitted=None, row_lse=None, err_flags=None, workspace=None, stream=None):
+    """spec_verify_sample with the draft rows' statistics from the draft's sampling
+    step (draft_stats [B, n, 2], or None) and the fused MTP step (tokens and the
+    hidden buffers, or None).  Returns (accepted_len, emitted)."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    if draft_stats is not None:
+        _check(draft_stats, "draft_stats", torch.float32, (B, n, 2), dev)
+    H = 0
+    if tokens is not None:
+        H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    elif hidden_src is not None or hidden_dst is not None:
+        raise ValueError("hidden buffers need the token buffer")
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n1), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    if row_lse is not None:
+        _check(row_lse, "row_lse", torch.float32, (B, 2 * n + 1), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, n, V, dt)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("spec_verify_sample_ex", _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+          _ptr(draft_lens), _ptr(temperature), _ptr(uniforms), _ptr(draft_stats), B, n, V, _ptr(accepted_len),
+          _ptr(emitted), _ptr(row_lse), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H,
+          _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted
+
+
+def draft_row_stats(draft_logits, temperature, *, workspace=None, stream=None):
+    """{max, sum 2^((z - max) log2e/T)} of every draft row [B, n, V] at the
+    sequences' temperatures, as the draft's sampling step writes them: one
+    sv_sample_rows call over the B*n rows (the sampled tokens are discarded)."""
+    B, n, V = draft_logits.shape
+    dev = draft_logits.device
+    rows = draft_logits.reshape(B * n, 1, V)
+    T = temperature.repeat_interleave(n).contiguous()
+    u = torch.zeros(B * n, dtype=torch.float32, device=dev)
+    stats = torch.empty((B * n, 2), dtype=torch.float32, device=dev)
+    sv_sample_rows(rows, T, u, row_stats=stats, workspace=workspace, stream=stream)
+    return stats.view(B, n, 2)
+
+
 def mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitted, *, stream=None):
     """MTP shift/insert (see include/specverify.h); tokens is updated in place,
     hidden_dst receives the carried hidden states."""
@@ -452,13 +514,43 @@ def prepare_spec_verify_sample_mtp(target_logits, draft_logits, draft_tokens, dr
                                                       hidden_src, hidden_dst, workspace, row_lse, err_flags))
 
 
+def prepare_spec_verify_sample_ex(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms,
+                                  accepted_len, emitted, workspace, draft_stats=None, tokens=None, hidden_src=None,
+                                  hidden_dst=None, row_lse=None, err_flags=None, stream=None) -> Prepared:
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    if draft_stats is not None:
+        _check(draft_stats, "draft_stats", torch.float32, (B, n, 2), dev)
+    H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev) if tokens is not None else 0
+    args = (_ptr(target_logits), _ptr(draft_logits), _dt(target_logits), _ptr(draft_tokens), _ptr(draft_lens),
+            _ptr(temperature), _ptr(uniforms), _ptr(draft_stats), B, n, V, _ptr(accepted_len), _ptr(emitted),
+            _ptr(row_lse), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(workspace),
+            workspace.numel(), _stream(stream, dev))
+    return Prepared("spec_verify_sample_ex", args, (target_logits, draft_logits, draft_tokens, draft_lens,
+                                                     temperature, uniforms, accepted_len, emitted, workspace,
+                                                     draft_stats, tokens, hidden_src, hidden_dst, row_lse,
+                                                     err_flags))
+
+
 # ------------------------------------------------------------------ standard sampling of chosen rows
 
 def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None, err_flags=None,
-                   workspace=None, stream=None):
+                   row_stats=None, workspace=None, stream=None):
     """One token per sequence from logits[b][row_index[b]] (row 0 when row_index
     is None): logits [B][R][V] (or [B][V]), temperature [B], uniforms [B].
-    Returns tokens [B] int32 (see include/specverify.h)."""
+    row_stats [B, 2] float32 (optional) receives {max, sum 2^((z - max) log2e/T)}
+    of the row drawn from.  Returns tokens [B] int32 (see include/specverify.h)."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(1)
     B, R, V = logits.shape
@@ -474,10 +566,12 @@ def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None
     _check(tokens, "tokens", torch.int32, (B,), dev)
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    if row_stats is not None:
+        _check(row_stats, "row_stats", torch.float32, (B, 2), dev)
     need = sv_workspace_bytes(B, 0, V, dt)
     if workspace is None:
         workspace = _default_ws(dev, need, stream)
     _check(workspace, "workspace", torch.uint8)
     _call("sv_sample_rows", _ptr(logits), dt, R, _ptr(row_index), _ptr(temperature), _ptr(uniforms), B, V,
-          _ptr(tokens), _ptr(err_flags), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+          _ptr(tokens), _ptr(err_flags), _ptr(row_stats), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     return tokens

@@ -210,7 +210,7 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
                           const int32_t* draft_tokens, const int32_t* draft_lens, const float* temperature,
                           const float* uniforms, int B, int n, int V, int32_t* accepted_len, int32_t* emitted,
                           float* row_lse, uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                          void* stream, const MtpArgs* mtp) {
+                          void* stream, const MtpArgs* mtp, const float* draft_stats) {
     if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_lens || !temperature || !uniforms || !accepted_len || !emitted ||
@@ -220,8 +220,9 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
     if (!aligned_to(target_logits, es) || (draft_logits && !aligned_to(draft_logits, es)) ||
         !aligned_to(draft_tokens, 4) || !aligned_to(draft_lens, 4) || !aligned_to(temperature, 4) ||
         !aligned_to(uniforms, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) ||
-        !aligned_to(row_lse, 4) || !aligned_to(err_flags, 4))
+        !aligned_to(row_lse, 4) || !aligned_to(err_flags, 4) || !aligned_to(draft_stats, 4))
         return SV_EALIGN;
+    if (draft_stats && !draft_logits) return SV_EINVAL;  // the gather and the residual need the rows
     sv::Layout L;
     if (!make_layout(B, n, V, dt, &L)) return SV_EINVAL;
     if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
@@ -245,6 +246,7 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
                                {accepted_len, (size_t)B * 4},
                                {emitted, (size_t)B * (n + 1) * 4},
                                {row_lse, row_lse ? (size_t)B * (2 * n + 1) * 4 : 0},
+                               {draft_stats, draft_stats ? (size_t)B * n * 8 : 0},
                                {err_flags, err_flags ? 4u : 0u},
                                {workspace, workspace_bytes},
                                tok};
@@ -275,6 +277,7 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
     sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
     sp.R = n + 1;
     sp.row_index = nullptr;
+    sp.dstats = draft_stats;
     if (mtp && pl.fused) sp.mtp = pl.f;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
@@ -378,7 +381,7 @@ sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logi
                                void* stream) {
     return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
                          V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream,
-                         nullptr);
+                         nullptr, nullptr);
 }
 
 sv_status_t spec_verify_sample_mtp(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
@@ -390,7 +393,22 @@ sv_status_t spec_verify_sample_mtp(const void* target_logits, const void* draft_
                                    void* stream) {
     const MtpArgs m{tokens, hidden_src, hidden_dst, H};
     return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
-                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream, &m);
+                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream, &m,
+                         nullptr);
+}
+
+sv_status_t spec_verify_sample_ex(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                                  const int32_t* draft_tokens, const int32_t* draft_lens,
+                                  const float* temperature, const float* uniforms, const float* draft_stats,
+                                  int B, int n, int V, int32_t* accepted_len, int32_t* emitted, float* row_lse,
+                                  uint32_t* err_flags, int32_t* tokens, const void* hidden_src,
+                                  void* hidden_dst, int H, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!tokens && (hidden_src || hidden_dst)) return SV_EINVAL;
+    const MtpArgs m{tokens, hidden_src, hidden_dst, H};
+    return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
+                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream,
+                         tokens ? &m : nullptr, draft_stats);
 }
 
 sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
@@ -413,13 +431,15 @@ sv_status_t spec_verify_greedy_mtp(const void* target_logits, sv_dtype_t dt, con
 
 sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32_t* row_index,
                            const float* temperature, const float* uniforms, int B, int V, int32_t* tokens,
-                           uint32_t* err_flags, void* workspace, size_t workspace_bytes, void* stream) {
+                           uint32_t* err_flags, float* row_stats, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     if (B < 0 || R < 1 || V < 1 || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
     if (B == 0) return SV_OK;
     if (!logits || !temperature || !uniforms || !tokens) return SV_EINVAL;
     const size_t es = elem_bytes(dt);
     if (!aligned_to(logits, es) || !aligned_to(row_index, 4) || !aligned_to(temperature, 4) ||
-        !aligned_to(uniforms, 4) || !aligned_to(tokens, 4) || !aligned_to(err_flags, 4))
+        !aligned_to(uniforms, 4) || !aligned_to(tokens, 4) || !aligned_to(err_flags, 4) ||
+        !aligned_to(row_stats, 4))
         return SV_EALIGN;
     sv::Layout L;
     if (!make_layout(B, 0, V, dt, &L)) return SV_EINVAL;
@@ -449,6 +469,7 @@ sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32
     sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
     sp.R = R;
     sp.row_index = row_index;
+    sp.out_stats = row_stats;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
     sv::DrawParams dp{};

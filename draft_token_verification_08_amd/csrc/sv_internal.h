@@ -51,10 +51,10 @@ struct DrawDesc {
     int k;          // row index of the draw (target row k, and draft row k if residual)
     float c;        // log2(e) / T as used for every exponent of this sequence
     float m_t;      // max of target row k
-    float inv_s_t;  // 1 / sum 2^((z - m_t) c) of target row k
-    float m_d;      // same for draft row k (residual only)
-    float inv_s_d;
+    float m_d;      // max of draft row k (residual only)
+    float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
+    float pad;
 };
 
 // Workspace layout (byte offsets from the workspace base; every region 256-aligned).
@@ -104,6 +104,9 @@ struct StatsParams {
     uint32_t* cnt;
     DrawDesc* desc;
     MtpFuse mtp;              // zero: not fused
+    const float* dstats;      // [B][n][2] {max, sum 2^((z - max) c)} of the draft rows, from the
+                              // draft's own sampling step, or nullptr (draft rows are then streamed)
+    float* out_stats;         // [B][2] or nullptr: the same statistics of the row of target slot 0
 };
 
 struct DrawParams {

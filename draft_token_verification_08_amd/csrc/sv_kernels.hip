@@ -39,6 +39,9 @@
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
 #endif
+#ifndef SV_DRAW_GRID
+#define SV_DRAW_GRID 0
+#endif
 #ifndef SV_LOAD_FENCE
 #define SV_LOAD_FENCE 0
 #endif
@@ -533,6 +536,29 @@ __device__ __forceinline__ void load_vec(const void* row, int e0, int hi, float*
     }
 }
 
+// The 16-byte vector of elements [e0, e0 + kVec) of a row whose base may not be
+// 16-byte aligned, as raw bits (element by element); indices at or past `hi`
+// hold -inf (never loaded).
+template <int DT>
+__device__ __forceinline__ uint4 load_raw(const void* row, int e0, int hi) {
+    constexpr int kVec = Elem<DT>::kVec;
+    unsigned w[4];
+    if constexpr (DT == kBF16) {
+        const uint16_t* r = (const uint16_t*)row;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const unsigned lo16 = (e0 + 2 * q < hi) ? r[e0 + 2 * q] : 0xff80u;
+            const unsigned hi16 = (e0 + 2 * q + 1 < hi) ? r[e0 + 2 * q + 1] : 0xff80u;
+            w[q] = lo16 | (hi16 << 16);
+        }
+    } else {
+        const unsigned* r = (const unsigned*)row;
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) w[q] = (e0 + q < hi) ? r[e0 + q] : 0xff800000u;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Sampling rows: softmax statistics over [lo, hi) (lo a multiple of the tile)
 // in tiles of kThreads * kVec contiguous elements.  Wave w takes tiles w,
 // w + kWaves, ...; inside a tile lane l reads vectors l, l + 64, l + 128, ...
@@ -668,13 +694,15 @@ __device__ __forceinline__ Pick block_first_crossing(int N, double t, W&& weight
 
 // Weight of one element for the draw.  Bonus / fallback rows: 2^((z - m_t) c),
 // on the same scale as the stored tile partials.  Residual rows:
-// max(0, p_k - q_k) with p and q normalised.
+// S_t * max(0, p_k - q_k) = max(0, 2^((z_t - m_t) c) - 2^((z_d - m_d) c + log2(S_t / S_d))):
+// the common factor S_t cancels in the draw, and the draft's normaliser enters
+// its exponent through one fma (z_d - m_d is exact for bf16).
 __device__ __forceinline__ float w_target(const DrawDesc& d, float zt) {
     return exp2_fast((zt - d.m_t) * d.c);
 }
 __device__ __forceinline__ float w_residual(const DrawDesc& d, float zt, float zd) {
-    const float pt = exp2_fast((zt - d.m_t) * d.c) * d.inv_s_t;
-    const float qd = exp2_fast((zd - d.m_d) * d.c) * d.inv_s_d;
+    const float pt = exp2_fast((zt - d.m_t) * d.c);
+    const float qd = exp2_fast(fmaf(zd - d.m_d, d.c, d.lq));
     return fmaxf(pt - qd, 0.f);
 }
 
@@ -852,7 +880,14 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     } else {
         for (int i = tid; i < S * NC; i += kThreads) s_part[i] = xchg64(part + i, 0ull);
         __syncthreads();
-        const bool row_read = (tid <= L) || (tid > n && tid < S && tid - n - 1 < L);
+        const bool draft_row = tid > n && tid < S && tid - n - 1 < L;
+        const bool row_read = (tid <= L) || (draft_row && p.dstats == nullptr);
+        if (draft_row && p.dstats != nullptr) {
+            // statistics the draft's sampling step computed over the same row at the same T
+            const float* ds = p.dstats + ((size_t)b * n + (tid - n - 1)) * 2;
+            s_m[tid] = ds[0];
+            s_S[tid] = (double)ds[1];
+        }
         if (row_read) {
             // online merge in double: running max, rescaled sum
             float m = -FLT_MAX;
@@ -877,6 +912,11 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             float v = __builtin_nanf("");
             if (row_read) v = (float)((double)s_m[tid] / (double)si.T + log(s_S[tid]));
             p.row_lse[(size_t)b * (2 * n + 1) + tid] = v;
+        }
+        if (p.out_stats && tid == 0) {
+            const float nan = __builtin_nanf("");
+            p.out_stats[(size_t)b * 2] = si.greedy ? nan : s_m[0];
+            p.out_stats[(size_t)b * 2 + 1] = si.greedy ? nan : (float)s_S[0];
         }
     }
     __syncthreads();
@@ -953,10 +993,10 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             d.k = k;
             d.c = cf;
             d.m_t = s_m[k];
-            d.inv_s_t = (float)(1.0 / s_S[k]);
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
-            d.inv_s_d = (k < L) ? (float)(1.0 / s_S[n + 1 + k]) : 0.f;
+            d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
+            d.pad = 0.f;
             p.desc[b] = d;
         }
         if (flags && p.flags) atomicOr(p.flags, flags);
@@ -977,12 +1017,14 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
 
     const SeqInfo si = seq_info<MODE>(p, b);
     const bool target_row = slot <= n;
-    const bool needed = target_row ? (slot <= si.L) : (!si.greedy && slot - n - 1 < si.L);
+    const bool needed =
+        target_row ? (slot <= si.L) : (!si.greedy && p.dstats == nullptr && slot - n - 1 < si.L);
     if (!needed) {
         copy_share(p.mtp, bid, gridDim.x);
         return;
     }
-    const unsigned expected = (unsigned)p.NC * (unsigned)(si.L + 1 + (si.greedy ? 0 : si.L));
+    const unsigned expected =
+        (unsigned)p.NC * (unsigned)(si.L + 1 + ((si.greedy || p.dstats != nullptr) ? 0 : si.L));
 
     const void* row = target_row ? row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, slot), p.V)
                                  : row_ptr<DT>(p.draft, (long long)b * n + (slot - n - 1), p.V);
@@ -1070,16 +1112,13 @@ __device__ __forceinline__ int tile_draw(const DrawParams& p, int b, const DrawD
 // last workgroup of the sequence picks the tile holding u * Z with one block
 // prefix scan and scans only that tile.
 template <int DT, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+__device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, double* s_buf) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
-    const int c = blockIdx.x % p.NCd;
-    const int b = blockIdx.x / p.NCd;
     const DrawDesc d = p.desc[b];
     if (d.kind == kDrawNone) return;
     const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
     const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
-    __shared__ double s_buf[kMaxTiles];
     if (d.kind == kDrawBonus) {
         if (c != 0) return;
         const int y = tile_draw<DT, ALIGNED>(p, b, d, trow, s_buf);
@@ -1095,59 +1134,57 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     unsigned* dres = reinterpret_cast<unsigned*>(p.dres) + (size_t)b * NT;
     unsigned* dp = reinterpret_cast<unsigned*>(p.dp) + (size_t)b * NT;
 
+    // chunk c: tiles [tile0, tile0 + cnt).  Wave w owns kTilesPerWave whole tiles
+    // (lane l reads vectors l, l + 64, ... of each, coalesced), so every tile sum
+    // is one wave reduction; all loads are issued before the first use.
+    constexpr int kTilesPerWave = kDrawTiles / kWaves;
+    constexpr int kU = kThreads / 64;  // vectors per lane per tile
+    static_assert(kDrawTiles % kWaves == 0, "draw chunk must split evenly over the waves");
     const int tile0 = c * kDrawTiles;
     const int cnt = min(kDrawTiles, NT - tile0);
-    __shared__ float s_r[kWaves][kDrawTiles], s_p[kWaves][kDrawTiles];
-    // every load of the chunk is issued before any is used (one memory round trip)
-    float zt[kDrawTiles][kVec], zd[kDrawTiles][kVec];
-    if constexpr (ALIGNED) {
-        uint4 rt[kDrawTiles], rd[kDrawTiles];
+    const int lane = tid & 63, wv = tid >> 6;
+    // raw 16-byte vectors (bf16 pairs or fp32), widened where they are used
+    uint4 rt[kTilesPerWave][kU], rd[kTilesPerWave][kU];
 #pragma unroll
-        for (int k = 0; k < kDrawTiles; ++k) {
-            const int e0 = (tile0 + k) * kTile + tid * kVec;
-            const bool ok = k < cnt && e0 < V;
-            rt[k] = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
-            rd[k] = ok ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+    for (int i = 0; i < kTilesPerWave; ++i)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int e0 = (tile0 + wv * kTilesPerWave + i) * kTile + (lane + 64 * u) * kVec;
+            const bool ok = wv * kTilesPerWave + i < cnt && e0 < V;
+            if constexpr (ALIGNED) {
+                rt[i][u] = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+                rd[i][u] = ok ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+            } else {
+                rt[i][u] = load_raw<DT>(trow, e0, ok ? V : 0);
+                rd[i][u] = load_raw<DT>(drow, e0, ok ? V : 0);
+            }
         }
+    unsigned dep = 0u;
 #pragma unroll
-        for (int k = 0; k < kDrawTiles; ++k) {
-            unpack<DT>(rt[k], zt[k]);
-            unpack<DT>(rd[k], zd[k]);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kDrawTiles; ++k) {
-            const int e0 = (tile0 + k) * kTile + tid * kVec;
-            const int lim = (k < cnt) ? V : 0;
-            load_vec<DT, ALIGNED>(trow, e0, lim, zt[k]);
-            load_vec<DT, ALIGNED>(drow, e0, lim, zd[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kDrawTiles; ++k) {
+    for (int i = 0; i < kTilesPerWave; ++i) {
         float ar = 0.f, ap = 0.f;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            ar += w_residual(d, zt[k][e], zd[k][e]);  // absent elements read -inf: weight 0
-            ap += w_target(d, zt[k][e]);
+        for (int u = 0; u < kU; ++u) {
+            float zt[kVec], zd[kVec];
+            unpack<DT>(rt[i][u], zt);
+            unpack<DT>(rd[i][u], zd);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                ar += w_residual(d, zt[e], zd[e]);  // absent elements read -inf: weight 0
+                ap += w_target(d, zt[e]);
+            }
         }
         ar = wave_sum(ar);
         ap = wave_sum(ap);
-        if ((tid & 63) == 0) {
-            s_r[tid >> 6][k] = ar;
-            s_p[tid >> 6][k] = ap;
+        const int t = wv * kTilesPerWave + i;
+        if (lane == 0 && t < cnt) {
+            dep ^= xchg32(dres + tile0 + t, __float_as_uint(ar));
+            dep ^= xchg32(dp + tile0 + t, __float_as_uint(ap));
         }
     }
-    __syncthreads();
-    if (tid < cnt) {
-        float r = s_r[0][tid], q = s_p[0][tid];
-        for (int w = 1; w < kWaves; ++w) {
-            r += s_r[w][tid];
-            q += s_p[w][tid];
-        }
-        const unsigned d1 = xchg32(dres + tile0 + tid, __float_as_uint(r));
-        const unsigned d2 = xchg32(dp + tile0 + tid, __float_as_uint(q));
-        asm volatile("" ::"v"(d1), "v"(d2));
+    if (lane == 0) {
+        // this wave's exchanges have been performed before the workgroup arrives
+        asm volatile("" ::"v"(dep));
         __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
@@ -1221,6 +1258,19 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
         if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.k] = y;
         p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         xchg32(&p.cnt[b], 0u);
+    }
+}
+
+// Work items (sequence, chunk) in sequence-major order.  SV_DRAW_GRID > 0: that
+// many workgroups stride over the items (items of sequences that draw nothing
+// then cost a descriptor load, not a workgroup dispatch); 0: one workgroup per item.
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+    __shared__ double s_buf[kMaxTiles];
+    const int items = p.B * p.NCd;
+    for (int w = blockIdx.x; w < items; w += gridDim.x) {
+        draw_item<DT, ALIGNED>(p, w / p.NCd, w % p.NCd, s_buf);
+        __syncthreads();  // LDS is reused by the next item
     }
 }
 
@@ -1312,7 +1362,8 @@ hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hi
 }
 
 hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s) {
-    const unsigned blocks = (unsigned)((long long)p.B * p.NCd);
+    long long items = (long long)p.B * p.NCd;
+    const unsigned blocks = (unsigned)((SV_DRAW_GRID > 0 && items > SV_DRAW_GRID) ? SV_DRAW_GRID : items);
     const dim3 grid(blocks), block(kThreads);
     if (dt == kBF16) {
         if (aligned) hipLaunchKernelGGL((k_draw<kBF16, true>), grid, block, 0, s, p);

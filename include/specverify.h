@@ -207,6 +207,31 @@ sv_status_t spec_verify_sample_mtp(const void *target_logits, const void *draft_
                                    void *hidden_dst, int H, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* spec_verify_sample() with two optional parts, each NULL to leave it out:
+ *
+ *   draft_stats [B][n][2] float: the {m, S} statistics of every draft row at the
+ *     sequence's temperature, as sv_sample_rows() writes them when the draft
+ *     samples its tokens (the draft-target loop of the Target-draft section,
+ *     decode paragraph: the draft samples from q_j, which already needs q_j's
+ *     normaliser).  The verify step then reads no draft row in full: q_j(x_j)
+ *     takes one gathered logit and the residual draw re-reads only draft row k.
+ *     Entries for rows j >= L_b and for T_b = 0 sequences are not read.
+ *     draft_logits must still be given.  Statistics that do not belong to the
+ *     rows (another temperature, other logits) give undefined tokens, never an
+ *     out-of-bounds access.  row_lse entries of draft rows come from draft_stats.
+ *   tokens, hidden_src, hidden_dst, H: the fused MTP step of
+ *     spec_verify_sample_mtp() (tokens NULL: no MTP step; hidden pointers must
+ *     then be NULL too).
+ */
+sv_status_t spec_verify_sample_ex(const void *target_logits, const void *draft_logits,
+                                  sv_dtype_t dt, const int32_t *draft_tokens,
+                                  const int32_t *draft_lens, const float *temperature,
+                                  const float *uniforms, const float *draft_stats, int B, int n,
+                                  int V, int32_t *accepted_len, int32_t *emitted, float *row_lse,
+                                  uint32_t *err_flags, int32_t *tokens, const void *hidden_src,
+                                  void *hidden_dst, int H, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Standard sampling of one token per sequence from a row chosen on the device.
  *
  * Sequence b draws from logits[b][r_b][:] with r_b = row_index[b] (clamped to
@@ -222,11 +247,16 @@ sv_status_t spec_verify_sample_mtp(const void *target_logits, const void *draft_
  *   logits     [B][R][V] dt      row_index [B] int32, nullable
  *   temperature [B] float        uniforms [B] float in [0,1)
  *   tokens     [B] int32 out     err_flags [1] uint32, nullable
+ *   row_stats  [B][2] float out, nullable: {m, S} of the row drawn from, with
+ *              m = max_i z_i and S = sum_i 2^((z_i - m) log2(e) / T_b) (NaN for
+ *              T_b = 0).  These are the draft-row statistics that
+ *              spec_verify_sample_ex() accepts, so the verify step need not
+ *              stream the draft rows again.
  *   workspace  >= sv_workspace_bytes(B, 0, V, dt) bytes, zero-filled before first use
  */
 sv_status_t sv_sample_rows(const void *logits, sv_dtype_t dt, int R, const int32_t *row_index,
                            const float *temperature, const float *uniforms, int B, int V,
-                           int32_t *tokens, uint32_t *err_flags, void *workspace,
+                           int32_t *tokens, uint32_t *err_flags, float *row_stats, void *workspace,
                            size_t workspace_bytes, void *stream);
 
 /* Parity/debug only (not on the hot path): full binary32 probabilities

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ["spec_verify_sample", "spec_verify_greedy", "mtp_shift_insert", "sv_workspace_bytes",
               "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug",
-              "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "sv_sample_rows"]:
+              "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "spec_verify_sample_ex", "sv_sample_rows"]:
         assert f in names, names
 
 
@@ -133,13 +133,14 @@ def test_sample_rows_host_checks():
     p = C.c_void_p(16)
     ws = C.c_void_p(256)
     args = lambda **kw: [kw.get(k, v) for k, v in dict(z=p, dt=sv.SV_BF16, R=2, ri=NULL, T=p, u=p, B=4, V=100,
-                                                       tok=p, fl=NULL, ws=ws, wsb=1 << 20, s=NULL).items()]
+                                                       tok=p, fl=NULL, st=NULL, ws=ws, wsb=1 << 20, s=NULL).items()]
     assert f(*args(B=0)) == sv.SV_OK
     assert f(*args(R=0)) == sv.SV_EINVAL
     assert f(*args(z=NULL)) == sv.SV_EINVAL
     assert f(*args(tok=NULL)) == sv.SV_EINVAL
     assert f(*args(ri=C.c_void_p(18))) == sv.SV_EALIGN
     assert f(*args(wsb=8)) == sv.SV_EWORKSPACE
+    assert f(*args(st=C.c_void_p(18))) == sv.SV_EALIGN
 
 
 def _addr(k):
@@ -186,3 +187,20 @@ def test_mtp_partial_overlap_rejected():
     p = C.c_void_p(16)
     src = C.c_void_p(1 << 20)
     assert f(p, src, C.c_void_p((1 << 20) + 64), 64, p, p, 4, 4, NULL) == sv.SV_EINVAL
+
+
+def _sample_ex(**kw):
+    args = dict(t=_addr(0), d=_addr(9), dt=sv.SV_BF16, x=_addr(1), L=_addr(2), T=_addr(10), u=_addr(11),
+                ds=_addr(12), B=4, n=4, V=1024, acc=_addr(3), emi=_addr(4), lse=NULL, fl=NULL, tok=NULL, hs=NULL,
+                hd=NULL, H=0, ws=_addr(8), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_sample_ex(*args.values())
+
+
+def test_sample_ex_host_checks():
+    assert _sample_ex(B=0) == sv.SV_OK
+    assert _sample_ex(d=NULL) == sv.SV_EINVAL                  # draft statistics still need the draft rows
+    assert _sample_ex(ds=C.c_void_p((1 << 40) + (12 << 32) + 2)) == sv.SV_EALIGN
+    assert _sample_ex(hs=_addr(6), hd=_addr(7), H=64) == sv.SV_EINVAL   # hidden buffers without tokens
+    assert _sample_ex(tok=_addr(5), hd=_addr(12), hs=_addr(6), H=64) == sv.SV_EINVAL  # hidden_dst over draft_stats
+    assert _sample_ex(wsb=8) == sv.SV_EWORKSPACE

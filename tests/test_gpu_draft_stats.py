@@ -1,0 +1,101 @@
+"""GPU parity of the verify step fed with the draft rows' statistics from the
+draft's own sampling step (sv_sample_rows row_stats -> spec_verify_sample_ex
+draft_stats): the decisions must match the oracle, which computes every row's
+softmax itself, decision by decision (near-ties below 1e-5 exempt), and the
+statistics must give the oracle's log-sum-exp within 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_08_amd as sv
+from draft_token_verification_08_amd import synth
+from svcompare import compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _oracle(oracle, d, seqs=None):
+    sl = slice(None) if seqs is None else torch.as_tensor(seqs, device=DEV)
+    return oracle.verify_sample(synth.host_logits(d["target"][sl]), synth.host_logits(d["draft"][sl]),
+                                d["draft_tokens"][sl].cpu().numpy(), d["draft_lens"][sl].cpu().numpy(),
+                                d["temperature"][sl].cpu().numpy(), d["uniforms"][sl].cpu().numpy(), threads=16)
+
+
+def _check_lse(lse, ora, seqs=None):
+    g = lse if seqs is None else lse[seqs]
+    o = ora["row_lse"]
+    assert np.array_equal(np.isnan(g), np.isnan(o))
+    ok = ~np.isnan(o)
+    err = np.abs(g.astype(np.float64) - o)[ok]
+    assert err.size == 0 or err.max() <= 1e-5, err.max()
+
+
+@pytest.mark.parametrize("cid,B,V,n,seed", [(2, 24, 5003, 4, 0), (4, 64, 4099, 1, 1), (5, 40, 3001, 8, 2),
+                                            (5, 16, 129, 3, 3)])
+def test_verify_with_draft_stats(oracle, cid, B, V, n, seed):
+    d = synth.make(cid, 500 + seed, device=DEV, B=B, V=V, n=n)
+    stats = sv.draft_row_stats(d["draft"], d["temperature"])
+    lse = torch.zeros((B, 2 * n + 1), dtype=torch.float32, device=DEV)
+    fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                        d["temperature"], d["uniforms"], draft_stats=stats, row_lse=lse,
+                                        err_flags=fl)
+    torch.cuda.synchronize()
+    ora = _oracle(oracle, d)
+    rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(),
+                  d["temperature"].cpu().numpy(), n)
+    assert rep.hard == 0, rep
+    _check_lse(lse.cpu().numpy(), ora)
+    assert int(fl.item()) == int(np.bitwise_or.reduce(ora["seq_flags"]))
+
+
+def test_draft_stats_match_oracle_rows(oracle):
+    """{m, S} of every draft row: m/T + ln S equals the oracle's lse."""
+    d = synth.make(5, 510, device=DEV, B=12, V=7001, n=5)
+    stats = sv.draft_row_stats(d["draft"], d["temperature"]).cpu().numpy().astype(np.float64)
+    zd = synth.host_logits(d["draft"])
+    T = d["temperature"].cpu().numpy()
+    for b in range(12):
+        for j in range(5):
+            if T[b] > 0:
+                lse, _ = oracle.softmax_row(zd[b, j], T[b])
+                got = stats[b, j, 0] / np.float64(np.float32(T[b])) + np.log(stats[b, j, 1])
+                assert abs(got - lse) <= 1e-5, (b, j, got, lse)
+            else:
+                assert np.isnan(stats[b, j]).all()
+
+
+def test_verify_with_draft_stats_full_config(oracle):
+    """Config 5 at full size (B=1024, n=8, V=152064); the oracle checks a sample."""
+    d = synth.make(5, 505, device=DEV)
+    stats = sv.draft_row_stats(d["draft"], d["temperature"])
+    acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                        d["temperature"], d["uniforms"], draft_stats=stats)
+    torch.cuda.synchronize()
+    seqs = np.sort(np.random.default_rng(5).choice(d["B"], size=64, replace=False))
+    ora = _oracle(oracle, d, seqs)
+    rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(),
+                  d["temperature"].cpu().numpy(), d["n"], seqs)
+    assert rep.hard == 0, rep
+
+
+def test_verify_with_draft_stats_and_mtp(oracle):
+    """Both optional parts at once: equals the oracle's verify followed by its
+    shift/insert on the GPU's outputs."""
+    d = synth.make(4, 520, device=DEV, B=48, V=6007, H=32)
+    stats = sv.draft_row_stats(d["draft"], d["temperature"])
+    tok = d["tokens"].clone()
+    dst = torch.zeros_like(d["hidden"])
+    acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                        d["temperature"], d["uniforms"], draft_stats=stats, tokens=tok,
+                                        hidden_src=d["hidden"], hidden_dst=dst)
+    torch.cuda.synchronize()
+    ora = _oracle(oracle, d)
+    rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(),
+                  d["temperature"].cpu().numpy(), d["n"])
+    assert rep.hard == 0, rep
+    ref_tok, ref_hid = oracle.mtp_shift_insert(d["tokens"].cpu().numpy(), d["hidden"].cpu().view(torch.int16).numpy(),
+                                               acc.cpu().numpy(), emi.cpu().numpy())
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
+    assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid)
