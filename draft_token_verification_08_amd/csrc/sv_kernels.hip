@@ -39,9 +39,6 @@
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
 #endif
-#ifndef SV_DRAW_GRID
-#define SV_DRAW_GRID 0
-#endif
 #ifndef SV_LOAD_FENCE
 #define SV_LOAD_FENCE 0
 #endif
@@ -1261,17 +1258,18 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     }
 }
 
-// Work items (sequence, chunk) in sequence-major order.  SV_DRAW_GRID > 0: that
-// many workgroups stride over the items (items of sequences that draw nothing
-// then cost a descriptor load, not a workgroup dispatch); 0: one workgroup per item.
-template <int DT, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+// One workgroup per (sequence, chunk), sequence-major.  The aligned kernel is
+// held to 80 VGPRs (6 waves per SIMD) without spilling; the element-wise
+// unaligned one is left to the compiler.
+template <int DT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_draw(DrawParams p) {
     __shared__ double s_buf[kMaxTiles];
-    const int items = p.B * p.NCd;
-    for (int w = blockIdx.x; w < items; w += gridDim.x) {
-        draw_item<DT, ALIGNED>(p, w / p.NCd, w % p.NCd, s_buf);
-        __syncthreads();  // LDS is reused by the next item
-    }
+    draw_item<DT, true>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
+}
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_draw_unaligned(DrawParams p) {
+    __shared__ double s_buf[kMaxTiles];
+    draw_item<DT, false>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
 }
 
 // --------------------------------------------------------------- MTP shift / insert
@@ -1362,15 +1360,14 @@ hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hi
 }
 
 hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s) {
-    long long items = (long long)p.B * p.NCd;
-    const unsigned blocks = (unsigned)((SV_DRAW_GRID > 0 && items > SV_DRAW_GRID) ? SV_DRAW_GRID : items);
+    const unsigned blocks = (unsigned)((long long)p.B * p.NCd);
     const dim3 grid(blocks), block(kThreads);
     if (dt == kBF16) {
-        if (aligned) hipLaunchKernelGGL((k_draw<kBF16, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_draw<kBF16, false>), grid, block, 0, s, p);
+        if (aligned) hipLaunchKernelGGL((k_draw<kBF16>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_draw_unaligned<kBF16>), grid, block, 0, s, p);
     } else {
-        if (aligned) hipLaunchKernelGGL((k_draw<kF32, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_draw<kF32, false>), grid, block, 0, s, p);
+        if (aligned) hipLaunchKernelGGL((k_draw<kF32>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_draw_unaligned<kF32>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }
