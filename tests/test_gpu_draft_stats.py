@@ -99,3 +99,25 @@ def test_verify_with_draft_stats_and_mtp(oracle):
                                                acc.cpu().numpy(), emi.cpu().numpy())
     assert np.array_equal(tok.cpu().numpy(), ref_tok)
     assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid)
+
+
+def test_verify_with_draft_stats_ragged_and_greedy_rows(oracle):
+    """Lengths 0..n, T = 0 sequences (their statistics are NaN and never read),
+    odd V, and a second call on the same workspace: decisions equal the plain
+    call's except at near-ties, and the oracle's everywhere."""
+    B, n, V = 30, 6, 1001
+    d = synth.make(5, 530, device=DEV, B=B, V=V, n=n)
+    d["draft_lens"].copy_(torch.arange(B, dtype=torch.int32, device=DEV) % (n + 1))
+    stats = sv.draft_row_stats(d["draft"], d["temperature"])
+    T = d["temperature"].cpu().numpy()
+    assert np.isnan(stats.cpu().numpy()[T == 0]).all()
+    need = sv.sv_workspace_bytes(B, n, V, sv.SV_BF16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                            d["temperature"], d["uniforms"], draft_stats=stats, workspace=ws)
+        torch.cuda.synchronize()
+        ora = _oracle(oracle, d)
+        rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(), T, n)
+        assert rep.hard == 0, rep
+    assert int(ws.count_nonzero()) == 0

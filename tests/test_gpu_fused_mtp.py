@@ -141,3 +141,31 @@ def test_fused_leaves_workspace_zero():
                                   workspace=ws)
     torch.cuda.synchronize()
     assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_fused_no_drafts(oracle, mode):
+    """n = 0 (standard sampling / argmax of one row, the token buffer has one
+    slot): the shift moves nothing and slot 0 receives the emitted token."""
+    B, V = 9, 4099
+    g = torch.Generator(device=DEV).manual_seed(77)
+    target = (torch.randn((B, 1, V), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    draft = torch.empty((B, 0, V), dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((B, 0), dtype=torch.int32, device=DEV)
+    lens = torch.zeros(B, dtype=torch.int32, device=DEV)
+    temp = torch.tensor([0.7, 1.0, 0.0, 0.5, 0.9, 0.0, 1.3, 0.7, 0.8], device=DEV)
+    u = torch.rand((B, 1), generator=g, device=DEV)
+    tok = torch.randint(0, V, (B, 1), generator=g, device=DEV, dtype=torch.int32)
+    tok0 = tok.clone()
+    hid = torch.randn((B, 1, 24), generator=g, device=DEV).to(torch.bfloat16)
+    dst = torch.zeros_like(hid)
+    if mode == "greedy":
+        acc, emi = sv.spec_verify_greedy_mtp(target, x, lens, tok, hid, dst)
+    else:
+        acc, emi = sv.spec_verify_sample_mtp(target, draft, x, lens, temp, u, tok, hid, dst)
+    torch.cuda.synchronize()
+    assert (acc.cpu().numpy() == 0).all()
+    assert np.array_equal(tok.cpu().numpy(), emi.cpu().numpy())
+    assert torch.equal(dst.view(torch.int16), hid.view(torch.int16))
+    ref_tok, _ = oracle.mtp_shift_insert(tok0.cpu().numpy(), None, acc.cpu().numpy(), emi.cpu().numpy())
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
