@@ -49,6 +49,8 @@ CONFIGS = {
     3: Config(3, "greedy_verify_mtp_shift", 256, 4, 128256, torch.bfloat16, H=8192, mode="greedy"),
     4: Config(4, "single_token_mtp", 512, 1, 129280, torch.bfloat16, H=7168),
     5: Config(5, "long_ragged_drafts", 1024, 8, 152064, torch.bfloat16),
+    # config 2's recipe at the greedy headline's shape (B=256, n=4, V=128256)
+    6: Config(6, "sampling_at_headline_shape", 256, 4, 128256, torch.bfloat16),
 }
 
 
@@ -78,6 +80,7 @@ def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None 
       hidden [B, n+1, H] (when H > 0).
     """
     cfg = CONFIGS[cid]
+    rc = 2 if cid == 6 else cid  # the recipe
     B = cfg.B if B is None else B
     V = cfg.V if V is None else V
     n = cfg.n if n is None else n
@@ -91,28 +94,28 @@ def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None 
     draft_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
 
     # per-sequence scalars first (small), drawn in a fixed order
-    if cid == 1:
+    if rc == 1:
         lens = torch.full((B,), n, dtype=torch.int32, device=dev)
         temp = torch.full((B,), 1.0, dtype=torch.float32, device=dev)
         sigma = torch.full((B,), 0.5, device=dev)
         scale = 2.0
-    elif cid == 2:
+    elif rc == 2:
         lens = torch.randint(1, n + 1, (B,), generator=g, device=dev, dtype=torch.int32) if n > 0 \
             else torch.zeros(B, dtype=torch.int32, device=dev)
         temp = torch.full((B,), 0.7, dtype=torch.float32, device=dev)
         sigma = torch.full((B,), 1.0, device=dev)
         scale = 3.0
-    elif cid == 3:
+    elif rc == 3:
         lens = torch.full((B,), n, dtype=torch.int32, device=dev)
         temp = torch.zeros((B,), dtype=torch.float32, device=dev)
         sigma = None
         scale = 3.0
-    elif cid == 4:
+    elif rc == 4:
         lens = torch.full((B,), n, dtype=torch.int32, device=dev)
         temp = torch.full((B,), 0.6, dtype=torch.float32, device=dev)
         sigma = torch.full((B,), 0.7, device=dev)
         scale = 3.0
-    elif cid == 5:
+    elif rc == 5:
         lens = torch.randint(0, n + 1, (B,), generator=g, device=dev, dtype=torch.int32)
         choices = torch.tensor([0.0, 0.7, 1.0], device=dev)
         temp = choices[torch.randint(0, 3, (B,), generator=g, device=dev)].to(torch.float32)
@@ -125,11 +128,11 @@ def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None 
         b1 = min(B, b0 + block)
         nb = b1 - b0
         zt = scale * torch.randn((nb, n + 1, V), generator=g, device=dev, dtype=torch.float32)
-        if cid == 2 and V > 20:
+        if rc == 2 and V > 20:
             # top-20 boost: the 20 largest logits of each target row gain +6
             top = torch.topk(zt, 20, dim=-1).indices
             zt.scatter_add_(-1, top, torch.full(top.shape, 6.0, device=dev))
-        if cid == 3:
+        if rc == 3:
             # plant the row's top token (in 1/8 of rows also a tied twin)
             rows = nb * (n + 1)
             ztf = zt.view(rows, V)
@@ -220,7 +223,7 @@ def expected_rows(cfg: Config) -> float:
     n = cfg.n
     if cfg.cid == 1:
         return 2 * n + 1
-    if cfg.cid == 2:
+    if cfg.cid in (2, 6):
         return sum((L + 1) + L for L in range(1, n + 1)) / n * cfg.B
     if cfg.cid == 3:
         return (n + 1) * cfg.B

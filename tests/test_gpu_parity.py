@@ -151,7 +151,7 @@ def test_sample_parity_small(oracle, cid, B, V, n, seed):
     assert fl == seq_flags_or(ora)
 
 
-@pytest.mark.parametrize("cid,nseq", [(2, 64), (4, 128), (5, 96)])
+@pytest.mark.parametrize("cid,nseq", [(2, 64), (4, 128), (5, 96), (6, 64)])
 def test_sample_parity_full_size(oracle, cid, nseq):
     """Full-size workloads; the oracle checks a sample of sequences."""
     d = synth.make(cid, cid * 101, device=DEV)
