@@ -179,15 +179,21 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    # HIP events on the launch stream bracket the verify launch of every 8th step
-    # and the MTP launch of every 8th step (offset 4): each event pair costs a few
-    # microseconds of queue time, so bracketing every launch would slow the step.
+    # HIP events on the launch stream.  An event pair costs a few microseconds of
+    # queue time, so when the step is one call (the fused step, or a verify with
+    # no MTP), one pair brackets RUN consecutive steps in every 2*RUN and the
+    # launch time is the bracket over RUN; with a separate MTP call, pairs bracket
+    # the verify launch of every 8th step and the MTP launch of every 8th step
+    # (offset 4).
     K = args.steps
     EVERY = 8
-    ev_v = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for i in range(0, K, EVERY)}
+    single = not (cfg.H and not fused)
+    RUN = 8 if single and K >= 8 else 1
+    starts = range(0, K - RUN + 1, 2 * RUN) if single else range(0, K, EVERY)
+    ev_v = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in starts}
+    ends = {i + RUN - 1: i for i in ev_v}
     ev_m = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for i in range(EVERY // 2, K, EVERY)} if cfg.H and not fused else {}
+            for i in range(EVERY // 2, K, EVERY)} if not single else {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -196,8 +202,8 @@ def main():
         if e:
             e[0].record(stream)
         verify(d)
-        if e:
-            e[1].record(stream)
+        if i in ends:
+            ev_v[ends[i]][1].record(stream)
         e = ev_m.get(i)
         if e:
             e[0].record(stream)
@@ -207,7 +213,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    verify_ms = [a.elapsed_time(b) for a, b in ev_v.values()]
+    verify_ms = [a.elapsed_time(b) / RUN for a, b in ev_v.values()]
     mtp_ms = [a.elapsed_time(b) for a, b in ev_m.values()] or [0.0]
     ms_per_step = elapsed * 1e3 / K
     rows_total = sum(rows_per_step[i % sets] for i in range(K))
@@ -219,7 +225,8 @@ def main():
     # fused: the hidden states and the token buffer cross HBM once each way (the
     # verify outputs are not read back)
     fused_mtp_bytes = 2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4
-    v_bytes = statistics.fmean(verify_bytes[i % sets] + (fused_mtp_bytes if fused else 0) for i in ev_v)
+    v_bytes = statistics.fmean(verify_bytes[(i + r) % sets] + (fused_mtp_bytes if fused else 0)
+                               for i in ev_v for r in range(RUN))
     v_gbps = v_bytes / (v_avg_ms * 1e-3) / 1e9
     m_avg_ms = statistics.fmean(mtp_ms) if cfg.H and not fused else 0.0
     mean_acc = float(torch.stack([d["acc"].float().mean() for d in data]).mean())
@@ -266,7 +273,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(v_gbps, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(v_gbps / PEAK_GBPS, 4),
                      "bytes_per_launch": int(v_bytes), "avg_launch_us": round(v_avg_ms * 1e3, 2),
-                     "timed_launches": len(verify_ms), "bare_event_pair_us": round(event_pair_us, 2),
+                     "timed_launches": len(verify_ms) * RUN,
+                     "timing": (f"HIP event pair around {RUN} consecutive launches, every {2 * RUN} steps"
+                                if RUN > 1 else "HIP event pair around the launch of every 8th step"),
+                     "bare_event_pair_us": round(event_pair_us, 2),
                      "traffic": traffic},
     }
 

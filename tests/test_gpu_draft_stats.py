@@ -121,3 +121,24 @@ def test_verify_with_draft_stats_ragged_and_greedy_rows(oracle):
         rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(), T, n)
         assert rep.hard == 0, rep
     assert int(ws.count_nonzero()) == 0
+
+
+def test_fp32_logits_with_draft_stats_and_mtp(oracle):
+    """fp32 logits (config 1's recipe, several sequences) through the extended
+    call with both optional parts."""
+    d = synth.make(1, 540, device=DEV, B=6, V=32000, H=16)
+    stats = sv.draft_row_stats(d["draft"], d["temperature"])
+    tok = d["tokens"].clone()
+    dst = torch.zeros_like(d["hidden"])
+    acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                        d["temperature"], d["uniforms"], draft_stats=stats, tokens=tok,
+                                        hidden_src=d["hidden"], hidden_dst=dst)
+    torch.cuda.synchronize()
+    ora = _oracle(oracle, d)
+    rep = compare(acc.cpu().numpy(), emi.cpu().numpy(), ora, d["draft_lens"].cpu().numpy(),
+                  d["temperature"].cpu().numpy(), d["n"])
+    assert rep.hard == 0, rep
+    ref_tok, ref_hid = oracle.mtp_shift_insert(d["tokens"].cpu().numpy(), d["hidden"].cpu().view(torch.int16).numpy(),
+                                               acc.cpu().numpy(), emi.cpu().numpy())
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
+    assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid)
