@@ -39,12 +39,6 @@
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
 #endif
-#ifndef SV_LOAD_FENCE
-#define SV_LOAD_FENCE 0
-#endif
-#ifndef SV_PIPELINE
-#define SV_PIPELINE 0
-#endif
 #ifndef SV_MS_UNROLL
 #define SV_MS_UNROLL 4
 #endif
@@ -64,14 +58,6 @@ namespace sv {
 
 // one 16-byte load of streamed logits (read once: optionally non-temporal)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Keeps the scheduler from moving the consumers of a group of loads above the
-// group: every load of the group is in flight before the first wait.
-#if SV_LOAD_FENCE
-#define SV_AFTER_LOADS() __builtin_amdgcn_sched_barrier(0)
-#else
-#define SV_AFTER_LOADS() ((void)0)
-#endif
-
 __device__ __forceinline__ uint4 ld16(const uint4* p) {
 #if SV_NT_LOAD
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -347,30 +333,10 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
         int bestv = -1;
         uint4 bestw = make_uint4(0, 0, 0, 0);
         int v = v0 + tid;
-#if SV_PIPELINE
-        uint4 nxt[U];
-        bool more = v + (U - 1) * kThreads < v1;
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + u * kThreads);
-        }
-        while (more) {
-            uint4 w[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nxt[u];
-            more = v + U * kThreads + (U - 1) * kThreads < v1;
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + U * kThreads + u * kThreads);
-            }
-            SV_AFTER_LOADS();
-#else
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
-            SV_AFTER_LOADS();
-#endif
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float f[kVec];
@@ -384,9 +350,6 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
                     bestw = w[u];
                 }
             }
-#if SV_PIPELINE
-            v += U * kThreads;
-#endif
         }
         for (; v < v1; v += kThreads) {
             const uint4 w = ld16(vrow + v);
@@ -440,31 +403,10 @@ __device__ MS thread_ms(const void* row, int lo, int hi, float c) {
         const int v0 = lo / kVec, v1 = hi / kVec;
         constexpr int U = SV_MS_UNROLL;
         int v = v0 + tid;
-#if SV_PIPELINE
-        uint4 nxt[U];
-        bool more = v + (U - 1) * kThreads < v1;
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + u * kThreads);
-        }
-        while (more) {
-            uint4 w[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = nxt[u];
-            more = v + U * kThreads + (U - 1) * kThreads < v1;
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) nxt[u] = ld16(vrow + v + U * kThreads + u * kThreads);
-            }
-            v += U * kThreads;
-            SV_AFTER_LOADS();
-#else
         for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
             uint4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
-            SV_AFTER_LOADS();
-#endif
             float f[U][kVec];
 #pragma unroll
             for (int u = 0; u < U; ++u) unpack<DT>(w[u], f[u]);
