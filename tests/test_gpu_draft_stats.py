@@ -142,3 +142,21 @@ def test_fp32_logits_with_draft_stats_and_mtp(oracle):
                                                acc.cpu().numpy(), emi.cpu().numpy())
     assert np.array_equal(tok.cpu().numpy(), ref_tok)
     assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid)
+
+
+def test_draft_loop_with_row_index_gives_the_same_statistics():
+    """The serving-loop form: step j samples from row j of the [B, n, V] draft
+    buffer through row_index and keeps that row's statistics; they are the ones
+    the one-call helper computes."""
+    d = synth.make(2, 550, device=DEV, B=20, V=9000)
+    B, n = d["B"], d["n"]
+    stats = torch.empty((B, n, 2), dtype=torch.float32, device=DEV)
+    stats_j = torch.empty((B, 2), dtype=torch.float32, device=DEV)
+    u = torch.rand((B, n), device=DEV)
+    for j in range(n):
+        row = torch.full((B,), j, dtype=torch.int32, device=DEV)
+        sv.sv_sample_rows(d["draft"], d["temperature"], u[:, j].contiguous(), row_index=row, row_stats=stats_j)
+        stats[:, j] = stats_j
+    ref = sv.draft_row_stats(d["draft"], d["temperature"])
+    torch.cuda.synchronize()
+    assert torch.equal(stats, ref)
