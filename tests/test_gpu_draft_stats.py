@@ -159,4 +159,7 @@ def test_draft_loop_with_row_index_gives_the_same_statistics():
         stats[:, j] = stats_j
     ref = sv.draft_row_stats(d["draft"], d["temperature"])
     torch.cuda.synchronize()
-    assert torch.equal(stats, ref)
+    # the maxima are exact; the sums agree to rounding (the two calls chunk the
+    # rows differently, so their fp32 partial sums are added in another order)
+    assert torch.equal(stats[..., 0], ref[..., 0])
+    assert torch.allclose(stats[..., 1], ref[..., 1], rtol=1e-5, atol=0)
