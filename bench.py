@@ -1,6 +1,6 @@
 """Benchmark of the verify-and-sample hot path on one MI355X.
 
-Default workload (the headline): greedy verify + MTP shift/insert at B=256
+Default workload: greedy verify + MTP shift/insert at B=256
 sequences, n=4 drafts, V=128256 bf16 logits, hidden size 8192.  One step =
 spec_verify_greedy_mtp(): the verification of the [256, 5, 128256] target
 logits with the shift/insert of the [256, 5] token buffer and the carry of the

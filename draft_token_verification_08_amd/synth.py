@@ -49,8 +49,8 @@ CONFIGS = {
     3: Config(3, "greedy_verify_mtp_shift", 256, 4, 128256, torch.bfloat16, H=8192, mode="greedy"),
     4: Config(4, "single_token_mtp", 512, 1, 129280, torch.bfloat16, H=7168),
     5: Config(5, "long_ragged_drafts", 1024, 8, 152064, torch.bfloat16),
-    # config 2's recipe at the greedy headline's shape (B=256, n=4, V=128256)
-    6: Config(6, "sampling_at_headline_shape", 256, 4, 128256, torch.bfloat16),
+    # the llama-vocab sampling recipe at B=256, n=4, V=128256 (the greedy workload's shape)
+    6: Config(6, "llama_vocab_sampling_b256", 256, 4, 128256, torch.bfloat16),
 }
 
 

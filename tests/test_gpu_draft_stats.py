@@ -124,7 +124,7 @@ def test_verify_with_draft_stats_ragged_and_greedy_rows(oracle):
 
 
 def test_fp32_logits_with_draft_stats_and_mtp(oracle):
-    """fp32 logits (config 1's recipe, several sequences) through the extended
+    """fp32 logits (the tiny fp32 sampling recipe, several sequences) through the extended
     call with both optional parts."""
     d = synth.make(1, 540, device=DEV, B=6, V=32000, H=16)
     stats = sv.draft_row_stats(d["draft"], d["temperature"])

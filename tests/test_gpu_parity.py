@@ -130,7 +130,7 @@ def test_greedy_ties_everywhere(oracle):
 # ------------------------------------------------------------------ sampling
 
 SMALL = [
-    (1, None, None, None, 101),       # config 1 in full (fp32, V=32000)
+    (1, None, None, None, 101),       # the tiny fp32 sampling workload in full (V=32000)
     (2, 16, 20000, None, 202),
     (2, 12, 9001, None, 203),         # V*2 % 16 != 0: scalar path
     (4, 64, 8192, None, 404),
