@@ -183,6 +183,80 @@ def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None 
     return out
 
 
+def make_lmhead(seed: int, device="cpu", B: int = 256, n: int = 4, V: int = 128256, H: int = 8192,
+                exact: bool = True, ragged: bool = False) -> dict:
+    """Inputs of the fused logit projection + greedy verify: the target's final
+    hidden states and its logit projection instead of materialised logits.
+
+    Returns hidden [B, n+1, H] bf16, weight [V, H] bf16 (one row per vocabulary
+    entry), draft_tokens [B, n], draft_lens [B], tokens [B, n+1] (MTP buffer).
+
+    exact=True: every hidden value is an integer in [-R, R] times 2^-4 and every
+    weight an integer in [-R, R] times 2^-e, with R = min(44, sqrt(2^24 / H)) and
+    e chosen so that the logits have a standard deviation near 3.  Every partial
+    sum of a logit is then an integer multiple of 2^-(4+e) below 2^24 such
+    units in magnitude, exactly representable in binary32, so the logits (and
+    their argmax) do not depend on the order of summation.
+    exact=False: weight ~ N(0, 9/H) and hidden ~ N(0, 1) (logits ~ N(0, 9)).
+
+    As in the greedy logits recipe, each row's top token is planted: hidden row
+    m leans towards weight row a_m (its logit sits about 6.5 standard deviations
+    above the mean), and in 1/8 of rows a twin index receives a copy of weight
+    row a_m, so the two logits tie exactly in every row.  Drafts are the planted
+    top (or its twin) with probability 0.7, otherwise another index.
+    """
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    M = B * (n + 1)
+    if exact:
+        R = int(min(44, math.isqrt((1 << 24) // H)))
+        Wi = torch.randint(-R, R + 1, (V, H), generator=g, device=dev, dtype=torch.int16)
+    else:
+        Wf = (3.0 / math.sqrt(H)) * torch.randn((V, H), generator=g, device=dev, dtype=torch.float32)
+    a_top = torch.randint(0, V, (M,), generator=g, device=dev)
+    a_tie = (a_top + 1 + torch.randint(0, max(V - 1, 1), (M,), generator=g, device=dev)) % V
+    tie = (torch.rand((M,), generator=g, device=dev) < 0.125) & (V > 1)
+    W = Wi if exact else Wf
+    for m in torch.nonzero(tie).flatten().tolist():  # in row order: later copies win
+        W[a_tie[m]] = W[a_top[m]]
+    if exact:
+        noise = torch.randint(-R + 3, R - 2, (M, H), generator=g, device=dev, dtype=torch.int16)
+        # the lean adds about lam * H * var(w) units to the planted logit: 6.5 standard deviations
+        lam = 6.5 * math.sqrt(((2 * R - 5) ** 2 - 1) / 12.0) / (math.sqrt(H) * math.sqrt((((2 * R + 1) ** 2) - 1) / 12.0))
+        lean = torch.round(lam * Wi[a_top].float()).to(torch.int16)
+        a = torch.clamp(noise + lean, -R, R)
+        hidden = (a.float() * 2.0 ** -4).to(torch.bfloat16)
+        var_w = (((2 * R + 1) ** 2) - 1) / 12.0
+        var_h = (((2 * R - 5) ** 2) - 1) / 12.0
+        e = round(math.log2(math.sqrt(H * var_h * var_w) / 16.0 / 3.0))
+        weight = (Wi.float() * 2.0 ** -e).to(torch.bfloat16)
+        del Wi, noise, lean, a
+    else:
+        mu = 6.5 / math.sqrt(H)
+        hidden = (torch.randn((M, H), generator=g, device=dev) + mu * Wf[a_top] * (math.sqrt(H) / 3.0))
+        hidden = hidden.to(torch.bfloat16)
+        weight = Wf.to(torch.bfloat16)
+        del Wf
+    hidden = hidden.view(B, n + 1, H)
+    if ragged:
+        lens = torch.randint(0, n + 1, (B,), generator=g, device=dev, dtype=torch.int32)
+    else:
+        lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    top = a_top.view(B, n + 1)[:, :n]
+    twin = a_tie.view(B, n + 1)[:, :n]
+    tie = tie.view(B, n + 1)[:, :n]
+    hit = torch.rand((B, n), generator=g, device=dev) < 0.7
+    pick_twin = tie & (torch.rand((B, n), generator=g, device=dev) < 0.5)
+    match = torch.where(pick_twin, twin, top)
+    other = torch.randint(0, max(V - 1, 1), (B, n), generator=g, device=dev)
+    other = torch.where(other >= top, other + 1, other) % V
+    draft_tokens = torch.where(hit, match, other).to(torch.int32)
+    first = torch.randint(0, V, (B, 1), generator=g, device=dev, dtype=torch.int32)
+    tokens = torch.cat([first, draft_tokens], dim=1).contiguous()
+    return dict(B=B, n=n, V=V, H=H, hidden=hidden.contiguous(), weight=weight.contiguous(),
+                draft_tokens=draft_tokens.contiguous(), draft_lens=lens, tokens=tokens)
+
+
 def make_law_case(seed: int, trials: int, V: int = 8, n: int = 4, T: float = 1.0,
                   draft_sigma: float = 1.0, device="cpu") -> dict:
     """Many trials of one fixed set of rows (for distribution-law tests).

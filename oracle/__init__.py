@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "specverify_oracle.c")
 LIB = os.path.join(HERE, "libspecverify_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 FLAG_LEN_CLAMPED, FLAG_TOKEN_OOR, FLAG_BAD_TEMP, FLAG_BAD_UNIFORM, FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
 FLAG_ROW_CLAMPED = 32
 
@@ -59,19 +59,23 @@ class Oracle:
         L.sv_oracle_sample_rows.argtypes = [vp, C.c_int, C.c_int, i32p, f32p, f32p, C.c_int, C.c_int, i32p,
                                             u32p, C.c_int]
         L.sv_oracle_sample_rows.restype = C.c_int
+        L.sv_oracle_lmhead_logits.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, i32p, C.c_int, f64p, C.c_int]
+        L.sv_oracle_lmhead_logits.restype = C.c_int
         L.sv_oracle_plant.argtypes = []
         L.sv_oracle_plant.restype = C.c_int
 
     # -- marshalling helpers -------------------------------------------------
     @staticmethod
     def _logits(a: np.ndarray):
-        """Accept fp32 arrays or bf16 bit patterns stored as uint16."""
+        """Accept fp32 or float64 arrays, or bf16 bit patterns stored as uint16."""
         a = np.ascontiguousarray(a)
         if a.dtype == np.float32:
             return a, F32
+        if a.dtype == np.float64:
+            return a, F64
         if a.dtype == np.uint16:
             return a, BF16
-        raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+        raise TypeError(f"logits must be float32, float64 or uint16 (bf16 bits), got {a.dtype}")
 
     @staticmethod
     def _p(a):
@@ -159,6 +163,26 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"sv_oracle_sample_rows failed: {rc}")
         return dict(tokens=tok, seq_flags=fl)
+
+    def lmhead_logits(self, hidden, weight, rows=None, threads=1):
+        """Logits of the target's logit projection in double: hidden [M, H] and
+        weight [V, H] as bf16 bit patterns (uint16); rows selects hidden rows
+        (all M when None).  Returns float64 [len(rows), V]."""
+        h = np.ascontiguousarray(hidden, dtype=np.uint16)
+        w = np.ascontiguousarray(weight, dtype=np.uint16)
+        H = h.shape[-1]
+        h = h.reshape(-1, H)
+        M = h.shape[0]
+        V = w.shape[0]
+        assert w.shape == (V, H)
+        r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32).reshape(-1)
+        nrows = M if r is None else r.shape[0]
+        out = np.empty((nrows, V), np.float64)
+        rc = self.lib.sv_oracle_lmhead_logits(self._p(h), self._p(w), M, H, V, self._p(r), nrows,
+                                              self._p(out), int(threads))
+        if rc != 0:
+            raise RuntimeError(f"sv_oracle_lmhead_logits failed: {rc}")
+        return out
 
     def softmax_row(self, z, T):
         z, dt = self._logits(np.asarray(z).reshape(-1))

@@ -60,6 +60,7 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F64 2 /* logits already in double (e.g. from sv_oracle_lmhead_logits) */
 
 #define OR_FLAG_LEN_CLAMPED 1u
 #define OR_FLAG_TOKEN_OOR 2u
@@ -76,6 +77,7 @@
  * widening is exact: place the 16 bits in the high half of a 32-bit word. */
 static double logit_at(const void *rows, int dt, size_t idx)
 {
+    if (dt == OR_F64) return ((const double *)rows)[idx];
     if (dt == OR_BF16) {
         uint32_t bits = ((uint32_t)((const uint16_t *)rows)[idx]) << 16;
         float f;
@@ -429,7 +431,7 @@ int sv_oracle_sample_rows(const void *logits, int dt, int R, const int32_t *row_
 {
     if (B < 0 || R < 1 || V < 1) return -1;
     if (B == 0) return 0;
-    const size_t es = (dt == OR_BF16) ? 2 : 4;
+    const size_t es = (dt == OR_BF16) ? 2 : (dt == OR_F64) ? 8 : 4;
     unsigned char *rows = (unsigned char *)malloc((size_t)B * (size_t)V * es);
     int32_t *zeros = (int32_t *)calloc((size_t)B, sizeof(int32_t));
     int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)B);
@@ -453,6 +455,96 @@ int sv_oracle_sample_rows(const void *logits, int dt, int R, const int32_t *row_
     free(rows);
     free(zeros);
     free(acc);
+    return rc;
+}
+
+/* ------------------------------------------------------- logit projection */
+
+/* The target's logit projection (its lm_head): a [V][H] matrix that maps a
+ * final hidden state to one logit per vocabulary entry.  The MTP section of
+ * "Accelerating Sonar through speculation" (the paragraph on the MTP head's
+ * normalisation layers) notes that the MTP head reuses this projection, which is
+ * about 2 GB for a 70B Llama; the model runs it to produce the logits the step
+ * samples from (Inference with speculative decoding section, first paragraph).
+ *
+ *   logits[i][v] = sum_k hidden[r_i][k] * weight[v][k]
+ *
+ * for the hidden rows r_i = rows[i] (rows NULL: r_i = i, nrows = M).  bf16
+ * inputs are widened exactly; each product is exact in double (two 8-bit
+ * significands) and the sum runs in double in ascending k. */
+typedef struct {
+    const uint16_t *hidden, *weight;
+    int M, H, V;
+    const int32_t *rows;
+    int nrows;
+    double *out;
+    long long i0, i1; /* flat output range [i0, i1) of this thread */
+    int status;
+} lm_job_t;
+
+static double bf16_at(const uint16_t *p, size_t idx)
+{
+    uint32_t bits = ((uint32_t)p[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static void *lm_slice(void *arg)
+{
+    lm_job_t *J = (lm_job_t *)arg;
+    const int H = J->H, V = J->V;
+    for (long long o = J->i0; o < J->i1; ++o) {
+        const int i = (int)(o / V), v = (int)(o % V);
+        const int r = J->rows ? J->rows[i] : i;
+        if (r < 0 || r >= J->M) {
+            J->status = -1;
+            return NULL;
+        }
+        double acc = 0.0;
+        for (int k = 0; k < H; ++k)
+            acc += bf16_at(J->hidden, (size_t)r * H + k) * bf16_at(J->weight, (size_t)v * H + k);
+        J->out[o] = acc;
+    }
+    return NULL;
+}
+
+int sv_oracle_lmhead_logits(const uint16_t *hidden, const uint16_t *weight, int M, int H, int V,
+                            const int32_t *rows, int nrows, double *out, int threads)
+{
+    if (M < 0 || H < 1 || V < 1 || nrows < 0 || (!rows && nrows != M)) return -1;
+    if (threads < 1) threads = 1;
+    const long long total = (long long)nrows * V;
+    if (total == 0) return 0;
+    if (threads > total) threads = (int)total;
+    lm_job_t *sl = (lm_job_t *)calloc((size_t)threads, sizeof(lm_job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!sl || !th) { free(sl); free(th); return -2; }
+    int rc = 0;
+    for (int t = 0; t < threads; ++t) {
+        lm_job_t J = {hidden, weight, M, H, V, rows, nrows, out,
+                      total * t / threads, total * (t + 1) / threads, 0};
+        sl[t] = J;
+    }
+    if (threads == 1) {
+        lm_slice(&sl[0]);
+        rc = sl[0].status;
+    } else {
+        /* a slice whose thread cannot be started runs on the calling thread */
+        unsigned char *started = (unsigned char *)calloc((size_t)threads, 1);
+        if (!started) { free(sl); free(th); return -2; }
+        for (int t = 0; t < threads; ++t) {
+            started[t] = pthread_create(&th[t], NULL, lm_slice, &sl[t]) == 0;
+            if (!started[t]) lm_slice(&sl[t]);
+        }
+        for (int t = 0; t < threads; ++t) {
+            if (started[t]) pthread_join(th[t], NULL);
+            if (sl[t].status) rc = sl[t].status;
+        }
+        free(started);
+    }
+    free(sl);
+    free(th);
     return rc;
 }
 
