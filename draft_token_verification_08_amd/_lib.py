@@ -68,6 +68,10 @@ def lib():
                                         vp, sz, vp]
     L.spec_verify_sample_ex.restype = i
     L.sv_sample_rows.restype = i
+    L.spec_verify_greedy_lmhead.argtypes = [vp, vp, i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy_lmhead.restype = i
+    L.sv_lmhead_logits_debug.argtypes = [vp, vp, i, i, i, vp, vp]
+    L.sv_lmhead_logits_debug.restype = i
     L.sv_softmax_rows_debug.argtypes = [vp, i, vp, i, i, vp, vp]
     L.sv_softmax_rows_debug.restype = i
     _lib = L
@@ -342,6 +346,68 @@ def spec_verify_sample_ex(target_logits, draft_logits, draft_tokens, draft_lens,
     return accepted_len, emitted
 
 
+def _lmhead_args(hidden, weight, draft_tokens, draft_lens, tokens, hidden_dst):
+    """Checks of the fused projection + greedy verify arguments; returns (B, n, V, H)."""
+    if hidden.dim() != 3:
+        raise ValueError("hidden must be [B, n+1, H]")
+    B, n1, H = hidden.shape
+    dev = hidden.device
+    _check(hidden, "hidden", torch.bfloat16, None, dev)
+    if weight.dim() != 2 or weight.shape[1] != H:
+        raise ValueError(f"weight must be [V, {H}], got {tuple(weight.shape)}")
+    _check(weight, "weight", torch.bfloat16, None, dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n1 - 1), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    if tokens is not None:
+        _check(tokens, "tokens", torch.int32, (B, n1), dev)
+    if hidden_dst is not None:
+        _check(hidden_dst, "hidden_dst", torch.bfloat16, (B, n1, H), dev)
+    return B, n1 - 1, weight.shape[0], H
+
+
+def spec_verify_greedy_lmhead(hidden, weight, draft_tokens, draft_lens, *, tokens=None, hidden_dst=None,
+                              accepted_len=None, emitted=None, err_flags=None, workspace=None, stream=None):
+    """Greedy verify on the logits hidden @ weight.T without materialising them
+    (see include/specverify.h).  hidden [B, n+1, H] and weight [V, H] bf16.
+    Returns (accepted_len, emitted); tokens (optional) gets the MTP shift/insert
+    and hidden_dst (optional) the carried hidden states."""
+    B, n, V, H = _lmhead_args(hidden, weight, draft_tokens, draft_lens, tokens, hidden_dst)
+    dev = hidden.device
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n + 1), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, n, V, SV_BF16)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("spec_verify_greedy_lmhead", _ptr(hidden), _ptr(weight), H, _ptr(draft_tokens), _ptr(draft_lens), B, n,
+          V, _ptr(accepted_len), _ptr(emitted), _ptr(err_flags), _ptr(tokens), _ptr(hidden_dst), _ptr(workspace),
+          workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted
+
+
+def sv_lmhead_logits_debug(hidden, weight, *, logits_out=None, stream=None):
+    """Parity/debug: the binary32 logits hidden @ weight.T from the projection
+    kernel.  hidden [M, H] (or [..., H]) and weight [V, H] bf16."""
+    H = hidden.shape[-1]
+    h2 = hidden.reshape(-1, H)
+    M = h2.shape[0]
+    dev = hidden.device
+    _check(h2, "hidden", torch.bfloat16, None, dev)
+    _check(weight, "weight", torch.bfloat16, None, dev)
+    V = weight.shape[0]
+    if logits_out is None:
+        logits_out = torch.empty((M, V), dtype=torch.float32, device=dev)
+    _check(logits_out, "logits_out", torch.float32, (M, V), dev)
+    _call("sv_lmhead_logits_debug", _ptr(h2), _ptr(weight), M, H, V, _ptr(logits_out), _stream(stream, dev))
+    return logits_out
+
+
 def draft_row_stats(draft_logits, temperature, *, workspace=None, stream=None):
     """{max, sum 2^((z - max) log2e/T)} of every draft row [B, n, V] at the
     sequences' temperatures, as the draft's sampling step writes them: one
@@ -575,3 +641,17 @@ def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None
     _call("sv_sample_rows", _ptr(logits), dt, R, _ptr(row_index), _ptr(temperature), _ptr(uniforms), B, V,
           _ptr(tokens), _ptr(err_flags), _ptr(row_stats), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     return tokens
+
+
+def prepare_spec_verify_greedy_lmhead(hidden, weight, draft_tokens, draft_lens, accepted_len, emitted, workspace,
+                                      tokens=None, hidden_dst=None, err_flags=None, stream=None) -> Prepared:
+    B, n, V, H = _lmhead_args(hidden, weight, draft_tokens, draft_lens, tokens, hidden_dst)
+    dev = hidden.device
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n + 1), dev)
+    _check(workspace, "workspace", torch.uint8)
+    args = (_ptr(hidden), _ptr(weight), H, _ptr(draft_tokens), _ptr(draft_lens), B, n, V, _ptr(accepted_len),
+            _ptr(emitted), _ptr(err_flags), _ptr(tokens), _ptr(hidden_dst), _ptr(workspace), workspace.numel(),
+            _stream(stream, dev))
+    return Prepared("spec_verify_greedy_lmhead", args, (hidden, weight, draft_tokens, draft_lens, accepted_len,
+                                                         emitted, workspace, tokens, hidden_dst, err_flags))

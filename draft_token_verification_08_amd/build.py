@@ -40,14 +40,17 @@ def build(out: str = LIB, verbose: bool = False, defines=(), objdir: str | None 
     objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     k_obj = os.path.join(objdir, "sv_kernels.o")
+    l_obj = os.path.join(objdir, "sv_lmhead.o")
     a_obj = os.path.join(objdir, "sv_api.o")
     logs = []
     dflags = [f"-D{d}" for d in defines]
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
                       os.path.join(CSRC, "sv_kernels.hip"), "-o", k_obj]))
+    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
+                      os.path.join(CSRC, "sv_lmhead.hip"), "-o", l_obj]))
     logs.append(_run([HIPCC, *COMMON, *dflags, "-c", os.path.join(CSRC, "sv_api.cpp"), "-o", a_obj]))
     tmp = out + ".tmp"
-    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp]))
+    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, l_obj, a_obj, "-o", tmp]))
     os.replace(tmp, out)
     if verbose:
         print("\n".join(l for l in logs if l))

@@ -513,6 +513,109 @@ sv_status_t mtp_shift_insert(int32_t* tokens, const void* hidden_src, void* hidd
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Size checks of the logit projection: H a positive multiple of kLmBK, and the
+// 16-byte vector offsets of both matrices within 32 bits.
+bool lmhead_sizes_ok(long long M, int H, int V) {
+    if (M < 0 || V < 1 || H < sv::kLmBK || H % sv::kLmBK != 0) return false;
+    const long long lim = 1ll << 34;  // elements: (elements / 8) vectors < 2^31
+    return M * (long long)H < lim && (long long)V * H < lim;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status_t spec_verify_greedy_lmhead(const void* hidden, const void* weight, int H, const int32_t* draft_tokens,
+                                      const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
+                                      int32_t* emitted, uint32_t* err_flags, int32_t* tokens, void* hidden_dst,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_sizes(B, n, V)) return SV_EINVAL;
+    const long long M = (long long)B * (n + 1);
+    if (!lmhead_sizes_ok(M, H, V)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!hidden || !weight || !draft_lens || !accepted_len || !emitted || (n > 0 && !draft_tokens))
+        return SV_EINVAL;
+    if (!tokens && hidden_dst) return SV_EINVAL;
+    if (!aligned_to(hidden, 16) || !aligned_to(weight, 16) || !aligned_to(hidden_dst, 16) ||
+        !aligned_to(draft_tokens, 4) || !aligned_to(draft_lens, 4) || !aligned_to(accepted_len, 4) ||
+        !aligned_to(emitted, 4) || !aligned_to(err_flags, 4) || !aligned_to(tokens, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, n, V, SV_BF16, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    const size_t hbytes = (size_t)M * H * 2;
+    const bool copy = hidden_dst && hidden_dst != hidden;
+    if (tokens) {
+        const Span tok{tokens, (size_t)M * 4};
+        const Span others[] = {{hidden, hbytes},
+                               {weight, (size_t)V * H * 2},
+                               {draft_tokens, (size_t)B * n * 4},
+                               {draft_lens, (size_t)B * 4},
+                               {accepted_len, (size_t)B * 4},
+                               {emitted, (size_t)M * 4},
+                               {err_flags, err_flags ? 4u : 0u},
+                               {workspace, workspace_bytes},
+                               tok};
+        constexpr int kOthers = sizeof(others) / sizeof(others[0]);
+        if (overlaps_any(tok, others, kOthers - 1)) return SV_EINVAL;
+        if (copy && overlaps_any(Span{hidden_dst, hbytes}, others, kOthers)) return SV_EINVAL;
+    }
+    hipStream_t s = (hipStream_t)stream;
+
+    // the projection: one argmax key per row, merged into the decision's
+    // partial slots (chunk slot 0 of row r of sequence b: b * (n+1) + r)
+    sv::LmParams lp{};
+    lp.hidden = hidden;
+    lp.weight = weight;
+    lp.M = (int)M;
+    lp.H = H;
+    lp.V = V;
+    lp.keys = at<unsigned long long>(workspace, L.off_part);
+    lp.lens = draft_lens;
+    lp.n = n;
+    lp.hidden_dst = copy ? hidden_dst : nullptr;
+    hipError_t e = sv::launch_lmhead(lp, s);
+    if (e != hipSuccess) return hip_fail(e);
+
+    sv::StatsParams sp{};
+    sp.tokens = draft_tokens;
+    sp.lens = draft_lens;
+    sp.B = B; sp.n = n; sp.V = V; sp.NC = 1; sp.CH = V; sp.S = n + 1;
+    sp.acc = accepted_len;
+    sp.emitted = emitted;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.R = n + 1;
+    sp.row_index = nullptr;
+    sp.mtp.tokens = tokens;
+    e = sv::launch_decide_greedy(sp, s);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+sv_status_t sv_lmhead_logits_debug(const void* hidden, const void* weight, int M, int H, int V, float* logits_out,
+                                   void* stream) {
+    if (!lmhead_sizes_ok(M, H, V)) return SV_EINVAL;
+    if (M == 0) return SV_OK;
+    if (!hidden || !weight || !logits_out) return SV_EINVAL;
+    if (!aligned_to(hidden, 16) || !aligned_to(weight, 16) || !aligned_to(logits_out, 4)) return SV_EALIGN;
+    sv::LmParams lp{};
+    lp.hidden = hidden;
+    lp.weight = weight;
+    lp.M = M;
+    lp.H = H;
+    lp.V = V;
+    lp.logits = logits_out;
+    hipError_t e = sv::launch_lmhead(lp, (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
 sv_status_t sv_softmax_rows_debug(const void* logits, sv_dtype_t dt, const float* temperature, int rows,
                                   int V, float* probs_out, void* stream) {
     if (rows < 0 || V < 1 || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;

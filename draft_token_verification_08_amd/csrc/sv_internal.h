@@ -135,11 +135,30 @@ struct MtpParams {
     int B, n;
 };
 
-// launches (sv_kernels.hip); return the hipGetLastError() after the launch
+// The target's logit projection (lm_head) on the bf16 matrix cores:
+// logits[m][v] = sum_k hidden[m][k] * weight[v][k], accumulated in binary32.
+// With `keys` set the logits stay in registers: each workgroup reduces its
+// tile to a per-row (max, lowest index) and merges it into keys[m] by atomic
+// max; with `logits` set they are stored (parity/debug).
+struct LmParams {
+    const void* hidden;        // [M][H] bf16, 16-byte aligned, H a multiple of kLmBK
+    const void* weight;        // [V][H] bf16, 16-byte aligned
+    int M, H, V;
+    float* logits;             // [M][V] or nullptr
+    unsigned long long* keys;  // [M] or nullptr
+    const int32_t* lens;       // [B] with keys: row m = b*(n+1) + r is needed iff r <= clamp(lens[b], 0, n)
+    int n;
+    void* hidden_dst;          // nullptr or [M][H]: the hidden-state carry of the MTP step
+};
+constexpr int kLmBK = 64;      // K elements per pipeline stage of the projection
+
+// launches (sv_kernels.hip, sv_lmhead.hip); return the hipGetLastError() after the launch
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s);
 hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s);
 hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
+hipError_t launch_lmhead(const LmParams& p, hipStream_t s);
+hipError_t launch_decide_greedy(const StatsParams& p, hipStream_t s);
 hipError_t launch_softmax_debug(const void* logits, Dt dt, const float* temp, int rows, int V,
                                 float* out, bool aligned, hipStream_t s);
 

@@ -35,6 +35,7 @@
 #include <cmath>
 
 #include "sv_internal.h"
+#include "sv_device.h"
 
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
@@ -135,9 +136,6 @@ __device__ __forceinline__ unsigned long long xchg64(unsigned long long* p, unsi
 __device__ __forceinline__ unsigned xchg32(unsigned* p, unsigned v) {
     return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned long long max64(unsigned long long* p, unsigned long long v) {
-    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Arrive on a counter after the data atomic whose returned value is `dep` has
 // completed; returns the counter value before this arrival.
 __device__ __forceinline__ unsigned arrive(unsigned* cnt, unsigned long long dep) {
@@ -154,47 +152,6 @@ __device__ __forceinline__ float hi_f(unsigned long long v) { return __uint_as_f
 // --------------------------------------------------------------- wave / block reductions
 // Lanes within a row of 16 combine with DPP (quad_perm, half-row and row
 // mirrors); rows combine with cross-lane shuffles (xor 16, xor 32).
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
-
-struct ArgMax {
-    float v;
-    int i;
-};
-__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
-    // larger value wins; equal values keep the lower index
-    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
-}
-
-// 64-bit key whose unsigned order is the argmax order: order-preserving map of
-// the float in the high word, the inverted index in the low word (equal values:
-// the lower index has the larger key).  Zero is below every key of a number.
-__device__ __forceinline__ unsigned long long argmax_key(ArgMax a) {
-    unsigned u = __float_as_uint(a.v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (unsigned)a.i);
-}
-__device__ __forceinline__ ArgMax argmax_unkey(unsigned long long k) {
-    unsigned u = (unsigned)(k >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    return ArgMax{__uint_as_float(u), (int)(0xFFFFFFFFu - (unsigned)k)};
-}
-
-template <int CTRL>
-__device__ __forceinline__ ArgMax dpp_am(ArgMax a) {
-    return ArgMax{dpp_f<CTRL>(a.v), dpp_i<CTRL>(a.i)};
-}
 
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
     a = better(a, dpp_am<kDppXor1>(a));
@@ -1285,6 +1242,20 @@ __global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, 
 }
 
 // --------------------------------------------------------------- launches
+
+// Decision of greedy sequences whose row argmax keys another pass has already
+// merged (one key per row at chunk slot 0, NC = 1): the fused logit projection.
+// One workgroup per sequence.
+__global__ __launch_bounds__(kThreads) void k_decide_greedy(StatsParams p) {
+    const int b = blockIdx.x;
+    decide<kBF16, kGreedy, true>(p, b, seq_info<kGreedy>(p, b));
+}
+
+hipError_t launch_decide_greedy(const StatsParams& p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decide_greedy, dim3((unsigned)p.B), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s) {
     const unsigned blocks = (unsigned)((long long)p.B * p.S * p.NC);

@@ -1,0 +1,214 @@
+// sv_lmhead.hip -- the target's logit projection (its lm_head) on the gfx950
+// bf16 matrix cores, fused with the greedy verify's row reduction.
+//
+// "Accelerating Sonar through speculation": the model runs to produce logits
+// from which the next token is sampled (Inference with speculative decoding
+// section, first paragraph), through a logit projection that the MTP head
+// reuses and that is about 2 GB for a 70B Llama (MTP section, the paragraph on
+// the head's normalisation layers).  A greedy verify needs only each row's
+// (max, lowest index), so the [B, n+1, V] logits never have to reach memory:
+// every workgroup reduces its tile of logits in registers and merges one
+// 64-bit key per row by atomic max; the per-sequence decision then runs on the
+// keys (k_decide_greedy).
+//
+// The product is logits[m][v] = sum_k hidden[m][k] * weight[v][k], hidden
+// [M][H] and weight [V][H] both K-contiguous bf16, accumulated in binary32 by
+// v_mfma_f32_32x32x16_bf16.  Lane layout of that instruction (checked on
+// MI355X): the A operand of lane l holds row l % 32, k = (l / 32) * 8 + e
+// (e = 0..7); the B operand column l % 32 at the same k; accumulator register
+// r of lane l is row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32.  Both
+// operands are therefore 16 contiguous bytes of a K-contiguous row: one
+// ds_read_b128 each.
+//
+// Workgroup tile BM x BN = (64 WM) x (128 WN), WM x WN waves, each wave a
+// 64 x 128 block (2 x 4 accumulators of 32 x 32).  K runs in stages of 64: the
+// stage's A and B rows are loaded to registers (16-byte loads, 8 lanes per
+// 128-byte row segment), written to LDS with a 16-byte pad per row (rows 144
+// bytes apart, so the 32 lanes of a fragment read hit distinct banks), and the
+// next stage's loads are issued before the current stage's MFMAs.
+#include <cfloat>
+#include <climits>
+#include <cmath>
+
+#include "sv_internal.h"
+#include "sv_device.h"
+
+namespace sv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte load (a native vector)
+
+constexpr int kPitch = kLmBK * 2 + 16;  // LDS bytes per tile row: one stage of K plus 16 bytes of pad
+
+template <int WM, int WN>
+struct Tile {
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int BM = 64 * WM;             // hidden rows per workgroup
+    static constexpr int BN = 128 * WN;            // vocabulary entries per workgroup
+    static constexpr int kRowStep = kThreads / 8;  // rows one pass of 16-byte loads covers
+    static constexpr int kA = BM / kRowStep;       // 16-byte loads per thread per stage (hidden)
+    static constexpr int kB = BN / kRowStep;       // (weight)
+    static constexpr int kLds = (BM + BN) * kPitch;
+    static_assert(BM % kRowStep == 0 && BN % kRowStep == 0, "tile rows per load pass");
+};
+
+template <int WM, int WN, bool KEYS>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+void k_lmhead(LmParams p, int tiles_m) {
+    using T = Tile<WM, WN>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[T::kLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+
+    // Workgroups are dealt to the 8 XCDs in turn (XCD = workgroup id mod 8).
+    // XCD x takes the contiguous tile numbers [start_x, start_x + count_x), and
+    // tile numbers run over the row tiles first, so the row tiles that share a
+    // weight tile run on one XCD at about the same time and read that weight
+    // tile through its L2 once.
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int q = G >> 3, rem = G & 7, x = bid & 7;
+    const int tile = x * q + min(x, rem) + (bid >> 3);
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+    // this thread's 16-byte loads: column lcol of rows lrow + i * kRowStep.
+    // Rows past M (or V) in the last tiles load the last row again: their
+    // products land in accumulator rows (columns) that are never stored or
+    // reduced, so no zero fill is needed and every load stays in bounds.
+    const int lrow = tid >> 3, lcol = tid & 7;
+    const unsigned vrow = (unsigned)(p.H / 8);  // 16-byte vectors per row
+    const v4u* const A = static_cast<const v4u*>(p.hidden);
+    const v4u* const W = static_cast<const v4u*>(p.weight);
+    unsigned aoff[T::kA], boff[T::kB];
+#pragma unroll
+    for (int i = 0; i < T::kA; ++i)
+        aoff[i] = (unsigned)min(m0 + lrow + i * T::kRowStep, p.M - 1) * vrow + lcol;
+#pragma unroll
+    for (int i = 0; i < T::kB; ++i)
+        boff[i] = (unsigned)min(n0 + lrow + i * T::kRowStep, p.V - 1) * vrow + lcol;
+    // the MTP hidden-state carry: the first column of tiles copies the rows it loads
+    const bool copy = KEYS && p.hidden_dst != nullptr && tn == 0;
+    v4u* const D = static_cast<v4u*>(p.hidden_dst);
+
+    v4u ra[T::kA], rb[T::kB];
+#pragma unroll
+    for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i]];
+#pragma unroll
+    for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i]];
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.f;
+
+    const int KT = p.H / kLmBK;
+    for (int kt = 0; kt < KT; ++kt) {
+        __syncthreads();  // every wave has read the previous stage
+#pragma unroll
+        for (int i = 0; i < T::kA; ++i)
+            *reinterpret_cast<v4u*>(lds + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
+#pragma unroll
+        for (int i = 0; i < T::kB; ++i)
+            *reinterpret_cast<v4u*>(lds + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
+        if (copy) {
+            const unsigned o = (unsigned)kt * (kLmBK / 8);
+#pragma unroll
+            for (int i = 0; i < T::kA; ++i)
+                if (m0 + lrow + i * T::kRowStep < p.M) D[aoff[i] + o] = ra[i];
+        }
+        __syncthreads();
+        if (kt + 1 < KT) {
+            const unsigned o = (unsigned)(kt + 1) * (kLmBK / 8);
+#pragma unroll
+            for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i] + o];
+#pragma unroll
+            for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
+        }
+#pragma unroll
+        for (int s = 0; s < kLmBK / 16; ++s) {
+            const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
+            bf16x8 af[2], bv[4];
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm)
+                af[bm] = *reinterpret_cast<const bf16x8*>(lds + (wm * 64 + bm * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+            for (int bn = 0; bn < 4; ++bn)
+                bv[bn] = *reinterpret_cast<const bf16x8*>(lds + (T::BM + wn * 128 + bn * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                for (int bn = 0; bn < 4; ++bn)
+                    acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bv[bn], acc[bm][bn], 0, 0, 0);
+        }
+    }
+
+    if constexpr (!KEYS) {
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+            for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = m0 + wm * 64 + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    const int j = n0 + wn * 128 + bn * 32 + (lane & 31);
+                    if (i < p.M && j < p.V) p.logits[(size_t)i * p.V + j] = acc[bm][bn][r];
+                }
+    } else {
+        // per row: (max, lowest index) over this wave's 128 columns, then over
+        // the WN waves of the row tile, then merged into keys[m] across tiles
+        __syncthreads();  // the last stage's fragment reads are done: reuse the LDS
+        unsigned long long* s_key = reinterpret_cast<unsigned long long*>(lds);  // [WN][BM]
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                ArgMax a{-INFINITY, INT_MAX};
+#pragma unroll
+                for (int bn = 0; bn < 4; ++bn) {
+                    const int j = n0 + wn * 128 + bn * 32 + (lane & 31);
+                    if (j < p.V) a = better(a, ArgMax{acc[bm][bn][r], j});
+                }
+                a = half_wave_argmax(a);
+                if ((lane & 31) == 0)
+                    s_key[wn * T::BM + wm * 64 + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)] = argmax_key(a);
+            }
+        __syncthreads();
+        for (int i = tid; i < T::BM; i += T::kThreads) {
+            const int m = m0 + i;
+            if (m >= p.M) continue;
+            const int b = m / (p.n + 1), r = m - b * (p.n + 1);
+            const int L = min(max(p.lens[b], 0), p.n);
+            if (r > L) continue;  // rows past the draft length take no part in the decision
+            unsigned long long k = s_key[i];
+#pragma unroll
+            for (int w = 1; w < WN; ++w) k = max(k, s_key[w * T::BM + i]);
+            max64(p.keys + m, k);
+        }
+    }
+}
+
+template <int WM, int WN, bool KEYS>
+hipError_t launch_tiles(const LmParams& p, hipStream_t s) {
+    using T = Tile<WM, WN>;
+    const long long tm = (p.M + T::BM - 1) / T::BM;
+    const long long tn = ((long long)p.V + T::BN - 1) / T::BN;
+    const long long G = tm * tn;
+    if (G == 0) return hipSuccess;
+    if (G > INT_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_lmhead<WM, WN, KEYS>), dim3((unsigned)G), dim3(T::kThreads), 0, s, p, (int)tm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const LmParams& p, hipStream_t s) {
+    if (p.H % kLmBK != 0 || p.H < kLmBK) return hipErrorInvalidValue;
+    return p.keys ? launch_tiles<2, 2, true>(p, s) : launch_tiles<2, 2, false>(p, s);
+}
+
+}  // namespace sv

@@ -259,6 +259,55 @@ sv_status_t sv_sample_rows(const void *logits, sv_dtype_t dt, int R, const int32
                            int32_t *tokens, uint32_t *err_flags, float *row_stats, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* Greedy verify fused with the target's logit projection: the [B][n+1][V]
+ * logits are never written to memory.
+ *
+ * "Accelerating Sonar through speculation": the model produces logits from
+ * which the next token is sampled (Inference with speculative decoding section,
+ * first paragraph) through its logit projection, which the MTP head reuses and
+ * which is about 2 GB for a 70B Llama (MTP section, the paragraph on the head's
+ * normalisation layers).  The greedy rule (spec_verify_greedy()) needs only
+ * the argmax of each row, so each workgroup of the projection reduces its tile
+ * of logits to a per-row (max, lowest index) in registers.
+ *
+ * The logits are z[b][r][v] = sum_k hidden[b][r][k] * weight[v][k], products
+ * of bfloat16 values accumulated in binary32 on the matrix cores (summation
+ * order unspecified); the greedy rule of spec_verify_greedy() is applied to
+ * them: lowest index on ties, rows r > L_b take no part.  Where two logits of
+ * a row are closer than the binary32 summation error, which one is the larger
+ * can differ from exact arithmetic; when every partial sum is exactly
+ * representable the result does not depend on the order.
+ *
+ *   hidden        [B][n+1][H] bf16, 16-byte aligned: the target's final hidden states
+ *                 (after its last normalisation), one per verified position
+ *   weight        [V][H] bf16, 16-byte aligned: the logit projection, one row per
+ *                 vocabulary entry
+ *   H             a multiple of 64 (SV_EINVAL otherwise); V * H and B*(n+1) * H
+ *                 below 2^34
+ *   draft_tokens, draft_lens, accepted_len, emitted, err_flags: as in spec_verify_greedy()
+ *   tokens        [B][n+1] int32 in/out, nullable: the MTP token shift/insert of
+ *                 mtp_shift_insert() done by the decision
+ *   hidden_dst    [B][n+1][H] bf16, nullable (needs tokens), 16-byte aligned: the
+ *                 MTP hidden-state carry, written by the projection's first
+ *                 column of workgroups from the tiles they load; hidden_dst ==
+ *                 hidden copies nothing
+ *   workspace     >= sv_workspace_bytes(B, n, V, SV_BF16) bytes, zero-filled before
+ *                 first use and left zero-filled
+ * tokens and hidden_dst must not overlap any other argument (SV_EINVAL).
+ */
+sv_status_t spec_verify_greedy_lmhead(const void *hidden, const void *weight, int H,
+                                      const int32_t *draft_tokens, const int32_t *draft_lens, int B,
+                                      int n, int V, int32_t *accepted_len, int32_t *emitted,
+                                      uint32_t *err_flags, int32_t *tokens, void *hidden_dst,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Parity/debug only (not on the hot path): the binary32 logits of the logit
+ * projection that spec_verify_greedy_lmhead() reduces, computed by the same
+ * kernel.  hidden [M][H], weight [V][H] bf16 (16-byte aligned, H a multiple of
+ * 64), logits_out [M][V] float. */
+sv_status_t sv_lmhead_logits_debug(const void *hidden, const void *weight, int M, int H, int V,
+                                   float *logits_out, void *stream);
+
 /* Parity/debug only (not on the hot path): full binary32 probabilities
  * softmax(logits[r] / temperature[r]) of `rows` rows of length V, computed with
  * the same row statistics the verify kernels use.  temperature[r] must be > 0

@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ["spec_verify_sample", "spec_verify_greedy", "mtp_shift_insert", "sv_workspace_bytes",
               "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug",
-              "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "spec_verify_sample_ex", "sv_sample_rows"]:
+              "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "spec_verify_sample_ex", "sv_sample_rows",
+              "spec_verify_greedy_lmhead", "sv_lmhead_logits_debug"]:
         assert f in names, names
 
 
@@ -204,3 +205,35 @@ def test_sample_ex_host_checks():
     assert _sample_ex(hs=_addr(6), hd=_addr(7), H=64) == sv.SV_EINVAL   # hidden buffers without tokens
     assert _sample_ex(tok=_addr(5), hd=_addr(12), hs=_addr(6), H=64) == sv.SV_EINVAL  # hidden_dst over draft_stats
     assert _sample_ex(wsb=8) == sv.SV_EWORKSPACE
+
+
+def _lmhead(**kw):
+    args = dict(h=_addr(0), w=_addr(9), H=128, x=_addr(1), L=_addr(2), B=4, n=4, V=1000, acc=_addr(3),
+                emi=_addr(4), fl=NULL, tok=_addr(5), hd=_addr(7), ws=_addr(8), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_greedy_lmhead(*args.values())
+
+
+def test_lmhead_host_checks():
+    assert _lmhead(B=0) == sv.SV_OK
+    assert _lmhead(H=100) == sv.SV_EINVAL                       # H not a multiple of 64
+    assert _lmhead(H=0) == sv.SV_EINVAL
+    assert _lmhead(V=0) == sv.SV_EINVAL
+    assert _lmhead(n=sv.SV_MAX_DRAFT + 1) == sv.SV_EINVAL
+    assert _lmhead(V=1 << 22, H=1 << 12) == sv.SV_EINVAL          # weight offsets beyond 32 bits of vectors
+    assert _lmhead(h=NULL) == sv.SV_EINVAL
+    assert _lmhead(w=NULL) == sv.SV_EINVAL
+    assert _lmhead(tok=NULL) == sv.SV_EINVAL                     # hidden_dst needs the token step
+    assert _lmhead(h=C.c_void_p((1 << 40) + 8)) == sv.SV_EALIGN  # 16-byte vectors
+    assert _lmhead(w=C.c_void_p((1 << 40) + (9 << 32) + 8)) == sv.SV_EALIGN
+    assert _lmhead(hd=C.c_void_p((1 << 40) + (7 << 32) + 8)) == sv.SV_EALIGN
+    assert _lmhead(wsb=8) == sv.SV_EWORKSPACE
+    assert _lmhead(tok=_addr(4)) == sv.SV_EINVAL                 # tokens == emitted
+    assert _lmhead(hd=_addr(9)) == sv.SV_EINVAL                  # hidden_dst over the weight
+    assert _lmhead(hd=C.c_void_p((1 << 40) + 4096)) == sv.SV_EINVAL  # partial overlap with hidden
+    f = sv.lib().sv_lmhead_logits_debug
+    assert f(_addr(0), _addr(9), 0, 64, 10, _addr(3), NULL) == sv.SV_OK
+    assert f(_addr(0), _addr(9), 4, 96, 10, _addr(3), NULL) == sv.SV_EINVAL
+    assert f(C.c_void_p((1 << 40) + 4), _addr(9), 4, 64, 10, _addr(3), NULL) == sv.SV_EALIGN
+    assert f(_addr(0), _addr(9), 4, 64, 10, NULL, NULL) == sv.SV_EINVAL
+

@@ -11,7 +11,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "draft_token_verification_08_amd", "csrc", "sv_kernels.hip")
+CSRC = os.path.join(ROOT, "draft_token_verification_08_amd", "csrc")
+SRCS = [os.path.join(CSRC, "sv_kernels.hip"), os.path.join(CSRC, "sv_lmhead.hip")]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 # mangled kernel name -> minimum waves per SIMD
@@ -20,6 +21,9 @@ BUDGET = {
     "_ZN2sv7k_statsILi1ELi0ELb1EEEvNS_11StatsParamsE": 7,   # sampling, bf16, aligned
     "_ZN2sv6k_drawILi1EEEvNS_10DrawParamsE": 6,             # draw pass, bf16, aligned
     "_ZN2sv5k_mtpILb1EEEvNS_9MtpParamsE": 8,               # MTP copy, aligned
+    # logit projection (128 x 256 tiles, 4 waves): two workgroups per CU share the
+    # LDS and the matrix cores; its accumulators alone take 128 registers
+    "_ZN2sv12_GLOBAL__N_18k_lmheadILi2ELi2ELb1EEEvNS_8LmParamsEi": 2,
 }
 
 
@@ -27,12 +31,14 @@ BUDGET = {
 def usage(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("ru") / "k.o"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"),
-           "-I" + os.path.dirname(SRC), "-x", "hip", "--cuda-device-only", "-c", SRC, "-o", str(out),
-           "-Rpass-analysis=kernel-resource-usage"]
-    text = subprocess.run(cmd, capture_output=True, text=True, check=True).stderr
+    text = ""
+    for i, src in enumerate(SRCS):
+        out = tmp_path_factory.mktemp("ru") / f"k{i}.o"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-Xclang",
+               "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"),
+               "-I" + CSRC, "-x", "hip", "--cuda-device-only", "-c", src, "-o", str(out),
+               "-Rpass-analysis=kernel-resource-usage"]
+        text += subprocess.run(cmd, capture_output=True, text=True, check=True).stderr
     kernels = {}
     cur = None
     for line in text.splitlines():
