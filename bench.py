@@ -13,7 +13,8 @@ Prints one JSON line: verified vocab rows/s (value), HBM GB/s and % of the
 8 TB/s peak, a roofline entry for the dominant kernel (the verify kernel,
 timed with HIP events on its stream), and the CPU oracle timed on host cores.
 
-    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--no-cpu] [--unfused]
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5,6}] [--no-cpu] [--unfused]
+    python bench.py --lmhead [--steps K]   # greedy verify fused with the logit projection
 """
 from __future__ import annotations
 
@@ -47,6 +48,9 @@ def parse():
                          "(spec_verify_sample_ex) instead of streaming the draft rows")
     ap.add_argument("--unfused", action="store_true",
                     help="separate verify and mtp_shift_insert calls instead of the fused call")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="greedy verify fused with the target's logit projection (spec_verify_greedy_lmhead): "
+                         "hidden states [256, 5, 8192] and a [128256, 8192] projection instead of logits")
     return ap.parse_args()
 
 
@@ -87,6 +91,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.lmhead:
+        bench_lmhead(args, dev)
+        return
     cfg = synth.CONFIGS[args.config]
     greedy = cfg.mode == "greedy"
     es = 2 if cfg.dtype == torch.bfloat16 else 4
@@ -336,6 +343,144 @@ def cpu_baseline(d, cfg, greedy):
                       f"about {nn * tn * threads:.0f} s of CPU work; single thread: {n1} steps",
             "single_thread_rows_per_s": round(rows / t1, 1), "seconds_per_step": round(tn, 4),
             "cpu_model": cpu_model()}
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def bench_lmhead(args, dev):
+    """The greedy verify step on hidden states instead of logits: the projection
+    hidden [B, n+1, H] x weight[V, H]^T runs on the matrix cores and each tile of
+    logits is reduced to per-row argmax keys in registers; the decision and the
+    MTP shift/insert (tokens and hidden-state carry) follow in the same call.
+    Reported against the dense bf16 matrix-core peak, beside the library path
+    (torch.matmul to bf16 logits, then spec_verify_greedy_mtp)."""
+    import torch
+
+    import draft_token_verification_08_amd as sv
+    from draft_token_verification_08_amd import synth
+
+    B, n, V, H = 256, 4, 128256, 8192
+    M = B * (n + 1)
+    d = synth.make_lmhead(args.seed, device=dev, B=B, n=n, V=V, H=H, exact=False)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    emi = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+    tokens = d["tokens"].clone()
+    hdst = torch.empty_like(d["hidden"])
+    wsbuf = sv.Workspace(dev).get(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16))
+    stream = torch.cuda.current_stream(dev)
+    call = sv.prepare_spec_verify_greedy_lmhead(d["hidden"], d["weight"], d["draft_tokens"], d["draft_lens"], acc,
+                                                emi, wsbuf, tokens=tokens, hidden_dst=hdst)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    avg_ms = statistics.fmean(step_ms)
+    flops = 2.0 * M * V * H
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+
+    # the library path on the same inputs: bf16 logits from the library GEMM,
+    # then the fused logits verify + MTP call
+    h2 = d["hidden"].view(M, H)
+    wt = d["weight"]
+    tok2 = d["tokens"].clone()
+    hdst2 = torch.empty_like(d["hidden"])
+    acc2 = torch.empty_like(acc)
+    emi2 = torch.empty_like(emi)
+
+    def library_step():
+        z = torch.matmul(h2, wt.t())
+        sv.spec_verify_greedy_mtp(z.view(B, n + 1, V), d["draft_tokens"], d["draft_lens"], tok2, d["hidden"], hdst2,
+                                  accepted_len=acc2, emitted=emi2, workspace=wsbuf)
+
+    for _ in range(3):
+        library_step()
+    torch.cuda.synchronize()
+    lib_ms = []
+    for _ in range(max(5, min(20, K))):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        library_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        lib_ms.append(a.elapsed_time(b))
+    lib_avg = statistics.fmean(lib_ms)
+    # the library path decides on bf16-rounded logits, this one on the binary32
+    # sums: they can differ where two top logits round to the same bf16 value
+    same_seq = ((acc == acc2) & (emi == emi2).all(dim=1)).float().mean()
+
+    out = {
+        "metric": "verified vocab rows/s, V=128256 bf16, B=256, n=4 (greedy, logits from the lm_head projection)",
+        "value": round(M * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 normals; hidden states and projection resident in HBM)",
+        "config": {"workload": "greedy verify fused with the lm_head projection + MTP shift/insert "
+                               f"(hidden [{B}, {n + 1}, {H}] x projection [{V}, {H}] bf16)",
+                   "B": B, "n": n, "V": V, "H": H, "parallelism": "none (1 GPU)"},
+        "step_us": round(avg_ms * 1e3, 1),
+        "library_path_us": round(lib_avg * 1e3, 1),
+        "library_path": "torch.matmul to bf16 logits + spec_verify_greedy_mtp",
+        "speedup_vs_library_path": round(lib_avg / avg_ms, 4),
+        "library_path_same_decisions_frac": round(float(same_seq), 4),
+        "mean_accepted": round(float(acc.float().mean()), 4),
+        "roofline": {"bound": "mfma", "kernel": "k_lmhead (+ k_decide_greedy)", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "flops_per_launch": flops, "avg_launch_us": round(avg_ms * 1e3, 1),
+                     "timed_launches": K,
+                     "timing": "HIP event pair around every step (the projection launch and the per-sequence "
+                               "decision launch, about 3 us)",
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_lmhead(d, B, n, V, H)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_lmhead(d, B, n, V, H):
+    """The oracle (plain C double projection + greedy rule, untuned) on a bounded
+    sample: the rows of whole sequences, as many as fit about 10 s of CPU work."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    h = synth.bf16_bits(d["hidden"]).reshape(-1, H)
+    w = synth.bf16_bits(d["weight"])
+    x = d["draft_tokens"].cpu().numpy()
+    L = d["draft_lens"].cpu().numpy()
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    seqs, t0 = 0, time.perf_counter()
+    while seqs < 1 or (time.perf_counter() - t0 < 10.0 / threads * 2 and seqs < B):
+        rows = np.arange(seqs * (n + 1), (seqs + 1) * (n + 1), dtype=np.int32)
+        z = orc.lmhead_logits(h, w, rows=rows, threads=threads).reshape(1, n + 1, V)
+        orc.verify_greedy(z, x[seqs:seqs + 1], L[seqs:seqs + 1])
+        seqs += 1
+    el = time.perf_counter() - t0
+    return {"value": round(seqs * (n + 1) / el, 3), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} sequences ({seqs * (n + 1)} projected rows of V={V}, H={H}) on {threads} threads, "
+                      f"about {el * threads:.0f} s of CPU work", "cpu_model": cpu_model()}
 
 
 def cpu_model() -> str:

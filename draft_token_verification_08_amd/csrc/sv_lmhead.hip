@@ -20,18 +20,47 @@
 // operands are therefore 16 contiguous bytes of a K-contiguous row: one
 // ds_read_b128 each.
 //
-// Workgroup tile BM x BN = (64 WM) x (128 WN), WM x WN waves, each wave a
-// 64 x 128 block (2 x 4 accumulators of 32 x 32).  K runs in stages of 64: the
-// stage's A and B rows are loaded to registers (16-byte loads, 8 lanes per
-// 128-byte row segment), written to LDS with a 16-byte pad per row (rows 144
-// bytes apart, so the 32 lanes of a fragment read hit distinct banks), and the
-// next stage's loads are issued before the current stage's MFMAs.
+// Workgroup tile BM x BN = 256 x 256 by default: 8 waves (4 along the rows, 2
+// along the vocabulary), each a 64 x 128 block held in 2 x 4 accumulators of
+// 32 x 32 (128 registers), so a workgroup per CU runs two waves per SIMD.  K
+// runs in stages of 64.  A stage's A and B rows are loaded to registers with
+// 16-byte loads (8 lanes per 128-byte row segment) and written to LDS with a
+// 16-byte pad per row (rows 144 bytes apart, so the 32 lanes of a fragment
+// read hit distinct banks).  Two LDS buffers alternate: while the waves run the
+// MFMAs of stage kt from one, stage kt+1 is stored to the other and stage kt+2
+// loaded, with one barrier per stage.  Tile shape, buffering and tile order
+// are compile-time knobs; the defaults are the fastest measured on MI355X.
 #include <cfloat>
 #include <climits>
 #include <cmath>
 
 #include "sv_internal.h"
 #include "sv_device.h"
+
+#ifndef SV_LM_WM
+#define SV_LM_WM 4  // waves along the hidden rows
+#endif
+#ifndef SV_LM_WN
+#define SV_LM_WN 2  // waves along the vocabulary
+#endif
+#ifndef SV_LM_WTM
+#define SV_LM_WTM 2  // 32 x 32 accumulator blocks per wave along the rows
+#endif
+#ifndef SV_LM_WTN
+#define SV_LM_WTN 4  // ... along the vocabulary
+#endif
+#ifndef SV_LM_WPE
+#define SV_LM_WPE 2  // waves per SIMD the register budget is sized for
+#endif
+#ifndef SV_LM_FRAG2
+#define SV_LM_FRAG2 0  // double-buffered MFMA fragments within a stage
+#endif
+#ifndef SV_LM_XCD
+#define SV_LM_XCD 1  // XCD-aware tile order
+#endif
+#ifndef SV_LM_LDSBUF
+#define SV_LM_LDSBUF 2  // LDS stages: 1 (two barriers per stage) or 2 (double buffer, one barrier)
+#endif
 
 namespace sv {
 namespace {
@@ -44,21 +73,22 @@ constexpr int kPitch = kLmBK * 2 + 16;  // LDS bytes per tile row: one stage of 
 
 template <int WM, int WN>
 struct Tile {
+    static constexpr int TM = SV_LM_WTM, TN = SV_LM_WTN;  // accumulator blocks per wave
     static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int BM = 64 * WM;             // hidden rows per workgroup
-    static constexpr int BN = 128 * WN;            // vocabulary entries per workgroup
+    static constexpr int BM = 32 * TM * WM;        // hidden rows per workgroup
+    static constexpr int BN = 32 * TN * WN;        // vocabulary entries per workgroup
     static constexpr int kRowStep = kThreads / 8;  // rows one pass of 16-byte loads covers
     static constexpr int kA = BM / kRowStep;       // 16-byte loads per thread per stage (hidden)
     static constexpr int kB = BN / kRowStep;       // (weight)
-    static constexpr int kLds = (BM + BN) * kPitch;
+    static constexpr int kLds = (BM + BN) * kPitch;  // one stage
     static_assert(BM % kRowStep == 0 && BN % kRowStep == 0, "tile rows per load pass");
 };
 
 template <int WM, int WN, bool KEYS>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(SV_LM_WPE, SV_LM_WPE)))
 void k_lmhead(LmParams p, int tiles_m) {
     using T = Tile<WM, WN>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[T::kLds];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[T::kLds * SV_LM_LDSBUF];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
 
@@ -69,7 +99,7 @@ void k_lmhead(LmParams p, int tiles_m) {
     // tile through its L2 once.
     const int G = gridDim.x, bid = blockIdx.x;
     const int q = G >> 3, rem = G & 7, x = bid & 7;
-    const int tile = x * q + min(x, rem) + (bid >> 3);
+    const int tile = SV_LM_XCD ? x * q + min(x, rem) + (bid >> 3) : bid;
     const int tm = tile % tiles_m, tn = tile / tiles_m;
     const int m0 = tm * T::BM, n0 = tn * T::BN;
 
@@ -98,64 +128,109 @@ void k_lmhead(LmParams p, int tiles_m) {
 #pragma unroll
     for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i]];
 
-    f32x16 acc[2][4];
+    constexpr int TM = T::TM, TN = T::TN;
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < TM; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn)
+        for (int bn = 0; bn < TN; ++bn)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.f;
 
     const int KT = p.H / kLmBK;
-    for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();  // every wave has read the previous stage
+    auto store_stage = [&](unsigned char* buf, int kt) {
 #pragma unroll
         for (int i = 0; i < T::kA; ++i)
-            *reinterpret_cast<v4u*>(lds + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
+            *reinterpret_cast<v4u*>(buf + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
 #pragma unroll
         for (int i = 0; i < T::kB; ++i)
-            *reinterpret_cast<v4u*>(lds + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
+            *reinterpret_cast<v4u*>(buf + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
         if (copy) {
             const unsigned o = (unsigned)kt * (kLmBK / 8);
 #pragma unroll
             for (int i = 0; i < T::kA; ++i)
                 if (m0 + lrow + i * T::kRowStep < p.M) D[aoff[i] + o] = ra[i];
         }
-        __syncthreads();
-        if (kt + 1 < KT) {
-            const unsigned o = (unsigned)(kt + 1) * (kLmBK / 8);
+    };
+    auto load_stage = [&](int kt) {
+        const unsigned o = (unsigned)kt * (kLmBK / 8);
 #pragma unroll
-            for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i] + o];
+        for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i] + o];
 #pragma unroll
-            for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
-        }
+        for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
+    };
+    auto load_frags = [&](const unsigned char* buf, int s, bf16x8* fa, bf16x8* fb) {
+        const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
+#pragma unroll
+        for (int bm = 0; bm < TM; ++bm)
+            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn)
+            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * 32 + (lane & 31)) * kPitch + kb);
+    };
+    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int bm = 0; bm < TM; ++bm)
+#pragma unroll
+            for (int bn = 0; bn < TN; ++bn)
+                acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
+    };
+    auto compute_stage = [&](const unsigned char* buf) {
+#if SV_LM_FRAG2
+        // fragments of step s+1 are read while the MFMAs of step s run
+        bf16x8 fa[2][TM], fb[2][TN];
+        load_frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
         for (int s = 0; s < kLmBK / 16; ++s) {
-            const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
-            bf16x8 af[2], bv[4];
-#pragma unroll
-            for (int bm = 0; bm < 2; ++bm)
-                af[bm] = *reinterpret_cast<const bf16x8*>(lds + (wm * 64 + bm * 32 + (lane & 31)) * kPitch + kb);
-#pragma unroll
-            for (int bn = 0; bn < 4; ++bn)
-                bv[bn] = *reinterpret_cast<const bf16x8*>(lds + (T::BM + wn * 128 + bn * 32 + (lane & 31)) * kPitch + kb);
-#pragma unroll
-            for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-                for (int bn = 0; bn < 4; ++bn)
-                    acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bv[bn], acc[bm][bn], 0, 0, 0);
+            if (s + 1 < kLmBK / 16) load_frags(buf, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads of step s+1 ahead of the MFMAs of step s
+            mfmas(fa[s & 1], fb[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+#else
+#pragma unroll
+        for (int s = 0; s < kLmBK / 16; ++s) {
+            bf16x8 fa[TM], fb[TN];
+            load_frags(buf, s, fa, fb);
+            mfmas(fa, fb);
+        }
+#endif
+    };
+#if SV_LM_LDSBUF == 1
+    // one LDS stage: store, barrier, issue the next stage's loads, compute, barrier
+    for (int kt = 0; kt < KT; ++kt) {
+        __syncthreads();  // every wave has read the previous stage
+        store_stage(lds, kt);
+        __syncthreads();
+        if (kt + 1 < KT) load_stage(kt + 1);
+        compute_stage(lds);
     }
+#else
+    // two LDS stages: while the waves compute stage kt from one buffer, stage
+    // kt+1 (already in registers) is stored to the other and stage kt+2 loaded;
+    // one barrier per stage
+    store_stage(lds, 0);
+    if (KT > 1) load_stage(1);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) {
+            store_stage(lds + ((kt + 1) & 1) * T::kLds, kt + 1);
+            if (kt + 2 < KT) load_stage(kt + 2);
+        }
+        compute_stage(lds + (kt & 1) * T::kLds);
+        __syncthreads();
+    }
+#endif
 
     if constexpr (!KEYS) {
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < TM; ++bm)
 #pragma unroll
-            for (int bn = 0; bn < 4; ++bn)
+            for (int bn = 0; bn < TN; ++bn)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int i = m0 + wm * 64 + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    const int j = n0 + wn * 128 + bn * 32 + (lane & 31);
+                    const int i = m0 + wm * 32 * TM + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    const int j = n0 + wn * 32 * TN + bn * 32 + (lane & 31);
                     if (i < p.M && j < p.V) p.logits[(size_t)i * p.V + j] = acc[bm][bn][r];
                 }
     } else {
@@ -164,18 +239,18 @@ void k_lmhead(LmParams p, int tiles_m) {
         __syncthreads();  // the last stage's fragment reads are done: reuse the LDS
         unsigned long long* s_key = reinterpret_cast<unsigned long long*>(lds);  // [WN][BM]
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < TM; ++bm)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 ArgMax a{-INFINITY, INT_MAX};
 #pragma unroll
-                for (int bn = 0; bn < 4; ++bn) {
-                    const int j = n0 + wn * 128 + bn * 32 + (lane & 31);
+                for (int bn = 0; bn < TN; ++bn) {
+                    const int j = n0 + wn * 32 * TN + bn * 32 + (lane & 31);
                     if (j < p.V) a = better(a, ArgMax{acc[bm][bn][r], j});
                 }
                 a = half_wave_argmax(a);
                 if ((lane & 31) == 0)
-                    s_key[wn * T::BM + wm * 64 + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)] = argmax_key(a);
+                    s_key[wn * T::BM + wm * 32 * TM + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)] = argmax_key(a);
             }
         __syncthreads();
         for (int i = tid; i < T::BM; i += T::kThreads) {
@@ -208,7 +283,7 @@ hipError_t launch_tiles(const LmParams& p, hipStream_t s) {
 
 hipError_t launch_lmhead(const LmParams& p, hipStream_t s) {
     if (p.H % kLmBK != 0 || p.H < kLmBK) return hipErrorInvalidValue;
-    return p.keys ? launch_tiles<2, 2, true>(p, s) : launch_tiles<2, 2, false>(p, s);
+    return p.keys ? launch_tiles<SV_LM_WM, SV_LM_WN, true>(p, s) : launch_tiles<SV_LM_WM, SV_LM_WN, false>(p, s);
 }
 
 }  // namespace sv

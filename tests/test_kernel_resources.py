@@ -21,9 +21,9 @@ BUDGET = {
     "_ZN2sv7k_statsILi1ELi0ELb1EEEvNS_11StatsParamsE": 7,   # sampling, bf16, aligned
     "_ZN2sv6k_drawILi1EEEvNS_10DrawParamsE": 6,             # draw pass, bf16, aligned
     "_ZN2sv5k_mtpILb1EEEvNS_9MtpParamsE": 8,               # MTP copy, aligned
-    # logit projection (128 x 256 tiles, 4 waves): two workgroups per CU share the
-    # LDS and the matrix cores; its accumulators alone take 128 registers
-    "_ZN2sv12_GLOBAL__N_18k_lmheadILi2ELi2ELb1EEEvNS_8LmParamsEi": 2,
+    # logit projection (256 x 256 tiles, 8 waves, one workgroup per CU): two
+    # waves per SIMD; the accumulators alone take 128 registers
+    "_ZN2sv12_GLOBAL__N_18k_lmheadILi4ELi2ELb1EEEvNS_8LmParamsEi": 2,
 }
 
 
