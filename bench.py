@@ -54,12 +54,15 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+LMHEAD_SRC = os.path.join(ROOT, "draft_token_verification_08_amd", "csrc", "sv_lmhead.hip")
+
+
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, src: str = KERNEL_SRC):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     only if they were taken on the current kernel source."""
     try:
@@ -68,7 +71,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     e = t.get(f"{kernel}|{workload}")
-    if not e or e.get("source_sha256_16") != kernel_source_hash():
+    if not e or e.get("source_sha256_16") != kernel_source_hash(src):
         return None
     return e.get("bytes_per_launch")
 
@@ -446,7 +449,9 @@ def bench_lmhead(args, dev):
                      "timed_launches": K,
                      "timing": "HIP event pair around every step (the projection launch and the per-sequence "
                                "decision launch, about 3 us)",
-                     "traffic": None},
+                     "traffic": measured_traffic("k_lmhead", "greedy_lmhead_projection", LMHEAD_SRC),
+                     "traffic_note": "HBM bytes per launch; the algorithmic minimum is the projection read "
+                                     "once plus the hidden states (read, and written by the carry)"},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_lmhead(d, B, n, V, H)

@@ -52,9 +52,6 @@
 #ifndef SV_LM_WPE
 #define SV_LM_WPE 2  // waves per SIMD the register budget is sized for
 #endif
-#ifndef SV_LM_FRAG2
-#define SV_LM_FRAG2 0  // double-buffered MFMA fragments within a stage
-#endif
 #ifndef SV_LM_XCD
 #define SV_LM_XCD 1  // XCD-aware tile order
 #endif
@@ -71,8 +68,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte lo
 
 constexpr int kPitch = kLmBK * 2 + 16;  // LDS bytes per tile row: one stage of K plus 16 bytes of pad
 
-template <int WM, int WN>
+template <int WM_, int WN_>
 struct Tile {
+    static constexpr int WM = WM_, WN = WN_;
     static constexpr int TM = SV_LM_WTM, TN = SV_LM_WTN;  // accumulator blocks per wave
     static constexpr int kThreads = 64 * WM * WN;
     static constexpr int BM = 32 * TM * WM;        // hidden rows per workgroup
@@ -84,144 +82,40 @@ struct Tile {
     static_assert(BM % kRowStep == 0 && BN % kRowStep == 0, "tile rows per load pass");
 };
 
-template <int WM, int WN, bool KEYS>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(SV_LM_WPE, SV_LM_WPE)))
-void k_lmhead(LmParams p, int tiles_m) {
-    using T = Tile<WM, WN>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[T::kLds * SV_LM_LDSBUF];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WM, wn = wave / WM;
-
-    // Workgroups are dealt to the 8 XCDs in turn (XCD = workgroup id mod 8).
-    // XCD x takes the contiguous tile numbers [start_x, start_x + count_x), and
-    // tile numbers run over the row tiles first, so the row tiles that share a
-    // weight tile run on one XCD at about the same time and read that weight
-    // tile through its L2 once.
+// Tile number of this workgroup.  Workgroups are dealt to the 8 XCDs in turn
+// (XCD = workgroup id mod 8).  XCD x takes the contiguous tile numbers
+// [start_x, start_x + count_x), and tile numbers run over the row tiles first,
+// so the row tiles that share a weight tile run on one XCD at about the same
+// time and read that weight tile through its L2 once.
+__device__ __forceinline__ int tile_of_workgroup() {
     const int G = gridDim.x, bid = blockIdx.x;
     const int q = G >> 3, rem = G & 7, x = bid & 7;
-    const int tile = SV_LM_XCD ? x * q + min(x, rem) + (bid >> 3) : bid;
-    const int tm = tile % tiles_m, tn = tile / tiles_m;
-    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    return SV_LM_XCD ? x * q + min(x, rem) + (bid >> 3) : bid;
+}
 
-    // this thread's 16-byte loads: column lcol of rows lrow + i * kRowStep.
-    // Rows past M (or V) in the last tiles load the last row again: their
-    // products land in accumulator rows (columns) that are never stored or
-    // reduced, so no zero fill is needed and every load stays in bounds.
-    const int lrow = tid >> 3, lcol = tid & 7;
-    const unsigned vrow = (unsigned)(p.H / 8);  // 16-byte vectors per row
-    const v4u* const A = static_cast<const v4u*>(p.hidden);
-    const v4u* const W = static_cast<const v4u*>(p.weight);
-    unsigned aoff[T::kA], boff[T::kB];
-#pragma unroll
-    for (int i = 0; i < T::kA; ++i)
-        aoff[i] = (unsigned)min(m0 + lrow + i * T::kRowStep, p.M - 1) * vrow + lcol;
-#pragma unroll
-    for (int i = 0; i < T::kB; ++i)
-        boff[i] = (unsigned)min(n0 + lrow + i * T::kRowStep, p.V - 1) * vrow + lcol;
-    // the MTP hidden-state carry: the first column of tiles copies the rows it loads
-    const bool copy = KEYS && p.hidden_dst != nullptr && tn == 0;
-    v4u* const D = static_cast<v4u*>(p.hidden_dst);
+// The MTP hidden-state carry: every workgroup copies an equal share of the
+// [M][H] hidden states (16-byte vectors) after its tile.
+__device__ __forceinline__ void hidden_copy_share(const LmParams& p) {
+    if (p.hidden_dst == nullptr) return;
+    const long long nvec = (long long)p.M * (p.H / 8);
+    const long long share = (nvec + gridDim.x - 1) / gridDim.x;
+    const long long v0 = (long long)blockIdx.x * share;
+    const long long v1 = min(nvec, v0 + share);
+    const v4u* src = static_cast<const v4u*>(p.hidden);
+    v4u* dst = static_cast<v4u*>(p.hidden_dst);
+    for (long long v = v0 + threadIdx.x; v < v1; v += blockDim.x) dst[v] = src[v];
+}
 
-    v4u ra[T::kA], rb[T::kB];
-#pragma unroll
-    for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i]];
-#pragma unroll
-    for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i]];
-
-    constexpr int TM = T::TM, TN = T::TN;
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int bm = 0; bm < TM; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < TN; ++bn)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.f;
-
-    const int KT = p.H / kLmBK;
-    auto store_stage = [&](unsigned char* buf, int kt) {
-#pragma unroll
-        for (int i = 0; i < T::kA; ++i)
-            *reinterpret_cast<v4u*>(buf + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
-#pragma unroll
-        for (int i = 0; i < T::kB; ++i)
-            *reinterpret_cast<v4u*>(buf + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
-        if (copy) {
-            const unsigned o = (unsigned)kt * (kLmBK / 8);
-#pragma unroll
-            for (int i = 0; i < T::kA; ++i)
-                if (m0 + lrow + i * T::kRowStep < p.M) D[aoff[i] + o] = ra[i];
-        }
-    };
-    auto load_stage = [&](int kt) {
-        const unsigned o = (unsigned)kt * (kLmBK / 8);
-#pragma unroll
-        for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i] + o];
-#pragma unroll
-        for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
-    };
-    auto load_frags = [&](const unsigned char* buf, int s, bf16x8* fa, bf16x8* fb) {
-        const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
-#pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
-            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * 32 + (lane & 31)) * kPitch + kb);
-#pragma unroll
-        for (int bn = 0; bn < TN; ++bn)
-            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * 32 + (lane & 31)) * kPitch + kb);
-    };
-    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
-#pragma unroll
-            for (int bn = 0; bn < TN; ++bn)
-                acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
-    };
-    auto compute_stage = [&](const unsigned char* buf) {
-#if SV_LM_FRAG2
-        // fragments of step s+1 are read while the MFMAs of step s run
-        bf16x8 fa[2][TM], fb[2][TN];
-        load_frags(buf, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int s = 0; s < kLmBK / 16; ++s) {
-            if (s + 1 < kLmBK / 16) load_frags(buf, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);  // keep the reads of step s+1 ahead of the MFMAs of step s
-            mfmas(fa[s & 1], fb[s & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#else
-#pragma unroll
-        for (int s = 0; s < kLmBK / 16; ++s) {
-            bf16x8 fa[TM], fb[TN];
-            load_frags(buf, s, fa, fb);
-            mfmas(fa, fb);
-        }
-#endif
-    };
-#if SV_LM_LDSBUF == 1
-    // one LDS stage: store, barrier, issue the next stage's loads, compute, barrier
-    for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();  // every wave has read the previous stage
-        store_stage(lds, kt);
-        __syncthreads();
-        if (kt + 1 < KT) load_stage(kt + 1);
-        compute_stage(lds);
-    }
-#else
-    // two LDS stages: while the waves compute stage kt from one buffer, stage
-    // kt+1 (already in registers) is stored to the other and stage kt+2 loaded;
-    // one barrier per stage
-    store_stage(lds, 0);
-    if (KT > 1) load_stage(1);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) {
-            store_stage(lds + ((kt + 1) & 1) * T::kLds, kt + 1);
-            if (kt + 2 < KT) load_stage(kt + 2);
-        }
-        compute_stage(lds + (kt & 1) * T::kLds);
-        __syncthreads();
-    }
-#endif
-
+// After the main loop: store the tile's logits (debug) or reduce each row to
+// (max, lowest index) over this wave's columns, then over the WN waves of the
+// row tile, and merge it into keys[m] across tiles.  `scratch` is LDS the main
+// loop no longer reads (at least WN * BM * 8 bytes).
+template <class T, bool KEYS>
+__device__ __forceinline__ void lmhead_epilogue(const LmParams& p, const f32x16 (&acc)[T::TM][T::TN],
+                                                unsigned char* scratch, int m0, int n0) {
+    constexpr int TM = T::TM, TN = T::TN, WN = T::WN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % T::WM, wn = wave / T::WM;
     if constexpr (!KEYS) {
 #pragma unroll
         for (int bm = 0; bm < TM; ++bm)
@@ -234,10 +128,7 @@ void k_lmhead(LmParams p, int tiles_m) {
                     if (i < p.M && j < p.V) p.logits[(size_t)i * p.V + j] = acc[bm][bn][r];
                 }
     } else {
-        // per row: (max, lowest index) over this wave's 128 columns, then over
-        // the WN waves of the row tile, then merged into keys[m] across tiles
-        __syncthreads();  // the last stage's fragment reads are done: reuse the LDS
-        unsigned long long* s_key = reinterpret_cast<unsigned long long*>(lds);  // [WN][BM]
+        unsigned long long* s_key = reinterpret_cast<unsigned long long*>(scratch);  // [WN][BM]
 #pragma unroll
         for (int bm = 0; bm < TM; ++bm)
 #pragma unroll
@@ -264,7 +155,121 @@ void k_lmhead(LmParams p, int tiles_m) {
             for (int w = 1; w < WN; ++w) k = max(k, s_key[w * T::BM + i]);
             max64(p.keys + m, k);
         }
+        hidden_copy_share(p);
     }
+}
+
+template <int WM, int WN, bool KEYS>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(SV_LM_WPE, SV_LM_WPE)))
+void k_lmhead(LmParams p, int tiles_m) {
+    using T = Tile<WM, WN>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[T::kLds * SV_LM_LDSBUF];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+
+    const int tile = tile_of_workgroup();
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+    // this thread's 16-byte loads: column lcol of rows lrow + i * kRowStep.
+    // Rows past M (or V) in the last tiles load the last row again: their
+    // products land in accumulator rows (columns) that are never stored or
+    // reduced, so no zero fill is needed and every load stays in bounds.
+    const int lrow = tid >> 3, lcol = tid & 7;
+    const unsigned vrow = (unsigned)(p.H / 8);  // 16-byte vectors per row
+    const v4u* const A = static_cast<const v4u*>(p.hidden);
+    const v4u* const W = static_cast<const v4u*>(p.weight);
+    unsigned aoff[T::kA], boff[T::kB];
+#pragma unroll
+    for (int i = 0; i < T::kA; ++i)
+        aoff[i] = (unsigned)min(m0 + lrow + i * T::kRowStep, p.M - 1) * vrow + lcol;
+#pragma unroll
+    for (int i = 0; i < T::kB; ++i)
+        boff[i] = (unsigned)min(n0 + lrow + i * T::kRowStep, p.V - 1) * vrow + lcol;
+
+    v4u ra[T::kA], rb[T::kB];
+#pragma unroll
+    for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i]];
+#pragma unroll
+    for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i]];
+
+    constexpr int TM = T::TM, TN = T::TN;
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int bm = 0; bm < TM; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.f;
+
+    const int KT = p.H / kLmBK;
+    auto store_stage = [&](unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < T::kA; ++i)
+            *reinterpret_cast<v4u*>(buf + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
+#pragma unroll
+        for (int i = 0; i < T::kB; ++i)
+            *reinterpret_cast<v4u*>(buf + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
+    };
+    auto load_stage = [&](int kt) {
+        const unsigned o = (unsigned)kt * (kLmBK / 8);
+#pragma unroll
+        for (int i = 0; i < T::kA; ++i) ra[i] = A[aoff[i] + o];
+#pragma unroll
+        for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
+    };
+    auto load_frags = [&](const unsigned char* buf, int s, bf16x8* fa, bf16x8* fb) {
+        const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
+#pragma unroll
+        for (int bm = 0; bm < TM; ++bm)
+            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn)
+            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * 32 + (lane & 31)) * kPitch + kb);
+    };
+    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int bm = 0; bm < TM; ++bm)
+#pragma unroll
+            for (int bn = 0; bn < TN; ++bn)
+                acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
+    };
+    auto compute_stage = [&](const unsigned char* buf) {
+#pragma unroll
+        for (int s = 0; s < kLmBK / 16; ++s) {
+            bf16x8 fa[TM], fb[TN];
+            load_frags(buf, s, fa, fb);
+            mfmas(fa, fb);
+        }
+    };
+#if SV_LM_LDSBUF == 1
+    // one LDS stage: store, barrier, issue the next stage's loads, compute, barrier
+    for (int kt = 0; kt < KT; ++kt) {
+        __syncthreads();  // every wave has read the previous stage
+        store_stage(lds);
+        __syncthreads();
+        if (kt + 1 < KT) load_stage(kt + 1);
+        compute_stage(lds);
+    }
+#else
+    // two LDS stages: while the waves compute stage kt from one buffer, stage
+    // kt+1 (already in registers) is stored to the other and stage kt+2 loaded;
+    // one barrier per stage
+    store_stage(lds);
+    if (KT > 1) load_stage(1);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) {
+            store_stage(lds + ((kt + 1) & 1) * T::kLds);
+            if (kt + 2 < KT) load_stage(kt + 2);
+        }
+        compute_stage(lds + (kt & 1) * T::kLds);
+        __syncthreads();
+    }
+#endif
+
+    if constexpr (KEYS) __syncthreads();  // the last stage's fragment reads are done: reuse the LDS
+    lmhead_epilogue<T, KEYS>(p, acc, lds, m0, n0);
 }
 
 template <int WM, int WN, bool KEYS>

@@ -53,7 +53,7 @@ def _run(d, **kw):
                                           (3, 0, 300, 128, 3)])
 def test_projection_bit_exact_on_exact_inputs(oracle, B, n, V, H, seed):
     """Several row and vocabulary tiles with ragged tails (M = B*(n+1) and V not
-    multiples of the 128 x 256 tile)."""
+    multiples of the 256 x 256 tile)."""
     d = synth.make_lmhead(100 + seed, device=DEV, B=B, n=n, V=V, H=H)
     got = sv.sv_lmhead_logits_debug(d["hidden"], d["weight"])
     torch.cuda.synchronize()
