@@ -13,23 +13,21 @@
 //
 // The product is logits[m][v] = sum_k hidden[m][k] * weight[v][k], hidden
 // [M][H] and weight [V][H] both K-contiguous bf16, accumulated in binary32 by
-// v_mfma_f32_32x32x16_bf16.  Lane layout of that instruction (checked on
-// MI355X): the A operand of lane l holds row l % 32, k = (l / 32) * 8 + e
-// (e = 0..7); the B operand column l % 32 at the same k; accumulator register
-// r of lane l is row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32.  Both
-// operands are therefore 16 contiguous bytes of a K-contiguous row: one
-// ds_read_b128 each.
+// the bf16 matrix cores (lane layouts of both instruction shapes checked on
+// MI355X; see Mfma below).  Both operands of a lane are 16 contiguous bytes of
+// a K-contiguous row: one ds_read_b128 each.
 //
-// Workgroup tile BM x BN = 256 x 256 by default: 8 waves (4 along the rows, 2
-// along the vocabulary), each a 64 x 128 block held in 2 x 4 accumulators of
-// 32 x 32 (128 registers), so a workgroup per CU runs two waves per SIMD.  K
-// runs in stages of 64.  A stage's A and B rows are loaded to registers with
-// 16-byte loads (8 lanes per 128-byte row segment) and written to LDS with a
-// 16-byte pad per row (rows 144 bytes apart, so the 32 lanes of a fragment
-// read hit distinct banks).  Two LDS buffers alternate: while the waves run the
-// MFMAs of stage kt from one, stage kt+1 is stored to the other and stage kt+2
-// loaded, with one barrier per stage.  Tile shape, buffering and tile order
-// are compile-time knobs; the defaults are the fastest measured on MI355X.
+// Workgroup tile BM x BN = 256 x 256 by default: 8 waves (2 along the rows, 4
+// along the vocabulary), each a 128 x 64 block held in 8 x 4 accumulators of
+// 16 x 16 (v_mfma_f32_16x16x32_bf16, 128 registers), so a workgroup per CU
+// runs two waves per SIMD.  K runs in stages of 64.  A stage's A and B rows
+// are loaded to registers with 16-byte loads (8 lanes per 128-byte row
+// segment) and written to LDS with a 16-byte pad per row (rows 144 bytes
+// apart, so the lanes of a fragment read hit distinct banks).  Two LDS buffers
+// alternate: while the waves run the MFMAs of stage kt from one, stage kt+1 is
+// stored to the other and stage kt+2 loaded, with one barrier per stage.  Tile
+// shape, matrix-core shape, buffering, scheduling strategy and tile order are
+// compile-time knobs; the defaults are the fastest measured on MI355X.
 #include <cfloat>
 #include <climits>
 #include <cmath>
@@ -38,19 +36,25 @@
 #include "sv_device.h"
 
 #ifndef SV_LM_WM
-#define SV_LM_WM 4  // waves along the hidden rows
+#define SV_LM_WM 2  // waves along the hidden rows
 #endif
 #ifndef SV_LM_WN
-#define SV_LM_WN 2  // waves along the vocabulary
+#define SV_LM_WN 4  // waves along the vocabulary
 #endif
 #ifndef SV_LM_WTM
-#define SV_LM_WTM 2  // 32 x 32 accumulator blocks per wave along the rows
+#define SV_LM_WTM 4  // 32-row units per wave
 #endif
 #ifndef SV_LM_WTN
-#define SV_LM_WTN 4  // ... along the vocabulary
+#define SV_LM_WTN 2  // 32-column units per wave
 #endif
 #ifndef SV_LM_WPE
 #define SV_LM_WPE 2  // waves per SIMD the register budget is sized for
+#endif
+#ifndef SV_LM_MFMA
+#define SV_LM_MFMA 16  // matrix-core block edge: 32 (32x32x16) or 16 (16x16x32)
+#endif
+#ifndef SV_LM_IGLP
+#define SV_LM_IGLP 1  // instruction-group scheduling strategy for the MFMA loop (-1: none)
 #endif
 #ifndef SV_LM_XCD
 #define SV_LM_XCD 1  // XCD-aware tile order
@@ -66,12 +70,51 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte load (a native vector)
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kPitch = kLmBK * 2 + 16;  // LDS bytes per tile row: one stage of K plus 16 bytes of pad
+
+// The two bf16 matrix-core shapes.  Both take 8 bf16 per lane per operand
+// (16 contiguous bytes of a K-contiguous row): lane l holds row (or column)
+// l % S at k = (l / S) * 8 + e.  Accumulator register r of lane l is column
+// l % S and row row_of(l, r).
+template <int S_>
+struct Mfma;
+template <>
+struct Mfma<32> {  // v_mfma_f32_32x32x16_bf16: 32 x 32 block, 16 k per instruction
+    static constexpr int S = 32, K = 16, NR = 16;
+    using acc_t = f32x16;
+    __device__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row_of(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+    // argmax over the lanes that share a row set (the 32 lanes of a half wave)
+    __device__ static ArgMax reduce(ArgMax a) { return half_wave_argmax(a); }
+};
+template <>
+struct Mfma<16> {  // v_mfma_f32_16x16x32_bf16: 16 x 16 block, 32 k per instruction
+    static constexpr int S = 16, K = 32, NR = 4;
+    using acc_t = f32x4;
+    __device__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row_of(int lane, int r) { return (lane >> 4) * 4 + r; }
+    // argmax over the 16 lanes of a DPP row
+    __device__ static ArgMax reduce(ArgMax a) {
+        a = better(a, dpp_am<kDppXor1>(a));
+        a = better(a, dpp_am<kDppXor2>(a));
+        a = better(a, dpp_am<kDppHalfMirror>(a));
+        a = better(a, dpp_am<kDppMirror>(a));
+        return a;
+    }
+};
+using MF = Mfma<SV_LM_MFMA>;
 
 template <int WM_, int WN_>
 struct Tile {
     static constexpr int WM = WM_, WN = WN_;
-    static constexpr int TM = SV_LM_WTM, TN = SV_LM_WTN;  // accumulator blocks per wave
+    static constexpr int TM = SV_LM_WTM, TN = SV_LM_WTN;  // 32 x 32 units per wave
+    static constexpr int QM = 32 * TM / MF::S, QN = 32 * TN / MF::S;  // accumulator blocks per wave
     static constexpr int kThreads = 64 * WM * WN;
     static constexpr int BM = 32 * TM * WM;        // hidden rows per workgroup
     static constexpr int BN = 32 * TN * WN;        // vocabulary entries per workgroup
@@ -111,37 +154,36 @@ __device__ __forceinline__ void hidden_copy_share(const LmParams& p) {
 // row tile, and merge it into keys[m] across tiles.  `scratch` is LDS the main
 // loop no longer reads (at least WN * BM * 8 bytes).
 template <class T, bool KEYS>
-__device__ __forceinline__ void lmhead_epilogue(const LmParams& p, const f32x16 (&acc)[T::TM][T::TN],
+__device__ __forceinline__ void lmhead_epilogue(const LmParams& p, const typename MF::acc_t (&acc)[T::QM][T::QN],
                                                 unsigned char* scratch, int m0, int n0) {
-    constexpr int TM = T::TM, TN = T::TN, WN = T::WN;
+    constexpr int TM = T::TM, TN = T::TN, QM = T::QM, QN = T::QN, WN = T::WN, S = MF::S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % T::WM, wn = wave / T::WM;
     if constexpr (!KEYS) {
 #pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
+        for (int bm = 0; bm < QM; ++bm)
 #pragma unroll
-            for (int bn = 0; bn < TN; ++bn)
+            for (int bn = 0; bn < QN; ++bn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = m0 + wm * 32 * TM + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    const int j = n0 + wn * 32 * TN + bn * 32 + (lane & 31);
+                for (int r = 0; r < MF::NR; ++r) {
+                    const int i = m0 + wm * 32 * TM + bm * S + MF::row_of(lane, r);
+                    const int j = n0 + wn * 32 * TN + bn * S + (lane % S);
                     if (i < p.M && j < p.V) p.logits[(size_t)i * p.V + j] = acc[bm][bn][r];
                 }
     } else {
         unsigned long long* s_key = reinterpret_cast<unsigned long long*>(scratch);  // [WN][BM]
 #pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
+        for (int bm = 0; bm < QM; ++bm)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < MF::NR; ++r) {
                 ArgMax a{-INFINITY, INT_MAX};
 #pragma unroll
-                for (int bn = 0; bn < TN; ++bn) {
-                    const int j = n0 + wn * 32 * TN + bn * 32 + (lane & 31);
+                for (int bn = 0; bn < QN; ++bn) {
+                    const int j = n0 + wn * 32 * TN + bn * S + (lane % S);
                     if (j < p.V) a = better(a, ArgMax{acc[bm][bn][r], j});
                 }
-                a = half_wave_argmax(a);
-                if ((lane & 31) == 0)
-                    s_key[wn * T::BM + wm * 32 * TM + bm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)] = argmax_key(a);
+                a = MF::reduce(a);
+                if ((lane % S) == 0) s_key[wn * T::BM + wm * 32 * TM + bm * S + MF::row_of(lane, r)] = argmax_key(a);
             }
         __syncthreads();
         for (int i = tid; i < T::BM; i += T::kThreads) {
@@ -193,14 +235,14 @@ void k_lmhead(LmParams p, int tiles_m) {
 #pragma unroll
     for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i]];
 
-    constexpr int TM = T::TM, TN = T::TN;
-    f32x16 acc[TM][TN];
+    constexpr int TM = T::TM, TN = T::TN, QM = T::QM, QN = T::QN, S = MF::S;
+    typename MF::acc_t acc[QM][QN];
 #pragma unroll
-    for (int bm = 0; bm < TM; ++bm)
+    for (int bm = 0; bm < QM; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < TN; ++bn)
+        for (int bn = 0; bn < QN; ++bn)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.f;
+            for (int r = 0; r < MF::NR; ++r) acc[bm][bn][r] = 0.f;
 
     const int KT = p.H / kLmBK;
     auto store_stage = [&](unsigned char* buf) {
@@ -219,28 +261,33 @@ void k_lmhead(LmParams p, int tiles_m) {
         for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
     };
     auto load_frags = [&](const unsigned char* buf, int s, bf16x8* fa, bf16x8* fb) {
-        const int kb = s * 32 + (lane >> 5) * 16;  // byte offset of this lane's 8 k values
+        const int kb = s * MF::K * 2 + (lane / S) * 16;  // byte offset of this lane's 8 k values
 #pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
-            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * 32 + (lane & 31)) * kPitch + kb);
+        for (int bm = 0; bm < QM; ++bm)
+            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * S + (lane % S)) * kPitch + kb);
 #pragma unroll
-        for (int bn = 0; bn < TN; ++bn)
-            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * 32 + (lane & 31)) * kPitch + kb);
-    };
-    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
-#pragma unroll
-            for (int bn = 0; bn < TN; ++bn)
-                acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
+        for (int bn = 0; bn < QN; ++bn)
+            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * S + (lane % S)) * kPitch + kb);
     };
     auto compute_stage = [&](const unsigned char* buf) {
+#if SV_LM_IGLP >= 0
+        __builtin_amdgcn_iglp_opt(SV_LM_IGLP);  // the compiler's MFMA / LDS-read interleaving strategy
+#endif
+#ifdef SV_LM_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
-        for (int s = 0; s < kLmBK / 16; ++s) {
-            bf16x8 fa[TM], fb[TN];
+        for (int s = 0; s < kLmBK / MF::K; ++s) {
+            bf16x8 fa[QM], fb[QN];
             load_frags(buf, s, fa, fb);
-            mfmas(fa, fb);
+#pragma unroll
+            for (int bm = 0; bm < QM; ++bm)
+#pragma unroll
+                for (int bn = 0; bn < QN; ++bn) acc[bm][bn] = MF::mma(fa[bm], fb[bn], acc[bm][bn]);
         }
+#ifdef SV_LM_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
 #if SV_LM_LDSBUF == 1
     // one LDS stage: store, barrier, issue the next stage's loads, compute, barrier

@@ -23,7 +23,7 @@ BUDGET = {
     "_ZN2sv5k_mtpILb1EEEvNS_9MtpParamsE": 8,               # MTP copy, aligned
     # logit projection (256 x 256 tiles, 8 waves, one workgroup per CU): two
     # waves per SIMD; the accumulators alone take 128 registers
-    "_ZN2sv12_GLOBAL__N_18k_lmheadILi4ELi2ELb1EEEvNS_8LmParamsEi": 2,
+    "_ZN2sv12_GLOBAL__N_18k_lmheadILi2ELi4ELb1EEEvNS_8LmParamsEi": 2,
 }
 
 
