@@ -273,9 +273,6 @@ void k_lmhead(LmParams p, int tiles_m) {
 #if SV_LM_IGLP >= 0
         __builtin_amdgcn_iglp_opt(SV_LM_IGLP);  // the compiler's MFMA / LDS-read interleaving strategy
 #endif
-#ifdef SV_LM_PRIO
-        __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
         for (int s = 0; s < kLmBK / MF::K; ++s) {
             bf16x8 fa[QM], fb[QN];
@@ -285,9 +282,6 @@ void k_lmhead(LmParams p, int tiles_m) {
 #pragma unroll
                 for (int bn = 0; bn < QN; ++bn) acc[bm][bn] = MF::mma(fa[bm], fb[bn], acc[bm][bn]);
         }
-#ifdef SV_LM_PRIO
-        __builtin_amdgcn_s_setprio(0);
-#endif
     };
 #if SV_LM_LDSBUF == 1
     // one LDS stage: store, barrier, issue the next stage's loads, compute, barrier

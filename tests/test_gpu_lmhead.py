@@ -100,6 +100,23 @@ def test_greedy_lmhead_full_config(oracle):
     assert acc.mean() > 0.5
 
 
+def test_greedy_lmhead_single_token_mtp_shape(oracle):
+    """The single-token MTP workload's projection shape (DeepSeek R1: D=512, n=1,
+    V=129280, H=7168, 1024 rows): a sample of 32 sequences, bit-exact, with the
+    MTP token shift/insert and hidden carry."""
+    d = synth.make_lmhead(304, device=DEV, B=512, n=1, V=129280, H=7168, ragged=True)
+    tok = d["tokens"].clone()
+    dst = torch.empty_like(d["hidden"])
+    acc, emi = _run(d, tokens=tok, hidden_dst=dst)
+    seqs = np.sort(np.random.default_rng(4).choice(d["B"], size=32, replace=False))
+    r, _ = _oracle_greedy(oracle, d, seqs)
+    assert np.array_equal(acc[seqs], r["accepted_len"])
+    assert np.array_equal(emi[seqs], r["emitted"])
+    ref_tok, _ = oracle.mtp_shift_insert(d["tokens"].cpu().numpy(), None, acc, emi)
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
+    assert torch.equal(dst.view(torch.int16), d["hidden"].view(torch.int16))
+
+
 def _gap_and_bound(d, z, seqs):
     """Per row (of the chosen sequences): the distance from the top exact logit
     to the next smaller one, and the binary32 bound 2 gamma_H max_v sum |h w|."""
