@@ -288,9 +288,9 @@ sv_status_t sv_sample_rows(const void *logits, sv_dtype_t dt, int R, const int32
  *   tokens        [B][n+1] int32 in/out, nullable: the MTP token shift/insert of
  *                 mtp_shift_insert() done by the decision
  *   hidden_dst    [B][n+1][H] bf16, nullable (needs tokens), 16-byte aligned: the
- *                 MTP hidden-state carry, written by the projection's first
- *                 column of workgroups from the tiles they load; hidden_dst ==
- *                 hidden copies nothing
+ *                 MTP hidden-state carry (a bit copy of hidden), done by the
+ *                 projection's workgroups, each copying an equal share after its
+ *                 tile; hidden_dst == hidden copies nothing
  *   workspace     >= sv_workspace_bytes(B, n, V, SV_BF16) bytes, zero-filled before
  *                 first use and left zero-filled
  * tokens and hidden_dst must not overlap any other argument (SV_EINVAL).
