@@ -211,3 +211,22 @@ def test_fused_equals_projection_then_greedy_verify():
     a2, e2 = sv.spec_verify_greedy(z, d["draft_tokens"], d["draft_lens"])
     torch.cuda.synchronize()
     assert np.array_equal(acc, a2.cpu().numpy()) and np.array_equal(emi, e2.cpu().numpy())
+
+
+def test_random_shapes_against_oracle(oracle):
+    """Twelve seeded random shapes (B, n, V, H with H a multiple of 64, V and
+    B*(n+1) mostly not multiples of the tile, n = 0 included): every decision and
+    every flag equal the oracle's on exact-sum inputs."""
+    rng = np.random.default_rng(2024)
+    for case in range(12):
+        B = int(rng.integers(1, 70))
+        n = int(rng.integers(0, 9))
+        V = int(rng.integers(1, 3000))
+        H = 64 * int(rng.integers(1, 9))
+        d = synth.make_lmhead(900 + case, device=DEV, B=B, n=n, V=V, H=H, ragged=True)
+        fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+        acc, emi = _run(d, err_flags=fl)
+        r, _ = _oracle_greedy(oracle, d)
+        assert np.array_equal(acc, r["accepted_len"]), (case, B, n, V, H)
+        assert np.array_equal(emi, r["emitted"]), (case, B, n, V, H)
+        assert int(fl.item()) == int(np.bitwise_or.reduce(r["seq_flags"])), (case, B, n, V, H)
