@@ -5,13 +5,18 @@ arithmetic (no softmax, no acceptance test, no inverse CDF, no shift).  The GPU
 parity tests, the CPU oracle tests and the benchmark all take their inputs from
 here, so both sides of every comparison see the same tensors.
 
-Workload shapes follow the five configurations the benchmark and tests use:
+Workload shapes follow the configurations the benchmark and tests use:
 
   1  tiny sampling:        B=1,    n=4, V=32000,  fp32, T=1.0, L=4
   2  Llama-vocab sampling: B=64,   n=4, V=128256, bf16, T=0.7, L ~ U{1..4}
   3  greedy + MTP shift:   B=256,  n=4, V=128256, bf16, greedy, L=4, H=8192
   4  single-token MTP:     B=512,  n=1, V=129280, bf16, T=0.6, L=1, H=7168
   5  long ragged drafts:   B=1024, n=8, V=152064, bf16, T in {0,0.7,1}, L ~ U{0..8}
+  6  recipe 2 at B=256:    B=256,  n=4, V=128256, bf16, T=0.7, L ~ U{1..4}
+
+and make_lmhead() draws hidden states and a logit projection (instead of
+logits) for the fused projection + greedy verify, B=256, n=4, V=128256, H=8192
+by default.
 
 Draft tokens for sampling sequences are drawn from the draft distribution
 softmax(z_d / T) with the Gumbel-max construction (argmax of z_d / T plus
