@@ -1,0 +1,160 @@
+"""The step inside a captured HIP graph (torch.cuda.CUDAGraph): every entry
+point enqueues kernels only (no allocation, no memset node, no host
+synchronisation) and leaves its workspace zero-filled, so one captured step can
+be replayed.  Each test captures once, then replays three times with fresh
+inputs copied into the captured buffers between replays (eager work between
+the replays), and checks every replay against the eager call on the same
+inputs."""
+import pytest
+import torch
+
+import draft_token_verification_08_amd as sv
+from draft_token_verification_08_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _refill(static, fresh):
+    for k, v in fresh.items():
+        if isinstance(v, torch.Tensor) and k in static:
+            static[k].copy_(v)
+
+
+def test_graph_greedy_mtp():
+    B, V, H = 32, 8192, 64
+    st = synth.make(3, 1, device=DEV, B=B, V=V, H=H)
+    n = st["n"]
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    emi = torch.empty((B, n + 1), dtype=torch.int32, device=DEV)
+    dst = torch.empty_like(st["hidden"])
+    ws = torch.zeros(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        sv.spec_verify_greedy_mtp(st["target"], st["draft_tokens"], st["draft_lens"], st["tokens"], st["hidden"], dst,
+                                  accepted_len=acc, emitted=emi, workspace=ws)
+
+    g = _capture(step)
+    for seed in (11, 12, 13):
+        fresh = synth.make(3, seed, device=DEV, B=B, V=V, H=H)
+        _refill(st, fresh)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        tok = fresh["tokens"].clone()
+        dst2 = torch.empty_like(dst)
+        a2, e2 = sv.spec_verify_greedy_mtp(fresh["target"], fresh["draft_tokens"], fresh["draft_lens"], tok,
+                                           fresh["hidden"], dst2)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, a2) and torch.equal(emi, e2), seed
+        assert torch.equal(st["tokens"], tok), seed
+        assert torch.equal(dst.view(torch.int16), dst2.view(torch.int16)), seed
+    assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_graph_sample_mtp_and_draft_stats(cid):
+    """Sampling verify with the MTP step, and the draft-loop form: draft
+    statistics from sv_sample_rows (row chosen on the device) feeding
+    spec_verify_sample_ex, all in one graph."""
+    B, V, H = 40, 6007, 32
+    st = synth.make(cid, 21, device=DEV, B=B, V=V, H=H)
+    n = st["n"]
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    emi = torch.empty((B, n + 1), dtype=torch.int32, device=DEV)
+    acc_x = torch.empty_like(acc)
+    emi_x = torch.empty_like(emi)
+    dst = torch.empty_like(st["hidden"])
+    tok_x = st["tokens"].clone()
+    stats = torch.empty((B, n, 2), dtype=torch.float32, device=DEV)
+    stats_j = torch.empty((B, 2), dtype=torch.float32, device=DEV)
+    first = torch.empty(B, dtype=torch.int32, device=DEV)
+    rows = [torch.full((B,), j, dtype=torch.int32, device=DEV) for j in range(n)]
+    u_d = torch.rand((max(n, 1), B), device=DEV)  # row j: the draft's uniforms of step j
+    ws = torch.zeros(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        sv.spec_verify_sample_mtp(st["target"], st["draft"], st["draft_tokens"], st["draft_lens"], st["temperature"],
+                                  st["uniforms"], st["tokens"], st["hidden"], dst, accepted_len=acc, emitted=emi,
+                                  workspace=ws)
+        for j in range(n):
+            sv.sv_sample_rows(st["draft"], st["temperature"], u_d[j], row_index=rows[j], tokens=first,
+                              row_stats=stats_j, workspace=ws2)
+            stats[:, j].copy_(stats_j)
+        sv.spec_verify_sample_ex(st["target"], st["draft"], st["draft_tokens"], st["draft_lens"], st["temperature"],
+                                 st["uniforms"], draft_stats=stats, tokens=tok_x, accepted_len=acc_x, emitted=emi_x,
+                                 workspace=ws2)
+
+    g = _capture(step)
+    for seed in (31, 32, 33):
+        fresh = synth.make(cid, seed, device=DEV, B=B, V=V, H=H)
+        _refill(st, fresh)
+        tok_x.copy_(fresh["tokens"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        tok = fresh["tokens"].clone()
+        dst2 = torch.empty_like(dst)
+        a2, e2 = sv.spec_verify_sample_mtp(fresh["target"], fresh["draft"], fresh["draft_tokens"], fresh["draft_lens"],
+                                           fresh["temperature"], fresh["uniforms"], tok, st["hidden"], dst2)
+        ref_stats = sv.draft_row_stats(fresh["draft"], fresh["temperature"])
+        tok_e = fresh["tokens"].clone()
+        a3, e3 = sv.spec_verify_sample_ex(fresh["target"], fresh["draft"], fresh["draft_tokens"], fresh["draft_lens"],
+                                          fresh["temperature"], fresh["uniforms"], draft_stats=stats.clone(),
+                                          tokens=tok_e)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, a2) and torch.equal(emi, e2), seed
+        assert torch.equal(st["tokens"], tok), seed
+        assert torch.equal(dst.view(torch.int16), dst2.view(torch.int16)), seed
+        # the graph's draft statistics are the row statistics of this replay's draft rows
+        ok = ~torch.isnan(ref_stats[..., 0])
+        assert torch.equal(stats[..., 0][ok], ref_stats[..., 0][ok]), seed
+        assert torch.allclose(stats[..., 1][ok], ref_stats[..., 1][ok], rtol=1e-5, atol=0), seed
+        assert torch.equal(acc_x, a3) and torch.equal(emi_x, e3) and torch.equal(tok_x, tok_e), seed
+    assert int(ws.count_nonzero()) == 0 and int(ws2.count_nonzero()) == 0
+
+
+def test_graph_greedy_lmhead():
+    B, n, V, H = 24, 4, 3000, 192
+    st = synth.make_lmhead(41, device=DEV, B=B, n=n, V=V, H=H, ragged=True)
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    emi = torch.empty((B, n + 1), dtype=torch.int32, device=DEV)
+    dst = torch.empty_like(st["hidden"])
+    ws = torch.zeros(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        sv.spec_verify_greedy_lmhead(st["hidden"], st["weight"], st["draft_tokens"], st["draft_lens"],
+                                     tokens=st["tokens"], hidden_dst=dst, accepted_len=acc, emitted=emi, workspace=ws)
+
+    g = _capture(step)
+    for seed in (42, 43, 44):
+        fresh = synth.make_lmhead(seed, device=DEV, B=B, n=n, V=V, H=H, ragged=True)
+        _refill(st, fresh)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        tok = fresh["tokens"].clone()
+        dst2 = torch.empty_like(dst)
+        a2, e2 = sv.spec_verify_greedy_lmhead(fresh["hidden"], fresh["weight"], fresh["draft_tokens"],
+                                              fresh["draft_lens"], tokens=tok, hidden_dst=dst2)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, a2) and torch.equal(emi, e2), seed
+        assert torch.equal(st["tokens"], tok), seed
+        assert torch.equal(dst.view(torch.int16), dst2.view(torch.int16)), seed
+    assert int(ws.count_nonzero()) == 0
