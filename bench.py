@@ -48,6 +48,8 @@ def parse():
                          "(spec_verify_sample_ex) instead of streaming the draft rows")
     ap.add_argument("--unfused", action="store_true",
                     help="separate verify and mtp_shift_insert calls instead of the fused call")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each input copy's step into a HIP graph and time graph replays")
     ap.add_argument("--lmhead", action="store_true",
                     help="greedy verify fused with the target's logit projection (spec_verify_greedy_lmhead): "
                          "hidden states [256, 5, 8192] and a [128256, 8192] projection instead of logits")
@@ -117,7 +119,9 @@ def main():
     wsbuf = ws.get(sv.sv_workspace_bytes(cfg.B, cfg.n, cfg.V, sv.SV_BF16 if es == 2 else sv.SV_F32))
     stream = torch.cuda.current_stream(dev)
 
-    # calls marshalled once per input copy (the C entry points are re-issued as is)
+    # calls marshalled once per input copy (the C entry points are re-issued as is);
+    # with --graph they are bound to the capture stream and captured below
+    cap = torch.cuda.Stream(dev) if args.graph else None
     fused = bool(cfg.H) and not args.unfused
     dstats = args.draft_stats and not greedy
     for d in data:
@@ -127,30 +131,51 @@ def main():
             d["verify"] = sv.prepare_spec_verify_sample_ex(
                 d["target"], d["draft"], d["draft_tokens"], d["draft_lens"], d["temperature"], d["uniforms"],
                 d["acc"], d["emi"], wsbuf, draft_stats=d["dstats"], tokens=d["tokens"] if fused else None,
-                hidden_src=d["hidden"] if fused else None, hidden_dst=d["hidden_dst"] if fused else None)
+                hidden_src=d["hidden"] if fused else None, hidden_dst=d["hidden_dst"] if fused else None,
+                stream=cap)
             d["mtp"] = (lambda: None) if fused or not cfg.H else sv.prepare_mtp_shift_insert(
-                d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+                d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"], stream=cap)
             continue
         if fused:
             if greedy:
                 d["verify"] = sv.prepare_spec_verify_greedy_mtp(d["target"], d["draft_tokens"], d["draft_lens"],
                                                                 d["acc"], d["emi"], d["tokens"], d["hidden"],
-                                                                d["hidden_dst"], wsbuf)
+                                                                d["hidden_dst"], wsbuf, stream=cap)
             else:
                 d["verify"] = sv.prepare_spec_verify_sample_mtp(d["target"], d["draft"], d["draft_tokens"],
                                                                 d["draft_lens"], d["temperature"], d["uniforms"],
                                                                 d["acc"], d["emi"], d["tokens"], d["hidden"],
-                                                                d["hidden_dst"], wsbuf)
+                                                                d["hidden_dst"], wsbuf, stream=cap)
             d["mtp"] = lambda: None
             continue
         if greedy:
             d["verify"] = sv.prepare_spec_verify_greedy(d["target"], d["draft_tokens"], d["draft_lens"], d["acc"],
-                                                        d["emi"], wsbuf)
+                                                        d["emi"], wsbuf, stream=cap)
         else:
             d["verify"] = sv.prepare_spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
-                                                        d["temperature"], d["uniforms"], d["acc"], d["emi"], wsbuf)
-        d["mtp"] = (sv.prepare_mtp_shift_insert(d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"])
+                                                        d["temperature"], d["uniforms"], d["acc"], d["emi"], wsbuf,
+                                                        stream=cap)
+        d["mtp"] = (sv.prepare_mtp_shift_insert(d["tokens"], d["hidden"], d["hidden_dst"], d["acc"], d["emi"],
+                                                stream=cap)
                     if cfg.H else (lambda: None))
+
+    if args.graph:
+        # one graph per input copy holding the whole step; replays run on the
+        # launch stream
+        cap.wait_stream(stream)
+        for d in data:
+            d["verify"]()
+            d["mtp"]()
+        torch.cuda.synchronize()
+        for d in data:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                d["verify"]()
+                d["mtp"]()
+            d["graph"] = g
+            d["verify"] = g.replay
+            d["mtp"] = lambda: None
+        torch.cuda.synchronize()
 
     def verify(d):
         d["verify"]()
@@ -197,7 +222,7 @@ def main():
     # (offset 4).
     K = args.steps
     EVERY = 8
-    single = not (cfg.H and not fused)
+    single = args.graph or not (cfg.H and not fused)
     RUN = 8 if single and K >= 8 else 1
     starts = range(0, K - RUN + 1, 2 * RUN) if single else range(0, K, EVERY)
     ev_v = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in starts}
@@ -235,8 +260,9 @@ def main():
     # fused: the hidden states and the token buffer cross HBM once each way (the
     # verify outputs are not read back)
     fused_mtp_bytes = 2 * cfg.B * (cfg.n + 1) * cfg.H * 2 + 2 * cfg.B * (cfg.n + 1) * 4
-    v_bytes = statistics.fmean(verify_bytes[(i + r) % sets] + (fused_mtp_bytes if fused else 0)
-                               for i in ev_v for r in range(RUN))
+    # a graph of an unfused step holds the MTP launch too
+    step_extra = fused_mtp_bytes if fused else (mtp_bytes if args.graph else 0)
+    v_bytes = statistics.fmean(verify_bytes[(i + r) % sets] + step_extra for i in ev_v for r in range(RUN))
     v_gbps = v_bytes / (v_avg_ms * 1e-3) / 1e9
     m_avg_ms = statistics.fmean(mtp_ms) if cfg.H and not fused else 0.0
     mean_acc = float(torch.stack([d["acc"].float().mean() for d in data]).mean())
@@ -255,7 +281,7 @@ def main():
     kernel = (("k_stats_greedy" if greedy else "k_stats_sample+k_draw") + ("+draft_stats" if dstats else "")
               + ("+mtp_fused" if fused else ""))
     workload = cfg.name
-    traffic = measured_traffic(kernel, workload)
+    traffic = measured_traffic(kernel, workload) if not (args.graph and cfg.H and not fused) else None
 
     out = {
         "metric": "verified vocab rows/s + HBM GB/s (% of peak), V=128256 bf16, B=256, n=4",
@@ -273,6 +299,7 @@ def main():
         "config": {"workload": ("greedy verify" if greedy else "sampling verify")
                    + (" with the draft's row statistics" if dstats else "")
                    + (" + MTP shift/insert" + (" (fused call)" if fused else " (two calls)") if cfg.H else "")
+                   + (", replayed from a HIP graph" if args.graph else "")
                    + f" ({cfg.name})", "B": cfg.B, "n": cfg.n, "V": cfg.V, "H": cfg.H,
                    "logits": "bf16" if es == 2 else "f32", "parallelism": "none (1 GPU)"},
         "hbm_gbps": round(gbps, 1),
