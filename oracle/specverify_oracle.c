@@ -502,8 +502,16 @@ static void *lm_slice(void *arg)
             return NULL;
         }
         double acc = 0.0;
+#if SV_ORACLE_PLANT == 4 /* negative control: the last product is dropped */
+        for (int k = 0; k < H - 1; ++k)
+#else
         for (int k = 0; k < H; ++k)
+#endif
+#if SV_ORACLE_PLANT == 5 /* negative control: the weight is indexed transposed */
+            acc += bf16_at(J->hidden, (size_t)r * H + k) * bf16_at(J->weight, (size_t)k * V + v);
+#else
             acc += bf16_at(J->hidden, (size_t)r * H + k) * bf16_at(J->weight, (size_t)v * H + k);
+#endif
         J->out[o] = acc;
     }
     return NULL;

@@ -116,3 +116,32 @@ def test_greedy_on_float64_logits_matches_numpy_and_float32(o):
         assert r64["emitted"][b, k] == am[b, k]
     assert r64["accepted_len"][1] == 1 and r64["emitted"][1, 1] == 7
     assert r64["accepted_len"][2] == 0 and r64["emitted"][2, 0] == 2
+
+
+def _pins_hold(orc):
+    """The projection pins above, as one boolean (for the negative controls)."""
+    ok = True
+    for M, H, V in [(7, 48, 33), (12, 64, 129)]:
+        h, w = _int_case(M * 1000 + H + V, M, H, V)
+        ok &= np.array_equal(orc.lmhead_logits(_bits(h), _bits(w)), h.astype(np.float64) @ w.astype(np.float64).T)
+    rng = np.random.default_rng(1)
+    M, H, V = 6, 10, 23
+    w = (rng.integers(-100, 101, (V, H)) / 64.0).astype(np.float32)
+    ks = rng.integers(0, H, M)
+    h = np.zeros((M, H), np.float32)
+    h[np.arange(M), ks] = 1.0
+    got = orc.lmhead_logits(_bits(h), _bits(w))
+    ok &= all(np.array_equal(got[i], w[:, ks[i]].astype(np.float64)) for i in range(M))
+    return bool(ok)
+
+
+def test_projection_pins_hold_for_the_oracle(o):
+    assert _pins_hold(o)
+
+
+@pytest.mark.parametrize("plant", [4, 5])
+def test_planted_projection_mistakes_fail_the_pins(planted, plant):
+    """Oracle builds with a dropped product (4) or a transposed weight index (5)
+    must fail the pins."""
+    assert not _pins_hold(planted(plant))
+
