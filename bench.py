@@ -278,6 +278,23 @@ def main():
     torch.cuda.synchronize()
     event_pair_us = statistics.median(a.elapsed_time(b2) for a, b2 in bare) * 1e3
 
+    # attainable-bandwidth reference on the same box: a 1 GiB device-to-device
+    # copy (read + write bytes over its event time, median of 10)
+    src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_c = torch.empty_like(src_c)
+    dst_c.copy_(src_c)
+    torch.cuda.synchronize()
+    cps = []
+    for _ in range(10):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst_c.copy_(src_c)
+        b2.record(stream)
+        torch.cuda.synchronize()
+        cps.append(2 * (1 << 30) / (a.elapsed_time(b2) * 1e-3) / 1e9)
+    copy_gbps = statistics.median(cps)
+    del src_c, dst_c
+
     kernel = (("k_stats_greedy" if greedy else "k_stats_sample+k_draw") + ("+draft_stats" if dstats else "")
               + ("+mtp_fused" if fused else ""))
     workload = cfg.name
@@ -314,6 +331,7 @@ def main():
                      "timing": (f"HIP event pair around {RUN} consecutive launches, every {2 * RUN} steps"
                                 if RUN > 1 else "HIP event pair around the launch of every 8th step"),
                      "bare_event_pair_us": round(event_pair_us, 2),
+                     "copy_1gib_gbps": round(copy_gbps, 1),
                      "traffic": traffic},
     }
 
