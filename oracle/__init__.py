@@ -22,13 +22,18 @@ FLAG_LEN_CLAMPED, FLAG_TOKEN_OOR, FLAG_BAD_TEMP, FLAG_BAD_UNIFORM, FLAG_ZERO_RES
 FLAG_ROW_CLAMPED = 32
 
 
-def build(out_path: str = LIB, plant: int = 0) -> str:
+def build(out_path: str = LIB, plant: int = 0, sanitize: bool = False) -> str:
     """Compile the oracle with gcc.  ``plant`` > 0 builds a test-only variant that
-    carries one deliberate mistake (used by negative-control tests)."""
+    carries one deliberate mistake (used by negative-control tests);
+    ``sanitize`` builds it with AddressSanitizer and UndefinedBehaviorSanitizer
+    (load it in a process that preloads their runtimes)."""
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-D_POSIX_C_SOURCE=200809L", SRC, "-o", out_path, "-lm", "-lpthread"]
     if plant:
         cmd.insert(1, f"-DSV_ORACLE_PLANT={int(plant)}")
+    if sanitize:
+        cmd[1:2] = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all"]
     subprocess.run(cmd, check=True)
     return out_path
 
