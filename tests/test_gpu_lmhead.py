@@ -50,7 +50,7 @@ def _run(d, **kw):
 
 
 @pytest.mark.parametrize("B,n,V,H,seed", [(9, 4, 1000, 192, 0), (26, 4, 257, 64, 1), (52, 4, 4096, 512, 2),
-                                          (3, 0, 300, 128, 3)])
+                                          (3, 0, 300, 128, 3), (2, 1, 1, 64, 4), (1, 0, 33, 64, 5)])
 def test_projection_bit_exact_on_exact_inputs(oracle, B, n, V, H, seed):
     """Several row and vocabulary tiles with ragged tails (M = B*(n+1) and V not
     multiples of the 256 x 256 tile)."""
@@ -76,7 +76,8 @@ def test_projection_within_summation_bound_on_gaussian_inputs(oracle):
 
 
 @pytest.mark.parametrize("B,n,V,H,ragged,seed", [(37, 4, 5003, 256, False, 0), (64, 4, 2048, 128, True, 1),
-                                                 (24, 8, 1001, 320, True, 2), (130, 1, 700, 64, False, 3)])
+                                                 (24, 8, 1001, 320, True, 2), (130, 1, 700, 64, False, 3),
+                                                 (5, 2, 1, 64, True, 4), (9, 3, 7, 128, True, 5)])
 def test_greedy_lmhead_exact(oracle, B, n, V, H, ragged, seed):
     d = synth.make_lmhead(200 + seed, device=DEV, B=B, n=n, V=V, H=H, ragged=ragged)
     fl = torch.zeros(1, dtype=torch.int32, device=DEV)
