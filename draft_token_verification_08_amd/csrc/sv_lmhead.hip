@@ -22,10 +22,11 @@
 // 16 x 16 (v_mfma_f32_16x16x32_bf16, 128 registers), so a workgroup per CU
 // runs two waves per SIMD.  K runs in stages of 64.  A stage's A and B rows
 // are loaded to registers with 16-byte loads (8 lanes per 128-byte row
-// segment) and written to LDS with a 16-byte pad per row (rows 144 bytes
-// apart, so the lanes of a fragment read hit distinct banks).  Two LDS buffers
-// alternate: while the waves run the MFMAs of stage kt from one, stage kt+1 is
-// stored to the other and stage kt+2 loaded, with one barrier per stage.  Tile
+// segment) and written to LDS with a 32-byte pad per row (rows 160 bytes
+// apart, so the lanes of a fragment read hit distinct banks; the two stage
+// buffers then fill the 160 KB of LDS exactly).  The two buffers alternate:
+// while the waves run the MFMAs of stage kt from one, stage kt+1 is stored to
+// the other and stage kt+2 loaded, with one barrier per stage.  Tile
 // shape, matrix-core shape, buffering, scheduling strategy and tile order are
 // compile-time knobs; the defaults are the fastest measured on MI355X.
 #include <cfloat>
@@ -56,6 +57,9 @@
 #ifndef SV_LM_IGLP
 #define SV_LM_IGLP 1  // instruction-group scheduling strategy for the MFMA loop (-1: none)
 #endif
+#ifndef SV_LM_PAD
+#define SV_LM_PAD 32  // LDS row pad in bytes (a multiple of 16)
+#endif
 #ifndef SV_LM_XCD
 #define SV_LM_XCD 1  // XCD-aware tile order
 #endif
@@ -72,7 +76,12 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte lo
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPitch = kLmBK * 2 + 16;  // LDS bytes per tile row: one stage of K plus 16 bytes of pad
+// LDS bytes per tile row: one stage of K plus a pad.  The pad decides the
+// bank pattern of the fragment reads (rows (lane % 16), 16-byte chunk lane / 16
+// for the 16 x 16 blocks): measured on MI355X, 144-byte rows give 2-way bank
+// conflicts for that pattern and 160-byte rows none.
+constexpr int kPitch = kLmBK * 2 + SV_LM_PAD;
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kPitch + (c << 4); }
 
 // The two bf16 matrix-core shapes.  Both take 8 bf16 per lane per operand
 // (16 contiguous bytes of a K-contiguous row): lane l holds row (or column)
@@ -248,10 +257,10 @@ void k_lmhead(LmParams p, int tiles_m) {
     auto store_stage = [&](unsigned char* buf) {
 #pragma unroll
         for (int i = 0; i < T::kA; ++i)
-            *reinterpret_cast<v4u*>(buf + (lrow + i * T::kRowStep) * kPitch + lcol * 16) = ra[i];
+            *reinterpret_cast<v4u*>(buf + lds_off(lrow + i * T::kRowStep, lcol)) = ra[i];
 #pragma unroll
         for (int i = 0; i < T::kB; ++i)
-            *reinterpret_cast<v4u*>(buf + (T::BM + lrow + i * T::kRowStep) * kPitch + lcol * 16) = rb[i];
+            *reinterpret_cast<v4u*>(buf + lds_off(T::BM + lrow + i * T::kRowStep, lcol)) = rb[i];
     };
     auto load_stage = [&](int kt) {
         const unsigned o = (unsigned)kt * (kLmBK / 8);
@@ -261,13 +270,13 @@ void k_lmhead(LmParams p, int tiles_m) {
         for (int i = 0; i < T::kB; ++i) rb[i] = W[boff[i] + o];
     };
     auto load_frags = [&](const unsigned char* buf, int s, bf16x8* fa, bf16x8* fb) {
-        const int kb = s * MF::K * 2 + (lane / S) * 16;  // byte offset of this lane's 8 k values
+        const int kc = s * (MF::K / 8) + lane / S;  // 16-byte chunk of this lane's 8 k values
 #pragma unroll
         for (int bm = 0; bm < QM; ++bm)
-            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + (wm * 32 * TM + bm * S + (lane % S)) * kPitch + kb);
+            fa[bm] = *reinterpret_cast<const bf16x8*>(buf + lds_off(wm * 32 * TM + bm * S + (lane % S), kc));
 #pragma unroll
         for (int bn = 0; bn < QN; ++bn)
-            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + (T::BM + wn * 32 * TN + bn * S + (lane % S)) * kPitch + kb);
+            fb[bn] = *reinterpret_cast<const bf16x8*>(buf + lds_off(T::BM + wn * 32 * TN + bn * S + (lane % S), kc));
     };
     auto compute_stage = [&](const unsigned char* buf) {
 #if SV_LM_IGLP >= 0
