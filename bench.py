@@ -81,7 +81,7 @@ def measured_traffic(kernel: str, workload: str, src: str = KERNEL_SRC):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sequences shard "
+        print("bench.py measures one GPU: the library has no multi-GPU path (sequences shard "
               "across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -32,7 +32,7 @@
  * Everything is computed in double precision, scalar, with sums taken in
  * ascending index order.  Nothing is blocked, fused or reordered.
  *
- * Readings of points the pages leave open (each is also listed in the design doc):
+ * Readings of points the pages leave open:
  *   - acceptance of draft x_j:  u[b][j] < p_j(x_j) / q_j(x_j); q(x) = 0 gives
  *     ratio +inf when p(x) > 0 and 0 when p(x) = 0;
  *   - p and q are softmax(z / T_b) at the same per-sequence temperature T_b;
@@ -579,7 +579,7 @@ int sv_oracle_draw_weights(const double *w, int V, double u, double *margin)
     return draw_inverse_cdf(w, V, u, margin);
 }
 
-/* Which planted mistake this build carries (0 = none).  Test-only builds set
+/* Which planted mistake this compiled oracle carries (0 = none).  Test-only builds set
  * SV_ORACLE_PLANT to show that the statistical tests reject a wrong rule. */
 int sv_oracle_plant(void)
 {

@@ -67,7 +67,7 @@ def test_draft_stats_match_oracle_rows(oracle):
 
 
 def test_verify_with_draft_stats_full_config(oracle):
-    """Config 5 at full size (B=1024, n=8, V=152064); the oracle checks a sample."""
+    """The long ragged drafts workload at full size (B=1024, n=8, V=152064); the oracle checks a sample."""
     d = synth.make(5, 505, device=DEV)
     stats = sv.draft_row_stats(d["draft"], d["temperature"])
     acc, emi = sv.spec_verify_sample_ex(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
