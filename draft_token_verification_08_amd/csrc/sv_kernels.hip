@@ -278,8 +278,26 @@ __device__ int block_max_all(int v) {
 // vector whose maximum beats its running maximum (index and contents, in
 // registers: the streamed lines are not cached, so nothing is re-read); the lane
 // inside that vector is resolved once at the end.
-template <int DT, bool ALIGNED>
-__device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
+// The first group of thread_argmax's aligned loop (U vectors per thread), issued
+// on its own so that a caller can start it before it knows the row is needed.
+// Loads nothing when the range holds no full group.
+template <int DT>
+__device__ __forceinline__ void argmax_first_group(const void* row, int lo, int hi, uint4 (&w)[SV_ARGMAX_UNROLL]) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int U = SV_ARGMAX_UNROLL;
+    const int v = lo / kVec + (int)threadIdx.x, v1 = hi / kVec;
+    if (v + (U - 1) * kThreads < v1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = ld16((const uint4*)row + v + u * kThreads);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// PRE: `pre` holds the first group, loaded by argmax_first_group on the same range.
+template <int DT, bool ALIGNED, bool PRE = false>
+__device__ ArgMax thread_argmax(const void* row, int lo, int hi, const uint4* pre = nullptr) {
     constexpr int kVec = Elem<DT>::kVec;
     const int tid = threadIdx.x;
     if constexpr (ALIGNED) {
@@ -290,10 +308,7 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
         int bestv = -1;
         uint4 bestw = make_uint4(0, 0, 0, 0);
         int v = v0 + tid;
-        for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
-            uint4 w[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
+        auto consume = [&](const uint4 (&w)[U], int vb) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float f[kVec];
@@ -303,10 +318,25 @@ __device__ ArgMax thread_argmax(const void* row, int lo, int hi) {
                 for (int e = 1; e < kVec; ++e) m = fmaxf(m, f[e]);
                 if (m > best) {
                     best = m;
-                    bestv = v + u * kThreads;
+                    bestv = vb + u * kThreads;
                     bestw = w[u];
                 }
             }
+        };
+        if constexpr (PRE) {
+            if (v + (U - 1) * kThreads < v1) {
+                uint4 w[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) w[u] = pre[u];
+                consume(w, v);
+                v += U * kThreads;
+            }
+        }
+        for (; v + (U - 1) * kThreads < v1; v += U * kThreads) {
+            uint4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = ld16(vrow + v + u * kThreads);
+            consume(w, v);
         }
         for (; v < v1; v += kThreads) {
             const uint4 w = ld16(vrow + v);
@@ -910,6 +940,15 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     const int slot = rest % p.S;
     const int b = rest / p.S;
     const int n = p.n;
+    const int lo = c * p.CH;
+    const int hi = min(p.V, lo + p.CH);
+
+    // Greedy launches read target rows only, and every slot <= n lies inside the
+    // [B][n+1][V] target buffer: the first load group is issued before the draft
+    // length says whether the row is needed (the values are used only if it is).
+    uint4 pre[SV_ARGMAX_UNROLL];
+    if constexpr (MODE == kGreedy && ALIGNED)
+        argmax_first_group<DT>(row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, slot), p.V), lo, hi, pre);
 
     const SeqInfo si = seq_info<MODE>(p, b);
     const bool target_row = slot <= n;
@@ -924,14 +963,14 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
 
     const void* row = target_row ? row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, slot), p.V)
                                  : row_ptr<DT>(p.draft, (long long)b * n + (slot - n - 1), p.V);
-    const int lo = c * p.CH;
-    const int hi = min(p.V, lo + p.CH);
-
     unsigned long long* slot_part =
         reinterpret_cast<unsigned long long*>(p.part) + ((size_t)b * p.S + slot) * p.NC;
     __shared__ int s_last;
     if (si.greedy) {
-        const ArgMax r = block_argmax(thread_argmax<DT, ALIGNED>(row, lo, hi));
+        ArgMax t;
+        if constexpr (MODE == kGreedy && ALIGNED) t = thread_argmax<DT, ALIGNED, true>(row, lo, hi, pre);
+        else t = thread_argmax<DT, ALIGNED>(row, lo, hi);
+        const ArgMax r = block_argmax(t);
         if (threadIdx.x == 0) {
             const unsigned long long dep = max64(slot_part, argmax_key(r));  // merged across chunks
             s_last = (arrive(&p.cnt[b], dep) == expected - 1u);

@@ -37,8 +37,12 @@
  *       uniform NaN or < 0 / >= 1      -> 0 / largest float < 1  SV_FLAG_BAD_UNIFORM
  *       residual mass not positive     -> draw from p_k          SV_FLAG_ZERO_RESIDUAL
  *       row_index[b] outside [0, R)    -> clamped                SV_FLAG_ROW_CLAMPED
- *   - Rows the step does not need are never read: target rows r > L_b, draft
- *     rows r >= L_b, and draft rows of sequences with T_b = 0.
+ *   - Rows the step does not need never enter a result: target rows r > L_b,
+ *     draft rows r >= L_b, and draft rows of sequences with T_b = 0.  The
+ *     sampling calls never load them; the greedy calls may fetch the first few
+ *     KB of an unneeded target row (its loads start before the draft length has
+ *     arrived) and discard them, so those rows must be allocated (they are: the
+ *     target buffer is [B][n+1][V]) but may hold anything, NaN included.
  *   - Calls that share one workspace must not overlap in time (same stream, or
  *     ordered by events).
  */
