@@ -1,0 +1,60 @@
+"""bench.py's host-side contract, on the CPU: it measures one GPU and refuses
+more; the measured-traffic table is well formed and is used only while the
+kernel source it was taken on is unchanged."""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _run(args, env_extra=None):
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT, env=env,
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], None), (["--gpus", "8"], None), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    r = _run(args, env)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line
+
+
+def test_traffic_table_is_well_formed():
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert t, "empty traffic table"
+    for key, e in t.items():
+        kernel, workload = key.split("|")
+        assert kernel and workload
+        assert len(e["source_sha256_16"]) == 16
+        for k in ("fetch_scale", "write_scale", "bytes_per_launch", "algorithmic_bytes_per_launch"):
+            assert e[k] > 0, (key, k)
+        # the copy-kernel calibration: FETCH_SIZE counts half the bytes on this part, WRITE_SIZE all of them
+        assert 1.9 < e["fetch_scale"] < 2.1 and 0.95 < e["write_scale"] < 1.05, key
+        # measured traffic is at least the algorithmic bytes (within counter noise)
+        assert e["bytes_per_launch"] >= 0.99 * e["algorithmic_bytes_per_launch"], key
+        if "stats_pass_bytes" in e:
+            assert e["stats_pass_bytes"] + e["draw_pass_bytes"] == e["bytes_per_launch"], key
+
+
+def test_traffic_used_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    h = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    table = tmp_path / "traffic.json"
+    table.write_text(json.dumps({"k|w": {"source_sha256_16": h, "bytes_per_launch": 1234}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(table))
+    assert bench.measured_traffic("k", "w", str(src)) == 1234
+    assert bench.measured_traffic("k", "other", str(src)) is None
+    src.write_text("// kernel v2\n")  # the kernel changed after the counters were taken
+    assert bench.measured_traffic("k", "w", str(src)) is None
