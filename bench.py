@@ -50,6 +50,9 @@ def parse():
                     help="separate verify and mtp_shift_insert calls instead of the fused call")
     ap.add_argument("--graph", action="store_true",
                     help="capture each input copy's step into a HIP graph and time graph replays")
+    ap.add_argument("--draft-step", action="store_true",
+                    help="the draft loop's per-step sampling (sv_sample_rows with row statistics): one token per "
+                         "sequence from logits [256, 128256] bf16 at T=0.7")
     ap.add_argument("--lmhead", action="store_true",
                     help="greedy verify fused with the target's logit projection (spec_verify_greedy_lmhead): "
                          "hidden states [256, 5, 8192] and a [128256, 8192] projection instead of logits")
@@ -98,6 +101,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.lmhead:
         bench_lmhead(args, dev)
+        return
+    if args.draft_step:
+        bench_draft_step(args, dev)
         return
     cfg = synth.CONFIGS[args.config]
     greedy = cfg.mode == "greedy"
@@ -501,6 +507,113 @@ def bench_lmhead(args, dev):
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_lmhead(d, B, n, V, H)
     print(json.dumps(out), flush=True)
+
+
+def bench_draft_step(args, dev):
+    """The draft loop's per-step sampling: one token per sequence from its logits
+    row at temperature T (sv_sample_rows), keeping the row statistics {max, sum}
+    that the verify later takes instead of streaming the draft rows.  Inputs: the
+    llama-vocab sampling recipe with no drafts, B=256, V=128256 bf16, T=0.7,
+    resident in HBM and rotated over input copies larger than the MALL together."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_08_amd as sv
+    from draft_token_verification_08_amd import synth
+
+    B, V = 256, 128256
+    sets = args.sets or 8
+    wsbuf = sv.Workspace(dev).get(sv.sv_workspace_bytes(B, 0, V, sv.SV_BF16))
+    stream = torch.cuda.current_stream(dev)
+    data, calls = [], []
+    for i in range(sets):
+        d = synth.make(6, args.seed + i, device=dev, n=0)
+        d["u"] = d["uniforms"][:, 0].contiguous()
+        d["tok"] = torch.empty(B, dtype=torch.int32, device=dev)
+        d["stats"] = torch.empty((B, 2), dtype=torch.float32, device=dev)
+        data.append(d)
+        calls.append(sv.prepare_sv_sample_rows(d["target"], d["temperature"], d["u"], d["tok"], wsbuf,
+                                               row_stats=d["stats"]))
+    torch.cuda.synchronize()
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        calls[i % sets]()
+    torch.cuda.synchronize()
+    # one event pair around 8 consecutive calls in every 16 steps
+    brackets = []
+    t0 = time.perf_counter()
+    i = 0
+    while i < K:
+        if i % 16 == 0 and i + 8 <= K:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for j in range(8):
+                calls[(i + j) % sets]()
+            b.record(stream)
+            brackets.append((a, b))
+            i += 8
+        else:
+            calls[i % sets]()
+            i += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_ms = statistics.fmean(a.elapsed_time(b) for a, b in brackets) / 8 if brackets else elapsed * 1e3 / K
+    nbytes = B * V * 2 + B * (4 + 4 + 4 + 8)  # rows read once; temperature, uniform, token, statistics
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "sampled vocab rows/s + HBM GB/s (% of peak), V=128256 bf16, B=256 (draft-step sampling)",
+        "value": round(B * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {sets} copies)",
+        "config": {"workload": "draft-step sampling with row statistics (sv_sample_rows), logits [256, 128256] "
+                               "bf16, T=0.7 (draft_step_sampling)", "B": B, "V": V, "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(nbytes * K / elapsed / 1e9, 1),
+        "pct_of_peak": round(nbytes * K / elapsed / 1e9 / PEAK_GBPS * 100, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_stats_sample+k_draw (no drafts)", "achieved": round(achieved, 1),
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "bytes_per_launch": nbytes, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "timed_launches": 8 * len(brackets),
+                     "timing": "HIP event pair around 8 consecutive calls, every 16 steps",
+                     "traffic": measured_traffic("k_stats_sample+k_draw", "draft_step_sampling")},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_draft_step(data[0], B, V)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_draft_step(d, B, V):
+    """The oracle (untuned) drawing one token per row on a bounded sample: whole
+    batches of the same rows, as many as fit about 10-20 s of CPU work."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    z = synth.host_logits(d["target"])
+    T = d["temperature"].cpu().numpy()
+    u = d["u"].cpu().numpy()
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    calls, t0 = 0, time.perf_counter()
+    while calls < 1 or (time.perf_counter() - t0 < 20.0 / threads and calls < 200):
+        orc.sample_rows(z, T, u, threads=threads)
+        calls += 1
+    el = time.perf_counter() - t0
+    return {"value": round(calls * B / el, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full steps ({B} rows of V={V}) on {threads} threads, about {el * threads:.0f} s "
+                      f"of CPU work", "cpu_model": cpu_model()}
 
 
 def cpu_baseline_lmhead(d, B, n, V, H):

@@ -643,6 +643,31 @@ def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None
     return tokens
 
 
+def prepare_sv_sample_rows(logits, temperature, uniforms, tokens, workspace, *, row_index=None, err_flags=None,
+                           row_stats=None, stream=None) -> Prepared:
+    """sv_sample_rows with its arguments marshalled once (see sv_sample_rows)."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(1)
+    B, R, V = logits.shape
+    dev = logits.device
+    dt = _dt(logits)
+    _check(logits, "logits")
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B,), dev)
+    _check(tokens, "tokens", torch.int32, (B,), dev)
+    if row_index is not None:
+        _check(row_index, "row_index", torch.int32, (B,), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    if row_stats is not None:
+        _check(row_stats, "row_stats", torch.float32, (B, 2), dev)
+    _check(workspace, "workspace", torch.uint8)
+    args = (_ptr(logits), dt, R, _ptr(row_index), _ptr(temperature), _ptr(uniforms), B, V, _ptr(tokens),
+            _ptr(err_flags), _ptr(row_stats), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return Prepared("sv_sample_rows", args, (logits, temperature, uniforms, tokens, workspace, row_index, err_flags,
+                                             row_stats))
+
+
 def prepare_spec_verify_greedy_lmhead(hidden, weight, draft_tokens, draft_lens, accepted_len, emitted, workspace,
                                       tokens=None, hidden_dst=None, err_flags=None, stream=None) -> Prepared:
     B, n, V, H = _lmhead_args(hidden, weight, draft_tokens, draft_lens, tokens, hidden_dst)

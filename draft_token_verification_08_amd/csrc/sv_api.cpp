@@ -73,6 +73,10 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     return true;
 }
 
+#ifndef SV_DRAW_IN_STATS
+#define SV_DRAW_IN_STATS 1  // calls with no drafts make their draws in the stats pass's decision
+#endif
+
 template <class T>
 T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -278,26 +282,30 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
     sp.R = n + 1;
     sp.row_index = nullptr;
     sp.dstats = draft_stats;
+    // no drafts: every draw is a bonus draw, made by the decision (no draw pass)
+    sp.draw_in_stats = (SV_DRAW_IN_STATS && n == 0) ? 1 : 0;
     if (mtp && pl.fused) sp.mtp = pl.f;
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
 
-    sv::DrawParams dp{};
-    dp.target = target_logits;
-    dp.draft = draft_logits;
-    dp.B = B; dp.n = n; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
-    dp.R = sp.R;
-    dp.row_index = sp.row_index;
-    dp.tiles = sp.tiles;
-    dp.emitted = emitted;
-    dp.flags = err_flags;
-    dp.desc = sp.desc;
-    dp.dres = at<float>(workspace, L.off_dres);
-    dp.dp = at<float>(workspace, L.off_dp);
-    dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
-    if (mtp && pl.fused) dp.mtp_tokens = pl.f.tokens;
-    e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
-    if (e != hipSuccess) return hip_fail(e);
+    if (!sp.draw_in_stats) {
+        sv::DrawParams dp{};
+        dp.target = target_logits;
+        dp.draft = draft_logits;
+        dp.B = B; dp.n = n; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
+        dp.R = sp.R;
+        dp.row_index = sp.row_index;
+        dp.tiles = sp.tiles;
+        dp.emitted = emitted;
+        dp.flags = err_flags;
+        dp.desc = sp.desc;
+        dp.dres = at<float>(workspace, L.off_dres);
+        dp.dp = at<float>(workspace, L.off_dp);
+        dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+        if (mtp && pl.fused) dp.mtp_tokens = pl.f.tokens;
+        e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     if (mtp && !pl.fused) {
         e = sv::launch_mtp(pl.sep, pl.sep_aligned, s);
         if (e != hipSuccess) return hip_fail(e);
@@ -470,8 +478,10 @@ sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32
     sp.R = R;
     sp.row_index = row_index;
     sp.out_stats = row_stats;
+    sp.draw_in_stats = SV_DRAW_IN_STATS;  // one row per sequence, no drafts: the decision draws
     hipError_t e = sv::launch_stats(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, sv::kSample, aligned, s);
     if (e != hipSuccess) return hip_fail(e);
+    if (sp.draw_in_stats) return SV_OK;
     sv::DrawParams dp{};
     dp.target = logits;
     dp.draft = nullptr;

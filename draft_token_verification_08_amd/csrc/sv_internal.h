@@ -107,6 +107,8 @@ struct StatsParams {
     const float* dstats;      // [B][n][2] {max, sum 2^((z - max) c)} of the draft rows, from the
                               // draft's own sampling step, or nullptr (draft rows are then streamed)
     float* out_stats;         // [B][2] or nullptr: the same statistics of the row of target slot 0
+    int draw_in_stats;        // 1 (n == 0 only): the decision makes the bonus draw itself and no
+                              // draw pass runs; row 0's tile partials are then exchanged atomically
 };
 
 struct DrawParams {

@@ -492,10 +492,13 @@ __device__ __forceinline__ uint4 load_raw(const void* row, int e0, int hi) {
 // each term formed as 2^fma(z, c, -fl(m_t c)) and the rounding of fl(m_t c)
 // corrected once per tile (its exact residual is fma(m_t, c, -fl(m_t c))).
 // Tile partials (m_t, s_t) are stored into `tiles` (when not null) for the
-// bonus draw of the draw pass; the workgroup's merged (m, s) is returned in
-// thread 0.
+// bonus draw: with plain stores when the draw pass reads them (the kernel
+// boundary orders them), with atomic exchanges, completed before the function
+// returns, when `coherent` (the last workgroup of the sequence reads them in the
+// same kernel).  The workgroup's merged (m, s) is returned in thread 0.
 template <int DT, bool ALIGNED>
-__device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigned long long* tiles) {
+__device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigned long long* tiles,
+                               bool coherent = false) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     constexpr int U = kThreads / 64;  // vectors per lane per tile
@@ -503,6 +506,7 @@ __device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigne
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t0 = lo / kTile, t1 = (hi + kTile - 1) / kTile;
     float M = -FLT_MAX, S = 0.f;
+    unsigned long long dep = 0ull;
     // aligned rows: the next tile's 16-byte loads are issued before the current
     // tile is reduced (double buffer in registers); vectors past `hi` read -inf
     uint4 nxt[U];
@@ -551,13 +555,22 @@ __device__ MS wg_softmax_tiles(const void* row, int lo, int hi, float c, unsigne
             for (int e = 1; e < kVec; ++e) ls += acc[e];
             ts = wave_sum(ls) * exp2_fast(-delta);
         }
-        // read only by the draw pass (the kernel boundary orders it): a plain store
-        if (tiles != nullptr && lane == 0) tiles[t] = pack2(tmax, ts);
+        if (tiles != nullptr && lane == 0) {
+            if (coherent) dep ^= xchg64(tiles + t, pack2(tmax, ts));
+            else tiles[t] = pack2(tmax, ts);
+        }
         const MS r = ms_combine(MS{M, S}, MS{tmax, ts}, c);
         M = r.m;
         S = r.s;
     }
-    if (lane == 0) s_wave[w] = MS{M, S};
+    if (lane == 0) {
+        if (coherent) {
+            // this wave's tile exchanges have been performed before the barrier
+            asm volatile("" ::"v"((unsigned)dep), "v"((unsigned)(dep >> 32)));
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        s_wave[w] = MS{M, S};
+    }
     __syncthreads();
     MS r = s_wave[0];
     if (threadIdx.x == 0)
@@ -729,6 +742,51 @@ __device__ __forceinline__ void shift_tokens(int32_t* tokens, int b, int n) {
     for (int i = 0; i < n; ++i) t[i] = t[i + 1];
 }
 
+// Draw from the target row's own distribution (the bonus token from p_L after
+// full acceptance): pick the tile holding u * Z from the tile partials (m_t, s_t)
+// the stats pass stored for this row, weighted on the scale 2^((z - m) c) of the
+// row maximum m, with one block prefix scan; then scan only that tile.
+// ATOMIC: the partials are read, and reset to zero, with atomic exchanges (the
+// stats pass's own decision); else with plain loads (the draw pass, which
+// clears them afterwards).
+template <int DT, bool ALIGNED, bool ATOMIC>
+__device__ __forceinline__ int tile_draw(unsigned long long* tiles, int NT, int V, const DrawDesc& d,
+                                         const void* trow, double* s_w /* LDS, >= kMaxTiles */) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    double mine = 0.0;
+    int my_last = -1;
+    for (int i = tid; i < NT; i += kThreads) {
+        const unsigned long long q = ATOMIC ? xchg64(tiles + i, 0ull) : tiles[i];
+        const float ts = hi_f(q);
+        const double wi = ts > 0.f ? (double)ts * exp2(((double)lo_f(q) - (double)d.m_t) * (double)d.c) : 0.0;
+        s_w[i] = wi;
+        mine += wi;
+        if (wi > 0.0) my_last = i;
+    }
+    __shared__ double s_part[kWaves];
+    __shared__ double s_t;
+    __shared__ int s_last_tile;
+    double incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_part[w] = incl;
+    const int last_tile = block_max_all(my_last);
+    if (tid == 0) {
+        double Z = 0.0;
+        for (int k = 0; k < kWaves; ++k) Z += s_part[k];
+        s_t = (double)d.u * Z;
+        s_last_tile = last_tile < 0 ? 0 : last_tile;
+    }
+    __syncthreads();
+    const double t = s_t;
+    const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_w[i]; });
+    if (pk.i >= 0) return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, V, pk.i, pk.before, t, false);
+    return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, V, s_last_tile, 0.0, t, true);
+}
+
 // --------------------------------------------------------------- decision helpers
 
 __device__ __forceinline__ int clamp_len(int L, int n, uint32_t& flags) {
@@ -780,8 +838,9 @@ __device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
     return s;
 }
 
-// The decision of sequence b, run by the last workgroup of b to finish.
-template <int DT, int MODE, bool ALIGNED>
+// The decision of sequence b, run by the last workgroup of b to finish.  DRAW
+// (calls with no drafts): it also makes the bonus draw.
+template <int DT, int MODE, bool ALIGNED, bool DRAW = false>
 __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __shared__ float s_m[kMaxSlots];
     __shared__ double s_S[kMaxSlots];
@@ -897,6 +956,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __syncthreads();
 
     // 3. emitted tokens; sampling sequences: the draw descriptor
+    __shared__ DrawDesc s_desc;
     if (tid == 0) {
         uint32_t flags = s_flags;
         const int k = s_k;
@@ -923,17 +983,34 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
             d.pad = 0.f;
-            p.desc[b] = d;
+            if constexpr (DRAW) s_desc = d;  // drawn below, by this workgroup
+            else p.desc[b] = d;
         }
         if (flags && p.flags) atomicOr(p.flags, flags);
         xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
+    }
+    if constexpr (MODE == kSample && DRAW) {
+        // calls with no drafts (n = 0): every draw is a bonus draw from target
+        // row 0, made here from its tile partials (exchanged atomically by the
+        // row's workgroups) instead of by the draw pass, which is not launched
+        if (!si.greedy) {
+            __syncthreads();
+            const DrawDesc d = s_desc;
+            const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
+            const int y = tile_draw<DT, ALIGNED, true>(p.tiles + (size_t)b * p.NT, p.NT, V, d, trow,
+                                                       reinterpret_cast<double*>(s_part));
+            if (tid == 0) {
+                p.emitted[(size_t)b * (n + 1) + d.k] = y;
+                if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + d.k] = y;
+            }
+        }
     }
 }
 
 // --------------------------------------------------------------- stats pass
 
-template <int DT, int MODE, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
+template <int DT, int MODE, bool ALIGNED, bool DRAW>
+__device__ __forceinline__ void stats_pass(const StatsParams& p) {
     const int bid = blockIdx.x;
     const int c = bid % p.NC;
     const int rest = bid / p.NC;
@@ -980,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
         // target row L is the only row a bonus token can be drawn from: it alone
         // streams in tiles and keeps per-tile partials
         const MS r = (target_row && slot == si.L)
-                         ? wg_softmax_tiles<DT, ALIGNED>(row, lo, hi, cf, p.tiles + (size_t)b * p.NT)
+                         ? wg_softmax_tiles<DT, ALIGNED>(row, lo, hi, cf, p.tiles + (size_t)b * p.NT, DRAW)
                          : block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
         if (threadIdx.x == 0) {
             const unsigned long long dep = xchg64(slot_part + c, pack2(r.m, r.s));
@@ -988,55 +1065,25 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
         }
     }
     __syncthreads();
-    if (s_last) decide<DT, MODE, ALIGNED>(p, b, si);
+    if (s_last) decide<DT, MODE, ALIGNED, DRAW>(p, b, si);
     // fused MTP step: every workgroup of the grid carries an equal share of the
     // hidden states once its row chunk is done (the copy's writes then come as
     // one burst at the end of the read stream instead of interleaved with it)
     copy_share(p.mtp, bid, gridDim.x);
 }
 
-// Draw from the target row's own distribution (the bonus token from p_L after
-// full acceptance): pick the tile holding u * Z from the tile partials (m_t, s_t)
-// the stats pass stored for this row, weighted on the scale 2^((z - m) c) of the
-// row maximum m, with one block prefix scan; then scan only that tile.
-template <int DT, bool ALIGNED>
-__device__ __forceinline__ int tile_draw(const DrawParams& p, int b, const DrawDesc& d, const void* trow,
-                                         double* s_w /* LDS, >= kMaxTiles */) {
-    const unsigned long long* tiles = p.tiles + (size_t)b * p.NT;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    double mine = 0.0;
-    int my_last = -1;
-    for (int i = tid; i < p.NT; i += kThreads) {
-        const unsigned long long q = tiles[i];
-        const float ts = hi_f(q);
-        const double wi = ts > 0.f ? (double)ts * exp2(((double)lo_f(q) - (double)d.m_t) * (double)d.c) : 0.0;
-        s_w[i] = wi;
-        mine += wi;
-        if (wi > 0.0) my_last = i;
-    }
-    __shared__ double s_part[kWaves];
-    __shared__ double s_t;
-    __shared__ int s_last_tile;
-    double incl = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) s_part[w] = incl;
-    const int last_tile = block_max_all(my_last);
-    if (tid == 0) {
-        double Z = 0.0;
-        for (int k = 0; k < kWaves; ++k) Z += s_part[k];
-        s_t = (double)d.u * Z;
-        s_last_tile = last_tile < 0 ? 0 : last_tile;
-    }
-    __syncthreads();
-    const double t = s_t;
-    const Pick pk = block_first_crossing(p.NT, t, [&](int i) { return s_w[i]; });
-    if (pk.i >= 0) return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, p.V, pk.i, pk.before, t, false);
-    return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, p.V, s_last_tile, 0.0, t, true);
+// The statistics pass (one workgroup per (sequence, row slot, vocab chunk)).
+template <int DT, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
+    stats_pass<DT, MODE, ALIGNED, false>(p);
 }
+// Sampling calls with no drafts: the statistics pass whose decision also makes
+// the (bonus) draw, so no draw pass follows.
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
+    stats_pass<DT, kSample, ALIGNED, true>(p);
+}
+
 
 // --------------------------------------------------------------- draw pass
 // Bonus draws (all drafts accepted): workgroup (b, 0) alone, with tile_draw().
@@ -1056,7 +1103,7 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
     if (d.kind == kDrawBonus) {
         if (c != 0) return;
-        const int y = tile_draw<DT, ALIGNED>(p, b, d, trow, s_buf);
+        const int y = tile_draw<DT, ALIGNED, false>(p.tiles + (size_t)b * NT, NT, V, d, trow, s_buf);
         for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;  // used: leave zero
         if (tid == 0) {
             p.emitted[(size_t)b * (n + 1) + d.k] = y;
@@ -1299,6 +1346,16 @@ hipError_t launch_decide_greedy(const StatsParams& p, hipStream_t s) {
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s) {
     const unsigned blocks = (unsigned)((long long)p.B * p.S * p.NC);
     const dim3 grid(blocks), block(kThreads);
+    if (mode == kSample && p.draw_in_stats) {
+        if (dt == kBF16) {
+            if (aligned) hipLaunchKernelGGL((k_stats_draw<kBF16, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((k_stats_draw<kBF16, false>), grid, block, 0, s, p);
+        } else {
+            if (aligned) hipLaunchKernelGGL((k_stats_draw<kF32, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((k_stats_draw<kF32, false>), grid, block, 0, s, p);
+        }
+        return hipGetLastError();
+    }
 #define SV_STATS(DT_, MODE_, AL_) hipLaunchKernelGGL((k_stats<DT_, MODE_, AL_>), grid, block, 0, s, p)
     if (dt == kBF16) {
         if (mode == kSample) { if (aligned) SV_STATS(kBF16, kSample, true); else SV_STATS(kBF16, kSample, false); }

@@ -247,6 +247,8 @@ sv_status_t spec_verify_sample_ex(const void *target_logits, const void *draft_l
  * paragraph; Single-token MTP scheduling section, second paragraph: pass the
  * [B][n+1][V] draft/MTP logits, R = n + 1 and row_index = accepted_len), and the
  * draft's own per-step sampling (R = 1, row_index = NULL).  No host sync.
+ * One kernel launch: the statistics pass's per-sequence decision also makes
+ * the draw (as do the spec_verify_sample calls with n = 0).
  *
  *   logits     [B][R][V] dt      row_index [B] int32, nullable
  *   temperature [B] float        uniforms [B] float in [0,1)
