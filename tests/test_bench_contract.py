@@ -58,3 +58,30 @@ def test_traffic_used_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch)
     assert bench.measured_traffic("k", "other", str(src)) is None
     src.write_text("// kernel v2\n")  # the kernel changed after the counters were taken
     assert bench.measured_traffic("k", "w", str(src)) is None
+
+
+def test_parity_report_counts_planted_differences():
+    """The bench's decision-by-decision comparison: equal outputs give no
+    mismatch; a changed draw or accepted length is a hard mismatch (no near-tie
+    in these inputs), with no exemption for greedy decisions."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    d = synth.make(5, 3, device="cpu", B=40, V=3000)
+    h = synth.host_logits
+    L, T, n = d["draft_lens"].numpy(), d["temperature"].numpy(), d["n"]
+    o = orc.verify_sample(h(d["target"]), h(d["draft"]), d["draft_tokens"].numpy(), L, T, d["uniforms"].numpy())
+    r = bench.parity_report(o["accepted_len"], o["emitted"], o, L, T, n)
+    assert r["hard_mismatches"] == 0 and r["exempt"] == 0 and r["sequences"] == 40
+    assert r["decisions"] >= 40
+    acc, emi = o["accepted_len"].copy(), o["emitted"].copy()
+    b = int(np.nonzero(T > 0)[0][0])
+    emi[b, acc[b]] = (emi[b, acc[b]] + 1) % 3000
+    assert bench.parity_report(acc, emi, o, L, T, n)["hard_mismatches"] == 1
+    g = orc.verify_greedy(h(d["target"]), d["draft_tokens"].numpy(), L)
+    acc2 = g["accepted_len"].copy()
+    acc2[0] = (acc2[0] + 1) % (n + 1)
+    assert bench.parity_report(acc2, g["emitted"], g, L, None, n)["hard_mismatches"] == 1
