@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "libspecverify_oracle.so")
 F32, BF16, F64 = 0, 1, 2
 FLAG_LEN_CLAMPED, FLAG_TOKEN_OOR, FLAG_BAD_TEMP, FLAG_BAD_UNIFORM, FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
 FLAG_ROW_CLAMPED = 32
+FLAG_BAD_PARENT = 64
 
 
 def build(out_path: str = LIB, plant: int = 0, sanitize: bool = False) -> str:
@@ -66,6 +67,9 @@ class Oracle:
         L.sv_oracle_sample_rows.restype = C.c_int
         L.sv_oracle_lmhead_logits.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, i32p, C.c_int, f64p, C.c_int]
         L.sv_oracle_lmhead_logits.restype = C.c_int
+        L.sv_oracle_verify_tree_greedy.argtypes = [vp, C.c_int, i32p, i32p, i32p, C.c_int, C.c_int, C.c_int,
+                                                   i32p, i32p, i32p, u32p]
+        L.sv_oracle_verify_tree_greedy.restype = C.c_int
         L.sv_oracle_plant.argtypes = []
         L.sv_oracle_plant.restype = C.c_int
 
@@ -132,6 +136,24 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"sv_oracle_verify_greedy failed: {rc}")
         return dict(accepted_len=acc, emitted=emi, seq_flags=fl)
+
+    def verify_tree_greedy(self, target, draft_tokens, draft_parents, draft_lens):
+        """Greedy tree verification (see sv_oracle_verify_tree_greedy)."""
+        target, dt = self._logits(target)
+        B, n1, V = target.shape
+        n = n1 - 1
+        x = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, n)
+        par = np.ascontiguousarray(draft_parents, dtype=np.int32).reshape(B, n)
+        L = np.ascontiguousarray(draft_lens, dtype=np.int32).reshape(B)
+        acc = np.empty(B, np.int32)
+        emi = np.empty((B, n + 1), np.int32)
+        path = np.empty((B, max(n, 1)), np.int32)[:, :n].copy()
+        fl = np.empty(B, np.uint32)
+        rc = self.lib.sv_oracle_verify_tree_greedy(self._p(target), dt, self._p(x), self._p(par), self._p(L), B, n,
+                                                   V, self._p(acc), self._p(emi), self._p(path), self._p(fl))
+        if rc != 0:
+            raise RuntimeError(f"sv_oracle_verify_tree_greedy failed: {rc}")
+        return dict(accepted_len=acc, emitted=emi, path=path, seq_flags=fl)
 
     def mtp_shift_insert(self, tokens, hidden_src, accepted_len, emitted, copy_hidden=True):
         """Returns (new_tokens, hidden_dst); inputs are not modified."""

@@ -67,6 +67,7 @@
 #define OR_FLAG_BAD_TEMP 4u
 #define OR_FLAG_BAD_UNIFORM 8u
 #define OR_FLAG_ZERO_RESIDUAL 16u
+#define OR_FLAG_BAD_PARENT 64u
 
 #define OR_MODE_SAMPLE 0
 #define OR_MODE_GREEDY 1
@@ -456,6 +457,98 @@ int sv_oracle_sample_rows(const void *logits, int dt, int R, const int32_t *row_
     free(zeros);
     free(acc);
     return rc;
+}
+
+/* ------------------------------------------------- tree verification (greedy)
+ *
+ * EAGLE section of "Accelerating Sonar through speculation": the draft explores
+ * a tree of candidate tokens, the target scores the candidate sequences, the
+ * longest suitable one is kept and one more token from the target is appended.
+ * Greedy reading, written out:
+ *   - node 0 is the root (the last committed token); node j + 1 (j < L_b) holds
+ *     draft token x_j and hangs below node parents[b][j], which must lie in
+ *     [0, j] (nodes in topological order); a node with another parent is left
+ *     out of the tree (flag OR_FLAG_BAD_PARENT);
+ *   - target row r holds the logits after node r; g_r = its argmax (lowest index
+ *     on ties);
+ *   - node i is accepted iff its parent p is accepted (the root is) and
+ *     x_{i-1} == g_p;
+ *   - the kept path runs from the root to the deepest accepted node (the lowest
+ *     index among equally deep ones); its draft tokens are emitted in order, then
+ *     g of its last node, then -1;
+ *   - path[b][0..]: the kept path's node indices (root excluded), then -1.
+ * With parents[b][j] = j (a chain) this is the linear greedy rule. */
+static void tree_one(const void *target, int dt, const int32_t *tokens, const int32_t *parents,
+                     int L, int n, int V, size_t trow0, int32_t *acc, int32_t *emitted, int32_t *path,
+                     uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (L < 0) { L = 0; flags |= OR_FLAG_LEN_CLAMPED; }
+    if (L > n) { L = n; flags |= OR_FLAG_LEN_CLAMPED; }
+    int parent[129], depth[129], accepted[129];
+    accepted[0] = 1;
+    depth[0] = 0;
+    int best = 0;
+    for (int i = 1; i <= L; ++i) {
+        const int p = parents[i - 1];
+        const int x = tokens[i - 1];
+        if (x < 0 || x >= V) flags |= OR_FLAG_TOKEN_OOR;
+        parent[i] = p;
+        accepted[i] = 0;
+        depth[i] = 0;
+        if (p < 0 || p >= i) {
+            flags |= OR_FLAG_BAD_PARENT;
+            continue;
+        }
+#if SV_ORACLE_PLANT == 6 /* negative control: the node's own row instead of its parent's */
+        const int gp = row_argmax(target, dt, trow0 + (size_t)i * V, V);
+#else
+        const int gp = row_argmax(target, dt, trow0 + (size_t)p * V, V);
+#endif
+#if SV_ORACLE_PLANT == 7 /* negative control: the parent's acceptance is not required */
+        if (x == gp) {
+#else
+        if (accepted[p] && x == gp) {
+#endif
+            accepted[i] = 1;
+            depth[i] = depth[p] + 1;
+            if (depth[i] > depth[best]) best = i;
+        }
+    }
+    const int k = depth[best];
+    /* the kept path, root excluded, from the root down */
+    int node = best;
+    for (int d = k - 1; d >= 0; --d) {
+        path[d] = node;
+        emitted[d] = tokens[node - 1];
+        node = parent[node];
+    }
+    emitted[k] = row_argmax(target, dt, trow0 + (size_t)best * V, V);
+    for (int d = k + 1; d <= n; ++d) emitted[d] = -1;
+    for (int d = k; d < n; ++d) path[d] = -1;
+    *acc = k;
+    *flags_out = flags;
+}
+
+/* Greedy tree verification for every sequence; target logits [B][n+1][V],
+ * draft_tokens and draft_parents [B][n], draft_lens [B]; outputs accepted_len
+ * [B], emitted [B][n+1], path [B][n] (nullable), seq_flags [B] (nullable).
+ * Returns 0, or -1 on bad sizes. */
+int sv_oracle_verify_tree_greedy(const void *target_logits, int dt, const int32_t *draft_tokens,
+                                 const int32_t *draft_parents, const int32_t *draft_lens, int B, int n,
+                                 int V, int32_t *accepted_len, int32_t *emitted, int32_t *path,
+                                 uint32_t *seq_flags)
+{
+    if (check_dims(B, n, V)) return -1;
+    int32_t scratch_path[128];
+    for (int b = 0; b < B; ++b) {
+        uint32_t f = 0;
+        tree_one(target_logits, dt, draft_tokens + (size_t)b * n, draft_parents + (size_t)b * n,
+                 draft_lens[b], n, V, (size_t)b * (size_t)(n + 1) * (size_t)V, &accepted_len[b],
+                 emitted + (size_t)b * (n + 1), path ? path + (size_t)b * n : scratch_path, &f);
+        if (seq_flags) seq_flags[b] = f;
+    }
+    return 0;
 }
 
 /* ------------------------------------------------------- logit projection */
