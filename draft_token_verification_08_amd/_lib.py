@@ -20,6 +20,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_OK, SV_EINVAL, SV_EALIGN, SV_EWORKSPACE, SV_EHIP = 0, 1, 2, 3, 4
 SV_FLAG_LEN_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_BAD_TEMP, SV_FLAG_BAD_UNIFORM, SV_FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
 SV_FLAG_ROW_CLAMPED = 32
+SV_FLAG_BAD_PARENT = 64
 SV_MAX_DRAFT = 64
 
 _lib = None
@@ -56,6 +57,8 @@ def lib():
     L.spec_verify_sample.restype = i
     L.spec_verify_greedy.argtypes = [vp, i, vp, vp, i, i, i, vp, vp, vp, vp, sz, vp]
     L.spec_verify_greedy.restype = i
+    L.spec_verify_tree_greedy.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_tree_greedy.restype = i
     L.spec_verify_sample_mtp.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, vp,
                                          sz, vp]
     L.spec_verify_sample_mtp.restype = i
@@ -189,6 +192,40 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, draft_lens, te
           _ptr(draft_lens), _ptr(temperature), _ptr(uniforms), B, n, V, _ptr(accepted_len), _ptr(emitted),
           _ptr(row_lse), _ptr(err_flags), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     return accepted_len, emitted
+
+
+def spec_verify_tree_greedy(target_logits, draft_tokens, draft_parents, draft_lens, *, accepted_len=None,
+                            emitted=None, path=None, err_flags=None, workspace=None, stream=None):
+    """Greedy tree verification (see include/specverify.h): node j + 1 holds
+    draft_tokens[b][j] below node draft_parents[b][j].  Returns (accepted_len,
+    emitted, path)."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_parents, "draft_parents", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, n), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n + 1), dev)
+    _check(path, "path", torch.int32, (B, n), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    need = sv_workspace_bytes(B, n, V, dt)
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    _check(workspace, "workspace", torch.uint8)
+    _call("spec_verify_tree_greedy", _ptr(target_logits), dt, _ptr(draft_tokens), _ptr(draft_parents),
+          _ptr(draft_lens), B, n, V, _ptr(accepted_len), _ptr(emitted), _ptr(path), _ptr(err_flags),
+          _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted, path
 
 
 def spec_verify_greedy(target_logits, draft_tokens, draft_lens, *, accepted_len=None, emitted=None,

@@ -427,6 +427,46 @@ sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const i
                          workspace, workspace_bytes, stream, nullptr);
 }
 
+sv_status_t spec_verify_tree_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                                    const int32_t* draft_parents, const int32_t* draft_lens, int B, int n, int V,
+                                    int32_t* accepted_len, int32_t* emitted, int32_t* path, uint32_t* err_flags,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_lens || !accepted_len || !emitted || (n > 0 && (!draft_tokens || !draft_parents)))
+        return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(target_logits, es) || !aligned_to(draft_tokens, 4) || !aligned_to(draft_parents, 4) ||
+        !aligned_to(draft_lens, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) ||
+        !aligned_to(path, 4) || !aligned_to(err_flags, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, n, V, dt, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    const int S = n + 1;
+    if (!grid_ok((long long)B * S * L.NC)) return SV_EINVAL;
+    sv::StatsParams sp{};
+    sp.target = target_logits;
+    sp.draft = nullptr;
+    sp.tokens = draft_tokens;
+    sp.lens = draft_lens;
+    sp.B = B; sp.n = n; sp.V = V; sp.NC = L.NC; sp.CH = L.CH; sp.S = S;
+    sp.acc = accepted_len;
+    sp.emitted = emitted;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.R = n + 1;
+    sp.row_index = nullptr;
+    sp.parents = draft_parents;
+    sp.path = path;
+    const hipError_t e = sv::launch_tree(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32,
+                                         rows_aligned(target_logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
 sv_status_t spec_verify_greedy_mtp(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,
                                    const int32_t* draft_lens, int B, int n, int V, int32_t* accepted_len,
                                    int32_t* emitted, uint32_t* err_flags, int32_t* tokens,

@@ -109,6 +109,8 @@ struct StatsParams {
     float* out_stats;         // [B][2] or nullptr: the same statistics of the row of target slot 0
     int draw_in_stats;        // 1 (n == 0 only): the decision makes the bonus draw itself and no
                               // draw pass runs; row 0's tile partials are then exchanged atomically
+    const int32_t* parents;   // [B][n] tree verification: node j + 1 hangs below node parents[j]
+    int32_t* path;            // [B][n] or nullptr: the kept path's node indices (tree verification)
 };
 
 struct DrawParams {
@@ -156,6 +158,7 @@ constexpr int kLmBK = 64;      // K elements per pipeline stage of the projectio
 
 // launches (sv_kernels.hip, sv_lmhead.hip); return the hipGetLastError() after the launch
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s);
+hipError_t launch_tree(const StatsParams& p, Dt dt, bool aligned, hipStream_t s);
 hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s);
 hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);

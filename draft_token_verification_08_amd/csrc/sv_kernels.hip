@@ -838,9 +838,68 @@ __device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
     return s;
 }
 
+// Greedy tree verification of sequence b ("Accelerating Sonar through
+// speculation", EAGLE section: the target scores the candidate sequences of the
+// draft tree, the longest suitable one is kept and one more target token is
+// appended).  Node 0 is the root; node j + 1 (j < L) holds draft token x_j
+// below node parents[j] in [0, j] (other parents leave the node out, flagged).
+// Node i is accepted iff its parent is and x_{i-1} is the target's argmax g at
+// the parent (g[r] = argmax of target row r, lowest index on ties).  The kept
+// path ends at the deepest accepted node, the lowest-numbered among equally deep
+// ones; its tokens are emitted, then g of its last node, then -1.  The node
+// tokens and parents are staged in LDS by all threads; one thread walks them.
+__device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const SeqInfo& si, const int* s_idx) {
+    __shared__ int s_x[kMaxDraft], s_par[kMaxDraft];
+    __shared__ int s_depth[kMaxDraft + 1], s_ok[kMaxDraft + 1];
+    const int tid = threadIdx.x, n = p.n, V = p.V, L = si.L;
+    if (tid < L) {
+        s_x[tid] = p.tokens[(size_t)b * n + tid];
+        s_par[tid] = p.parents[(size_t)b * n + tid];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t flags = si.flags;
+        s_depth[0] = 0;
+        s_ok[0] = 1;
+        int best = 0;
+        for (int i = 1; i <= L; ++i) {
+            const int pi = s_par[i - 1], xi = s_x[i - 1];
+            if (xi < 0 || xi >= V) flags |= SV_FLAG_TOKEN_OOR;
+            s_ok[i] = 0;
+            s_depth[i] = 0;
+            if (pi < 0 || pi >= i) {
+                flags |= SV_FLAG_BAD_PARENT;
+                continue;
+            }
+            if (s_ok[pi] && xi == s_idx[pi]) {
+                s_ok[i] = 1;
+                s_depth[i] = s_depth[pi] + 1;
+                if (s_depth[i] > s_depth[best]) best = i;
+            }
+        }
+        const int k = s_depth[best];
+        int32_t* e = p.emitted + (size_t)b * (n + 1);
+        int32_t* path = p.path ? p.path + (size_t)b * n : nullptr;
+        int node = best;
+        for (int d = k - 1; d >= 0; --d) {
+            if (path) path[d] = node;
+            e[d] = s_x[node - 1];
+            node = s_par[node - 1];
+        }
+        e[k] = s_idx[best];
+        for (int d = k + 1; d <= n; ++d) e[d] = -1;
+        if (path)
+            for (int d = k; d < n; ++d) path[d] = -1;
+        p.acc[b] = k;
+        if (flags && p.flags) atomicOr(p.flags, flags);
+        xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
+    }
+}
+
 // The decision of sequence b, run by the last workgroup of b to finish.  DRAW
-// (calls with no drafts): it also makes the bonus draw.
-template <int DT, int MODE, bool ALIGNED, bool DRAW = false>
+// (calls with no drafts): it also makes the bonus draw.  TREE (greedy): the
+// drafts form a tree, and the kept path is found by tree_walk.
+template <int DT, int MODE, bool ALIGNED, bool DRAW = false, bool TREE = false>
 __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __shared__ float s_m[kMaxSlots];
     __shared__ double s_S[kMaxSlots];
@@ -891,6 +950,10 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
         }
     }
     __syncthreads();
+    if constexpr (TREE) {
+        tree_walk(p, b, si, s_idx);
+        return;
+    }
     if constexpr (MODE == kSample) {
         if (p.row_lse && tid < 2 * n + 1) {
             const bool row_read = !si.greedy && ((tid <= L) || (tid > n && tid - n - 1 < L));
@@ -1011,7 +1074,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
 
 // The parameters are taken by value: taken by reference, the inlined sampling
 // pass compiled to different code that measured 13% slower at B=256, n=4.
-template <int DT, int MODE, bool ALIGNED, bool DRAW>
+template <int DT, int MODE, bool ALIGNED, bool DRAW, bool TREE = false>
 __device__ __forceinline__ void stats_pass(StatsParams p) {
     const int bid = blockIdx.x;
     const int c = bid % p.NC;
@@ -1067,7 +1130,7 @@ __device__ __forceinline__ void stats_pass(StatsParams p) {
         }
     }
     __syncthreads();
-    if (s_last) decide<DT, MODE, ALIGNED, DRAW>(p, b, si);
+    if (s_last) decide<DT, MODE, ALIGNED, DRAW, TREE>(p, b, si);
     // fused MTP step: every workgroup of the grid carries an equal share of the
     // hidden states once its row chunk is done (the copy's writes then come as
     // one burst at the end of the read stream instead of interleaved with it)
@@ -1078,6 +1141,12 @@ __device__ __forceinline__ void stats_pass(StatsParams p) {
 template <int DT, int MODE, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     stats_pass<DT, MODE, ALIGNED, false>(p);
+}
+// Greedy tree verification: the greedy statistics pass over the tree's node
+// rows, then the tree walk.
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_stats_tree(StatsParams p) {
+    stats_pass<DT, kGreedy, ALIGNED, false, true>(p);
 }
 // Sampling calls with no drafts: the statistics pass whose decision also makes
 // the (bonus) draw, so no draw pass follows.
@@ -1367,6 +1436,19 @@ hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hi
         else { if (aligned) SV_STATS(kF32, kGreedy, true); else SV_STATS(kF32, kGreedy, false); }
     }
 #undef SV_STATS
+    return hipGetLastError();
+}
+
+hipError_t launch_tree(const StatsParams& p, Dt dt, bool aligned, hipStream_t s) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.S * p.NC);
+    const dim3 grid(blocks), block(kThreads);
+    if (dt == kBF16) {
+        if (aligned) hipLaunchKernelGGL((k_stats_tree<kBF16, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_stats_tree<kBF16, false>), grid, block, 0, s, p);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_stats_tree<kF32, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_stats_tree<kF32, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

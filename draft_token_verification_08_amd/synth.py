@@ -188,6 +188,75 @@ def make(cid: int, seed: int, device="cpu", B: int | None = None, V: int | None 
     return out
 
 
+def tree_parents(n: int, widths=(3, 2, 1)) -> list:
+    """Parents of nodes 1..n of a top-k style draft tree, built level by level:
+    a node at depth d gets up to widths[d] children (1 beyond the listed depths),
+    so the tree is bushy near the root and thins to chains.  Entry j is the
+    parent of node j + 1."""
+    par, depth, q = [], [0], [0]
+    while len(par) < n and q:
+        nxt = []
+        for node in q:
+            w = widths[depth[node]] if depth[node] < len(widths) else 1
+            for _ in range(w):
+                if len(par) == n:
+                    break
+                par.append(node)
+                depth.append(depth[node] + 1)
+                nxt.append(len(par))
+        q = nxt
+    return par
+
+
+def make_tree(seed: int, device="cpu", B: int = 64, n: int = 25, V: int = 128256, shape: str = "topk",
+              dtype=torch.bfloat16, ragged: bool = False) -> dict:
+    """Inputs of greedy tree verification: target logits [B, n+1, V] (row r = the
+    target's logits after node r) drawn like the greedy logits recipe (N(0, 3^2)
+    with every row's top token planted at a random index, in 1/8 of rows also a
+    tied twin), draft_parents [B, n] (shape "topk": tree_parents(n) for every
+    sequence; "random": node j + 1 below a uniform node in [0, j]), draft_tokens
+    [B, n]: among each node's children one, chosen at random, carries the node's
+    planted top (or its twin) with probability 0.8; the others carry other
+    tokens.  draft_lens [B]: n, or uniform in 0..n when ragged."""
+    import numpy as np
+
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    rows = B * (n + 1)
+    zt = 3.0 * torch.randn((rows, V), generator=g, device=dev, dtype=torch.float32)
+    a_top = torch.randint(0, V, (rows,), generator=g, device=dev)
+    a_tie = (a_top + 1 + torch.randint(0, max(V - 1, 1), (rows,), generator=g, device=dev)) % V
+    tie = torch.rand((rows,), generator=g, device=dev) < 0.125
+    level = 20.0 + 4.0 * torch.rand((rows,), generator=g, device=dev)
+    r = torch.arange(rows, device=dev)
+    zt[r, a_top] = level
+    zt[r[tie], a_tie[tie]] = level[tie]
+    target = zt.view(B, n + 1, V).to(dtype)
+    top = a_top.view(B, n + 1).cpu().numpy()
+    twin = a_tie.view(B, n + 1).cpu().numpy()
+    has_twin = tie.view(B, n + 1).cpu().numpy()
+    rng = np.random.default_rng(seed)
+    if shape == "topk":
+        par = np.tile(np.array(tree_parents(n), dtype=np.int32), (B, 1)) if n > 0 else np.zeros((B, 0), np.int32)
+    else:
+        par = np.array([[rng.integers(0, j + 1) for j in range(n)] for _ in range(B)], dtype=np.int32).reshape(B, n)
+    tok = np.empty((B, n), dtype=np.int64)
+    for b in range(B):
+        for p in np.unique(par[b]):
+            kids = np.nonzero(par[b] == p)[0]
+            hit = kids[rng.integers(0, len(kids))] if rng.random() < 0.8 else -1
+            for j in kids:
+                if j == hit:
+                    tok[b, j] = twin[b, p] if has_twin[b, p] and rng.random() < 0.5 else top[b, p]
+                else:
+                    o = int(rng.integers(0, max(V - 1, 1)))
+                    tok[b, j] = (o + 1) % V if o >= top[b, p] else o
+    lens = rng.integers(0, n + 1, B) if ragged else np.full(B, n)
+    return dict(target=target, draft_parents=torch.as_tensor(par, dtype=torch.int32, device=dev),
+                draft_tokens=torch.as_tensor(tok, dtype=torch.int32, device=dev),
+                draft_lens=torch.as_tensor(lens, dtype=torch.int32, device=dev), B=B, n=n, V=V)
+
+
 def make_lmhead(seed: int, device="cpu", B: int = 256, n: int = 4, V: int = 128256, H: int = 8192,
                 exact: bool = True, ragged: bool = False) -> dict:
     """Inputs of the fused logit projection + greedy verify: the target's final

@@ -74,7 +74,8 @@ enum {
     SV_FLAG_BAD_TEMP = 4,
     SV_FLAG_BAD_UNIFORM = 8,
     SV_FLAG_ZERO_RESIDUAL = 16,
-    SV_FLAG_ROW_CLAMPED = 32
+    SV_FLAG_ROW_CLAMPED = 32,
+    SV_FLAG_BAD_PARENT = 64
 };
 
 /* Bytes of device workspace spec_verify_sample() and spec_verify_greedy() need
@@ -146,6 +147,35 @@ sv_status_t spec_verify_greedy(const void *target_logits, sv_dtype_t dt,
                                int n, int V, int32_t *accepted_len, int32_t *emitted,
                                uint32_t *err_flags, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* Greedy tree verification.  "Accelerating Sonar through speculation", EAGLE
+ * section: the draft explores a tree of candidate tokens, the target scores the
+ * candidate sequences, the longest suitable one is kept and one more token from
+ * the target is appended.  The greedy reading of "suitable":
+ *   - node 0 is the root (the last committed token); node j + 1 (j < L_b) holds
+ *     draft_tokens[b][j] and hangs below node draft_parents[b][j], which must lie
+ *     in [0, j] (nodes in topological order; any other parent leaves the node
+ *     out and sets SV_FLAG_BAD_PARENT);
+ *   - target row r (of [B][n+1][V]) holds the target's logits after node r, as
+ *     the target's tree-masked forward produces them; g_r = its argmax (lowest
+ *     index on ties);
+ *   - node i is accepted iff its parent p is accepted (the root is) and its
+ *     token equals g_p;
+ *   - the kept path runs from the root to the deepest accepted node (the
+ *     lowest-numbered among equally deep ones).
+ * Outputs: accepted_len[b] = the kept path's length; emitted[b] = its draft
+ * tokens in order, then g of its last node, then -1; path[b] (nullable) = its
+ * node indices (root excluded), then -1.  With draft_parents[b][j] = j (a chain)
+ * the result is spec_verify_greedy's.  Tokens outside [0, V) are never accepted
+ * (SV_FLAG_TOKEN_OOR).  Rows r > L_b are not used.  Sizes, workspace and
+ * errors as in spec_verify_greedy().
+ *   draft_tokens, draft_parents [B][n] int32     draft_lens [B] int32
+ *   accepted_len [B] int32 out   emitted [B][n+1] int32 out   path [B][n] int32 out, nullable */
+sv_status_t spec_verify_tree_greedy(const void *target_logits, sv_dtype_t dt, const int32_t *draft_tokens,
+                                    const int32_t *draft_parents, const int32_t *draft_lens, int B, int n,
+                                    int V, int32_t *accepted_len, int32_t *emitted, int32_t *path,
+                                    uint32_t *err_flags, void *workspace, size_t workspace_bytes,
+                                    void *stream);
 
 /* MTP bookkeeping on the device, with no host synchronisation.
  *

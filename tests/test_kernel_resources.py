@@ -18,6 +18,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # mangled kernel name -> minimum waves per SIMD
 BUDGET = {
     "_ZN2sv7k_statsILi1ELi1ELb1EEEvNS_11StatsParamsE": 8,   # greedy, bf16, aligned
+    "_ZN2sv12k_stats_treeILi1ELb1EEEvNS_11StatsParamsE": 8,  # greedy tree verification, bf16, aligned
     "_ZN2sv7k_statsILi1ELi0ELb1EEEvNS_11StatsParamsE": 7,   # sampling, bf16, aligned
     # sampling with no drafts (the draw inside), bf16: no-draft launches run about
     # 1024 workgroups, which 6 waves per SIMD keep resident
