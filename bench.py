@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--draft-step", action="store_true",
                     help="the draft loop's per-step sampling (sv_sample_rows with row statistics): one token per "
                          "sequence from logits [256, 128256] bf16 at T=0.7")
+    ap.add_argument("--tree", action="store_true",
+                    help="greedy tree verification (spec_verify_tree_greedy): 64 sequences with a 26-node top-k "
+                         "draft tree over V=128256 bf16 logits")
     ap.add_argument("--lmhead", action="store_true",
                     help="greedy verify fused with the target's logit projection (spec_verify_greedy_lmhead): "
                          "hidden states [256, 5, 8192] and a [128256, 8192] projection instead of logits")
@@ -104,6 +107,9 @@ def main():
         return
     if args.draft_step:
         bench_draft_step(args, dev)
+        return
+    if args.tree:
+        bench_tree(args, dev)
         return
     cfg = synth.CONFIGS[args.config]
     greedy = cfg.mode == "greedy"
@@ -633,6 +639,119 @@ def bench_draft_step(args, dev):
         out["cpu_baseline"] = cpu_baseline_draft_step(data[0], B, V)
         out["oracle_parity"] = out["cpu_baseline"].pop("oracle_parity")
     print(json.dumps(out), flush=True)
+
+
+def bench_tree(args, dev):
+    """Greedy tree verification: every sequence's target rows (one per tree node)
+    reduced to argmax keys, then the tree walk.  64 sequences, each a 26-node
+    top-k tree (3 children at the root, 2 below each of those, then chains) over
+    V=128256 bf16 rows of the greedy logits recipe, resident in HBM and rotated
+    over input copies."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_08_amd as sv
+    from draft_token_verification_08_amd import synth
+
+    B, n, V = 64, 25, 128256
+    sets = args.sets or 4
+    wsbuf = sv.Workspace(dev).get(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16))
+    stream = torch.cuda.current_stream(dev)
+    data = []
+    for i in range(sets):
+        d = synth.make_tree(args.seed + i, device=dev, B=B, n=n, V=V)
+        d["acc"] = torch.empty(B, dtype=torch.int32, device=dev)
+        d["emi"] = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+        d["path"] = torch.empty((B, n), dtype=torch.int32, device=dev)
+        data.append(d)
+    torch.cuda.synchronize()
+
+    for d in data:
+        d["call"] = sv.prepare_spec_verify_tree_greedy(d["target"], d["draft_tokens"], d["draft_parents"],
+                                                       d["draft_lens"], d["acc"], d["emi"], d["path"], wsbuf)
+
+    def call(d):
+        d["call"]()
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        call(data[i % sets])
+    torch.cuda.synchronize()
+    brackets = []
+    t0 = time.perf_counter()
+    i = 0
+    while i < K:
+        if i % 16 == 0 and i + 8 <= K:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for j in range(8):
+                call(data[(i + j) % sets])
+            b.record(stream)
+            brackets.append((a, b))
+            i += 8
+        else:
+            call(data[i % sets])
+            i += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_ms = statistics.fmean(a.elapsed_time(b) for a, b in brackets) / 8 if brackets else elapsed * 1e3 / K
+    rows = B * (n + 1)
+    nbytes = rows * V * 2 + B * n * 8 + B * 4 + B * (n + 1) * 4 + B * n * 4 + B * 4
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "verified vocab rows/s + HBM GB/s (% of peak), V=128256 bf16, B=64 (greedy tree of 26 nodes)",
+        "value": round(rows * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {sets} copies)",
+        "config": {"workload": "greedy tree verification, 64 sequences x 26-node top-k tree, V=128256 bf16 "
+                               "(greedy_tree_verify)", "B": B, "nodes": n + 1, "V": V, "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(nbytes * K / elapsed / 1e9, 1),
+        "pct_of_peak": round(nbytes * K / elapsed / 1e9 / PEAK_GBPS * 100, 2),
+        "mean_accepted": round(float(data[0]["acc"].float().mean()), 4),
+        "roofline": {"bound": "hbm", "kernel": "k_stats_tree", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(avg_ms * 1e3, 2), "timed_launches": 8 * len(brackets),
+                     "timing": "HIP event pair around 8 consecutive calls, every 16 steps",
+                     "traffic": measured_traffic("k_stats_tree", "greedy_tree_verify")},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_tree(data[0], B, n, V)
+        out["oracle_parity"] = out["cpu_baseline"].pop("oracle_parity")
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_tree(d, B, n, V):
+    """The oracle (untuned, one thread) on whole steps of the same workload for
+    about 10-20 s of CPU work; then the GPU's outputs for this input copy against
+    the oracle's, exactly (greedy decisions have no near-tie exemption)."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    z = synth.host_logits(d["target"])
+    x, par, L = d["draft_tokens"].cpu().numpy(), d["draft_parents"].cpu().numpy(), d["draft_lens"].cpu().numpy()
+    calls, t0 = 0, time.perf_counter()
+    while calls < 1 or (time.perf_counter() - t0 < 15.0 and calls < 100):
+        o = orc.verify_tree_greedy(z, x, par, L)
+        calls += 1
+    el = time.perf_counter() - t0
+    acc, emi, path = d["acc"].cpu().numpy(), d["emi"].cpu().numpy(), d["path"].cpu().numpy()
+    bad = int(((acc != o["accepted_len"]) | (emi != o["emitted"]).any(1) | (path != o["path"]).any(1)).sum())
+    return {"value": round(calls * B * (n + 1) / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full steps ({B} sequences, {B * (n + 1)} rows of V={V}) on 1 thread, about "
+                      f"{el:.0f} s of CPU work", "cpu_model": cpu_model(),
+            "oracle_parity": {"sequences": B, "decisions": int(B + acc.sum()), "exempt": 0, "hard_mismatches": bad,
+                              "inputs": "the first input copy of the timed workload, whole batch"}}
 
 
 def cpu_baseline_draft_step(d, B, V):

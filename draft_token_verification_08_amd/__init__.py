@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     SV_OK, Prepared, SpecVerifyError, Workspace, lib, mtp_shift_insert, prepare_mtp_shift_insert,
     prepare_spec_verify_greedy, prepare_spec_verify_greedy_mtp, prepare_spec_verify_sample,
     prepare_spec_verify_greedy_lmhead, prepare_spec_verify_sample_ex, prepare_spec_verify_sample_mtp,
-    prepare_sv_sample_rows,
+    prepare_sv_sample_rows, prepare_spec_verify_tree_greedy,
     spec_verify_greedy, spec_verify_greedy_lmhead, spec_verify_tree_greedy, spec_verify_greedy_mtp, spec_verify_sample, sv_lmhead_logits_debug,
     spec_verify_sample_ex, spec_verify_sample_mtp, sv_sample_rows, draft_row_stats, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
 )

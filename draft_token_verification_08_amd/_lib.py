@@ -680,6 +680,31 @@ def sv_sample_rows(logits, temperature, uniforms, row_index=None, *, tokens=None
     return tokens
 
 
+def prepare_spec_verify_tree_greedy(target_logits, draft_tokens, draft_parents, draft_lens, accepted_len, emitted,
+                                    path, workspace, *, err_flags=None, stream=None) -> Prepared:
+    """spec_verify_tree_greedy with its arguments marshalled once."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_parents, "draft_parents", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n + 1), dev)
+    if path is not None:
+        _check(path, "path", torch.int32, (B, n), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    _check(workspace, "workspace", torch.uint8)
+    args = (_ptr(target_logits), dt, _ptr(draft_tokens), _ptr(draft_parents), _ptr(draft_lens), B, n, V,
+            _ptr(accepted_len), _ptr(emitted), _ptr(path), _ptr(err_flags), _ptr(workspace), workspace.numel(),
+            _stream(stream, dev))
+    return Prepared("spec_verify_tree_greedy", args, (target_logits, draft_tokens, draft_parents, draft_lens,
+                                                      accepted_len, emitted, path, err_flags, workspace))
+
+
 def prepare_sv_sample_rows(logits, temperature, uniforms, tokens, workspace, *, row_index=None, err_flags=None,
                            row_stats=None, stream=None) -> Prepared:
     """sv_sample_rows with its arguments marshalled once (see sv_sample_rows)."""
