@@ -846,51 +846,70 @@ __device__ __forceinline__ SeqInfo seq_info(const StatsParams& p, int b) {
 // Node i is accepted iff its parent is and x_{i-1} is the target's argmax g at
 // the parent (g[r] = argmax of target row r, lowest index on ties).  The kept
 // path ends at the deepest accepted node, the lowest-numbered among equally deep
-// ones; its tokens are emitted, then g of its last node, then -1.  The node
-// tokens and parents are staged in LDS by all threads; one thread walks them.
+// ones; its tokens are emitted, then g of its last node, then -1.
+//
+// One wave does it, lane j holding node j + 1 (L <= 64), with no serial walk:
+// pointer doubling (6 rounds of shuffles) gives every node its depth and whether
+// every edge up to the root matches, a wave max picks the kept node, and binary
+// lifting over the doubling's ancestor tables (6 more rounds) tells each node
+// whether it lies on the kept path, so each writes its own output slot.
 __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const SeqInfo& si, const int* s_idx) {
-    __shared__ int s_x[kMaxDraft], s_par[kMaxDraft];
-    __shared__ int s_depth[kMaxDraft + 1], s_ok[kMaxDraft + 1];
-    const int tid = threadIdx.x, n = p.n, V = p.V, L = si.L;
-    if (tid < L) {
-        s_x[tid] = p.tokens[(size_t)b * n + tid];
-        s_par[tid] = p.parents[(size_t)b * n + tid];
+    constexpr int kLog = 6;  // 2^6 = kMaxDraft: the longest root path
+    static_assert((1 << kLog) == kMaxDraft && kMaxDraft == 64, "one wave64 holds the tree");
+    const int j = threadIdx.x, n = p.n, V = p.V, L = si.L;
+    if (j >= 64) return;  // waves 1..3: nothing left to do
+    const int i = j + 1;  // this lane's node
+    const bool live = j < L;
+    const int x = live ? p.tokens[(size_t)b * n + j] : 0;
+    const int par = live ? p.parents[(size_t)b * n + j] : 0;
+    const bool good = live && par >= 0 && par < i;
+    const unsigned long long oor = __ballot(live && (x < 0 || x >= V));
+    const unsigned long long bad = __ballot(live && !good);
+
+    // (a, ok, d): an ancestor a of node i (0 once the root is reached), whether
+    // every edge from i up to a matches, and how many edges that is.
+    int a = good ? par : 0;
+    const int gp = s_idx[good ? par : 0];  // g at the parent (row 0 when none)
+    int ok = good && x == gp;
+    int d = 1;
+    int up[kLog];  // up[k]: the ancestor 2^k edges above node i (0 past the root)
+#pragma unroll
+    for (int k = 0; k < kLog; ++k) {
+        up[k] = a;
+        const int src = a > 0 ? a - 1 : j;
+        const int a2 = __shfl(a, src, 64), ok2 = __shfl(ok, src, 64), d2 = __shfl(d, src, 64);
+        if (a > 0) {
+            ok &= ok2;
+            d += d2;
+            a = a2;
+        }
     }
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t flags = si.flags;
-        s_depth[0] = 0;
-        s_ok[0] = 1;
-        int best = 0;
-        for (int i = 1; i <= L; ++i) {
-            const int pi = s_par[i - 1], xi = s_x[i - 1];
-            if (xi < 0 || xi >= V) flags |= SV_FLAG_TOKEN_OOR;
-            s_ok[i] = 0;
-            s_depth[i] = 0;
-            if (pi < 0 || pi >= i) {
-                flags |= SV_FLAG_BAD_PARENT;
-                continue;
-            }
-            if (s_ok[pi] && xi == s_idx[pi]) {
-                s_ok[i] = 1;
-                s_depth[i] = s_depth[pi] + 1;
-                if (s_depth[i] > s_depth[best]) best = i;
-            }
-        }
-        const int k = s_depth[best];
-        int32_t* e = p.emitted + (size_t)b * (n + 1);
-        int32_t* path = p.path ? p.path + (size_t)b * n : nullptr;
-        int node = best;
-        for (int d = k - 1; d >= 0; --d) {
-            if (path) path[d] = node;
-            e[d] = s_x[node - 1];
-            node = s_par[node - 1];
-        }
-        e[k] = s_idx[best];
-        for (int d = k + 1; d <= n; ++d) e[d] = -1;
-        if (path)
-            for (int d = k; d < n; ++d) path[d] = -1;
+    // after 64 edges every path has met the root: ok = accepted, d = depth
+    const int key = wave_max_i(good && ok ? (d << 7) | (127 - j) : 0);
+    const int k = key >> 7;                          // depth of the kept node
+    const int best = key ? 128 - (key & 127) : 0;   // its node index (0: the root)
+
+    // binary lifting: the ancestor of `best` at this node's depth
+    int node = best;
+    const int lift = k - d;
+#pragma unroll
+    for (int t = 0; t < kLog; ++t) {
+        const int src = node > 0 ? node - 1 : j;
+        const int nu = __shfl(up[t], src, 64);
+        if (node > 0 && lift >= 0 && ((lift >> t) & 1)) node = nu;
+    }
+    int32_t* e = p.emitted + (size_t)b * (n + 1);
+    int32_t* path = p.path ? p.path + (size_t)b * n : nullptr;
+    if (good && ok && lift >= 0 && node == i) {  // on the kept path, at depth d
+        e[d - 1] = x;
+        if (path) path[d - 1] = i;
+    }
+    for (int t = k + j; t <= n; t += 64) e[t] = t == k ? s_idx[best] : -1;
+    if (path)
+        for (int t = k + j; t < n; t += 64) path[t] = -1;
+    if (j == 0) {
         p.acc[b] = k;
+        const uint32_t flags = si.flags | (oor ? SV_FLAG_TOKEN_OOR : 0u) | (bad ? SV_FLAG_BAD_PARENT : 0u);
         if (flags && p.flags) atomicOr(p.flags, flags);
         xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
     }
