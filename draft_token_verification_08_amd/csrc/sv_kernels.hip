@@ -915,6 +915,41 @@ __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const Seq
     }
 }
 
+// The greedy decision of sequence b after its argmax keys are merged (g[r] in
+// s_idx): the longest prefix of drafts equal to g, then g at the first mismatch.
+// One wave writes the outputs, lane j its own emitted slot and, with the fused
+// MTP step, its own token slot (t[j] = t[j + 1] for j < n, then t[k] = g[k]);
+// every lane's load of t[j + 1] completes before any lane's store, since the
+// stores take their data from those loads.
+__device__ __forceinline__ void greedy_finish(const StatsParams& p, int b, const SeqInfo& si, const int* s_idx) {
+    const int j = threadIdx.x, n = p.n, V = p.V, L = si.L;
+    if (j >= 64) return;  // waves 1..3: nothing left to do
+    const int x = j < L ? p.tokens[(size_t)b * n + j] : 0;
+    const bool oor = j < L && (x < 0 || x >= V);
+    const bool rej = j < L && (oor || x != s_idx[j]);
+    const unsigned long long rmask = __ballot(rej);
+    const unsigned long long omask = __ballot(oor);
+    const int k = rmask ? __ffsll((long long)rmask) - 1 : L;  // first rejection, or L
+    const int g = s_idx[k];
+    int32_t* e = p.emitted + (size_t)b * (n + 1);
+    if (j <= n) e[j] = j < k ? x : (j == k ? g : -1);
+    if (n == kMaxDraft && j == 0) e[n] = k == n ? g : -1;
+    if (p.mtp.tokens) {
+        int32_t* t = p.mtp.tokens + (size_t)b * (n + 1);
+        const int next = j < n ? t[j + 1] : 0;
+        if (j < n) t[j] = j == k ? g : next;
+        if (k == n && j == 0) t[n] = g;
+    }
+    if (j == 0) {
+        uint32_t f = si.flags;
+        const unsigned long long upto = (k >= 63) ? ~0ull : ((2ull << k) - 1ull);  // slots 0..k
+        if (omask & upto) f |= SV_FLAG_TOKEN_OOR;
+        p.acc[b] = k;
+        if (f && p.flags) atomicOr(p.flags, f);
+        xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
+    }
+}
+
 // The decision of sequence b, run by the last workgroup of b to finish.  DRAW
 // (calls with no drafts): it also makes the bonus draw.  TREE (greedy): the
 // drafts form a tree, and the kept path is found by tree_walk.
@@ -971,6 +1006,10 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     __syncthreads();
     if constexpr (TREE) {
         tree_walk(p, b, si, s_idx);
+        return;
+    }
+    if constexpr (MODE == kGreedy) {
+        greedy_finish(p, b, si, s_idx);
         return;
     }
     if constexpr (MODE == kSample) {
