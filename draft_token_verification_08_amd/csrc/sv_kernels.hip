@@ -1035,8 +1035,10 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     if (tid < 64) {
         const int j = tid;
         bool rej = false, oor = false, badu = false;
+        int x = 0;
+        if constexpr (!DRAW) x = j < L ? p.tokens[(size_t)b * n + j] : 0;
         if (j < L) {
-            const int x = p.tokens[(size_t)b * n + j];
+            if constexpr (DRAW) x = p.tokens[(size_t)b * n + j];
             if (x < 0 || x >= V) {
                 oor = true;
                 rej = true;
@@ -1066,6 +1068,21 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
         const unsigned long long bmask = __ballot(badu);
         const int k = rmask ? __ffsll((long long)rmask) - 1 : L;
         const unsigned long long upto = (k >= 63) ? ~0ull : ((2ull << k) - 1ull);  // slots 0..k
+        if constexpr (!DRAW) {
+            // the emitted prefix and the fused MTP token shift, lane j its own
+            // slots (as in greedy_finish); slot k: g for greedy sequences, else
+            // the draw pass's
+            const int yk = si.greedy ? s_idx[k] : -1;
+            int32_t* e = p.emitted + (size_t)b * (n + 1);
+            if (j <= n) e[j] = j < k ? x : (j == k ? yk : -1);
+            if (n == kMaxDraft && j == 0) e[n] = k == n ? yk : -1;
+            if (p.mtp.tokens) {
+                int32_t* t = p.mtp.tokens + (size_t)b * (n + 1);
+                const int next = j < n ? t[j + 1] : 0;
+                if (j < n) t[j] = (j == k && si.greedy) ? yk : next;
+                if (k == n && si.greedy && j == 0) t[n] = yk;
+            }
+        }
         if (tid == 0) {
             uint32_t f = si.flags;
             if (omask & upto) f |= SV_FLAG_TOKEN_OOR;
@@ -1081,20 +1098,27 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     if (tid == 0) {
         uint32_t flags = s_flags;
         const int k = s_k;
+        // calls with no drafts write their outputs here, from one thread (the
+        // wave-wide writes above measured slower in that kernel's code)
         int32_t* e = p.emitted + (size_t)b * (n + 1);
-        const int32_t* x = p.tokens + (size_t)b * n;
-        for (int j = 0; j < k; ++j) e[j] = x[j];
-        for (int j = k + 1; j <= n; ++j) e[j] = -1;
+        if constexpr (DRAW) {
+            const int32_t* x = p.tokens + (size_t)b * n;
+            for (int j = 0; j < k; ++j) e[j] = x[j];
+            for (int j = k + 1; j <= n; ++j) e[j] = -1;
+        }
         p.acc[b] = k;
-        if (p.mtp.tokens) shift_tokens(p.mtp.tokens, b, n);  // fused MTP step
+        if constexpr (DRAW)
+            if (p.mtp.tokens) shift_tokens(p.mtp.tokens, b, n);  // fused MTP step
         if (si.greedy) {
-            e[k] = s_idx[k];
-            if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + k] = s_idx[k];
+            if constexpr (DRAW) {
+                e[k] = s_idx[k];
+                if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + k] = s_idx[k];
+            }
         } else {
             const double u = sanitize_u(p.unif[(size_t)b * (n + 1) + n], flags);
             // the draw (residual after a rejection, bonus after full acceptance)
             // is done by the draw pass
-            e[k] = -1;
+            if constexpr (DRAW) e[k] = -1;
             DrawDesc d;
             d.kind = (k < L) ? kDrawResidual : kDrawBonus;
             d.k = k;

@@ -402,3 +402,37 @@ def test_max_vocab(oracle):
     g_acc, g_emi, _ = run_greedy(g)
     gor = oracle_greedy(oracle, g)
     assert np.array_equal(g_acc, gor["accepted_len"]) and np.array_equal(g_emi, gor["emitted"])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_max_draft_length_greedy_full_acceptance(oracle, fused):
+    """n = 64 with drafts equal to the target's argmax up to slot k for
+    k in {64, 63, 32, 0} and a shorter length: the accepted length reaches 64,
+    the last emitted slot and, with the MTP step fused, the last token slot are
+    written; outputs and the shifted token buffer equal the oracle's."""
+    B, n, V, H = 6, sv.SV_MAX_DRAFT, 2003, 24
+    d = synth.make(3, 640 + int(fused), device=DEV, B=B, V=V, n=n, H=H)
+    g = d["target"].float().cpu().numpy().argmax(axis=-1)  # lowest index of the maximum
+    tok = g[:, :n].astype(np.int32)
+    for b, k in ((1, 63), (2, 32), (3, 0), (5, 10)):
+        tok[b, k] = (tok[b, k] + 1) % V
+    d["draft_tokens"].copy_(torch.from_numpy(tok))
+    d["draft_lens"].copy_(torch.tensor([64, 64, 64, 64, 40, 64], dtype=torch.int32))
+    lens = d["draft_lens"].cpu().numpy()
+    gor = oracle.verify_greedy(synth.host_logits(d["target"]), tok, lens)
+    assert list(gor["accepted_len"]) == [64, 63, 32, 0, 40, 10]
+    if fused:
+        t = d["tokens"].clone()
+        dst = torch.zeros_like(d["hidden"])
+        acc, emi = sv.spec_verify_greedy_mtp(d["target"], d["draft_tokens"], d["draft_lens"], t, d["hidden"], dst)
+        _sync()
+        ref_tok, ref_hid = oracle.mtp_shift_insert(d["tokens"].cpu().numpy(),
+                                                   d["hidden"].cpu().view(torch.int16).numpy(),
+                                                   gor["accepted_len"], gor["emitted"])
+        assert np.array_equal(t.cpu().numpy(), ref_tok)
+        assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid)
+        acc, emi = acc.cpu().numpy(), emi.cpu().numpy()
+    else:
+        acc, emi, fl = run_greedy(d)
+        assert fl == 0
+    assert np.array_equal(acc, gor["accepted_len"]) and np.array_equal(emi, gor["emitted"])

@@ -85,3 +85,38 @@ def test_workspace_reused_across_shapes(oracle):
         o = _oracle(oracle, d)
         assert np.array_equal(acc.cpu().numpy(), o["accepted_len"]) and np.array_equal(emi.cpu().numpy(), o["emitted"])
     assert int(ws.count_nonzero()) == 0  # every call leaves the workspace zero-filled
+
+
+def _argmax_first(target):
+    """g[b, r]: lowest index of the maximum of target row (b, r), on the host."""
+    return target.float().cpu().numpy().argmax(axis=-1).astype(np.int32)
+
+
+@pytest.mark.parametrize("depth_cut", [64, 63, 33, 32, 31, 1, 0])
+def test_deep_paths_at_the_largest_tree(oracle, depth_cut):
+    """n = 64 nodes: a spine 0 -> 1 -> ... whose tokens follow the target's
+    argmax down to depth `depth_cut` (one wrong token below it), with side
+    leaves hanging off it, so the kept path is up to 64 nodes deep and crosses
+    the power-of-two depths the walk's pointer doubling and lifting split at."""
+    B, n, V = 3, 64, 503
+    d = synth.make_tree(900 + depth_cut, device=DEV, B=B, n=n, V=V, shape="random")
+    g = _argmax_first(d["target"])
+    par = np.zeros((B, n), np.int32)
+    tok = np.zeros((B, n), np.int32)
+    for b in range(B):
+        spine = [0]
+        for j in range(n):
+            node = j + 1
+            if b > 0 and node % 5 == 0 and len(spine) > 1:
+                par[b, j] = spine[-2]          # a side leaf below the spine's second-to-last node
+                tok[b, j] = (g[b, spine[-2]] + 1) % V
+                continue
+            par[b, j] = spine[-1]
+            depth = len(spine)                # this node's depth
+            tok[b, j] = g[b, spine[-1]] if depth <= depth_cut else (g[b, spine[-1]] + 1) % V
+            spine.append(node)
+    d["draft_parents"].copy_(torch.from_numpy(par))
+    d["draft_tokens"].copy_(torch.from_numpy(tok))
+    d["draft_lens"].fill_(n)
+    acc = _same(oracle, d, depth_cut)
+    assert acc[0] == depth_cut  # the plain chain is accepted exactly down to the cut
