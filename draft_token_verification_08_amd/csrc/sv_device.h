@@ -37,8 +37,10 @@ __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
 // 64-bit key whose unsigned order is the argmax order: order-preserving map of
 // the float in the high word, the inverted index in the low word (equal values:
 // the lower index has the larger key).  Zero is below every key of a number.
+// -0.0 is keyed as +0.0: the two compare equal in better() and in the row
+// scan's strict '>', so across chunks too the lower index must win between them.
 __device__ __forceinline__ unsigned long long argmax_key(ArgMax a) {
-    unsigned u = __float_as_uint(a.v);
+    unsigned u = (a.v == 0.f) ? 0u : __float_as_uint(a.v);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (unsigned)a.i);
 }
