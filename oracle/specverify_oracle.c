@@ -29,8 +29,13 @@
  *     input tokens are shifted, a kernel writes the next target token into its
  *     slot, so no CPU sync is needed after acceptance.
  *
- * Everything is computed in double precision, scalar, with sums taken in
- * ascending index order.  Nothing is blocked, fused or reordered.
+ * Everything is computed scalar, with sums taken in ascending index order, in
+ * double precision except the final draw: its weights (p_L, or max(0, p_k - q_k)
+ * after a rejection) and their running sum are formed in 80-bit extended
+ * precision (long double).  When the draft is almost the target, p_k - q_k is
+ * a difference of nearly equal numbers; at a residual mass near 1e-10 binary64
+ * keeps only about five of its digits, too few to place the draw to 1e-5 of the
+ * mass.  Nothing is blocked, fused or reordered.
  *
  * Readings of points the pages leave open:
  *   - acceptance of draft x_j:  u[b][j] < p_j(x_j) / q_j(x_j); q(x) = 0 gives
@@ -130,32 +135,49 @@ static double prob_at(const void *rows, int dt, size_t base, int i, double T, do
     return exp((logit_at(rows, dt, base + (size_t)i) - m) / T - logS);
 }
 
+/* The whole distribution softmax(z / T) of one row in extended precision:
+ * p_i = exp((z_i - m) / T) / S with S = sum_i exp((z_i - m) / T), m the row max. */
+static void row_probs_ld(const void *rows, int dt, size_t base, int V, double T, long double *p)
+{
+    double m = logit_at(rows, dt, base);
+    for (int i = 1; i < V; ++i) {
+        double v = logit_at(rows, dt, base + (size_t)i);
+        if (v > m) m = v;
+    }
+    long double S = 0.0L;
+    for (int i = 0; i < V; ++i) {
+        p[i] = expl(((long double)logit_at(rows, dt, base + (size_t)i) - (long double)m) / (long double)T);
+        S += p[i];
+    }
+    for (int i = 0; i < V; ++i) p[i] /= S;
+}
+
 /* Inverse CDF over unnormalised weights in ascending index order.
  *   Z = sum w_i,  t = u * Z,  C_i = w_0 + ... + w_i,  y = min{i : C_i > t};
  *   if no index qualifies (t >= C_{V-1} through rounding), y = the last i with
  *   w_i > 0 (or 0 if all weights are zero).
  * *margin receives min(t - C_{y-1}, C_y - t) / Z with C_{-1} = 0: the distance of
  * the threshold to the nearest CDF boundary of the chosen bucket. */
-static int draw_inverse_cdf(const double *w, int V, double u, double *margin)
+static int draw_inverse_cdf(const long double *w, int V, double u, double *margin)
 {
-    double Z = 0.0;
+    long double Z = 0.0L;
     for (int i = 0; i < V; ++i) Z += w[i];
-    double t = u * Z;
-    double C = 0.0;
+    long double t = (long double)u * Z;
+    long double C = 0.0L;
     for (int i = 0; i < V; ++i) {
-        double prev = C;
+        long double prev = C;
         C += w[i];
         if (C > t) {
             if (margin) {
-                double a = t - prev, b = C - t;
-                *margin = (Z > 0.0) ? ((a < b ? a : b) / Z) : 0.0;
+                long double a = t - prev, b = C - t;
+                *margin = (Z > 0.0L) ? (double)((a < b ? a : b) / Z) : 0.0;
             }
             return i;
         }
     }
     int last = 0;
     for (int i = 0; i < V; ++i)
-        if (w[i] > 0.0) last = i;
+        if (w[i] > 0.0L) last = i;
     if (margin) *margin = 0.0;
     return last;
 }
@@ -193,7 +215,7 @@ typedef struct {
     uint32_t *seq_flags;    /* [B] nullable */
 } job_t;
 
-static void verify_one(const job_t *J, int b, double *w /* scratch [V] */)
+static void verify_one(const job_t *J, int b, long double *w /* scratch [2V] */)
 {
     const int n = J->n, V = J->V;
     uint32_t flags = 0;
@@ -267,28 +289,27 @@ static void verify_one(const job_t *J, int b, double *w /* scratch [V] */)
         if (rejected) ufinal = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + k], &flags);
 #endif
         if (rejected) {
-            /* residual distribution max(0, p_k - q_k) */
-            double Z = 0.0;
+            /* residual distribution max(0, p_k - q_k), in extended precision */
+            long double *q = w + V;
+            row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
+            row_probs_ld(J->draft, J->dt, drow0 + (size_t)k * V, V, T, q);
+            long double Z = 0.0L;
             for (int i = 0; i < V; ++i) {
-                double p = prob_at(J->target, J->dt, trow0 + (size_t)k * V, i, T, mt[k], lst[k]);
-                double q = prob_at(J->draft, J->dt, drow0 + (size_t)k * V, i, T, md[k], lsd[k]);
-                double d = p - q;
-                w[i] = d > 0.0 ? d : 0.0;
+                long double d = w[i] - q[i];
 #if SV_ORACLE_PLANT == 1
                 /* planted mistake: plain target sampling at the rejection */
-                w[i] = p;
+                d = w[i];
 #endif
+                w[i] = d > 0.0L ? d : 0.0L;
                 Z += w[i];
             }
-            if (!(Z > 0.0)) {
+            if (!(Z > 0.0L)) {
                 flags |= OR_FLAG_ZERO_RESIDUAL;
-                for (int i = 0; i < V; ++i)
-                    w[i] = prob_at(J->target, J->dt, trow0 + (size_t)k * V, i, T, mt[k], lst[k]);
+                row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
             }
         } else {
             /* every draft accepted: the bonus token comes from p_L */
-            for (int i = 0; i < V; ++i)
-                w[i] = prob_at(J->target, J->dt, trow0 + (size_t)L * V, i, T, mt[L], lst[L]);
+            row_probs_ld(J->target, J->dt, trow0 + (size_t)L * V, V, T, w);
         }
         double margin = 0.0;
         y = draw_inverse_cdf(w, V, ufinal, &margin);
@@ -313,7 +334,7 @@ typedef struct {
 static void *run_slice(void *arg)
 {
     slice_t *s = (slice_t *)arg;
-    double *w = (double *)malloc(sizeof(double) * (size_t)s->job->V);
+    long double *w = (long double *)malloc(sizeof(long double) * 2 * (size_t)s->job->V);
     if (!w) { s->status = -2; return NULL; }
     for (int b = s->b0; b < s->b1; ++b) verify_one(s->job, b, w);
     free(w);
@@ -666,10 +687,17 @@ int sv_oracle_argmax_row(const void *z, int dt, int V)
     return row_argmax(z, dt, 0, V);
 }
 
-/* The inverse-CDF step on explicit weights (exposed for pinning). */
+/* The inverse-CDF step on explicit weights (exposed for pinning; the weights
+ * are widened to extended precision as the step's own draw forms them).
+ * Returns -2 if scratch memory cannot be had. */
 int sv_oracle_draw_weights(const double *w, int V, double u, double *margin)
 {
-    return draw_inverse_cdf(w, V, u, margin);
+    long double *wl = (long double *)malloc(sizeof(long double) * (size_t)(V > 0 ? V : 1));
+    if (!wl) return -2;
+    for (int i = 0; i < V; ++i) wl[i] = w[i];
+    int y = draw_inverse_cdf(wl, V, u, margin);
+    free(wl);
+    return y;
 }
 
 /* Which planted mistake this compiled oracle carries (0 = none).  Test-only builds set

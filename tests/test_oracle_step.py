@@ -213,6 +213,46 @@ def test_residual_never_emits_where_target_not_above_draft(oracle):
     assert checked > 50
 
 
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_residual_of_one_raised_token_is_target_without_it(oracle, T):
+    """Closed form at any residual mass: a draft row equal to the target row
+    except one token x whose logit is raised has q_i < p_i for every i != x
+    (same logit, larger normaliser) and q_x > p_x, so max(0, p - q) is p_i (1 -
+    S_t / S_d) for i != x and 0 at x: after the rejection at x the token is
+    drawn from p with x removed.  x runs from likely to very unlikely tokens, so
+    the residual mass q_x - p_x spans about 1e-2 down to 1e-11, where p - q
+    formed in binary64 keeps only a few digits."""
+    V, B = 3000, 96
+    rng = np.random.default_rng(17)
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    order = np.argsort(-z, axis=1)
+    zt = np.stack([z, z], axis=1)                        # slot 1 (the bonus row) unused
+    zd = z[:, None, :].copy()
+    x = np.empty((B, 1), np.int32)
+    for b in range(B):
+        x[b, 0] = order[b, [0, 5, 50, 300, 1500, 2900][b % 6]]   # from the top token to the tail
+        zd[b, 0, x[b, 0]] += np.float32(0.25 + 2.0 * rng.random())
+    u = rng.random((B, 2)).astype(np.float32)
+    u[:, 0] = np.float32(1.0 - 2.0 ** -24)
+    out = oracle.verify_sample(zt, zd, x, np.ones(B, np.int32), np.full(B, T, np.float32), u)
+    assert (out["accepted_len"] == 0).all()
+    Tf = float(np.float32(T))
+    zs = []
+    for b in range(B):
+        p = sps.softmax(z[b].astype(np.float64) / Tf)
+        q = sps.softmax(zd[b, 0].astype(np.float64) / Tf)
+        zs.append(q[x[b, 0]] - p[x[b, 0]])
+        w = p.copy()
+        w[x[b, 0]] = 0.0
+        c = np.cumsum(w)
+        t = float(u[b, 1]) * c[-1]
+        y = int(np.searchsorted(c, t, side="right"))
+        margin = min(t - (c[y - 1] if y > 0 else 0.0), c[y] - t) / c[-1]
+        assert out["emitted"][b, 0] == y or margin < 1e-12, (b, out["emitted"][b, 0], y, zs[-1])
+        assert abs(out["draw_margin"][b] - margin) <= 1e-9 + 1e-6 * margin, (b, out["draw_margin"][b], margin)
+    assert min(zs) < (1e-10 if T < 1 else 1e-8) and max(zs) > 1e-3
+
+
 def test_emitted_layout_and_length_bounds(oracle):
     zt, zd, x, u = _case(8, B=100, n=6, V=100)
     B, n = x.shape
