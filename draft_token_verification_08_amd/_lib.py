@@ -77,6 +77,8 @@ def lib():
     L.sv_lmhead_logits_debug.restype = i
     L.sv_softmax_rows_debug.argtypes = [vp, i, vp, i, i, vp, vp]
     L.sv_softmax_rows_debug.restype = i
+    L.sv_residual_weights_debug.argtypes = [vp, vp, i, vp, i, i, vp, vp, vp, vp]
+    L.sv_residual_weights_debug.restype = i
     _lib = L
     return L
 
@@ -478,6 +480,25 @@ def mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitted, *, s
     _call("mtp_shift_insert", _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H, _ptr(accepted_len),
           _ptr(emitted), B, n, _stream(stream, dev))
     return tokens, hidden_dst
+
+
+def sv_residual_weights_debug(target_rows, draft_rows, temperature, *, stream=None):
+    """Residual weights the draw pass scans after a rejection (parity/debug only).
+    Returns (weights [rows, V] float32, tile_weights [rows, NT] float64,
+    info [rows, 4] float32: near form, rho0, rho, sum of tile weights)."""
+    dev = target_rows.device
+    rows, V = target_rows.shape
+    _check(target_rows, "target_rows", device=dev)
+    _check(draft_rows, "draft_rows", dtype=target_rows.dtype, shape=(rows, V), device=dev)
+    _check(temperature, "temperature", torch.float32, (rows,), dev)
+    tile = 2048 if target_rows.dtype == torch.bfloat16 else 1024
+    NT = (V + tile - 1) // tile
+    w = torch.empty((rows, V), dtype=torch.float32, device=dev)
+    tw = torch.empty((rows, NT), dtype=torch.float64, device=dev)
+    info = torch.empty((rows, 4), dtype=torch.float32, device=dev)
+    _call("sv_residual_weights_debug", _ptr(target_rows), _ptr(draft_rows), _dt(target_rows), _ptr(temperature),
+          rows, V, _ptr(w), _ptr(tw), _ptr(info), _stream(stream, dev))
+    return w, tw, info
 
 
 def sv_softmax_rows_debug(logits, temperature, *, probs_out=None, stream=None):

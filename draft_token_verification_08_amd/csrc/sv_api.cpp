@@ -63,10 +63,8 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     off = align_up(off + (size_t)B * sizeof(sv::DrawDesc), 256);
     L->off_tiles = off;
     off = align_up(off + (size_t)B * nt * sizeof(unsigned long long), 256);
-    L->off_dres = off;
-    off = align_up(off + (size_t)B * nt * sizeof(float), 256);
-    L->off_dp = off;
-    off = align_up(off + (size_t)B * nt * sizeof(float), 256);
+    L->off_dsum = off;
+    off = align_up(off + (size_t)B * sv::kDrawSums * nt * sizeof(float), 256);
     L->off_acc = off;
     off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L->bytes = off < 256 ? 256 : off;
@@ -299,8 +297,7 @@ sv_status_t verify_sample(const void* target_logits, const void* draft_logits, s
         dp.emitted = emitted;
         dp.flags = err_flags;
         dp.desc = sp.desc;
-        dp.dres = at<float>(workspace, L.off_dres);
-        dp.dp = at<float>(workspace, L.off_dp);
+        dp.dsum = at<float>(workspace, L.off_dsum);
         dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
         if (mtp && pl.fused) dp.mtp_tokens = pl.f.tokens;
         e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
@@ -532,8 +529,7 @@ sv_status_t sv_sample_rows(const void* logits, sv_dtype_t dt, int R, const int32
     dp.emitted = tokens;
     dp.flags = err_flags;
     dp.desc = sp.desc;
-    dp.dres = at<float>(workspace, L.off_dres);
-    dp.dp = at<float>(workspace, L.off_dp);
+    dp.dsum = at<float>(workspace, L.off_dsum);
     dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
     e = sv::launch_draw(dp, dt == SV_BF16 ? sv::kBF16 : sv::kF32, aligned, s);
     return e == hipSuccess ? SV_OK : hip_fail(e);
@@ -675,6 +671,25 @@ sv_status_t sv_softmax_rows_debug(const void* logits, sv_dtype_t dt, const float
         return SV_EALIGN;
     hipError_t e = sv::launch_softmax_debug(logits, dt == SV_BF16 ? sv::kBF16 : sv::kF32, temperature, rows,
                                             V, probs_out, rows_aligned(logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+sv_status_t sv_residual_weights_debug(const void* target_rows, const void* draft_rows, sv_dtype_t dt,
+                                      const float* temperature, int rows, int V, float* weights_out,
+                                      double* tile_weights_out, float* info_out, void* stream) {
+    if (rows < 0 || V < 1 || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (rows == 0) return SV_OK;
+    if (!target_rows || !draft_rows || !temperature || !weights_out) return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(target_rows, es) || !aligned_to(draft_rows, es) || !aligned_to(temperature, 4) ||
+        !aligned_to(weights_out, 4) || !aligned_to(tile_weights_out, 8) || !aligned_to(info_out, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(1, 0, V, dt, &L)) return SV_EINVAL;
+    const bool aligned = rows_aligned(target_rows, V, dt) && aligned_to(draft_rows, 16);
+    hipError_t e = sv::launch_residual_debug(target_rows, draft_rows, dt == SV_BF16 ? sv::kBF16 : sv::kF32,
+                                             temperature, rows, V, L.NT, weights_out, tile_weights_out, info_out,
+                                             aligned, (hipStream_t)stream);
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 

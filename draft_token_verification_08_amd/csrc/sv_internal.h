@@ -30,12 +30,17 @@ constexpr int kDrawTiles = SV_DRAW_TILES;  // draw pass: tiles (kThreads * eleme
 constexpr int kMaxTiles = 1024;      // tiles per row (4 per thread in the draw selections)
 constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
+constexpr int kDrawSums = 5;         // per-tile sums a residual draw chunk hands over
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
 
-// kinds of the final draw of a sequence
-enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
+// kinds of the final draw of a sequence.  The residual max(0, p_k - q_k) is
+// weighted in one of two forms (see the draw pass): rows whose maxima are close
+// (|m_t - m_d| c <= 32) scale both rows by one common maximum, so that tokens
+// the rows share cancel exactly ("near"); other rows scale each row by its own
+// maximum ("far").
+enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2, kDrawResidualNear = 3 };
 
 // One 64-bit slot per (sequence, row slot, vocab chunk), exchanged atomically:
 //   sampling rows: low word chunk max m_c, high word sum over the chunk of 2^((z - m_c) c)
@@ -54,7 +59,8 @@ struct DrawDesc {
     float m_d;      // max of draft row k (residual only)
     float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
-    float pad;
+    float rho0;     // near residual: S'_d / S'_t - 1 from the statistics pass, S' = the sums
+                    // scaled by the common maximum max(m_t, m_d)
 };
 
 // Workspace layout (byte offsets from the workspace base; every region 256-aligned).
@@ -68,8 +74,7 @@ struct Layout {
     size_t off_cnt_draw; // uint32 [B]   draw-pass arrival counters
     size_t off_desc;     // DrawDesc [B]
     size_t off_tiles;    // uint64 [B][NT] tile partials (m_t, s_t) of target row L (sampling)
-    size_t off_dres;     // float [B][NT] residual mass per tile (draw pass)
-    size_t off_dp;       // float [B][NT] 2^((z - m_t) c) mass per tile of target row k (draw pass)
+    size_t off_dsum;     // float [B][kDrawSums][NT] per-tile sums of the residual draw (draw pass)
     size_t off_acc;      // int32 [B] accepted lengths of sv_sample_rows (always 0)
     size_t bytes;
 };
@@ -123,8 +128,7 @@ struct DrawParams {
     int32_t* emitted;
     uint32_t* flags;
     DrawDesc* desc;
-    float* dres;
-    float* dp;
+    float* dsum;              // [B][kDrawSums][NT]
     uint32_t* cnt;
     int32_t* mtp_tokens;      // [B][n+1] or nullptr: the drawn token is also written to slot k
 };
@@ -164,6 +168,9 @@ hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
 hipError_t launch_lmhead(const LmParams& p, hipStream_t s);
 hipError_t launch_decide_greedy(const StatsParams& p, hipStream_t s);
+hipError_t launch_residual_debug(const void* target, const void* draft, Dt dt, const float* temp, int rows, int V,
+                                 int NT, float* w_out, double* tile_out, float* info_out, bool aligned,
+                                 hipStream_t s);
 hipError_t launch_softmax_debug(const void* logits, Dt dt, const float* temp, int rows, int V,
                                 float* out, bool aligned, hipStream_t s);
 

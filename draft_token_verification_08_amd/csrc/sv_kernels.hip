@@ -631,57 +631,113 @@ __device__ __forceinline__ Pick block_first_crossing(int N, double t, W&& weight
     return Pick{-1, carry};
 }
 
-// Weight of one element for the draw.  Bonus / fallback rows: 2^((z - m_t) c),
-// on the same scale as the stored tile partials.  Residual rows:
-// S_t * max(0, p_k - q_k) = max(0, 2^((z_t - m_t) c) - 2^((z_d - m_d) c + log2(S_t / S_d))):
-// the common factor S_t cancels in the draw, and the draft's normaliser enters
-// its exponent through one fma (z_d - m_d is exact for bf16).
-__device__ __forceinline__ float w_target(const DrawDesc& d, float zt) {
-    return exp2_fast((zt - d.m_t) * d.c);
+// 2^x - 1 for |x| <= 1/2: the exponential series in x ln 2 to degree 8, in
+// Horner form (relative error about 1.2e-7 in binary32; exp2(x) - 1 would lose
+// every digit as x -> 0).
+__device__ __forceinline__ float exp2m1_small(float x) {
+    float a = 1.3215486790144305e-06f;
+    a = fmaf(a, x, 1.5252733804059838e-05f);
+    a = fmaf(a, x, 1.5403530393381606e-04f);
+    a = fmaf(a, x, 1.3333558146428441e-03f);
+    a = fmaf(a, x, 9.618129107628477e-03f);
+    a = fmaf(a, x, 5.5504108664821576e-02f);
+    a = fmaf(a, x, 2.402265069591007e-01f);
+    a = fmaf(a, x, 6.931471805599453e-01f);
+    return a * x;
 }
-__device__ __forceinline__ float w_residual(const DrawDesc& d, float zt, float zd) {
-    const float pt = exp2_fast((zt - d.m_t) * d.c);
-    const float qd = exp2_fast(fmaf(zd - d.m_d, d.c, d.lq));
-    return fmaxf(pt - qd, 0.f);
+
+// Residual terms of one token when both rows are scaled by one common maximum M
+// (near residual): A = 2^((z_t - M) c), B = 2^((z_d - M) c) and Dl = B - A.
+// With x = (z_d - z_t) c, Dl is formed as A (2^x - 1) when |x| <= 1/2 (no
+// cancellation), else as B - A; a token the two rows share has x = 0 and
+// Dl = 0 exactly.  With S'_t = sum A, S'_d = sum B and rho = S'_d / S'_t - 1,
+//   p - q = A / S'_t - B / S'_d = (rho A - Dl) / (S'_t (1 + rho)),
+// so max(0, rho A - Dl) are residual weights up to one common factor.
+struct NearTerm {
+    float A, Dl;
+    bool same;  // x == 0: the token's logit is the same in both rows
+};
+__device__ __forceinline__ NearTerm near_term(float M, float c, float zt, float zd) {
+    const float A = exp2_fast((zt - M) * c);
+    const float x = (zd - zt) * c;
+    const float small = A * exp2m1_small(x);
+    const float direct = exp2_fast((zd - M) * c) - A;
+    return NearTerm{A, fabsf(x) <= 0.5f ? small : direct, x == 0.f};
+}
+
+// How a draw weighs one element (all weights up to a factor common to the row):
+//   kWTarget:   2^((z_t - mA) c), the target's own distribution (bonus draws, and
+//               the fallback when no residual mass is left);
+//   kWResFar:   max(0, 2^((z_t - m_t) c) - 2^((z_d - m_d) c + log2(S_t / S_d))),
+//               each row scaled by its own maximum (mA = m_t);
+//   kWResNear:  max(0, rho A - Dl) of near_term() with M = mA.
+enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
+struct WSpec {
+    int mode;
+    float c;    // log2(e) / T
+    float mA;   // maximum the target row is scaled by
+    float m_d;  // kWResFar: the draft row's maximum
+    float lq;   // kWResFar: log2(S_t / S_d)
+    float rho;  // kWResNear
+};
+__device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
+    if (s.mode == kWTarget) return exp2_fast((zt - s.mA) * s.c);
+    if (s.mode == kWResFar) {
+        const float pt = exp2_fast((zt - s.mA) * s.c);
+        const float qd = exp2_fast(fmaf(zd - s.m_d, s.c, s.lq));
+        return fmaxf(pt - qd, 0.f);
+    }
+    const NearTerm t = near_term(s.mA, s.c, zt, zd);
+    return fmaxf(s.rho * t.A - t.Dl, 0.f);
+}
+__device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
+    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f};
 }
 
 // Scan one tile: returns the element whose running weight (starting at P)
-// first exceeds t, or, if none does (rounding), the tile's last element with
-// positive weight, or the tile's first element.
+// first exceeds t.  The thread holding t is picked from per-thread sums taken in
+// binary64 over the same terms the element scan adds, so the two agree; if
+// rounding still leaves t unreached inside that thread, its last element of
+// positive weight is taken (the neighbour of the boundary).  If t lies past the
+// whole tile (or take_last), the tile's last element of positive weight is
+// taken, or the tile's first element when it has none.
 template <int DT, bool ALIGNED>
-__device__ __forceinline__ int scan_tile(const DrawDesc& d, bool residual, const void* trow, const void* drow, int V, int tile,
-                         double P, double t, bool take_last) {
+__device__ __forceinline__ int scan_tile(const WSpec& ws, const void* trow, const void* drow, int V, int tile,
+                                         double P, double t, bool take_last) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     const int e0 = tile * kTile + threadIdx.x * kVec;
+    const bool residual = ws.mode != kWTarget;
     float zt[kVec], zd[kVec], wv[kVec];
     load_vec<DT, ALIGNED>(trow, e0, V, zt);
     if (residual) load_vec<DT, ALIGNED>(drow, e0, V, zd);
-    float ts = 0.f;
+    double ts = 0.0;
     int my_last = -1;
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        wv[e] = (e0 + e < V) ? (residual ? w_residual(d, zt[e], zd[e]) : w_target(d, zt[e])) : 0.f;
-        ts += wv[e];
+        wv[e] = (e0 + e < V) ? elem_weight(ws, zt[e], residual ? zd[e] : 0.f) : 0.f;
+        ts += (double)wv[e];
         if (wv[e] > 0.f) my_last = e0 + e;
     }
-    __shared__ float s_ts[kThreads];
+    __shared__ double s_ts[kThreads];
     __shared__ int s_y;
     s_ts[threadIdx.x] = ts;
     if (threadIdx.x == 0) s_y = -1;
     __syncthreads();
     Pick pk{-1, 0.0};
-    if (!take_last) pk = block_first_crossing(kThreads, t - P, [&](int i) { return (double)s_ts[i]; });
+    if (!take_last) pk = block_first_crossing(kThreads, t - P, [&](int i) { return s_ts[i]; });
     if (pk.i == (int)threadIdx.x) {
         double run = P + pk.before;
+        int y = my_last;  // t unreached through rounding: the boundary's neighbour
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
             run += (double)wv[e];
             if (run > t && wv[e] > 0.f) {
-                s_y = e0 + e;
+                y = e0 + e;
                 break;
             }
         }
+        s_y = y;
     }
     const int last = block_max_all(my_last);
     __syncthreads();
@@ -783,8 +839,9 @@ __device__ __forceinline__ int tile_draw(unsigned long long* tiles, int NT, int 
     __syncthreads();
     const double t = s_t;
     const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_w[i]; });
-    if (pk.i >= 0) return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, V, pk.i, pk.before, t, false);
-    return scan_tile<DT, ALIGNED>(d, false, trow, nullptr, V, s_last_tile, 0.0, t, true);
+    const WSpec ws = target_spec(d);
+    if (pk.i >= 0) return scan_tile<DT, ALIGNED>(ws, trow, nullptr, V, pk.i, pk.before, t, false);
+    return scan_tile<DT, ALIGNED>(ws, trow, nullptr, V, s_last_tile, 0.0, t, true);
 }
 
 // --------------------------------------------------------------- decision helpers
@@ -1127,7 +1184,16 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
             d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
-            d.pad = 0.f;
+            d.rho0 = 0.f;
+            if (k < L) {
+                // near residual when the row maxima lie within 2^32 of each other
+                // on the exponent scale: both rows then fit one common maximum
+                const double gap = ((double)d.m_d - (double)d.m_t) * cd;
+                if (fabs(gap) <= 32.0) {
+                    d.kind = kDrawResidualNear;
+                    d.rho0 = (float)(s_S[n + 1 + k] / s_S[k] * exp2(gap) - 1.0);
+                }
+            }
             if constexpr (DRAW) s_desc = d;  // drawn below, by this workgroup
             else p.desc[b] = d;
         }
@@ -1242,10 +1308,93 @@ __global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
 // Bonus draws (all drafts accepted): workgroup (b, 0) alone, with tile_draw().
 // Residual draws (draft k rejected) from max(0, p_k - q_k): workgroup (b, c)
 // reads its chunk of kDrawTiles tiles of target row k and draft row k once
-// (thread i: vector i of every tile), and hands over per-tile sums of the
-// residual and of 2^((z - m_t) c) (the p_k fallback) by atomic exchange.  The
-// last workgroup of the sequence picks the tile holding u * Z with one block
-// prefix scan and scans only that tile.
+// (thread i: vector i of every tile) and hands over per-tile sums by atomic
+// exchange; the last workgroup of the sequence picks the tile holding u * Z with
+// one block prefix scan and scans only that tile.
+//
+// Far residual (row maxima far apart): the tile sums are those of the weights
+// kWResFar and of the target's 2^((z - m_t) c) (the p_k fallback).
+// Near residual: both rows are scaled by M = max(m_t, m_d) (near_term()).  The
+// weights max(0, rho A - Dl) need rho = S'_d / S'_t - 1 exactly, since tokens
+// the rows share carry weight rho A: when the rows are almost equal, rho is the
+// whole residual and the statistics pass's binary32 normalisers do not give it
+// to enough digits.  The chunks therefore sum, per tile, X = sum A and
+// D = sum Dl (so that rho = D / X, in which shared tokens add nothing), and, at
+// the statistics pass's estimate rho0, P0 = sum A over shared tokens and
+// W' = sum (rho0 A - Dl), LA = sum A over the other tokens with rho0 A > Dl.
+// The last workgroup forms each tile's weight at the exact rho as
+//   max(0, rho) P0 + W' + (rho - rho0) LA,
+// which is exact for shared tokens and, for the others, exact unless a token's
+// ratio Dl / A lies between rho0 and rho (a kink of max(0, rho A - Dl) crossed);
+// the tile it picks is then scanned with the exact per-token weights.
+constexpr int kSumX = 0, kSumW = 1, kSumD = 2, kSumP0 = 3, kSumLA = 4;
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+// Two sums over the workgroup, the same value in every thread.
+__device__ void block_sum2_all(double& a, double& b) {
+    __shared__ double sh[2][kWaves];
+    a = wave_sum_d(a);
+    b = wave_sum_d(b);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        sh[0][w] = a;
+        sh[1][w] = b;
+    }
+    __syncthreads();
+    a = sh[0][0];
+    b = sh[1][0];
+    for (int i = 1; i < kWaves; ++i) {
+        a += sh[0][i];
+        b += sh[1][i];
+    }
+    __syncthreads();
+}
+
+// Per-element accumulation of a residual tile's sums (lane-private, in the
+// order the caller visits the elements).  The draw pass and the parity/debug
+// kernel both use these, so both form the same sums.
+struct TileSums {
+    float x, w, d, p0, la;
+};
+__device__ __forceinline__ void near_accum(TileSums& s, float M, float c, float rho0, float zt, float zd) {
+    const NearTerm tm = near_term(M, c, zt, zd);
+    const float w0 = rho0 * tm.A - tm.Dl;
+    const bool lin = !tm.same && w0 > 0.f;
+    s.x += tm.A;
+    s.d += tm.Dl;
+    s.p0 += tm.same ? tm.A : 0.f;
+    s.w += lin ? w0 : 0.f;
+    s.la += lin ? tm.A : 0.f;
+}
+__device__ __forceinline__ void far_accum(TileSums& s, const WSpec& far_ws, float zt, float zd) {
+    s.x += exp2_fast((zt - far_ws.mA) * far_ws.c);
+    s.w += elem_weight(far_ws, zt, zd);
+}
+// The tile's sums over the wave, the same value in every lane.
+__device__ __forceinline__ TileSums wave_tile_sums(TileSums s, bool near) {
+    s.x = wave_sum(s.x);
+    s.w = wave_sum(s.w);
+    if (near) {
+        s.d = wave_sum(s.d);
+        s.p0 = wave_sum(s.p0);
+        s.la = wave_sum(s.la);
+    }
+    return s;
+}
+__device__ __forceinline__ float tile_sum_at(const TileSums& s, int q) {
+    return q == kSumX ? s.x : q == kSumW ? s.w : q == kSumD ? s.d : q == kSumP0 ? s.p0 : s.la;
+}
+// Weight of a tile at the exact rho (near) from its sums at rho0; far: the sum itself.
+__device__ __forceinline__ double tile_weight(const float* v, bool near, double rho, float rho0) {
+    double w = (double)v[kSumW];
+    if (near) w += fmax(rho, 0.0) * (double)v[kSumP0] + (rho - (double)rho0) * (double)v[kSumLA];
+    return w > 0.0 ? w : 0.0;
+}
+
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, double* s_buf) {
     constexpr int kVec = Elem<DT>::kVec;
@@ -1266,8 +1415,11 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
         return;
     }
     const void* drow = row_ptr<DT>(p.draft, (long long)b * n + d.k, V);
-    unsigned* dres = reinterpret_cast<unsigned*>(p.dres) + (size_t)b * NT;
-    unsigned* dp = reinterpret_cast<unsigned*>(p.dp) + (size_t)b * NT;
+    const bool near = d.kind == kDrawResidualNear;
+    const float M = near ? fmaxf(d.m_t, d.m_d) : d.m_t;  // the target row's scale
+    const int nq = near ? kDrawSums : 2;                  // sums handed over per tile
+    unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
+    const WSpec far_ws{kWResFar, d.c, d.m_t, d.m_d, d.lq, 0.f};
 
     // chunk c: tiles [tile0, tile0 + cnt).  Wave w owns kTilesPerWave whole tiles
     // (lane l reads vectors l, l + 64, ... of each, coalesced), so every tile sum
@@ -1297,31 +1449,34 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     unsigned dep = 0u;
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
-        float ar = 0.f, ap = 0.f;
+        // absent elements read -inf on both rows: every term is 0
+        TileSums ts{0.f, 0.f, 0.f, 0.f, 0.f};
+        if (near) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            float zt[kVec], zd[kVec];
-            unpack<DT>(rt[i][u], zt);
-            unpack<DT>(rd[i][u], zd);
+            for (int u = 0; u < kU; ++u) {
+                float zt[kVec], zd[kVec];
+                unpack<DT>(rt[i][u], zt);
+                unpack<DT>(rd[i][u], zd);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                ar += w_residual(d, zt[e], zd[e]);  // absent elements read -inf: weight 0
-                ap += w_target(d, zt[e]);
+                for (int e = 0; e < kVec; ++e) near_accum(ts, M, d.c, d.rho0, zt[e], zd[e]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                float zt[kVec], zd[kVec];
+                unpack<DT>(rt[i][u], zt);
+                unpack<DT>(rd[i][u], zd);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) far_accum(ts, far_ws, zt[e], zd[e]);
             }
         }
-        ar = wave_sum(ar);
-        ap = wave_sum(ap);
+        ts = wave_tile_sums(ts, near);
         const int t = wv * kTilesPerWave + i;
-        if (lane == 0 && t < cnt) {
-            dep ^= xchg32(dres + tile0 + t, __float_as_uint(ar));
-            dep ^= xchg32(dp + tile0 + t, __float_as_uint(ap));
-        }
+        if (lane < nq && t < cnt) dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(tile_sum_at(ts, lane)));
     }
-    if (lane == 0) {
-        // this wave's exchanges have been performed before the workgroup arrives
-        asm volatile("" ::"v"(dep));
-        __builtin_amdgcn_s_waitcnt(0);
-    }
+    // this wave's exchanges have been performed before the workgroup arrives
+    asm volatile("" ::"v"(dep));
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ int s_last;
     if (tid == 0) s_last = (arrive(&p.cnt[b], 0ull) == (unsigned)p.NCd - 1u);
@@ -1329,63 +1484,58 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     if (!s_last) return;
 
     // last workgroup: collect (and reset) the per-tile sums of the whole row pair
-    float* s_wr = reinterpret_cast<float*>(s_buf);
-    float* s_wp = s_wr + kMaxTiles;
-    double mr = 0.0, mp = 0.0;
-    for (int i = tid; i < NT; i += kThreads) {
-        const float r = __uint_as_float(xchg32(dres + i, 0u));
-        const float q = __uint_as_float(xchg32(dp + i, 0u));
-        s_wr[i] = r;
-        s_wp[i] = q;
-        mr += (double)r;
-        mp += (double)q;
-    }
-    __shared__ double s_zr[kWaves], s_zp[kWaves];
-    __shared__ double s_t;
-    __shared__ int s_use_p;
-    {
-        const int lane = tid & 63, w = tid >> 6;
-        double ir = mr, ip = mp;
+    constexpr int kTPT = kMaxTiles / kThreads;  // tiles per thread, at most
+    float v[kTPT][kDrawSums];
+    double X = 0.0, D = 0.0;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double o1 = __shfl_up(ir, off, 64), o2 = __shfl_up(ip, off, 64);
-            if (lane >= off) {
-                ir += o1;
-                ip += o2;
-            }
-        }
-        if (lane == 63) {
-            s_zr[w] = ir;
-            s_zp[w] = ip;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double Zr = 0.0, Zp = 0.0;
-            for (int k = 0; k < kWaves; ++k) {
-                Zr += s_zr[k];
-                Zp += s_zp[k];
-            }
-            s_use_p = !(Zr > 0.0);
-            s_t = (double)d.u * (s_use_p ? Zp : Zr);
-            if (s_use_p && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
-        }
-        __syncthreads();
+    for (int r = 0; r < kTPT; ++r) {
+        const int i = tid + r * kThreads;
+#pragma unroll
+        for (int q = 0; q < kDrawSums; ++q)
+            v[r][q] = (i < NT && q < nq) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
+        X += (double)v[r][kSumX];
+        D += (double)v[r][kSumD];
     }
-    const bool use_p = s_use_p;  // no residual mass left after rounding: draw from p_k
-    const float* sw = use_p ? s_wp : s_wr;
-    const double t = s_t;
-    const Pick pk = block_first_crossing(NT, t, [&](int i) { return (double)sw[i]; });
+    block_sum2_all(X, D);
+    const double rho = near ? D / X : 0.0;
+    double Zr = 0.0, Zp = 0.0;
+#pragma unroll
+    for (int r = 0; r < kTPT; ++r) {
+        const int i = tid + r * kThreads;
+        if (i < NT) {
+            const double w = tile_weight(v[r], near, rho, d.rho0);
+            s_buf[i] = w;
+            Zr += w;
+            Zp += (double)v[r][kSumX];
+        }
+    }
+    block_sum2_all(Zr, Zp);
+    const bool use_p = !(Zr > 0.0);  // no residual mass left after rounding: draw from p_k
+    if (use_p) {
+#pragma unroll
+        for (int r = 0; r < kTPT; ++r) {
+            const int i = tid + r * kThreads;
+            if (i < NT) s_buf[i] = (double)v[r][kSumX];
+        }
+        if (tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
+    }
+    __syncthreads();
+    const double t = (double)d.u * (use_p ? Zp : Zr);
+    const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_buf[i]; });
     int tile = pk.i;
     bool take_last = false;
     if (tile < 0) {  // t at or past the total through rounding: the last tile with mass
         int my_last = -1;
         for (int i = tid; i < NT; i += kThreads)
-            if (sw[i] > 0.f) my_last = i;
+            if (s_buf[i] > 0.0) my_last = i;
         const int lt = block_max_all(my_last);
         tile = lt < 0 ? 0 : lt;
         take_last = true;
     }
-    const int y = scan_tile<DT, ALIGNED>(d, !use_p, trow, drow, V, tile, pk.before, t, take_last);
+    const WSpec ws = use_p  ? WSpec{kWTarget, d.c, M, 0.f, 0.f, 0.f}
+                     : near ? WSpec{kWResNear, d.c, M, 0.f, 0.f, (float)rho}
+                            : far_ws;
+    const int y = scan_tile<DT, ALIGNED>(ws, trow, drow, V, tile, pk.before, t, take_last);
     // row L's tile partials (written by the stats pass, unused here): leave them zero
     for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;
     if (tid == 0) {
@@ -1397,10 +1547,11 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
 }
 
 // One workgroup per (sequence, chunk), sequence-major.  The aligned kernel is
-// held to 80 VGPRs (6 waves per SIMD) without spilling; the element-wise
-// unaligned one is left to the compiler.
+// held to 96 VGPRs (5 waves per SIMD; the near residual's five tile sums do not
+// fit 80 without spilling); the element-wise unaligned one is left to the
+// compiler.
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_draw(DrawParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void k_draw(DrawParams p) {
     __shared__ double s_buf[kMaxTiles];
     draw_item<DT, true>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
 }
@@ -1478,6 +1629,112 @@ __global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, 
     const float m = s_ms.m;
     const float inv_s = (float)(1.0 / (double)s_ms.s);
     for (int i = threadIdx.x; i < V; i += kThreads) o[i] = exp2_fast((load_elem<DT>(row, i) - m) * c) * inv_s;
+}
+
+// --------------------------------------------------------------- debug residual weights
+
+// Parity/debug only: for row pair r (target row r, draft row r, temperature
+// temp[r] > 0), the residual weights a draw after a rejection would scan, formed
+// by the draw pass's own code: the descriptor as the decision forms it (from
+// this kernel's own row statistics), the tile sums as the draw chunks form them
+// (wave w takes tiles w, w + kWaves, ..., lane l the same elements of a tile),
+// rho as the last workgroup forms it, then every element's weight.  Outputs:
+// w_out[r][V] the element weights, tile_out[r][NT] (nullable) the tiles'
+// weights at rho (the numbers the tile pick is made on), info_out[r][4]
+// (nullable) {1 near / 0 far, rho0, rho, sum of tile weights}.
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target, const void* draft, const float* temp,
+                                                             int V, int NT, float* w_out, double* tile_out,
+                                                             float* info_out) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kTile = kThreads * kVec;
+    constexpr int kU = kThreads / 64;
+    constexpr int kTPT = kMaxTiles / kThreads;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const void* trow = row_ptr<DT>(target, r, V);
+    const void* drow = row_ptr<DT>(draft, r, V);
+    const float T = temp[r];
+    if (!(T > 0.f)) {
+        for (int i = tid; i < V; i += kThreads) w_out[(size_t)r * V + i] = __builtin_nanf("");
+        return;
+    }
+    const float c = exp2_scale(T);
+    __shared__ MS s_t, s_d;
+    const MS a = wg_softmax_tiles<DT, ALIGNED>(trow, 0, V, c, nullptr);
+    if (tid == 0) s_t = a;
+    __syncthreads();
+    const MS bq = wg_softmax_tiles<DT, ALIGNED>(drow, 0, V, c, nullptr);
+    if (tid == 0) s_d = bq;
+    __syncthreads();
+    const double gap = ((double)s_d.m - (double)s_t.m) * (double)c;
+    const bool near = fabs(gap) <= 32.0;
+    const float rho0 = near ? (float)((double)s_d.s / (double)s_t.s * exp2(gap) - 1.0) : 0.f;
+    const float lq = (float)log2((double)s_t.s / (double)s_d.s);
+    const float M = near ? fmaxf(s_t.m, s_d.m) : s_t.m;
+    const WSpec far_ws{kWResFar, c, s_t.m, s_d.m, lq, 0.f};
+    __shared__ float s_sum[kDrawSums][kMaxTiles];
+    for (int t = w; t < NT; t += kWaves) {
+        TileSums ts{0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float zt[kVec], zd[kVec];
+            const int e0 = t * kTile + (lane + 64 * u) * kVec;
+            load_vec<DT, ALIGNED>(trow, e0, V, zt);
+            load_vec<DT, ALIGNED>(drow, e0, V, zd);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                if (near) near_accum(ts, M, c, rho0, zt[e], zd[e]);
+                else far_accum(ts, far_ws, zt[e], zd[e]);
+            }
+        }
+        ts = wave_tile_sums(ts, near);
+        if (lane < kDrawSums) s_sum[lane][t] = tile_sum_at(ts, lane);
+    }
+    __syncthreads();
+    float v[kTPT][kDrawSums];
+    double X = 0.0, D = 0.0;
+#pragma unroll
+    for (int q = 0; q < kTPT; ++q) {
+        const int i = tid + q * kThreads;
+#pragma unroll
+        for (int k = 0; k < kDrawSums; ++k) v[q][k] = (i < NT && (near || k < 2)) ? s_sum[k][i] : 0.f;
+        X += (double)v[q][kSumX];
+        D += (double)v[q][kSumD];
+    }
+    block_sum2_all(X, D);
+    const double rho = near ? D / X : 0.0;
+    double Z = 0.0, unused = 0.0;
+#pragma unroll
+    for (int q = 0; q < kTPT; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < NT) {
+            const double tw = tile_weight(v[q], near, rho, rho0);
+            if (tile_out) tile_out[(size_t)r * NT + i] = tw;
+            Z += tw;
+        }
+    }
+    block_sum2_all(Z, unused);
+    const WSpec ws = near ? WSpec{kWResNear, c, M, 0.f, 0.f, (float)rho} : far_ws;
+    for (int i = tid; i < V; i += kThreads)
+        w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
+    if (info_out && tid == 0) {
+        info_out[(size_t)r * 4 + 0] = near ? 1.f : 0.f;
+        info_out[(size_t)r * 4 + 1] = rho0;
+        info_out[(size_t)r * 4 + 2] = (float)rho;
+        info_out[(size_t)r * 4 + 3] = (float)Z;
+    }
+}
+
+hipError_t launch_residual_debug(const void* target, const void* draft, Dt dt, const float* temp, int rows, int V,
+                                 int NT, float* w_out, double* tile_out, float* info_out, bool aligned,
+                                 hipStream_t s) {
+    const dim3 grid((unsigned)rows), block(kThreads);
+#define SV_RD(DT_, AL_) \
+    hipLaunchKernelGGL((k_residual_debug<DT_, AL_>), grid, block, 0, s, target, draft, temp, V, NT, w_out, tile_out, info_out)
+    if (dt == kBF16) { if (aligned) SV_RD(kBF16, true); else SV_RD(kBF16, false); }
+    else { if (aligned) SV_RD(kF32, true); else SV_RD(kF32, false); }
+#undef SV_RD
+    return hipGetLastError();
 }
 
 // --------------------------------------------------------------- launches

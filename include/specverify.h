@@ -351,6 +351,26 @@ sv_status_t sv_lmhead_logits_debug(const void *hidden, const void *weight, int M
 sv_status_t sv_softmax_rows_debug(const void *logits, sv_dtype_t dt, const float *temperature,
                                   int rows, int V, float *probs_out, void *stream);
 
+/* Parity/debug only (not on the hot path): the residual weights a draw after a
+ * rejection scans, for `rows` row pairs (target_rows[r], draft_rows[r], each
+ * [V] dt, temperature[r] > 0), formed by the draw pass's own device code.
+ * After a rejection the token is drawn from max(0, p - q) normalised (the first
+ * reference of "Accelerating Sonar through speculation"; that page's
+ * Target-draft section, decode paragraph, compares the full distributions).
+ *   weights_out      [rows][V] float: each token's weight, up to a factor common
+ *                    to the row (NaN for rows with T <= 0 or NaN)
+ *   tile_weights_out [rows][NT] double, nullable: the per-tile weights the tile
+ *                    pick uses (NT = ceil(V / 2048) for bf16, ceil(V / 1024) for f32)
+ *   info_out         [rows][4] float, nullable: {1 if both rows were scaled by one
+ *                    common maximum (near form) else 0, rho0, rho, sum of the
+ *                    tile weights}
+ * The row statistics come from this call's own reduction of each row, so the
+ * tile weights may differ from a verify call's in the last digits; the element
+ * weights do not depend on them. */
+sv_status_t sv_residual_weights_debug(const void *target_rows, const void *draft_rows, sv_dtype_t dt,
+                                      const float *temperature, int rows, int V, float *weights_out,
+                                      double *tile_weights_out, float *info_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     for f in ["spec_verify_sample", "spec_verify_greedy", "mtp_shift_insert", "sv_workspace_bytes",
               "sv_workspace_clear", "sv_status_string", "sv_last_hip_error", "sv_softmax_rows_debug",
               "spec_verify_greedy_mtp", "spec_verify_sample_mtp", "spec_verify_sample_ex", "sv_sample_rows",
-              "spec_verify_greedy_lmhead", "sv_lmhead_logits_debug"]:
+              "spec_verify_greedy_lmhead", "sv_lmhead_logits_debug", "sv_residual_weights_debug"]:
         assert f in names, names
 
 
@@ -237,3 +237,17 @@ def test_lmhead_host_checks():
     assert f(C.c_void_p((1 << 40) + 4), _addr(9), 4, 64, 10, _addr(3), NULL) == sv.SV_EALIGN
     assert f(_addr(0), _addr(9), 4, 64, 10, NULL, NULL) == sv.SV_EINVAL
 
+
+
+def test_residual_debug_host_checks():
+    f = sv.lib().sv_residual_weights_debug
+    a = lambda **kw: [kw.get(k, v) for k, v in dict(t=_addr(0), d=_addr(1), dt=sv.SV_BF16, T=_addr(2), rows=4,
+                                                     V=1000, w=_addr(3), tw=NULL, info=NULL, s=NULL).items()]
+    assert f(*a(rows=0)) == sv.SV_OK
+    assert f(*a(rows=-1)) == sv.SV_EINVAL
+    assert f(*a(V=0)) == sv.SV_EINVAL
+    assert f(*a(dt=3)) == sv.SV_EINVAL
+    assert f(*a(d=NULL)) == sv.SV_EINVAL
+    assert f(*a(w=NULL)) == sv.SV_EINVAL
+    assert f(*a(tw=C.c_void_p((1 << 40) + 4))) == sv.SV_EALIGN
+    assert f(*a(V=1024 * 2048 + 1)) == sv.SV_EINVAL

@@ -1,0 +1,131 @@
+"""GPU parity of the residual draw when the draft is almost the target, so the
+residual mass Z = sum max(0, p - q) is small and any rounding in the weights is
+magnified by 1 / Z.
+
+Two kinds of row pairs (V = 128256 bf16, the llama-vocab recipe for the target):
+  - "handful": the draft row equals the target row except a few tokens, whose
+    logits move by up to +-3 (the draft raises the drafted token, so it is
+    rejected when its uniform is 1 - 2^-24);
+  - "sigma": draft = bf16(target + N(0, sigma^2)) for sigma in {0.003, 0.01,
+    0.03}; the drafted token is the one with the smallest ratio p / q (at the
+    token with the largest q - p the ratio can lie within 1e-10 of 1, where no
+    binary32 uniform below 1 rejects it).
+
+For each pair the test reports the maximum normalised CDF error of the weights
+the draw pass scans, max_i |C_gpu(i) / Z_gpu - C(i) / Z| with C the running sum
+in ascending index and the exact weights max(0, p - q) from the oracle's double
+softmax, and it must stay below the 1e-5 near-tie band.  Then whole verify calls
+with a forced rejection at slot 0 and stratified final uniforms are compared
+with the oracle decision by decision: no hard mismatch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_08_amd as sv
+from draft_token_verification_08_amd import synth
+from svcompare import compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+V = 128256
+U_REJECT = 1.0 - 2.0 ** -24
+
+
+def _target_rows(seed, rows):
+    d = synth.make(2, seed, device=DEV, B=rows, V=V, n=0)
+    return d["target"][:, 0].contiguous()
+
+
+def _pairs(kind, seed, rows):
+    """(target [rows, V], draft [rows, V], drafted token [rows]) as bf16 rows."""
+    zt = _target_rows(seed, rows)
+    g = torch.Generator(device=DEV).manual_seed(seed + 7919)  # not the target's stream
+    if kind == "handful":
+        zd = zt.clone()
+        x = torch.empty(rows, dtype=torch.int32)
+        for r in range(rows):
+            idx = torch.randperm(V, generator=g, device=DEV)[:5]
+            deltas = torch.tensor([1.5, -1.0, 0.5, -3.0, 3.0], device=DEV)
+            zd[r, idx] = (zt[r, idx].float() + deltas).to(torch.bfloat16)
+            x[r] = int(idx[0])  # raised by the draft: q(x) > p(x)
+        return zt, zd, x
+    sigma = float(kind)
+    noise = torch.randn((rows, V), generator=g, device=DEV)
+    zd = (zt.float() + sigma * noise).to(torch.bfloat16)
+    return zt, zd, None
+
+
+def _oracle_residual(oracle, zt, zd, T):
+    """Exact residual weights max(0, p - q) (double) of one row pair."""
+    _, p = oracle.softmax_row(synth.host_logits(zt), T)
+    _, q = oracle.softmax_row(synth.host_logits(zd), T)
+    return np.maximum(p - q, 0.0), p, q
+
+
+CASES = [("handful", 0.7), ("handful", 1.0), ("0.003", 0.7), ("0.01", 0.7), ("0.03", 0.7)]
+
+
+@pytest.mark.parametrize("kind,T", CASES)
+def test_residual_weights_cdf_error(oracle, kind, T):
+    rows = 4
+    zt, zd, _ = _pairs(kind, 1000 + CASES.index((kind, T)), rows)
+    temp = torch.full((rows,), T, device=DEV)
+    w, tw, info = sv.sv_residual_weights_debug(zt, zd, temp)
+    torch.cuda.synchronize()
+    w = w.cpu().numpy().astype(np.float64)
+    tw = tw.cpu().numpy()
+    info = info.cpu().numpy()
+    worst = worst_tile = 0.0
+    for r in range(rows):
+        wo, p, q = _oracle_residual(oracle, zt[r], zd[r], T)
+        Zo = wo.sum()
+        assert Zo > 0, "the row pair must differ"
+        assert np.isfinite(w[r]).all() and (w[r] >= 0).all()
+        Cg = np.cumsum(w[r]) / w[r].sum()
+        Co = np.cumsum(wo) / Zo
+        err = np.abs(Cg - Co).max()
+        # the tile pick: cumulative tile weights against the exact CDF at tile ends
+        tile = 2048
+        ends = np.minimum(np.arange(1, tw.shape[1] + 1) * tile, V) - 1
+        Ct = np.cumsum(tw[r]) / tw[r].sum()
+        err_t = np.abs(Ct - Co[ends]).max()
+        worst, worst_tile = max(worst, err), max(worst_tile, err_t)
+        print(f"\n{kind} T={T} row {r}: Z={Zo:.3e} near={int(info[r, 0])} rho0={info[r, 1]:.3e} "
+              f"rho={info[r, 2]:.3e} max normalised CDF error: elements {err:.2e}, tile ends {err_t:.2e}")
+    assert worst < 1e-5 and worst_tile < 1e-5, (worst, worst_tile)
+
+
+@pytest.mark.parametrize("kind,T", CASES)
+def test_forced_rejection_draws(oracle, kind, T):
+    """B sequences, n = 1, L = 1, u[b][0] = 1 - 2^-24 (rejection unless p(x) >= q(x)),
+    stratified final uniforms over 8 row pairs."""
+    pairs, B = 8, 256
+    zt, zd, x = _pairs(kind, 2000 + CASES.index((kind, T)), pairs)
+    if x is None:
+        x = torch.empty(pairs, dtype=torch.int32)
+        for r in range(pairs):
+            _, p, q = _oracle_residual(oracle, zt[r], zd[r], T)
+            x[r] = int(np.argmin(np.where(q > 0, p / np.where(q > 0, q, 1.0), np.inf)))
+    rep_of = np.arange(B) % pairs
+    ri = torch.as_tensor(rep_of, device=DEV)
+    target = torch.stack([zt[ri], zt[ri]], dim=1).contiguous()   # slot 1 (the bonus row) unused after a rejection
+    draft = zd[ri].unsqueeze(1).contiguous()
+    toks = x.to(DEV)[ri].view(B, 1).contiguous()
+    lens = torch.ones(B, dtype=torch.int32, device=DEV)
+    temp = torch.full((B,), T, device=DEV)
+    u = torch.empty((B, 2), device=DEV)
+    u[:, 0] = U_REJECT
+    u[:, 1] = torch.as_tensor((np.arange(B) // pairs + 0.5) / (B // pairs), dtype=torch.float32, device=DEV)
+    fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc, emi = sv.spec_verify_sample(target, draft, toks, lens, temp, u, err_flags=fl)
+    torch.cuda.synchronize()
+    acc, emi = acc.cpu().numpy(), emi.cpu().numpy()
+    ora = oracle.verify_sample(synth.host_logits(target), synth.host_logits(draft), toks.cpu().numpy(),
+                               lens.cpu().numpy(), temp.cpu().numpy(), u.cpu().numpy(), threads=16)
+    assert (ora["accepted_len"] == 0).all()
+    rep = compare(acc, emi, ora, lens.cpu().numpy(), temp.cpu().numpy(), 1)
+    Z = [_oracle_residual(oracle, zt[r], zd[r], T)[0].sum() for r in range(pairs)]
+    print(f"\n{kind} T={T}: residual mass {min(Z):.2e}..{max(Z):.2e}; {rep}")
+    assert rep.hard == 0, rep
+    assert int(fl.item()) & sv.SV_FLAG_ZERO_RESIDUAL == 0
