@@ -127,6 +127,54 @@ def test_greedy_ties_everywhere(oracle):
     assert compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), None, n).hard == 0
 
 
+def _signed_zero_rows(rows, V, seed):
+    """Rows whose maximum is 0, held by -0.0 at a low index and +0.0 at a higher
+    index in a later vocabulary chunk (every other entry negative): the lowest
+    index (the -0.0) is the greedy choice."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    z = -torch.rand((rows, V), generator=g, device=DEV) - 0.5
+    lo = torch.randint(0, V // 4, (rows,), generator=g, device=DEV)
+    hi = torch.randint(V // 2, V, (rows,), generator=g, device=DEV)
+    r = torch.arange(rows, device=DEV)
+    z[r, lo] = -0.0
+    z[r, hi] = 0.0
+    # every third row the other way round (+0.0 first): also the lower index wins
+    z[r[::3], lo[::3]] = 0.0
+    z[r[::3], hi[::3]] = -0.0
+    return z, lo
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_greedy_signed_zero_maximum_across_chunks(oracle, dt):
+    """B (n+1) < 1024 splits every row over several chunks: -0.0 and +0.0 in
+    different chunks compare equal, so the chunk merge must keep the lower index
+    (spec_verify_greedy, T = 0 inside spec_verify_sample, and sv_sample_rows)."""
+    B, n, V = 24, 4, 128256
+    z, lo = _signed_zero_rows(B * (n + 1), V, 11)
+    z = z.view(B, n + 1, V).to(dt)
+    lo = lo.view(B, n + 1).cpu()
+    x = lo[:, :n].clone().to(torch.int32)
+    x[::2, 2] = (x[::2, 2] + 1) % V                       # some mismatches
+    d = dict(target=z.contiguous(), draft_tokens=x.to(DEV), n=n, B=B,
+             draft_lens=torch.full((B,), n, dtype=torch.int32, device=DEV))
+    acc, emi, fl = run_greedy(d)
+    ora = oracle_greedy(oracle, d)
+    rep = compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), None, n)
+    assert rep.hard == 0, rep
+    assert np.array_equal(ora["emitted"][:, 0], lo[:, 0].numpy())
+    # the T = 0 rule inside the sampling call
+    d2 = dict(d, draft=z[:, :n].contiguous(), temperature=torch.zeros(B, device=DEV),
+              uniforms=torch.rand((B, n + 1), device=DEV))
+    acc2, emi2, _, _ = run_sample(d2)
+    assert np.array_equal(acc2, acc) and np.array_equal(emi2, emi)
+    # one row per sequence at B = 256 (4 chunks per row), T = 0
+    rows, lo_r = _signed_zero_rows(256, V, 12)
+    tok = sv.sv_sample_rows(rows.to(dt).view(256, 1, V).contiguous(), torch.zeros(256, device=DEV),
+                            torch.rand(256, device=DEV))
+    _sync()
+    assert np.array_equal(tok.cpu().numpy(), lo_r.cpu().numpy())
+
+
 # ------------------------------------------------------------------ sampling
 
 SMALL = [
@@ -151,16 +199,15 @@ def test_sample_parity_small(oracle, cid, B, V, n, seed):
     assert fl == seq_flags_or(ora)
 
 
-@pytest.mark.parametrize("cid,nseq", [(2, 64), (4, 128), (5, 96), (6, 64)])
-def test_sample_parity_full_size(oracle, cid, nseq):
-    """Full-size workloads; the oracle checks a sample of sequences."""
+@pytest.mark.parametrize("cid", [2, 4, 5, 6])
+def test_sample_parity_full_size(oracle, cid):
+    """Full-size workloads; the oracle checks every sequence of the batch."""
     d = synth.make(cid, cid * 101, device=DEV)
     acc, emi, lse, fl = run_sample(d)
     B = d["B"]
-    seqs = np.sort(np.random.default_rng(cid).choice(B, size=min(nseq, B), replace=False))
-    ora = oracle_sample(oracle, d, seqs)
-    rep = compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), d["temperature"].cpu().numpy(), d["n"], seqs)
-    err = check_lse(lse, ora, seqs)
+    ora = oracle_sample(oracle, d)
+    rep = compare(acc, emi, ora, d["draft_lens"].cpu().numpy(), d["temperature"].cpu().numpy(), d["n"])
+    err = check_lse(lse, ora)
     assert rep.hard == 0, rep
     print(f"\nconfig {cid} B={B}: {rep}; max |dlse|={err:.2e}; mean accepted {acc.mean():.3f}")
     # invariants on every sequence
@@ -177,7 +224,7 @@ def test_law_v8_chi_square_on_gpu(oracle):
     and its emitted marginals follow the target rows."""
     crit = st.chi2.ppf(1 - 1e-3, 7)
     fails = 0
-    for seed in range(4):
+    for seed in range(20):
         h = synth.make_law_case(seed, 200_000, V=8, n=4, T=1.0)
         d = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in h.items()}
         acc, emi, lse, fl = run_sample(d)
@@ -192,7 +239,8 @@ def test_law_v8_chi_square_on_gpu(oracle):
             obs = np.bincount(emi[reached, j], minlength=8)
             exp = reached.sum() * p[j]
             fails += (((obs - exp) ** 2 / exp).sum() > crit)
-    assert fails <= 1
+    # 100 tests at alpha = 1e-3: more than 2 failures has probability < 2e-4
+    assert fails <= 2, fails
 
 
 def test_padding_rows_are_not_read(oracle):
