@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     prepare_spec_verify_greedy_lmhead, prepare_spec_verify_sample_ex, prepare_spec_verify_sample_mtp,
     prepare_sv_sample_rows, prepare_spec_verify_tree_greedy,
     spec_verify_greedy, spec_verify_greedy_lmhead, spec_verify_tree_greedy, spec_verify_greedy_mtp, spec_verify_sample, sv_lmhead_logits_debug,
-    spec_verify_sample_ex, spec_verify_sample_mtp, sv_sample_rows, draft_row_stats, sv_residual_weights_debug, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
+    spec_verify_sample_ex, spec_verify_sample_ex_noalloc, spec_verify_sample_mtp, sv_sample_rows, draft_row_stats, sv_residual_weights_debug, sv_softmax_rows_debug, sv_workspace_bytes, sv_workspace_clear,
 )

@@ -70,6 +70,9 @@ def lib():
     L.spec_verify_sample_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i,
                                         vp, sz, vp]
     L.spec_verify_sample_ex.restype = i
+    L.spec_verify_sample_ex_noalloc.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp,
+                                                i, vp]
+    L.spec_verify_sample_ex_noalloc.restype = i
     L.sv_sample_rows.restype = i
     L.spec_verify_greedy_lmhead.argtypes = [vp, vp, i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_greedy_lmhead.restype = i
@@ -382,6 +385,48 @@ def spec_verify_sample_ex(target_logits, draft_logits, draft_tokens, draft_lens,
           _ptr(draft_lens), _ptr(temperature), _ptr(uniforms), _ptr(draft_stats), B, n, V, _ptr(accepted_len),
           _ptr(emitted), _ptr(row_lse), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src), _ptr(hidden_dst), H,
           _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    return accepted_len, emitted
+
+
+def spec_verify_sample_ex_noalloc(target_logits, draft_logits, draft_tokens, draft_lens, temperature, uniforms, *,
+                                  draft_stats=None, tokens=None, hidden_src=None, hidden_dst=None,
+                                  accepted_len=None, emitted=None, row_lse=None, err_flags=None, stream=None):
+    """spec_verify_sample_ex with the library's own static device workspace (no
+    workspace argument, no allocation inside the library; outputs not passed in
+    are still allocated here).  Returns (accepted_len, emitted)."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    if draft_stats is not None:
+        _check(draft_stats, "draft_stats", torch.float32, (B, n, 2), dev)
+    H = 0
+    if tokens is not None:
+        H = _mtp_args(tokens, hidden_src, hidden_dst, B, n1, dev)
+    elif hidden_src is not None or hidden_dst is not None:
+        raise ValueError("hidden buffers need the token buffer")
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n1), dtype=torch.int32, device=dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    if row_lse is not None:
+        _check(row_lse, "row_lse", torch.float32, (B, 2 * n + 1), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    with torch.cuda.device(dev):
+        _call("spec_verify_sample_ex_noalloc", _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+              _ptr(draft_lens), _ptr(temperature), _ptr(uniforms), _ptr(draft_stats), B, n, V,
+              _ptr(accepted_len), _ptr(emitted), _ptr(row_lse), _ptr(err_flags), _ptr(tokens), _ptr(hidden_src),
+              _ptr(hidden_dst), H, _stream(stream, dev))
     return accepted_len, emitted
 
 

@@ -42,6 +42,7 @@ def build(out: str = LIB, verbose: bool = False, defines=(), objdir: str | None 
     k_obj = os.path.join(objdir, "sv_kernels.o")
     l_obj = os.path.join(objdir, "sv_lmhead.o")
     a_obj = os.path.join(objdir, "sv_api.o")
+    n_obj = os.path.join(objdir, "sv_noalloc.o")
     logs = []
     dflags = [f"-D{d}" for d in defines]
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
@@ -49,8 +50,10 @@ def build(out: str = LIB, verbose: bool = False, defines=(), objdir: str | None 
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
                       os.path.join(CSRC, "sv_lmhead.hip"), "-o", l_obj]))
     logs.append(_run([HIPCC, *COMMON, *dflags, "-c", os.path.join(CSRC, "sv_api.cpp"), "-o", a_obj]))
+    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *dflags, "-x", "hip", "-c",
+                      os.path.join(CSRC, "sv_noalloc.hip"), "-o", n_obj]))
     tmp = out + ".tmp"
-    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, l_obj, a_obj, "-o", tmp]))
+    logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, l_obj, a_obj, n_obj, "-o", tmp]))
     os.replace(tmp, out)
     if verbose:
         print("\n".join(l for l in logs if l))

@@ -376,6 +376,24 @@ sv_status_t verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_
 
 }  // namespace
 
+namespace sv {
+
+sv_status_t hip_status(hipError_t e) { return hip_fail(e); }
+
+sv_status_t sample_ex(const void* target_logits, const void* draft_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                      const int32_t* draft_lens, const float* temperature, const float* uniforms,
+                      const float* draft_stats, int B, int n, int V, int32_t* accepted_len, int32_t* emitted,
+                      float* row_lse, uint32_t* err_flags, int32_t* tokens, const void* hidden_src, void* hidden_dst,
+                      int H, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!tokens && (hidden_src || hidden_dst)) return SV_EINVAL;
+    const MtpArgs m{tokens, hidden_src, hidden_dst, H};
+    return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
+                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream,
+                         tokens ? &m : nullptr, draft_stats);
+}
+
+}  // namespace sv
+
 extern "C" {
 
 sv_status_t spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
@@ -409,11 +427,9 @@ sv_status_t spec_verify_sample_ex(const void* target_logits, const void* draft_l
                                   uint32_t* err_flags, int32_t* tokens, const void* hidden_src,
                                   void* hidden_dst, int H, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-    if (!tokens && (hidden_src || hidden_dst)) return SV_EINVAL;
-    const MtpArgs m{tokens, hidden_src, hidden_dst, H};
-    return verify_sample(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms, B, n,
-                         V, accepted_len, emitted, row_lse, err_flags, workspace, workspace_bytes, stream,
-                         tokens ? &m : nullptr, draft_stats);
+    return sv::sample_ex(target_logits, draft_logits, dt, draft_tokens, draft_lens, temperature, uniforms,
+                         draft_stats, B, n, V, accepted_len, emitted, row_lse, err_flags, tokens, hidden_src,
+                         hidden_dst, H, workspace, workspace_bytes, stream);
 }
 
 sv_status_t spec_verify_greedy(const void* target_logits, sv_dtype_t dt, const int32_t* draft_tokens,

@@ -160,6 +160,16 @@ struct LmParams {
 };
 constexpr int kLmBK = 64;      // K elements per pipeline stage of the projection
 
+// Host layer (sv_api.cpp): the body of spec_verify_sample_ex() on a given
+// workspace, and the SV_EHIP status for a HIP error (its text recorded for
+// sv_last_hip_error()).
+sv_status_t sample_ex(const void* target_logits, const void* draft_logits, sv_dtype_t dt, const int32_t* draft_tokens,
+                      const int32_t* draft_lens, const float* temperature, const float* uniforms,
+                      const float* draft_stats, int B, int n, int V, int32_t* accepted_len, int32_t* emitted,
+                      float* row_lse, uint32_t* err_flags, int32_t* tokens, const void* hidden_src, void* hidden_dst,
+                      int H, void* workspace, size_t workspace_bytes, void* stream);
+sv_status_t hip_status(hipError_t e);
+
 // launches (sv_kernels.hip, sv_lmhead.hip); return the hipGetLastError() after the launch
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s);
 hipError_t launch_tree(const StatsParams& p, Dt dt, bool aligned, hipStream_t s);

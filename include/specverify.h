@@ -266,6 +266,28 @@ sv_status_t spec_verify_sample_ex(const void *target_logits, const void *draft_l
                                   void *hidden_dst, int H, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* spec_verify_sample_ex() without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * The workspace is a device array of SV_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU, held until the process ends.  Sizes whose
+ * sv_workspace_bytes(B, n, V, dt) exceed it return SV_EWORKSPACE before anything
+ * is touched (B up to 7358 at n = 8, V = 152064 bf16; 8923 at n = 4, V = 128256).  The first
+ * call on a GPU enqueues a clear of the array (a kernel) on `stream`; every
+ * call leaves it zero-filled again.  All calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (different streams, or threads) race
+ * and give undefined results; order them (one stream, or events).  Arguments,
+ * results and other status codes are those of spec_verify_sample_ex(). */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+sv_status_t spec_verify_sample_ex_noalloc(const void *target_logits, const void *draft_logits,
+                                          sv_dtype_t dt, const int32_t *draft_tokens,
+                                          const int32_t *draft_lens, const float *temperature,
+                                          const float *uniforms, const float *draft_stats, int B, int n,
+                                          int V, int32_t *accepted_len, int32_t *emitted, float *row_lse,
+                                          uint32_t *err_flags, int32_t *tokens, const void *hidden_src,
+                                          void *hidden_dst, int H, void *stream);
+
 /* Standard sampling of one token per sequence from a row chosen on the device.
  *
  * Sequence b draws from logits[b][r_b][:] with r_b = row_index[b] (clamped to

@@ -251,3 +251,17 @@ def test_residual_debug_host_checks():
     assert f(*a(w=NULL)) == sv.SV_EINVAL
     assert f(*a(tw=C.c_void_p((1 << 40) + 4))) == sv.SV_EALIGN
     assert f(*a(V=1024 * 2048 + 1)) == sv.SV_EINVAL
+
+
+def test_noalloc_size_checks_touch_nothing():
+    """The no-allocation entry point rejects sizes before any device call."""
+    f = sv.lib().spec_verify_sample_ex_noalloc
+    a = lambda **kw: [kw.get(k, v) for k, v in dict(
+        t=_addr(0), d=_addr(9), dt=sv.SV_BF16, x=_addr(1), L=_addr(2), T=_addr(10), u=_addr(11), ds=NULL, B=4, n=4,
+        V=1024, acc=_addr(3), emi=_addr(4), lse=NULL, fl=NULL, tok=NULL, hs=NULL, hd=NULL, H=0, s=NULL).items()]
+    assert f(*a(B=0)) == sv.SV_OK
+    assert f(*a(n=sv.SV_MAX_DRAFT + 1)) == sv.SV_EINVAL
+    assert f(*a(V=0)) == sv.SV_EINVAL
+    assert f(*a(dt=4)) == sv.SV_EINVAL
+    assert f(*a(B=8192, n=8, V=152064)) == sv.SV_EWORKSPACE      # beyond SV_NOALLOC_SCRATCH_BYTES
+    assert sv.sv_workspace_bytes(7358, 8, 152064, sv.SV_BF16) <= 16 << 20 < sv.sv_workspace_bytes(7359, 8, 152064, sv.SV_BF16)
