@@ -30,17 +30,13 @@ constexpr int kDrawTiles = SV_DRAW_TILES;  // draw pass: tiles (kThreads * eleme
 constexpr int kMaxTiles = 1024;      // tiles per row (4 per thread in the draw selections)
 constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
-constexpr int kDrawSums = 5;         // per-tile sums a residual draw chunk hands over
+constexpr int kDrawSums = 4;         // per-tile sums a residual draw chunk hands over
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
 
-// kinds of the final draw of a sequence.  The residual max(0, p_k - q_k) is
-// weighted in one of two forms (see the draw pass): rows whose maxima are close
-// (|m_t - m_d| c <= 32) scale both rows by one common maximum, so that tokens
-// the rows share cancel exactly ("near"); other rows scale each row by its own
-// maximum ("far").
-enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2, kDrawResidualNear = 3 };
+// kinds of the final draw of a sequence
+enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
 
 // One 64-bit slot per (sequence, row slot, vocab chunk), exchanged atomically:
 //   sampling rows: low word chunk max m_c, high word sum over the chunk of 2^((z - m_c) c)
@@ -59,8 +55,7 @@ struct DrawDesc {
     float m_d;      // max of draft row k (residual only)
     float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
-    float rho0;     // near residual: S'_d / S'_t - 1 from the statistics pass, S' = the sums
-                    // scaled by the common maximum max(m_t, m_d)
+    float pad;
 };
 
 // Workspace layout (byte offsets from the workspace base; every region 256-aligned).

@@ -52,6 +52,12 @@
 #ifndef SV_COPY_VECS
 #define SV_COPY_VECS 8  // 16-byte vectors per thread in the hidden-state copy
 #endif
+#ifndef SV_DRAW_NEAR
+#define SV_DRAW_NEAR 1  // residual draws of rows with close maxima use the near form
+#endif
+#ifndef SV_DRAW_WPE
+#define SV_DRAW_WPE 5   // waves per SIMD the draw pass's registers are sized for
+#endif
 
 namespace sv {
 
@@ -631,13 +637,11 @@ __device__ __forceinline__ Pick block_first_crossing(int N, double t, W&& weight
     return Pick{-1, carry};
 }
 
-// 2^x - 1 for |x| <= 1/2: the exponential series in x ln 2 to degree 8, in
-// Horner form (relative error about 1.2e-7 in binary32; exp2(x) - 1 would lose
-// every digit as x -> 0).
+// 2^x - 1 for |x| <= 1/4: the exponential series in x ln 2 to degree 6, in
+// Horner form (truncation below 3e-9 relative, binary32 rounding about 1e-7;
+// exp2(x) - 1 would lose every digit as x -> 0).
 __device__ __forceinline__ float exp2m1_small(float x) {
-    float a = 1.3215486790144305e-06f;
-    a = fmaf(a, x, 1.5252733804059838e-05f);
-    a = fmaf(a, x, 1.5403530393381606e-04f);
+    float a = 1.5403530393381606e-04f;
     a = fmaf(a, x, 1.3333558146428441e-03f);
     a = fmaf(a, x, 9.618129107628477e-03f);
     a = fmaf(a, x, 5.5504108664821576e-02f);
@@ -648,7 +652,9 @@ __device__ __forceinline__ float exp2m1_small(float x) {
 
 // Residual terms of one token when both rows are scaled by one common maximum M
 // (near residual): A = 2^((z_t - M) c), B = 2^((z_d - M) c) and Dl = B - A.
-// With x = (z_d - z_t) c, Dl is formed as A (2^x - 1) when |x| <= 1/2 (no
+// The exponents are formed as fma(z, c, -Mc) with Mc = fl(M c): the rounding of
+// Mc scales every A and B alike, which no ratio or normalised weight sees.
+// With x = (z_d - z_t) c, Dl is formed as A (2^x - 1) when |x| <= 1/4 (no
 // cancellation), else as B - A; a token the two rows share has x = 0 and
 // Dl = 0 exactly.  With S'_t = sum A, S'_d = sum B and rho = S'_d / S'_t - 1,
 //   p - q = A / S'_t - B / S'_d = (rho A - Dl) / (S'_t (1 + rho)),
@@ -657,41 +663,44 @@ struct NearTerm {
     float A, Dl;
     bool same;  // x == 0: the token's logit is the same in both rows
 };
-__device__ __forceinline__ NearTerm near_term(float M, float c, float zt, float zd) {
-    const float A = exp2_fast((zt - M) * c);
+__device__ __forceinline__ NearTerm near_term(float Mc, float c, float zt, float zd) {
+    const float A = exp2_fast(fmaf(zt, c, -Mc));
     const float x = (zd - zt) * c;
     const float small = A * exp2m1_small(x);
-    const float direct = exp2_fast((zd - M) * c) - A;
-    return NearTerm{A, fabsf(x) <= 0.5f ? small : direct, x == 0.f};
+    const float direct = exp2_fast(fmaf(zd, c, -Mc)) - A;
+    return NearTerm{A, fabsf(x) <= 0.25f ? small : direct, x == 0.f};
 }
 
 // How a draw weighs one element (all weights up to a factor common to the row):
 //   kWTarget:   2^((z_t - mA) c), the target's own distribution (bonus draws, and
 //               the fallback when no residual mass is left);
-//   kWResFar:   max(0, 2^((z_t - m_t) c) - 2^((z_d - m_d) c + log2(S_t / S_d))),
-//               each row scaled by its own maximum (mA = m_t);
-//   kWResNear:  max(0, rho A - Dl) of near_term() with M = mA.
+//   kWResFar:   max(0, P - lam Q) with P = 2^((z_t - m_t) c), Q = 2^((z_d - m_d) c),
+//               each row scaled by its own maximum (mA = m_t) and lam the ratio of
+//               their sums (S_t / S_d);
+//   kWResNear:  max(0, rho A - Dl) of near_term() with M = mA (Mc = fl(mA c)).
 enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
 struct WSpec {
     int mode;
     float c;    // log2(e) / T
     float mA;   // maximum the target row is scaled by
     float m_d;  // kWResFar: the draft row's maximum
-    float lq;   // kWResFar: log2(S_t / S_d)
+    float lam;  // kWResFar
     float rho;  // kWResNear
+    float Mc;   // kWResNear: fl(mA c)
 };
+__device__ __forceinline__ float far_p(float mt, float c, float zt) { return exp2_fast((zt - mt) * c); }
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
     if (s.mode == kWTarget) return exp2_fast((zt - s.mA) * s.c);
     if (s.mode == kWResFar) {
-        const float pt = exp2_fast((zt - s.mA) * s.c);
-        const float qd = exp2_fast(fmaf(zd - s.m_d, s.c, s.lq));
-        return fmaxf(pt - qd, 0.f);
+        const float P = far_p(s.mA, s.c, zt);
+        const float Q = far_p(s.m_d, s.c, zd);
+        return fmaxf(fmaf(-s.lam, Q, P), 0.f);
     }
-    const NearTerm t = near_term(s.mA, s.c, zt, zd);
-    return fmaxf(s.rho * t.A - t.Dl, 0.f);
+    const NearTerm t = near_term(s.Mc, s.c, zt, zd);
+    return fmaxf(fmaf(s.rho, t.A, -t.Dl), 0.f);
 }
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
-    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f};
+    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f};
 }
 
 // Scan one tile: returns the element whose running weight (starting at P)
@@ -1184,16 +1193,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
             d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
-            d.rho0 = 0.f;
-            if (k < L) {
-                // near residual when the row maxima lie within 2^32 of each other
-                // on the exponent scale: both rows then fit one common maximum
-                const double gap = ((double)d.m_d - (double)d.m_t) * cd;
-                if (fabs(gap) <= 32.0) {
-                    d.kind = kDrawResidualNear;
-                    d.rho0 = (float)(s_S[n + 1 + k] / s_S[k] * exp2(gap) - 1.0);
-                }
-            }
+            d.pad = 0.f;
             if constexpr (DRAW) s_desc = d;  // drawn below, by this workgroup
             else p.desc[b] = d;
         }
@@ -1312,22 +1312,26 @@ __global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
 // exchange; the last workgroup of the sequence picks the tile holding u * Z with
 // one block prefix scan and scans only that tile.
 //
-// Far residual (row maxima far apart): the tile sums are those of the weights
-// kWResFar and of the target's 2^((z - m_t) c) (the p_k fallback).
-// Near residual: both rows are scaled by M = max(m_t, m_d) (near_term()).  The
-// weights max(0, rho A - Dl) need rho = S'_d / S'_t - 1 exactly, since tokens
-// the rows share carry weight rho A: when the rows are almost equal, rho is the
-// whole residual and the statistics pass's binary32 normalisers do not give it
-// to enough digits.  The chunks therefore sum, per tile, X = sum A and
-// D = sum Dl (so that rho = D / X, in which shared tokens add nothing), and, at
-// the statistics pass's estimate rho0, P0 = sum A over shared tokens and
-// W' = sum (rho0 A - Dl), LA = sum A over the other tokens with rho0 A > Dl.
-// The last workgroup forms each tile's weight at the exact rho as
-//   max(0, rho) P0 + W' + (rho - rho0) LA,
-// which is exact for shared tokens and, for the others, exact unless a token's
-// ratio Dl / A lies between rho0 and rho (a kink of max(0, rho A - Dl) crossed);
-// the tile it picks is then scanned with the exact per-token weights.
-constexpr int kSumX = 0, kSumW = 1, kSumD = 2, kSumP0 = 3, kSumLA = 4;
+// The weights are max(0, P - lam Q), each row scaled by its own maximum
+// (kWResFar), with lam = S_t / S_d taken from the same P and Q terms: the chunks
+// hand over, per tile, sum P, sum Q, and at the statistics pass's estimate lam0
+// the weight sum W = sum max(0, P - lam0 Q) and its slope G = sum Q over the
+// tokens with P > lam0 Q.  The last workgroup forms lam = sum P / sum Q and each
+// tile's weight W - (lam - lam0) G (exact unless a token's P / Q lies between
+// lam0 and lam).  Each weight then carries binary32 rounding relative to P and
+// lam Q, not to their difference: measured, the normalised CDF error of these
+// weights is about 3e-8 / Z for residual mass Z = sum W / sum P.  When Z is
+// below kNearZ (the draft is almost the target) the last workgroup re-forms the
+// row pair's weights by itself in the near form (near_exact_tiles()), in which
+// the tokens the rows share cancel exactly.  That is slow (one workgroup reads
+// the pair twice) but rare: draft k is rejected with probability Z_k, so a
+// position whose residual mass is below kNearZ reaches this draw at most that
+// often.
+constexpr int kSumP = 0, kSumQ = 1, kSumW = 2, kSumG = 3;
+#ifndef SV_NEAR_Z
+#define SV_NEAR_Z 0.01
+#endif
+constexpr double kNearZ = SV_NEAR_Z;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
@@ -1354,45 +1358,163 @@ __device__ void block_sum2_all(double& a, double& b) {
     __syncthreads();
 }
 
-// Per-element accumulation of a residual tile's sums (lane-private, in the
-// order the caller visits the elements).  The draw pass and the parity/debug
-// kernel both use these, so both form the same sums.
-struct TileSums {
-    float x, w, d, p0, la;
+// Per-element accumulation of a residual tile's far-form sums (lane-private, in
+// the order the caller visits the elements); the draw pass and the parity/debug
+// kernel both use it, so both form the same sums.
+struct FarSums {
+    float p, q, w, g;
 };
-__device__ __forceinline__ void near_accum(TileSums& s, float M, float c, float rho0, float zt, float zd) {
-    const NearTerm tm = near_term(M, c, zt, zd);
-    const float w0 = rho0 * tm.A - tm.Dl;
-    const bool lin = !tm.same && w0 > 0.f;
-    s.x += tm.A;
-    s.d += tm.Dl;
-    s.p0 += tm.same ? tm.A : 0.f;
-    s.w += lin ? w0 : 0.f;
-    s.la += lin ? tm.A : 0.f;
+__device__ __forceinline__ void far_accum(FarSums& s, float mt, float md, float c, float lam0, float zt, float zd) {
+    const float P = far_p(mt, c, zt);
+    const float Q = far_p(md, c, zd);
+    const float w0 = fmaf(-lam0, Q, P);
+    s.p += P;
+    s.q += Q;
+    s.w += fmaxf(w0, 0.f);
+    s.g += w0 > 0.f ? Q : 0.f;
 }
-__device__ __forceinline__ void far_accum(TileSums& s, const WSpec& far_ws, float zt, float zd) {
-    s.x += exp2_fast((zt - far_ws.mA) * far_ws.c);
-    s.w += elem_weight(far_ws, zt, zd);
+__device__ __forceinline__ FarSums wave_far_sums(FarSums s) {
+    return FarSums{wave_sum(s.p), wave_sum(s.q), wave_sum(s.w), wave_sum(s.g)};
 }
-// The tile's sums over the wave, the same value in every lane.
-__device__ __forceinline__ TileSums wave_tile_sums(TileSums s, bool near) {
-    s.x = wave_sum(s.x);
-    s.w = wave_sum(s.w);
-    if (near) {
-        s.d = wave_sum(s.d);
-        s.p0 = wave_sum(s.p0);
-        s.la = wave_sum(s.la);
+__device__ __forceinline__ float far_sum_at(const FarSums& s, int q) {
+    return q == kSumP ? s.p : q == kSumQ ? s.q : q == kSumW ? s.w : s.g;
+}
+
+// The near form of one row pair, formed by one workgroup from the rows
+// themselves: first rho = sum Dl / sum A over the whole pair, then each tile's
+// exact weight sum max(0, rho A - Dl) into s_w[NT].  Returns rho (binary32, as
+// the tile scan uses it); *Z receives the sum of the tile weights.  Wave w
+// takes tiles w, w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
+template <int DT, bool ALIGNED>
+__device__ float near_exact_tiles(const void* trow, const void* drow, int V, int NT, float Mc, float c, double* s_w,
+                                  double* Z) {
+    constexpr int kVec = Elem<DT>::kVec;
+    constexpr int kTile = kThreads * kVec;
+    constexpr int kU = kThreads / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // a tile's 16-byte vectors of both rows (absent ones -inf), all loads
+    // issued before the first use
+    auto load_tile = [&](int t, uint4 (&wt)[kU], uint4 (&wd)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int e0 = t * kTile + (lane + 64 * u) * kVec;
+            if constexpr (ALIGNED) {
+                wt[u] = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+                wd[u] = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+            } else {
+                wt[u] = load_raw<DT>(trow, e0, V);
+                wd[u] = load_raw<DT>(drow, e0, V);
+            }
+        }
+    };
+    double X = 0.0, D = 0.0;
+    for (int t = w; t < NT; t += kWaves) {
+        uint4 wt[kU], wd[kU];
+        load_tile(t, wt, wd);
+        float sx = 0.f, sd = 0.f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float zt[kVec], zd[kVec];
+            unpack<DT>(wt[u], zt);
+            unpack<DT>(wd[u], zd);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const NearTerm tm = near_term(Mc, c, zt[e], zd[e]);  // absent elements: -inf, terms 0
+                sx += tm.A;
+                sd += tm.Dl;
+            }
+        }
+        X += (double)wave_sum(sx);
+        D += (double)wave_sum(sd);
     }
-    return s;
+    if (lane != 0) X = D = 0.0;  // every lane of a wave holds the wave's sums
+    block_sum2_all(X, D);
+    const float rho = (float)(D / X);
+    double zsum = 0.0, unused = 0.0;
+    for (int t = w; t < NT; t += kWaves) {
+        uint4 wt[kU], wd[kU];
+        load_tile(t, wt, wd);
+        float sw = 0.f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float zt[kVec], zd[kVec];
+            unpack<DT>(wt[u], zt);
+            unpack<DT>(wd[u], zd);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const NearTerm tm = near_term(Mc, c, zt[e], zd[e]);
+                sw += fmaxf(fmaf(rho, tm.A, -tm.Dl), 0.f);
+            }
+        }
+        sw = wave_sum(sw);
+        if (lane == 0) {
+            s_w[t] = (double)sw;
+            zsum += (double)sw;
+        }
+    }
+    block_sum2_all(zsum, unused);
+    *Z = zsum;
+    return rho;
 }
-__device__ __forceinline__ float tile_sum_at(const TileSums& s, int q) {
-    return q == kSumX ? s.x : q == kSumW ? s.w : q == kSumD ? s.d : q == kSumP0 ? s.p0 : s.la;
-}
-// Weight of a tile at the exact rho (near) from its sums at rho0; far: the sum itself.
-__device__ __forceinline__ double tile_weight(const float* v, bool near, double rho, float rho0) {
-    double w = (double)v[kSumW];
-    if (near) w += fmax(rho, 0.0) * (double)v[kSumP0] + (rho - (double)rho0) * (double)v[kSumLA];
-    return w > 0.0 ? w : 0.0;
+
+// The residual draw's set-up in the deciding workgroup, from the far-form tile
+// sums v[r][*] of tiles tid + r kThreads: the tile weights into s_w[NT], the
+// element weighting into *ws, the residual total into *Z (at or below zero:
+// no residual mass left, s_w then holds the target's own tile masses and *ws
+// weighs by the target).  *near_out: the near form was used.
+template <int DT, bool ALIGNED, int TPT>
+__device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& d, const void* trow, const void* drow,
+                              int V, double* s_w, WSpec* ws, double* Z, bool* near_out, double* lam_out) {
+    const int tid = threadIdx.x;
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+        sp += (double)v[r][kSumP];
+        sq += (double)v[r][kSumQ];
+    }
+    block_sum2_all(sp, sq);
+    const double lam = sq > 0.0 ? sp / sq : 0.0;
+    const double lam0 = exp2((double)d.lq);
+    double zr = 0.0, zp = 0.0;
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+        const int i = tid + r * kThreads;
+        if (i < NT) {
+            double w = (double)v[r][kSumW] - (lam - lam0) * (double)v[r][kSumG];
+            w = w > 0.0 ? w : 0.0;
+            s_w[i] = w;
+            zr += w;
+            zp += (double)v[r][kSumP];
+        }
+    }
+    block_sum2_all(zr, zp);
+    *lam_out = lam;
+    *near_out = false;
+    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)lam, 0.f, 0.f};
+    const bool close = fabs(((double)d.m_d - (double)d.m_t) * (double)d.c) <= 32.0;
+    if (close && zr < kNearZ * sp) {
+        // small residual: the near form, exactly, by this workgroup alone
+        // (both rows scaled by M = max(m_t, m_d); the maxima lie within 2^32)
+        const float M = fmaxf(d.m_t, d.m_d);
+        const float Mc = M * d.c;
+        __syncthreads();
+        const float rho = near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, Mc, d.c, s_w, &zr);
+        *ws = WSpec{kWResNear, d.c, M, 0.f, 0.f, rho, Mc};
+        *near_out = true;
+    }
+    if (!(zr > 0.0)) {
+        // no residual mass left after rounding: draw from p_k
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < TPT; ++r) {
+            const int i = tid + r * kThreads;
+            if (i < NT) s_w[i] = (double)v[r][kSumP];
+        }
+        *ws = target_spec(d);
+        zr = -zp;  // the caller draws from the target's masses (total zp)
+    }
+    *Z = zr;
+    __syncthreads();
 }
 
 template <int DT, bool ALIGNED>
@@ -1415,11 +1537,8 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
         return;
     }
     const void* drow = row_ptr<DT>(p.draft, (long long)b * n + d.k, V);
-    const bool near = d.kind == kDrawResidualNear;
-    const float M = near ? fmaxf(d.m_t, d.m_d) : d.m_t;  // the target row's scale
-    const int nq = near ? kDrawSums : 2;                  // sums handed over per tile
+    const float lam0 = exp2_fast(d.lq);
     unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
-    const WSpec far_ws{kWResFar, d.c, d.m_t, d.m_d, d.lq, 0.f};
 
     // chunk c: tiles [tile0, tile0 + cnt).  Wave w owns kTilesPerWave whole tiles
     // (lane l reads vectors l, l + 64, ... of each, coalesced), so every tile sum
@@ -1449,30 +1568,18 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     unsigned dep = 0u;
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
-        // absent elements read -inf on both rows: every term is 0
-        TileSums ts{0.f, 0.f, 0.f, 0.f, 0.f};
-        if (near) {
+        FarSums fs{0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                float zt[kVec], zd[kVec];
-                unpack<DT>(rt[i][u], zt);
-                unpack<DT>(rd[i][u], zd);
+        for (int u = 0; u < kU; ++u) {
+            float zt[kVec], zd[kVec];
+            unpack<DT>(rt[i][u], zt);
+            unpack<DT>(rd[i][u], zd);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) near_accum(ts, M, d.c, d.rho0, zt[e], zd[e]);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                float zt[kVec], zd[kVec];
-                unpack<DT>(rt[i][u], zt);
-                unpack<DT>(rd[i][u], zd);
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) far_accum(ts, far_ws, zt[e], zd[e]);
-            }
+            for (int e = 0; e < kVec; ++e) far_accum(fs, d.m_t, d.m_d, d.c, lam0, zt[e], zd[e]);
         }
-        ts = wave_tile_sums(ts, near);
+        fs = wave_far_sums(fs);
         const int t = wv * kTilesPerWave + i;
-        if (lane < nq && t < cnt) dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(tile_sum_at(ts, lane)));
+        if (lane < 4 && t < cnt) dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(far_sum_at(fs, lane)));
     }
     // this wave's exchanges have been performed before the workgroup arrives
     asm volatile("" ::"v"(dep));
@@ -1485,42 +1592,19 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
 
     // last workgroup: collect (and reset) the per-tile sums of the whole row pair
     constexpr int kTPT = kMaxTiles / kThreads;  // tiles per thread, at most
-    float v[kTPT][kDrawSums];
-    double X = 0.0, D = 0.0;
+    float v[kTPT][4];
 #pragma unroll
     for (int r = 0; r < kTPT; ++r) {
         const int i = tid + r * kThreads;
 #pragma unroll
-        for (int q = 0; q < kDrawSums; ++q)
-            v[r][q] = (i < NT && q < nq) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
-        X += (double)v[r][kSumX];
-        D += (double)v[r][kSumD];
+        for (int q = 0; q < 4; ++q) v[r][q] = (i < NT) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
     }
-    block_sum2_all(X, D);
-    const double rho = near ? D / X : 0.0;
-    double Zr = 0.0, Zp = 0.0;
-#pragma unroll
-    for (int r = 0; r < kTPT; ++r) {
-        const int i = tid + r * kThreads;
-        if (i < NT) {
-            const double w = tile_weight(v[r], near, rho, d.rho0);
-            s_buf[i] = w;
-            Zr += w;
-            Zp += (double)v[r][kSumX];
-        }
-    }
-    block_sum2_all(Zr, Zp);
-    const bool use_p = !(Zr > 0.0);  // no residual mass left after rounding: draw from p_k
-    if (use_p) {
-#pragma unroll
-        for (int r = 0; r < kTPT; ++r) {
-            const int i = tid + r * kThreads;
-            if (i < NT) s_buf[i] = (double)v[r][kSumX];
-        }
-        if (tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
-    }
-    __syncthreads();
-    const double t = (double)d.u * (use_p ? Zp : Zr);
+    WSpec ws;
+    double Z, lam;
+    bool near;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &near, &lam);
+    if (Z <= 0.0 && tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
+    const double t = (double)d.u * fabs(Z);
     const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_buf[i]; });
     int tile = pk.i;
     bool take_last = false;
@@ -1532,9 +1616,6 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
         tile = lt < 0 ? 0 : lt;
         take_last = true;
     }
-    const WSpec ws = use_p  ? WSpec{kWTarget, d.c, M, 0.f, 0.f, 0.f}
-                     : near ? WSpec{kWResNear, d.c, M, 0.f, 0.f, (float)rho}
-                            : far_ws;
     const int y = scan_tile<DT, ALIGNED>(ws, trow, drow, V, tile, pk.before, t, take_last);
     // row L's tile partials (written by the stats pass, unused here): leave them zero
     for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;
@@ -1551,7 +1632,7 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
 // fit 80 without spilling); the element-wise unaligned one is left to the
 // compiler.
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void k_draw(DrawParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WPE))) void k_draw(DrawParams p) {
     __shared__ double s_buf[kMaxTiles];
     draw_item<DT, true>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
 }
@@ -1635,13 +1716,14 @@ __global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, 
 
 // Parity/debug only: for row pair r (target row r, draft row r, temperature
 // temp[r] > 0), the residual weights a draw after a rejection would scan, formed
-// by the draw pass's own code: the descriptor as the decision forms it (from
-// this kernel's own row statistics), the tile sums as the draw chunks form them
+// by the draw pass's own code: the descriptor's statistics from this kernel's
+// own reduction of each row, the far-form tile sums as the draw chunks form them
 // (wave w takes tiles w, w + kWaves, ..., lane l the same elements of a tile),
-// rho as the last workgroup forms it, then every element's weight.  Outputs:
-// w_out[r][V] the element weights, tile_out[r][NT] (nullable) the tiles'
-// weights at rho (the numbers the tile pick is made on), info_out[r][4]
-// (nullable) {1 near / 0 far, rho0, rho, sum of tile weights}.
+// the deciding workgroup's set-up (plan_residual(): the far form, or the near
+// form when the residual mass is small), then every element's weight.
+// Outputs: w_out[r][V] the element weights, tile_out[r][NT] (nullable) the
+// tiles' weights the tile pick uses, info_out[r][4] (nullable) {1 near / 0 far,
+// lam, rho (near form) or 0, residual mass sum of tile weights / sum P}.
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target, const void* draft, const float* temp,
                                                              int V, int NT, float* w_out, double* tile_out,
@@ -1666,15 +1748,11 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     const MS bq = wg_softmax_tiles<DT, ALIGNED>(drow, 0, V, c, nullptr);
     if (tid == 0) s_d = bq;
     __syncthreads();
-    const double gap = ((double)s_d.m - (double)s_t.m) * (double)c;
-    const bool near = fabs(gap) <= 32.0;
-    const float rho0 = near ? (float)((double)s_d.s / (double)s_t.s * exp2(gap) - 1.0) : 0.f;
-    const float lq = (float)log2((double)s_t.s / (double)s_d.s);
-    const float M = near ? fmaxf(s_t.m, s_d.m) : s_t.m;
-    const WSpec far_ws{kWResFar, c, s_t.m, s_d.m, lq, 0.f};
-    __shared__ float s_sum[kDrawSums][kMaxTiles];
+    DrawDesc d{kDrawResidual, 0, c, s_t.m, s_d.m, (float)log2((double)s_t.s / (double)s_d.s), 0.f, 0.f};
+    const float lam0 = exp2_fast(d.lq);
+    __shared__ float s_sum[4][kMaxTiles];
     for (int t = w; t < NT; t += kWaves) {
-        TileSums ts{0.f, 0.f, 0.f, 0.f, 0.f};
+        FarSums fs{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float zt[kVec], zd[kVec];
@@ -1682,46 +1760,37 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
             load_vec<DT, ALIGNED>(trow, e0, V, zt);
             load_vec<DT, ALIGNED>(drow, e0, V, zd);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                if (near) near_accum(ts, M, c, rho0, zt[e], zd[e]);
-                else far_accum(ts, far_ws, zt[e], zd[e]);
-            }
+            for (int e = 0; e < kVec; ++e) far_accum(fs, d.m_t, d.m_d, c, lam0, zt[e], zd[e]);
         }
-        ts = wave_tile_sums(ts, near);
-        if (lane < kDrawSums) s_sum[lane][t] = tile_sum_at(ts, lane);
+        fs = wave_far_sums(fs);
+        if (lane < 4) s_sum[lane][t] = far_sum_at(fs, lane);
     }
     __syncthreads();
-    float v[kTPT][kDrawSums];
-    double X = 0.0, D = 0.0;
+    float v[kTPT][4];
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
         const int i = tid + q * kThreads;
 #pragma unroll
-        for (int k = 0; k < kDrawSums; ++k) v[q][k] = (i < NT && (near || k < 2)) ? s_sum[k][i] : 0.f;
-        X += (double)v[q][kSumX];
-        D += (double)v[q][kSumD];
+        for (int k = 0; k < 4; ++k) v[q][k] = (i < NT) ? s_sum[k][i] : 0.f;
     }
-    block_sum2_all(X, D);
-    const double rho = near ? D / X : 0.0;
-    double Z = 0.0, unused = 0.0;
-#pragma unroll
-    for (int q = 0; q < kTPT; ++q) {
-        const int i = tid + q * kThreads;
-        if (i < NT) {
-            const double tw = tile_weight(v[q], near, rho, rho0);
-            if (tile_out) tile_out[(size_t)r * NT + i] = tw;
-            Z += tw;
-        }
+    __shared__ double s_w[kMaxTiles];
+    WSpec ws;
+    double Z, lam;
+    bool near;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &Z, &near, &lam);
+    double sp = 0.0, unused = 0.0;
+    for (int i = tid; i < NT; i += kThreads) {
+        if (tile_out) tile_out[(size_t)r * NT + i] = s_w[i];
+        sp += (double)v[i / kThreads][kSumP];
     }
-    block_sum2_all(Z, unused);
-    const WSpec ws = near ? WSpec{kWResNear, c, M, 0.f, 0.f, (float)rho} : far_ws;
+    block_sum2_all(sp, unused);
     for (int i = tid; i < V; i += kThreads)
         w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
     if (info_out && tid == 0) {
         info_out[(size_t)r * 4 + 0] = near ? 1.f : 0.f;
-        info_out[(size_t)r * 4 + 1] = rho0;
-        info_out[(size_t)r * 4 + 2] = (float)rho;
-        info_out[(size_t)r * 4 + 3] = (float)Z;
+        info_out[(size_t)r * 4 + 1] = (float)lam;
+        info_out[(size_t)r * 4 + 2] = near ? ws.rho : 0.f;
+        info_out[(size_t)r * 4 + 3] = near ? 0.f : (float)(Z / sp);
     }
 }
 

@@ -13,10 +13,13 @@ Two kinds of row pairs (V = 128256 bf16, the llama-vocab recipe for the target):
 
 For each pair the test reports the maximum normalised CDF error of the weights
 the draw pass scans, max_i |C_gpu(i) / Z_gpu - C(i) / Z| with C the running sum
-in ascending index and the exact weights max(0, p - q) from the oracle's double
-softmax, and it must stay below the 1e-5 near-tie band.  Then whole verify calls
-with a forced rejection at slot 0 and stratified final uniforms are compared
-with the oracle decision by decision: no hard mismatch.
+in ascending index and the exact weights max(0, p - q) from the oracle's softmax,
+and it must stay below the 1e-5 near-tie band.  The cases with a small residual
+mass take the draw's near form; drafts with sigma 0.3 and 1.0 (residual mass
+0.1 to 0.6, the benchmark workloads' range) take its far form, whose error is
+held to 1e-6.  Then whole verify calls with a forced rejection at slot 0 and
+stratified final uniforms are compared with the oracle decision by decision: no
+hard mismatch.
 """
 import numpy as np
 import pytest
@@ -64,12 +67,13 @@ def _oracle_residual(oracle, zt, zd, T):
 
 
 CASES = [("handful", 0.7), ("handful", 1.0), ("0.003", 0.7), ("0.01", 0.7), ("0.03", 0.7)]
+FAR_CASES = [("0.3", 0.7), ("1.0", 0.7), ("1.0", 1.0)]
 
 
-@pytest.mark.parametrize("kind,T", CASES)
+@pytest.mark.parametrize("kind,T", CASES + FAR_CASES)
 def test_residual_weights_cdf_error(oracle, kind, T):
     rows = 4
-    zt, zd, _ = _pairs(kind, 1000 + CASES.index((kind, T)), rows)
+    zt, zd, _ = _pairs(kind, 1000 + (CASES + FAR_CASES).index((kind, T)), rows)
     temp = torch.full((rows,), T, device=DEV)
     w, tw, info = sv.sv_residual_weights_debug(zt, zd, temp)
     torch.cuda.synchronize()
@@ -91,8 +95,10 @@ def test_residual_weights_cdf_error(oracle, kind, T):
         Ct = np.cumsum(tw[r]) / tw[r].sum()
         err_t = np.abs(Ct - Co[ends]).max()
         worst, worst_tile = max(worst, err), max(worst_tile, err_t)
-        print(f"\n{kind} T={T} row {r}: Z={Zo:.3e} near={int(info[r, 0])} rho0={info[r, 1]:.3e} "
+        print(f"\n{kind} T={T} row {r}: Z={Zo:.3e} form={'near' if info[r, 0] else 'far'} lam={info[r, 1]:.6g} "
               f"rho={info[r, 2]:.3e} max normalised CDF error: elements {err:.2e}, tile ends {err_t:.2e}")
+        if Zo >= 0.05:
+            assert not info[r, 0] and err < 1e-6 and err_t < 1e-6, (Zo, err, err_t)
     assert worst < 1e-5 and worst_tile < 1e-5, (worst, worst_tile)
 
 

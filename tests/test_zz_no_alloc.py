@@ -49,10 +49,12 @@ def test_noalloc_equals_workspace_call(order):
 
 
 def test_noalloc_rejects_sizes_beyond_its_array():
-    t = torch.zeros((1, 1, 8), dtype=torch.bfloat16, device=DEV)
-    L = sv.lib()
-    # 16 MiB holds B = 7358 at n = 8, V = 152064 bf16; B = 8192 does not
-    st = L.spec_verify_sample_ex_noalloc(t.data_ptr(), t.data_ptr(), sv.SV_BF16, t.data_ptr(), t.data_ptr(),
-                                         t.data_ptr(), t.data_ptr(), None, 8192, 8, 152064, t.data_ptr(),
-                                         t.data_ptr(), None, None, None, None, None, 0, None)
+    """Sizes whose workspace exceeds the static array are rejected before any
+    device work.  The data pointers are NULL, so even a call that got past the
+    size check would be rejected by the argument checks and launch nothing."""
+    B, n, V = 32768, 8, 152064
+    need = sv.sv_workspace_bytes(B, n, V, sv.SV_BF16)
+    assert need > 2 * (16 << 20), need
+    st = sv.lib().spec_verify_sample_ex_noalloc(None, None, sv.SV_BF16, None, None, None, None, None, B, n, V, None,
+                                                None, None, None, None, None, None, 0, None)
     assert st == sv.SV_EWORKSPACE
