@@ -353,6 +353,54 @@ def make_law_case(seed: int, trials: int, V: int = 8, n: int = 4, T: float = 1.0
                 uniforms=uniforms, rows_t=zt, rows_d=zd, T=T, B=trials, n=n, V=V)
 
 
+def make_tree_law_case(seed: int, trials: int, V: int = 8, widths=(3, 2), T: float = 1.0, draft_sigma: float = 1.0,
+                       device="cpu") -> dict:
+    """Many trials of sampling tree verification on one two-level draft tree
+    (widths[0] children of the root, widths[1] below each), fp32 logits.
+
+    The target's and the draft's logits after a node depend only on the tokens
+    on the way to it (tables drawn once from the seed: z0 for the root, z1[v]
+    after token v, z2[v][w] after v then w; draft = target + N(0, sigma^2)), as
+    they do for a real model.  Each trial draws the children of every node
+    independently from the draft's distribution at that node (Gumbel-max on the
+    draft logits / T) and its own uniforms.  Returns the step's inputs (target
+    [trials, n+1, V], draft [trials, n, V], draft_tokens, draft_parents,
+    draft_lens, temperature, uniforms) and the tables rows_t0, rows_t1, rows_t2.
+    """
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    k1, k2 = widths
+    par = tree_parents(k1 + k1 * k2, widths=(k1, k2, 0))
+    n = len(par)
+    z0 = 1.5 * torch.randn((V,), generator=g, device=dev)
+    d0 = z0 + draft_sigma * torch.randn((V,), generator=g, device=dev)
+    z1 = 1.5 * torch.randn((V, V), generator=g, device=dev)
+    d1 = z1 + draft_sigma * torch.randn((V, V), generator=g, device=dev)
+    z2 = 1.5 * torch.randn((V, V, V), generator=g, device=dev)
+    d2 = z2 + draft_sigma * torch.randn((V, V, V), generator=g, device=dev)
+    temp = torch.full((trials,), float(T), device=dev)
+    # children of the root, then k2 children below each of them
+    x1 = _gumbel_draft(d0.expand(trials, k1, V), temp, g).long()                    # [trials, k1]
+    x2 = _gumbel_draft(d1[x1].repeat_interleave(k2, dim=1), temp, g).long()
+    x2 = x2.view(trials, k1, k2)
+    tokens = torch.cat([x1, x2.reshape(trials, k1 * k2)], dim=1)                     # node order of tree_parents
+    target = torch.empty((trials, n + 1, V), device=dev)
+    draft = torch.empty((trials, n, V), device=dev)
+    target[:, 0] = z0
+    draft[:, 0] = d0
+    target[:, 1:1 + k1] = z1[x1]
+    draft[:, 1:1 + k1] = d1[x1]
+    v = x1.repeat_interleave(k2, dim=1)                                               # parent token of each leaf
+    w = x2.reshape(trials, k1 * k2)
+    target[:, 1 + k1:] = z2[v, w]
+    draft[:, 1 + k1:] = d2[v, w][:, :n - 1 - k1]                                     # leaves' rows (unused)
+    uniforms = torch.rand((trials, n + 1), generator=g, device=dev)
+    return dict(target=target, draft=draft, draft_tokens=tokens.to(torch.int32),
+                draft_parents=torch.as_tensor(par, dtype=torch.int32, device=dev).expand(trials, n).contiguous(),
+                draft_lens=torch.full((trials,), n, dtype=torch.int32, device=dev), temperature=temp,
+                uniforms=uniforms, rows_t0=z0, rows_t1=z1, rows_t2=z2, B=trials, n=n, V=V, T=T, widths=widths)
+
+
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bfloat16 tensor (for the oracle)."""
     import numpy as np

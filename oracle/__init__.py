@@ -70,6 +70,9 @@ class Oracle:
         L.sv_oracle_verify_tree_greedy.argtypes = [vp, C.c_int, i32p, i32p, i32p, C.c_int, C.c_int, C.c_int,
                                                    i32p, i32p, i32p, u32p]
         L.sv_oracle_verify_tree_greedy.restype = C.c_int
+        L.sv_oracle_verify_tree_sample.argtypes = [vp, vp, C.c_int, i32p, i32p, i32p, f32p, f32p, C.c_int, C.c_int,
+                                                   C.c_int, i32p, i32p, i32p, f64p, f64p, u32p]
+        L.sv_oracle_verify_tree_sample.restype = C.c_int
         L.sv_oracle_plant.argtypes = []
         L.sv_oracle_plant.restype = C.c_int
 
@@ -154,6 +157,31 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"sv_oracle_verify_tree_greedy failed: {rc}")
         return dict(accepted_len=acc, emitted=emi, path=path, seq_flags=fl)
+
+    def verify_tree_sample(self, target, draft, draft_tokens, draft_parents, draft_lens, temperature, uniforms):
+        """Sampling tree verification (see sv_oracle_verify_tree_sample)."""
+        target, dt = self._logits(target)
+        B, n1, V = target.shape
+        n = n1 - 1
+        draft, dt2 = self._logits(draft)
+        assert dt2 == dt and draft.shape == (B, n, V)
+        x = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, n)
+        par = np.ascontiguousarray(draft_parents, dtype=np.int32).reshape(B, n)
+        L = np.ascontiguousarray(draft_lens, dtype=np.int32).reshape(B)
+        T = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+        u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, n + 1)
+        acc = np.empty(B, np.int32)
+        emi = np.empty((B, n + 1), np.int32)
+        path = np.empty((B, max(n, 1)), np.int32)[:, :n].copy()
+        am = np.empty((B, n), np.float64)
+        dm = np.empty(B, np.float64)
+        fl = np.empty(B, np.uint32)
+        rc = self.lib.sv_oracle_verify_tree_sample(self._p(target), self._p(draft), dt, self._p(x), self._p(par),
+                                                   self._p(L), self._p(T), self._p(u), B, n, V, self._p(acc),
+                                                   self._p(emi), self._p(path), self._p(am), self._p(dm), self._p(fl))
+        if rc != 0:
+            raise RuntimeError(f"sv_oracle_verify_tree_sample failed: {rc}")
+        return dict(accepted_len=acc, emitted=emi, path=path, accept_margin=am, draw_margin=dm, seq_flags=fl)
 
     def mtp_shift_insert(self, tokens, hidden_src, accepted_len, emitted, copy_hidden=True):
         """Returns (new_tokens, hidden_dst); inputs are not modified."""

@@ -572,6 +572,189 @@ int sv_oracle_verify_tree_greedy(const void *target_logits, int dt, const int32_
     return 0;
 }
 
+/* ----------------------------------------------- tree verification (sampling)
+ *
+ * EAGLE section of "Accelerating Sonar through speculation": the draft proposes
+ * a tree of candidate tokens (several candidates per node), the target scores
+ * every candidate sequence, the longest suitable one is kept and one more token
+ * from the target is appended.  The page gives no acceptance rule for sampling;
+ * the rule taken is SpecInfer's multi-step speculative sampling (Miao et al.,
+ * "SpecInfer: Accelerating Large Language Model Serving with Tree-based
+ * Speculative Inference and Verification"), which keeps the target's
+ * distribution when every node's children are independent draws from the
+ * draft's distribution at that node:
+ *   - node 0 is the root; node j + 1 (j < L) holds x_j below parents[j] in
+ *     [0, j] (other parents leave the node out, flagged);
+ *   - target row r is p_r = softmax(z_t[r] / T), the target after node r; draft
+ *     row r is q_r = softmax(z_d[r] / T), the draft at node r, from which node
+ *     r's children were drawn;
+ *   - at node u with children c_1 < c_2 < ... (index order): the current target
+ *     residual starts as p' = p_u; child c_i is accepted iff
+ *     u[c_i - 1] < p'(x) / q_u(x) (q_u(x) = 0: ratio +inf if p'(x) > 0, else 0);
+ *     accepting it moves the walk to c_i; rejecting it replaces p' by
+ *     max(0, p' - q_u) normalised.  After k rejections p' is
+ *     max(0, p_u - lam_k q_u) / M_k with lam_0 = 0, M_0 = 1 and
+ *     lam_{k+1} = lam_k + M_k, M_{k+1} = sum_i max(0, p_u,i - lam_{k+1} q_u,i)
+ *     (the same residual, written without nesting);
+ *   - when no child of the current node is accepted the token is drawn with
+ *     u[n] from p' (p_u itself when the node has no children: the bonus
+ *     token); a residual with no mass left falls back to p_u (flagged);
+ *   - outputs as in the greedy tree rule: the kept path's tokens, the drawn
+ *     token, then -1; path[] the kept path's nodes.
+ * With parents[j] = j (a chain) this is the linear sampling rule.  T_b = 0 takes
+ * the greedy tree rule.  The residual sums and the draw are formed in extended
+ * precision, the first acceptance test at a node as the linear rule forms it. */
+typedef struct {
+    const void *target, *draft;
+    int dt;
+    const int32_t *tokens, *parents, *lens;
+    const float *temperature, *uniforms;
+    int B, n, V;
+    int32_t *acc, *emitted, *path;
+    double *accept_margin, *draw_margin;
+    uint32_t *seq_flags;
+} tree_job_t;
+
+static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratch [2V] */)
+{
+    const int n = J->n, V = J->V;
+    uint32_t flags = 0;
+    int L = J->lens[b];
+    if (L < 0) { L = 0; flags |= OR_FLAG_LEN_CLAMPED; }
+    if (L > n) { L = n; flags |= OR_FLAG_LEN_CLAMPED; }
+    double T = (double)J->temperature[b];
+    if (!(T >= 0.0)) { T = 0.0; flags |= OR_FLAG_BAD_TEMP; }
+    const int32_t *x = J->tokens + (size_t)b * n;
+    const int32_t *par = J->parents + (size_t)b * n;
+    const float *uni = J->uniforms + (size_t)b * (n + 1);
+    int32_t *e = J->emitted + (size_t)b * (n + 1);
+    int32_t scratch_path[128];
+    int32_t *path = J->path ? J->path + (size_t)b * n : scratch_path;
+    for (int j = 0; j < n; ++j) J->accept_margin[(size_t)b * n + j] = INFINITY;
+    J->draw_margin[b] = INFINITY;
+    if (T == 0.0) {
+        uint32_t f = 0;
+        tree_one(J->target, J->dt, x, par, J->lens[b], n, V, (size_t)b * (size_t)(n + 1) * (size_t)V, &J->acc[b],
+                 e, path, &f);
+        J->seq_flags[b] = flags | f;
+        return;
+    }
+    for (int j = 0; j < L; ++j) {
+        if (par[j] < 0 || par[j] > j) flags |= OR_FLAG_BAD_PARENT;
+        if (x[j] < 0 || x[j] >= V) flags |= OR_FLAG_TOKEN_OOR;
+    }
+    const size_t trow0 = (size_t)b * (size_t)(n + 1) * (size_t)V;
+    const size_t drow0 = (size_t)b * (size_t)n * (size_t)V;
+    long double *p = w, *q = w + V;
+    int u = 0, depth = 0, y = -1;
+    for (;;) {
+        /* the target at node u, and (if u has children) the draft at node u */
+        int first = -1;
+        for (int j = 0; j < L; ++j)
+            if (par[j] == u && par[j] <= j) { first = j; break; }
+        row_probs_ld(J->target, J->dt, trow0 + (size_t)u * V, V, T, p);
+        if (first < 0) {
+            /* no children: the bonus token from p_u */
+            double margin = 0.0;
+            y = draw_inverse_cdf(p, V, sanitize_uniform(uni[n], &flags), &margin);
+            J->draw_margin[b] = margin;
+            break;
+        }
+        row_probs_ld(J->draft, J->dt, drow0 + (size_t)u * V, V, T, q);
+        double mt, lst, md, lsd;
+        (void)row_softmax_stats(J->target, J->dt, trow0 + (size_t)u * V, V, T, &mt, &lst);
+        (void)row_softmax_stats(J->draft, J->dt, drow0 + (size_t)u * V, V, T, &md, &lsd);
+        long double lam = 0.0L, M = 1.0L;
+        int accepted = -1;
+        for (int j = first; j < L; ++j) {
+            if (par[j] != u || par[j] > j) continue;
+            const int xc = x[j];
+            double ratio = 0.0;
+            if (xc >= 0 && xc < V) {
+                if (lam == 0.0L) {
+                    /* the first test at a node: p_u(x) / q_u(x), as the linear rule forms it */
+                    const double pp = prob_at(J->target, J->dt, trow0 + (size_t)u * V, xc, T, mt, lst);
+                    const double qq = prob_at(J->draft, J->dt, drow0 + (size_t)u * V, xc, T, md, lsd);
+                    ratio = (qq > 0.0) ? pp / qq : (pp > 0.0 ? INFINITY : 0.0);
+                } else {
+                    const long double r = p[xc] - lam * q[xc];
+                    const long double pr = (M > 0.0L && r > 0.0L) ? r / M : 0.0L;
+                    ratio = (q[xc] > 0.0L) ? (double)(pr / q[xc]) : (pr > 0.0L ? INFINITY : 0.0);
+                }
+            }
+            const double uu = sanitize_uniform(uni[j], &flags);
+            J->accept_margin[(size_t)b * n + j] = fabs(uu - ratio);
+            if (uu < ratio) { accepted = j; break; }
+#if SV_ORACLE_PLANT == 8
+            /* planted mistake: every sibling tested against p_u itself (no
+             * residual update between siblings); the draw still takes
+             * max(0, p_u - q_u) */
+            continue;
+#endif
+            /* rejected: p' <- max(0, p' - q_u) normalised */
+            lam += M;
+            M = 0.0L;
+            for (int i = 0; i < V; ++i) {
+                const long double d = p[i] - lam * q[i];
+                if (d > 0.0L) M += d;
+            }
+        }
+        if (accepted >= 0) {
+            path[depth] = accepted + 1;
+            e[depth] = x[accepted];
+            ++depth;
+            u = accepted + 1;
+            continue;
+        }
+        /* every child rejected: draw from max(0, p_u - lam q_u) */
+#if SV_ORACLE_PLANT == 8 || SV_ORACLE_PLANT == 9
+        lam = 1.0L; /* planted mistakes: the draw ignores the later siblings' updates */
+#endif
+        long double Z = 0.0L;
+        for (int i = 0; i < V; ++i) {
+            const long double d = p[i] - lam * q[i];
+            q[i] = d > 0.0L ? d : 0.0L;
+            Z += q[i];
+        }
+        double margin = 0.0;
+        if (Z > 0.0L) {
+            y = draw_inverse_cdf(q, V, sanitize_uniform(uni[n], &flags), &margin);
+        } else {
+            flags |= OR_FLAG_ZERO_RESIDUAL;
+            y = draw_inverse_cdf(p, V, sanitize_uniform(uni[n], &flags), &margin);
+        }
+        J->draw_margin[b] = margin;
+        break;
+    }
+    J->acc[b] = depth;
+    e[depth] = y;
+    for (int d = depth + 1; d <= n; ++d) e[d] = -1;
+    for (int d = depth; d < n; ++d) path[d] = -1;
+    J->seq_flags[b] = flags;
+}
+
+/* Sampling tree verification for every sequence.  target [B][n+1][V], draft
+ * [B][n][V] (row r = the draft at node r), draft_tokens / draft_parents [B][n],
+ * draft_lens [B], temperature [B], uniforms [B][n+1] (u[j]: the test of node
+ * j + 1, u[n]: the final draw).  Outputs accepted_len [B], emitted [B][n+1],
+ * path [B][n] (nullable), accept_margin [B][n] (+inf for nodes not tested),
+ * draw_margin [B], seq_flags [B].  Returns 0, -1 on bad sizes, -2 without memory. */
+int sv_oracle_verify_tree_sample(const void *target_logits, const void *draft_logits, int dt,
+                                 const int32_t *draft_tokens, const int32_t *draft_parents,
+                                 const int32_t *draft_lens, const float *temperature, const float *uniforms,
+                                 int B, int n, int V, int32_t *accepted_len, int32_t *emitted, int32_t *path,
+                                 double *accept_margin, double *draw_margin, uint32_t *seq_flags)
+{
+    if (check_dims(B, n, V)) return -1;
+    long double *w = (long double *)malloc(sizeof(long double) * 2 * (size_t)V);
+    if (!w) return -2;
+    tree_job_t J = {target_logits, draft_logits, dt, draft_tokens, draft_parents, draft_lens, temperature,
+                    uniforms, B, n, V, accepted_len, emitted, path, accept_margin, draw_margin, seq_flags};
+    for (int b = 0; b < B; ++b) tree_sample_one(&J, b, w);
+    free(w);
+    return 0;
+}
+
 /* ------------------------------------------------------- logit projection */
 
 /* The target's logit projection (its lm_head): a [V][H] matrix that maps a
