@@ -21,6 +21,7 @@ SV_OK, SV_EINVAL, SV_EALIGN, SV_EWORKSPACE, SV_EHIP = 0, 1, 2, 3, 4
 SV_FLAG_LEN_CLAMPED, SV_FLAG_TOKEN_OOR, SV_FLAG_BAD_TEMP, SV_FLAG_BAD_UNIFORM, SV_FLAG_ZERO_RESIDUAL = 1, 2, 4, 8, 16
 SV_FLAG_ROW_CLAMPED = 32
 SV_FLAG_BAD_PARENT = 64
+SV_FLAG_TREE_TRUNCATED = 128
 SV_MAX_DRAFT = 64
 
 _lib = None
@@ -59,6 +60,10 @@ def lib():
     L.spec_verify_greedy.restype = i
     L.spec_verify_tree_greedy.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_tree_greedy.restype = i
+    L.spec_verify_tree_sample.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_tree_sample.restype = i
+    L.sv_tree_rounds.argtypes = [vp, i]
+    L.sv_tree_rounds.restype = i
     L.spec_verify_sample_mtp.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, vp,
                                          sz, vp]
     L.spec_verify_sample_mtp.restype = i
@@ -231,6 +236,75 @@ def spec_verify_tree_greedy(target_logits, draft_tokens, draft_parents, draft_le
           _ptr(draft_lens), B, n, V, _ptr(accepted_len), _ptr(emitted), _ptr(path), _ptr(err_flags),
           _ptr(workspace), workspace.numel(), _stream(stream, dev))
     return accepted_len, emitted, path
+
+
+def sv_tree_rounds(parents) -> int:
+    """Rounds spec_verify_tree_sample needs so that no walk of the tree given by
+    the host sequence `parents` (node j + 1 below parents[j]) is truncated."""
+    a = (C.c_int32 * len(parents))(*[int(x) for x in parents])
+    return int(lib().sv_tree_rounds(C.cast(a, C.c_void_p), len(parents)))
+
+
+def _tree_sample_args(target_logits, draft_logits, draft_tokens, draft_parents, draft_lens, temperature, uniforms,
+                      max_rounds, accepted_len, emitted, path, err_flags, workspace, stream):
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    dt = _dt(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, n, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, n), dev)
+    _check(draft_parents, "draft_parents", torch.int32, (B, n), dev)
+    _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, n1), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(emitted, "emitted", torch.int32, (B, n1), dev)
+    if path is not None:
+        _check(path, "path", torch.int32, (B, n), dev)
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, (1,), dev)
+    _check(workspace, "workspace", torch.uint8)
+    return (_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(draft_parents), _ptr(draft_lens),
+            _ptr(temperature), _ptr(uniforms), B, n, V, int(max_rounds), _ptr(accepted_len), _ptr(emitted),
+            _ptr(path), _ptr(err_flags), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+
+
+def spec_verify_tree_sample(target_logits, draft_logits, draft_tokens, draft_parents, draft_lens, temperature,
+                            uniforms, max_rounds, *, accepted_len=None, emitted=None, path=None, err_flags=None,
+                            workspace=None, stream=None):
+    """Sampling tree verification (see include/specverify.h): node j + 1 holds
+    draft_tokens[b][j] below node draft_parents[b][j]; draft row r is the draft's
+    logits at node r.  max_rounds bounds the residual updates a walk may take
+    (sv_tree_rounds(parents) is enough for one tree).  Returns (accepted_len,
+    emitted, path)."""
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if emitted is None:
+        emitted = torch.empty((B, n1), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, n), dtype=torch.int32, device=dev)
+    need = sv_workspace_bytes(B, n, V, _dt(target_logits))
+    if workspace is None:
+        workspace = _default_ws(dev, need, stream)
+    args = _tree_sample_args(target_logits, draft_logits, draft_tokens, draft_parents, draft_lens, temperature,
+                             uniforms, max_rounds, accepted_len, emitted, path, err_flags, workspace, stream)
+    _call("spec_verify_tree_sample", *args)
+    return accepted_len, emitted, path
+
+
+def prepare_spec_verify_tree_sample(target_logits, draft_logits, draft_tokens, draft_parents, draft_lens,
+                                    temperature, uniforms, max_rounds, accepted_len, emitted, path, workspace, *,
+                                    err_flags=None, stream=None) -> Prepared:
+    """spec_verify_tree_sample with its arguments marshalled once."""
+    args = _tree_sample_args(target_logits, draft_logits, draft_tokens, draft_parents, draft_lens, temperature,
+                             uniforms, max_rounds, accepted_len, emitted, path, err_flags, workspace, stream)
+    return Prepared("spec_verify_tree_sample", args, (target_logits, draft_logits, draft_tokens, draft_parents,
+                                                      draft_lens, temperature, uniforms, accepted_len, emitted, path,
+                                                      err_flags, workspace))
 
 
 def spec_verify_greedy(target_logits, draft_tokens, draft_lens, *, accepted_len=None, emitted=None,

@@ -65,6 +65,10 @@ bool make_layout(int B, int n, int V, sv_dtype_t dt, sv::Layout* L) {
     off = align_up(off + (size_t)B * nt * sizeof(unsigned long long), 256);
     L->off_dsum = off;
     off = align_up(off + (size_t)B * sv::kDrawSums * nt * sizeof(float), 256);
+    L->off_walk = off;
+    off = align_up(off + (size_t)B * sizeof(sv::TreeWalk), 256);
+    L->off_trows = off;
+    off = align_up(off + (size_t)B * sv::tree_rows_layout(n).stride, 256);
     L->off_acc = off;
     off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L->bytes = off < 256 ? 256 : off;
@@ -477,6 +481,113 @@ sv_status_t spec_verify_tree_greedy(const void* target_logits, sv_dtype_t dt, co
     sp.path = path;
     const hipError_t e = sv::launch_tree(sp, dt == SV_BF16 ? sv::kBF16 : sv::kF32,
                                          rows_aligned(target_logits, V, dt), (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e);
+}
+
+int sv_tree_rounds(const int32_t* parents, int L) {
+    if (!parents || L <= 0) return 0;
+    if (L > sv::kMaxDraft) L = sv::kMaxDraft;
+    int kids[sv::kMaxDraft + 1] = {0}, acc[sv::kMaxDraft + 1] = {0};
+    for (int j = 0; j < L; ++j)
+        if (parents[j] >= 0 && parents[j] <= j) ++kids[parents[j]];
+    // rounds a walk can need at node a: one per rejected child that has a later sibling
+    int best = acc[0] = kids[0] > 1 ? kids[0] - 1 : 0;
+    for (int i = 1; i <= L; ++i) {
+        const int p = parents[i - 1];
+        if (!(p >= 0 && p < i)) continue;
+        acc[i] = acc[p] + (kids[i] > 1 ? kids[i] - 1 : 0);
+        if (acc[i] > best) best = acc[i];
+    }
+    return best;
+}
+
+sv_status_t spec_verify_tree_sample(const void* target_logits, const void* draft_logits, sv_dtype_t dt,
+                                    const int32_t* draft_tokens, const int32_t* draft_parents,
+                                    const int32_t* draft_lens, const float* temperature, const float* uniforms,
+                                    int B, int n, int V, int max_rounds, int32_t* accepted_len, int32_t* emitted,
+                                    int32_t* path, uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (!valid_sizes(B, n, V) || (dt != SV_F32 && dt != SV_BF16)) return SV_EINVAL;
+    if (max_rounds < 0 || max_rounds > sv::kMaxDraft * sv::kMaxDraft) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_lens || !temperature || !uniforms || !accepted_len || !emitted ||
+        (n > 0 && (!draft_logits || !draft_tokens || !draft_parents)))
+        return SV_EINVAL;
+    const size_t es = elem_bytes(dt);
+    if (!aligned_to(target_logits, es) || !aligned_to(draft_logits, es) || !aligned_to(draft_tokens, 4) ||
+        !aligned_to(draft_parents, 4) || !aligned_to(draft_lens, 4) || !aligned_to(temperature, 4) ||
+        !aligned_to(uniforms, 4) || !aligned_to(accepted_len, 4) || !aligned_to(emitted, 4) || !aligned_to(path, 4) ||
+        !aligned_to(err_flags, 4))
+        return SV_EALIGN;
+    sv::Layout L;
+    if (!make_layout(B, n, V, dt, &L)) return SV_EINVAL;
+    if (!workspace || workspace_bytes < L.bytes) return SV_EWORKSPACE;
+    if (!aligned_to(workspace, 16)) return SV_EALIGN;
+    const int S = 2 * n + 1;
+    if (!grid_ok((long long)B * S * L.NC) || !grid_ok((long long)B * L.NCd)) return SV_EINVAL;
+    const bool aligned = rows_aligned(target_logits, V, dt) && aligned_to(draft_logits, 16);
+    const sv::Dt kdt = dt == SV_BF16 ? sv::kBF16 : sv::kF32;
+    hipStream_t s = (hipStream_t)stream;
+
+    sv::StatsParams sp{};
+    sp.target = target_logits;
+    sp.draft = draft_logits;
+    sp.tokens = draft_tokens;
+    sp.lens = draft_lens;
+    sp.temp = temperature;
+    sp.unif = uniforms;
+    sp.B = B; sp.n = n; sp.V = V; sp.NC = L.NC; sp.CH = L.CH; sp.S = S;
+    sp.acc = accepted_len;
+    sp.emitted = emitted;
+    sp.flags = err_flags;
+    sp.part = at<sv::Partial>(workspace, L.off_part);
+    sp.cnt = at<uint32_t>(workspace, L.off_cnt);
+    sp.desc = at<sv::DrawDesc>(workspace, L.off_desc);
+    sp.NT = L.NT;
+    sp.tiles = at<unsigned long long>(workspace, L.off_tiles);
+    sp.R = n + 1;
+    sp.parents = draft_parents;
+    sp.path = path;
+    sp.walk = at<sv::TreeWalk>(workspace, L.off_walk);
+    sp.trows = at<char>(workspace, L.off_trows);
+    sp.can_pend = max_rounds > 0;
+    hipError_t e = sv::launch_tree_sample(sp, kdt, aligned, s);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int r = 0; r < max_rounds; ++r) {
+        sv::RoundParams rp{};
+        rp.target = target_logits;
+        rp.draft = draft_logits;
+        rp.tokens = draft_tokens;
+        rp.parents = draft_parents;
+        rp.lens = draft_lens;
+        rp.unif = uniforms;
+        rp.B = B; rp.n = n; rp.V = V; rp.NT = L.NT; rp.NCd = L.NCd;
+        rp.walk = sp.walk;
+        rp.trows = sp.trows;
+        rp.can_pend = r + 1 < max_rounds;
+        rp.dsum = at<float>(workspace, L.off_dsum);
+        rp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+        rp.desc = sp.desc;
+        rp.acc = accepted_len;
+        rp.emitted = emitted;
+        rp.path = path;
+        rp.flags = err_flags;
+        e = sv::launch_tree_round(rp, kdt, aligned, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    sv::DrawParams dp{};
+    dp.target = target_logits;
+    dp.draft = draft_logits;
+    dp.B = B; dp.n = n; dp.V = V; dp.NT = L.NT; dp.NCd = L.NCd;
+    dp.R = n + 1;
+    dp.row_index = nullptr;
+    dp.tiles = sp.tiles;
+    dp.emitted = emitted;
+    dp.flags = err_flags;
+    dp.desc = sp.desc;
+    dp.dsum = at<float>(workspace, L.off_dsum);
+    dp.cnt = at<uint32_t>(workspace, L.off_cnt_draw);
+    e = sv::launch_draw(dp, kdt, aligned, s);
     return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 

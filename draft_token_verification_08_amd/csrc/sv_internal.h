@@ -35,8 +35,10 @@ constexpr int kDrawSums = 4;         // per-tile sums a residual draw chunk hand
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
 
-// kinds of the final draw of a sequence
-enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
+// kinds of the final draw of a sequence: a bonus draw from target row L's tile
+// partials, a residual draw max(0, p_k - lamq q_k) from row pair k, or a draw
+// from the whole of target row k alone (the bonus token at a tree's leaf)
+enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2, kDrawTarget = 3 };
 
 // One 64-bit slot per (sequence, row slot, vocab chunk), exchanged atomically:
 //   sampling rows: low word chunk max m_c, high word sum over the chunk of 2^((z - m_c) c)
@@ -46,17 +48,55 @@ struct Partial {
     float b;
 };
 
-// Per sequence, written by the decision and read by the draw pass.
+// Per sequence, written by the decision and read by the draw pass.  A zero
+// descriptor is kDrawNone.
 struct DrawDesc {
     int kind;       // DrawKind
     int k;          // row index of the draw (target row k, and draft row k if residual)
+    int slot;       // output slot of the drawn token (emitted[b][slot])
     float c;        // log2(e) / T as used for every exponent of this sequence
     float m_t;      // max of target row k
     float m_d;      // max of draft row k (residual only)
     float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
+    float lamq;     // residual weights max(0, p - lamq q): 1 after one rejection (tree walks: more)
     float pad;
 };
+
+// A sampling tree walk (per sequence), kept in the workspace between the
+// statistics pass, the rounds and the draw pass.
+enum WalkStatus : int { kWalkIdle = 0, kWalkPending = 1 };
+struct TreeWalk {
+    int status;     // WalkStatus: pending = the walk needs M at lam for node u
+    int u;          // current node
+    int next;       // the next child to test is the first node j + 1 with j >= next below u
+    int depth;      // nodes on the kept path so far
+    double lam;     // lam_k at node u (0: no child rejected yet)
+    double M;       // M_k = sum max(0, p_u - lam q_u) (1 while lam = 0)
+    uint32_t flags;
+    float c;        // log2(e) / T
+    int path[kMaxDraft];
+};
+
+// Per-sequence rows of a sampling tree walk: the statistics of target rows
+// 0..n and draft rows 0..n-1, and each node's gathered logits (node j + 1:
+// target and draft logit of x_j in its parent's rows).  Byte offsets inside a
+// sequence's block of tree_rows_stride(n) bytes.
+struct TreeRowsLayout {
+    int mt, St, md, Sd, gt, gd, stride;
+};
+__host__ __device__ inline TreeRowsLayout tree_rows_layout(int n) {
+    auto up8 = [](int x) { return (x + 7) / 8 * 8; };
+    TreeRowsLayout l;
+    l.mt = 0;
+    l.St = up8(4 * (n + 1));
+    l.md = l.St + 8 * (n + 1);
+    l.Sd = up8(l.md + 4 * n);
+    l.gt = l.Sd + 8 * n;
+    l.gd = l.gt + 4 * n;
+    l.stride = (l.gd + 4 * n + 15) / 16 * 16;
+    return l;
+}
 
 // Workspace layout (byte offsets from the workspace base; every region 256-aligned).
 struct Layout {
@@ -70,6 +110,8 @@ struct Layout {
     size_t off_desc;     // DrawDesc [B]
     size_t off_tiles;    // uint64 [B][NT] tile partials (m_t, s_t) of target row L (sampling)
     size_t off_dsum;     // float [B][kDrawSums][NT] per-tile sums of the residual draw (draw pass)
+    size_t off_walk;     // TreeWalk [B] (sampling tree walks)
+    size_t off_trows;    // [B][tree_rows_layout(n).stride] bytes (sampling tree walks)
     size_t off_acc;      // int32 [B] accepted lengths of sv_sample_rows (always 0)
     size_t bytes;
 };
@@ -111,6 +153,31 @@ struct StatsParams {
                               // draw pass runs; row 0's tile partials are then exchanged atomically
     const int32_t* parents;   // [B][n] tree verification: node j + 1 hangs below node parents[j]
     int32_t* path;            // [B][n] or nullptr: the kept path's node indices (tree verification)
+    TreeWalk* walk;           // [B] sampling tree walks
+    char* trows;              // [B][stride] sampling tree walks' rows
+    int can_pend;             // a sampling tree walk may stop to wait for a round (rounds follow)
+};
+
+// One round of the sampling tree walks: the residual mass of every pending
+// walk's row pair, then the walk goes on.
+struct RoundParams {
+    const void* target;       // [B][n+1][V]
+    const void* draft;        // [B][n][V]
+    const int32_t* tokens;    // [B][n]
+    const int32_t* parents;   // [B][n]
+    const int32_t* lens;      // [B]
+    const float* unif;        // [B][n+1]
+    int B, n, V, NT, NCd;
+    TreeWalk* walk;
+    char* trows;
+    int can_pend;             // not the last round
+    float* dsum;              // [B][kDrawSums][NT]
+    uint32_t* cnt;            // [B]
+    DrawDesc* desc;           // [B]
+    int32_t* acc;
+    int32_t* emitted;
+    int32_t* path;            // or nullptr
+    uint32_t* flags;          // or nullptr
 };
 
 struct DrawParams {
@@ -168,6 +235,8 @@ sv_status_t hip_status(hipError_t e);
 // launches (sv_kernels.hip, sv_lmhead.hip); return the hipGetLastError() after the launch
 hipError_t launch_stats(const StatsParams& p, Dt dt, Mode mode, bool aligned, hipStream_t s);
 hipError_t launch_tree(const StatsParams& p, Dt dt, bool aligned, hipStream_t s);
+hipError_t launch_tree_sample(const StatsParams& p, Dt dt, bool aligned, hipStream_t s);
+hipError_t launch_tree_round(const RoundParams& p, Dt dt, bool aligned, hipStream_t s);
 hipError_t launch_draw(const DrawParams& p, Dt dt, bool aligned, hipStream_t s);
 hipError_t launch_mtp(const MtpParams& p, bool aligned, hipStream_t s);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);

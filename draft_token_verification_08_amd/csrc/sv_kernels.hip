@@ -677,7 +677,9 @@ __device__ __forceinline__ NearTerm near_term(float Mc, float c, float zt, float
 //   kWResFar:   max(0, P - lam Q) with P = 2^((z_t - m_t) c), Q = 2^((z_d - m_d) c),
 //               each row scaled by its own maximum (mA = m_t) and lam the ratio of
 //               their sums (S_t / S_d);
-//   kWResNear:  max(0, rho A - Dl) of near_term() with M = mA (Mc = fl(mA c)).
+//   kWResNear:  max(0, rho A - opm Dl) of near_term() with M = mA (Mc = fl(mA c)):
+//               the residual max(0, p - lam q) with rho = rho' - (lam - 1) and
+//               opm = lam (rho' = S'_d / S'_t - 1; lam = 1 after one rejection).
 enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
 struct WSpec {
     int mode;
@@ -687,6 +689,7 @@ struct WSpec {
     float lam;  // kWResFar
     float rho;  // kWResNear
     float Mc;   // kWResNear: fl(mA c)
+    float opm;  // kWResNear
 };
 __device__ __forceinline__ float far_p(float mt, float c, float zt) { return exp2_fast((zt - mt) * c); }
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
@@ -697,10 +700,10 @@ __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd)
         return fmaxf(fmaf(-s.lam, Q, P), 0.f);
     }
     const NearTerm t = near_term(s.Mc, s.c, zt, zd);
-    return fmaxf(fmaf(s.rho, t.A, -t.Dl), 0.f);
+    return fmaxf(fmaf(s.rho, t.A, -s.opm * t.Dl), 0.f);
 }
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
-    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f};
+    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f};
 }
 
 // Scan one tile: returns the element whose running weight (starting at P)
@@ -981,6 +984,213 @@ __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const Seq
     }
 }
 
+// --------------------------------------------------------------- sampling tree walks
+// Sampling tree verification ("Accelerating Sonar through speculation", EAGLE
+// section: the target scores the draft's candidate tree, the longest suitable
+// sequence is kept, one target token appended), with SpecInfer's multi-step
+// speculative sampling as the acceptance rule.  At node u the children are
+// tested in index order against the current target residual: child j + 1 is
+// accepted iff u[j] < max(0, p_u(x) - lam q_u(x)) / (M q_u(x)), where after k
+// rejections at u lam = lam_k and M = M_k = sum max(0, p_u - lam_k q_u)
+// (lam_0 = 0, M_0 = 1, lam_{k+1} = lam_k + M_k).  An accepted child moves the
+// walk down; with no child left the token is drawn from max(0, p_u - lam q_u)
+// (from p_u itself when u has no children).  The first test at a node needs
+// only the rows' statistics; each later one needs M_k, a full reduction of the
+// pair (p_u, q_u), which a round kernel provides: the walk then stops, pending.
+
+// One sequence's walk inputs, staged in LDS: statistics of target rows (mt, St)
+// and draft rows (md, Sd) by node, and node j + 1's token, parent (-1 when not
+// an earlier node) and gathered logits gt = z_t[parent][x_j], gd = z_d[parent][x_j].
+struct WalkRows {
+    const float* mt;
+    const double* St;
+    const float* md;
+    const double* Sd;
+    const float* gt;
+    const float* gd;
+    const int* x;
+    const int* par;
+};
+
+// The acceptance ratio of node j + 1 below node u at (lam, M).  lam = 0 forms
+// p/q as the linear decision does.
+__device__ double tree_ratio(const WalkRows& r, int j, int u, int V, float c, double lam, double M) {
+    const int x = r.x[j];
+    if (x < 0 || x >= V) return 0.0;
+    const float zt = r.gt[j], zd = r.gd[j];
+    const bool pz = zt == -INFINITY, qz = zd == -INFINITY;
+    const double cd = (double)c;
+    if (lam == 0.0) {
+        if (qz) return pz ? 0.0 : INFINITY;
+        if (pz) return 0.0;
+        const double lr = ((double)zt - (double)r.mt[u]) * cd - ((double)zd - (double)r.md[u]) * cd;
+        return exp2(lr) * (r.Sd[u] / r.St[u]);
+    }
+    const double pv = pz ? 0.0 : exp2(((double)zt - (double)r.mt[u]) * cd) / r.St[u];
+    const double qv = qz ? 0.0 : exp2(((double)zd - (double)r.md[u]) * cd) / r.Sd[u];
+    const double num = pv - lam * qv;
+    if (!(num > 0.0) || !(M > 0.0)) return 0.0;
+    return qv > 0.0 ? num / (M * qv) : INFINITY;
+}
+
+// Runs the walk from its state (one thread).  Returns true when it has
+// finished: *d then describes the draw (kDrawTarget at a node with no child
+// left and no rejection, else kDrawResidual with lamq = lam).  Returns false,
+// with the state pending, when the next test needs M at the current lam (only
+// if can_pend; otherwise the children not yet tested are left out, which is the
+// same rule on a smaller tree, and SV_FLAG_TREE_TRUNCATED is raised).
+__device__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, int L, int V, const float* uni, bool can_pend,
+                              DrawDesc* d) {
+    for (;;) {
+        int j = -1;
+        for (int t = w.next; t < L; ++t)
+            if (r.par[t] == w.u) {
+                j = t;
+                break;
+            }
+        if (j < 0) {  // no child left to test at u
+            const int u = w.u;
+            *d = DrawDesc{};
+            d->k = u;
+            d->slot = w.depth;
+            d->c = w.c;
+            d->m_t = r.mt[u];
+            if (w.lam == 0.0) {
+                d->kind = kDrawTarget;
+                d->m_d = r.mt[u];
+                d->lamq = 0.f;
+            } else {
+                d->kind = kDrawResidual;
+                d->m_d = r.md[u];
+                d->lq = (float)log2(r.St[u] / r.Sd[u]);
+                d->lamq = (float)w.lam;
+            }
+            w.status = kWalkIdle;
+            return true;
+        }
+        if (w.lam > 0.0 && !(w.M >= 0.0)) {  // M at lam not known yet
+            if (can_pend) {
+                w.next = j;
+                w.status = kWalkPending;
+                return false;
+            }
+            w.flags |= SV_FLAG_TREE_TRUNCATED;
+            w.next = L;
+            continue;
+        }
+        const double ratio = tree_ratio(r, j, w.u, V, w.c, w.lam, w.M);
+        const double uj = sanitize_u(uni[j], w.flags);
+        if (uj < ratio) {  // accepted: one level down
+            w.path[w.depth++] = j + 1;
+            w.u = j + 1;
+            w.lam = 0.0;
+            w.M = 1.0;
+        } else {  // rejected: the residual loses q_u once more
+            w.lam = w.lam + w.M;
+            w.M = -1.0;
+        }
+        w.next = j + 1;
+    }
+}
+
+// Writes a finished walk's outputs (accepted length, emitted prefix, -1 in the
+// drawn slot and after it, the path) and its draw descriptor; one thread.
+__device__ void tree_walk_finish(const TreeWalk& w, DrawDesc d, const int* x, int n, float u_final, int32_t* acc,
+                                 int32_t* emitted, int32_t* path, DrawDesc* desc, uint32_t* flags, int b) {
+    uint32_t f = w.flags;
+    d.u = (float)sanitize_u(u_final, f);
+    desc[b] = d;
+    acc[b] = w.depth;
+    int32_t* e = emitted + (size_t)b * (n + 1);
+    for (int i = 0; i <= n; ++i) e[i] = i < w.depth ? x[w.path[i] - 1] : -1;
+    if (path)
+        for (int i = 0; i < n; ++i) path[(size_t)b * n + i] = i < w.depth ? w.path[i] : -1;
+    if (f && flags) atomicOr(flags, f);
+}
+
+// Stores (pending) or clears (finished) a walk's persistent state: the walk and
+// its rows block, which stay zero while no walk is pending.
+__device__ void tree_walk_store(const TreeWalk& w, bool pending, const WalkRows& r, int L, int n, TreeWalk* gw,
+                                char* rows) {
+    const TreeRowsLayout lay = tree_rows_layout(n);
+    float* mt = reinterpret_cast<float*>(rows + lay.mt);
+    double* St = reinterpret_cast<double*>(rows + lay.St);
+    float* md = reinterpret_cast<float*>(rows + lay.md);
+    double* Sd = reinterpret_cast<double*>(rows + lay.Sd);
+    float* gt = reinterpret_cast<float*>(rows + lay.gt);
+    float* gd = reinterpret_cast<float*>(rows + lay.gd);
+    for (int i = 0; i <= L; ++i) {
+        mt[i] = pending ? r.mt[i] : 0.f;
+        St[i] = pending ? r.St[i] : 0.0;
+    }
+    for (int i = 0; i < L; ++i) {
+        md[i] = pending ? r.md[i] : 0.f;
+        Sd[i] = pending ? r.Sd[i] : 0.0;
+        gt[i] = pending ? r.gt[i] : 0.f;
+        gd[i] = pending ? r.gd[i] : 0.f;
+    }
+    if (pending) *gw = w;
+    else *gw = TreeWalk{};
+}
+
+// The statistics pass's decision for a sampling tree (T > 0): stage the walk's
+// rows (statistics merged in LDS, gathered logits), flag bad parents and tokens,
+// run the walk from the root.
+__device__ void tree_sample_decide(const StatsParams& p, int b, const SeqInfo& si, float* s_m, double* s_S,
+                                   const void* target, const void* draft, bool bf16) {
+    __shared__ int s_x[kMaxDraft], s_par[kMaxDraft];
+    __shared__ float s_gt[kMaxDraft], s_gd[kMaxDraft];
+    const int tid = threadIdx.x, n = p.n, V = p.V, L = si.L;
+    uint32_t bad = 0;
+    if (tid < 64) {
+        const int j = tid;
+        bool oor = false, badp = false;
+        if (j < L) {
+            const int x = p.tokens[(size_t)b * n + j];
+            const int par = p.parents[(size_t)b * n + j];
+            badp = !(par >= 0 && par <= j);
+            oor = x < 0 || x >= V;
+            float gt = -INFINITY, gd = -INFINITY;
+            if (!badp && !oor) {
+                const size_t tr = (size_t)b * (n + 1) + par, dr = (size_t)b * n + par;
+                if (bf16) {
+                    gt = __uint_as_float(((uint32_t)((const uint16_t*)target)[tr * V + x]) << 16);
+                    gd = __uint_as_float(((uint32_t)((const uint16_t*)draft)[dr * V + x]) << 16);
+                } else {
+                    gt = ((const float*)target)[tr * V + x];
+                    gd = ((const float*)draft)[dr * V + x];
+                }
+            }
+            s_x[j] = x;
+            s_par[j] = badp ? -1 : par;
+            s_gt[j] = gt;
+            s_gd[j] = gd;
+        }
+        const unsigned long long mo = __ballot(oor), mb = __ballot(badp);
+        bad = (mo ? (uint32_t)SV_FLAG_TOKEN_OOR : 0u) | (mb ? (uint32_t)SV_FLAG_BAD_PARENT : 0u);
+    }
+    __shared__ TreeWalk s_walk;  // the walk's state (LDS: its path is indexed at run time)
+    __shared__ uint32_t s_bad;
+    if (tid == 0) s_bad = bad;
+    __syncthreads();
+    if (tid == 0) {
+        const WalkRows r{s_m, s_S, s_m + n + 1, s_S + n + 1, s_gt, s_gd, s_x, s_par};
+        TreeWalk& w = s_walk;
+        w = TreeWalk{};
+        w.u = 0;
+        w.M = 1.0;
+        w.c = exp2_scale(si.T);
+        w.flags = si.flags | s_bad;
+        DrawDesc d;
+        const float* uni = p.unif + (size_t)b * (n + 1);
+        if (tree_walk_run(w, r, L, V, uni, p.can_pend != 0, &d))
+            tree_walk_finish(w, d, s_x, n, uni[n], p.acc, p.emitted, p.path, p.desc, p.flags, b);
+        else
+            tree_walk_store(w, true, r, L, n, p.walk + b, p.trows + (size_t)b * tree_rows_layout(n).stride);
+        xchg32(&p.cnt[b], 0u);  // leave the counter zero for the next call
+    }
+}
+
 // The greedy decision of sequence b after its argmax keys are merged (g[r] in
 // s_idx): the longest prefix of drafts equal to g, then g at the first mismatch.
 // One wave writes the outputs, lane j its own emitted slot and, with the fused
@@ -1071,7 +1281,8 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     }
     __syncthreads();
     if constexpr (TREE) {
-        tree_walk(p, b, si, s_idx);
+        if (MODE == kGreedy || si.greedy) tree_walk(p, b, si, s_idx);
+        else tree_sample_decide(p, b, si, s_m, s_S, p.target, p.draft, DT == kBF16);
         return;
     }
     if constexpr (MODE == kGreedy) {
@@ -1188,6 +1399,8 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             DrawDesc d;
             d.kind = (k < L) ? kDrawResidual : kDrawBonus;
             d.k = k;
+            d.slot = k;
+            d.lamq = 1.f;
             d.c = cf;
             d.m_t = s_m[k];
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
@@ -1211,8 +1424,8 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             const int y = tile_draw<DT, ALIGNED, true>(p.tiles + (size_t)b * p.NT, p.NT, V, d, trow,
                                                        reinterpret_cast<double*>(s_part));
             if (tid == 0) {
-                p.emitted[(size_t)b * (n + 1) + d.k] = y;
-                if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + d.k] = y;
+                p.emitted[(size_t)b * (n + 1) + d.slot] = y;
+                if (p.mtp.tokens) p.mtp.tokens[(size_t)b * (n + 1) + d.slot] = y;
             }
         }
     }
@@ -1269,7 +1482,7 @@ __device__ __forceinline__ void stats_pass(StatsParams p) {
         const float cf = exp2_scale(si.T);
         // target row L is the only row a bonus token can be drawn from: it alone
         // streams in tiles and keeps per-tile partials
-        const MS r = (target_row && slot == si.L)
+        const MS r = (target_row && slot == si.L && !TREE)
                          ? wg_softmax_tiles<DT, ALIGNED>(row, lo, hi, cf, p.tiles + (size_t)b * p.NT, DRAW)
                          : block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
         if (threadIdx.x == 0) {
@@ -1295,6 +1508,12 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_stats_tree(StatsParams p) {
     stats_pass<DT, kGreedy, ALIGNED, false, true>(p);
+}
+// Sampling tree verification: the sampling statistics pass over the tree's node
+// rows, then the walk from the root.
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_stats_tree_sample(StatsParams p) {
+    stats_pass<DT, kSample, ALIGNED, false, true>(p);
 }
 // Sampling calls with no drafts: the statistics pass whose decision also makes
 // the (bonus) draw, so no draw pass follows.
@@ -1381,13 +1600,16 @@ __device__ __forceinline__ float far_sum_at(const FarSums& s, int q) {
 }
 
 // The near form of one row pair, formed by one workgroup from the rows
-// themselves: first rho = sum Dl / sum A over the whole pair, then each tile's
-// exact weight sum max(0, rho A - Dl) into s_w[NT].  Returns rho (binary32, as
-// the tile scan uses it); *Z receives the sum of the tile weights.  Wave w
-// takes tiles w, w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
+// themselves: first rho' = sum Dl / sum A over the whole pair, then each tile's
+// exact weight sum max(0, rho A - lam Dl) with rho = rho' - (lam - 1) into
+// s_w[NT] (the residual max(0, p - lam q); p - lam q = (rho A - lam Dl) /
+// (S'_t (1 + rho'))).  Returns rho (binary32, as the tile scan uses it); *Z
+// receives the sum of the tile weights and *mass the residual mass
+// sum max(0, p - lam q).  Wave w takes tiles w, w + kWaves, ...; lane l the
+// vectors l, l + 64, ... of a tile.
 template <int DT, bool ALIGNED>
-__device__ float near_exact_tiles(const void* trow, const void* drow, int V, int NT, float Mc, float c, double* s_w,
-                                  double* Z) {
+__device__ float near_exact_tiles(const void* trow, const void* drow, int V, int NT, float Mc, float c, float lam,
+                                  double* s_w, double* Z, double* mass) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     constexpr int kU = kThreads / 64;
@@ -1429,7 +1651,8 @@ __device__ float near_exact_tiles(const void* trow, const void* drow, int V, int
     }
     if (lane != 0) X = D = 0.0;  // every lane of a wave holds the wave's sums
     block_sum2_all(X, D);
-    const float rho = (float)(D / X);
+    const double rho1 = D / X;
+    const float rho = (float)(rho1 - ((double)lam - 1.0));
     double zsum = 0.0, unused = 0.0;
     for (int t = w; t < NT; t += kWaves) {
         uint4 wt[kU], wd[kU];
@@ -1443,7 +1666,7 @@ __device__ float near_exact_tiles(const void* trow, const void* drow, int V, int
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 const NearTerm tm = near_term(Mc, c, zt[e], zd[e]);
-                sw += fmaxf(fmaf(rho, tm.A, -tm.Dl), 0.f);
+                sw += fmaxf(fmaf(rho, tm.A, -lam * tm.Dl), 0.f);
             }
         }
         sw = wave_sum(sw);
@@ -1454,17 +1677,19 @@ __device__ float near_exact_tiles(const void* trow, const void* drow, int V, int
     }
     block_sum2_all(zsum, unused);
     *Z = zsum;
+    *mass = zsum / (X * (1.0 + rho1));
     return rho;
 }
 
 // The residual draw's set-up in the deciding workgroup, from the far-form tile
-// sums v[r][*] of tiles tid + r kThreads: the tile weights into s_w[NT], the
-// element weighting into *ws, the residual total into *Z (at or below zero:
-// no residual mass left, s_w then holds the target's own tile masses and *ws
-// weighs by the target).  *near_out: the near form was used.
+// sums v[r][*] of tiles tid + r kThreads, for the residual max(0, p - lq q) with
+// lq = d.lamq: the tile weights into s_w[NT], the element weighting into *ws,
+// the total of the tile weights into *Z (at or below zero: no residual mass
+// left, s_w then holds the target's own tile masses, *ws weighs by the target
+// and -*Z is their total), the residual mass sum max(0, p - lq q) into *mass.
 template <int DT, bool ALIGNED, int TPT>
 __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& d, const void* trow, const void* drow,
-                              int V, double* s_w, WSpec* ws, double* Z, bool* near_out, double* lam_out) {
+                              int V, double* s_w, WSpec* ws, double* Z, double* mass) {
     const int tid = threadIdx.x;
     double sp = 0.0, sq = 0.0;
 #pragma unroll
@@ -1473,14 +1698,15 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
         sq += (double)v[r][kSumQ];
     }
     block_sum2_all(sp, sq);
-    const double lam = sq > 0.0 ? sp / sq : 0.0;
-    const double lam0 = exp2((double)d.lq);
+    const double lq = (double)d.lamq;
+    const double Lam = sq > 0.0 ? lq * (sp / sq) : 0.0;  // lq S_t / S_d from the same terms
+    const double Lam0 = lq * exp2((double)d.lq);
     double zr = 0.0, zp = 0.0;
 #pragma unroll
     for (int r = 0; r < TPT; ++r) {
         const int i = tid + r * kThreads;
         if (i < NT) {
-            double w = (double)v[r][kSumW] - (lam - lam0) * (double)v[r][kSumG];
+            double w = (double)v[r][kSumW] - (Lam - Lam0) * (double)v[r][kSumG];
             w = w > 0.0 ? w : 0.0;
             s_w[i] = w;
             zr += w;
@@ -1488,19 +1714,17 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
         }
     }
     block_sum2_all(zr, zp);
-    *lam_out = lam;
-    *near_out = false;
-    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)lam, 0.f, 0.f};
+    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, 0.f};
+    *mass = sp > 0.0 ? zr / sp : 0.0;
     const bool close = fabs(((double)d.m_d - (double)d.m_t) * (double)d.c) <= 32.0;
-    if (close && zr < kNearZ * sp) {
+    if (close && sq > 0.0 && zr < kNearZ * sp) {
         // small residual: the near form, exactly, by this workgroup alone
         // (both rows scaled by M = max(m_t, m_d); the maxima lie within 2^32)
         const float M = fmaxf(d.m_t, d.m_d);
         const float Mc = M * d.c;
         __syncthreads();
-        const float rho = near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, Mc, d.c, s_w, &zr);
-        *ws = WSpec{kWResNear, d.c, M, 0.f, 0.f, rho, Mc};
-        *near_out = true;
+        const float rho = near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, Mc, d.c, d.lamq, s_w, &zr, mass);
+        *ws = WSpec{kWResNear, d.c, M, 0.f, 0.f, rho, Mc, d.lamq};
     }
     if (!(zr > 0.0)) {
         // no residual mass left after rounding: draw from p_k
@@ -1511,44 +1735,31 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
             if (i < NT) s_w[i] = (double)v[r][kSumP];
         }
         *ws = target_spec(d);
-        zr = -zp;  // the caller draws from the target's masses (total zp)
+        *mass = 0.0;
+        zr = -zp;
     }
     *Z = zr;
     __syncthreads();
 }
 
+// One chunk of a residual reduction of the pair (trow, drow) (drow unused when
+// !has_draft: the target row alone): its tiles [c kDrawTiles, ...) loaded once
+// (wave w owns kDrawTiles / kWaves whole tiles, lane l reads vectors l, l + 64,
+// ... of each, all loads issued before the first use), the far-form tile sums
+// at lam0 = d.lamq 2^d.lq handed over by atomic exchange into dsum[q][tile],
+// completed before the function returns.
 template <int DT, bool ALIGNED>
-__device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, double* s_buf) {
+__device__ __forceinline__ void residual_chunk(const void* trow, const void* drow, bool has_draft, const DrawDesc& d,
+                                               int V, int NT, int c, unsigned* dsum) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
-    const DrawDesc d = p.desc[b];
-    if (d.kind == kDrawNone) return;
-    const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
-    const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
-    if (d.kind == kDrawBonus) {
-        if (c != 0) return;
-        const int y = tile_draw<DT, ALIGNED, false>(p.tiles + (size_t)b * NT, NT, V, d, trow, s_buf);
-        for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;  // used: leave zero
-        if (tid == 0) {
-            p.emitted[(size_t)b * (n + 1) + d.k] = y;
-            if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.k] = y;
-            p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        }
-        return;
-    }
-    const void* drow = row_ptr<DT>(p.draft, (long long)b * n + d.k, V);
-    const float lam0 = exp2_fast(d.lq);
-    unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
-
-    // chunk c: tiles [tile0, tile0 + cnt).  Wave w owns kTilesPerWave whole tiles
-    // (lane l reads vectors l, l + 64, ... of each, coalesced), so every tile sum
-    // is one wave reduction; all loads are issued before the first use.
     constexpr int kTilesPerWave = kDrawTiles / kWaves;
     constexpr int kU = kThreads / 64;  // vectors per lane per tile
     static_assert(kDrawTiles % kWaves == 0, "draw chunk must split evenly over the waves");
+    const float lam0 = d.lamq * exp2_fast(d.lq);
     const int tile0 = c * kDrawTiles;
     const int cnt = min(kDrawTiles, NT - tile0);
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     // raw 16-byte vectors (bf16 pairs or fp32), widened where they are used
     uint4 rt[kTilesPerWave][kU], rd[kTilesPerWave][kU];
 #pragma unroll
@@ -1559,10 +1770,10 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
             const bool ok = wv * kTilesPerWave + i < cnt && e0 < V;
             if constexpr (ALIGNED) {
                 rt[i][u] = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
-                rd[i][u] = ok ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+                rd[i][u] = (ok && has_draft) ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
             } else {
                 rt[i][u] = load_raw<DT>(trow, e0, ok ? V : 0);
-                rd[i][u] = load_raw<DT>(drow, e0, ok ? V : 0);
+                rd[i][u] = load_raw<DT>(drow, e0, (ok && has_draft) ? V : 0);
             }
         }
     unsigned dep = 0u;
@@ -1584,6 +1795,43 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     // this wave's exchanges have been performed before the workgroup arrives
     asm volatile("" ::"v"(dep));
     __builtin_amdgcn_s_waitcnt(0);
+}
+
+constexpr int kTPT = kMaxTiles / kThreads;  // tiles per thread, at most, in the deciding workgroup
+
+// The deciding workgroup collects (and resets to zero) the tile sums of the whole
+// row pair: v[r][q] = sum q of tile tid + r kThreads.
+__device__ __forceinline__ void collect_tile_sums(float (&v)[kTPT][4], int NT, unsigned* dsum) {
+#pragma unroll
+    for (int r = 0; r < kTPT; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[r][q] = (i < NT) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
+    }
+}
+
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, double* s_buf) {
+    const DrawDesc d = p.desc[b];
+    if (d.kind == kDrawNone) return;
+    const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
+    const void* trow = row_ptr<DT>(p.target, target_row_of(p.R, p.row_index, b, d.k), V);
+    if (d.kind == kDrawBonus) {
+        if (c != 0) return;
+        const int y = tile_draw<DT, ALIGNED, false>(p.tiles + (size_t)b * NT, NT, V, d, trow, s_buf);
+        for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;  // used: leave zero
+        if (tid == 0) {
+            p.emitted[(size_t)b * (n + 1) + d.slot] = y;
+            if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.slot] = y;
+            p.desc[b] = DrawDesc{};
+        }
+        return;
+    }
+    // kDrawTarget: the whole of target row k alone (no draft row: Q = 0, W = P)
+    const bool has_draft = d.kind == kDrawResidual;
+    const void* drow = has_draft ? row_ptr<DT>(p.draft, (long long)b * n + d.k, V) : nullptr;
+    unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
+    residual_chunk<DT, ALIGNED>(trow, drow, has_draft, d, V, NT, c, dsum);
     __syncthreads();
     __shared__ int s_last;
     if (tid == 0) s_last = (arrive(&p.cnt[b], 0ull) == (unsigned)p.NCd - 1u);
@@ -1591,18 +1839,12 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     if (!s_last) return;
 
     // last workgroup: collect (and reset) the per-tile sums of the whole row pair
-    constexpr int kTPT = kMaxTiles / kThreads;  // tiles per thread, at most
     float v[kTPT][4];
-#pragma unroll
-    for (int r = 0; r < kTPT; ++r) {
-        const int i = tid + r * kThreads;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[r][q] = (i < NT) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
-    }
+    collect_tile_sums(v, NT, dsum);
     WSpec ws;
-    double Z, lam;
-    bool near;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &near, &lam);
+    double Z, mass;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &mass);
+    if (!has_draft) ws = target_spec(d);  // weights P: the target row's own distribution
     if (Z <= 0.0 && tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
     const double t = (double)d.u * fabs(Z);
     const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_buf[i]; });
@@ -1620,9 +1862,84 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     // row L's tile partials (written by the stats pass, unused here): leave them zero
     for (int i = tid; i < NT; i += kThreads) p.tiles[(size_t)b * NT + i] = 0ull;
     if (tid == 0) {
-        p.emitted[(size_t)b * (n + 1) + d.k] = y;
-        if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.k] = y;
-        p.desc[b] = DrawDesc{kDrawNone, 0, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        p.emitted[(size_t)b * (n + 1) + d.slot] = y;
+        if (p.mtp_tokens) p.mtp_tokens[(size_t)b * (n + 1) + d.slot] = y;
+        p.desc[b] = DrawDesc{};
+        xchg32(&p.cnt[b], 0u);
+    }
+}
+
+// One round of the sampling tree walks, workgroup (b, c): if sequence b's walk
+// is pending at node u with lam, chunk c of the residual reduction of the pair
+// (target row u, draft row u); the last workgroup forms M = sum max(0, p_u -
+// lam q_u) (plan_residual: exact ratio, near form when small) and runs the walk
+// on: it finishes (outputs, draw descriptor; its state cleared) or stops
+// pending again for the next round.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, double* s_buf) {
+    const TreeWalk* gw = p.walk + b;
+    if (gw->status != kWalkPending) return;
+    const int n = p.n, V = p.V, NT = p.NT, tid = threadIdx.x;
+    const int u = gw->u;
+    const TreeRowsLayout lay = tree_rows_layout(n);
+    char* rows = p.trows + (size_t)b * lay.stride;
+    const float* gmt = reinterpret_cast<const float*>(rows + lay.mt);
+    const double* gSt = reinterpret_cast<const double*>(rows + lay.St);
+    const float* gmd = reinterpret_cast<const float*>(rows + lay.md);
+    const double* gSd = reinterpret_cast<const double*>(rows + lay.Sd);
+    DrawDesc d{};
+    d.kind = kDrawResidual;
+    d.k = u;
+    d.c = gw->c;
+    d.m_t = gmt[u];
+    d.m_d = gmd[u];
+    d.lq = (float)log2(gSt[u] / gSd[u]);
+    d.lamq = (float)gw->lam;
+    const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + u, V);
+    const void* drow = row_ptr<DT>(p.draft, (long long)b * n + u, V);
+    unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
+    residual_chunk<DT, ALIGNED>(trow, drow, true, d, V, NT, c, dsum);
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) s_last = (arrive(&p.cnt[b], 0ull) == (unsigned)p.NCd - 1u);
+    __syncthreads();
+    if (!s_last) return;
+
+    float v[kTPT][4];
+    collect_tile_sums(v, NT, dsum);
+    WSpec ws;
+    double Z, mass;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &mass);
+    // the walk's rows, staged in LDS
+    __shared__ float s_mt[kMaxDraft + 1], s_md[kMaxDraft], s_gt[kMaxDraft], s_gd[kMaxDraft];
+    __shared__ double s_St[kMaxDraft + 1], s_Sd[kMaxDraft];
+    __shared__ int s_x[kMaxDraft], s_par[kMaxDraft];
+    const int L = min(max(p.lens[b], 0), n);
+    for (int i = tid; i <= L; i += kThreads) {
+        s_mt[i] = gmt[i];
+        s_St[i] = gSt[i];
+    }
+    for (int j = tid; j < L; j += kThreads) {
+        s_md[j] = gmd[j];
+        s_Sd[j] = gSd[j];
+        s_gt[j] = reinterpret_cast<const float*>(rows + lay.gt)[j];
+        s_gd[j] = reinterpret_cast<const float*>(rows + lay.gd)[j];
+        s_x[j] = p.tokens[(size_t)b * n + j];
+        const int par = p.parents[(size_t)b * n + j];
+        s_par[j] = (par >= 0 && par <= j) ? par : -1;
+    }
+    __shared__ TreeWalk s_walk;  // the walk's state (LDS: its path is indexed at run time)
+    __syncthreads();
+    if (tid == 0) {
+        const WalkRows r{s_mt, s_St, s_md, s_Sd, s_gt, s_gd, s_x, s_par};
+        TreeWalk& w = s_walk;
+        w = *gw;
+        w.M = mass;
+        DrawDesc dd;
+        const float* uni = p.unif + (size_t)b * (n + 1);
+        const bool done = tree_walk_run(w, r, L, V, uni, p.can_pend != 0, &dd);
+        if (done) tree_walk_finish(w, dd, s_x, n, uni[n], p.acc, p.emitted, p.path, p.desc, p.flags, b);
+        tree_walk_store(w, !done, r, L, n, p.walk + b, rows);
         xchg32(&p.cnt[b], 0u);
     }
 }
@@ -1640,6 +1957,13 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_draw_unaligned(DrawParams p) {
     __shared__ double s_buf[kMaxTiles];
     draw_item<DT, false>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
+}
+
+// One round of the sampling tree walks (the draw pass's layout).
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k_tree_round(RoundParams p) {
+    __shared__ double s_buf[kMaxTiles];
+    round_item<DT, ALIGNED>(p, blockIdx.x / p.NCd, blockIdx.x % p.NCd, s_buf);
 }
 
 // --------------------------------------------------------------- MTP shift / insert
@@ -1748,7 +2072,13 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     const MS bq = wg_softmax_tiles<DT, ALIGNED>(drow, 0, V, c, nullptr);
     if (tid == 0) s_d = bq;
     __syncthreads();
-    DrawDesc d{kDrawResidual, 0, c, s_t.m, s_d.m, (float)log2((double)s_t.s / (double)s_d.s), 0.f, 0.f};
+    DrawDesc d{};
+    d.kind = kDrawResidual;
+    d.c = c;
+    d.m_t = s_t.m;
+    d.m_d = s_d.m;
+    d.lq = (float)log2((double)s_t.s / (double)s_d.s);
+    d.lamq = 1.f;
     const float lam0 = exp2_fast(d.lq);
     __shared__ float s_sum[4][kMaxTiles];
     for (int t = w; t < NT; t += kWaves) {
@@ -1775,9 +2105,9 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     }
     __shared__ double s_w[kMaxTiles];
     WSpec ws;
-    double Z, lam;
-    bool near;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &Z, &near, &lam);
+    double Z, mass;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &Z, &mass);
+    const bool near = ws.mode == kWResNear;
     double sp = 0.0, unused = 0.0;
     for (int i = tid; i < NT; i += kThreads) {
         if (tile_out) tile_out[(size_t)r * NT + i] = s_w[i];
@@ -1788,9 +2118,9 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
         w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
     if (info_out && tid == 0) {
         info_out[(size_t)r * 4 + 0] = near ? 1.f : 0.f;
-        info_out[(size_t)r * 4 + 1] = (float)lam;
+        info_out[(size_t)r * 4 + 1] = ws.mode == kWResFar ? ws.lam : 0.f;
         info_out[(size_t)r * 4 + 2] = near ? ws.rho : 0.f;
-        info_out[(size_t)r * 4 + 3] = near ? 0.f : (float)(Z / sp);
+        info_out[(size_t)r * 4 + 3] = (float)mass;
     }
 }
 
@@ -1856,6 +2186,32 @@ hipError_t launch_tree(const StatsParams& p, Dt dt, bool aligned, hipStream_t s)
     } else {
         if (aligned) hipLaunchKernelGGL((k_stats_tree<kF32, true>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((k_stats_tree<kF32, false>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_sample(const StatsParams& p, Dt dt, bool aligned, hipStream_t s) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.S * p.NC);
+    const dim3 grid(blocks), block(kThreads);
+    if (dt == kBF16) {
+        if (aligned) hipLaunchKernelGGL((k_stats_tree_sample<kBF16, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_stats_tree_sample<kBF16, false>), grid, block, 0, s, p);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_stats_tree_sample<kF32, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_stats_tree_sample<kF32, false>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_round(const RoundParams& p, Dt dt, bool aligned, hipStream_t s) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.NCd);
+    const dim3 grid(blocks), block(kThreads);
+    if (dt == kBF16) {
+        if (aligned) hipLaunchKernelGGL((k_tree_round<kBF16, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_tree_round<kBF16, false>), grid, block, 0, s, p);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_tree_round<kF32, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_tree_round<kF32, false>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }

@@ -257,6 +257,63 @@ def make_tree(seed: int, device="cpu", B: int = 64, n: int = 25, V: int = 128256
                 draft_lens=torch.as_tensor(lens, dtype=torch.int32, device=dev), B=B, n=n, V=V)
 
 
+def make_tree_sample(seed: int, device="cpu", B: int = 64, n: int = 25, V: int = 128256, shape: str = "topk",
+                     dtype=torch.bfloat16, ragged: bool = False, temps=(0.7,), sigma: float = 1.0,
+                     block: int = 16) -> dict:
+    """Inputs of sampling tree verification.  Target row r [B, n+1, V] (the
+    target after node r) follows the llama-vocab sampling recipe: N(0, 3^2) with
+    the row's 20 largest logits raised by 6.  Draft row r [B, n, V] is the
+    target row r as stored plus N(0, sigma^2).  draft_parents as in make_tree
+    ("topk": tree_parents(n); "random": node j + 1 below a uniform node in
+    [0, j]); node j + 1's token is drawn from softmax(draft row parent / T) by
+    Gumbel-max, independently for every child (the draft's own sampling), or
+    is the argmax of that row when T = 0.  temperature: uniform over `temps`;
+    draft_lens: n, or uniform in 0..n when ragged; uniforms [B, n+1]."""
+    import numpy as np
+
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    rng = np.random.default_rng(seed)
+    if shape == "topk":
+        par = np.tile(np.array(tree_parents(n), dtype=np.int32), (B, 1)) if n > 0 else np.zeros((B, 0), np.int32)
+    else:
+        par = np.array([[rng.integers(0, j + 1) for j in range(n)] for _ in range(B)], dtype=np.int32).reshape(B, n)
+    tv = torch.tensor([float(t) for t in temps], device=dev)
+    temp = tv[torch.randint(0, len(temps), (B,), generator=g, device=dev)].to(torch.float32)
+    lens = torch.randint(0, n + 1, (B,), generator=g, device=dev, dtype=torch.int32) if ragged \
+        else torch.full((B,), n, dtype=torch.int32, device=dev)
+    target = torch.empty((B, n + 1, V), dtype=dtype, device=dev)
+    draft = torch.empty((B, n, V), dtype=dtype, device=dev)
+    tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+    parents = torch.as_tensor(par, dtype=torch.int32, device=dev)
+    for b0 in range(0, B, block):
+        b1 = min(B, b0 + block)
+        nb = b1 - b0
+        zt = 3.0 * torch.randn((nb, n + 1, V), generator=g, device=dev, dtype=torch.float32)
+        if V > 20:
+            top = torch.topk(zt, 20, dim=-1).indices
+            zt.scatter_add_(-1, top, torch.full(top.shape, 6.0, device=dev))
+        target[b0:b1] = zt.to(dtype)
+        del zt
+        noise = torch.randn((nb, n, V), generator=g, device=dev, dtype=torch.float32)
+        draft[b0:b1] = (target[b0:b1, :n].float() + sigma * noise).to(dtype)
+        del noise
+        if n == 0:
+            continue
+        tb = temp[b0:b1]
+        greedy = tb == 0
+        tsafe = torch.where(greedy, torch.ones_like(tb), tb)
+        pr = parents[b0:b1].long()
+        at_parent = draft[b0:b1].gather(1, pr.unsqueeze(-1).expand(nb, n, V))   # draft row of each node's parent
+        x = _gumbel_draft(at_parent, tsafe, g)
+        xg = torch.argmax(at_parent.float(), dim=-1).to(torch.int32)
+        tokens[b0:b1] = torch.where(greedy.view(-1, 1), xg, x)
+        del at_parent
+    uniforms = torch.rand((B, n + 1), generator=g, device=dev, dtype=torch.float32)
+    return dict(target=target, draft=draft, draft_tokens=tokens, draft_parents=parents, draft_lens=lens,
+                temperature=temp, uniforms=uniforms, B=B, n=n, V=V, parents_host=par)
+
+
 def make_lmhead(seed: int, device="cpu", B: int = 256, n: int = 4, V: int = 128256, H: int = 8192,
                 exact: bool = True, ragged: bool = False) -> dict:
     """Inputs of the fused logit projection + greedy verify: the target's final

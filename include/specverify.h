@@ -75,7 +75,8 @@ enum {
     SV_FLAG_BAD_UNIFORM = 8,
     SV_FLAG_ZERO_RESIDUAL = 16,
     SV_FLAG_ROW_CLAMPED = 32,
-    SV_FLAG_BAD_PARENT = 64
+    SV_FLAG_BAD_PARENT = 64,
+    SV_FLAG_TREE_TRUNCATED = 128
 };
 
 /* Bytes of device workspace spec_verify_sample() and spec_verify_greedy() need
@@ -176,6 +177,52 @@ sv_status_t spec_verify_tree_greedy(const void *target_logits, sv_dtype_t dt, co
                                     int V, int32_t *accepted_len, int32_t *emitted, int32_t *path,
                                     uint32_t *err_flags, void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/* Sampling tree verification.  "Accelerating Sonar through speculation", EAGLE
+ * section: the draft explores a tree of candidate tokens, the target scores
+ * every candidate sequence, the longest suitable one is kept and one more token
+ * from the target is appended.  The page gives no acceptance rule for sampling;
+ * the rule is SpecInfer's multi-step speculative sampling (Miao et al.,
+ * "SpecInfer: Accelerating Large Language Model Serving with Tree-based
+ * Speculative Inference and Verification"), under which the emitted tokens
+ * follow the target's distribution when the children of every node are
+ * independent draws from the draft's distribution at that node:
+ *   - tree as in spec_verify_tree_greedy(): node 0 the root, node j + 1 holds
+ *     draft_tokens[b][j] below draft_parents[b][j] in [0, j];
+ *   - target row r = the target's logits after node r; draft row r (r < n) = the
+ *     draft's logits at node r, from which node r's children were drawn;
+ *     p_r = softmax(target row / T_b), q_r = softmax(draft row / T_b);
+ *   - at node u the children are tested in index order against the current
+ *     target residual p' (p_u at first): child j + 1 is accepted iff
+ *     uniforms[b][j] < p'(x_j) / q_u(x_j); an accepted child moves the walk down;
+ *     a rejected one replaces p' by max(0, p' - q_u) normalised; with no child
+ *     left the token is drawn by inverse CDF with uniforms[b][n] from p' (from
+ *     p_u itself at a node with no children);
+ *   - T_b = 0: the greedy rule of spec_verify_tree_greedy().
+ * Each test after a rejection at a node needs the residual's mass, a full
+ * reduction of that node's row pair; one reduction per pending walk is made by
+ * each of `max_rounds` round kernels (sv_tree_rounds() gives the bound for one
+ * tree).  A walk that would need more leaves the remaining children of that
+ * node untested and draws from the current residual -- the same rule on a
+ * smaller tree, so the law is kept -- and sets SV_FLAG_TREE_TRUNCATED.
+ * Outputs as in spec_verify_tree_greedy(): accepted_len = the kept path's
+ * length, emitted = its tokens, the drawn token, then -1; path (nullable) = its
+ * nodes.  Other arguments, limits and errors as in spec_verify_sample();
+ * draft_logits [B][n][V] is required when n > 0.  Launches 2 + max_rounds kernels. */
+sv_status_t spec_verify_tree_sample(const void *target_logits, const void *draft_logits, sv_dtype_t dt,
+                                    const int32_t *draft_tokens, const int32_t *draft_parents,
+                                    const int32_t *draft_lens, const float *temperature,
+                                    const float *uniforms, int B, int n, int V, int max_rounds,
+                                    int32_t *accepted_len, int32_t *emitted, int32_t *path,
+                                    uint32_t *err_flags, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Host helper: the number of rounds spec_verify_tree_sample() needs for one tree
+ * so that no walk is truncated: the largest, over the tree's root-to-node paths,
+ * of the sum over the path's nodes of (number of children - 1).  parents: HOST
+ * array of L entries (node j + 1 below parents[j]; entries outside [0, j] leave
+ * the node out).  Returns 0 for L <= 0 or NULL. */
+int sv_tree_rounds(const int32_t *parents, int L);
 
 /* MTP bookkeeping on the device, with no host synchronisation.
  *

@@ -71,7 +71,7 @@ class Oracle:
                                                    i32p, i32p, i32p, u32p]
         L.sv_oracle_verify_tree_greedy.restype = C.c_int
         L.sv_oracle_verify_tree_sample.argtypes = [vp, vp, C.c_int, i32p, i32p, i32p, f32p, f32p, C.c_int, C.c_int,
-                                                   C.c_int, i32p, i32p, i32p, f64p, f64p, u32p]
+                                                   C.c_int, C.c_int, i32p, i32p, i32p, f64p, f64p, u32p]
         L.sv_oracle_verify_tree_sample.restype = C.c_int
         L.sv_oracle_plant.argtypes = []
         L.sv_oracle_plant.restype = C.c_int
@@ -158,8 +158,10 @@ class Oracle:
             raise RuntimeError(f"sv_oracle_verify_tree_greedy failed: {rc}")
         return dict(accepted_len=acc, emitted=emi, path=path, seq_flags=fl)
 
-    def verify_tree_sample(self, target, draft, draft_tokens, draft_parents, draft_lens, temperature, uniforms):
-        """Sampling tree verification (see sv_oracle_verify_tree_sample)."""
+    def verify_tree_sample(self, target, draft, draft_tokens, draft_parents, draft_lens, temperature, uniforms,
+                           max_rounds=None):
+        """Sampling tree verification (see sv_oracle_verify_tree_sample);
+        max_rounds None: no limit on the residual sums of a walk."""
         target, dt = self._logits(target)
         B, n1, V = target.shape
         n = n1 - 1
@@ -177,7 +179,8 @@ class Oracle:
         dm = np.empty(B, np.float64)
         fl = np.empty(B, np.uint32)
         rc = self.lib.sv_oracle_verify_tree_sample(self._p(target), self._p(draft), dt, self._p(x), self._p(par),
-                                                   self._p(L), self._p(T), self._p(u), B, n, V, self._p(acc),
+                                                   self._p(L), self._p(T), self._p(u), B, n, V,
+                                                   -1 if max_rounds is None else int(max_rounds), self._p(acc),
                                                    self._p(emi), self._p(path), self._p(am), self._p(dm), self._p(fl))
         if rc != 0:
             raise RuntimeError(f"sv_oracle_verify_tree_sample failed: {rc}")

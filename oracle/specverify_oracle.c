@@ -73,6 +73,7 @@
 #define OR_FLAG_BAD_UNIFORM 8u
 #define OR_FLAG_ZERO_RESIDUAL 16u
 #define OR_FLAG_BAD_PARENT 64u
+#define OR_FLAG_TREE_TRUNCATED 128u
 
 #define OR_MODE_SAMPLE 0
 #define OR_MODE_GREEDY 1
@@ -602,14 +603,19 @@ int sv_oracle_verify_tree_greedy(const void *target_logits, int dt, const int32_
  *   - outputs as in the greedy tree rule: the kept path's tokens, the drawn
  *     token, then -1; path[] the kept path's nodes.
  * With parents[j] = j (a chain) this is the linear sampling rule.  T_b = 0 takes
- * the greedy tree rule.  The residual sums and the draw are formed in extended
+ * the greedy tree rule.  A limit on the number of M_k a walk may form
+ * (max_rounds >= 0; negative: none) is the same rule on a smaller tree: when a
+ * rejection leaves a later sibling to test and the walk has formed its
+ * max_rounds sums already, the untested siblings are dropped, the token is
+ * drawn from max(0, p_u - lam_{k+1} q_u) (that residual needs no new sum
+ * before the draw), and the sequence is flagged.  The residual sums and the draw are formed in extended
  * precision, the first acceptance test at a node as the linear rule forms it. */
 typedef struct {
     const void *target, *draft;
     int dt;
     const int32_t *tokens, *parents, *lens;
     const float *temperature, *uniforms;
-    int B, n, V;
+    int B, n, V, max_rounds;
     int32_t *acc, *emitted, *path;
     double *accept_margin, *draw_margin;
     uint32_t *seq_flags;
@@ -646,7 +652,7 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
     const size_t trow0 = (size_t)b * (size_t)(n + 1) * (size_t)V;
     const size_t drow0 = (size_t)b * (size_t)n * (size_t)V;
     long double *p = w, *q = w + V;
-    int u = 0, depth = 0, y = -1;
+    int u = 0, depth = 0, y = -1, sums = 0;
     for (;;) {
         /* the target at node u, and (if u has children) the draft at node u */
         int first = -1;
@@ -693,6 +699,14 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
 #endif
             /* rejected: p' <- max(0, p' - q_u) normalised */
             lam += M;
+            int later = 0;
+            for (int t = j + 1; t < L && !later; ++t) later = (par[t] == u);
+            if (!later) break; /* the draw forms its own sum */
+            if (J->max_rounds >= 0 && sums >= J->max_rounds) {
+                flags |= OR_FLAG_TREE_TRUNCATED; /* the later siblings stay untested */
+                break;
+            }
+            ++sums;
             M = 0.0L;
             for (int i = 0; i < V; ++i) {
                 const long double d = p[i] - lam * q[i];
@@ -736,20 +750,21 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
 /* Sampling tree verification for every sequence.  target [B][n+1][V], draft
  * [B][n][V] (row r = the draft at node r), draft_tokens / draft_parents [B][n],
  * draft_lens [B], temperature [B], uniforms [B][n+1] (u[j]: the test of node
- * j + 1, u[n]: the final draw).  Outputs accepted_len [B], emitted [B][n+1],
+ * j + 1, u[n]: the final draw), max_rounds (the limit on the residual sums a
+ * walk forms before a later sibling's test; negative: none).  Outputs accepted_len [B], emitted [B][n+1],
  * path [B][n] (nullable), accept_margin [B][n] (+inf for nodes not tested),
  * draw_margin [B], seq_flags [B].  Returns 0, -1 on bad sizes, -2 without memory. */
 int sv_oracle_verify_tree_sample(const void *target_logits, const void *draft_logits, int dt,
                                  const int32_t *draft_tokens, const int32_t *draft_parents,
                                  const int32_t *draft_lens, const float *temperature, const float *uniforms,
-                                 int B, int n, int V, int32_t *accepted_len, int32_t *emitted, int32_t *path,
-                                 double *accept_margin, double *draw_margin, uint32_t *seq_flags)
+                                 int B, int n, int V, int max_rounds, int32_t *accepted_len, int32_t *emitted,
+                                 int32_t *path, double *accept_margin, double *draw_margin, uint32_t *seq_flags)
 {
     if (check_dims(B, n, V)) return -1;
     long double *w = (long double *)malloc(sizeof(long double) * 2 * (size_t)V);
     if (!w) return -2;
     tree_job_t J = {target_logits, draft_logits, dt, draft_tokens, draft_parents, draft_lens, temperature,
-                    uniforms, B, n, V, accepted_len, emitted, path, accept_margin, draw_margin, seq_flags};
+                    uniforms, B, n, V, max_rounds, accepted_len, emitted, path, accept_margin, draw_margin, seq_flags};
     for (int b = 0; b < B; ++b) tree_sample_one(&J, b, w);
     free(w);
     return 0;

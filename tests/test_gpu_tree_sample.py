@@ -1,0 +1,158 @@
+"""GPU parity of sampling tree verification (spec_verify_tree_sample) against
+the oracle (SpecInfer's multi-step speculative sampling on the draft tree).
+
+Every sequence is compared in full: accepted length, emitted tokens, kept path
+and the OR of the flags.  A sequence may differ only when the oracle's margin
+of one of its decisions (|u - ratio| of a test, the draw's distance to a CDF
+boundary over the residual's mass) is below 1e-5, the rounding band between a
+float kernel and a double/extended-precision oracle; it is then counted as
+exempt.  Cases: random and top-k trees over several tiles with a ragged tail,
+bf16 and fp32, temperatures 0 / 0.7 / 1 mixed in one batch; round limits that
+truncate walks (compared with the oracle under the same limit); the top-k tree
+at full size (B = 64, 26 nodes, V = 128256); the chain tree against the linear
+call; bad parents, tokens and lengths; the workspace left zero-filled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_08_amd as sv
+from draft_token_verification_08_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-5
+
+
+def _rounds(d):
+    par = d["parents_host"] if "parents_host" in d else d["draft_parents"].cpu().numpy()
+    return max([sv.sv_tree_rounds(list(p)) for p in par] + [0])
+
+
+def _run(d, max_rounds, ws=None):
+    fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc, emi, path = sv.spec_verify_tree_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_parents"],
+                                                d["draft_lens"], d["temperature"], d["uniforms"], max_rounds,
+                                                err_flags=fl, workspace=ws)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), emi.cpu().numpy(), path.cpu().numpy(), int(fl.item())
+
+
+def _oracle(oracle, d, max_rounds=None):
+    return oracle.verify_tree_sample(synth.host_logits(d["target"]), synth.host_logits(d["draft"]),
+                                     d["draft_tokens"].cpu().numpy(), d["draft_parents"].cpu().numpy(),
+                                     d["draft_lens"].cpu().numpy(), d["temperature"].cpu().numpy(),
+                                     d["uniforms"].cpu().numpy(), max_rounds=max_rounds)
+
+
+def _compare(oracle, d, max_rounds, oracle_rounds="same", ws=None, tag=""):
+    acc, emi, path, fl = _run(d, max_rounds, ws)
+    o = _oracle(oracle, d, max_rounds if oracle_rounds == "same" else oracle_rounds)
+    B = acc.shape[0]
+    temp = d["temperature"].cpu().numpy()
+    am, dm = o["accept_margin"], o["draw_margin"]
+    exempt = hard = 0
+    first = None
+    for b in range(B):
+        same = (acc[b] == o["accepted_len"][b] and np.array_equal(emi[b], o["emitted"][b])
+                and np.array_equal(path[b], o["path"][b]))
+        if same:
+            continue
+        tie = temp[b] > 0 and ((am[b] < TOL).any() or dm[b] < TOL)
+        if tie:
+            exempt += 1
+            continue
+        hard += 1
+        if first is None:
+            first = (b, int(acc[b]), int(o["accepted_len"][b]), emi[b].tolist(), o["emitted"][b].tolist(),
+                     path[b].tolist(), o["path"][b].tolist())
+    oflags = int(np.bitwise_or.reduce(o["seq_flags"])) if B else 0
+    print(f"\n{tag}: B={B} mean accepted {acc.mean():.2f} exempt={exempt} hard={hard} flags gpu={fl} oracle={oflags}")
+    assert hard == 0, (tag, first)
+    if exempt == 0:
+        assert fl == oflags, (tag, fl, oflags)
+    return acc, fl
+
+
+@pytest.mark.parametrize("B,n,V,shape,f32", [(48, 12, 5003, "random", False), (33, 25, 4096, "topk", False),
+                                             (20, 8, 1, "random", False), (17, 0, 999, "random", False),
+                                             (40, 30, 2000, "random", True), (9, 64, 257, "random", False),
+                                             (64, 25, 20000, "topk", True)])
+def test_trees_against_oracle(oracle, B, n, V, shape, f32):
+    d = synth.make_tree_sample(300 + B + n, device=DEV, B=B, n=n, V=V, shape=shape, ragged=True,
+                               temps=(0.0, 0.7, 1.0), dtype=torch.float32 if f32 else torch.bfloat16)
+    _compare(oracle, d, _rounds(d), tag=(B, n, V, shape, f32))
+
+
+@pytest.mark.parametrize("max_rounds", [0, 1, 2])
+def test_round_limit_truncates_like_the_oracle(oracle, max_rounds):
+    d = synth.make_tree_sample(400 + max_rounds, device=DEV, B=64, n=20, V=6007, shape="random",
+                               temps=(0.7, 1.0), sigma=2.0)
+    d["uniforms"][:, :20] = torch.sqrt(d["uniforms"][:, :20])    # more rejections, so limits bite
+    assert _rounds(d) > max_rounds
+    _, fl = _compare(oracle, d, max_rounds, tag=f"max_rounds={max_rounds}")
+    assert fl & sv.SV_FLAG_TREE_TRUNCATED
+
+
+def test_enough_rounds_never_truncate(oracle):
+    d = synth.make_tree_sample(410, device=DEV, B=64, n=20, V=6007, shape="random", temps=(0.7,), sigma=2.0)
+    R = _rounds(d)
+    _, fl = _compare(oracle, d, R + 3, oracle_rounds=None, tag="rounds to spare")
+    assert not fl & sv.SV_FLAG_TREE_TRUNCATED
+
+
+def test_topk_tree_full_size(oracle):
+    """64 sequences, the 26-node top-k tree, V = 128256 bf16, T = 0.7."""
+    d = synth.make_tree_sample(7, device=DEV, B=64, n=25, V=128256)
+    R = _rounds(d)
+    assert R == 3
+    acc, _ = _compare(oracle, d, R, tag="full size")
+    assert acc.max() >= 2
+
+
+def test_chain_tree_equals_linear_call():
+    d = synth.make(2, 41, device=DEV, B=64, V=9001)
+    B, n = d["B"], d["n"]
+    chain = torch.arange(n, dtype=torch.int32, device=DEV).repeat(B, 1).contiguous()
+    acc, emi, path = sv.spec_verify_tree_sample(d["target"], d["draft"], d["draft_tokens"], chain, d["draft_lens"],
+                                                d["temperature"], d["uniforms"], 0)
+    acc2, emi2 = sv.spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                       d["temperature"], d["uniforms"])
+    torch.cuda.synchronize()
+    assert torch.equal(acc, acc2) and torch.equal(emi, emi2)
+    for b in range(B):
+        k = int(acc[b])
+        assert path[b, :k].tolist() == list(range(1, k + 1)) and (path[b, k:] == -1).all()
+
+
+def test_law_on_the_gpu(oracle):
+    """The two-level law case (V = 8, 3 candidates at the root, 2 below each,
+    rows that depend on the token prefix), 2 * 10^5 trials in one call: the GPU
+    agrees with the oracle trial by trial."""
+    h = synth.make_tree_law_case(5, 200_000, device=DEV)
+    d = dict(target=h["target"], draft=h["draft"], draft_tokens=h["draft_tokens"], draft_parents=h["draft_parents"],
+             draft_lens=h["draft_lens"], temperature=h["temperature"], uniforms=h["uniforms"])
+    _compare(oracle, d, sv.sv_tree_rounds(h["draft_parents"][0].tolist()), tag="law case")
+
+
+def test_bad_parents_tokens_and_lengths(oracle):
+    d = synth.make_tree_sample(21, device=DEV, B=6, n=5, V=700, shape="random", temps=(0.8,))
+    par = d["draft_parents"]
+    par[0, 2] = 4                  # not an earlier node
+    par[1, 0] = -1
+    d["draft_tokens"][2, 0] = 700  # out of range
+    d["draft_tokens"][3, 1] = -5
+    d["draft_lens"][4] = 9         # clamped
+    d["uniforms"][5, 0] = float("nan")
+    _, fl = _compare(oracle, d, 4, tag="bad values")
+    want = sv.SV_FLAG_BAD_PARENT | sv.SV_FLAG_TOKEN_OOR | sv.SV_FLAG_LEN_CLAMPED | sv.SV_FLAG_BAD_UNIFORM
+    assert fl & want == want, fl
+
+
+def test_workspace_left_zero(oracle):
+    ws = torch.zeros(sv.sv_workspace_bytes(64, 25, 40000, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+    for seed, (B, n, V, R) in enumerate([(64, 25, 40000, 1), (10, 5, 3001, 4), (64, 25, 40000, 0), (30, 20, 9000, 9)]):
+        d = synth.make_tree_sample(500 + seed, device=DEV, B=B, n=n, V=V, shape="random", ragged=True,
+                                   temps=(0.0, 0.7))
+        _compare(oracle, d, R, ws=ws, tag=f"shared workspace {seed}")
+        assert int(ws.count_nonzero()) == 0  # walks, row blocks, counters and sums all cleared

@@ -24,6 +24,9 @@ BUDGET = {
     # 1024 workgroups, which 6 waves per SIMD keep resident
     "_ZN2sv12k_stats_drawILi1ELb1EEEvNS_11StatsParamsE": 6,
     "_ZN2sv6k_drawILi1EEEvNS_10DrawParamsE": 5,             # draw pass, bf16, aligned
+    # sampling tree verification, bf16, aligned: statistics pass and round kernel
+    "_ZN2sv19k_stats_tree_sampleILi1ELb1EEEvNS_11StatsParamsE": 6,
+    "_ZN2sv12k_tree_roundILi1ELb1EEEvNS_11RoundParamsE": 5,
     "_ZN2sv5k_mtpILb1EEEvNS_9MtpParamsE": 8,               # MTP copy, aligned
     # logit projection (256 x 256 tiles, 8 waves, one workgroup per CU): two
     # waves per SIMD; the accumulators alone take 128 registers

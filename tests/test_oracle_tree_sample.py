@@ -17,7 +17,11 @@ independent draws from the draft at that node.  The pins:
   final draw that ignores the later siblings' updates) fail the same test;
 - temperature 0 is the greedy tree rule; a fully accepted path draws the bonus
   token from its leaf's row by inverse CDF; bad parents and out-of-range tokens
-  are flagged.
+  are flagged;
+- a limit on the residual sums a walk may form drops the untested siblings,
+  which is the rule on a smaller tree: with no sum allowed, the walk is the
+  linear rule on the chain of first children (rows and uniforms gathered along
+  it), and the law test passes with limits 0 and 1 as well.
 """
 import numpy as np
 import pytest
@@ -62,7 +66,7 @@ def test_chain_tree_equals_linear_rule(oracle, T):
         assert list(t["path"][b, :k]) == list(range(1, k + 1))
 
 
-def _law_failures(o, seeds, trials=200_000, widths=(3, 2)):
+def _law_failures(o, seeds, trials=200_000, widths=(3, 2), max_rounds=None):
     """Chi-square tests (alpha = 1e-3, 7 dof) of the emitted tokens against the
     target rows; returns (failures, tests, largest statistic)."""
     crit = st.chi2.ppf(1 - 1e-3, 7)
@@ -73,7 +77,7 @@ def _law_failures(o, seeds, trials=200_000, widths=(3, 2)):
         T = h["T"]
         out = o.verify_tree_sample(h["target"].numpy(), h["draft"].numpy(), h["draft_tokens"].numpy(),
                                    h["draft_parents"].numpy(), h["draft_lens"].numpy(), h["temperature"].numpy(),
-                                   h["uniforms"].numpy())
+                                   h["uniforms"].numpy(), max_rounds=max_rounds)
         acc, emi = out["accepted_len"], out["emitted"]
         tok = h["draft_tokens"].numpy()
         path = out["path"]
@@ -106,6 +110,54 @@ def test_tree_law_chi_square(oracle):
     print(f"\ntree law: {tests} chi-square tests, {fails} above the 1e-3 critical value, largest {worst:.1f}")
     assert tests >= 40
     assert fails <= 2, (fails, tests)
+
+
+@pytest.mark.parametrize("max_rounds", [0, 1])
+def test_tree_law_with_round_limit(oracle, max_rounds):
+    fails, tests, worst = _law_failures(oracle, range(3), max_rounds=max_rounds)
+    print(f"\nround limit {max_rounds}: {tests} chi-square tests, {fails} above 1e-3, largest {worst:.1f}")
+    assert tests >= 20
+    assert fails <= 1, (fails, tests)
+
+
+def test_no_rounds_is_linear_rule_on_first_children(oracle):
+    rng = np.random.default_rng(11)
+    B, n, V, T = 64, 10, 400, 0.8
+    zt, zd = _rows(rng, B, n, V)
+    par = np.array([[rng.integers(max(0, j - 3), j + 1) for j in range(n)] for _ in range(B)], np.int32)
+    x = _draft_from_q(rng, zd[np.arange(B)[:, None], par], T)
+    L = rng.integers(0, n + 1, B).astype(np.int32)
+    u = rng.random((B, n + 1)).astype(np.float32)
+    u[:, :n] *= 1.5                                    # more rejections
+    u = np.minimum(u, np.float32(1 - 2 ** -24))
+    temp = np.full(B, T, np.float32)
+    out = oracle.verify_tree_sample(zt, zd, x, par, L, temp, u, max_rounds=0)
+    # the chain of first children, gathered into a linear case of length m
+    ct, cd = np.zeros_like(zt), np.zeros_like(zd)
+    cx, cu = np.zeros((B, n), np.int32), np.zeros((B, n + 1), np.float32)
+    cL = np.zeros(B, np.int32)
+    truncated = np.zeros(B, bool)
+    for b in range(B):
+        node, m = 0, 0
+        while True:
+            kids = [j for j in range(L[b]) if par[b, j] == node]
+            ct[b, m] = zt[b, node]
+            if not kids:
+                break
+            cd[b, m], cx[b, m], cu[b, m] = zd[b, node], x[b, kids[0]], u[b, kids[0]]
+            m += 1
+            node = kids[0] + 1
+        cL[b], cu[b, n] = m, u[b, n]
+    lin = oracle.verify_sample(ct, cd, cx, cL, temp, cu)
+    assert np.array_equal(out["accepted_len"], lin["accepted_len"])
+    assert np.array_equal(out["emitted"], lin["emitted"])
+    for b in range(B):
+        k = out["accepted_len"][b]
+        node = 0 if k == 0 else out["path"][b, k - 1]
+        kids = [j for j in range(L[b]) if par[b, j] == node]
+        truncated[b] = len(kids) > 1 and k < cL[b]    # stopped at a node whose first child was rejected
+    assert np.array_equal((out["seq_flags"] & 128) != 0, truncated)
+    assert truncated.sum() >= 10
 
 
 @pytest.mark.parametrize("plant", [8, 9])
