@@ -15,6 +15,7 @@ timed with HIP events on its stream), and the CPU oracle timed on host cores.
 
     python bench.py [--steps K] [--warmup W] [--config {2,3,4,5,6}] [--no-cpu] [--unfused]
     python bench.py --lmhead [--steps K]   # greedy verify fused with the logit projection
+    python bench.py --tree | --tree-sample  # greedy / sampling tree verification
 """
 from __future__ import annotations
 
@@ -56,6 +57,9 @@ def parse():
     ap.add_argument("--tree", action="store_true",
                     help="greedy tree verification (spec_verify_tree_greedy): 64 sequences with a 26-node top-k "
                          "draft tree over V=128256 bf16 logits")
+    ap.add_argument("--tree-sample", action="store_true",
+                    help="sampling tree verification (spec_verify_tree_sample): 64 sequences with a 26-node top-k "
+                         "draft tree over V=128256 bf16 target and draft logits, T=0.7")
     ap.add_argument("--lmhead", action="store_true",
                     help="greedy verify fused with the target's logit projection (spec_verify_greedy_lmhead): "
                          "hidden states [256, 5, 8192] and a [128256, 8192] projection instead of logits")
@@ -110,6 +114,9 @@ def main():
         return
     if args.tree:
         bench_tree(args, dev)
+        return
+    if args.tree_sample:
+        bench_tree_sample(args, dev)
         return
     cfg = synth.CONFIGS[args.config]
     greedy = cfg.mode == "greedy"
@@ -726,6 +733,129 @@ def bench_tree(args, dev):
         out["cpu_baseline"] = cpu_baseline_tree(data[0], B, n, V)
         out["oracle_parity"] = out["cpu_baseline"].pop("oracle_parity")
     print(json.dumps(out), flush=True)
+
+
+def bench_tree_sample(args, dev):
+    """Sampling tree verification: the statistics pass over every node's target
+    row and every inner node's draft row with the walks from the root, the round
+    kernels (3 for this tree: one residual mass per pending walk each) and the
+    draw pass.  64 sequences, each the 26-node top-k tree (3 children at the
+    root, 2 below each of those, then chains; 20 inner nodes), V=128256 bf16
+    rows of the llama-vocab sampling recipe, children drawn from the draft at
+    their parent, T=0.7; inputs resident in HBM, rotated over input copies."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_08_amd as sv
+    from draft_token_verification_08_amd import synth
+
+    B, n, V = 64, 25, 128256
+    sets = args.sets or 3
+    wsbuf = sv.Workspace(dev).get(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16))
+    stream = torch.cuda.current_stream(dev)
+    par = synth.tree_parents(n)
+    R = sv.sv_tree_rounds(par)
+    inner = len(set(par))
+    data = []
+    for i in range(sets):
+        d = synth.make_tree_sample(args.seed + i, device=dev, B=B, n=n, V=V)
+        d["acc"] = torch.empty(B, dtype=torch.int32, device=dev)
+        d["emi"] = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+        d["path"] = torch.empty((B, n), dtype=torch.int32, device=dev)
+        data.append(d)
+    torch.cuda.synchronize()
+    for d in data:
+        d["call"] = sv.prepare_spec_verify_tree_sample(d["target"], d["draft"], d["draft_tokens"],
+                                                       d["draft_parents"], d["draft_lens"], d["temperature"],
+                                                       d["uniforms"], R, d["acc"], d["emi"], d["path"], wsbuf)
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        data[i % sets]["call"]()
+    torch.cuda.synchronize()
+    brackets = []
+    t0 = time.perf_counter()
+    i = 0
+    while i < K:
+        if i % 16 == 0 and i + 8 <= K:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for j in range(8):
+                data[(i + j) % sets]["call"]()
+            b.record(stream)
+            brackets.append((a, b))
+            i += 8
+        else:
+            data[i % sets]["call"]()
+            i += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_ms = statistics.fmean(a.elapsed_time(b) for a, b in brackets) / 8 if brackets else elapsed * 1e3 / K
+    # every row the rule needs, counted once: all node target rows, inner node draft rows
+    rows = B * (n + 1 + inner)
+    side = B * n * 8 + B * 4 * 2 + B * (n + 1) * 4 * 2 + B * n * 4
+    nbytes = rows * V * 2 + side
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    kernel = f"k_stats_tree_sample+{R}xk_tree_round+k_draw"
+    out = {
+        "metric": "verified vocab rows/s + HBM GB/s (% of peak), V=128256 bf16, B=64 (sampling tree of 26 nodes)",
+        "value": round(rows * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {sets} copies)",
+        "config": {"workload": "sampling tree verification, 64 sequences x 26-node top-k tree, V=128256 bf16, "
+                               "T=0.7 (sampling_tree_verify)", "B": B, "nodes": n + 1, "inner_nodes": inner,
+                   "rounds": R, "V": V, "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(nbytes * K / elapsed / 1e9, 1),
+        "pct_of_peak": round(nbytes * K / elapsed / 1e9 / PEAK_GBPS * 100, 2),
+        "mean_accepted": round(float(torch.stack([d["acc"].float().mean() for d in data]).mean()), 4),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(avg_ms * 1e3, 2), "timed_launches": 8 * len(brackets),
+                     "timing": "HIP event pair around 8 consecutive calls, every 16 steps",
+                     "traffic": measured_traffic(kernel, "sampling_tree_verify")},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_tree_sample(data[0], B, n, V, rows)
+        out["oracle_parity"] = out["cpu_baseline"].pop("oracle_parity")
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_tree_sample(d, B, n, V, rows):
+    """The oracle (untuned, one thread) on whole steps of the same workload for
+    about 10-20 s of CPU work; then the GPU's outputs for this input copy against
+    the oracle's, sequence by sequence (a difference is exempt only where one of
+    the oracle's decision margins is below 1e-5)."""
+    import numpy as np
+
+    import oracle
+    from draft_token_verification_08_amd import synth
+
+    orc = oracle.Oracle()
+    zt, zd = synth.host_logits(d["target"]), synth.host_logits(d["draft"])
+    args = (d["draft_tokens"].cpu().numpy(), d["draft_parents"].cpu().numpy(), d["draft_lens"].cpu().numpy(),
+            d["temperature"].cpu().numpy(), d["uniforms"].cpu().numpy())
+    calls, t0 = 0, time.perf_counter()
+    while calls < 1 or (time.perf_counter() - t0 < 12.0 and calls < 100):
+        o = orc.verify_tree_sample(zt, zd, *args)
+        calls += 1
+    el = time.perf_counter() - t0
+    acc, emi, path = d["acc"].cpu().numpy(), d["emi"].cpu().numpy(), d["path"].cpu().numpy()
+    diff = (acc != o["accepted_len"]) | (emi != o["emitted"]).any(1) | (path != o["path"]).any(1)
+    tie = (o["accept_margin"] < NEAR_TIE).any(1) | (o["draw_margin"] < NEAR_TIE)
+    return {"value": round(calls * rows / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full steps ({B} sequences, {rows} needed rows of V={V}) on 1 thread, about "
+                      f"{el:.0f} s of CPU work", "cpu_model": cpu_model(),
+            "oracle_parity": {"sequences": B, "exempt": int((diff & tie).sum()),
+                              "hard_mismatches": int((diff & ~tie).sum()),
+                              "inputs": "the first input copy of the timed workload, whole batch"}}
 
 
 def cpu_baseline_tree(d, B, n, V):

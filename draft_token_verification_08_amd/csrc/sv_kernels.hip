@@ -674,9 +674,9 @@ __device__ __forceinline__ NearTerm near_term(float Mc, float c, float zt, float
 // How a draw weighs one element (all weights up to a factor common to the row):
 //   kWTarget:   2^((z_t - mA) c), the target's own distribution (bonus draws, and
 //               the fallback when no residual mass is left);
-//   kWResFar:   max(0, P - lam Q) with P = 2^((z_t - m_t) c), Q = 2^((z_d - m_d) c),
-//               each row scaled by its own maximum (mA = m_t) and lam the ratio of
-//               their sums (S_t / S_d);
+//   kWResFar:   max(0, P - lam Q) with P = 2^(z_t c - fl(m_t c)), Q = 2^(z_d c -
+//               fl(m_d c)) (one rounding each: far_p()), each row scaled by its own
+//               maximum (mA = m_t) and lam the ratio of their sums (S_t / S_d);
 //   kWResNear:  max(0, rho A - opm Dl) of near_term() with M = mA (Mc = fl(mA c)):
 //               the residual max(0, p - lam q) with rho = rho' - (lam - 1) and
 //               opm = lam (rho' = S'_d / S'_t - 1; lam = 1 after one rejection).
@@ -690,20 +690,29 @@ struct WSpec {
     float rho;  // kWResNear
     float Mc;   // kWResNear: fl(mA c)
     float opm;  // kWResNear
+    float nmt;  // kWResFar: neg_scaled(mA, c)
+    float nmd;  // kWResFar: neg_scaled(m_d, c)
 };
-__device__ __forceinline__ float far_p(float mt, float c, float zt) { return exp2_fast((zt - mt) * c); }
+// -fl(m c) for a row maximum m, the offset of far_p(); 0 when the row has no
+// finite element (m = -FLT_MAX), whose terms are then all 2^-inf = 0.
+__device__ __forceinline__ float neg_scaled(float m, float c) { return m > -FLT_MAX ? -(m * c) : 0.f; }
+// 2^(z c - fl(m c)) with nm = neg_scaled(m, c), one rounding (fma) before the
+// power.  Every far-form sum and weight of a row pair takes its terms from here,
+// so the rounding of fl(m c), a factor common to the whole row, cancels in the
+// ratio lam = sum P / sum Q and in the normalised weights.
+__device__ __forceinline__ float far_p(float nm, float c, float z) { return exp2_fast(fmaf(z, c, nm)); }
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
     if (s.mode == kWTarget) return exp2_fast((zt - s.mA) * s.c);
     if (s.mode == kWResFar) {
-        const float P = far_p(s.mA, s.c, zt);
-        const float Q = far_p(s.m_d, s.c, zd);
+        const float P = far_p(s.nmt, s.c, zt);
+        const float Q = far_p(s.nmd, s.c, zd);
         return fmaxf(fmaf(-s.lam, Q, P), 0.f);
     }
     const NearTerm t = near_term(s.Mc, s.c, zt, zd);
     return fmaxf(fmaf(s.rho, t.A, -s.opm * t.Dl), 0.f);
 }
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
-    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f};
+    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 }
 
 // Scan one tile: returns the element whose running weight (starting at P)
@@ -1583,9 +1592,9 @@ __device__ void block_sum2_all(double& a, double& b) {
 struct FarSums {
     float p, q, w, g;
 };
-__device__ __forceinline__ void far_accum(FarSums& s, float mt, float md, float c, float lam0, float zt, float zd) {
-    const float P = far_p(mt, c, zt);
-    const float Q = far_p(md, c, zd);
+__device__ __forceinline__ void far_accum(FarSums& s, float nmt, float nmd, float c, float lam0, float zt, float zd) {
+    const float P = far_p(nmt, c, zt);
+    const float Q = far_p(nmd, c, zd);
     const float w0 = fmaf(-lam0, Q, P);
     s.p += P;
     s.q += Q;
@@ -1714,7 +1723,7 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
         }
     }
     block_sum2_all(zr, zp);
-    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, 0.f};
+    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, 0.f, neg_scaled(d.m_t, d.c), neg_scaled(d.m_d, d.c)};
     *mass = sp > 0.0 ? zr / sp : 0.0;
     const bool close = fabs(((double)d.m_d - (double)d.m_t) * (double)d.c) <= 32.0;
     if (close && sq > 0.0 && zr < kNearZ * sp) {
@@ -1757,6 +1766,7 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
     constexpr int kU = kThreads / 64;  // vectors per lane per tile
     static_assert(kDrawTiles % kWaves == 0, "draw chunk must split evenly over the waves");
     const float lam0 = d.lamq * exp2_fast(d.lq);
+    const float nmt = neg_scaled(d.m_t, d.c), nmd = neg_scaled(d.m_d, d.c);
     const int tile0 = c * kDrawTiles;
     const int cnt = min(kDrawTiles, NT - tile0);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1786,7 +1796,7 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
             unpack<DT>(rt[i][u], zt);
             unpack<DT>(rd[i][u], zd);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) far_accum(fs, d.m_t, d.m_d, d.c, lam0, zt[e], zd[e]);
+            for (int e = 0; e < kVec; ++e) far_accum(fs, nmt, nmd, d.c, lam0, zt[e], zd[e]);
         }
         fs = wave_far_sums(fs);
         const int t = wv * kTilesPerWave + i;
@@ -2080,6 +2090,7 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     d.lq = (float)log2((double)s_t.s / (double)s_d.s);
     d.lamq = 1.f;
     const float lam0 = exp2_fast(d.lq);
+    const float nmt = neg_scaled(d.m_t, c), nmd = neg_scaled(d.m_d, c);
     __shared__ float s_sum[4][kMaxTiles];
     for (int t = w; t < NT; t += kWaves) {
         FarSums fs{0.f, 0.f, 0.f, 0.f};
@@ -2090,7 +2101,7 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
             load_vec<DT, ALIGNED>(trow, e0, V, zt);
             load_vec<DT, ALIGNED>(drow, e0, V, zd);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) far_accum(fs, d.m_t, d.m_d, c, lam0, zt[e], zd[e]);
+            for (int e = 0; e < kVec; ++e) far_accum(fs, nmt, nmd, c, lam0, zt[e], zd[e]);
         }
         fs = wave_far_sums(fs);
         if (lane < 4) s_sum[lane][t] = far_sum_at(fs, lane);
