@@ -1489,9 +1489,19 @@ __device__ __forceinline__ void stats_pass(StatsParams p) {
         }
     } else {
         const float cf = exp2_scale(si.T);
+        // sampling tree: the draft row of a node with no child is never used (no
+        // test is made and no residual formed there), so it is not read
+        bool skip = false;
+        if constexpr (TREE) {
+            if (!target_row) {
+                const int k = slot - n - 1, j = threadIdx.x;
+                skip = !__syncthreads_or(j < si.L && j >= k && p.parents[(size_t)b * n + j] == k);
+            }
+        }
         // target row L is the only row a bonus token can be drawn from: it alone
         // streams in tiles and keeps per-tile partials
-        const MS r = (target_row && slot == si.L && !TREE)
+        const MS r = skip ? MS{-INFINITY, 0.f}
+                     : (target_row && slot == si.L && !TREE)
                          ? wg_softmax_tiles<DT, ALIGNED>(row, lo, hi, cf, p.tiles + (size_t)b * p.NT, DRAW)
                          : block_ms(thread_ms<DT, ALIGNED>(row, lo, hi, cf), cf);
         if (threadIdx.x == 0) {
