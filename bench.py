@@ -13,7 +13,7 @@ Prints one JSON line: verified vocab rows/s (value), HBM GB/s and % of the
 8 TB/s peak, a roofline entry for the dominant kernel (the verify kernel,
 timed with HIP events on its stream), and the CPU oracle timed on host cores.
 
-    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5,6}] [--no-cpu] [--unfused]
+    python bench.py [--steps K] [--warmup W] [--config {1,...,6}] [--no-cpu] [--unfused]
     python bench.py --lmhead [--steps K]   # greedy verify fused with the logit projection
     python bench.py --tree | --tree-sample  # greedy / sampling tree verification
 """
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=303)
@@ -448,11 +448,18 @@ def cpu_baseline(d, cfg, greedy):
     parity = parity_report(d["acc"].cpu().numpy(), d["emi"].cpu().numpy(), o, host["L"],
                            None if greedy else host["T"], cfg.n)
     parity["inputs"] = "the first input copy of the timed workload, whole batch"
+    # the greedy oracle stops at a sequence's first mismatch: it reads acc + 1 of
+    # the L + 1 rows the step verifies (the GPU reads all of them, in parallel)
+    read = int((o["accepted_len"] + 1).sum()) if greedy else rows
     return {"value": round(rows / tn, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
             "oracle_parity": parity,
             "sample": f"{nn} full steps ({cfg.B} sequences, {rows} rows of V={cfg.V} each"
-                      + (", + MTP shift/hidden copy" if cfg.H else "") + f") on {threads} threads, "
-                      f"about {nn * tn * threads:.0f} s of CPU work; single thread: {n1} steps",
+                      + (", + MTP shift/hidden copy" if cfg.H else "") + f") on {threads} threads "
+                      f"(this process's CPU share, at most 16), mean time per step over a 1 s budget, "
+                      f"about {nn * tn * threads:.0f} s of CPU work; single thread: {n1} steps over 2 s"
+                      + (f"; the oracle stops at each sequence's first mismatch and reads {read} of the "
+                         f"{rows} rows (value = the step's rows / its time)" if greedy else ""),
+            "rows_read_by_oracle": read,
             "single_thread_rows_per_s": round(rows / t1, 1), "seconds_per_step": round(tn, 4),
             "cpu_model": cpu_model()}
 
