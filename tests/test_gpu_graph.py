@@ -158,3 +158,34 @@ def test_graph_greedy_lmhead():
         assert torch.equal(st["tokens"], tok), seed
         assert torch.equal(dst.view(torch.int16), dst2.view(torch.int16)), seed
     assert int(ws.count_nonzero()) == 0
+
+
+def test_graph_tree_sample():
+    """Sampling tree verification (statistics pass, round kernels, draw pass) in
+    one graph: replays equal eager calls, and the walks leave the workspace zero."""
+    B, n, V = 24, 12, 6007
+    st = synth.make_tree_sample(31, device=DEV, B=B, n=n, V=V, shape="random", ragged=True, temps=(0.0, 0.7, 1.0))
+    R = max(sv.sv_tree_rounds(list(p)) for p in st["parents_host"])
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    emi = torch.empty((B, n + 1), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, n), dtype=torch.int32, device=DEV)
+    ws = torch.zeros(sv.sv_workspace_bytes(B, n, V, sv.SV_BF16), dtype=torch.uint8, device=DEV)
+    keys = ("target", "draft", "draft_tokens", "draft_parents", "draft_lens", "temperature", "uniforms")
+
+    def step():
+        sv.spec_verify_tree_sample(*(st[k] for k in keys), R, accepted_len=acc, emitted=emi, path=path, workspace=ws)
+
+    g = _capture(step)
+    for seed in (32, 33, 34):
+        fresh = synth.make_tree_sample(seed, device=DEV, B=B, n=n, V=V, shape="random", ragged=True,
+                                       temps=(0.0, 0.7, 1.0))
+        fresh["draft_parents"] = st["draft_parents"]  # the rounds captured are for this tree set
+        _refill(st, fresh)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (acc.clone(), emi.clone(), path.clone())
+        a2, e2, p2 = sv.spec_verify_tree_sample(*(st[k] for k in keys), R)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], a2) and torch.equal(got[1], e2) and torch.equal(got[2], p2), seed
+        assert int(ws.count_nonzero()) == 0

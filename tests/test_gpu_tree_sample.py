@@ -77,7 +77,7 @@ def _compare(oracle, d, max_rounds, oracle_rounds="same", ws=None, tag=""):
 @pytest.mark.parametrize("B,n,V,shape,f32", [(48, 12, 5003, "random", False), (33, 25, 4096, "topk", False),
                                              (20, 8, 1, "random", False), (17, 0, 999, "random", False),
                                              (40, 30, 2000, "random", True), (9, 64, 257, "random", False),
-                                             (64, 25, 20000, "topk", True)])
+                                             (64, 25, 20000, "topk", True), (31, 18, 2001, "random", True)])
 def test_trees_against_oracle(oracle, B, n, V, shape, f32):
     d = synth.make_tree_sample(300 + B + n, device=DEV, B=B, n=n, V=V, shape=shape, ragged=True,
                                temps=(0.0, 0.7, 1.0), dtype=torch.float32 if f32 else torch.bfloat16)
