@@ -52,9 +52,6 @@
 #ifndef SV_COPY_VECS
 #define SV_COPY_VECS 8  // 16-byte vectors per thread in the hidden-state copy
 #endif
-#ifndef SV_DRAW_NEAR
-#define SV_DRAW_NEAR 1  // residual draws of rows with close maxima use the near form
-#endif
 #ifndef SV_DRAW_WPE
 #define SV_DRAW_WPE 5   // waves per SIMD the draw pass's registers are sized for
 #endif

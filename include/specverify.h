@@ -208,7 +208,8 @@ sv_status_t spec_verify_tree_greedy(const void *target_logits, sv_dtype_t dt, co
  * Outputs as in spec_verify_tree_greedy(): accepted_len = the kept path's
  * length, emitted = its tokens, the drawn token, then -1; path (nullable) = its
  * nodes.  Other arguments, limits and errors as in spec_verify_sample();
- * draft_logits [B][n][V] is required when n > 0.  Launches 2 + max_rounds kernels. */
+ * draft_logits [B][n][V] is required when n > 0.  max_rounds outside
+ * [0, 4096] returns SV_EINVAL.  Launches 2 + max_rounds kernels. */
 sv_status_t spec_verify_tree_sample(const void *target_logits, const void *draft_logits, sv_dtype_t dt,
                                     const int32_t *draft_tokens, const int32_t *draft_parents,
                                     const int32_t *draft_lens, const float *temperature,

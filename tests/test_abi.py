@@ -103,6 +103,45 @@ def test_greedy_host_checks():
     assert _greedy(wsb=0) == sv.SV_EWORKSPACE
 
 
+def _tree_sample(**kw):
+    p = C.c_void_p(16)
+    args = dict(t=p, d=p, dt=sv.SV_BF16, x=p, par=p, L=p, T=p, u=p, B=4, n=4, V=1024, R=2, acc=p, emi=p,
+                path=NULL, fl=NULL, ws=C.c_void_p(256), wsb=1 << 20, s=NULL)
+    args.update(kw)
+    return sv.lib().spec_verify_tree_sample(*args.values())
+
+
+def test_tree_sample_host_checks():
+    # every case has one bad argument, so nothing is launched
+    assert _tree_sample(B=0) == sv.SV_OK
+    assert _tree_sample(B=-1) == sv.SV_EINVAL
+    assert _tree_sample(n=sv.SV_MAX_DRAFT + 1) == sv.SV_EINVAL
+    assert _tree_sample(R=-1) == sv.SV_EINVAL
+    assert _tree_sample(R=4097) == sv.SV_EINVAL
+    assert _tree_sample(d=NULL) == sv.SV_EINVAL           # draft logits required when n > 0
+    assert _tree_sample(par=NULL) == sv.SV_EINVAL
+    assert _tree_sample(x=NULL) == sv.SV_EINVAL
+    assert _tree_sample(u=NULL) == sv.SV_EINVAL
+    assert _tree_sample(par=C.c_void_p(18)) == sv.SV_EALIGN
+    assert _tree_sample(ws=NULL) == sv.SV_EWORKSPACE
+    assert _tree_sample(wsb=64) == sv.SV_EWORKSPACE
+
+
+def test_tree_rounds_helper():
+    assert sv.sv_tree_rounds([]) == 0
+    assert sv.sv_tree_rounds(list(range(10))) == 0            # a chain: one child per node
+    assert sv.sv_tree_rounds([0, 0, 0]) == 2                  # a star of 3
+    assert sv.sv_tree_rounds([0, 0, 0, 1, 1, 2]) == 3         # 3 at the root, 2 below node 1
+    assert sv.sv_tree_rounds([0, 0, 1, 1, 2, 2, 3, 3]) == 3   # binary tree of depth 3
+    assert sv.sv_tree_rounds([0, 5, 0]) == 1                  # node 2's parent is not earlier: left out
+    assert sv.sv_tree_rounds(_lib_tree_parents(25)) == 3      # the 26-node top-k tree
+
+
+def _lib_tree_parents(n):
+    from draft_token_verification_08_amd import synth
+    return synth.tree_parents(n)
+
+
 def test_mtp_host_checks():
     f = sv.lib().mtp_shift_insert
     p = C.c_void_p(16)
