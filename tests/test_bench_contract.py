@@ -44,7 +44,8 @@ def test_traffic_table_is_well_formed():
         # measured traffic is at least the algorithmic bytes (within counter noise)
         assert e["bytes_per_launch"] >= 0.99 * e["algorithmic_bytes_per_launch"], key
         if "stats_pass_bytes" in e:
-            assert e["stats_pass_bytes"] + e["draw_pass_bytes"] == e["bytes_per_launch"], key
+            rounds = e.get("rounds_per_call", 0) * e.get("round_bytes", 0)
+            assert e["stats_pass_bytes"] + rounds + e["draw_pass_bytes"] == e["bytes_per_launch"], key
 
 
 def test_traffic_used_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
