@@ -276,11 +276,16 @@ def spec_verify_tree_sample(target_logits, draft_logits, draft_tokens, draft_par
     """Sampling tree verification (see include/specverify.h): node j + 1 holds
     draft_tokens[b][j] below node draft_parents[b][j]; draft row r is the draft's
     logits at node r.  max_rounds bounds the residual updates a walk may take
-    (sv_tree_rounds(parents) is enough for one tree).  Returns (accepted_len,
-    emitted, path)."""
+    (sv_tree_rounds(parents) is enough for one tree); None takes the largest
+    sv_tree_rounds over the batch's trees, which copies draft_parents to the host
+    (a synchronisation).  Returns (accepted_len, emitted, path)."""
     B, n1, V = target_logits.shape
     n = n1 - 1
     dev = target_logits.device
+    if max_rounds is None:
+        par = draft_parents.cpu().tolist()
+        lens = draft_lens.cpu().tolist()
+        max_rounds = max([sv_tree_rounds(p[:max(0, min(L, n))]) for p, L in zip(par, lens)] + [0])
     if accepted_len is None:
         accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
     if emitted is None:

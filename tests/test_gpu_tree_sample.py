@@ -101,6 +101,22 @@ def test_enough_rounds_never_truncate(oracle):
     assert not fl & sv.SV_FLAG_TREE_TRUNCATED
 
 
+def test_default_rounds_from_the_trees(oracle):
+    """max_rounds=None: the binding takes the largest need over the batch's
+    trees (each cut to its draft length), so no walk is truncated."""
+    d = synth.make_tree_sample(420, device=DEV, B=40, n=16, V=4001, shape="random", ragged=True, temps=(0.7, 1.0),
+                               sigma=2.0)
+    fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    acc, emi, path = sv.spec_verify_tree_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_parents"],
+                                                d["draft_lens"], d["temperature"], d["uniforms"], None, err_flags=fl)
+    torch.cuda.synchronize()
+    o = _oracle(oracle, d)
+    assert not int(fl.item()) & sv.SV_FLAG_TREE_TRUNCATED
+    same = (acc.cpu().numpy() == o["accepted_len"]) & (emi.cpu().numpy() == o["emitted"]).all(1)
+    tie = (o["accept_margin"] < TOL).any(1) | (o["draw_margin"] < TOL)
+    assert (same | tie).all()
+
+
 def test_topk_tree_full_size(oracle):
     """64 sequences, the 26-node top-k tree, V = 128256 bf16, T = 0.7."""
     d = synth.make_tree_sample(7, device=DEV, B=64, n=25, V=128256)
