@@ -306,3 +306,14 @@ def test_noalloc_size_checks_touch_nothing():
     big = sv.sv_workspace_bytes(32768, 8, 152064, sv.SV_BF16)
     assert big > 2 * (16 << 20), big
     assert f(*a(B=32768, n=8, V=152064)) == sv.SV_EWORKSPACE      # beyond SV_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_capacity_as_documented():
+    """The capacities the header states for the static workspace (16 MiB) are
+    the largest batches whose sv_workspace_bytes fit it."""
+    text = open(HEADER).read()
+    cap = 16 << 20
+    assert "SV_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    for B, n, V in ((6563, 8, 152064), (8081, 4, 128256)):
+        assert f"{B} at n = {n}" in text or f"B up to {B} at n = {n}" in text, B
+        assert sv.sv_workspace_bytes(B, n, V, sv.SV_BF16) <= cap < sv.sv_workspace_bytes(B + 1, n, V, sv.SV_BF16)
