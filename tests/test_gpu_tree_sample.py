@@ -151,6 +151,23 @@ def test_law_on_the_gpu(oracle):
     _compare(oracle, d, sv.sv_tree_rounds(h["draft_parents"][0].tolist()), tag="law case")
 
 
+def test_masked_vocabulary(oracle):
+    """Rows with -inf entries (a masked vocabulary): target and draft rows mask
+    different random subsets, so drafted tokens can have p = 0 (never accepted)
+    or q = 0 (accepted whenever p > 0), and residuals skip masked entries."""
+    d = synth.make_tree_sample(430, device=DEV, B=48, n=14, V=3001, shape="random", ragged=True,
+                               temps=(0.0, 0.7, 1.0), dtype=torch.float32)
+    g = torch.Generator(device=DEV).manual_seed(431)
+    for key, frac in (("target", 0.3), ("draft", 0.3)):
+        m = torch.rand(d[key].shape, generator=g, device=DEV) < frac
+        d[key].masked_fill_(m, float("-inf"))
+    # every row keeps at least one finite entry
+    d["target"][..., 0] = 0.0
+    d["draft"][..., 0] = 0.0
+    acc, fl = _compare(oracle, d, _rounds(d), tag="masked vocabulary")
+    assert acc.max() >= 1
+
+
 def test_bad_parents_tokens_and_lengths(oracle):
     d = synth.make_tree_sample(21, device=DEV, B=6, n=5, V=700, shape="random", temps=(0.8,))
     par = d["draft_parents"]
