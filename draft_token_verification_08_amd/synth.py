@@ -458,6 +458,47 @@ def make_tree_law_case(seed: int, trials: int, V: int = 8, widths=(3, 2), T: flo
                 uniforms=uniforms, rows_t0=z0, rows_t1=z1, rows_t2=z2, B=trials, n=n, V=V, T=T, widths=widths)
 
 
+def make_tree_law_case3(seed: int, trials: int, V: int = 4, draft_sigma: float = 1.0, T: float = 1.0,
+                        device="cpu") -> dict:
+    """make_tree_law_case on a three-level binary tree (2 candidates at every
+    inner node, 14 candidates; nodes numbered level by level as tree_parents
+    does).  Tables z0, z1[a], z2[a][b], z3[a][b][c] (the target after the token
+    prefix; N(0, 1.5^2)) and the draft's (+ N(0, sigma^2)); every trial draws
+    each inner node's 2 children independently from the draft at that node."""
+    dev = torch.device(device)
+    g = _gen(seed, dev)
+    par = tree_parents(14, widths=(2, 2, 2, 0))
+    n = len(par)
+    zs, ds = [], []
+    for k in range(4):
+        z = 1.5 * torch.randn((V,) * (k + 1), generator=g, device=dev)
+        zs.append(z)
+        ds.append(z + draft_sigma * torch.randn((V,) * (k + 1), generator=g, device=dev))
+    temp = torch.full((trials,), float(T), device=dev)
+
+    def draw(rows):  # rows [trials, m, V]: one Gumbel-max draw from each
+        return _gumbel_draft(rows, temp, g).long()
+
+    x1 = draw(ds[0].expand(trials, 2, V))                                         # nodes 1, 2
+    x2 = draw(ds[1][x1].repeat_interleave(2, dim=1))                              # nodes 3..6
+    a2 = x1.repeat_interleave(2, dim=1)                                           # their parents' tokens
+    x3 = draw(ds[2][a2, x2].repeat_interleave(2, dim=1))                          # nodes 7..14
+    a3, b3 = a2.repeat_interleave(2, dim=1), x2.repeat_interleave(2, dim=1)
+    tokens = torch.cat([x1, x2, x3], dim=1)
+    target = torch.empty((trials, n + 1, V), device=dev)
+    draft = torch.empty((trials, n, V), device=dev)
+    target[:, 0], draft[:, 0] = zs[0], ds[0]
+    target[:, 1:3], draft[:, 1:3] = zs[1][x1], ds[1][x1]
+    target[:, 3:7], draft[:, 3:7] = zs[2][a2, x2], ds[2][a2, x2]
+    target[:, 7:15] = zs[3][a3, b3, x3]
+    draft[:, 7:14] = ds[3][a3, b3, x3][:, :7]                                    # leaves' rows (unused)
+    uniforms = torch.rand((trials, n + 1), generator=g, device=dev)
+    return dict(target=target, draft=draft, draft_tokens=tokens.to(torch.int32),
+                draft_parents=torch.as_tensor(par, dtype=torch.int32, device=dev).expand(trials, n).contiguous(),
+                draft_lens=torch.full((trials,), n, dtype=torch.int32, device=dev), temperature=temp,
+                uniforms=uniforms, tables=zs, B=trials, n=n, V=V, T=T)
+
+
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bfloat16 tensor (for the oracle)."""
     import numpy as np

@@ -151,6 +151,26 @@ def test_law_on_the_gpu(oracle):
     _compare(oracle, d, sv.sv_tree_rounds(h["draft_parents"][0].tolist()), tag="law case")
 
 
+@pytest.mark.parametrize("max_rounds", [63, 20])
+def test_star_tree_many_rounds(oracle, max_rounds):
+    """A star: 64 candidates below the root, so a walk can reject up to 63 of
+    them before the last, each later test needing one more round; with 20
+    rounds the walks that reject 21 times are truncated like the oracle's."""
+    B, n, V = 16, 64, 500
+    d = synth.make_tree_sample(440, device=DEV, B=B, n=n, V=V, shape="random", temps=(1.0,), sigma=3.0)
+    d["draft_parents"].zero_()
+    d["draft_lens"].fill_(n)
+    # the candidates are independent draws from the draft at the root
+    g = torch.Generator(device=DEV).manual_seed(441)
+    gum = -torch.log(-torch.log(torch.rand((B, n, V), generator=g, device=DEV).clamp_(1e-12, 1 - 1e-7)))
+    d["draft_tokens"].copy_(torch.argmax(d["draft"][:, :1].float() + gum, dim=-1).to(torch.int32))
+    d["uniforms"][:, :n] = 1.0 - (1.0 - d["uniforms"][:, :n]) ** 4     # mostly rejections
+    assert sv.sv_tree_rounds([0] * n) == 63
+    acc, fl = _compare(oracle, d, max_rounds, tag=f"star, {max_rounds} rounds")
+    if max_rounds < 63:
+        assert fl & sv.SV_FLAG_TREE_TRUNCATED
+
+
 def test_masked_vocabulary(oracle):
     """Rows with -inf entries (a masked vocabulary): target and draft rows mask
     different random subsets, so drafted tokens can have p = 0 (never accepted)
@@ -166,6 +186,15 @@ def test_masked_vocabulary(oracle):
     d["draft"][..., 0] = 0.0
     acc, fl = _compare(oracle, d, _rounds(d), tag="masked vocabulary")
     assert acc.max() >= 1
+
+
+def test_law_three_levels_on_the_gpu(oracle):
+    """The three-level law case (V = 4, binary tree of 14 candidates), 2 * 10^5
+    trials in one call, against the oracle trial by trial."""
+    h = synth.make_tree_law_case3(6, 200_000, device=DEV)
+    d = dict(target=h["target"], draft=h["draft"], draft_tokens=h["draft_tokens"], draft_parents=h["draft_parents"],
+             draft_lens=h["draft_lens"], temperature=h["temperature"], uniforms=h["uniforms"])
+    _compare(oracle, d, sv.sv_tree_rounds(h["draft_parents"][0].tolist()), tag="three-level law case")
 
 
 def test_bad_parents_tokens_and_lengths(oracle):

@@ -18,6 +18,8 @@ independent draws from the draft at that node.  The pins:
 - temperature 0 is the greedy tree rule; a fully accepted path draws the bonus
   token from its leaf's row by inverse CDF; bad parents and out-of-range tokens
   are flagged;
+- the law on a three-level binary tree (V = 4): the emitted token at every depth
+  follows the target row after the walk's token prefix;
 - a limit on the residual sums a walk may form drops the untested siblings,
   which is the rule on a smaller tree: with no sum allowed, the walk is the
   linear rule on the chain of first children (rows and uniforms gathered along
@@ -110,6 +112,53 @@ def test_tree_law_chi_square(oracle):
     print(f"\ntree law: {tests} chi-square tests, {fails} above the 1e-3 critical value, largest {worst:.1f}")
     assert tests >= 40
     assert fails <= 2, (fails, tests)
+
+
+def _law3_failures(o, seeds, trials=200_000, min_count=600):
+    """Chi-square tests (alpha = 1e-3, V - 1 dof) on the three-level tree: the
+    token emitted at depth k, given the walk's first k tokens, against the target
+    row after that prefix."""
+    fails = tests = 0
+    worst = 0.0
+    for seed in seeds:
+        h = synth.make_tree_law_case3(seed, trials)
+        V, T = h["V"], h["T"]
+        crit = st.chi2.ppf(1 - 1e-3, V - 1)
+        out = o.verify_tree_sample(h["target"].numpy(), h["draft"].numpy(), h["draft_tokens"].numpy(),
+                                   h["draft_parents"].numpy(), h["draft_lens"].numpy(), h["temperature"].numpy(),
+                                   h["uniforms"].numpy())
+        acc, emi = out["accepted_len"], out["emitted"]
+        for k in range(4):
+            z = h["tables"][k].numpy().reshape(-1, V)     # rows by prefix (a, b, c) in C order
+            sel = acc >= k
+            prefix = np.zeros(len(acc), np.int64)
+            for j in range(k):
+                prefix = prefix * V + emi[:, j]
+            for key in range(V ** k):
+                m_sel = sel & (prefix == key)
+                m = int(m_sel.sum())
+                if m < min_count:
+                    continue
+                pr = sps.softmax(z[key].astype(np.float64) / T)
+                obs = np.bincount(emi[m_sel, k], minlength=V)
+                stat = float(((obs - m * pr) ** 2 / (m * pr)).sum())
+                worst = max(worst, stat)
+                tests += 1
+                fails += stat > crit
+    return fails, tests, worst
+
+
+def test_tree_law_three_levels(oracle):
+    fails, tests, worst = _law3_failures(oracle, range(3))
+    print(f"\nthree-level law: {tests} chi-square tests, {fails} above 1e-3, largest {worst:.1f}")
+    assert tests >= 40
+    assert fails <= 2, (fails, tests)
+
+
+@pytest.mark.parametrize("plant", [8, 9])
+def test_tree_law_three_levels_rejects_planted_mistakes(planted, plant):
+    fails, tests, worst = _law3_failures(planted(plant), range(1))
+    assert worst > 100 and fails >= 2, (plant, fails, tests, worst)
 
 
 @pytest.mark.parametrize("max_rounds", [0, 1])
