@@ -35,7 +35,11 @@
  * precision (long double).  When the draft is almost the target, p_k - q_k is
  * a difference of nearly equal numbers; at a residual mass near 1e-10 binary64
  * keeps only about five of its digits, too few to place the draw to 1e-5 of the
- * mass.  Nothing is blocked, fused or reordered.
+ * mass.  As T -> 0 with both rows on one top token no precision suffices for
+ * the difference itself (p_0 = 1 / (1 + tail) rounds to 1), so the residual is
+ * written as an exact rearrangement in which tokens that the rows share cancel
+ * before anything is rounded (resid_t).  Nothing is blocked, fused or
+ * reordered.
  *
  * Readings of points the pages leave open:
  *   - acceptance of draft x_j:  u[b][j] < p_j(x_j) / q_j(x_j); q(x) = 0 gives
@@ -136,6 +140,19 @@ static double prob_at(const void *rows, int dt, size_t base, int i, double T, do
     return exp((logit_at(rows, dt, base + (size_t)i) - m) / T - logS);
 }
 
+/* The acceptance ratio p(x) / q(x) of a target and a draft probability at the
+ * same temperature (Speculative decoding section: x is kept iff u < p(x) /
+ * q(x)), formed from their logarithms log p = (z_t - m_t) / T - log S_t and
+ * log q = (z_d - m_d) / T - log S_d, so that it keeps its value when both
+ * probabilities lie below the binary64 range (T -> 0).  A -inf logit is a
+ * probability of exactly 0: q(x) = 0 < p(x) gives +inf, p(x) = 0 gives 0. */
+static double accept_ratio(double zt, double mt, double lst, double zd, double md, double lsd, double T)
+{
+    if (zt == -INFINITY) return 0.0;
+    if (zd == -INFINITY) return INFINITY;
+    return exp(((zt - mt) / T - lst) - ((zd - md) / T - lsd));
+}
+
 /* The whole distribution softmax(z / T) of one row in extended precision:
  * p_i = exp((z_i - m) / T) / S with S = sum_i exp((z_i - m) / T), m the row max. */
 static void row_probs_ld(const void *rows, int dt, size_t base, int V, double T, long double *p)
@@ -151,6 +168,106 @@ static void row_probs_ld(const void *rows, int dt, size_t base, int V, double T,
         S += p[i];
     }
     for (int i = 0; i < V; ++i) p[i] /= S;
+}
+
+/* Row maximum (-inf for an empty or fully masked row). */
+static double row_max(const void *rows, int dt, size_t base, int V)
+{
+    double m = -INFINITY;
+    for (int i = 0; i < V; ++i) {
+        double v = logit_at(rows, dt, base + (size_t)i);
+        if (v > m) m = v;
+    }
+    return m;
+}
+
+/* The residual of a target row and a draft row at lam = 1 + mu, exactly as
+ * defined (Speculative decoding section, the first reference: after a rejection
+ * the token is drawn from max(0, p - q) normalised; SpecInfer: after k rejections
+ * at a node, from max(0, p - lam_k q)).  With a_i = (z_t,i - m_t) / T and
+ * b_i = (z_d,i - m_d) / T (each row relative to its own maximum), S_t = sum e^a
+ * and S_d = sum e^b, multiplying p_i - lam q_i by the positive S_t S_d gives
+ *   R_i = (e^{a_i} - e^{b_i}) S_t + e^{a_i} Delta - mu e^{b_i} S_t,
+ *   Delta = S_d - S_t = sum_j (e^{b_j} - e^{a_j}).
+ * A token with a_j = b_j adds exactly zero to Delta and to its own first term, so
+ * the digits that p_i - q_i loses where p and q agree beyond the arithmetic's
+ * precision (T -> 0 with both rows on the same top token: 1 + tail rounds to 1)
+ * are never formed.  Every term is carried in units of e^s, s the largest of a_j
+ * and b_j over the tokens with a_j != b_j, so that none leaves the range however
+ * small the residual is; mu and the residual mass are carried in the same units.
+ * A -inf logit is a probability of 0 (its e^a is 0); a row with no finite logit
+ * takes every a_i = -inf. */
+typedef struct {
+    const void *trows, *drows;
+    int dt, V;
+    size_t tb, db;      /* first element of the target row and of the draft row */
+    long double T, mt, md;
+    long double St, Sd; /* sum e^{a_i}, sum e^{b_i} */
+    long double s;      /* the unit exponent; -inf when a_i = b_i for every i (p = q) */
+    long double dlt;    /* Delta e^{-s} */
+} resid_t;
+
+static long double rel_logit(const void *rows, int dt, size_t at, long double m, long double T)
+{
+    if (m == -INFINITY) return -INFINITY;
+    return ((long double)logit_at(rows, dt, at) - m) / T;
+}
+
+static void resid_setup(resid_t *r, const void *trows, const void *drows, int dt, size_t tb, size_t db, int V,
+                        double T)
+{
+    r->trows = trows;
+    r->drows = drows;
+    r->dt = dt;
+    r->V = V;
+    r->tb = tb;
+    r->db = db;
+    r->T = T;
+    r->mt = row_max(trows, dt, tb, V);
+    r->md = row_max(drows, dt, db, V);
+    r->St = r->Sd = 0.0L;
+    r->s = -INFINITY;
+    for (int i = 0; i < V; ++i) {
+        const long double a = rel_logit(trows, dt, tb + (size_t)i, r->mt, r->T);
+        const long double b = rel_logit(drows, dt, db + (size_t)i, r->md, r->T);
+        r->St += expl(a);
+        r->Sd += expl(b);
+        if (a != b) {
+            if (a > r->s) r->s = a;
+            if (b > r->s) r->s = b;
+        }
+    }
+    r->dlt = 0.0L;
+    if (r->s == -INFINITY) return;
+    for (int i = 0; i < V; ++i) {
+        const long double a = rel_logit(trows, dt, tb + (size_t)i, r->mt, r->T);
+        const long double b = rel_logit(drows, dt, db + (size_t)i, r->md, r->T);
+        if (a != b) r->dlt += expl(b - r->s) - expl(a - r->s);
+    }
+}
+
+/* R_i e^{-s} at mu = mu_s e^s (see resid_t); only for rows with s > -inf. */
+static long double resid_at(const resid_t *r, int i, long double mu_s)
+{
+    const long double a = rel_logit(r->trows, r->dt, r->tb + (size_t)i, r->mt, r->T);
+    const long double b = rel_logit(r->drows, r->dt, r->db + (size_t)i, r->md, r->T);
+    long double R = expl(a) * r->dlt;
+    if (a != b) R += (expl(a - r->s) - expl(b - r->s)) * r->St;
+    if (mu_s != 0.0L && b != -INFINITY) R -= mu_s * expl(b) * r->St;
+    return R;
+}
+
+/* Weights w_i = max(0, R_i e^{-s}) at mu = mu_s e^s into w[V]; returns the
+ * residual mass sum max(0, p - lam q) in units of e^s, sum w / (S_t S_d). */
+static long double resid_weights(const resid_t *r, long double mu_s, long double *w)
+{
+    long double Z = 0.0L;
+    for (int i = 0; i < r->V; ++i) {
+        const long double R = r->s == -INFINITY ? 0.0L : resid_at(r, i, mu_s);
+        w[i] = R > 0.0L ? R : 0.0L;
+        Z += w[i];
+    }
+    return Z / (r->St * r->Sd);
 }
 
 /* Inverse CDF over unnormalised weights in ascending index order.
@@ -270,13 +387,13 @@ static void verify_one(const job_t *J, int b, long double *w /* scratch [2V] */)
                 break;
             }
             double u = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + j], &flags);
-            double p = prob_at(J->target, J->dt, trow0 + (size_t)j * V, x[j], T, mt[j], lst[j]);
-            double q = prob_at(J->draft, J->dt, drow0 + (size_t)j * V, x[j], T, md[j], lsd[j]);
-            double ratio = (q > 0.0) ? p / q : (p > 0.0 ? INFINITY : 0.0);
+            const double zt = logit_at(J->target, J->dt, trow0 + (size_t)j * V + (size_t)x[j]);
+            const double zd = logit_at(J->draft, J->dt, drow0 + (size_t)j * V + (size_t)x[j]);
+            double ratio = accept_ratio(zt, mt[j], lst[j], zd, md[j], lsd[j], T);
             if (J->accept_margin) J->accept_margin[(size_t)b * n + j] = fabs(u - ratio);
 #if SV_ORACLE_PLANT == 3
             /* planted mistake for negative-control tests: the ratio inverted */
-            ratio = (p > 0.0) ? q / p : (q > 0.0 ? INFINITY : 0.0);
+            ratio = accept_ratio(zd, md[j], lsd[j], zt, mt[j], lst[j], T);
 #endif
             if (!(u < ratio)) {
                 k = j;
@@ -290,20 +407,15 @@ static void verify_one(const job_t *J, int b, long double *w /* scratch [2V] */)
         if (rejected) ufinal = sanitize_uniform(J->uniforms[(size_t)b * (n + 1) + k], &flags);
 #endif
         if (rejected) {
-            /* residual distribution max(0, p_k - q_k), in extended precision */
-            long double *q = w + V;
-            row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
-            row_probs_ld(J->draft, J->dt, drow0 + (size_t)k * V, V, T, q);
-            long double Z = 0.0L;
-            for (int i = 0; i < V; ++i) {
-                long double d = w[i] - q[i];
+            /* residual distribution max(0, p_k - q_k), formed exactly (resid_t) */
+            resid_t rs;
+            resid_setup(&rs, J->target, J->draft, J->dt, trow0 + (size_t)k * V, drow0 + (size_t)k * V, V, T);
+            long double Z = resid_weights(&rs, 0.0L, w);
 #if SV_ORACLE_PLANT == 1
-                /* planted mistake: plain target sampling at the rejection */
-                d = w[i];
+            /* planted mistake: plain target sampling at the rejection */
+            row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
+            Z = 1.0L;
 #endif
-                w[i] = d > 0.0L ? d : 0.0L;
-                Z += w[i];
-            }
             if (!(Z > 0.0L)) {
                 flags |= OR_FLAG_ZERO_RESIDUAL;
                 row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
@@ -608,8 +720,9 @@ int sv_oracle_verify_tree_greedy(const void *target_logits, int dt, const int32_
  * rejection leaves a later sibling to test and the walk has formed its
  * max_rounds sums already, the untested siblings are dropped, the token is
  * drawn from max(0, p_u - lam_{k+1} q_u) (that residual needs no new sum
- * before the draw), and the sequence is flagged.  The residual sums and the draw are formed in extended
- * precision, the first acceptance test at a node as the linear rule forms it. */
+ * before the draw), and the sequence is flagged.  The residual sums, the later
+ * siblings' ratios and the draw are formed from resid_t in extended precision,
+ * the first acceptance test at a node as the linear rule forms it. */
 typedef struct {
     const void *target, *draft;
     int dt;
@@ -666,39 +779,49 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
             J->draw_margin[b] = margin;
             break;
         }
-        row_probs_ld(J->draft, J->dt, drow0 + (size_t)u * V, V, T, q);
         double mt, lst, md, lsd;
         (void)row_softmax_stats(J->target, J->dt, trow0 + (size_t)u * V, V, T, &mt, &lst);
         (void)row_softmax_stats(J->draft, J->dt, drow0 + (size_t)u * V, V, T, &md, &lsd);
-        long double lam = 0.0L, M = 1.0L;
-        int accepted = -1;
+        /* after k >= 1 rejections at u: lam_k = 1 + mu, mu and M_k carried in
+         * units of e^s of the pair's resid_t (mu_s = mu e^{-s}, M_s = M_k e^{-s}) */
+        resid_t rs;
+        int rejections = 0, accepted = -1, have_rs = 0;
+        long double mu_s = 0.0L, M_s = 0.0L;
         for (int j = first; j < L; ++j) {
             if (par[j] != u || par[j] > j) continue;
             const int xc = x[j];
             double ratio = 0.0;
             if (xc >= 0 && xc < V) {
-                if (lam == 0.0L) {
-                    /* the first test at a node: p_u(x) / q_u(x), as the linear rule forms it */
-                    const double pp = prob_at(J->target, J->dt, trow0 + (size_t)u * V, xc, T, mt, lst);
-                    const double qq = prob_at(J->draft, J->dt, drow0 + (size_t)u * V, xc, T, md, lsd);
-                    ratio = (qq > 0.0) ? pp / qq : (pp > 0.0 ? INFINITY : 0.0);
+                if (rejections == 0) {
+                    /* p_u(x) / q_u(x), as the linear rule forms it */
+                    ratio = accept_ratio(logit_at(J->target, J->dt, trow0 + (size_t)u * V + (size_t)xc), mt, lst,
+                                         logit_at(J->draft, J->dt, drow0 + (size_t)u * V + (size_t)xc), md, lsd, T);
                 } else {
-                    const long double r = p[xc] - lam * q[xc];
-                    const long double pr = (M > 0.0L && r > 0.0L) ? r / M : 0.0L;
-                    ratio = (q[xc] > 0.0L) ? (double)(pr / q[xc]) : (pr > 0.0L ? INFINITY : 0.0);
+                    /* the residual's ratio (p_u(x) - lam q_u(x)) / (M_k q_u(x)) =
+                     * R_x / (S_t e^{b_x} M_s) with R_x in units of e^s (resid_t);
+                     * q_u(x) = 0 < p_u(x) - lam q_u(x) gives +inf */
+                    const long double R = resid_at(&rs, xc, mu_s);
+                    const long double bx = rel_logit(J->draft, J->dt, drow0 + (size_t)u * V + (size_t)xc, rs.md, rs.T);
+                    if (R > 0.0L && M_s > 0.0L) ratio = (double)(R / (rs.St * expl(bx) * M_s));
                 }
             }
             const double uu = sanitize_uniform(uni[j], &flags);
             J->accept_margin[(size_t)b * n + j] = fabs(uu - ratio);
             if (uu < ratio) { accepted = j; break; }
+            if (!have_rs) {
+                resid_setup(&rs, J->target, J->draft, J->dt, trow0 + (size_t)u * V, drow0 + (size_t)u * V, V, T);
+                have_rs = 1;
+            }
 #if SV_ORACLE_PLANT == 8
             /* planted mistake: every sibling tested against p_u itself (no
              * residual update between siblings); the draw still takes
              * max(0, p_u - q_u) */
             continue;
 #endif
-            /* rejected: p' <- max(0, p' - q_u) normalised */
-            lam += M;
+            /* rejected: p' <- max(0, p' - q_u) normalised, i.e. lam_{k+1} = lam_k + M_k
+             * (lam_1 = 1: mu stays 0) */
+            if (rejections > 0) mu_s += M_s;
+            ++rejections;
             int later = 0;
             for (int t = j + 1; t < L && !later; ++t) later = (par[t] == u);
             if (!later) break; /* the draw forms its own sum */
@@ -707,11 +830,7 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
                 break;
             }
             ++sums;
-            M = 0.0L;
-            for (int i = 0; i < V; ++i) {
-                const long double d = p[i] - lam * q[i];
-                if (d > 0.0L) M += d;
-            }
+            M_s = resid_weights(&rs, mu_s, q);
         }
         if (accepted >= 0) {
             path[depth] = accepted + 1;
@@ -722,14 +841,9 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
         }
         /* every child rejected: draw from max(0, p_u - lam q_u) */
 #if SV_ORACLE_PLANT == 8 || SV_ORACLE_PLANT == 9
-        lam = 1.0L; /* planted mistakes: the draw ignores the later siblings' updates */
+        mu_s = 0.0L; /* planted mistakes: the draw ignores the later siblings' updates */
 #endif
-        long double Z = 0.0L;
-        for (int i = 0; i < V; ++i) {
-            const long double d = p[i] - lam * q[i];
-            q[i] = d > 0.0L ? d : 0.0L;
-            Z += q[i];
-        }
+        const long double Z = resid_weights(&rs, mu_s, q);
         double margin = 0.0;
         if (Z > 0.0L) {
             y = draw_inverse_cdf(q, V, sanitize_uniform(uni[n], &flags), &margin);

@@ -364,3 +364,65 @@ def test_sample_rows_clamps_row_index(oracle):
     assert (out["seq_flags"] & orc.FLAG_ROW_CLAMPED).tolist() == [32, 0, 32, 0]
     none = oracle.sample_rows(z, np.zeros(4, np.float32), np.zeros(4, np.float32), None)
     assert none["tokens"].tolist() == [int(np.argmax(z[b, 0])) for b in range(4)]
+
+
+def test_acceptance_ratio_survives_underflow(oracle):
+    """At T = 1e-3 a token 1.0 below the target's maximum and 0.999 below the
+    draft's has p(x) ~ e^-1000 and q(x) ~ e^-999, both below the binary64 range,
+    while p(x) / q(x) = (1 + e^(d/T)) / (1 + e^(b/T)) (two-entry rows) is about
+    e^-1: uniforms below the ratio accept, above it reject, and the margin is
+    |u - ratio|."""
+    T = np.float32(1e-3)
+    b, d = np.float32(1.0), np.float32(0.999)
+    zt = np.array([[[0.0, b], [0.0, 0.0]]] * 4, np.float32)     # slot 1: the bonus row
+    zd = np.array([[[0.0, d]]] * 4, np.float32)
+    x = np.zeros((4, 1), np.int32)
+    Td = float(T)
+    ratio = np.exp((float(d) - float(b)) / Td) * (1.0 + np.exp(-float(d) / Td)) / (1.0 + np.exp(-float(b) / Td))
+    assert 0.3 < ratio < 0.45
+    u = np.array([[ratio - 1e-3, 0.5], [ratio + 1e-3, 0.5], [0.0, 0.5], [0.99, 0.5]], np.float32)
+    out = oracle.verify_sample(zt, zd, x, np.ones(4, np.int32), np.full(4, T, np.float32), u)
+    assert list(out["accepted_len"]) == [1, 0, 1, 0]
+    for i in range(4):
+        assert abs(out["accept_margin"][i, 0] - abs(float(u[i, 0]) - ratio)) < 1e-9
+
+
+def test_residual_of_rows_sharing_their_top_token_at_low_temperature(oracle):
+    """Both rows put all but a sliver of mass on token 0.  Target [0, -3, -2],
+    draft [0, -1, -4] at T = 1e-3, e = e^-1000: with S_t = 1 + e^3 + e^2 and
+    S_d = 1 + e + e^4 the residual is
+      p_0 - q_0 = (S_d - S_t) / (S_t S_d) ~ e,   p_1 - q_1 < 0,
+      p_2 - q_2 = (e^2 S_d - e^4 S_t) / (S_t S_d) ~ e^2,
+    so after the rejection of token 1 (p_1 / q_1 ~ e^-2000) the draw is token
+    0 except with probability ~ e^-1000: token 0 for every binary32 uniform.  The
+    top token's weight is a difference of the two normalisers' tails: forming p_0
+    and q_0 first rounds both to 1 and leaves only token 2.  At T = 1e-5 every
+    tail lies below the extended range too (e^-100000) and the residual is still
+    token 0, with no zero-residual flag."""
+    for T in (1e-3, 1e-5):
+        zt = np.array([[[0.0, -3.0, -2.0], [0.0, 0.0, 0.0]]] * 3, np.float32)
+        zd = np.array([[[0.0, -1.0, -4.0]]] * 3, np.float32)
+        x = np.ones((3, 1), np.int32)
+        u = np.array([[0.5, 0.0], [0.5, 0.5], [0.0, 1.0 - 2.0 ** -24]], np.float32)
+        out = oracle.verify_sample(zt, zd, x, np.ones(3, np.int32), np.full(3, T, np.float32), u)
+        assert list(out["accepted_len"]) == [0, 0, 0], T       # p(1) / q(1) ~ e^(-2/T)
+        assert out["emitted"].tolist() == [[0, -1]] * 3, T
+        assert not (out["seq_flags"] & 16).any(), T
+        # the draw margin: the CDF boundary at token 0's end lies e^(-1/T) below 1
+        assert abs(out["draw_margin"][1] - 0.5) < 1e-12
+
+
+def test_residual_of_rows_sharing_their_top_token_in_the_tail(oracle):
+    """Target [0, -1, -9, -5], draft [0, -2, -9, -3] at T = 1e-3: the drafted
+    token 3 has p / q ~ e^-2000 and is rejected; token 2 has the same relative
+    logit in both rows (p_2 - q_2 = e^-9000 (1 / S_t - 1 / S_d) < 0), the
+    target's tail is the heavier (S_t - S_d ~ e^-1000 > 0, so p_0 < q_0), and
+    token 1 alone has p > q: the draw is token 1 for every uniform.  (With the
+    sign of S_d - S_t reversed the top token would carry half the weight.)"""
+    zt = np.array([[[0.0, -1.0, -9.0, -5.0], [0.0, 0.0, 0.0, 0.0]]] * 3, np.float32)
+    zd = np.array([[[0.0, -2.0, -9.0, -3.0]]] * 3, np.float32)
+    x = np.full((3, 1), 3, np.int32)
+    u = np.array([[0.5, 0.0], [0.5, 0.5], [0.0, 1.0 - 2.0 ** -24]], np.float32)
+    out = oracle.verify_sample(zt, zd, x, np.ones(3, np.int32), np.full(3, 1e-3, np.float32), u)
+    assert list(out["accepted_len"]) == [0, 0, 0]
+    assert out["emitted"].tolist() == [[1, -1]] * 3

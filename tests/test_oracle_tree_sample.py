@@ -276,3 +276,25 @@ def test_flags_and_out_of_range(oracle):
     assert f[0] & 64 and f[1] & 2 and f[2] & 1
     assert 3 not in list(out["path"][0])              # node 3 (bad parent) is never on the path
     assert out["path"][1, 0] != 1                     # node 1 (out of range) is not accepted
+
+
+def test_later_sibling_on_a_shared_top_token_at_low_temperature(oracle):
+    """Root children: token 1, then token 0, at T = 1e-3 with target row 0
+    [0, -3, -2] and draft row 0 [0, -1, -4] (e = e^-1000, S_t = 1 + e^3 + e^2,
+    S_d = 1 + e + e^4).  Token 1 has p / q ~ e^-2000: rejected.  The residual is
+    then max(0, p - q) / M_1 with M_1 = (S_d - S_t + e^2 S_d - e^4 S_t) / (S_t S_d),
+    and token 0's ratio (p_0 - q_0) / (M_1 q_0) = (S_d - S_t) S_d / (S_d - S_t +
+    e^2 S_d - e^4 S_t) = 1 - 2 e^2 + ...: accepted for every binary32 uniform.
+    The walk moves to node 2, a leaf, whose row [-1, 5, 0] puts all but e^-5000
+    of its mass on token 1, the bonus token.  Forming p_0 and q_0 first rounds
+    both to 1, so p_0 / q_0 - lam_1 is 0 and token 0 would be rejected."""
+    zt = np.array([[[0.0, -3.0, -2.0], [0.0, 0.0, 0.0], [-1.0, 5.0, 0.0]]] * 3, np.float32)
+    zd = np.array([[[0.0, -1.0, -4.0], [0.0, 0.0, 0.0]]] * 3, np.float32)
+    x = np.array([[1, 0]] * 3, np.int32)
+    par = np.array([[0, 0]] * 3, np.int32)
+    u = np.array([[0.5, 0.5, 0.5], [0.0, 1.0 - 2.0 ** -24, 0.5], [1.0 - 2.0 ** -24, 0.0, 0.999]], np.float32)
+    out = oracle.verify_tree_sample(zt, zd, x, par, np.full(3, 2, np.int32), np.full(3, 1e-3, np.float32), u)
+    assert list(out["accepted_len"]) == [1, 1, 1]
+    assert out["path"].tolist() == [[2, -1]] * 3
+    assert out["emitted"].tolist() == [[0, 1, -1]] * 3
+    assert not (out["seq_flags"] & 16).any()
