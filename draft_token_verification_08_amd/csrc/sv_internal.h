@@ -60,7 +60,8 @@ struct DrawDesc {
     float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
     float lamq;     // residual weights max(0, p - lamq q): 1 after one rejection (tree walks: more)
-    float pad;
+    float mu;       // lam - 1 of a residual draw for the near form (0 after one rejection):
+                    // the value itself when at least 2^-126, else log2(lam - 1) (< -126)
 };
 
 // A sampling tree walk (per sequence), kept in the workspace between the
@@ -72,7 +73,8 @@ struct TreeWalk {
     int next;       // the next child to test is the first node j + 1 with j >= next below u
     int depth;      // nodes on the kept path so far
     double lam;     // lam_k at node u (0: no child rejected yet)
-    double M;       // M_k = sum max(0, p_u - lam q_u) (1 while lam = 0)
+    double lmu;     // log2(lam_k - 1) once lam_k >= 1 (-inf: lam_k = 1), kept where lam_k - 1
+                    // lies below binary64's resolution at 1
     uint32_t flags;
     float c;        // log2(e) / T
     int path[kMaxDraft];

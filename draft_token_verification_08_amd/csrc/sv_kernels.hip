@@ -647,25 +647,42 @@ __device__ __forceinline__ float exp2m1_small(float x) {
     return a * x;
 }
 
-// Residual terms of one token when both rows are scaled by one common maximum M
-// (near residual): A = 2^((z_t - M) c), B = 2^((z_d - M) c) and Dl = B - A.
-// The exponents are formed as fma(z, c, -Mc) with Mc = fl(M c): the rounding of
-// Mc scales every A and B alike, which no ratio or normalised weight sees.
-// With x = (z_d - z_t) c, Dl is formed as A (2^x - 1) when |x| <= 1/4 (no
-// cancellation), else as B - A; a token the two rows share has x = 0 and
-// Dl = 0 exactly.  With S'_t = sum A, S'_d = sum B and rho = S'_d / S'_t - 1,
-//   p - q = A / S'_t - B / S'_d = (rho A - Dl) / (S'_t (1 + rho)),
-// so max(0, rho A - Dl) are residual weights up to one common factor.
+// Residual terms of one token in the near form, each row relative to its own
+// maximum (at = z_t - m_t, ad = z_d - m_d, both <= 0 and exact for bf16 logits):
+// A = 2^(at c), B = 2^(ad c) and the difference Dl = B - A in units of
+// 2^(sl c), sl <= 0 a shift common to the row pair.  With x = (ad - at) c, Dl is
+// formed as 2^((at - sl) c) (2^x - 1) when |x| <= 1/4 (no cancellation), else
+// as 2^((ad - sl) c) - 2^((at - sl) c); a token whose relative logits agree
+// (at = ad, masked in both rows included) has Dl = 0 exactly and no power of
+// the shift is formed for it (only tokens with at != ad lie at or below sl).
+// With S_t = sum A, S_d = sum B, rho = (S_d - S_t) 2^(-sl c) / S_t = sum Dl / S_t
+// and lam = 1 + mu:
+//   p - lam q = A / S_t - lam B / S_d = 2^(sl c) (rho A - Dl - mu' B) / S_d,
+// mu' = mu 2^(-sl c), so max(0, rho A - Dl - mu' B) are residual weights up to
+// one common factor; the tokens the rows share never enter a difference.
 struct NearTerm {
     float A, Dl;
-    bool same;  // x == 0: the token's logit is the same in both rows
 };
-__device__ __forceinline__ NearTerm near_term(float Mc, float c, float zt, float zd) {
-    const float A = exp2_fast(fmaf(zt, c, -Mc));
-    const float x = (zd - zt) * c;
-    const float small = A * exp2m1_small(x);
-    const float direct = exp2_fast(fmaf(zd, c, -Mc)) - A;
-    return NearTerm{A, fabsf(x) <= 0.25f ? small : direct, x == 0.f};
+__device__ __forceinline__ float near_rel(float z, float m) { return m > -FLT_MAX ? z - m : -INFINITY; }
+__device__ __forceinline__ NearTerm near_term(float m_t, float m_d, float sl, float c, float zt, float zd) {
+    const float at = near_rel(zt, m_t), ad = near_rel(zd, m_d);
+    const float A = exp2_fast(at * c);
+    if (at == ad) return NearTerm{A, 0.f};
+    const float x = (ad - at) * c;
+    const float As = exp2_fast((at - sl) * c);
+    const float Dl = fabsf(x) <= 0.25f ? As * exp2m1_small(x) : exp2_fast((ad - sl) * c) - As;
+    return NearTerm{A, Dl};
+}
+// The residual weight of one token in the near form (see near_term()).
+__device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, float c, float rho, float mu, float zt,
+                                            float zd) {
+    const NearTerm t = near_term(m_t, m_d, sl, c, zt, zd);
+    float w = fmaf(rho, t.A, -t.Dl);
+    if (mu != 0.f) {
+        const float B = exp2_fast(near_rel(zd, m_d) * c);
+        if (B > 0.f) w = fmaf(-mu, B, w);
+    }
+    return fmaxf(w, 0.f);
 }
 
 // How a draw weighs one element (all weights up to a factor common to the row):
@@ -674,9 +691,10 @@ __device__ __forceinline__ NearTerm near_term(float Mc, float c, float zt, float
 //   kWResFar:   max(0, P - lam Q) with P = 2^(z_t c - fl(m_t c)), Q = 2^(z_d c -
 //               fl(m_d c)) (one rounding each: far_p()), each row scaled by its own
 //               maximum (mA = m_t) and lam the ratio of their sums (S_t / S_d);
-//   kWResNear:  max(0, rho A - opm Dl) of near_term() with M = mA (Mc = fl(mA c)):
-//               the residual max(0, p - lam q) with rho = rho' - (lam - 1) and
-//               opm = lam (rho' = S'_d / S'_t - 1; lam = 1 after one rejection).
+//   kWResNear:  near_weight(): max(0, rho A - Dl - mu B) of near_term(), each
+//               row relative to its own maximum (mA = m_t), differences in
+//               units of 2^(sl c): the residual max(0, p - lam q) with
+//               lam = 1 + mu 2^(sl c) (mu = 0 after one rejection).
 enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
 struct WSpec {
     int mode;
@@ -685,8 +703,8 @@ struct WSpec {
     float m_d;  // kWResFar: the draft row's maximum
     float lam;  // kWResFar
     float rho;  // kWResNear
-    float Mc;   // kWResNear: fl(mA c)
-    float opm;  // kWResNear
+    float sl;   // kWResNear: the shift of the differences (<= 0)
+    float mu;   // kWResNear: (lam - 1) 2^(-sl c)
     float nmt;  // kWResFar: neg_scaled(mA, c)
     float nmd;  // kWResFar: neg_scaled(m_d, c)
 };
@@ -705,8 +723,7 @@ __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd)
         const float Q = far_p(s.nmd, s.c, zd);
         return fmaxf(fmaf(-s.lam, Q, P), 0.f);
     }
-    const NearTerm t = near_term(s.Mc, s.c, zt, zd);
-    return fmaxf(fmaf(s.rho, t.A, -s.opm * t.Dl), 0.f);
+    return near_weight(s.mA, s.m_d, s.sl, s.c, s.rho, s.mu, zt, zd);
 }
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
     return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1001,8 +1018,11 @@ __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const Seq
 // (lam_0 = 0, M_0 = 1, lam_{k+1} = lam_k + M_k).  An accepted child moves the
 // walk down; with no child left the token is drawn from max(0, p_u - lam q_u)
 // (from p_u itself when u has no children).  The first test at a node needs
-// only the rows' statistics; each later one needs M_k, a full reduction of the
-// pair (p_u, q_u), which a round kernel provides: the walk then stops, pending.
+// only the rows' statistics; each later one needs the residual at lam_k, a full
+// reduction of the pair (p_u, q_u), which a round kernel provides (the test's
+// ratio and log2 M_k, RoundStep): the walk then stops, pending.  lam_k - 1 is
+// kept as log2 (lmu) besides lam_k, so that a residual mass below binary64's
+// resolution at 1 (T -> 0, rows on one top token) still enters lam.
 
 // One sequence's walk inputs, staged in LDS: statistics of target rows (mt, St)
 // and draft rows (md, Sd) by node, and node j + 1's token, parent (-1 when not
@@ -1018,35 +1038,53 @@ struct WalkRows {
     const int* par;
 };
 
-// The acceptance ratio of node j + 1 below node u at (lam, M).  lam = 0 forms
-// p/q as the linear decision does.
-__device__ double tree_ratio(const WalkRows& r, int j, int u, int V, float c, double lam, double M) {
+// The first acceptance ratio at node u, of node j + 1: p_u(x) / q_u(x) formed in
+// log space as the linear decision forms it (so it keeps its value when both
+// probabilities are below the binary64 range).
+__device__ double tree_ratio(const WalkRows& r, int j, int u, int V, float c) {
     const int x = r.x[j];
     if (x < 0 || x >= V) return 0.0;
     const float zt = r.gt[j], zd = r.gd[j];
-    const bool pz = zt == -INFINITY, qz = zd == -INFINITY;
+    if (zt == -INFINITY) return 0.0;
+    if (zd == -INFINITY) return INFINITY;
     const double cd = (double)c;
-    if (lam == 0.0) {
-        if (qz) return pz ? 0.0 : INFINITY;
-        if (pz) return 0.0;
-        const double lr = ((double)zt - (double)r.mt[u]) * cd - ((double)zd - (double)r.md[u]) * cd;
-        return exp2(lr) * (r.Sd[u] / r.St[u]);
-    }
-    const double pv = pz ? 0.0 : exp2(((double)zt - (double)r.mt[u]) * cd) / r.St[u];
-    const double qv = qz ? 0.0 : exp2(((double)zd - (double)r.md[u]) * cd) / r.Sd[u];
-    const double num = pv - lam * qv;
-    if (!(num > 0.0) || !(M > 0.0)) return 0.0;
-    return qv > 0.0 ? num / (M * qv) : INFINITY;
+    const double lr = ((double)zt - (double)r.mt[u]) * cd - ((double)zd - (double)r.md[u]) * cd;
+    return exp2(lr) * (r.Sd[u] / r.St[u]);
+}
+
+// What one round hands the walk for the one test it makes possible: the
+// pending child's acceptance ratio under the residual at the current lam_k,
+// (p_u(x) - lam_k q_u(x)) / (M_k q_u(x)), and log2 M_k for lam_{k+1} = lam_k + M_k.
+struct RoundStep {
+    double ratio, lM;
+};
+
+// log2(2^a + 2^b)
+__device__ __forceinline__ double log2_add(double a, double b) {
+    if (a == -INFINITY) return b;
+    if (b == -INFINITY) return a;
+    const double hi = fmax(a, b), lo = fmin(a, b);
+    return hi + log2(1.0 + exp2(lo - hi));
+}
+// DrawDesc::mu from log2(lam - 1), and back (see DrawDesc)
+__device__ __forceinline__ float encode_mu(double lmu) {
+    if (lmu == -INFINITY) return 0.f;
+    return lmu >= -126.0 ? (float)exp2(lmu) : (float)lmu;
+}
+__device__ __forceinline__ double decode_lmu(float mu) {
+    if (mu == 0.f) return -INFINITY;
+    return mu > 0.f ? log2((double)mu) : (double)mu;
 }
 
 // Runs the walk from its state (one thread).  Returns true when it has
 // finished: *d then describes the draw (kDrawTarget at a node with no child
 // left and no rejection, else kDrawResidual with lamq = lam).  Returns false,
-// with the state pending, when the next test needs M at the current lam (only
-// if can_pend; otherwise the children not yet tested are left out, which is the
+// with the state pending, when the next test needs the residual at the current
+// lam and no round's result for that test (`step`, when have_step) is left (only if
+// can_pend; otherwise the children not yet tested are left out, which is the
 // same rule on a smaller tree, and SV_FLAG_TREE_TRUNCATED is raised).
-__device__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, int L, int V, const float* uni, bool can_pend,
-                              DrawDesc* d) {
+__device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, int L, int V, const float* uni,
+                                              bool can_pend, RoundStep step, bool have_step, DrawDesc* d) {
     for (;;) {
         int j = -1;
         for (int t = w.next; t < L; ++t)
@@ -1070,11 +1108,19 @@ __device__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, int L, int V, cons
                 d->m_d = r.md[u];
                 d->lq = (float)log2(r.St[u] / r.Sd[u]);
                 d->lamq = (float)w.lam;
+                d->mu = encode_mu(w.lmu);
             }
             w.status = kWalkIdle;
             return true;
         }
-        if (w.lam > 0.0 && !(w.M >= 0.0)) {  // M at lam not known yet
+        double ratio, lM = -INFINITY;
+        if (w.lam == 0.0) {
+            ratio = tree_ratio(r, j, w.u, V, w.c);
+        } else if (have_step) {  // the round's result is for this child
+            ratio = step.ratio;
+            lM = step.lM;
+            have_step = false;
+        } else {  // the residual at lam not formed yet
             if (can_pend) {
                 w.next = j;
                 w.status = kWalkPending;
@@ -1084,16 +1130,18 @@ __device__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, int L, int V, cons
             w.next = L;
             continue;
         }
-        const double ratio = tree_ratio(r, j, w.u, V, w.c, w.lam, w.M);
         const double uj = sanitize_u(uni[j], w.flags);
         if (uj < ratio) {  // accepted: one level down
             w.path[w.depth++] = j + 1;
             w.u = j + 1;
             w.lam = 0.0;
-            w.M = 1.0;
-        } else {  // rejected: the residual loses q_u once more
-            w.lam = w.lam + w.M;
-            w.M = -1.0;
+            w.lmu = -INFINITY;
+        } else if (w.lam == 0.0) {  // first rejection: lam_1 = lam_0 + M_0 = 1
+            w.lam = 1.0;
+            w.lmu = -INFINITY;
+        } else {  // the residual loses q_u once more: lam_{k+1} = lam_k + M_k
+            w.lam += exp2(lM);
+            w.lmu = log2_add(w.lmu, lM);
         }
         w.next = j + 1;
     }
@@ -1184,12 +1232,12 @@ __device__ void tree_sample_decide(const StatsParams& p, int b, const SeqInfo& s
         TreeWalk& w = s_walk;
         w = TreeWalk{};
         w.u = 0;
-        w.M = 1.0;
+        w.lmu = -INFINITY;
         w.c = exp2_scale(si.T);
         w.flags = si.flags | s_bad;
         DrawDesc d;
         const float* uni = p.unif + (size_t)b * (n + 1);
-        if (tree_walk_run(w, r, L, V, uni, p.can_pend != 0, &d))
+        if (tree_walk_run(w, r, L, V, uni, p.can_pend != 0, RoundStep{0.0, 0.0}, false, &d))
             tree_walk_finish(w, d, s_x, n, uni[n], p.acc, p.emitted, p.path, p.desc, p.flags, b);
         else
             tree_walk_store(w, true, r, L, n, p.walk + b, p.trows + (size_t)b * tree_rows_layout(n).stride);
@@ -1412,7 +1460,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
             d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
-            d.pad = 0.f;
+            d.mu = 0.f;
             if constexpr (DRAW) s_desc = d;  // drawn below, by this workgroup
             else p.desc[b] = d;
         }
@@ -1556,12 +1604,14 @@ __global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
 // lam0 and lam).  Each weight then carries binary32 rounding relative to P and
 // lam Q, not to their difference: measured, the normalised CDF error of these
 // weights is about 3e-8 / Z for residual mass Z = sum W / sum P.  When Z is
-// below kNearZ (the draft is almost the target) the last workgroup re-forms the
-// row pair's weights by itself in the near form (near_exact_tiles()), in which
-// the tokens the rows share cancel exactly.  That is slow (one workgroup reads
-// the pair twice) but rare: draft k is rejected with probability Z_k, so a
-// position whose residual mass is below kNearZ reaches this draw at most that
-// often.
+// below kNearZ (the draft is almost the target, or T -> 0 with both rows on one
+// top token, where every other term lies below the binary32 range) the last
+// workgroup re-forms the row pair's weights by itself in the near form
+// (near_exact_tiles()), in which the tokens the rows share cancel exactly and
+// the differences are scaled to the largest of them.  That is slow (one
+// workgroup reads the pair three times) but rare: draft k is rejected with
+// probability Z_k, so a position whose residual mass is below kNearZ reaches
+// this draw at most that often.
 constexpr int kSumP = 0, kSumQ = 1, kSumW = 2, kSumG = 3;
 #ifndef SV_NEAR_Z
 #define SV_NEAR_Z 0.01
@@ -1615,76 +1665,116 @@ __device__ __forceinline__ float far_sum_at(const FarSums& s, int q) {
     return q == kSumP ? s.p : q == kSumQ ? s.q : q == kSumW ? s.w : s.g;
 }
 
+// What plan_residual() decided besides the tile weights and the element
+// weighting: Z the total of the tile weights (at or below zero: no residual
+// mass left, -Z the target's own total), mass = sum max(0, p - lam q) in
+// binary64 (0 where it lies below that range) and lmass its log2 (kept there;
+// -inf: none), sq the draft row's sum in the weights' units (far form sum Q,
+// near form S_d in A's units), and the near form's rho and mu in binary64.
+struct ResidPlan {
+    double Z, mass, lmass, sq, rho, mu;
+};
+
 // The near form of one row pair, formed by one workgroup from the rows
-// themselves: first rho' = sum Dl / sum A over the whole pair, then each tile's
-// exact weight sum max(0, rho A - lam Dl) with rho = rho' - (lam - 1) into
-// s_w[NT] (the residual max(0, p - lam q); p - lam q = (rho A - lam Dl) /
-// (S'_t (1 + rho'))).  Returns rho (binary32, as the tile scan uses it); *Z
-// receives the sum of the tile weights and *mass the residual mass
-// sum max(0, p - lam q).  Wave w takes tiles w, w + kWaves, ...; lane l the
-// vectors l, l + 64, ... of a tile.
+// themselves (near_term()): first the shift sl = max(at, ad) over the tokens
+// whose relative logits differ (-inf when none does: p = q), then
+// S_t = sum A and rho = sum Dl / S_t over the whole pair, then each tile's
+// weight sum max(0, rho A - Dl - mu' B) into s_w[NT], the residual
+// max(0, p - lam q) at lam = 1 + mu (mu' = mu 2^(-sl c)).  Fills *ws (element
+// weighting) and *pl (ResidPlan).  Wave w
+// takes tiles w, w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
+__device__ float block_max_f_all(float v) {
+    __shared__ float sh[kWaves];
+    v = wave_max_f(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    v = sh[0];
+    for (int i = 1; i < kWaves; ++i) v = fmaxf(v, sh[i]);
+    __syncthreads();
+    return v;
+}
 template <int DT, bool ALIGNED>
-__device__ float near_exact_tiles(const void* trow, const void* drow, int V, int NT, float Mc, float c, float lam,
-                                  double* s_w, double* Z, double* mass) {
+__device__ void near_exact_tiles(const void* trow, const void* drow, int V, int NT, const DrawDesc& d, double* s_w,
+                                 WSpec* ws, ResidPlan* pl) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     constexpr int kU = kThreads / 64;
+    constexpr int kH = ALIGNED ? kU : 1;  // vectors per row in flight
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    // a tile's 16-byte vectors of both rows (absent ones -inf), all loads
-    // issued before the first use
-    auto load_tile = [&](int t, uint4 (&wt)[kU], uint4 (&wd)[kU]) {
+    const float c = d.c, m_t = d.m_t, m_d = d.m_d;
+    // calls f(zt, zd) for the elements of vectors u0 .. u0 + kH - 1 of tile t
+    // (absent elements -inf).  The element math is long: unrolled over a
+    // vector it would set the kernel's register count, so the elements are
+    // visited one 32-bit word of each row at a time (aligned rows, all loads
+    // issued before the first use) or one element at a time (element-wise loads).
+    auto visit = [&](int t, int u0, auto&& f) {
+        if constexpr (ALIGNED) {
+            uint4 wt[kH], wd[kH];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int e0 = t * kTile + (lane + 64 * u) * kVec;
-            if constexpr (ALIGNED) {
-                wt[u] = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
-                wd[u] = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
-            } else {
-                wt[u] = load_raw<DT>(trow, e0, V);
-                wd[u] = load_raw<DT>(drow, e0, V);
+            for (int h = 0; h < kH; ++h) {
+                const int e0 = t * kTile + (lane + 64 * (u0 + h)) * kVec;
+                wt[h] = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+                wd[h] = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+            }
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+#pragma unroll 1
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t a = q == 0 ? wt[h].x : q == 1 ? wt[h].y : q == 2 ? wt[h].z : wt[h].w;
+                    const uint32_t b = q == 0 ? wd[h].x : q == 1 ? wd[h].y : q == 2 ? wd[h].z : wd[h].w;
+                    if constexpr (DT == kBF16) {
+                        f(bf16_lo(a), bf16_lo(b));
+                        f(bf16_hi(a), bf16_hi(b));
+                    } else {
+                        f(__uint_as_float(a), __uint_as_float(b));
+                    }
+                }
+            }
+        } else {
+            const int e0 = t * kTile + (lane + 64 * u0) * kVec;
+#pragma unroll 1
+            for (int e = e0; e < e0 + kVec; ++e) {
+                const bool in = e < V;
+                f(in ? load_elem<DT>(trow, e) : -INFINITY, in ? load_elem<DT>(drow, e) : -INFINITY);
             }
         }
     };
+    float sl = -INFINITY;
+    for (int t = w; t < NT; t += kWaves)
+        for (int u0 = 0; u0 < kU; u0 += kH)
+            visit(t, u0, [&](float zt, float zd) {
+                const float at = near_rel(zt, m_t), ad = near_rel(zd, m_d);
+                if (at != ad) sl = fmaxf(sl, fmaxf(at, ad));
+            });
+    sl = block_max_f_all(sl);
     double X = 0.0, D = 0.0;
     for (int t = w; t < NT; t += kWaves) {
-        uint4 wt[kU], wd[kU];
-        load_tile(t, wt, wd);
         float sx = 0.f, sd = 0.f;
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            float zt[kVec], zd[kVec];
-            unpack<DT>(wt[u], zt);
-            unpack<DT>(wd[u], zd);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                const NearTerm tm = near_term(Mc, c, zt[e], zd[e]);  // absent elements: -inf, terms 0
+        for (int u0 = 0; u0 < kU; u0 += kH)
+            visit(t, u0, [&](float zt, float zd) {
+                const NearTerm tm = near_term(m_t, m_d, sl, c, zt, zd);  // absent elements: terms 0
                 sx += tm.A;
                 sd += tm.Dl;
-            }
-        }
+            });
         X += (double)wave_sum(sx);
         D += (double)wave_sum(sd);
     }
     if (lane != 0) X = D = 0.0;  // every lane of a wave holds the wave's sums
     block_sum2_all(X, D);
-    const double rho1 = D / X;
-    const float rho = (float)(rho1 - ((double)lam - 1.0));
+    const double rho = X > 0.0 ? D / X : 0.0;
+    const double sig = (double)sl * (double)c;                 // the shift, log2 units
+    const double scale = sl > -INFINITY ? exp2(sig) : 0.0;     // 2^(sl c), binary64
+    const double lmu = decode_lmu(d.mu);
+    double mu = 0.0;
+    if (lmu > -INFINITY) mu = sl > -INFINITY ? exp2(lmu - sig) : (double)FLT_MAX;
+    const float rho_f = (float)rho, mu_f = (float)fmin(mu, (double)FLT_MAX);
+    *ws = WSpec{kWResNear, c, m_t, m_d, 0.f, rho_f, sl, mu_f, 0.f, 0.f};
     double zsum = 0.0, unused = 0.0;
     for (int t = w; t < NT; t += kWaves) {
-        uint4 wt[kU], wd[kU];
-        load_tile(t, wt, wd);
         float sw = 0.f;
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            float zt[kVec], zd[kVec];
-            unpack<DT>(wt[u], zt);
-            unpack<DT>(wd[u], zd);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                const NearTerm tm = near_term(Mc, c, zt[e], zd[e]);
-                sw += fmaxf(fmaf(rho, tm.A, -lam * tm.Dl), 0.f);
-            }
-        }
+        for (int u0 = 0; u0 < kU; u0 += kH)
+            visit(t, u0, [&](float zt, float zd) { sw += near_weight(m_t, m_d, sl, c, rho_f, mu_f, zt, zd); });
         sw = wave_sum(sw);
         if (lane == 0) {
             s_w[t] = (double)sw;
@@ -1692,20 +1782,24 @@ __device__ float near_exact_tiles(const void* trow, const void* drow, int V, int
         }
     }
     block_sum2_all(zsum, unused);
-    *Z = zsum;
-    *mass = zsum / (X * (1.0 + rho1));
-    return rho;
+    const double Sd = X * (1.0 + rho * scale);  // the draft row's sum in A's units
+    pl->Z = zsum;
+    pl->sq = Sd;
+    pl->rho = rho;
+    pl->mu = (double)mu_f;
+    pl->mass = X > 0.0 ? scale * zsum / Sd : 0.0;
+    pl->lmass = (X > 0.0 && zsum > 0.0) ? sig + log2(zsum / Sd) : -INFINITY;
 }
 
 // The residual draw's set-up in the deciding workgroup, from the far-form tile
 // sums v[r][*] of tiles tid + r kThreads, for the residual max(0, p - lq q) with
-// lq = d.lamq: the tile weights into s_w[NT], the element weighting into *ws,
-// the total of the tile weights into *Z (at or below zero: no residual mass
-// left, s_w then holds the target's own tile masses, *ws weighs by the target
-// and -*Z is their total), the residual mass sum max(0, p - lq q) into *mass.
+// lq = d.lamq (near form: lam = 1 + mu from d.mu): the tile weights into
+// s_w[NT], the element weighting into *ws, the rest into *pl (with no residual
+// mass left, s_w holds the target's own tile masses and *ws weighs by the
+// target).
 template <int DT, bool ALIGNED, int TPT>
 __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& d, const void* trow, const void* drow,
-                              int V, double* s_w, WSpec* ws, double* Z, double* mass) {
+                              int V, double* s_w, WSpec* ws, ResidPlan* pl) {
     const int tid = threadIdx.x;
     double sp = 0.0, sq = 0.0;
 #pragma unroll
@@ -1731,16 +1825,12 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
     }
     block_sum2_all(zr, zp);
     *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, 0.f, neg_scaled(d.m_t, d.c), neg_scaled(d.m_d, d.c)};
-    *mass = sp > 0.0 ? zr / sp : 0.0;
-    const bool close = fabs(((double)d.m_d - (double)d.m_t) * (double)d.c) <= 32.0;
-    if (close && sq > 0.0 && zr < kNearZ * sp) {
+    *pl = ResidPlan{zr, sp > 0.0 ? zr / sp : 0.0, (sp > 0.0 && zr > 0.0) ? log2(zr / sp) : -INFINITY, sq, 0.0, 0.0};
+    if (sq > 0.0 && zr < kNearZ * sp) {
         // small residual: the near form, exactly, by this workgroup alone
-        // (both rows scaled by M = max(m_t, m_d); the maxima lie within 2^32)
-        const float M = fmaxf(d.m_t, d.m_d);
-        const float Mc = M * d.c;
         __syncthreads();
-        const float rho = near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, Mc, d.c, d.lamq, s_w, &zr, mass);
-        *ws = WSpec{kWResNear, d.c, M, 0.f, 0.f, rho, Mc, d.lamq};
+        near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, d, s_w, ws, pl);
+        zr = pl->Z;
     }
     if (!(zr > 0.0)) {
         // no residual mass left after rounding: draw from p_k
@@ -1751,11 +1841,42 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
             if (i < NT) s_w[i] = (double)v[r][kSumP];
         }
         *ws = target_spec(d);
-        *mass = 0.0;
-        zr = -zp;
+        *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0};
     }
-    *Z = zr;
     __syncthreads();
+}
+
+// The acceptance ratio (p(x) - lam q(x)) / (M q(x)) of a token with logits zt,
+// zt under the residual that plan_residual() formed (M its mass; 0 when it has
+// none), in binary64 from the plan's own terms:
+//   far form:  p - lam q = (P - Lam Q) / sum P, M = Z / sum P, q = Q / sum Q;
+//   near form: p - lam q = 2^(sl c) w / S_d, M = 2^(sl c) Z / S_d, q = B / S_d
+//              (w = rho A - Dl - mu B of near_term());
+// both give w sq / (Z q') with q' = Q or B.  q(x) = 0 < p(x) - lam q(x): +inf.
+__device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& pl, float zt, float zd) {
+    if (!(pl.Z > 0.0) || ws.mode == kWTarget) return 0.0;
+    double w, q;
+    if (ws.mode == kWResFar) {
+        const float P = far_p(ws.nmt, ws.c, zt), Q = far_p(ws.nmd, ws.c, zd);
+        w = (double)P - (double)ws.lam * (double)Q;
+        q = (double)Q;
+    } else {
+        const double c = (double)ws.c;
+        const float at = near_rel(zt, ws.mA), ad = near_rel(zd, ws.m_d);
+        const double A = exp2((double)at * c);
+        q = exp2((double)ad * c);
+        double Dl = 0.0;
+        if (at != ad) {
+            const double xs = ((double)ad - (double)at) * c;
+            const double As = exp2(((double)at - (double)ws.sl) * c);
+            Dl = fabs(xs) <= 0.25 ? As * expm1(xs * 0.6931471805599453) : exp2(((double)ad - (double)ws.sl) * c) - As;
+        }
+        w = pl.rho * A - Dl;
+        if (pl.mu != 0.0 && q > 0.0) w -= pl.mu * q;
+    }
+    if (!(w > 0.0)) return 0.0;
+    if (!(q > 0.0)) return INFINITY;
+    return w * pl.sq / (pl.Z * q);
 }
 
 // One chunk of a residual reduction of the pair (trow, drow) (drow unused when
@@ -1859,8 +1980,9 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     float v[kTPT][4];
     collect_tile_sums(v, NT, dsum);
     WSpec ws;
-    double Z, mass;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &mass);
+    ResidPlan pl;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl);
+    const double Z = pl.Z;
     if (!has_draft) ws = target_spec(d);  // weights P: the target row's own distribution
     if (Z <= 0.0 && tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
     const double t = (double)d.u * fabs(Z);
@@ -1912,6 +2034,7 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     d.m_d = gmd[u];
     d.lq = (float)log2(gSt[u] / gSd[u]);
     d.lamq = (float)gw->lam;
+    d.mu = (float)(gw->lam - 1.0);
     const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + u, V);
     const void* drow = row_ptr<DT>(p.draft, (long long)b * n + u, V);
     unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
@@ -1925,8 +2048,24 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     float v[kTPT][4];
     collect_tile_sums(v, NT, dsum);
     WSpec ws;
-    double Z, mass;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &Z, &mass);
+    ResidPlan pl;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl);
+    // the pending test: the walk's next child at u, under this residual
+    __shared__ RoundStep s_step;
+    if (tid == 0) {
+        RoundStep st{0.0, pl.lmass};
+        const int* par = p.parents + (size_t)b * n;
+        const int L0 = min(max(p.lens[b], 0), n);
+        for (int t = gw->next; t < L0; ++t)
+            if (par[t] == u) {
+                const int x = p.tokens[(size_t)b * n + t];
+                if (x >= 0 && x < V)
+                    st.ratio = resid_ratio(ws, pl, reinterpret_cast<const float*>(rows + lay.gt)[t],
+                                           reinterpret_cast<const float*>(rows + lay.gd)[t]);
+                break;
+            }
+        s_step = st;
+    }
     // the walk's rows, staged in LDS
     __shared__ float s_mt[kMaxDraft + 1], s_md[kMaxDraft], s_gt[kMaxDraft], s_gd[kMaxDraft];
     __shared__ double s_St[kMaxDraft + 1], s_Sd[kMaxDraft];
@@ -1951,10 +2090,9 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
         const WalkRows r{s_mt, s_St, s_md, s_Sd, s_gt, s_gd, s_x, s_par};
         TreeWalk& w = s_walk;
         w = *gw;
-        w.M = mass;
         DrawDesc dd;
         const float* uni = p.unif + (size_t)b * (n + 1);
-        const bool done = tree_walk_run(w, r, L, V, uni, p.can_pend != 0, &dd);
+        const bool done = tree_walk_run(w, r, L, V, uni, p.can_pend != 0, s_step, true, &dd);
         if (done) tree_walk_finish(w, dd, s_x, n, uni[n], p.acc, p.emitted, p.path, p.desc, p.flags, b);
         tree_walk_store(w, !done, r, L, n, p.walk + b, rows);
         xchg32(&p.cnt[b], 0u);
@@ -2123,22 +2261,18 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     }
     __shared__ double s_w[kMaxTiles];
     WSpec ws;
-    double Z, mass;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &Z, &mass);
+    ResidPlan pl;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &pl);
     const bool near = ws.mode == kWResNear;
-    double sp = 0.0, unused = 0.0;
-    for (int i = tid; i < NT; i += kThreads) {
-        if (tile_out) tile_out[(size_t)r * NT + i] = s_w[i];
-        sp += (double)v[i / kThreads][kSumP];
-    }
-    block_sum2_all(sp, unused);
+    if (tile_out)
+        for (int i = tid; i < NT; i += kThreads) tile_out[(size_t)r * NT + i] = s_w[i];
     for (int i = tid; i < V; i += kThreads)
         w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
     if (info_out && tid == 0) {
         info_out[(size_t)r * 4 + 0] = near ? 1.f : 0.f;
         info_out[(size_t)r * 4 + 1] = ws.mode == kWResFar ? ws.lam : 0.f;
         info_out[(size_t)r * 4 + 2] = near ? ws.rho : 0.f;
-        info_out[(size_t)r * 4 + 3] = (float)mass;
+        info_out[(size_t)r * 4 + 3] = (float)pl.mass;
     }
 }
 

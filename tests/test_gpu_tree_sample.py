@@ -171,6 +171,12 @@ def test_star_tree_many_rounds(oracle, max_rounds):
         assert fl & sv.SV_FLAG_TREE_TRUNCATED
 
 
+@pytest.mark.parametrize("T", [1e-3, 100.0])
+def test_extreme_temperatures(oracle, T):
+    d = synth.make_tree_sample(450, device=DEV, B=32, n=12, V=3001, shape="random", temps=(T,))
+    _compare(oracle, d, _rounds(d), tag=f"T={T}")
+
+
 def test_masked_vocabulary(oracle):
     """Rows with -inf entries (a masked vocabulary): target and draft rows mask
     different random subsets, so drafted tokens can have p = 0 (never accepted)
