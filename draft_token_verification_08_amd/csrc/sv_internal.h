@@ -37,8 +37,12 @@ enum Mode : int { kSample = 0, kGreedy = 1 };
 
 // kinds of the final draw of a sequence: a bonus draw from target row L's tile
 // partials, a residual draw max(0, p_k - lamq q_k) from row pair k, or a draw
-// from the whole of target row k alone (the bonus token at a tree's leaf)
-enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2, kDrawTarget = 3 };
+// from the whole of target row k alone (the bonus token at a tree's leaf).
+// kDrawResidualNear is a residual draw whose mass may be small (below the near
+// form's threshold): its chunks hand over the near form's tile sums instead of
+// the far form's.
+enum DrawKind : int { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2, kDrawTarget = 3, kDrawResidualNear = 4 };
+__host__ __device__ inline bool is_residual_draw(int kind) { return kind == kDrawResidual || kind == kDrawResidualNear; }
 
 // One 64-bit slot per (sequence, row slot, vocab chunk), exchanged atomically:
 //   sampling rows: low word chunk max m_c, high word sum over the chunk of 2^((z - m_c) c)
@@ -59,10 +63,11 @@ struct DrawDesc {
     float m_d;      // max of draft row k (residual only)
     float lq;       // log2(S_t / S_d), S = sum 2^((z - m) c) of target / draft row k (residual only)
     float u;        // the (sanitised) final uniform u[b][n]
-    float lamq;     // residual weights max(0, p - lamq q): 1 after one rejection (tree walks: more)
-    float mu;       // lam - 1 of a residual draw for the near form (0 after one rejection):
-                    // the value itself when at least 2^-126, else log2(lam - 1) (< -126)
+    double mu;      // residual draws: the weights are max(0, p - lam q) with lam = 1 + mu (mu = 0
+                    // after one rejection; tree walks: more), mu itself when at least 2^-1000,
+                    // else log2(mu) (< -1000)
 };
+static_assert(sizeof(DrawDesc) == 40, "the workspace layout sizes DrawDesc at 40 bytes");
 
 // A sampling tree walk (per sequence), kept in the workspace between the
 // statistics pass, the rounds and the draw pass.
@@ -72,9 +77,8 @@ struct TreeWalk {
     int u;          // current node
     int next;       // the next child to test is the first node j + 1 with j >= next below u
     int depth;      // nodes on the kept path so far
-    double lam;     // lam_k at node u (0: no child rejected yet)
-    double lmu;     // log2(lam_k - 1) once lam_k >= 1 (-inf: lam_k = 1), kept where lam_k - 1
-                    // lies below binary64's resolution at 1
+    double zb;      // a lower bound of sum max(0, p_u - lam_k q_u) (< 0: no child rejected yet)
+    double lmu;     // log2(lam_k - 1) once a child is rejected (-inf: lam_k = 1)
     uint32_t flags;
     float c;        // log2(e) / T
     int path[kMaxDraft];

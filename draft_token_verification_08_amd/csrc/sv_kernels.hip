@@ -55,8 +55,13 @@
 #ifndef SV_DRAW_WPE
 #define SV_DRAW_WPE 5   // waves per SIMD the draw pass's registers are sized for
 #endif
+#ifndef SV_NEAR_Z
+#define SV_NEAR_Z 0.01  // residual mass below which a draw takes the near form
+#endif
 
 namespace sv {
+
+constexpr double kNearZ = SV_NEAR_Z;
 
 // --------------------------------------------------------------- element access
 
@@ -656,10 +661,11 @@ __device__ __forceinline__ float exp2m1_small(float x) {
 // (at = ad, masked in both rows included) has Dl = 0 exactly and no power of
 // the shift is formed for it (only tokens with at != ad lie at or below sl).
 // With S_t = sum A, S_d = sum B, rho = (S_d - S_t) 2^(-sl c) / S_t = sum Dl / S_t
-// and lam = 1 + mu:
-//   p - lam q = A / S_t - lam B / S_d = 2^(sl c) (rho A - Dl - mu' B) / S_d,
-// mu' = mu 2^(-sl c), so max(0, rho A - Dl - mu' B) are residual weights up to
-// one common factor; the tokens the rows share never enter a difference.
+// and lam = 1 + mu (B = A + 2^(sl c) Dl):
+//   p - lam q = A / S_t - lam B / S_d = 2^(sl c) (kappa A - lam Dl) / S_d,
+// kappa = rho - mu 2^(-sl c) (formed in binary64), so max(0, kappa A - lam Dl)
+// are residual weights up to one common factor; the tokens the rows share never
+// enter a difference, and their weight kappa A carries one rounding.
 struct NearTerm {
     float A, Dl;
 };
@@ -674,15 +680,10 @@ __device__ __forceinline__ NearTerm near_term(float m_t, float m_d, float sl, fl
     return NearTerm{A, Dl};
 }
 // The residual weight of one token in the near form (see near_term()).
-__device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, float c, float rho, float mu, float zt,
+__device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, float c, float kappa, float lam, float zt,
                                             float zd) {
     const NearTerm t = near_term(m_t, m_d, sl, c, zt, zd);
-    float w = fmaf(rho, t.A, -t.Dl);
-    if (mu != 0.f) {
-        const float B = exp2_fast(near_rel(zd, m_d) * c);
-        if (B > 0.f) w = fmaf(-mu, B, w);
-    }
-    return fmaxf(w, 0.f);
+    return fmaxf(fmaf(kappa, t.A, -lam * t.Dl), 0.f);
 }
 
 // How a draw weighs one element (all weights up to a factor common to the row):
@@ -691,20 +692,18 @@ __device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, flo
 //   kWResFar:   max(0, P - lam Q) with P = 2^(z_t c - fl(m_t c)), Q = 2^(z_d c -
 //               fl(m_d c)) (one rounding each: far_p()), each row scaled by its own
 //               maximum (mA = m_t) and lam the ratio of their sums (S_t / S_d);
-//   kWResNear:  near_weight(): max(0, rho A - Dl - mu B) of near_term(), each
+//   kWResNear:  near_weight(): max(0, kappa A - lam Dl) of near_term(), each
 //               row relative to its own maximum (mA = m_t), differences in
-//               units of 2^(sl c): the residual max(0, p - lam q) with
-//               lam = 1 + mu 2^(sl c) (mu = 0 after one rejection).
+//               units of 2^(sl c): the residual max(0, p - lam q).
 enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
 struct WSpec {
     int mode;
     float c;    // log2(e) / T
     float mA;   // maximum the target row is scaled by
     float m_d;  // kWResFar: the draft row's maximum
-    float lam;  // kWResFar
-    float rho;  // kWResNear
-    float sl;   // kWResNear: the shift of the differences (<= 0)
-    float mu;   // kWResNear: (lam - 1) 2^(-sl c)
+    float lam;    // kWResFar: lam S_t / S_d; kWResNear: lam
+    float kappa;  // kWResNear
+    float sl;     // kWResNear: the shift of the differences (<= 0)
     float nmt;  // kWResFar: neg_scaled(mA, c)
     float nmd;  // kWResFar: neg_scaled(m_d, c)
 };
@@ -723,10 +722,10 @@ __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd)
         const float Q = far_p(s.nmd, s.c, zd);
         return fmaxf(fmaf(-s.lam, Q, P), 0.f);
     }
-    return near_weight(s.mA, s.m_d, s.sl, s.c, s.rho, s.mu, zt, zd);
+    return near_weight(s.mA, s.m_d, s.sl, s.c, s.kappa, s.lam, zt, zd);
 }
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
-    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 }
 
 // Scan one tile: returns the element whose running weight (starting at P)
@@ -1066,14 +1065,31 @@ __device__ __forceinline__ double log2_add(double a, double b) {
     const double hi = fmax(a, b), lo = fmin(a, b);
     return hi + log2(1.0 + exp2(lo - hi));
 }
-// DrawDesc::mu from log2(lam - 1), and back (see DrawDesc)
-__device__ __forceinline__ float encode_mu(double lmu) {
-    if (lmu == -INFINITY) return 0.f;
-    return lmu >= -126.0 ? (float)exp2(lmu) : (float)lmu;
+// DrawDesc::mu from log2(lam - 1), and back: log2 mu, and mu (0 below binary64)
+__device__ __forceinline__ double encode_mu(double lmu) {
+    if (lmu == -INFINITY) return 0.0;
+    return lmu >= -1000.0 ? exp2(lmu) : lmu;
 }
-__device__ __forceinline__ double decode_lmu(float mu) {
-    if (mu == 0.f) return -INFINITY;
-    return mu > 0.f ? log2((double)mu) : (double)mu;
+__device__ __forceinline__ double desc_lmu(const DrawDesc& d) {
+    if (d.mu == 0.0) return -INFINITY;
+    return d.mu > 0.0 ? log2(d.mu) : d.mu;
+}
+__device__ __forceinline__ double desc_mu(const DrawDesc& d) { return d.mu > 0.0 ? d.mu : 0.0; }
+
+// A lower bound of the residual mass sum max(0, p - q) after a rejection of x:
+// q(x) - p(x), and from the rows' sums (S = sum 2^((z - m) c), so each row's top
+// token has probability 1 / S) |1 / S_t - 1 / S_d| (the target's top token gives
+// p - q >= 1 / S_t - 1 / S_d, the draft's q - p >= 1 / S_d - 1 / S_t, and the
+// mass is both sum max(0, p - q) and sum max(0, q - p)).  A draw whose bound is
+// below the near form's threshold hands over the near form's sums
+// (kDrawResidualNear).  After a later rejection at a tree node (lam_{k+1} =
+// lam_k + M_k) the mass is M_k times that of max(0, r_k - q) with r_k the
+// residual the child was tested against, so M_k (q(x) - r_k(x)) bounds it, and
+// so does M_k (q(y) - r_k(y)) at the draft's top token y, where q(y) = 1 / S_d and
+// M_k r_k(y) = max(0, p(y) - lam_k / S_d) <= max(0, 1 / S_t - lam_k / S_d); the
+// target's top token gives 1 / S_t - lam_{k+1} / S_d.
+__device__ __forceinline__ double resid_mass_bound(double St, double Sd, double gap) {
+    return fmax(gap, fabs(1.0 / St - 1.0 / Sd));
 }
 
 // Runs the walk from its state (one thread).  Returns true when it has
@@ -1099,22 +1115,20 @@ __device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, in
             d->slot = w.depth;
             d->c = w.c;
             d->m_t = r.mt[u];
-            if (w.lam == 0.0) {
+            if (w.zb < 0.0) {
                 d->kind = kDrawTarget;
                 d->m_d = r.mt[u];
-                d->lamq = 0.f;
             } else {
-                d->kind = kDrawResidual;
+                d->kind = w.zb < kNearZ ? kDrawResidualNear : kDrawResidual;
                 d->m_d = r.md[u];
                 d->lq = (float)log2(r.St[u] / r.Sd[u]);
-                d->lamq = (float)w.lam;
                 d->mu = encode_mu(w.lmu);
             }
             w.status = kWalkIdle;
             return true;
         }
         double ratio, lM = -INFINITY;
-        if (w.lam == 0.0) {
+        if (w.zb < 0.0) {
             ratio = tree_ratio(r, j, w.u, V, w.c);
         } else if (have_step) {  // the round's result is for this child
             ratio = step.ratio;
@@ -1134,14 +1148,23 @@ __device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, in
         if (uj < ratio) {  // accepted: one level down
             w.path[w.depth++] = j + 1;
             w.u = j + 1;
-            w.lam = 0.0;
+            w.zb = -1.0;
             w.lmu = -INFINITY;
-        } else if (w.lam == 0.0) {  // first rejection: lam_1 = lam_0 + M_0 = 1
-            w.lam = 1.0;
-            w.lmu = -INFINITY;
-        } else {  // the residual loses q_u once more: lam_{k+1} = lam_k + M_k
-            w.lam += exp2(lM);
-            w.lmu = log2_add(w.lmu, lM);
+        } else {
+            // q_u(x) (1 - the ratio x was tested at): the rejected child's share of
+            // the next residual mass (resid_mass_bound())
+            const int x = r.x[j];
+            double gap = 0.0;
+            if (x >= 0 && x < V && r.gd[j] > -INFINITY)
+                gap = exp2(((double)r.gd[j] - (double)r.md[w.u]) * (double)w.c) / r.Sd[w.u] * (1.0 - fmin(ratio, 1.0));
+            if (w.zb < 0.0) {  // first rejection: lam_1 = lam_0 + M_0 = 1
+                w.zb = resid_mass_bound(r.St[w.u], r.Sd[w.u], gap);
+                w.lmu = -INFINITY;
+            } else {  // the residual loses q_u once more: lam_{k+1} = lam_k + M_k
+                const double St = r.St[w.u], Sd = r.Sd[w.u], Mk = exp2(lM), lam = 1.0 + exp2(w.lmu);
+                w.zb = fmax(Mk * gap, fmax(Mk / Sd - fmax(0.0, 1.0 / St - lam / Sd), 1.0 / St - (lam + Mk) / Sd));
+                w.lmu = log2_add(w.lmu, lM);
+            }
         }
         w.next = j + 1;
     }
@@ -1232,6 +1255,7 @@ __device__ void tree_sample_decide(const StatsParams& p, int b, const SeqInfo& s
         TreeWalk& w = s_walk;
         w = TreeWalk{};
         w.u = 0;
+        w.zb = -1.0;
         w.lmu = -INFINITY;
         w.c = exp2_scale(si.T);
         w.flags = si.flags | s_bad;
@@ -1363,9 +1387,11 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
     //    rejection k (slots past k are evaluated but unused)
     __shared__ int s_k;
     __shared__ uint32_t s_flags;
+    __shared__ double s_gap;
     if (tid < 64) {
         const int j = tid;
         bool rej = false, oor = false, badu = false;
+        double gap = 0.0;  // q(x) - p(x), a lower bound of the residual mass after rejecting x
         int x = 0;
         if constexpr (!DRAW) x = j < L ? p.tokens[(size_t)b * n + j] : 0;
         if (j < L) {
@@ -1391,6 +1417,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
                     const double lr = ((double)zt - (double)s_m[j]) * cd - ((double)zd - (double)s_m[jd]) * cd;
                     ratio = exp2(lr) * (s_S[jd] / s_S[j]);
                 }
+                if (!qz) gap = exp2(((double)zd - (double)s_m[jd]) * cd) / s_S[jd] * (1.0 - fmin(ratio, 1.0));
                 rej = !(u < ratio);
             }
         }
@@ -1414,6 +1441,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
                 if (k == n && si.greedy && j == 0) t[n] = yk;
             }
         }
+        if (j == k) s_gap = gap;
         if (tid == 0) {
             uint32_t f = si.flags;
             if (omask & upto) f |= SV_FLAG_TOKEN_OOR;
@@ -1451,16 +1479,18 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             // is done by the draw pass
             if constexpr (DRAW) e[k] = -1;
             DrawDesc d;
-            d.kind = (k < L) ? kDrawResidual : kDrawBonus;
+            // a rejection whose residual mass may lie below the near form's
+            // threshold (resid_mass_bound()) hands the draw the near form's sums
+            const double zb = (k < L) ? resid_mass_bound(s_S[k], s_S[n + 1 + k], s_gap) : 0.0;
+            d.kind = (k < L) ? (zb < kNearZ ? kDrawResidualNear : kDrawResidual) : kDrawBonus;
             d.k = k;
             d.slot = k;
-            d.lamq = 1.f;
             d.c = cf;
             d.m_t = s_m[k];
             d.m_d = (k < L) ? s_m[n + 1 + k] : 0.f;
             d.lq = (k < L) ? (float)log2(s_S[k] / s_S[n + 1 + k]) : 0.f;
             d.u = (float)u;
-            d.mu = 0.f;
+            d.mu = 0.0;
             if constexpr (DRAW) s_desc = d;  // drawn below, by this workgroup
             else p.desc[b] = d;
         }
@@ -1613,10 +1643,6 @@ __global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
 // probability Z_k, so a position whose residual mass is below kNearZ reaches
 // this draw at most that often.
 constexpr int kSumP = 0, kSumQ = 1, kSumW = 2, kSumG = 3;
-#ifndef SV_NEAR_Z
-#define SV_NEAR_Z 0.01
-#endif
-constexpr double kNearZ = SV_NEAR_Z;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
@@ -1665,23 +1691,59 @@ __device__ __forceinline__ float far_sum_at(const FarSums& s, int q) {
     return q == kSumP ? s.p : q == kSumQ ? s.q : q == kSumW ? s.w : s.g;
 }
 
+// The near form handed over by a draw's chunks (kDrawResidualNear): its weights
+// max(0, kappa A - lam Dl) (near_term() with no shift) are linear in kappa
+// between the tokens' crossing points, so the chunks hand over, per tile, sum A,
+// sum Dl, and at the estimate kappa0 = rho0 - mu (rho0 = S_d / S_t - 1 from the
+// statistics pass, one binary32 rounding of lq) the weight sum W and its slope
+// G = sum A over the tokens with a positive weight; the deciding workgroup forms
+// kappa = sum Dl / sum A - mu and each tile's weight W + (kappa - kappa0) G.
+// That is exact unless a token's crossing point lies between kappa0 and kappa;
+// the tokens the rows share all cross at kappa = 0, which the plan keeps apart.
+constexpr int kSumA = 0, kSumDl = 1;  // near form: the slots of sum P and sum Q
+struct NearLin {
+    float kappa0, lam;
+};
+__device__ __forceinline__ NearLin near_lin(const DrawDesc& d) {
+    const double rho0 = fabs((double)d.lq) <= 0.25 ? (double)exp2m1_small(-d.lq) : exp2(-(double)d.lq) - 1.0;
+    const double mu = desc_mu(d);
+    return NearLin{(float)(rho0 - mu), (float)(1.0 + mu)};
+}
+__device__ __forceinline__ void near_accum(FarSums& s, const DrawDesc& d, const NearLin& nl, float zt, float zd) {
+    // near_term() with no shift (the powers of (a - 0) c are those of a c)
+    const float at = near_rel(zt, d.m_t), ad = near_rel(zd, d.m_d);
+    const float A = exp2_fast(at * d.c);
+    float Dl = 0.f;
+    if (at != ad) {
+        const float x = (ad - at) * d.c;
+        Dl = fabsf(x) <= 0.25f ? A * exp2m1_small(x) : exp2_fast(ad * d.c) - A;
+    }
+    const float w0 = fmaf(nl.kappa0, A, -nl.lam * Dl);
+    s.p += A;
+    s.q += Dl;
+    s.w += fmaxf(w0, 0.f);
+    s.g += w0 > 0.f ? A : 0.f;
+}
+
 // What plan_residual() decided besides the tile weights and the element
 // weighting: Z the total of the tile weights (at or below zero: no residual
 // mass left, -Z the target's own total), mass = sum max(0, p - lam q) in
 // binary64 (0 where it lies below that range) and lmass its log2 (kept there;
 // -inf: none), sq the draft row's sum in the weights' units (far form sum Q,
-// near form S_d in A's units), and the near form's rho and mu in binary64.
+// near form S_d in A's units), and the near form's kappa and lam in binary64.
 struct ResidPlan {
-    double Z, mass, lmass, sq, rho, mu;
+    double Z, mass, lmass, sq, kappa, lam;
+    double sh;   // near form: 2^(-sl c), the unit of its differences (binary64; may be +inf)
+    bool exact;  // the near form by the deciding workgroup alone (near_exact_tiles())
 };
 
 // The near form of one row pair, formed by one workgroup from the rows
 // themselves (near_term()): first the shift sl = max(at, ad) over the tokens
 // whose relative logits differ (-inf when none does: p = q), then
 // S_t = sum A and rho = sum Dl / S_t over the whole pair, then each tile's
-// weight sum max(0, rho A - Dl - mu' B) into s_w[NT], the residual
-// max(0, p - lam q) at lam = 1 + mu (mu' = mu 2^(-sl c)).  Fills *ws (element
-// weighting) and *pl (ResidPlan).  Wave w
+// weight sum max(0, kappa A - lam Dl) into s_w[NT], the residual
+// max(0, p - lam q) at lam = 1 + mu (kappa = rho - mu 2^(-sl c)).  Fills *ws
+// (element weighting) and *pl (ResidPlan).  Wave w
 // takes tiles w, w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
 __device__ float block_max_f_all(float v) {
     __shared__ float sh[kWaves];
@@ -1765,16 +1827,17 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
     const double rho = X > 0.0 ? D / X : 0.0;
     const double sig = (double)sl * (double)c;                 // the shift, log2 units
     const double scale = sl > -INFINITY ? exp2(sig) : 0.0;     // 2^(sl c), binary64
-    const double lmu = decode_lmu(d.mu);
-    double mu = 0.0;
-    if (lmu > -INFINITY) mu = sl > -INFINITY ? exp2(lmu - sig) : (double)FLT_MAX;
-    const float rho_f = (float)rho, mu_f = (float)fmin(mu, (double)FLT_MAX);
-    *ws = WSpec{kWResNear, c, m_t, m_d, 0.f, rho_f, sl, mu_f, 0.f, 0.f};
+    const double lmu = desc_lmu(d);
+    double mus = 0.0;  // mu 2^(-sl c)
+    if (lmu > -INFINITY) mus = sl > -INFINITY ? exp2(lmu - sig) : (double)FLT_MAX;
+    const double kappa = rho - mus, lam = 1.0 + desc_mu(d);
+    const float kappa_f = (float)fmax(kappa, -(double)FLT_MAX), lam_f = (float)lam;
+    *ws = WSpec{kWResNear, c, m_t, m_d, lam_f, kappa_f, sl, 0.f, 0.f};
     double zsum = 0.0, unused = 0.0;
     for (int t = w; t < NT; t += kWaves) {
         float sw = 0.f;
         for (int u0 = 0; u0 < kU; u0 += kH)
-            visit(t, u0, [&](float zt, float zd) { sw += near_weight(m_t, m_d, sl, c, rho_f, mu_f, zt, zd); });
+            visit(t, u0, [&](float zt, float zd) { sw += near_weight(m_t, m_d, sl, c, kappa_f, lam_f, zt, zd); });
         sw = wave_sum(sw);
         if (lane == 0) {
             s_w[t] = (double)sw;
@@ -1785,8 +1848,10 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
     const double Sd = X * (1.0 + rho * scale);  // the draft row's sum in A's units
     pl->Z = zsum;
     pl->sq = Sd;
-    pl->rho = rho;
-    pl->mu = (double)mu_f;
+    pl->kappa = kappa;
+    pl->lam = lam;
+    pl->sh = sl > -INFINITY ? exp2(-sig) : 1.0;
+    pl->exact = true;
     pl->mass = X > 0.0 ? scale * zsum / Sd : 0.0;
     pl->lmass = (X > 0.0 && zsum > 0.0) ? sig + log2(zsum / Sd) : -INFINITY;
 }
@@ -1801,33 +1866,66 @@ template <int DT, bool ALIGNED, int TPT>
 __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& d, const void* trow, const void* drow,
                               int V, double* s_w, WSpec* ws, ResidPlan* pl) {
     const int tid = threadIdx.x;
-    double sp = 0.0, sq = 0.0;
+    const double lq = 1.0 + desc_mu(d);  // lam
+    double sp = 0.0, sq = 0.0;           // far form: sum P, sum Q; near form: sum A, sum Dl
 #pragma unroll
     for (int r = 0; r < TPT; ++r) {
         sp += (double)v[r][kSumP];
         sq += (double)v[r][kSumQ];
     }
     block_sum2_all(sp, sq);
-    const double lq = (double)d.lamq;
-    const double Lam = sq > 0.0 ? lq * (sp / sq) : 0.0;  // lq S_t / S_d from the same terms
-    const double Lam0 = lq * exp2((double)d.lq);
     double zr = 0.0, zp = 0.0;
+    bool exact = false;  // the near form by this workgroup alone
+    if (d.kind == kDrawResidualNear) {
+        // the chunks' near-form sums (near_lin()): kappa = sum Dl / sum A - mu
+        const NearLin nl = near_lin(d);
+        const double kappa = sp > 0.0 ? sq / sp - desc_mu(d) : 0.0;
+        const double dk = kappa - (double)nl.kappa0;
 #pragma unroll
-    for (int r = 0; r < TPT; ++r) {
-        const int i = tid + r * kThreads;
-        if (i < NT) {
-            double w = (double)v[r][kSumW] - (Lam - Lam0) * (double)v[r][kSumG];
-            w = w > 0.0 ? w : 0.0;
-            s_w[i] = w;
-            zr += w;
-            zp += (double)v[r][kSumP];
+        for (int r = 0; r < TPT; ++r) {
+            const int i = tid + r * kThreads;
+            if (i < NT) {
+                double w = (double)v[r][kSumW] + dk * (double)v[r][kSumG];
+                w = w > 0.0 ? w : 0.0;
+                s_w[i] = w;
+                zr += w;
+                zp += (double)v[r][kSumA];
+            }
         }
+        block_sum2_all(zr, zp);
+        // trusted when the tokens the rows share (crossing at kappa = 0) lie on
+        // one side of both kappa0 and kappa with room to spare, and the mass is
+        // far above what binary32 terms without a shift can carry
+        const bool ok = sp > 0.0 && kappa * (double)nl.kappa0 > 0.0 && fabs(kappa) > 4.0 * fabs(dk) &&
+                        zr > 0x1p-60 * sp;
+        if (ok) {
+            *ws = WSpec{kWResNear, d.c, d.m_t, d.m_d, nl.lam, (float)kappa, 0.f, 0.f, 0.f};
+            const double Sd = sp + sq;  // S_d = sum B = sum A + sum Dl
+            *pl = ResidPlan{zr, zr / Sd, log2(zr / Sd), Sd, kappa, (double)nl.lam, 1.0, false};
+        } else {
+            exact = true;
+        }
+    } else {
+        const double Lam = sq > 0.0 ? lq * (sp / sq) : 0.0;  // lam S_t / S_d from the same terms
+        const double Lam0 = lq * exp2((double)d.lq);
+#pragma unroll
+        for (int r = 0; r < TPT; ++r) {
+            const int i = tid + r * kThreads;
+            if (i < NT) {
+                double w = (double)v[r][kSumW] - (Lam - Lam0) * (double)v[r][kSumG];
+                w = w > 0.0 ? w : 0.0;
+                s_w[i] = w;
+                zr += w;
+                zp += (double)v[r][kSumP];
+            }
+        }
+        block_sum2_all(zr, zp);
+        *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, neg_scaled(d.m_t, d.c), neg_scaled(d.m_d, d.c)};
+        *pl = ResidPlan{zr, sp > 0.0 ? zr / sp : 0.0, (sp > 0.0 && zr > 0.0) ? log2(zr / sp) : -INFINITY, sq, 0.0, 0.0,
+                        1.0, false};
+        exact = sq > 0.0 && zr < kNearZ * sp;  // a small residual after all
     }
-    block_sum2_all(zr, zp);
-    *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, 0.f, neg_scaled(d.m_t, d.c), neg_scaled(d.m_d, d.c)};
-    *pl = ResidPlan{zr, sp > 0.0 ? zr / sp : 0.0, (sp > 0.0 && zr > 0.0) ? log2(zr / sp) : -INFINITY, sq, 0.0, 0.0};
-    if (sq > 0.0 && zr < kNearZ * sp) {
-        // small residual: the near form, exactly, by this workgroup alone
+    if (exact) {
         __syncthreads();
         near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, d, s_w, ws, pl);
         zr = pl->Z;
@@ -1841,17 +1939,17 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
             if (i < NT) s_w[i] = (double)v[r][kSumP];
         }
         *ws = target_spec(d);
-        *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0};
+        *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0, 1.0, false};
     }
     __syncthreads();
 }
 
 // The acceptance ratio (p(x) - lam q(x)) / (M q(x)) of a token with logits zt,
-// zt under the residual that plan_residual() formed (M its mass; 0 when it has
+// zd under the residual that plan_residual() formed (M its mass; 0 when it has
 // none), in binary64 from the plan's own terms:
 //   far form:  p - lam q = (P - Lam Q) / sum P, M = Z / sum P, q = Q / sum Q;
 //   near form: p - lam q = 2^(sl c) w / S_d, M = 2^(sl c) Z / S_d, q = B / S_d
-//              (w = rho A - Dl - mu B of near_term());
+//              (w = kappa A - lam Dl of near_term());
 // both give w sq / (Z q') with q' = Q or B.  q(x) = 0 < p(x) - lam q(x): +inf.
 __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& pl, float zt, float zd) {
     if (!(pl.Z > 0.0) || ws.mode == kWTarget) return 0.0;
@@ -1861,18 +1959,21 @@ __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& 
         w = (double)P - (double)ws.lam * (double)Q;
         q = (double)Q;
     } else {
-        const double c = (double)ws.c;
+        // w / B with r = A / B = 2^((at - ad) c): w / B = kappa r - lam (1 - r) 2^(-sl c)
+        // (a token the rows share has r = 1 and no second term)
         const float at = near_rel(zt, ws.mA), ad = near_rel(zd, ws.m_d);
-        const double A = exp2((double)at * c);
-        q = exp2((double)ad * c);
-        double Dl = 0.0;
+        if (ad == -INFINITY) return at == -INFINITY ? 0.0 : INFINITY;  // q(x) = 0
+        if (at == -INFINITY) return 0.0;                                  // p(x) = 0 < q(x)
+        double wb = pl.kappa;
         if (at != ad) {
-            const double xs = ((double)ad - (double)at) * c;
-            const double As = exp2(((double)at - (double)ws.sl) * c);
-            Dl = fabs(xs) <= 0.25 ? As * expm1(xs * 0.6931471805599453) : exp2(((double)ad - (double)ws.sl) * c) - As;
+            // 1 - r in binary64 keeps about 16 - log10(1 / |xr|) digits, and two
+            // distinct binary32 relative logits give |xr| far above 1e-8
+            const double xr = ((double)at - (double)ad) * (double)ws.c;
+            const double r = exp2(xr), sh = pl.sh;  // sh = 2^(-sl c) >= 1
+            if (!(r < INFINITY)) return pl.kappa + pl.lam * sh > 0.0 ? INFINITY : 0.0;  // w / B = r (kappa + lam sh) - lam sh
+            wb = pl.kappa * r - pl.lam * (1.0 - r) * sh;
         }
-        w = pl.rho * A - Dl;
-        if (pl.mu != 0.0 && q > 0.0) w -= pl.mu * q;
+        return wb > 0.0 ? wb * pl.sq / pl.Z : 0.0;
     }
     if (!(w > 0.0)) return 0.0;
     if (!(q > 0.0)) return INFINITY;
@@ -1893,42 +1994,80 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
     constexpr int kTilesPerWave = kDrawTiles / kWaves;
     constexpr int kU = kThreads / 64;  // vectors per lane per tile
     static_assert(kDrawTiles % kWaves == 0, "draw chunk must split evenly over the waves");
-    const float lam0 = d.lamq * exp2_fast(d.lq);
+    const float lam0 = (float)(1.0 + desc_mu(d)) * exp2_fast(d.lq);
     const float nmt = neg_scaled(d.m_t, d.c), nmd = neg_scaled(d.m_d, d.c);
     const int tile0 = c * kDrawTiles;
     const int cnt = min(kDrawTiles, NT - tile0);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    // raw 16-byte vectors (bf16 pairs or fp32), widened where they are used
-    uint4 rt[kTilesPerWave][kU], rd[kTilesPerWave][kU];
-#pragma unroll
-    for (int i = 0; i < kTilesPerWave; ++i)
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int e0 = (tile0 + wv * kTilesPerWave + i) * kTile + (lane + 64 * u) * kVec;
-            const bool ok = wv * kTilesPerWave + i < cnt && e0 < V;
-            if constexpr (ALIGNED) {
-                rt[i][u] = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
-                rd[i][u] = (ok && has_draft) ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
-            } else {
-                rt[i][u] = load_raw<DT>(trow, e0, ok ? V : 0);
-                rd[i][u] = load_raw<DT>(drow, e0, (ok && has_draft) ? V : 0);
-            }
+    // vector u of tile i of this wave (raw 16-byte vectors: bf16 pairs or fp32)
+    auto load = [&](int i, int u, uint4& vt, uint4& vd) {
+        const int e0 = (tile0 + wv * kTilesPerWave + i) * kTile + (lane + 64 * u) * kVec;
+        const bool ok = wv * kTilesPerWave + i < cnt && e0 < V;
+        if constexpr (ALIGNED) {
+            vt = ok ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+            vd = (ok && has_draft) ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+        } else {
+            vt = load_raw<DT>(trow, e0, ok ? V : 0);
+            vd = load_raw<DT>(drow, e0, (ok && has_draft) ? V : 0);
         }
+    };
     unsigned dep = 0u;
-#pragma unroll
-    for (int i = 0; i < kTilesPerWave; ++i) {
-        FarSums fs{0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            float zt[kVec], zd[kVec];
-            unpack<DT>(rt[i][u], zt);
-            unpack<DT>(rd[i][u], zd);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) far_accum(fs, nmt, nmd, d.c, lam0, zt[e], zd[e]);
-        }
+    auto hand_over = [&](int i, FarSums fs) {
         fs = wave_far_sums(fs);
         const int t = wv * kTilesPerWave + i;
         if (lane < 4 && t < cnt) dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(far_sum_at(fs, lane)));
+    };
+    if (d.kind == kDrawResidualNear) {
+        // the near form's sums (near_lin()), every vector of the chunk in flight
+        // before the first use; the element math is long, so four elements of
+        // each row at a time (unrolled over a whole vector it spills)
+        const NearLin nl = near_lin(d);
+        uint4 rt[kTilesPerWave][kU], rd[kTilesPerWave][kU];
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i)
+#pragma unroll
+            for (int u = 0; u < kU; ++u) load(i, u, rt[i][u], rd[i][u]);
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            FarSums fs{0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+#pragma unroll 4
+                for (int e = 0; e < kVec; ++e) {
+                    const int q = DT == kBF16 ? e >> 1 : e;
+                    const uint4 vt = rt[i][u], vd = rd[i][u];
+                    const uint32_t a = q == 0 ? vt.x : q == 1 ? vt.y : q == 2 ? vt.z : vt.w;
+                    const uint32_t bb = q == 0 ? vd.x : q == 1 ? vd.y : q == 2 ? vd.z : vd.w;
+                    if constexpr (DT == kBF16) {
+                        const bool hi = e & 1;
+                        near_accum(fs, d, nl, hi ? bf16_hi(a) : bf16_lo(a), hi ? bf16_hi(bb) : bf16_lo(bb));
+                    } else {
+                        near_accum(fs, d, nl, __uint_as_float(a), __uint_as_float(bb));
+                    }
+                }
+            }
+            hand_over(i, fs);
+        }
+    } else {
+        // the far form's sums, every vector of the chunk in flight before the first use
+        uint4 rt[kTilesPerWave][kU], rd[kTilesPerWave][kU];
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i)
+#pragma unroll
+            for (int u = 0; u < kU; ++u) load(i, u, rt[i][u], rd[i][u]);
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            FarSums fs{0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                float zt[kVec], zd[kVec];
+                unpack<DT>(rt[i][u], zt);
+                unpack<DT>(rd[i][u], zd);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) far_accum(fs, nmt, nmd, d.c, lam0, zt[e], zd[e]);
+            }
+            hand_over(i, fs);
+        }
     }
     // this wave's exchanges have been performed before the workgroup arrives
     asm volatile("" ::"v"(dep));
@@ -1966,7 +2105,7 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
         return;
     }
     // kDrawTarget: the whole of target row k alone (no draft row: Q = 0, W = P)
-    const bool has_draft = d.kind == kDrawResidual;
+    const bool has_draft = is_residual_draw(d.kind);
     const void* drow = has_draft ? row_ptr<DT>(p.draft, (long long)b * n + d.k, V) : nullptr;
     unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
     residual_chunk<DT, ALIGNED>(trow, drow, has_draft, d, V, NT, c, dsum);
@@ -2027,14 +2166,13 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     const float* gmd = reinterpret_cast<const float*>(rows + lay.md);
     const double* gSd = reinterpret_cast<const double*>(rows + lay.Sd);
     DrawDesc d{};
-    d.kind = kDrawResidual;
+    d.kind = gw->zb < kNearZ ? kDrawResidualNear : kDrawResidual;
     d.k = u;
     d.c = gw->c;
     d.m_t = gmt[u];
     d.m_d = gmd[u];
     d.lq = (float)log2(gSt[u] / gSd[u]);
-    d.lamq = (float)gw->lam;
-    d.mu = (float)(gw->lam - 1.0);
+    d.mu = encode_mu(gw->lmu);
     const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + u, V);
     const void* drow = row_ptr<DT>(p.draft, (long long)b * n + u, V);
     unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
@@ -2050,17 +2188,24 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     WSpec ws;
     ResidPlan pl;
     plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl);
-    // the pending test: the walk's next child at u, under this residual
+    // the pending test: the walk's next child at u, under this residual (the
+    // plan goes through LDS, so its registers are free for the ratio's binary64 math)
     __shared__ RoundStep s_step;
+    __shared__ WSpec s_ws;
+    __shared__ ResidPlan s_pl;
     if (tid == 0) {
-        RoundStep st{0.0, pl.lmass};
+        s_ws = ws;
+        s_pl = pl;
+    }
+    if (tid == 0) {
+        RoundStep st{0.0, s_pl.lmass};
         const int* par = p.parents + (size_t)b * n;
         const int L0 = min(max(p.lens[b], 0), n);
         for (int t = gw->next; t < L0; ++t)
             if (par[t] == u) {
                 const int x = p.tokens[(size_t)b * n + t];
                 if (x >= 0 && x < V)
-                    st.ratio = resid_ratio(ws, pl, reinterpret_cast<const float*>(rows + lay.gt)[t],
+                    st.ratio = resid_ratio(s_ws, s_pl, reinterpret_cast<const float*>(rows + lay.gt)[t],
                                            reinterpret_cast<const float*>(rows + lay.gd)[t]);
                 break;
             }
@@ -2233,7 +2378,6 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     d.m_t = s_t.m;
     d.m_d = s_d.m;
     d.lq = (float)log2((double)s_t.s / (double)s_d.s);
-    d.lamq = 1.f;
     const float lam0 = exp2_fast(d.lq);
     const float nmt = neg_scaled(d.m_t, c), nmd = neg_scaled(d.m_d, c);
     __shared__ float s_sum[4][kMaxTiles];
@@ -2252,6 +2396,32 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
         if (lane < 4) s_sum[lane][t] = far_sum_at(fs, lane);
     }
     __syncthreads();
+    // a residual mass below the near form's threshold: the tile sums a draw's
+    // chunks hand over when the decision marks it (kDrawResidualNear)
+    double zw = 0.0, zp = 0.0;
+    for (int i = tid; i < NT; i += kThreads) {
+        zw += (double)s_sum[kSumW][i];
+        zp += (double)s_sum[kSumP][i];
+    }
+    block_sum2_all(zw, zp);
+    if (zw < kNearZ * zp) {
+        d.kind = kDrawResidualNear;
+        const NearLin nl = near_lin(d);
+        for (int t = w; t < NT; t += kWaves) {
+            FarSums fs{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < kU; ++u) {
+                float zt[kVec], zd[kVec];
+                const int e0 = t * kTile + (lane + 64 * u) * kVec;
+                load_vec<DT, ALIGNED>(trow, e0, V, zt);
+                load_vec<DT, ALIGNED>(drow, e0, V, zd);
+#pragma unroll 1
+                for (int e = 0; e < kVec; ++e) near_accum(fs, d, nl, zt[e], zd[e]);
+            }
+            fs = wave_far_sums(fs);
+            if (lane < 4) s_sum[lane][t] = far_sum_at(fs, lane);
+        }
+        __syncthreads();
+    }
     float v[kTPT][4];
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
@@ -2269,9 +2439,9 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     for (int i = tid; i < V; i += kThreads)
         w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
     if (info_out && tid == 0) {
-        info_out[(size_t)r * 4 + 0] = near ? 1.f : 0.f;
+        info_out[(size_t)r * 4 + 0] = near ? (pl.exact ? 2.f : 1.f) : 0.f;
         info_out[(size_t)r * 4 + 1] = ws.mode == kWResFar ? ws.lam : 0.f;
-        info_out[(size_t)r * 4 + 2] = near ? ws.rho : 0.f;
+        info_out[(size_t)r * 4 + 2] = near ? ws.kappa : 0.f;
         info_out[(size_t)r * 4 + 3] = (float)pl.mass;
     }
 }

@@ -26,7 +26,9 @@ BUDGET = {
     "_ZN2sv6k_drawILi1EEEvNS_10DrawParamsE": 5,             # draw pass, bf16, aligned
     # sampling tree verification, bf16, aligned: statistics pass and round kernel
     "_ZN2sv19k_stats_tree_sampleILi1ELb1EEEvNS_11StatsParamsE": 6,
-    "_ZN2sv12k_tree_roundILi1ELb1EEEvNS_11RoundParamsE": 5,
+    # tree round: its deciding workgroup also forms the pending child's ratio in binary64
+    # from the residual's plan (98 registers: 4 waves per SIMD; 1.5% of the tree step)
+    "_ZN2sv12k_tree_roundILi1ELb1EEEvNS_11RoundParamsE": 4,
     "_ZN2sv5k_mtpILb1EEEvNS_9MtpParamsE": 8,               # MTP copy, aligned
     # logit projection (256 x 256 tiles, 8 waves, one workgroup per CU): two
     # waves per SIMD; the accumulators alone take 128 registers
