@@ -224,3 +224,34 @@ def test_workspace_left_zero(oracle):
                                    temps=(0.0, 0.7))
         _compare(oracle, d, R, ws=ws, tag=f"shared workspace {seed}")
         assert int(ws.count_nonzero()) == 0  # walks, row blocks, counters and sums all cleared
+
+
+def test_confident_rows_take_the_near_form(oracle):
+    """Star trees of 8 candidates at the root whose rows put about 99.9% on one
+    shared top token (same logit in both rows) and differ by N(0, 0.3^2) on every
+    other token, T = 1: the candidates are the tail tokens the draft favours most,
+    so most walks reject several of them and every residual after the first has
+    a mass near 1e-4 or below.  The walks' bounds mark those rounds and draws for
+    the near form's chunk sums; outputs against the oracle, walk by walk."""
+    B, n, V, T = 48, 8, 8192, 1.0
+    d = synth.make_tree_sample(460, device=DEV, B=B, n=n, V=V, shape="random", temps=(T,))
+    g = torch.Generator(device=DEV).manual_seed(461)
+    zt = 3.0 * torch.randn((B, n + 1, V), device=DEV, generator=g)
+    top = torch.randint(0, V, (B,), device=DEV, generator=g)
+    ar = torch.arange(B, device=DEV)
+    zt[ar, 0, top] = zt[:, 0].max(dim=1).values + 9.0
+    zd = zt[:, :n].clone() + 0.3 * torch.randn((B, n, V), device=DEV, generator=g)
+    zd[ar, 0, top] = zt[ar, 0, top]
+    d["target"] = zt.to(d["target"].dtype).contiguous()
+    d["draft"] = zd.to(d["draft"].dtype).contiguous()
+    t0 = d["target"][:, 0].float()
+    q0 = d["draft"][:, 0].float()
+    rel = (q0 - q0.max(dim=1, keepdim=True).values) - (t0 - t0.max(dim=1, keepdim=True).values)
+    rel[ar, top] = -1e9
+    d["draft_tokens"].copy_(torch.topk(rel, n, dim=1).indices.to(torch.int32))
+    d["draft_parents"].zero_()
+    d["parents_host"] = np.zeros((B, n), np.int32)
+    d["draft_lens"].fill_(n)
+    d["uniforms"][:, :n] = (1.0 - (1.0 - d["uniforms"][:, :n]) ** 8).clamp_(max=1.0 - 2.0 ** -24)  # mostly rejections
+    acc, fl = _compare(oracle, d, _rounds(d), tag="confident rows")
+    assert fl == 0
