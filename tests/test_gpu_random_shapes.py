@@ -112,3 +112,60 @@ def test_random_shapes_against_oracle(oracle, case, B, n, V, H, f32):
                                                gacc, gemi)
     assert np.array_equal(tok.cpu().numpy(), ref_tok), tag
     assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref_hid), tag
+
+
+def _shapes_wide_t():
+    rng = np.random.default_rng(4343)
+    out = []
+    for case in range(12):
+        B = int(rng.integers(1, 200))
+        n = int(rng.integers(1, 9))
+        V = int(rng.integers(2, 40000))
+        if rng.random() < 0.4:
+            V = max(8, V // 8 * 8)
+        while B * (2 * n + 1) * V > 60_000_000:
+            V = max(2, V // 2)
+        out.append((case, B, n, V, bool(rng.random() < 0.35)))
+    return out
+
+
+@pytest.mark.parametrize("case,B,n,V,f32", _shapes_wide_t())
+def test_random_temperatures_and_close_drafts(oracle, case, B, n, V, f32):
+    """Per-sequence temperatures log-uniform in [1e-3, 10] (a fifth of them 0),
+    and in half of the sequences draft rows that are the target rows plus
+    N(0, s^2) noise with s in {0.01, 0.05} (close drafts: small residual masses,
+    the near form's chunk sums or its one-workgroup form); the sampling verify
+    against the oracle, decision by decision, with the row lse within 1e-5 plus
+    the binary32 rounding of the value."""
+    d = synth.make(5, 9100 + case, device=DEV, B=B, V=V, n=n, H=8)
+    rng = np.random.default_rng(9200 + case)
+    temps = np.exp(rng.uniform(np.log(1e-3), np.log(10.0), B)).astype(np.float32)
+    temps[rng.random(B) < 0.2] = 0.0
+    d["temperature"].copy_(torch.as_tensor(temps, device=DEV))
+    g = torch.Generator(device=DEV).manual_seed(9300 + case)
+    close = torch.as_tensor(rng.random(B) < 0.5, device=DEV)
+    s = torch.where(torch.as_tensor(rng.random(B) < 0.5, device=DEV), 0.01, 0.05).view(B, 1, 1)
+    noisy = (d["target"][:, :n].float() + s * torch.randn((B, n, V), generator=g, device=DEV)).to(d["draft"].dtype)
+    d["draft"] = torch.where(close.view(B, 1, 1), noisy, d["draft"]).contiguous()
+    if f32:
+        d["target"] = d["target"].float()
+        d["draft"] = d["draft"].float()
+    lens = d["draft_lens"].cpu().numpy()
+    tag = (case, B, n, V, f32)
+    fl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lse = torch.zeros((B, 2 * n + 1), dtype=torch.float32, device=DEV)
+    acc, emi = sv.spec_verify_sample(d["target"], d["draft"], d["draft_tokens"], d["draft_lens"],
+                                     d["temperature"], d["uniforms"], row_lse=lse, err_flags=fl)
+    torch.cuda.synchronize()
+    ora = oracle.verify_sample(_host(d["target"]), _host(d["draft"]), d["draft_tokens"].cpu().numpy(), lens,
+                               temps, d["uniforms"].cpu().numpy(), threads=16)
+    acc, emi = acc.cpu().numpy(), emi.cpu().numpy()
+    rep = compare(acc, emi, ora, lens, temps, n)
+    print(f"\n{tag}: {rep}")
+    assert rep.hard == 0, (tag, rep)
+    g_, o = lse.cpu().numpy(), ora["row_lse"]
+    assert np.array_equal(np.isnan(g_), np.isnan(o)), tag
+    both = ~np.isnan(o)
+    err = np.abs(g_.astype(np.float64) - o)[both]
+    assert not both.any() or (err <= 1e-5 + 2.0 ** -23 * np.abs(o[both])).all(), tag
+    assert int(fl.item()) == int(np.bitwise_or.reduce(ora["seq_flags"])), tag
