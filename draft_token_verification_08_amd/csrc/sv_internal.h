@@ -36,7 +36,7 @@ enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
 
 // kinds of the final draw of a sequence: a bonus draw from target row L's tile
-// partials, a residual draw max(0, p_k - lamq q_k) from row pair k, or a draw
+// partials, a residual draw max(0, p_k - lam q_k) from row pair k, or a draw
 // from the whole of target row k alone (the bonus token at a tree's leaf).
 // kDrawResidualNear is a residual draw whose mass may be small (below the near
 // form's threshold): its chunks hand over the near form's tile sums instead of

@@ -1020,8 +1020,9 @@ __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const Seq
 // only the rows' statistics; each later one needs the residual at lam_k, a full
 // reduction of the pair (p_u, q_u), which a round kernel provides (the test's
 // ratio and log2 M_k, RoundStep): the walk then stops, pending.  lam_k - 1 is
-// kept as log2 (lmu) besides lam_k, so that a residual mass below binary64's
-// resolution at 1 (T -> 0, rows on one top token) still enters lam.
+// kept as log2 (lmu), so that a residual mass below binary64's resolution at 1
+// (T -> 0, rows on one top token) still enters lam, and with it a lower bound
+// of the next residual's mass (zb), which picks the draw's form.
 
 // One sequence's walk inputs, staged in LDS: statistics of target rows (mt, St)
 // and draft rows (md, Sd) by node, and node j + 1's token, parent (-1 when not
@@ -1094,7 +1095,7 @@ __device__ __forceinline__ double resid_mass_bound(double St, double Sd, double 
 
 // Runs the walk from its state (one thread).  Returns true when it has
 // finished: *d then describes the draw (kDrawTarget at a node with no child
-// left and no rejection, else kDrawResidual with lamq = lam).  Returns false,
+// left and no rejection, else a residual draw at the walk's lam).  Returns false,
 // with the state pending, when the next test needs the residual at the current
 // lam and no round's result for that test (`step`, when have_step) is left (only if
 // can_pend; otherwise the children not yet tested are left out, which is the
@@ -1635,13 +1636,15 @@ __global__ __launch_bounds__(kThreads) void k_stats_draw(StatsParams p) {
 // lam Q, not to their difference: measured, the normalised CDF error of these
 // weights is about 3e-8 / Z for residual mass Z = sum W / sum P.  When Z is
 // below kNearZ (the draft is almost the target, or T -> 0 with both rows on one
-// top token, where every other term lies below the binary32 range) the last
-// workgroup re-forms the row pair's weights by itself in the near form
-// (near_exact_tiles()), in which the tokens the rows share cancel exactly and
-// the differences are scaled to the largest of them.  That is slow (one
-// workgroup reads the pair three times) but rare: draft k is rejected with
-// probability Z_k, so a position whose residual mass is below kNearZ reaches
-// this draw at most that often.
+// top token) the weights take the near form, in which the tokens the rows share
+// cancel exactly.  The decision marks the draws whose mass may be that small
+// (resid_mass_bound()), and their chunks hand over the near form's sums instead
+// (near_lin()).  Where those cannot settle the tile weights (the mass below what
+// the statistics' sums resolve, or below the binary32 range), and for an
+// unmarked draw whose far-form mass turns out small, the last workgroup re-forms
+// the pair's weights by itself (near_exact_tiles(): the differences scaled to
+// the largest of them, the pair read three times): slow, but reached with
+// probability about Z_k <= 1e-6.
 constexpr int kSumP = 0, kSumQ = 1, kSumW = 2, kSumG = 3;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -1858,7 +1861,7 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
 
 // The residual draw's set-up in the deciding workgroup, from the far-form tile
 // sums v[r][*] of tiles tid + r kThreads, for the residual max(0, p - lq q) with
-// lq = d.lamq (near form: lam = 1 + mu from d.mu): the tile weights into
+// lam = 1 + mu (mu from d.mu): the tile weights into
 // s_w[NT], the element weighting into *ws, the rest into *pl (with no residual
 // mass left, s_w holds the target's own tile masses and *ws weighs by the
 // target).
@@ -1984,8 +1987,9 @@ __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& 
 // !has_draft: the target row alone): its tiles [c kDrawTiles, ...) loaded once
 // (wave w owns kDrawTiles / kWaves whole tiles, lane l reads vectors l, l + 64,
 // ... of each, all loads issued before the first use), the far-form tile sums
-// at lam0 = d.lamq 2^d.lq handed over by atomic exchange into dsum[q][tile],
-// completed before the function returns.
+// at lam0 = (1 + mu) 2^d.lq, or for a kDrawResidualNear draw the near form's
+// (near_lin()), handed over by atomic exchange into dsum[q][tile], completed
+// before the function returns.
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ void residual_chunk(const void* trow, const void* drow, bool has_draft, const DrawDesc& d,
                                                int V, int NT, int c, unsigned* dsum) {
