@@ -38,8 +38,8 @@
  * mass.  As T -> 0 with both rows on one top token no precision suffices for
  * the difference itself (p_0 = 1 / (1 + tail) rounds to 1), so the residual is
  * written as an exact rearrangement in which tokens that the rows share cancel
- * before anything is rounded (resid_t).  Nothing is blocked, fused or
- * reordered.
+ * before anything is rounded, and its terms are carried as signed logarithms
+ * (resid_t).  Nothing is blocked, fused or reordered.
  *
  * Readings of points the pages leave open:
  *   - acceptance of draft x_j:  u[b][j] < p_j(x_j) / q_j(x_j); q(x) = 0 gives
@@ -181,21 +181,58 @@ static double row_max(const void *rows, int dt, size_t base, int V)
     return m;
 }
 
-/* The residual of a target row and a draft row at lam = 1 + mu, exactly as
- * defined (Speculative decoding section, the first reference: after a rejection
- * the token is drawn from max(0, p - q) normalised; SpecInfer: after k rejections
- * at a node, from max(0, p - lam_k q)).  With a_i = (z_t,i - m_t) / T and
- * b_i = (z_d,i - m_d) / T (each row relative to its own maximum), S_t = sum e^a
- * and S_d = sum e^b, multiplying p_i - lam q_i by the positive S_t S_d gives
- *   R_i = (e^{a_i} - e^{b_i}) S_t + e^{a_i} Delta - mu e^{b_i} S_t,
- *   Delta = S_d - S_t = sum_j (e^{b_j} - e^{a_j}).
- * A token with a_j = b_j adds exactly zero to Delta and to its own first term, so
- * the digits that p_i - q_i loses where p and q agree beyond the arithmetic's
- * precision (T -> 0 with both rows on the same top token: 1 + tail rounds to 1)
- * are never formed.  Every term is carried in units of e^s, s the largest of a_j
- * and b_j over the tokens with a_j != b_j, so that none leaves the range however
- * small the residual is; mu and the residual mass are carried in the same units.
- * A -inf logit is a probability of 0 (its e^a is 0); a row with no finite logit
+/* A signed quantity s e^l (s = +1, -1, or 0 with l = -inf), so that residual
+ * terms far below the range of long double keep their value and sign. */
+typedef struct {
+    int s;
+    long double l;
+} slog_t;
+
+static slog_t slog_zero(void)
+{
+    slog_t z = {0, -INFINITY};
+    return z;
+}
+
+/* x + y: the larger magnitude keeps its sign; a difference is formed as
+ * e^hi (1 - e^{lo - hi}) with -expm1l, so that no digit is lost to 1 - e^d. */
+static slog_t slog_add(slog_t x, slog_t y)
+{
+    if (x.s == 0) return y;
+    if (y.s == 0) return x;
+    const slog_t hi = x.l >= y.l ? x : y, lo = x.l >= y.l ? y : x;
+    const long double d = lo.l - hi.l;
+    slog_t r = {hi.s, hi.l};
+    if (hi.s == lo.s) {
+        r.l = hi.l + log1pl(expl(d));
+    } else {
+        if (d == 0.0L) return slog_zero();
+        r.l = hi.l + logl(-expm1l(d));
+    }
+    return r;
+}
+
+/* The residual of a target row and a draft row at lam (Speculative decoding
+ * section, the first reference: after a rejection the token is drawn from
+ * max(0, p - q) normalised; SpecInfer: after k rejections at a node, from
+ * max(0, p - lam_k q), lam_1 = 1, lam_{k+1} = lam_k + M_k, M_k the mass of
+ * max(0, p - lam_k q)).  With a_i = (z_t,i - m_t) / T and b_i = (z_d,i - m_d) / T
+ * (each row relative to its own maximum), S_t = sum e^a and S_d = sum e^b:
+ *   p_i - lam q_i = R_i / S_d,  R_i = kappa e^{a_i} + lam (e^{a_i} - e^{b_i}),
+ *   kappa = S_d / S_t - lam,
+ * an exact rearrangement in which a token whose relative logits agree
+ * (a_i = b_i, "shared") contributes kappa e^{a_i} alone.  As T -> 0 with both
+ * rows on one top token, p_i - q_i is a difference of two numbers that agree
+ * beyond any precision (1 + tail rounds to 1), and so is kappa = S_d / S_t - lam
+ * formed from its parts; here kappa is formed from the differing tokens only:
+ *   kappa_1 = Delta / S_t,  Delta = sum over differing tokens of (e^b - e^a),
+ *   kappa_{k+1} = kappa_k - M_k = (kappa_k Y - W) / S_d   if kappa_k > 0,
+ *               = kappa_k - W / S_d                          otherwise,
+ * with Y = sum e^b over the differing tokens (= S_d - the shared tokens' sum)
+ * and W = sum max(0, R_i) over the differing tokens (M_k = (W + max(0, kappa_k)
+ * times the shared tokens' sum) / S_d).  kappa and every R_i are carried as
+ * signed logarithms (slog_t), so none leaves the range however small it is.  A
+ * -inf logit is a probability of 0 (its e^a is 0); a row with no finite logit
  * takes every a_i = -inf. */
 typedef struct {
     const void *trows, *drows;
@@ -203,8 +240,9 @@ typedef struct {
     size_t tb, db;      /* first element of the target row and of the draft row */
     long double T, mt, md;
     long double St, Sd; /* sum e^{a_i}, sum e^{b_i} */
-    long double s;      /* the unit exponent; -inf when a_i = b_i for every i (p = q) */
-    long double dlt;    /* Delta e^{-s} */
+    long double lY;     /* log of sum e^{b_i} over the tokens with a_i != b_i */
+    slog_t kap;         /* kappa at the current lam */
+    long double lam;    /* the current lam (1 after the first rejection) */
 } resid_t;
 
 static long double rel_logit(const void *rows, int dt, size_t at, long double m, long double T)
@@ -213,6 +251,21 @@ static long double rel_logit(const void *rows, int dt, size_t at, long double m,
     return ((long double)logit_at(rows, dt, at) - m) / T;
 }
 
+/* e^a - e^b (a != b) as a signed logarithm */
+static slog_t exp_diff(long double a, long double b)
+{
+    slog_t r;
+    if (a > b) {
+        r.s = 1;
+        r.l = a + logl(-expm1l(b - a));
+    } else {
+        r.s = -1;
+        r.l = b + logl(-expm1l(a - b));
+    }
+    return r;
+}
+
+/* The residual of the pair at lam = 1: S_t, S_d, Y and kappa_1 = Delta / S_t. */
 static void resid_setup(resid_t *r, const void *trows, const void *drows, int dt, size_t tb, size_t db, int V,
                         double T)
 {
@@ -226,48 +279,105 @@ static void resid_setup(resid_t *r, const void *trows, const void *drows, int dt
     r->mt = row_max(trows, dt, tb, V);
     r->md = row_max(drows, dt, db, V);
     r->St = r->Sd = 0.0L;
-    r->s = -INFINITY;
+    r->lY = -INFINITY;
+    slog_t dlt = slog_zero();
     for (int i = 0; i < V; ++i) {
         const long double a = rel_logit(trows, dt, tb + (size_t)i, r->mt, r->T);
         const long double b = rel_logit(drows, dt, db + (size_t)i, r->md, r->T);
         r->St += expl(a);
         r->Sd += expl(b);
         if (a != b) {
-            if (a > r->s) r->s = a;
-            if (b > r->s) r->s = b;
+            slog_t d = exp_diff(a, b);
+            d.s = -d.s; /* e^b - e^a */
+            dlt = slog_add(dlt, d);
+            if (b > -INFINITY) {
+                const slog_t eb = {1, b};
+                const slog_t y = {r->lY > -INFINITY ? 1 : 0, r->lY};
+                r->lY = slog_add(y, eb).l;
+            }
         }
     }
-    r->dlt = 0.0L;
-    if (r->s == -INFINITY) return;
-    for (int i = 0; i < V; ++i) {
-        const long double a = rel_logit(trows, dt, tb + (size_t)i, r->mt, r->T);
-        const long double b = rel_logit(drows, dt, db + (size_t)i, r->md, r->T);
-        if (a != b) r->dlt += expl(b - r->s) - expl(a - r->s);
-    }
+    r->kap = dlt;
+    if (dlt.s != 0) r->kap.l -= logl(r->St);
+    r->lam = 1.0L;
 }
 
-/* R_i e^{-s} at mu = mu_s e^s (see resid_t); only for rows with s > -inf. */
-static long double resid_at(const resid_t *r, int i, long double mu_s)
+/* R_i = kappa e^{a_i} + lam (e^{a_i} - e^{b_i}) at the current lam (resid_t),
+ * as a signed logarithm; *shared receives whether a_i = b_i. */
+static slog_t resid_at(const resid_t *r, int i, int *shared)
 {
     const long double a = rel_logit(r->trows, r->dt, r->tb + (size_t)i, r->mt, r->T);
     const long double b = rel_logit(r->drows, r->dt, r->db + (size_t)i, r->md, r->T);
-    long double R = expl(a) * r->dlt;
-    if (a != b) R += (expl(a - r->s) - expl(b - r->s)) * r->St;
-    if (mu_s != 0.0L && b != -INFINITY) R -= mu_s * expl(b) * r->St;
+    slog_t R = slog_zero();
+    if (r->kap.s != 0 && a > -INFINITY) {
+        R.s = r->kap.s;
+        R.l = r->kap.l + a;
+    }
+    *shared = (a == b);
+    if (a != b) {
+        slog_t d = exp_diff(a, b);
+        d.l += logl(r->lam);
+        R = slog_add(R, d);
+    }
     return R;
 }
 
-/* Weights w_i = max(0, R_i e^{-s}) at mu = mu_s e^s into w[V]; returns the
- * residual mass sum max(0, p - lam q) in units of e^s, sum w / (S_t S_d). */
-static long double resid_weights(const resid_t *r, long double mu_s, long double *w)
+/* The log-weights lw_i = log max(0, R_i) (-inf where R_i <= 0) into lw[V];
+ * returns log of their sum (-inf: no residual mass), and the log of the
+ * differing tokens' part of it in *lw_diff. */
+static long double resid_log_weights(const resid_t *r, long double *lw, long double *lw_diff)
 {
-    long double Z = 0.0L;
+    slog_t tot = slog_zero(), dif = slog_zero();
     for (int i = 0; i < r->V; ++i) {
-        const long double R = r->s == -INFINITY ? 0.0L : resid_at(r, i, mu_s);
-        w[i] = R > 0.0L ? R : 0.0L;
-        Z += w[i];
+        int shared = 0;
+        const slog_t R = resid_at(r, i, &shared);
+        lw[i] = R.s > 0 ? R.l : -INFINITY;
+        if (R.s > 0) {
+            tot = slog_add(tot, R);
+            if (!shared) dif = slog_add(dif, R);
+        }
     }
-    return Z / (r->St * r->Sd);
+    if (lw_diff) *lw_diff = dif.l;
+    return tot.l;
+}
+
+/* lam_{k+1} = lam_k + M_k and kappa_{k+1} (resid_t) from the log of the
+ * residual's total lw_tot and of its differing tokens' part lw_diff. */
+static void resid_advance(resid_t *r, long double lw_tot, long double lw_diff)
+{
+    const long double lSd = logl(r->Sd);
+    const slog_t W = {lw_diff > -INFINITY ? 1 : 0, lw_diff};
+    slog_t next;
+    if (r->kap.s > 0) {
+        slog_t kY = slog_zero();
+        if (r->lY > -INFINITY) {
+            kY.s = 1;
+            kY.l = r->kap.l + r->lY;
+        }
+        slog_t mW = W;
+        mW.s = -mW.s;
+        next = slog_add(kY, mW);
+        next.l -= lSd;
+    } else {
+        slog_t mWS = W;
+        mWS.s = -mWS.s;
+        mWS.l -= lSd;
+        next = slog_add(r->kap, mWS);
+    }
+    if (next.s == 0) next.l = -INFINITY;
+    r->kap = next;
+    if (lw_tot > -INFINITY) r->lam += expl(lw_tot - lSd);
+}
+
+/* Weights proportional to max(0, p_i - lam q_i) from the log-weights: w_i =
+ * e^{lw_i - max lw}; returns 1 if any is positive, 0 if none is. */
+static int resid_weights_from_log(const long double *lw, int V, long double *w)
+{
+    long double mx = -INFINITY;
+    for (int i = 0; i < V; ++i)
+        if (lw[i] > mx) mx = lw[i];
+    for (int i = 0; i < V; ++i) w[i] = (mx > -INFINITY && lw[i] > -INFINITY) ? expl(lw[i] - mx) : 0.0L;
+    return mx > -INFINITY;
 }
 
 /* Inverse CDF over unnormalised weights in ascending index order.
@@ -410,7 +520,9 @@ static void verify_one(const job_t *J, int b, long double *w /* scratch [2V] */)
             /* residual distribution max(0, p_k - q_k), formed exactly (resid_t) */
             resid_t rs;
             resid_setup(&rs, J->target, J->draft, J->dt, trow0 + (size_t)k * V, drow0 + (size_t)k * V, V, T);
-            long double Z = resid_weights(&rs, 0.0L, w);
+            long double *lw = w + V;
+            (void)resid_log_weights(&rs, lw, NULL);
+            long double Z = resid_weights_from_log(lw, V, w) ? 1.0L : 0.0L;
 #if SV_ORACLE_PLANT == 1
             /* planted mistake: plain target sampling at the rejection */
             row_probs_ld(J->target, J->dt, trow0 + (size_t)k * V, V, T, w);
@@ -734,7 +846,7 @@ typedef struct {
     uint32_t *seq_flags;
 } tree_job_t;
 
-static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratch [2V] */)
+static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratch [3V] */)
 {
     const int n = J->n, V = J->V;
     uint32_t flags = 0;
@@ -764,7 +876,7 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
     }
     const size_t trow0 = (size_t)b * (size_t)(n + 1) * (size_t)V;
     const size_t drow0 = (size_t)b * (size_t)n * (size_t)V;
-    long double *p = w, *q = w + V;
+    long double *p = w, *q = w + V, *lw = w + 2 * (size_t)V;
     int u = 0, depth = 0, y = -1, sums = 0;
     for (;;) {
         /* the target at node u, and (if u has children) the draft at node u */
@@ -782,11 +894,13 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
         double mt, lst, md, lsd;
         (void)row_softmax_stats(J->target, J->dt, trow0 + (size_t)u * V, V, T, &mt, &lst);
         (void)row_softmax_stats(J->draft, J->dt, drow0 + (size_t)u * V, V, T, &md, &lsd);
-        /* after k >= 1 rejections at u: lam_k = 1 + mu, mu and M_k carried in
-         * units of e^s of the pair's resid_t (mu_s = mu e^{-s}, M_s = M_k e^{-s}) */
+        /* after k >= 1 rejections at u: the residual max(0, p_u - lam_k q_u) of
+         * resid_t (lam_k, kappa_k), its log-weights in lw, log M_k in lM */
         resid_t rs;
         int rejections = 0, accepted = -1, have_rs = 0;
-        long double mu_s = 0.0L, M_s = 0.0L;
+        long double lW = -INFINITY, lWd = -INFINITY, lM = -INFINITY;
+        slog_t kap1 = slog_zero(); /* kappa_1, for the planted mistakes below */
+        (void)kap1;
         for (int j = first; j < L; ++j) {
             if (par[j] != u || par[j] > j) continue;
             const int xc = x[j];
@@ -798,11 +912,12 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
                                          logit_at(J->draft, J->dt, drow0 + (size_t)u * V + (size_t)xc), md, lsd, T);
                 } else {
                     /* the residual's ratio (p_u(x) - lam q_u(x)) / (M_k q_u(x)) =
-                     * R_x / (S_t e^{b_x} M_s) with R_x in units of e^s (resid_t);
-                     * q_u(x) = 0 < p_u(x) - lam q_u(x) gives +inf */
-                    const long double R = resid_at(&rs, xc, mu_s);
+                     * R_x / (M_k e^{b_x}) (resid_t); q_u(x) = 0 < p_u(x) - lam q_u(x)
+                     * gives +inf */
+                    int shared = 0;
+                    const slog_t R = resid_at(&rs, xc, &shared);
                     const long double bx = rel_logit(J->draft, J->dt, drow0 + (size_t)u * V + (size_t)xc, rs.md, rs.T);
-                    if (R > 0.0L && M_s > 0.0L) ratio = (double)(R / (rs.St * expl(bx) * M_s));
+                    if (R.s > 0 && lM > -INFINITY) ratio = (double)expl(R.l - lM - bx);
                 }
             }
             const double uu = sanitize_uniform(uni[j], &flags);
@@ -810,6 +925,7 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
             if (uu < ratio) { accepted = j; break; }
             if (!have_rs) {
                 resid_setup(&rs, J->target, J->draft, J->dt, trow0 + (size_t)u * V, drow0 + (size_t)u * V, V, T);
+                kap1 = rs.kap;
                 have_rs = 1;
             }
 #if SV_ORACLE_PLANT == 8
@@ -819,8 +935,8 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
             continue;
 #endif
             /* rejected: p' <- max(0, p' - q_u) normalised, i.e. lam_{k+1} = lam_k + M_k
-             * (lam_1 = 1: mu stays 0) */
-            if (rejections > 0) mu_s += M_s;
+             * (the first rejection leaves lam_1 = 1 as resid_setup() formed it) */
+            if (rejections > 0) resid_advance(&rs, lW, lWd);
             ++rejections;
             int later = 0;
             for (int t = j + 1; t < L && !later; ++t) later = (par[t] == u);
@@ -830,7 +946,8 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
                 break;
             }
             ++sums;
-            M_s = resid_weights(&rs, mu_s, q);
+            lW = resid_log_weights(&rs, lw, &lWd);
+            lM = lW > -INFINITY ? lW - logl(rs.Sd) : -INFINITY;
         }
         if (accepted >= 0) {
             path[depth] = accepted + 1;
@@ -841,11 +958,13 @@ static void tree_sample_one(const tree_job_t *J, int b, long double *w /* scratc
         }
         /* every child rejected: draw from max(0, p_u - lam q_u) */
 #if SV_ORACLE_PLANT == 8 || SV_ORACLE_PLANT == 9
-        mu_s = 0.0L; /* planted mistakes: the draw ignores the later siblings' updates */
+        /* planted mistakes: the draw ignores the later siblings' updates */
+        rs.kap = kap1;
+        rs.lam = 1.0L;
 #endif
-        const long double Z = resid_weights(&rs, mu_s, q);
+        (void)resid_log_weights(&rs, lw, NULL);
         double margin = 0.0;
-        if (Z > 0.0L) {
+        if (resid_weights_from_log(lw, V, q)) {
             y = draw_inverse_cdf(q, V, sanitize_uniform(uni[n], &flags), &margin);
         } else {
             flags |= OR_FLAG_ZERO_RESIDUAL;
@@ -875,7 +994,7 @@ int sv_oracle_verify_tree_sample(const void *target_logits, const void *draft_lo
                                  int32_t *path, double *accept_margin, double *draw_margin, uint32_t *seq_flags)
 {
     if (check_dims(B, n, V)) return -1;
-    long double *w = (long double *)malloc(sizeof(long double) * 2 * (size_t)V);
+    long double *w = (long double *)malloc(sizeof(long double) * 3 * (size_t)V);
     if (!w) return -2;
     tree_job_t J = {target_logits, draft_logits, dt, draft_tokens, draft_parents, draft_lens, temperature,
                     uniforms, B, n, V, max_rounds, accepted_len, emitted, path, accept_margin, draw_margin, seq_flags};
