@@ -30,7 +30,7 @@ constexpr int kDrawTiles = SV_DRAW_TILES;  // draw pass: tiles (kThreads * eleme
 constexpr int kMaxTiles = 1024;      // tiles per row (4 per thread in the draw selections)
 constexpr int kTargetWorkgroups = SV_TARGET_WORKGROUPS;  // stats pass: workgroups over the target rows
 constexpr int kMaxPartials = 2048;       // (2n+1) * chunks per row, staged in LDS by the decision
-constexpr int kDrawSums = 4;         // per-tile sums a residual draw chunk hands over
+constexpr int kDrawSums = 6;         // per-tile sums a residual draw chunk hands over (far form: the first 4)
 
 enum Dt : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int { kSample = 0, kGreedy = 1 };
@@ -66,8 +66,12 @@ struct DrawDesc {
     double mu;      // residual draws: the weights are max(0, p - lam q) with lam = 1 + mu (mu = 0
                     // after one rejection; tree walks: more), mu itself when at least 2^-1000,
                     // else log2(mu) (< -1000)
+    double lkap;    // skap != 0: log2 |kappa|, kappa = S_d / S_t - lam (-inf: kappa = 0)
+    int skap;       // the sign of kappa (+1 or -1) when a tree walk carries it (after two or
+                    // more rejections at a node); 0: kappa = S_d / S_t - 1, formed by the draw
+    int pad_;
 };
-static_assert(sizeof(DrawDesc) == 40, "the workspace layout sizes DrawDesc at 40 bytes");
+static_assert(sizeof(DrawDesc) == 56, "the workspace layout sizes DrawDesc at 56 bytes");
 
 // A sampling tree walk (per sequence), kept in the workspace between the
 // statistics pass, the rounds and the draw pass.
@@ -79,6 +83,8 @@ struct TreeWalk {
     int depth;      // nodes on the kept path so far
     double zb;      // a lower bound of sum max(0, p_u - lam_k q_u) (< 0: no child rejected yet)
     double lmu;     // log2(lam_k - 1) once a child is rejected (-inf: lam_k = 1)
+    double lkap;    // skap != 0: log2 |kappa_k|, kappa_k = S_d / S_t - lam_k at node u (-inf: 0)
+    int skap;       // the sign of kappa_k once two children at u are rejected; 0: not carried
     uint32_t flags;
     float c;        // log2(e) / T
     int path[kMaxDraft];

@@ -668,16 +668,21 @@ __device__ __forceinline__ float exp2m1_small(float x) {
 // enter a difference, and their weight kappa A carries one rounding.
 struct NearTerm {
     float A, Dl;
+    float Bs;  // 2^((ad - sl) c), B in the units of Dl (0 for a token the rows share)
 };
 __device__ __forceinline__ float near_rel(float z, float m) { return m > -FLT_MAX ? z - m : -INFINITY; }
 __device__ __forceinline__ NearTerm near_term(float m_t, float m_d, float sl, float c, float zt, float zd) {
     const float at = near_rel(zt, m_t), ad = near_rel(zd, m_d);
     const float A = exp2_fast(at * c);
-    if (at == ad) return NearTerm{A, 0.f};
+    if (at == ad) return NearTerm{A, 0.f, 0.f};
     const float x = (ad - at) * c;
     const float As = exp2_fast((at - sl) * c);
-    const float Dl = fabsf(x) <= 0.25f ? As * exp2m1_small(x) : exp2_fast((ad - sl) * c) - As;
-    return NearTerm{A, Dl};
+    if (fabsf(x) <= 0.25f) {
+        const float Dl = As * exp2m1_small(x);
+        return NearTerm{A, Dl, As + Dl};
+    }
+    const float Bs = exp2_fast((ad - sl) * c);
+    return NearTerm{A, Bs - As, Bs};
 }
 // The residual weight of one token in the near form (see near_term()).
 __device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, float c, float kappa, float lam, float zt,
@@ -694,18 +699,25 @@ __device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, flo
 //               maximum (mA = m_t) and lam the ratio of their sums (S_t / S_d);
 //   kWResNear:  near_weight(): max(0, kappa A - lam Dl) of near_term(), each
 //               row relative to its own maximum (mA = m_t), differences in
-//               units of 2^(sl c): the residual max(0, p - lam q).
-enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2 };
+//               units of 2^(sl c): the residual max(0, p - lam q);
+//   kWResNearLog: the same weights formed from their log2 in binary64
+//               (near_log_weight()) and scaled by 2^-E, for residuals whose
+//               weights lie below the binary32 range in units of 2^(sl c).
+enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2, kWResNearLog = 3 };
 struct WSpec {
     int mode;
     float c;    // log2(e) / T
     float mA;   // maximum the target row is scaled by
     float m_d;  // kWResFar: the draft row's maximum
-    float lam;    // kWResFar: lam S_t / S_d; kWResNear: lam
+    float lam;    // kWResFar: lam S_t / S_d; kWResNear(Log): lam
     float kappa;  // kWResNear
-    float sl;     // kWResNear: the shift of the differences (<= 0)
+    float sl;     // kWResNear(Log): the shift of the differences (<= 0)
     float nmt;  // kWResFar: neg_scaled(mA, c)
     float nmd;  // kWResFar: neg_scaled(m_d, c)
+    int ks;      // kWResNearLog: the sign of kappa (0: kappa = 0)
+    double lk;   // kWResNearLog: log2 |kappa| (kappa in units of 2^(sl c))
+    double sig;  // kWResNearLog: sl c
+    double E;    // kWResNearLog: the weights' scale (an integer): weights are 2^(log2 w - E)
 };
 // -fl(m c) for a row maximum m, the offset of far_p(); 0 when the row has no
 // finite element (m = -FLT_MAX), whose terms are then all 2^-inf = 0.
@@ -715,8 +727,46 @@ __device__ __forceinline__ float neg_scaled(float m, float c) { return m > -FLT_
 // so the rounding of fl(m c), a factor common to the whole row, cancels in the
 // ratio lam = sum P / sum Q and in the normalised weights.
 __device__ __forceinline__ float far_p(float nm, float c, float z) { return exp2_fast(fmaf(z, c, nm)); }
+// log2(2^a + 2^b)
+__device__ __forceinline__ double log2_add(double a, double b) {
+    if (a == -INFINITY) return b;
+    if (b == -INFINITY) return a;
+    const double hi = fmax(a, b), lo = fmin(a, b);
+    return hi + log2(1.0 + exp2(lo - hi));
+}
+// log2 of the near form's weight max(0, kappa A - lam Dl) of near_term() in
+// units of 2^(sl c) (-inf: no weight).  The exponents (log2 A = at c, log2 |kappa|,
+// the shift) are added in binary64, so that no weight leaves the range; the
+// corrections of order 1 are binary32: lam |Dl| = lam 2^(at c - sl c) |2^x - 1|
+// with x = (ad - at) c and |2^x - 1| = 2^max(x, 0) (1 - 2^-|x|), 1 - 2^-|x| by
+// expm1f, and sums and differences of two weights as 2^hi (1 +- 2^(lo - hi)).
+__device__ __forceinline__ double near_log_weight(const WSpec& s, float zt, float zd) {
+    constexpr float kLn2f = 0.69314718f;
+    const float at = near_rel(zt, s.mA), ad = near_rel(zd, s.m_d);
+    if (at == -INFINITY) return -INFINITY;  // p = 0: max(0, -lam q) = 0
+    const double ac = (double)at * (double)s.c;
+    const double lkA = s.ks != 0 ? s.lk + ac : -INFINITY;  // log2 (|kappa| A)
+    if (at == ad) return s.ks > 0 ? lkA : -INFINITY;
+    const double x = ad == -INFINITY ? -INFINITY : ((double)ad - (double)at) * (double)s.c;
+    const float xa = (float)fabs(x);
+    const double lD = (double)log2f(s.lam) + ac - s.sig + fmax(x, 0.0) + (double)log2f(-expm1f(-xa * kLn2f));
+    if (x < 0.0) {  // target above draft: -lam Dl > 0
+        if (s.ks > 0) {
+            const double hi = fmax(lkA, lD), lo = fmin(lkA, lD);
+            return hi + (double)log2f(1.f + exp2f((float)(lo - hi)));
+        }
+        if (s.ks < 0) return lkA < lD ? lD + (double)log2f(-expm1f((float)(lkA - lD) * kLn2f)) : -INFINITY;
+        return lD;
+    }
+    return (s.ks > 0 && lkA > lD) ? lkA + (double)log2f(-expm1f((float)(lD - lkA) * kLn2f)) : -INFINITY;
+}
+
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
     if (s.mode == kWTarget) return exp2_fast((zt - s.mA) * s.c);
+    if (s.mode == kWResNearLog) {
+        const double lw = near_log_weight(s, zt, zd);
+        return lw == -INFINITY ? 0.f : exp2_fast((float)(lw - s.E));
+    }
     if (s.mode == kWResFar) {
         const float P = far_p(s.nmt, s.c, zt);
         const float Q = far_p(s.nmd, s.c, zd);
@@ -1022,7 +1072,11 @@ __device__ __forceinline__ void tree_walk(const StatsParams& p, int b, const Seq
 // ratio and log2 M_k, RoundStep): the walk then stops, pending.  lam_k - 1 is
 // kept as log2 (lmu), so that a residual mass below binary64's resolution at 1
 // (T -> 0, rows on one top token) still enters lam, and with it a lower bound
-// of the next residual's mass (zb), which picks the draw's form.
+// of the next residual's mass (zb), which picks the draw's form.  The weight of
+// the tokens whose relative logits agree in both rows is kappa_k 2^(a c) / S_d
+// with kappa_k = S_d / S_t - lam_k; after the second rejection it can be a
+// product of two tails, far below the binary64 resolution of lam_k, so the walk
+// carries kappa_k itself from the round that formed M_k (sign and log2).
 
 // One sequence's walk inputs, staged in LDS: statistics of target rows (mt, St)
 // and draft rows (md, Sd) by node, and node j + 1's token, parent (-1 when not
@@ -1054,18 +1108,13 @@ __device__ double tree_ratio(const WalkRows& r, int j, int u, int V, float c) {
 
 // What one round hands the walk for the one test it makes possible: the
 // pending child's acceptance ratio under the residual at the current lam_k,
-// (p_u(x) - lam_k q_u(x)) / (M_k q_u(x)), and log2 M_k for lam_{k+1} = lam_k + M_k.
+// (p_u(x) - lam_k q_u(x)) / (M_k q_u(x)), log2 M_k for lam_{k+1} = lam_k + M_k,
+// and kappa_{k+1} = S_d / S_t - lam_{k+1} as sign and log2 (next_kappa()).
 struct RoundStep {
-    double ratio, lM;
+    double ratio, lM, lkap;
+    int skap;
 };
 
-// log2(2^a + 2^b)
-__device__ __forceinline__ double log2_add(double a, double b) {
-    if (a == -INFINITY) return b;
-    if (b == -INFINITY) return a;
-    const double hi = fmax(a, b), lo = fmin(a, b);
-    return hi + log2(1.0 + exp2(lo - hi));
-}
 // DrawDesc::mu from log2(lam - 1), and back: log2 mu, and mu (0 below binary64)
 __device__ __forceinline__ double encode_mu(double lmu) {
     if (lmu == -INFINITY) return 0.0;
@@ -1076,6 +1125,29 @@ __device__ __forceinline__ double desc_lmu(const DrawDesc& d) {
     return d.mu > 0.0 ? log2(d.mu) : d.mu;
 }
 __device__ __forceinline__ double desc_mu(const DrawDesc& d) { return d.mu > 0.0 ? d.mu : 0.0; }
+
+// A signed quantity s 2^l (s = +1 or -1, l = -inf: zero), for kappa = S_d / S_t
+// - lam, which after later rejections at a tree node is a product of tails and
+// may lie below the binary64 range.
+struct SLog2 {
+    int s;
+    double l;
+};
+// a + b, the difference formed as 2^hi (1 - 2^(lo - hi)) with expm1 (no digit lost to 1 - 2^d)
+__device__ __forceinline__ SLog2 slog2_add(SLog2 a, SLog2 b) {
+    if (a.l == -INFINITY) return b;
+    if (b.l == -INFINITY) return a;
+    const SLog2 hi = a.l >= b.l ? a : b, lo = a.l >= b.l ? b : a;
+    const double dd = lo.l - hi.l;
+    if (hi.s == lo.s) return SLog2{hi.s, hi.l + log2(1.0 + exp2(dd))};
+    if (dd == 0.0) return SLog2{1, -INFINITY};
+    return SLog2{hi.s, hi.l + log2(-expm1(dd * 0.6931471805599453))};
+}
+__device__ __forceinline__ SLog2 slog2_of(double v) { return SLog2{v < 0.0 ? -1 : 1, v != 0.0 ? log2(fabs(v)) : -INFINITY}; }
+// kappa carried by a tree walk (d.skap != 0), in units of 2^lu (0 below binary64)
+__device__ __forceinline__ double desc_kappa(const DrawDesc& d, double lu) {
+    return d.lkap == -INFINITY ? 0.0 : (double)d.skap * exp2(d.lkap - lu);
+}
 
 // A lower bound of the residual mass sum max(0, p - q) after a rejection of x:
 // q(x) - p(x), and from the rows' sums (S = sum 2^((z - m) c), so each row's top
@@ -1124,16 +1196,20 @@ __device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, in
                 d->m_d = r.md[u];
                 d->lq = (float)log2(r.St[u] / r.Sd[u]);
                 d->mu = encode_mu(w.lmu);
+                d->skap = w.skap;
+                d->lkap = w.lkap;
             }
             w.status = kWalkIdle;
             return true;
         }
         double ratio, lM = -INFINITY;
+        SLog2 kn{0, -INFINITY};  // kappa after this child's rejection (a round's result)
         if (w.zb < 0.0) {
             ratio = tree_ratio(r, j, w.u, V, w.c);
         } else if (have_step) {  // the round's result is for this child
             ratio = step.ratio;
             lM = step.lM;
+            kn = SLog2{step.skap, step.lkap};
             have_step = false;
         } else {  // the residual at lam not formed yet
             if (can_pend) {
@@ -1151,6 +1227,8 @@ __device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, in
             w.u = j + 1;
             w.zb = -1.0;
             w.lmu = -INFINITY;
+            w.skap = 0;
+            w.lkap = -INFINITY;
         } else {
             // q_u(x) (1 - the ratio x was tested at): the rejected child's share of
             // the next residual mass (resid_mass_bound())
@@ -1162,9 +1240,15 @@ __device__ __forceinline__ bool tree_walk_run(TreeWalk& w, const WalkRows& r, in
                 w.zb = resid_mass_bound(r.St[w.u], r.Sd[w.u], gap);
                 w.lmu = -INFINITY;
             } else {  // the residual loses q_u once more: lam_{k+1} = lam_k + M_k
-                const double St = r.St[w.u], Sd = r.Sd[w.u], Mk = exp2(lM), lam = 1.0 + exp2(w.lmu);
-                w.zb = fmax(Mk * gap, fmax(Mk / Sd - fmax(0.0, 1.0 / St - lam / Sd), 1.0 / St - (lam + Mk) / Sd));
+                // 1 / S_t - lam / S_d = kappa / S_d, from the carried kappa once there is one
+                const double St = r.St[w.u], Sd = r.Sd[w.u], Mk = exp2(lM);
+                const double k_now = w.skap != 0 ? (w.lkap == -INFINITY ? 0.0 : w.skap * exp2(w.lkap))
+                                                 : Sd / St - 1.0;
+                const double k_next = kn.l == -INFINITY ? 0.0 : kn.s * exp2(kn.l);
+                w.zb = fmax(Mk * gap, fmax(Mk / Sd - fmax(0.0, k_now / Sd), k_next / Sd));
                 w.lmu = log2_add(w.lmu, lM);
+                w.skap = kn.s != 0 ? kn.s : 1;
+                w.lkap = kn.l;
             }
         }
         w.next = j + 1;
@@ -1258,11 +1342,13 @@ __device__ void tree_sample_decide(const StatsParams& p, int b, const SeqInfo& s
         w.u = 0;
         w.zb = -1.0;
         w.lmu = -INFINITY;
+        w.skap = 0;
+        w.lkap = -INFINITY;
         w.c = exp2_scale(si.T);
         w.flags = si.flags | s_bad;
         DrawDesc d;
         const float* uni = p.unif + (size_t)b * (n + 1);
-        if (tree_walk_run(w, r, L, V, uni, p.can_pend != 0, RoundStep{0.0, 0.0}, false, &d))
+        if (tree_walk_run(w, r, L, V, uni, p.can_pend != 0, RoundStep{0.0, 0.0, -INFINITY, 0}, false, &d))
             tree_walk_finish(w, d, s_x, n, uni[n], p.acc, p.emitted, p.path, p.desc, p.flags, b);
         else
             tree_walk_store(w, true, r, L, n, p.walk + b, p.trows + (size_t)b * tree_rows_layout(n).stride);
@@ -1479,7 +1565,7 @@ __device__ void decide(const StatsParams& p, int b, const SeqInfo& si) {
             // the draw (residual after a rejection, bonus after full acceptance)
             // is done by the draw pass
             if constexpr (DRAW) e[k] = -1;
-            DrawDesc d;
+            DrawDesc d{};  // skap = 0: kappa = S_d / S_t - 1, formed by the draw
             // a rejection whose residual mass may lie below the near form's
             // threshold (resid_mass_bound()) hands the draw the near form's sums
             const double zb = (k < L) ? resid_mass_bound(s_S[k], s_S[n + 1 + k], s_gap) : 0.0;
@@ -1703,29 +1789,54 @@ __device__ __forceinline__ float far_sum_at(const FarSums& s, int q) {
 // kappa = sum Dl / sum A - mu and each tile's weight W + (kappa - kappa0) G.
 // That is exact unless a token's crossing point lies between kappa0 and kappa;
 // the tokens the rows share all cross at kappa = 0, which the plan keeps apart.
-constexpr int kSumA = 0, kSumDl = 1;  // near form: the slots of sum P and sum Q
+// A tree walk's round needs kappa after the next rejection too, which the
+// chunks' sums give without a difference of nearly equal numbers (next_kappa()):
+// per tile they also hand over, over the tokens whose relative logits differ,
+// sum B and the sum of the positive weights at kappa0.  After two or more
+// rejections at a node the walk carries kappa itself (DrawDesc::skap), and
+// kappa0 is that value.
+constexpr int kSumA = 0, kSumDl = 1;   // near form: the slots of sum P and sum Q
+constexpr int kSumY = 4, kSumWd = 5;   // near form only
+struct NearSums {
+    float a, dl, w, g, y, wd;
+};
+__device__ __forceinline__ NearSums wave_near_sums(NearSums s) {
+    return NearSums{wave_sum(s.a), wave_sum(s.dl), wave_sum(s.w), wave_sum(s.g), wave_sum(s.y), wave_sum(s.wd)};
+}
+__device__ __forceinline__ float near_sum_at(const NearSums& s, int q) {
+    return q == 0 ? s.a : q == 1 ? s.dl : q == 2 ? s.w : q == 3 ? s.g : q == 4 ? s.y : s.wd;
+}
 struct NearLin {
     float kappa0, lam;
 };
 __device__ __forceinline__ NearLin near_lin(const DrawDesc& d) {
-    const double rho0 = fabs((double)d.lq) <= 0.25 ? (double)exp2m1_small(-d.lq) : exp2(-(double)d.lq) - 1.0;
     const double mu = desc_mu(d);
+    if (d.skap != 0) return NearLin{(float)desc_kappa(d, 0.0), (float)(1.0 + mu)};
+    const double rho0 = fabs((double)d.lq) <= 0.25 ? (double)exp2m1_small(-d.lq) : exp2(-(double)d.lq) - 1.0;
     return NearLin{(float)(rho0 - mu), (float)(1.0 + mu)};
 }
-__device__ __forceinline__ void near_accum(FarSums& s, const DrawDesc& d, const NearLin& nl, float zt, float zd) {
+__device__ __forceinline__ void near_accum(NearSums& s, const DrawDesc& d, const NearLin& nl, float zt, float zd) {
     // near_term() with no shift (the powers of (a - 0) c are those of a c)
     const float at = near_rel(zt, d.m_t), ad = near_rel(zd, d.m_d);
     const float A = exp2_fast(at * d.c);
-    float Dl = 0.f;
+    float Dl = 0.f, B = 0.f;
     if (at != ad) {
         const float x = (ad - at) * d.c;
-        Dl = fabsf(x) <= 0.25f ? A * exp2m1_small(x) : exp2_fast(ad * d.c) - A;
+        if (fabsf(x) <= 0.25f) {
+            Dl = A * exp2m1_small(x);
+            B = A + Dl;
+        } else {
+            B = exp2_fast(ad * d.c);
+            Dl = B - A;
+        }
     }
     const float w0 = fmaf(nl.kappa0, A, -nl.lam * Dl);
-    s.p += A;
-    s.q += Dl;
+    s.a += A;
+    s.dl += Dl;
     s.w += fmaxf(w0, 0.f);
     s.g += w0 > 0.f ? A : 0.f;
+    s.y += B;
+    s.wd += (at != ad && w0 > 0.f) ? w0 : 0.f;
 }
 
 // What plan_residual() decided besides the tile weights and the element
@@ -1738,6 +1849,12 @@ struct ResidPlan {
     double Z, mass, lmass, sq, kappa, lam;
     double sh;   // near form: 2^(-sl c), the unit of its differences (binary64; may be +inf)
     bool exact;  // the near form by the deciding workgroup alone (near_exact_tiles())
+    // near form, for next_kappa(): over the tokens whose relative logits differ,
+    // yd = sum B and lwd = log2 sum max(0, kappa A - lam Dl), in units of 2^lu
+    // (lu = sl c, 0 for the chunks' sums); kappa in those units as sign ks and
+    // log2 |kappa| lk
+    double yd, lwd, lu, lk;
+    int ks;
 };
 
 // The near form of one row pair, formed by one workgroup from the rows
@@ -1759,9 +1876,31 @@ __device__ float block_max_f_all(float v) {
     __syncthreads();
     return v;
 }
+// Two maxima over the workgroup, the same values in every thread.
+__device__ void block_max2_d_all(double& a, double& b) {
+    __shared__ double sh[2][kWaves];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        a = fmax(a, __shfl_xor(a, off, 64));
+        b = fmax(b, __shfl_xor(b, off, 64));
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        sh[0][w] = a;
+        sh[1][w] = b;
+    }
+    __syncthreads();
+    a = sh[0][0];
+    b = sh[1][0];
+    for (int i = 1; i < kWaves; ++i) {
+        a = fmax(a, sh[0][i]);
+        b = fmax(b, sh[1][i]);
+    }
+    __syncthreads();
+}
 template <int DT, bool ALIGNED>
 __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int NT, const DrawDesc& d, double* s_w,
-                                 WSpec* ws, ResidPlan* pl) {
+                                 WSpec* ws, ResidPlan* pl, bool need_next) {
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     constexpr int kU = kThreads / 64;
@@ -1805,6 +1944,28 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
             }
         }
     };
+    // the same elements one vector of each row at a time (the cold log2 passes,
+    // whose element math is longest)
+    auto visit1 = [&](int t, int u0, auto&& f) {
+        if constexpr (ALIGNED) {
+            const int e0 = t * kTile + (lane + 64 * u0) * kVec;
+            const uint4 wt = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+            const uint4 wd = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t a = q == 0 ? wt.x : q == 1 ? wt.y : q == 2 ? wt.z : wt.w;
+                const uint32_t b = q == 0 ? wd.x : q == 1 ? wd.y : q == 2 ? wd.z : wd.w;
+                if constexpr (DT == kBF16) {
+                    f(bf16_lo(a), bf16_lo(b));
+                    f(bf16_hi(a), bf16_hi(b));
+                } else {
+                    f(__uint_as_float(a), __uint_as_float(b));
+                }
+            }
+        } else {
+            visit(t, u0, f);
+        }
+    };
     float sl = -INFINITY;
     for (int t = w; t < NT; t += kWaves)
         for (int u0 = 0; u0 < kU; u0 += kH)
@@ -1813,50 +1974,130 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
                 if (at != ad) sl = fmaxf(sl, fmaxf(at, ad));
             });
     sl = block_max_f_all(sl);
-    double X = 0.0, D = 0.0;
+    double X = 0.0, D = 0.0, Y = 0.0, unused = 0.0;
     for (int t = w; t < NT; t += kWaves) {
-        float sx = 0.f, sd = 0.f;
+        float sx = 0.f, sd = 0.f, sy = 0.f;
         for (int u0 = 0; u0 < kU; u0 += kH)
             visit(t, u0, [&](float zt, float zd) {
                 const NearTerm tm = near_term(m_t, m_d, sl, c, zt, zd);  // absent elements: terms 0
                 sx += tm.A;
                 sd += tm.Dl;
+                sy += tm.Bs;
             });
         X += (double)wave_sum(sx);
         D += (double)wave_sum(sd);
+        Y += (double)wave_sum(sy);
     }
-    if (lane != 0) X = D = 0.0;  // every lane of a wave holds the wave's sums
+    if (lane != 0) X = D = Y = 0.0;  // every lane of a wave holds the wave's sums
     block_sum2_all(X, D);
+    block_sum2_all(Y, unused);
     const double rho = X > 0.0 ? D / X : 0.0;
-    const double sig = (double)sl * (double)c;                 // the shift, log2 units
-    const double scale = sl > -INFINITY ? exp2(sig) : 0.0;     // 2^(sl c), binary64
-    const double lmu = desc_lmu(d);
-    double mus = 0.0;  // mu 2^(-sl c)
-    if (lmu > -INFINITY) mus = sl > -INFINITY ? exp2(lmu - sig) : (double)FLT_MAX;
-    const double kappa = rho - mus, lam = 1.0 + desc_mu(d);
-    const float kappa_f = (float)fmax(kappa, -(double)FLT_MAX), lam_f = (float)lam;
+    const double sig = sl > -INFINITY ? (double)sl * (double)c : 0.0;  // the shift, log2 units
+    const double scale = sl > -INFINITY ? exp2(sig) : 0.0;              // 2^(sl c), binary64
+    // kappa in units of 2^(sl c): carried by a tree walk (after two or more
+    // rejections at a node), else rho - mu 2^(-sl c) (mu = 0 after one rejection)
+    double kappa;
+    if (d.skap != 0) {
+        kappa = desc_kappa(d, sig);
+    } else {
+        const double lmu = desc_lmu(d);
+        double mus = 0.0;  // mu 2^(-sl c)
+        if (lmu > -INFINITY) mus = sl > -INFINITY ? exp2(lmu - sig) : (double)FLT_MAX;
+        kappa = rho - mus;
+    }
+    const double lam = 1.0 + desc_mu(d);
+    const float kappa_f = (float)fmin(fmax(kappa, -(double)FLT_MAX), (double)FLT_MAX), lam_f = (float)lam;
     *ws = WSpec{kWResNear, c, m_t, m_d, lam_f, kappa_f, sl, 0.f, 0.f};
-    double zsum = 0.0, unused = 0.0;
+    double zsum = 0.0, wdsum = 0.0;
     for (int t = w; t < NT; t += kWaves) {
-        float sw = 0.f;
+        float sw = 0.f, swd = 0.f;
         for (int u0 = 0; u0 < kU; u0 += kH)
-            visit(t, u0, [&](float zt, float zd) { sw += near_weight(m_t, m_d, sl, c, kappa_f, lam_f, zt, zd); });
+            visit(t, u0, [&](float zt, float zd) {
+                const float wt = near_weight(m_t, m_d, sl, c, kappa_f, lam_f, zt, zd);
+                sw += wt;
+                if (near_rel(zt, m_t) != near_rel(zd, m_d)) swd += wt;
+            });
         sw = wave_sum(sw);
+        swd = wave_sum(swd);
         if (lane == 0) {
             s_w[t] = (double)sw;
             zsum += (double)sw;
+            wdsum += (double)swd;
         }
     }
-    block_sum2_all(zsum, unused);
+    block_sum2_all(zsum, wdsum);
     const double Sd = X * (1.0 + rho * scale);  // the draft row's sum in A's units
+    // kappa as sign and log2 (a carried kappa without forming 2^(lkap - sl c))
+    int ks;
+    double lk;
+    if (d.skap != 0) {
+        ks = d.lkap == -INFINITY ? 0 : d.skap;
+        lk = d.lkap - sig;
+    } else {
+        ks = kappa > 0.0 ? 1 : kappa < 0.0 ? -1 : 0;
+        lk = kappa != 0.0 ? log2(fabs(kappa)) : -INFINITY;
+    }
+    double lz = zsum > 0.0 ? log2(zsum) : -INFINITY, lwd = wdsum > 0.0 ? log2(wdsum) : -INFINITY;
+    // binary32 terms in units of 2^(sl c) may have lost every weight that decides
+    // the draw (their total far below 1), or, for a round, the comparison of
+    // kappa Y with W (both far below 1): the weights are re-formed from their
+    // log2 (near_log_weight()), scaled by 2^-E with E the largest (an integer)
+    const bool log_draw = !(zsum > 0x1p-100);
+    const bool log_w = need_next && !(wdsum > 0x1p-90) && ks > 0 && !(lk + sig + log2(Y) > -90.0);
+    if (log_draw || log_w) {
+        WSpec wl{kWResNearLog, c, m_t, m_d, lam_f, 0.f, sl, 0.f, 0.f, ks, lk, sig, 0.0};
+        double E = -INFINITY, Ed = -INFINITY;  // the largest log2 weight; over the differing tokens
+        for (int t = w; t < NT; t += kWaves)
+            for (int u0 = 0; u0 < kU; ++u0)
+                visit1(t, u0, [&](float zt, float zd) {
+                    const double lw = near_log_weight(wl, zt, zd);
+                    E = fmax(E, lw);
+                    if (near_rel(zt, m_t) != near_rel(zd, m_d)) Ed = fmax(Ed, lw);
+                });
+        block_max2_d_all(E, Ed);
+        E = E > -INFINITY ? floor(E) : 0.0;
+        Ed = Ed > -INFINITY ? floor(Ed) : -INFINITY;
+        wl.E = E;
+        double zl = 0.0, wdl = 0.0;
+        for (int t = w; t < NT; t += kWaves) {
+            float sw = 0.f, swd = 0.f;
+            for (int u0 = 0; u0 < kU; ++u0)
+                visit1(t, u0, [&](float zt, float zd) {
+                    const double lw = near_log_weight(wl, zt, zd);
+                    if (lw > -INFINITY) {
+                        sw += exp2_fast((float)(lw - E));
+                        if (near_rel(zt, m_t) != near_rel(zd, m_d)) swd += exp2_fast((float)(lw - Ed));
+                    }
+                });
+            sw = wave_sum(sw);
+            swd = wave_sum(swd);
+            if (lane == 0) {
+                if (log_draw) s_w[t] = (double)sw;
+                zl += (double)sw;
+                wdl += (double)swd;
+            }
+        }
+        block_sum2_all(zl, wdl);
+        lwd = wdl > 0.0 ? Ed + log2(wdl) : -INFINITY;
+        if (log_draw) {
+            *ws = wl;
+            zsum = zl;
+            lz = zl > 0.0 ? E + log2(zl) : -INFINITY;
+        }
+    }
     pl->Z = zsum;
     pl->sq = Sd;
     pl->kappa = kappa;
     pl->lam = lam;
     pl->sh = sl > -INFINITY ? exp2(-sig) : 1.0;
     pl->exact = true;
-    pl->mass = X > 0.0 ? scale * zsum / Sd : 0.0;
-    pl->lmass = (X > 0.0 && zsum > 0.0) ? sig + log2(zsum / Sd) : -INFINITY;
+    pl->lmass = (X > 0.0 && lz > -INFINITY) ? sig + lz - log2(Sd) : -INFINITY;
+    pl->mass = pl->lmass > -INFINITY ? exp2(pl->lmass) : 0.0;
+    pl->yd = Y;
+    pl->lwd = lwd;
+    pl->lu = sig;
+    pl->lk = lk;
+    pl->ks = ks;
 }
 
 // The residual draw's set-up in the deciding workgroup, from the far-form tile
@@ -1864,10 +2105,12 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
 // lam = 1 + mu (mu from d.mu): the tile weights into
 // s_w[NT], the element weighting into *ws, the rest into *pl (with no residual
 // mass left, s_w holds the target's own tile masses and *ws weighs by the
-// target).
+// target).  need_next: a tree walk's round, which also needs kappa after the
+// next rejection (next_kappa()), so the chunks' near form is trusted only where
+// its sums over the differing tokens lie far inside the binary32 range.
 template <int DT, bool ALIGNED, int TPT>
-__device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& d, const void* trow, const void* drow,
-                              int V, double* s_w, WSpec* ws, ResidPlan* pl) {
+__device__ __forceinline__ void plan_residual(const float (&v)[TPT][kDrawSums], int NT, const DrawDesc& d, const void* trow,
+                              const void* drow, int V, double* s_w, WSpec* ws, ResidPlan* pl, bool need_next) {
     const int tid = threadIdx.x;
     const double lq = 1.0 + desc_mu(d);  // lam
     double sp = 0.0, sq = 0.0;           // far form: sum P, sum Q; near form: sum A, sum Dl
@@ -1880,10 +2123,12 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
     double zr = 0.0, zp = 0.0;
     bool exact = false;  // the near form by this workgroup alone
     if (d.kind == kDrawResidualNear) {
-        // the chunks' near-form sums (near_lin()): kappa = sum Dl / sum A - mu
+        // the chunks' near-form sums (near_lin()): kappa carried by a tree walk,
+        // else sum Dl / sum A - mu
         const NearLin nl = near_lin(d);
-        const double kappa = sp > 0.0 ? sq / sp - desc_mu(d) : 0.0;
+        const double kappa = d.skap != 0 ? desc_kappa(d, 0.0) : sp > 0.0 ? sq / sp - desc_mu(d) : 0.0;
         const double dk = kappa - (double)nl.kappa0;
+        double yd = 0.0, wd = 0.0;
 #pragma unroll
         for (int r = 0; r < TPT; ++r) {
             const int i = tid + r * kThreads;
@@ -1893,18 +2138,25 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
                 s_w[i] = w;
                 zr += w;
                 zp += (double)v[r][kSumA];
+                yd += (double)v[r][kSumY];
+                wd += (double)v[r][kSumWd];
             }
         }
         block_sum2_all(zr, zp);
+        block_sum2_all(yd, wd);
         // trusted when the tokens the rows share (crossing at kappa = 0) lie on
         // one side of both kappa0 and kappa with room to spare, and the mass is
-        // far above what binary32 terms without a shift can carry
-        const bool ok = sp > 0.0 && kappa * (double)nl.kappa0 > 0.0 && fabs(kappa) > 4.0 * fabs(dk) &&
-                        zr > 0x1p-60 * sp;
+        // far above what binary32 terms without a shift can carry (for a round,
+        // the differing tokens' draft mass and kappa times it too)
+        bool ok = sp > 0.0 && kappa * (double)nl.kappa0 > 0.0 && fabs(kappa) > 4.0 * fabs(dk) &&
+                  zr > 0x1p-60 * sp;
+        if (need_next) ok = ok && yd > 0x1p-80 * sp && (kappa <= 0.0 || kappa * yd > 0x1p-80 * sp);
         if (ok) {
             *ws = WSpec{kWResNear, d.c, d.m_t, d.m_d, nl.lam, (float)kappa, 0.f, 0.f, 0.f};
             const double Sd = sp + sq;  // S_d = sum B = sum A + sum Dl
-            *pl = ResidPlan{zr, zr / Sd, log2(zr / Sd), Sd, kappa, (double)nl.lam, 1.0, false};
+            *pl = ResidPlan{zr,    zr / Sd, log2(zr / Sd), Sd, kappa, (double)nl.lam, 1.0, false, yd,
+                            wd > 0.0 ? log2(wd) : -INFINITY, 0.0, kappa != 0.0 ? log2(fabs(kappa)) : -INFINITY,
+                            kappa > 0.0 ? 1 : -1};
         } else {
             exact = true;
         }
@@ -1925,12 +2177,12 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
         block_sum2_all(zr, zp);
         *ws = WSpec{kWResFar, d.c, d.m_t, d.m_d, (float)Lam, 0.f, 0.f, neg_scaled(d.m_t, d.c), neg_scaled(d.m_d, d.c)};
         *pl = ResidPlan{zr, sp > 0.0 ? zr / sp : 0.0, (sp > 0.0 && zr > 0.0) ? log2(zr / sp) : -INFINITY, sq, 0.0, 0.0,
-                        1.0, false};
+                        1.0, false, 0.0, -INFINITY, 0.0, -INFINITY, 0};
         exact = sq > 0.0 && zr < kNearZ * sp;  // a small residual after all
     }
     if (exact) {
         __syncthreads();
-        near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, d, s_w, ws, pl);
+        near_exact_tiles<DT, ALIGNED>(trow, drow, V, NT, d, s_w, ws, pl, need_next);
         zr = pl->Z;
     }
     if (!(zr > 0.0)) {
@@ -1942,7 +2194,7 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
             if (i < NT) s_w[i] = (double)v[r][kSumP];
         }
         *ws = target_spec(d);
-        *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0, 1.0, false};
+        *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0, 1.0, false, 0.0, -INFINITY, 0.0, -INFINITY, 0};
     }
     __syncthreads();
 }
@@ -1956,6 +2208,14 @@ __device__ void plan_residual(const float (&v)[TPT][4], int NT, const DrawDesc& 
 // both give w sq / (Z q') with q' = Q or B.  q(x) = 0 < p(x) - lam q(x): +inf.
 __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& pl, float zt, float zd) {
     if (!(pl.Z > 0.0) || ws.mode == kWTarget) return 0.0;
+    if (ws.mode == kWResNearLog) {
+        // w S_d / (Z B) from the log2 weight: Z = 2^E sum in units of 2^(sl c)
+        const float ad = near_rel(zd, ws.m_d);
+        if (ad == -INFINITY) return near_rel(zt, ws.mA) == -INFINITY ? 0.0 : INFINITY;  // q(x) = 0
+        const double lw = near_log_weight(ws, zt, zd);
+        if (lw == -INFINITY) return 0.0;
+        return exp2(lw - (ws.E + log2(pl.Z)) + log2(pl.sq) - (double)ad * (double)ws.c);
+    }
     double w, q;
     if (ws.mode == kWResFar) {
         const float P = far_p(ws.nmt, ws.c, zt), Q = far_p(ws.nmd, ws.c, zd);
@@ -2021,6 +2281,12 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
         const int t = wv * kTilesPerWave + i;
         if (lane < 4 && t < cnt) dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(far_sum_at(fs, lane)));
     };
+    auto hand_over_near = [&](int i, NearSums ns) {
+        ns = wave_near_sums(ns);
+        const int t = wv * kTilesPerWave + i;
+        if (lane < kDrawSums && t < cnt)
+            dep ^= xchg32(dsum + (size_t)lane * NT + tile0 + t, __float_as_uint(near_sum_at(ns, lane)));
+    };
     if (d.kind == kDrawResidualNear) {
         // the near form's sums (near_lin()), every vector of the chunk in flight
         // before the first use; the element math is long, so four elements of
@@ -2033,7 +2299,7 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
             for (int u = 0; u < kU; ++u) load(i, u, rt[i][u], rd[i][u]);
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) {
-            FarSums fs{0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
+            NearSums fs{0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // absent elements read -inf on both rows: every term is 0
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
 #pragma unroll 4
@@ -2050,7 +2316,7 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
                     }
                 }
             }
-            hand_over(i, fs);
+            hand_over_near(i, fs);
         }
     } else {
         // the far form's sums, every vector of the chunk in flight before the first use
@@ -2081,13 +2347,15 @@ __device__ __forceinline__ void residual_chunk(const void* trow, const void* dro
 constexpr int kTPT = kMaxTiles / kThreads;  // tiles per thread, at most, in the deciding workgroup
 
 // The deciding workgroup collects (and resets to zero) the tile sums of the whole
-// row pair: v[r][q] = sum q of tile tid + r kThreads.
-__device__ __forceinline__ void collect_tile_sums(float (&v)[kTPT][4], int NT, unsigned* dsum) {
+// row pair: v[r][q] = sum q of tile tid + r kThreads, the first nq sums (the far
+// form hands over 4, the near form kDrawSums; the rest read 0).
+__device__ __forceinline__ void collect_tile_sums(float (&v)[kTPT][kDrawSums], int NT, unsigned* dsum, int nq) {
 #pragma unroll
     for (int r = 0; r < kTPT; ++r) {
         const int i = threadIdx.x + r * kThreads;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[r][q] = (i < NT) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
+        for (int q = 0; q < kDrawSums; ++q)
+            v[r][q] = (i < NT && q < nq) ? __uint_as_float(xchg32(dsum + (size_t)q * NT + i, 0u)) : 0.f;
     }
 }
 
@@ -2120,11 +2388,11 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     if (!s_last) return;
 
     // last workgroup: collect (and reset) the per-tile sums of the whole row pair
-    float v[kTPT][4];
-    collect_tile_sums(v, NT, dsum);
+    float v[kTPT][kDrawSums];
+    collect_tile_sums(v, NT, dsum, d.kind == kDrawResidualNear ? kDrawSums : 4);
     WSpec ws;
     ResidPlan pl;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl);
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl, false);
     const double Z = pl.Z;
     if (!has_draft) ws = target_spec(d);  // weights P: the target row's own distribution
     if (Z <= 0.0 && tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
@@ -2149,6 +2417,35 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
         p.desc[b] = DrawDesc{};
         xchg32(&p.cnt[b], 0u);
     }
+}
+
+// kappa_{k+1} = kappa_k - M_k from the residual the round formed at lam_k.  The
+// near form has the sums over the tokens whose relative logits differ, Y = sum B
+// and W = sum max(0, kappa_k A - lam_k Dl), while the tokens the rows share
+// contribute max(0, kappa_k) times their own sum to M_k S_d and their sum is
+// S_d - Y, so
+//   kappa_{k+1} = (kappa_k Y - W) / S_d  (kappa_k > 0),  kappa_k - W / S_d  (else):
+// no difference of nearly equal numbers is formed unless kappa_k Y and W are
+// themselves that close.  The far form (mass above the near form's threshold,
+// where the difference keeps its digits) and a residual with no mass left
+// (M_k = 0) take kappa_k - M_k in binary64.
+__device__ __forceinline__ SLog2 next_kappa(const DrawDesc& d, const WSpec& ws, const ResidPlan& pl, double St,
+                                           double Sd) {
+    if ((ws.mode == kWResNear || ws.mode == kWResNearLog) && pl.Z > 0.0) {
+        SLog2 r;
+        if (pl.ks > 0) {
+            const SLog2 ky{1, pl.yd > 0.0 ? pl.lk + pl.lu + log2(pl.yd) : -INFINITY};
+            r = slog2_add(ky, SLog2{-1, pl.lwd});
+        } else {
+            // -(|kappa_k| S_d + W)
+            r = SLog2{-1, log2_add(pl.ks != 0 ? pl.lk + log2(pl.sq) : -INFINITY, pl.lwd)};
+        }
+        if (r.l == -INFINITY) return SLog2{1, -INFINITY};
+        return SLog2{r.s, r.l + pl.lu - log2(pl.sq)};
+    }
+    const double kk = d.skap != 0 ? desc_kappa(d, 0.0) : Sd / St - 1.0;
+    const double M = (ws.mode != kWTarget && pl.Z > 0.0) ? exp2(pl.lmass) : 0.0;
+    return slog2_of(kk - M);
 }
 
 // One round of the sampling tree walks, workgroup (b, c): if sequence b's walk
@@ -2177,6 +2474,8 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     d.m_d = gmd[u];
     d.lq = (float)log2(gSt[u] / gSd[u]);
     d.mu = encode_mu(gw->lmu);
+    d.skap = gw->skap;
+    d.lkap = gw->lkap;
     const void* trow = row_ptr<DT>(p.target, (long long)b * (n + 1) + u, V);
     const void* drow = row_ptr<DT>(p.draft, (long long)b * n + u, V);
     unsigned* dsum = reinterpret_cast<unsigned*>(p.dsum) + (size_t)b * kDrawSums * NT;
@@ -2187,11 +2486,11 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
     __syncthreads();
     if (!s_last) return;
 
-    float v[kTPT][4];
-    collect_tile_sums(v, NT, dsum);
+    float v[kTPT][kDrawSums];
+    collect_tile_sums(v, NT, dsum, d.kind == kDrawResidualNear ? kDrawSums : 4);
     WSpec ws;
     ResidPlan pl;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl);
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl, true);
     // the pending test: the walk's next child at u, under this residual (the
     // plan goes through LDS, so its registers are free for the ratio's binary64 math)
     __shared__ RoundStep s_step;
@@ -2202,7 +2501,8 @@ __device__ __forceinline__ void round_item(const RoundParams& p, int b, int c, d
         s_pl = pl;
     }
     if (tid == 0) {
-        RoundStep st{0.0, s_pl.lmass};
+        const SLog2 kn = next_kappa(d, s_ws, s_pl, gSt[u], gSd[u]);
+        RoundStep st{0.0, s_pl.lmass, kn.l, kn.s};
         const int* par = p.parents + (size_t)b * n;
         const int L0 = min(max(p.lens[b], 0), n);
         for (int t = gw->next; t < L0; ++t)
@@ -2384,7 +2684,7 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
     d.lq = (float)log2((double)s_t.s / (double)s_d.s);
     const float lam0 = exp2_fast(d.lq);
     const float nmt = neg_scaled(d.m_t, c), nmd = neg_scaled(d.m_d, c);
-    __shared__ float s_sum[4][kMaxTiles];
+    __shared__ float s_sum[kDrawSums][kMaxTiles];
     for (int t = w; t < NT; t += kWaves) {
         FarSums fs{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -2412,7 +2712,7 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
         d.kind = kDrawResidualNear;
         const NearLin nl = near_lin(d);
         for (int t = w; t < NT; t += kWaves) {
-            FarSums fs{0.f, 0.f, 0.f, 0.f};
+            NearSums fs{0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int u = 0; u < kU; ++u) {
                 float zt[kVec], zd[kVec];
                 const int e0 = t * kTile + (lane + 64 * u) * kVec;
@@ -2421,29 +2721,30 @@ __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target,
 #pragma unroll 1
                 for (int e = 0; e < kVec; ++e) near_accum(fs, d, nl, zt[e], zd[e]);
             }
-            fs = wave_far_sums(fs);
-            if (lane < 4) s_sum[lane][t] = far_sum_at(fs, lane);
+            fs = wave_near_sums(fs);
+            if (lane < kDrawSums) s_sum[lane][t] = near_sum_at(fs, lane);
         }
         __syncthreads();
     }
-    float v[kTPT][4];
+    float v[kTPT][kDrawSums];
+    const int nq = d.kind == kDrawResidualNear ? kDrawSums : 4;
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
         const int i = tid + q * kThreads;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[q][k] = (i < NT) ? s_sum[k][i] : 0.f;
+        for (int k = 0; k < kDrawSums; ++k) v[q][k] = (i < NT && k < nq) ? s_sum[k][i] : 0.f;
     }
     __shared__ double s_w[kMaxTiles];
     WSpec ws;
     ResidPlan pl;
-    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &pl);
-    const bool near = ws.mode == kWResNear;
+    plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_w, &ws, &pl, false);
+    const bool near = ws.mode == kWResNear || ws.mode == kWResNearLog;
     if (tile_out)
         for (int i = tid; i < NT; i += kThreads) tile_out[(size_t)r * NT + i] = s_w[i];
     for (int i = tid; i < V; i += kThreads)
         w_out[(size_t)r * V + i] = elem_weight(ws, load_elem<DT>(trow, i), load_elem<DT>(drow, i));
     if (info_out && tid == 0) {
-        info_out[(size_t)r * 4 + 0] = near ? (pl.exact ? 2.f : 1.f) : 0.f;
+        info_out[(size_t)r * 4 + 0] = ws.mode == kWResNearLog ? 3.f : near ? (pl.exact ? 2.f : 1.f) : 0.f;
         info_out[(size_t)r * 4 + 1] = ws.mode == kWResFar ? ws.lam : 0.f;
         info_out[(size_t)r * 4 + 2] = near ? ws.kappa : 0.f;
         info_out[(size_t)r * 4 + 3] = (float)pl.mass;

@@ -321,7 +321,7 @@ sv_status_t spec_verify_sample_ex(const void *target_logits, const void *draft_l
  * The workspace is a device array of SV_NOALLOC_SCRATCH_BYTES bytes inside the
  * library, one per GPU, held until the process ends.  Sizes whose
  * sv_workspace_bytes(B, n, V, dt) exceed it return SV_EWORKSPACE before anything
- * is touched (B up to 6563 at n = 8, V = 152064 bf16; 8081 at n = 4, V = 128256).  The first
+ * is touched (B up to 5262 at n = 8, V = 152064 bf16; 6422 at n = 4, V = 128256).  The first
  * call on a GPU enqueues a clear of the array (a kernel) on `stream`; every
  * call leaves it zero-filled again.  All calls on one GPU share the array, so
  * calls that overlap in time on one GPU (different streams, or threads) race

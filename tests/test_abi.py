@@ -314,6 +314,6 @@ def test_noalloc_capacity_as_documented():
     text = open(HEADER).read()
     cap = 16 << 20
     assert "SV_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
-    for B, n, V in ((6563, 8, 152064), (8081, 4, 128256)):
+    for B, n, V in ((5262, 8, 152064), (6422, 4, 128256)):
         assert f"{B} at n = {n}" in text or f"B up to {B} at n = {n}" in text, B
         assert sv.sv_workspace_bytes(B, n, V, sv.SV_BF16) <= cap < sv.sv_workspace_bytes(B + 1, n, V, sv.SV_BF16)

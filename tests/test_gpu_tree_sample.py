@@ -255,3 +255,60 @@ def test_confident_rows_take_the_near_form(oracle):
     d["uniforms"][:, :n] = (1.0 - (1.0 - d["uniforms"][:, :n]) ** 8).clamp_(max=1.0 - 2.0 ** -24)  # mostly rejections
     acc, fl = _compare(oracle, d, _rounds(d), tag="confident rows")
     assert fl == 0
+
+
+@pytest.mark.parametrize("T", [0.002, 0.005, 0.01, 0.02])
+@pytest.mark.parametrize("V", [5814, 6144])
+def test_repeated_rejections_at_low_temperature(oracle, T, V):
+    """Drafts that are the target plus N(0, 0.003^2) in bf16 (most tokens keep
+    the target's logit, the top token among them), tokens drawn from the
+    draft's own rows (at low T mostly its top token, so siblings repeat), and
+    uniforms pushed towards 1 (mostly rejections): after two or more
+    rejections at a node the weight of the tokens the rows share is a product
+    of two tails set against first-order terms, which the walk carries as
+    kappa = S_d / S_t - lam.  Outputs against the oracle, walk by walk; V = 5814
+    takes the element-wise loads."""
+    B, n = 64, 12
+    seed = 900 + int(T * 1e4) + V
+    d = synth.make_tree_sample(seed, device=DEV, B=B, n=n, V=V, shape="random", temps=(T,))
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    d["draft"] = (d["target"][:, :n].float() + 0.003 * torch.randn((B, n, V), generator=g, device=DEV)).to(
+        d["draft"].dtype).contiguous()
+    d["uniforms"][:, :n] = (1.0 - (1.0 - d["uniforms"][:, :n]) ** 6).clamp_(max=1.0 - 2.0 ** -24)
+    _compare(oracle, d, _rounds(d), tag=f"repeated rejections T={T} V={V}")
+
+
+@pytest.mark.parametrize("embed", [False, True])
+def test_six_token_trees_at_low_temperature(oracle, embed):
+    """The six-token trees the oracle is pinned on against exact arithmetic
+    (rows sharing their top token, repeated and distinct siblings, T from 0.003
+    to 1), bare (element-wise loads) and embedded in 4096-token rows whose
+    other entries are -inf in both rows (16-byte loads)."""
+    import importlib.util, os
+    spec = importlib.util.spec_from_file_location(
+        "tree_exact", os.path.join(os.path.dirname(__file__), "test_oracle_tree_exact.py"))
+    te = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(te)
+    rng = np.random.default_rng(20261203)
+    temps = [0.003, 0.01, 0.03, 0.1, 1.0]
+    cases = [te._case(rng) for _ in range(300)]
+    zt = np.stack([c[0] for c in cases])
+    zd = np.stack([c[1] for c in cases])
+    x = np.stack([c[2] for c in cases])
+    par = np.stack([c[3] for c in cases])
+    B, n = x.shape
+    temp = np.array([temps[i % len(temps)] for i in range(B)], np.float32)
+    u = rng.random((B, n + 1)).astype(np.float32)
+    if embed:
+        where = np.array([5, 700, 1501, 2048, 3333, 4095])
+        big_t = np.full((B, n + 1, 4096), -np.inf, np.float32)
+        big_d = np.full((B, n, 4096), -np.inf, np.float32)
+        big_t[..., where] = zt
+        big_d[..., where] = zd
+        zt, zd, x = big_t, big_d, where[x].astype(np.int32)
+    d = {"target": torch.as_tensor(zt, device=DEV).to(torch.bfloat16).contiguous(),
+         "draft": torch.as_tensor(zd, device=DEV).to(torch.bfloat16).contiguous(),
+         "draft_tokens": torch.as_tensor(x, device=DEV), "draft_parents": torch.as_tensor(par, device=DEV),
+         "parents_host": par, "draft_lens": torch.full((B,), n, dtype=torch.int32, device=DEV),
+         "temperature": torch.as_tensor(temp, device=DEV), "uniforms": torch.as_tensor(u, device=DEV)}
+    _compare(oracle, d, _rounds(d), tag=f"six-token trees embed={embed}")
