@@ -2216,31 +2216,32 @@ __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& 
         if (lw == -INFINITY) return 0.0;
         return exp2(lw - (ws.E + log2(pl.Z)) + log2(pl.sq) - (double)ad * (double)ws.c);
     }
-    double w, q;
     if (ws.mode == kWResFar) {
-        const float P = far_p(ws.nmt, ws.c, zt), Q = far_p(ws.nmd, ws.c, zd);
-        w = (double)P - (double)ws.lam * (double)Q;
-        q = (double)Q;
-    } else {
-        // w / B with r = A / B = 2^((at - ad) c): w / B = kappa r - lam (1 - r) 2^(-sl c)
-        // (a token the rows share has r = 1 and no second term)
-        const float at = near_rel(zt, ws.mA), ad = near_rel(zd, ws.m_d);
-        if (ad == -INFINITY) return at == -INFINITY ? 0.0 : INFINITY;  // q(x) = 0
-        if (at == -INFINITY) return 0.0;                                  // p(x) = 0 < q(x)
-        double wb = pl.kappa;
-        if (at != ad) {
-            // 1 - r in binary64 keeps about 16 - log10(1 / |xr|) digits, and two
-            // distinct binary32 relative logits give |xr| far above 1e-8
-            const double xr = ((double)at - (double)ad) * (double)ws.c;
-            const double r = exp2(xr), sh = pl.sh;  // sh = 2^(-sl c) >= 1
-            if (!(r < INFINITY)) return pl.kappa + pl.lam * sh > 0.0 ? INFINITY : 0.0;  // w / B = r (kappa + lam sh) - lam sh
-            wb = pl.kappa * r - pl.lam * (1.0 - r) * sh;
-        }
-        return wb > 0.0 ? wb * pl.sq / pl.Z : 0.0;
+        // (P - Lam Q) sq / (Z Q) = (P / Q - Lam) sq / Z, with P / Q from the exponents in
+        // binary64, so that the ratio keeps its value where P and Q lie below the
+        // binary32 range (a token far below both rows' maxima at low T)
+        if (zt == -INFINITY) return 0.0;       // p(x) = 0
+        if (zd == -INFINITY) return INFINITY;  // q(x) = 0 < p(x)
+        const double c = (double)ws.c;
+        const double lpq = ((double)zt * c + (double)ws.nmt) - ((double)zd * c + (double)ws.nmd);
+        const double v = exp2(lpq) - (double)ws.lam;
+        return v > 0.0 ? v * pl.sq / pl.Z : 0.0;
     }
-    if (!(w > 0.0)) return 0.0;
-    if (!(q > 0.0)) return INFINITY;
-    return w * pl.sq / (pl.Z * q);
+    // near form: w / B with r = A / B = 2^((at - ad) c): w / B = kappa r - lam (1 - r) 2^(-sl c)
+    // (a token the rows share has r = 1 and no second term)
+    const float at = near_rel(zt, ws.mA), ad = near_rel(zd, ws.m_d);
+    if (ad == -INFINITY) return at == -INFINITY ? 0.0 : INFINITY;  // q(x) = 0
+    if (at == -INFINITY) return 0.0;                                  // p(x) = 0 < q(x)
+    double wb = pl.kappa;
+    if (at != ad) {
+        // 1 - r in binary64 keeps about 16 - log10(1 / |xr|) digits, and two
+        // distinct binary32 relative logits give |xr| far above 1e-8
+        const double xr = ((double)at - (double)ad) * (double)ws.c;
+        const double r = exp2(xr), sh = pl.sh;  // sh = 2^(-sl c) >= 1
+        if (!(r < INFINITY)) return pl.kappa + pl.lam * sh > 0.0 ? INFINITY : 0.0;  // w / B = r (kappa + lam sh) - lam sh
+        wb = pl.kappa * r - pl.lam * (1.0 - r) * sh;
+    }
+    return wb > 0.0 ? wb * pl.sq / pl.Z : 0.0;
 }
 
 // One chunk of a residual reduction of the pair (trow, drow) (drow unused when

@@ -312,3 +312,32 @@ def test_six_token_trees_at_low_temperature(oracle, embed):
          "parents_host": par, "draft_lens": torch.full((B,), n, dtype=torch.int32, device=DEV),
          "temperature": torch.as_tensor(temp, device=DEV), "uniforms": torch.as_tensor(u, device=DEV)}
     _compare(oracle, d, _rounds(d), tag=f"six-token trees embed={embed}")
+
+
+@pytest.mark.parametrize("V", [4096, 4099])
+def test_later_sibling_far_below_both_maxima(oracle, V):
+    """The oracle's closed form with the rows embedded in V tokens (-5 below
+    the top elsewhere): the later sibling's p and q are ~e^-200, far below the
+    binary32 range of the far form's terms, and its ratio is exactly 3
+    (S_d / S_t = 3, M_1 = 2/3), so it is accepted at every uniform; the
+    accepted node's bonus token follows."""
+    B = 8
+    zt = np.full((B, 3, V), -5.0, np.float32)
+    zd = np.full((B, 2, V), -5.0, np.float32)
+    zt[:, 0, 100] = 0.0
+    zt[:, 0, V - 3] = -2.0
+    zd[:, 0, [100, 2000, V - 1]] = 0.0
+    zd[:, 0, V - 3] = -2.0
+    zt[:, 2, 7] = 0.0
+    x = np.array([[2000, V - 3]] * B, np.int32)
+    par = np.zeros((B, 2), np.int32)
+    u = np.random.default_rng(5).random((B, 3)).astype(np.float32)
+    t = lambda a: torch.as_tensor(a, device=DEV)
+    d = {"target": t(zt).to(torch.bfloat16).contiguous(), "draft": t(zd).to(torch.bfloat16).contiguous(),
+         "draft_tokens": t(x), "draft_parents": t(par), "parents_host": par,
+         "draft_lens": torch.full((B,), 2, dtype=torch.int32, device=DEV),
+         "temperature": torch.full((B,), 0.01, dtype=torch.float32, device=DEV), "uniforms": t(u)}
+    acc, emi, path, fl = _run(d, _rounds(d))
+    assert acc.tolist() == [1] * B, acc
+    assert emi[:, :3].tolist() == [[V - 3, 7, -1]] * B, emi
+    _compare(oracle, d, _rounds(d), tag=f"deep later sibling V={V}")

@@ -298,3 +298,29 @@ def test_later_sibling_on_a_shared_top_token_at_low_temperature(oracle):
     assert out["path"].tolist() == [[2, -1]] * 3
     assert out["emitted"].tolist() == [[0, 1, -1]] * 3
     assert not (out["seq_flags"] & 16).any()
+
+
+def test_later_sibling_far_below_both_maxima(oracle):
+    """A closed form where the later sibling's probabilities lie ~e^-200 below
+    both rows' maxima at T = 0.01: the target puts all but e^-200 of its mass
+    on token 0, the draft splits it over tokens 0, 1, 2 (so S_d / S_t = 3), and
+    token 3 sits 2.0 below the top in both rows (relative logits equal).
+    Rejecting token 1 leaves M_1 = sum max(0, p - q) = 2/3 (up to e^-200), and
+    token 3's ratio (p - q) / (M_1 q) = (S_d / S_t - 1) / M_1 = 3: accepted at
+    any uniform, its margin |u - 3|."""
+    V = 8
+    zt = np.full((1, 3, V), -5.0, np.float32)
+    zd = np.full((1, 2, V), -5.0, np.float32)
+    zt[0, 0, 0] = 0.0
+    zt[0, 0, 3] = -2.0
+    zd[0, 0, :3] = 0.0
+    zd[0, 0, 3] = -2.0
+    zt[0, 2, 6] = 0.0            # the accepted node's row: its bonus token is 6
+    x = np.array([[1, 3]], np.int32)
+    par = np.array([[0, 0]], np.int32)
+    u = np.array([[0.5, 0.9, 0.5]], np.float32)
+    o = oracle.verify_tree_sample(zt, zd, x, par, np.array([2], np.int32), np.array([0.01], np.float32), u)
+    assert o["accepted_len"].tolist() == [1]
+    assert o["emitted"].tolist() == [[3, 6, -1]]
+    assert o["path"].tolist() == [[2, -1]]
+    assert abs(o["accept_margin"][0, 1] - (3.0 - float(np.float32(0.9)))) < 1e-9
