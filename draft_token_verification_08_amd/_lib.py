@@ -609,7 +609,8 @@ def mtp_shift_insert(tokens, hidden_src, hidden_dst, accepted_len, emitted, *, s
 def sv_residual_weights_debug(target_rows, draft_rows, temperature, *, stream=None):
     """Residual weights the draw pass scans after a rejection (parity/debug only).
     Returns (weights [rows, V] float32, tile_weights [rows, NT] float64,
-    info [rows, 4] float32: near form (1) or far form (0), the far form's lambda, the near form's rho,
+    info [rows, 4] float32: the form (0 far, 1 near from the chunks' sums, 2 near formed by one
+    workgroup, 3 that form from log2 weights), the far form's lambda, the near form's kappa,
     the residual mass)."""
     dev = target_rows.device
     rows, V = target_rows.shape

@@ -734,31 +734,60 @@ __device__ __forceinline__ double log2_add(double a, double b) {
     const double hi = fmax(a, b), lo = fmin(a, b);
     return hi + log2(1.0 + exp2(lo - hi));
 }
+// log2(1 - 2^y) for y <= 0 (-inf at 0), and log2(1 + 2^y): 1 - 2^y from the
+// series of exp2m1_small() where |y| <= 1/4 (no digit lost), the logarithm by
+// the hardware's log2.
+__device__ __forceinline__ float log2_1m_exp2(float y) {
+    const float v = y > -0.25f ? -exp2m1_small(y) : 1.f - exp2_fast(y);
+    return __builtin_amdgcn_logf(v);
+}
+__device__ __forceinline__ float log2_1p_exp2(float y) { return __builtin_amdgcn_logf(1.f + exp2_fast(y)); }
+
 // log2 of the near form's weight max(0, kappa A - lam Dl) of near_term() in
 // units of 2^(sl c) (-inf: no weight).  The exponents (log2 A = at c, log2 |kappa|,
 // the shift) are added in binary64, so that no weight leaves the range; the
 // corrections of order 1 are binary32: lam |Dl| = lam 2^(at c - sl c) |2^x - 1|
-// with x = (ad - at) c and |2^x - 1| = 2^max(x, 0) (1 - 2^-|x|), 1 - 2^-|x| by
-// expm1f, and sums and differences of two weights as 2^hi (1 +- 2^(lo - hi)).
+// with x = (ad - at) c and |2^x - 1| = 2^max(x, 0) (1 - 2^-|x|), and sums and
+// differences of two weights as 2^hi (1 +- 2^(lo - hi)).
 __device__ __forceinline__ double near_log_weight(const WSpec& s, float zt, float zd) {
-    constexpr float kLn2f = 0.69314718f;
     const float at = near_rel(zt, s.mA), ad = near_rel(zd, s.m_d);
     if (at == -INFINITY) return -INFINITY;  // p = 0: max(0, -lam q) = 0
     const double ac = (double)at * (double)s.c;
     const double lkA = s.ks != 0 ? s.lk + ac : -INFINITY;  // log2 (|kappa| A)
     if (at == ad) return s.ks > 0 ? lkA : -INFINITY;
     const double x = ad == -INFINITY ? -INFINITY : ((double)ad - (double)at) * (double)s.c;
-    const float xa = (float)fabs(x);
-    const double lD = (double)log2f(s.lam) + ac - s.sig + fmax(x, 0.0) + (double)log2f(-expm1f(-xa * kLn2f));
+    const double lD = (double)__builtin_amdgcn_logf(s.lam) + ac - s.sig + fmax(x, 0.0) +
+                      (double)log2_1m_exp2(-(float)fabs(x));
     if (x < 0.0) {  // target above draft: -lam Dl > 0
         if (s.ks > 0) {
             const double hi = fmax(lkA, lD), lo = fmin(lkA, lD);
-            return hi + (double)log2f(1.f + exp2f((float)(lo - hi)));
+            return hi + (double)log2_1p_exp2((float)(lo - hi));
         }
-        if (s.ks < 0) return lkA < lD ? lD + (double)log2f(-expm1f((float)(lkA - lD) * kLn2f)) : -INFINITY;
+        if (s.ks < 0) return lkA < lD ? lD + (double)log2_1m_exp2((float)(lkA - lD)) : -INFINITY;
         return lD;
     }
-    return (s.ks > 0 && lkA > lD) ? lkA + (double)log2f(-expm1f((float)(lD - lkA) * kLn2f)) : -INFINITY;
+    return (s.ks > 0 && lkA > lD) ? lkA + (double)log2_1m_exp2((float)(lD - lkA)) : -INFINITY;
+}
+
+// An upper bound of near_log_weight() from the exponents alone, in binary32
+// with a margin e = 1 + 2^-20 (|at c| + |sl c| + |log2 |kappa||) for the
+// roundings of its handful of operations: within 1 + 2e of the weight where the
+// target's logit exceeds the draft's.  lkf = log2 |kappa|, sgf = sl c, llf =
+// log2 lam.  Where the draft's exceeds the target's by x = (ad - at) c >= 1, the
+// weight is positive only if log2 |kappa| + sl c - log2 lam > x + log2(1 - 2^-x)
+// >= x - 1.
+__device__ __forceinline__ float near_log_bound(int ks, float lkf, float sgf, float llf, float c, float m_t,
+                                                float m_d, float zt, float zd) {
+    const float at = near_rel(zt, m_t), ad = near_rel(zd, m_d);
+    if (at == -INFINITY) return -INFINITY;
+    const float ac = at * c;
+    const float e = 1.f + 0x1p-20f * (fabsf(ac) + fabsf(sgf) + fabsf(lkf));
+    const float lkA = ks != 0 ? lkf + ac : -INFINITY;
+    if (ad < at) return fmaxf(lkA, llf + ac - sgf) + 1.f + e;
+    if (ks <= 0) return -INFINITY;
+    if (ad == at) return lkA + e;
+    const float x = (ad - at) * c;
+    return (x >= 1.f + e && x - 1.f - e >= lkf + sgf - llf) ? -INFINITY : lkA + e;
 }
 
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
@@ -1944,36 +1973,55 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
             }
         }
     };
-    // the same elements one vector of each row at a time (the cold log2 passes,
-    // whose element math is longest)
-    auto visit1 = [&](int t, int u0, auto&& f) {
+    // the same elements kHL vectors of each row at a time (the cold log2 passes,
+    // whose element math is longest: more in flight does not fit the registers)
+    constexpr int kHL = (ALIGNED && DT == kF32) ? 2 : 1;  // 8 elements of each row
+    auto visit_log = [&](int t, int u0, auto&& f) {
         if constexpr (ALIGNED) {
-            const int e0 = t * kTile + (lane + 64 * u0) * kVec;
-            const uint4 wt = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
-            const uint4 wd = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+            uint4 wt[kHL], wd[kHL];
+#pragma unroll
+            for (int h = 0; h < kHL; ++h) {
+                const int e0 = t * kTile + (lane + 64 * (u0 + h)) * kVec;
+                wt[h] = e0 < V ? ld16((const uint4*)trow + e0 / kVec) : neg_inf_vec<DT>();
+                wd[h] = e0 < V ? ld16((const uint4*)drow + e0 / kVec) : neg_inf_vec<DT>();
+            }
+#pragma unroll
+            for (int h = 0; h < kHL; ++h) {
 #pragma unroll 1
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t a = q == 0 ? wt.x : q == 1 ? wt.y : q == 2 ? wt.z : wt.w;
-                const uint32_t b = q == 0 ? wd.x : q == 1 ? wd.y : q == 2 ? wd.z : wd.w;
-                if constexpr (DT == kBF16) {
-                    f(bf16_lo(a), bf16_lo(b));
-                    f(bf16_hi(a), bf16_hi(b));
-                } else {
-                    f(__uint_as_float(a), __uint_as_float(b));
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t a = q == 0 ? wt[h].x : q == 1 ? wt[h].y : q == 2 ? wt[h].z : wt[h].w;
+                    const uint32_t b = q == 0 ? wd[h].x : q == 1 ? wd[h].y : q == 2 ? wd[h].z : wd[h].w;
+                    if constexpr (DT == kBF16) {
+                        f(bf16_lo(a), bf16_lo(b));
+                        f(bf16_hi(a), bf16_hi(b));
+                    } else {
+                        f(__uint_as_float(a), __uint_as_float(b));
+                    }
                 }
             }
         } else {
             visit(t, u0, f);
         }
     };
-    float sl = -INFINITY;
+    // the shift, and the largest relative target logit of the tokens the rows
+    // share, of those where the target's exceeds the draft's, and of the others
+    float sl = -INFINITY, m_sh = -INFINITY, m_tf = -INFINITY, m_df = -INFINITY;
+    float g_df = INFINITY;  // the smallest ad - at where the draft's exceeds the target's
     for (int t = w; t < NT; t += kWaves)
         for (int u0 = 0; u0 < kU; u0 += kH)
             visit(t, u0, [&](float zt, float zd) {
                 const float at = near_rel(zt, m_t), ad = near_rel(zd, m_d);
                 if (at != ad) sl = fmaxf(sl, fmaxf(at, ad));
+                // one update per maximum, no branch between them
+                m_sh = fmaxf(m_sh, at == ad ? at : -INFINITY);
+                m_tf = fmaxf(m_tf, ad < at ? at : -INFINITY);
+                m_df = fmaxf(m_df, ad > at ? at : -INFINITY);
+                g_df = fminf(g_df, ad > at ? ad - at : INFINITY);
             });
     sl = block_max_f_all(sl);
+    double msh = (double)m_sh, mtf = (double)m_tf, mdf = (double)m_df, ngdf = -(double)g_df;
+    block_max2_d_all(msh, mtf);
+    block_max2_d_all(mdf, ngdf);
     double X = 0.0, D = 0.0, Y = 0.0, unused = 0.0;
     for (int t = w; t < NT; t += kWaves) {
         float sx = 0.f, sd = 0.f, sy = 0.f;
@@ -2008,24 +2056,6 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
     const double lam = 1.0 + desc_mu(d);
     const float kappa_f = (float)fmin(fmax(kappa, -(double)FLT_MAX), (double)FLT_MAX), lam_f = (float)lam;
     *ws = WSpec{kWResNear, c, m_t, m_d, lam_f, kappa_f, sl, 0.f, 0.f};
-    double zsum = 0.0, wdsum = 0.0;
-    for (int t = w; t < NT; t += kWaves) {
-        float sw = 0.f, swd = 0.f;
-        for (int u0 = 0; u0 < kU; u0 += kH)
-            visit(t, u0, [&](float zt, float zd) {
-                const float wt = near_weight(m_t, m_d, sl, c, kappa_f, lam_f, zt, zd);
-                sw += wt;
-                if (near_rel(zt, m_t) != near_rel(zd, m_d)) swd += wt;
-            });
-        sw = wave_sum(sw);
-        swd = wave_sum(swd);
-        if (lane == 0) {
-            s_w[t] = (double)sw;
-            zsum += (double)sw;
-            wdsum += (double)swd;
-        }
-    }
-    block_sum2_all(zsum, wdsum);
     const double Sd = X * (1.0 + rho * scale);  // the draft row's sum in A's units
     // kappa as sign and log2 (a carried kappa without forming 2^(lkap - sl c))
     int ks;
@@ -2037,49 +2067,119 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
         ks = kappa > 0.0 ? 1 : kappa < 0.0 ? -1 : 0;
         lk = kappa != 0.0 ? log2(fabs(kappa)) : -INFINITY;
     }
-    double lz = zsum > 0.0 ? log2(zsum) : -INFINITY, lwd = wdsum > 0.0 ? log2(wdsum) : -INFINITY;
-    // binary32 terms in units of 2^(sl c) may have lost every weight that decides
-    // the draw (their total far below 1), or, for a round, the comparison of
-    // kappa Y with W (both far below 1): the weights are re-formed from their
-    // log2 (near_log_weight()), scaled by 2^-E with E the largest (an integer)
-    const bool log_draw = !(zsum > 0x1p-100);
-    const bool log_w = need_next && !(wdsum > 0x1p-90) && ks > 0 && !(lk + sig + log2(Y) > -90.0);
-    if (log_draw || log_w) {
-        WSpec wl{kWResNearLog, c, m_t, m_d, lam_f, 0.f, sl, 0.f, 0.f, ks, lk, sig, 0.0};
-        double E = -INFINITY, Ed = -INFINITY;  // the largest log2 weight; over the differing tokens
-        for (int t = w; t < NT; t += kWaves)
-            for (int u0 = 0; u0 < kU; ++u0)
-                visit1(t, u0, [&](float zt, float zd) {
-                    const double lw = near_log_weight(wl, zt, zd);
-                    E = fmax(E, lw);
-                    if (near_rel(zt, m_t) != near_rel(zd, m_d)) Ed = fmax(Ed, lw);
-                });
-        block_max2_d_all(E, Ed);
-        E = E > -INFINITY ? floor(E) : 0.0;
-        Ed = Ed > -INFINITY ? floor(Ed) : -INFINITY;
-        wl.E = E;
-        double zl = 0.0, wdl = 0.0;
+    // binary32 terms in units of 2^(sl c) may lose every weight that decides the
+    // draw (their total far below 1), or, for a round, the comparison of kappa Y
+    // with W (both far below 1): then the weights are formed from their log2
+    // (near_log_weight()), scaled by 2^-E with E the largest (an integer).
+    // Bounds of the largest weights from the maxima above say so in advance
+    // where they can (the binary32 pass is then skipped); else the binary32
+    // sums say so afterwards.
+    const double llam = log2(lam), lV = log2((double)V);
+    const double lky = (ks > 0 && Y > 0.0) ? lk + sig + log2(Y) : -INFINITY;  // log2 (kappa Y), units of 2^(sl c)
+    const double e_sh = ks > 0 ? lk + msh * (double)c : -INFINITY;
+    const double e_tf = llam + mtf * (double)c - sig + 1.0;
+    // a token where the draft's logit exceeds the target's by x >= 1 has a
+    // positive weight only if log2 |kappa| + sl c - log2 lam > x - 1 (near_log_bound())
+    const double xg = -ngdf * (double)c;
+    const bool df_zero = xg >= 1.0 && xg - 1.0 >= lk + sig - llam;
+    const double e_df = (ks > 0 && !df_zero) ? lk + mdf * (double)c : -INFINITY;
+    const bool pred_log = fmax(e_sh, fmax(e_tf, e_df)) + lV < -100.0 ||
+                          (need_next && ks > 0 && !(lky > -90.0) && fmax(e_tf, e_df) + lV < -90.0);
+    double zsum = 0.0, wdsum = 0.0;
+    if (!pred_log) {
         for (int t = w; t < NT; t += kWaves) {
             float sw = 0.f, swd = 0.f;
-            for (int u0 = 0; u0 < kU; ++u0)
-                visit1(t, u0, [&](float zt, float zd) {
-                    const double lw = near_log_weight(wl, zt, zd);
-                    if (lw > -INFINITY) {
-                        sw += exp2_fast((float)(lw - E));
-                        if (near_rel(zt, m_t) != near_rel(zd, m_d)) swd += exp2_fast((float)(lw - Ed));
-                    }
+            for (int u0 = 0; u0 < kU; u0 += kH)
+                visit(t, u0, [&](float zt, float zd) {
+                    const float wt = near_weight(m_t, m_d, sl, c, kappa_f, lam_f, zt, zd);
+                    sw += wt;
+                    if (near_rel(zt, m_t) != near_rel(zd, m_d)) swd += wt;
                 });
             sw = wave_sum(sw);
             swd = wave_sum(swd);
             if (lane == 0) {
-                if (log_draw) s_w[t] = (double)sw;
-                zl += (double)sw;
-                wdl += (double)swd;
+                s_w[t] = (double)sw;
+                zsum += (double)sw;
+                wdsum += (double)swd;
             }
         }
-        block_sum2_all(zl, wdl);
-        lwd = wdl > 0.0 ? Ed + log2(wdl) : -INFINITY;
+        block_sum2_all(zsum, wdsum);
+    }
+    double lz = zsum > 0.0 ? log2(zsum) : -INFINITY, lwd = wdsum > 0.0 ? log2(wdsum) : -INFINITY;
+    const bool log_draw = pred_log || !(zsum > 0x1p-100);
+    const bool log_w = pred_log || (need_next && !(wdsum > 0x1p-90) && ks > 0 && !(lky > -90.0));
+    if (log_draw || log_w) {
+        WSpec wl{kWResNearLog, c, m_t, m_d, lam_f, 0.f, sl, 0.f, 0.f, ks, lk, sig, 0.0};
+        const float lkf = (float)fmax(lk, -3e38), sgf = (float)sig, llf = (float)llam;
+        // one pass: each lane keeps a running largest log2 weight and the sum of
+        // its weights scaled to it, for the tile (all tokens) and for the
+        // differing tokens (all its tiles); a weight whose bound lies 64 below
+        // the lane's largest adds less than 2^-63 of it and is left out.  For the
+        // draw each tile's log2 sum goes to s_w[t] first (else s_w keeps the
+        // binary32 pass's tile weights).
+        // the running maxima are binary32 (reference points only: every difference
+        // to them is formed in binary64)
+        float mw = -INFINITY;  // the differing tokens (W)
+        float sw_d = 0.f;
+        for (int t = w; t < NT; t += kWaves) {
+            float mt = -INFINITY;
+            float st = 0.f;
+            // the wave's largest so far (one threshold for the whole wave, so
+            // that the long element math runs only where some lane needs it)
+            float thr = -INFINITY;
+            for (int u0 = 0; u0 < kU; u0 += kHL) {
+                visit_log(t, u0, [&](float zt, float zd) {
+                    if (!(near_log_bound(ks, lkf, sgf, llf, c, m_t, m_d, zt, zd) >= thr)) return;
+                    const double lw = near_log_weight(wl, zt, zd);
+                    if (lw == -INFINITY) return;
+                    if (lw > (double)mt) {
+                        const float nm = (float)lw;
+                        st *= exp2_fast((float)((double)mt - (double)nm));
+                        mt = nm;
+                    }
+                    st += exp2_fast((float)(lw - (double)mt));
+                    if (near_rel(zt, m_t) != near_rel(zd, m_d)) {
+                        if (lw > (double)mw) {
+                            const float nm = (float)lw;
+                            sw_d *= exp2_fast((float)((double)mw - (double)nm));
+                            mw = nm;
+                        }
+                        sw_d += exp2_fast((float)(lw - (double)mw));
+                    }
+                });
+                float th = fminf(mt, mw);
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) th = fmaxf(th, __shfl_xor(th, off, 64));
+                thr = fmaxf(thr, th - 64.f);
+            }
+            // the tile's log2 sum over the wave
+            float M = mt;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+            const float S = wave_sum(M > -INFINITY && mt > -INFINITY ? st * exp2_fast((float)((double)mt - (double)M)) : 0.f);
+            if (log_draw && lane == 0) s_w[t] = S > 0.f ? (double)M + log2((double)S) : -INFINITY;
+        }
+        // W over the workgroup (per-lane values into the block sum)
+        double Mw = (double)mw, unused_w = -INFINITY;
+        block_max2_d_all(Mw, unused_w);  // also orders the s_w writes above before the reads below
+        double wdl = (Mw > -INFINITY && mw > -INFINITY) ? (double)sw_d * exp2((double)mw - Mw) : 0.0, unused_s = 0.0;
+        block_sum2_all(wdl, unused_s);
+        lwd = wdl > 0.0 ? Mw + log2(wdl) : -INFINITY;
         if (log_draw) {
+            // the draw's scale E: the largest tile's log2 sum, rounded down
+            double E = -INFINITY;
+            for (int t = threadIdx.x; t < NT; t += kThreads) E = fmax(E, s_w[t]);
+            double unused_e = -INFINITY;
+            block_max2_d_all(E, unused_e);
+            E = E > -INFINITY ? floor(E) : 0.0;
+            wl.E = E;
+            double zl = 0.0;
+            for (int t = threadIdx.x; t < NT; t += kThreads) {
+                const double v = s_w[t] > -INFINITY ? exp2(s_w[t] - E) : 0.0;
+                s_w[t] = v;
+                zl += v;
+            }
+            block_sum2_all(zl, unused_s);
             *ws = wl;
             zsum = zl;
             lz = zl > 0.0 ? E + log2(zl) : -INFINITY;
@@ -2651,8 +2751,9 @@ __global__ __launch_bounds__(kThreads) void k_softmax_debug(const void* logits, 
 // the deciding workgroup's set-up (plan_residual(): the far form, or the near
 // form when the residual mass is small), then every element's weight.
 // Outputs: w_out[r][V] the element weights, tile_out[r][NT] (nullable) the
-// tiles' weights the tile pick uses, info_out[r][4] (nullable) {1 near / 0 far,
-// lam, rho (near form) or 0, residual mass sum of tile weights / sum P}.
+// tiles' weights the tile pick uses, info_out[r][4] (nullable) {0 far / 1 near from
+// the chunks' sums / 2 near by one workgroup / 3 the same from log2 weights, lam
+// (far form) or 0, kappa (near form) or 0, the residual mass}.
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k_residual_debug(const void* target, const void* draft, const float* temp,
                                                              int V, int NT, float* w_out, double* tile_out,

@@ -431,11 +431,13 @@ sv_status_t sv_softmax_rows_debug(const void *logits, sv_dtype_t dt, const float
  *                    to the row (NaN for rows with T <= 0 or NaN)
  *   tile_weights_out [rows][NT] double, nullable: the per-tile weights the tile
  *                    pick uses (NT = ceil(V / 2048) for bf16, ceil(V / 1024) for f32)
- *   info_out         [rows][4] float, nullable: {1 for the near form (taken when
- *                    the residual mass is below 0.01: each row relative to its
- *                    own maximum, differences scaled to the largest of them)
- *                    else 0, lambda of the far form (else 0), rho of the near
- *                    form (else 0), the residual mass sum max(0, p - q)}
+ *   info_out         [rows][4] float, nullable: {the form: 0 far, 1 near from
+ *                    the chunks' sums, 2 near formed by one workgroup (each
+ *                    row relative to its own maximum, differences scaled to the
+ *                    largest of them), 3 that form with its weights formed from
+ *                    their log2; the near form is taken when the residual mass
+ *                    is below 0.01), lambda of the far form (else 0), kappa of
+ *                    the near form (else 0), the residual mass sum max(0, p - q)}
  * The row statistics come from this call's own reduction of each row, so the
  * tile weights may differ from a verify call's in the last digits; the element
  * weights do not depend on them. */
