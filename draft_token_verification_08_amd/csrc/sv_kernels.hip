@@ -1889,11 +1889,13 @@ struct ResidPlan {
 // The near form of one row pair, formed by one workgroup from the rows
 // themselves (near_term()): first the shift sl = max(at, ad) over the tokens
 // whose relative logits differ (-inf when none does: p = q), then
-// S_t = sum A and rho = sum Dl / S_t over the whole pair, then each tile's
-// weight sum max(0, kappa A - lam Dl) into s_w[NT], the residual
-// max(0, p - lam q) at lam = 1 + mu (kappa = rho - mu 2^(-sl c)).  Fills *ws
-// (element weighting) and *pl (ResidPlan).  Wave w
-// takes tiles w, w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
+// S_t = sum A, rho = sum Dl / S_t and Y = sum B over the differing tokens, then
+// each tile's weight sum max(0, kappa A - lam Dl) into s_w[NT], the residual
+// max(0, p - lam q) at lam = 1 + mu (kappa carried by a tree walk, else
+// rho - mu 2^(-sl c)), in binary32 or, where that range cannot hold them, from
+// their log2 (near_log_weight()).  Fills *ws (element weighting) and *pl
+// (ResidPlan, with the sums next_kappa() needs).  Wave w takes tiles w,
+// w + kWaves, ...; lane l the vectors l, l + 64, ... of a tile.
 __device__ float block_max_f_all(float v) {
     __shared__ float sh[kWaves];
     v = wave_max_f(v);
@@ -1973,7 +1975,7 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
             }
         }
     };
-    // the same elements kHL vectors of each row at a time (the cold log2 passes,
+    // the same elements kHL vectors of each row at a time (the cold log2 pass,
     // whose element math is longest: more in flight does not fit the registers)
     constexpr int kHL = (ALIGNED && DT == kF32) ? 2 : 1;  // 8 elements of each row
     auto visit_log = [&](int t, int u0, auto&& f) {
@@ -2070,7 +2072,8 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
     // binary32 terms in units of 2^(sl c) may lose every weight that decides the
     // draw (their total far below 1), or, for a round, the comparison of kappa Y
     // with W (both far below 1): then the weights are formed from their log2
-    // (near_log_weight()), scaled by 2^-E with E the largest (an integer).
+    // (near_log_weight()), scaled by 2^-E with E the largest tile's log2 sum
+    // rounded down.
     // Bounds of the largest weights from the maxima above say so in advance
     // where they can (the binary32 pass is then skipped); else the binary32
     // sums say so afterwards.
@@ -2114,9 +2117,9 @@ __device__ void near_exact_tiles(const void* trow, const void* drow, int V, int 
         // one pass: each lane keeps a running largest log2 weight and the sum of
         // its weights scaled to it, for the tile (all tokens) and for the
         // differing tokens (all its tiles); a weight whose bound lies 64 below
-        // the lane's largest adds less than 2^-63 of it and is left out.  For the
-        // draw each tile's log2 sum goes to s_w[t] first (else s_w keeps the
-        // binary32 pass's tile weights).
+        // the wave's largest so far adds less than 2^-63 of it and is left out.
+        // For the draw each tile's log2 sum goes to s_w[t] first (else s_w keeps
+        // the binary32 pass's tile weights).
         // the running maxima are binary32 (reference points only: every difference
         // to them is formed in binary64)
         float mw = -INFINITY;  // the differing tokens (W)
