@@ -702,8 +702,14 @@ __device__ __forceinline__ float near_weight(float m_t, float m_d, float sl, flo
 //               units of 2^(sl c): the residual max(0, p - lam q);
 //   kWResNearLog: the same weights formed from their log2 in binary64
 //               (near_log_weight()) and scaled by 2^-E, for residuals whose
-//               weights lie below the binary32 range in units of 2^(sl c).
-enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2, kWResNearLog = 3 };
+//               weights lie below the binary32 range in units of 2^(sl c);
+//   kWTargetP:  the target's own distribution in the far form's units
+//               P = 2^(z_t c - fl(m_t c)) (far_p()), for draws whose tile sums
+//               were taken in those units.  The two target weightings differ by
+//               the factor 2^(m_t c - fl(m_t c)), 1 + 1e-7 at ordinary
+//               temperatures but up to 2 once m_t c passes 2^24 (T near 1e-6):
+//               a draw scans its tile in the units its tile sums were taken in.
+enum WMode : int { kWTarget = 0, kWResFar = 1, kWResNear = 2, kWResNearLog = 3, kWTargetP = 4 };
 struct WSpec {
     int mode;
     float c;    // log2(e) / T
@@ -712,7 +718,7 @@ struct WSpec {
     float lam;    // kWResFar: lam S_t / S_d; kWResNear(Log): lam
     float kappa;  // kWResNear
     float sl;     // kWResNear(Log): the shift of the differences (<= 0)
-    float nmt;  // kWResFar: neg_scaled(mA, c)
+    float nmt;  // kWResFar, kWTargetP: neg_scaled(mA, c)
     float nmd;  // kWResFar: neg_scaled(m_d, c)
     int ks;      // kWResNearLog: the sign of kappa (0: kappa = 0)
     double lk;   // kWResNearLog: log2 |kappa| (kappa in units of 2^(sl c))
@@ -792,6 +798,7 @@ __device__ __forceinline__ float near_log_bound(int ks, float lkf, float sgf, fl
 
 __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd) {
     if (s.mode == kWTarget) return exp2_fast((zt - s.mA) * s.c);
+    if (s.mode == kWTargetP) return far_p(s.nmt, s.c, zt);
     if (s.mode == kWResNearLog) {
         const double lw = near_log_weight(s, zt, zd);
         return lw == -INFINITY ? 0.f : exp2_fast((float)(lw - s.E));
@@ -806,6 +813,10 @@ __device__ __forceinline__ float elem_weight(const WSpec& s, float zt, float zd)
 __device__ __forceinline__ WSpec target_spec(const DrawDesc& d) {
     return WSpec{kWTarget, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 }
+__device__ __forceinline__ WSpec target_p_spec(const DrawDesc& d) {
+    return WSpec{kWTargetP, d.c, d.m_t, 0.f, 0.f, 0.f, 0.f, neg_scaled(d.m_t, d.c), 0.f};
+}
+__device__ __forceinline__ bool target_only(const WSpec& s) { return s.mode == kWTarget || s.mode == kWTargetP; }
 
 // Scan one tile: returns the element whose running weight (starting at P)
 // first exceeds t.  The thread holding t is picked from per-thread sums taken in
@@ -820,7 +831,7 @@ __device__ __forceinline__ int scan_tile(const WSpec& ws, const void* trow, cons
     constexpr int kVec = Elem<DT>::kVec;
     constexpr int kTile = kThreads * kVec;
     const int e0 = tile * kTile + threadIdx.x * kVec;
-    const bool residual = ws.mode != kWTarget;
+    const bool residual = !target_only(ws);
     float zt[kVec], zd[kVec], wv[kVec];
     load_vec<DT, ALIGNED>(trow, e0, V, zt);
     if (residual) load_vec<DT, ALIGNED>(drow, e0, V, zd);
@@ -2296,7 +2307,9 @@ __device__ __forceinline__ void plan_residual(const float (&v)[TPT][kDrawSums], 
             const int i = tid + r * kThreads;
             if (i < NT) s_w[i] = (double)v[r][kSumP];
         }
-        *ws = target_spec(d);
+        // (the chunks' sum P is in the near form's units 2^((z - m_t) c), else in
+        // the far form's)
+        *ws = d.kind == kDrawResidualNear ? target_spec(d) : target_p_spec(d);
         *pl = ResidPlan{-zp, 0.0, -INFINITY, 0.0, 0.0, 0.0, 1.0, false, 0.0, -INFINITY, 0.0, -INFINITY, 0};
     }
     __syncthreads();
@@ -2310,7 +2323,7 @@ __device__ __forceinline__ void plan_residual(const float (&v)[TPT][kDrawSums], 
 //              (w = kappa A - lam Dl of near_term());
 // both give w sq / (Z q') with q' = Q or B.  q(x) = 0 < p(x) - lam q(x): +inf.
 __device__ __forceinline__ double resid_ratio(const WSpec& ws, const ResidPlan& pl, float zt, float zd) {
-    if (!(pl.Z > 0.0) || ws.mode == kWTarget) return 0.0;
+    if (!(pl.Z > 0.0) || target_only(ws)) return 0.0;
     if (ws.mode == kWResNearLog) {
         // w S_d / (Z B) from the log2 weight: Z = 2^E sum in units of 2^(sl c)
         const float ad = near_rel(zd, ws.m_d);
@@ -2498,7 +2511,7 @@ __device__ __forceinline__ void draw_item(const DrawParams& p, int b, int c, dou
     ResidPlan pl;
     plan_residual<DT, ALIGNED, kTPT>(v, NT, d, trow, drow, V, s_buf, &ws, &pl, false);
     const double Z = pl.Z;
-    if (!has_draft) ws = target_spec(d);  // weights P: the target row's own distribution
+    if (!has_draft) ws = target_p_spec(d);  // weights P: the target row's own distribution, in its tile sums' units
     if (Z <= 0.0 && tid == 0 && p.flags) atomicOr(p.flags, (uint32_t)SV_FLAG_ZERO_RESIDUAL);
     const double t = (double)d.u * fabs(Z);
     const Pick pk = block_first_crossing(NT, t, [&](int i) { return s_buf[i]; });
@@ -2548,7 +2561,7 @@ __device__ __forceinline__ SLog2 next_kappa(const DrawDesc& d, const WSpec& ws, 
         return SLog2{r.s, r.l + pl.lu - log2(pl.sq)};
     }
     const double kk = d.skap != 0 ? desc_kappa(d, 0.0) : Sd / St - 1.0;
-    const double M = (ws.mode != kWTarget && pl.Z > 0.0) ? exp2(pl.lmass) : 0.0;
+    const double M = (!target_only(ws) && pl.Z > 0.0) ? exp2(pl.lmass) : 0.0;
     return slog2_of(kk - M);
 }
 

@@ -341,3 +341,41 @@ def test_later_sibling_far_below_both_maxima(oracle, V):
     assert acc.tolist() == [1] * B, acc
     assert emi[:, :3].tolist() == [[V - 3, 7, -1]] * B, emi
     _compare(oracle, d, _rounds(d), tag=f"deep later sibling V={V}")
+
+
+@pytest.mark.parametrize("same_tile", [True, False])
+@pytest.mark.parametrize("T", [1.3e-6, 1e-5, 0.7])
+def test_leaf_draw_among_tied_maxima(oracle, same_tile, T):
+    """A walk that accepts the root's only child draws from the leaf's target
+    row alone.  That row holds three tokens tied at its maximum 15.375 (next
+    value 15.0625); at T = 1.3e-6, m c passes 2^24, where the far form's units
+    2^(z c - fl(m c)) and the target's 2^((z - m) c) differ by up to a factor
+    2, so the draw must scan the picked tile in the units of its tile sums.
+    The tie splits the draw in thirds: uniforms in each third pick the first,
+    second and third tied token in index order (ties in one tile, or in three)."""
+    V = 3344
+    ties = [89, 1038, 1413] if same_tile else [89, 2100, 3300]
+    us = [0.1, 0.4, 0.7, 0.95, 0.34, 0.66]
+    B = len(us)
+    g = np.random.default_rng(3)
+    zt = np.round((13.0 + g.random((B, 2, V))) * 16.0) / 16.0  # values below the tie, bf16-exact
+    zt[:, 1, ties] = 15.375
+    zt[:, 1, 7] = 15.0625
+    zt = zt.astype(np.float32)
+    zd = zt[:, :1].copy()                                        # draft = target at the root: accepted
+    x = np.full((B, 1), 500, np.int32)
+    par = np.zeros((B, 1), np.int32)
+    u = np.zeros((B, 2), np.float32)
+    u[:, 0] = 0.5
+    u[:, 1] = us
+    t = lambda a: torch.as_tensor(a, device=DEV)
+    d = {"target": t(zt).to(torch.bfloat16).contiguous(), "draft": t(zd).to(torch.bfloat16).contiguous(),
+         "draft_tokens": t(x), "draft_parents": t(par), "parents_host": par,
+         "draft_lens": torch.ones(B, dtype=torch.int32, device=DEV),
+         "temperature": torch.full((B,), T, dtype=torch.float32, device=DEV), "uniforms": t(u)}
+    acc, emi, path, fl = _run(d, _rounds(d))
+    assert acc.tolist() == [1] * B, acc
+    if T < 1e-4:
+        want = [ties[min(int(uu * 3), 2)] for uu in us]
+        assert emi[:, 1].tolist() == want, (emi[:, 1].tolist(), want)
+    _compare(oracle, d, _rounds(d), tag=f"leaf draw T={T} same_tile={same_tile}")
