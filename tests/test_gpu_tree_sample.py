@@ -379,3 +379,28 @@ def test_leaf_draw_among_tied_maxima(oracle, same_tile, T):
         want = [ties[min(int(uu * 3), 2)] for uu in us]
         assert emi[:, 1].tolist() == want, (emi[:, 1].tolist(), want)
     _compare(oracle, d, _rounds(d), tag=f"leaf draw T={T} same_tile={same_tile}")
+
+
+@pytest.mark.parametrize("T", [1e-5, 1e-3, 0.7])
+def test_masked_rows_at_low_temperature(oracle, T):
+    """Sampling trees whose rows mask tokens (-inf) in both rows, in the draft
+    only (q(x) = 0: a drafted token there is accepted) or in the target only
+    (p(x) = 0: rejected), drafts close to the target (most tokens share their
+    relative logits), uniforms pushed towards rejection: outputs against the
+    oracle, walk by walk."""
+    B, n, V = 48, 12, 6144
+    seed = 1700 + int(T * 1e5)
+    d = synth.make_tree_sample(seed, device=DEV, B=B, n=n, V=V, shape="random", temps=(T,))
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    d["draft"] = (d["target"][:, :n].float() + 0.01 * torch.randn((B, n, V), generator=g, device=DEV)).to(
+        d["draft"].dtype)
+    for which, frac in (("both", 0.3), ("draft", 0.05), ("target", 0.05)):
+        m = torch.rand((B, 1, V), generator=g, device=DEV) < frac
+        if which in ("both", "target"):
+            d["target"] = d["target"].masked_fill(m, float("-inf"))
+        if which in ("both", "draft"):
+            d["draft"] = d["draft"].masked_fill(m, float("-inf"))
+    d["target"] = d["target"].contiguous()
+    d["draft"] = d["draft"].contiguous()
+    d["uniforms"][:, :n] = (1.0 - (1.0 - d["uniforms"][:, :n]) ** 6).clamp_(max=1.0 - 2.0 ** -24)
+    _compare(oracle, d, _rounds(d), tag=f"masked rows T={T}")
