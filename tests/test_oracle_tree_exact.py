@@ -13,7 +13,8 @@ token at low temperature, so that after two rejections at a node the weight of
 the tokens the rows share is a second-order quantity (the product of two tails)
 set against first-order ones, and p - lam q computed from its parts keeps none
 of its digits.  Cases whose uniforms lie within 1e-9 of a decision boundary
-(relative) are not compared, and are counted.
+(relative) are not compared, and are counted.  The linear rule is pinned the
+same way, on the chain tree.
 """
 from decimal import Decimal, localcontext
 
@@ -130,3 +131,39 @@ def test_tree_walk_matches_exact_brute_force(oracle):
             mism.append((case, T, acc, y, int(o["accepted_len"][0]), int(o["emitted"][0, acc])))
     assert not mism, mism[:10]
     assert compared >= 270 and deep >= 30, (compared, deep, skipped)
+
+
+def test_linear_rule_matches_exact_brute_force(oracle):
+    """The linear rule (`verify_sample`: the first rejection ends the prefix and
+    the token is drawn from max(0, p - q) normalised) on the same kind of rows,
+    n = 3 drafts, against the brute force on the chain tree (node j + 1 below
+    node j), which is the same rule."""
+    rng = np.random.default_rng(777)
+    temps = [0.003, 0.01, 0.03, 0.1, 1.0]
+    compared = rejected = skipped = 0
+    mism = []
+    chain = np.array([0, 1, 2], np.int32)
+    for case in range(300):
+        zt, zd, _, _ = _case(rng)
+        zt, zd = zt[:4], zd[:3]
+        T = temps[case % len(temps)]
+        x = np.array([int(np.argmax((zd[j] - zd[j].max()) - (zt[j] - zt[j].max()))) if rng.random() < 0.6
+                      else int(rng.integers(6)) for j in range(3)], np.int32)
+        L = int(rng.integers(0, 4))
+        u = rng.random(4).astype(np.float32)
+        rel = np.concatenate([(zt - zt.max(1, keepdims=True)).ravel(), (zd - zd.max(1, keepdims=True)).ravel()])
+        with localcontext() as c:
+            c.prec = int(2.2 * float(-rel.min()) / T / 2.302) + 60
+            c.Emin, c.Emax = -10 ** 9, 10 ** 9
+            acc, y, margin, rej = exact_walk(zt, zd, x, chain, L, T, u)
+        if margin < Decimal("1e-9"):
+            skipped += 1
+            continue
+        o = oracle.verify_sample(zt[None], zd[None], x[None], np.array([L], np.int32), np.array([T], np.float32),
+                                 u[None])
+        compared += 1
+        rejected += acc < L
+        if int(o["accepted_len"][0]) != acc or int(o["emitted"][0, acc]) != y:
+            mism.append((case, T, L, acc, y, int(o["accepted_len"][0]), int(o["emitted"][0, acc])))
+    assert not mism, mism[:10]
+    assert compared >= 270 and rejected >= 60, (compared, rejected, skipped)
